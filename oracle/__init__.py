@@ -1,0 +1,278 @@
+"""CPU oracle for the batched Qwen3-style GQA decode step.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may use it; the GPU library never does.  It
+shares no code with the GPU path.  The arithmetic lives in ``qd_oracle.c``
+(plain loops, fp64 throughout; only the weights and the KV pool are bf16, as
+the pages fix); this module marshals numpy arrays into it.
+
+Every function here is pinned by tests under ``tests/`` against closed forms,
+invariants, library routines or brute force (see the test module docstrings).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_oracle.so")
+_lib = None
+
+PAGE = 16
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int), ("hidden", ctypes.c_int),
+                ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
+                ("head_dim", ctypes.c_int), ("intermediate", ctypes.c_int),
+                ("vocab", ctypes.c_int), ("tie_embeddings", ctypes.c_int),
+                ("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("in_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm",
+                                  "post_norm", "wgate", "wup", "wdown")]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("embed", _P), ("final_norm", _P), ("lm_head", _P),
+                ("layers", ctypes.POINTER(_Layer))]
+
+
+class _Taps(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int)] + [
+        (n, _P) for n in ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out",
+                          "final_h")]
+
+
+TAP_NAMES = ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out", "final_h")
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.or_bf16_to_f64.restype = ctypes.c_double
+        lib.or_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.or_f64_to_bf16.restype = ctypes.c_uint16
+        lib.or_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.or_rmsnorm.restype = None
+        lib.or_rmsnorm.argtypes = [_P, ctypes.c_int, _P, ctypes.c_double, _P]
+        lib.or_linear.restype = None
+        lib.or_linear.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P]
+        lib.or_rope_neox.restype = None
+        lib.or_rope_neox.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.or_attention.restype = None
+        lib.or_attention.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
+                                     ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P]
+        lib.or_silu.restype = ctypes.c_double
+        lib.or_silu.argtypes = [ctypes.c_double]
+        lib.or_argmax.restype = ctypes.c_int
+        lib.or_argmax.argtypes = [_P, ctypes.c_int]
+        lib.or_decode_step.restype = ctypes.c_int
+        lib.or_decode_step.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights),
+                                       ctypes.c_int, _P, _P, _P, ctypes.c_int, _P,
+                                       ctypes.c_int, _P, _P, ctypes.POINTER(_Taps)]
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _req(a, dtype) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"expected C-contiguous {np.dtype(dtype)} array, got {a.dtype}")
+    return a
+
+
+# ----------------------------------------------------------------------------- scalar ops
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """float64 -> nearest bf16 bit pattern (ties to even), one rounding step."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for i, v in enumerate(flat):
+        out[i] = lib.or_f64_to_bf16(float(v))
+    return out.reshape(x.shape)
+
+
+def rmsnorm(x, gain_bf16, eps: float = 1e-6) -> np.ndarray:
+    lib = _load()
+    x = _f64(x)
+    g = _req(gain_bf16, np.uint16)
+    n = x.shape[-1]
+    assert g.shape == (n,)
+    y = np.empty_like(x)
+    xf, yf = x.reshape(-1, n), y.reshape(-1, n)
+    for r in range(xf.shape[0]):
+        lib.or_rmsnorm(xf[r].ctypes.data, n, g.ctypes.data, eps, yf[r].ctypes.data)
+    return y
+
+
+def linear(x, w_bf16) -> np.ndarray:
+    """x [B, K] float64, w [N, K] bf16 -> [B, N]."""
+    lib = _load()
+    x = _f64(np.atleast_2d(x))
+    w = _req(w_bf16, np.uint16)
+    B, K = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, K)
+    y = np.empty((B, N), dtype=np.float64)
+    lib.or_linear(x.ctypes.data, B, K, w.ctypes.data, N, y.ctypes.data)
+    return y
+
+
+def rope_neox(v, pos: int, theta: float = 1e6) -> np.ndarray:
+    """NeoX rotary embedding of each row of v (last axis = head_dim) at pos."""
+    lib = _load()
+    v = _f64(v).copy()
+    D = v.shape[-1]
+    vf = v.reshape(-1, D)
+    for r in range(vf.shape[0]):
+        lib.or_rope_neox(vf[r].ctypes.data, D, int(pos), theta)
+    return v
+
+
+def attention(q, pool, layer: int, table_row, ctx: int, num_kv_heads: int) -> np.ndarray:
+    """q [Hq, D] float64; pool uint16 [L][P][2][Hkv][16][D]; -> o [Hq, D]."""
+    lib = _load()
+    q = _f64(q)
+    pool = _req(pool, np.uint16)
+    row = _req(np.asarray(table_row, dtype=np.int32), np.int32)
+    Hq, D = q.shape
+    assert pool.shape[3] == num_kv_heads and pool.shape[5] == D and pool.shape[4] == PAGE
+    assert len(row) * PAGE >= ctx
+    o = np.empty_like(q)
+    lib.or_attention(q.ctypes.data, Hq, num_kv_heads, D, pool.ctypes.data, pool.shape[1],
+                     layer, row.ctypes.data, ctx, o.ctypes.data)
+    return o
+
+
+def silu(z) -> np.ndarray:
+    lib = _load()
+    z = np.asarray(z, dtype=np.float64)
+    return np.vectorize(lib.or_silu, otypes=[np.float64])(z)
+
+
+def argmax(v) -> int:
+    lib = _load()
+    v = _f64(v)
+    return int(lib.or_argmax(v.ctypes.data, v.shape[0]))
+
+
+# ----------------------------------------------------------------------------- decode step
+
+class Oracle:
+    """Holds a model's bf16 weights (HF names) and runs decode steps on a pool."""
+
+    def __init__(self, shape, weights: Dict[str, np.ndarray]):
+        self.shape = shape
+        self._keep = []
+        c = _Config(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
+                    shape.head_dim, shape.intermediate, shape.vocab,
+                    int(shape.tie_embeddings), shape.rms_eps, shape.rope_theta)
+        self._cfg = c
+
+        def ptr(name):
+            a = _req(weights[name], np.uint16)
+            self._keep.append(a)
+            return a.ctypes.data
+
+        L = shape.num_layers
+        layers = (_Layer * L)()
+        for l in range(L):
+            p = f"model.layers.{l}."
+            layers[l] = _Layer(ptr(p + "input_layernorm.weight"),
+                               ptr(p + "self_attn.q_proj.weight"),
+                               ptr(p + "self_attn.k_proj.weight"),
+                               ptr(p + "self_attn.v_proj.weight"),
+                               ptr(p + "self_attn.o_proj.weight"),
+                               ptr(p + "self_attn.q_norm.weight"),
+                               ptr(p + "self_attn.k_norm.weight"),
+                               ptr(p + "post_attention_layernorm.weight"),
+                               ptr(p + "mlp.gate_proj.weight"),
+                               ptr(p + "mlp.up_proj.weight"),
+                               ptr(p + "mlp.down_proj.weight"))
+        self._layers = layers
+        lm = None if shape.tie_embeddings else ptr("lm_head.weight")
+        self._w = _Weights(ptr("model.embed_tokens.weight"), ptr("model.norm.weight"), lm,
+                           ctypes.cast(layers, ctypes.POINTER(_Layer)))
+
+    def decode_step(self, tokens, positions, block_tables, pool: np.ndarray,
+                    want_logits: bool = True, tap_layer: Optional[int] = None):
+        """One decode step; appends to ``pool`` in place.
+
+        Returns (logits [B, V] float64 or None, next [B] int32, taps dict)."""
+        lib = _load()
+        s = self.shape
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        positions = np.ascontiguousarray(positions, dtype=np.int32)
+        tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        pool = _req(pool, np.uint16)
+        B = tokens.shape[0]
+        assert positions.shape == (B,) and tables.shape[0] == B
+        assert pool.shape[0] == s.num_layers and pool.shape[2] == 2
+        logits = np.empty((B, s.vocab), dtype=np.float64) if want_logits else None
+        nxt = np.empty(B, dtype=np.int32)
+        taps = {}
+        tp = None
+        if tap_layer is not None:
+            QD, KD = s.q_dim, s.kv_dim
+            dims = {"x_in": (B, s.hidden), "qkv": (B, QD + 2 * KD),
+                    "q_rot": (B, s.num_q_heads, s.head_dim),
+                    "k_rot": (B, s.num_kv_heads, s.head_dim),
+                    "attn": (B, s.num_q_heads, s.head_dim), "x_mid": (B, s.hidden),
+                    "act": (B, s.intermediate), "x_out": (B, s.hidden),
+                    "final_h": (B, s.hidden)}
+            taps = {k: np.zeros(v, dtype=np.float64) for k, v in dims.items()}
+            tp = _Taps(int(tap_layer), *[taps[n].ctypes.data for n in TAP_NAMES])
+        rc = lib.or_decode_step(ctypes.byref(self._cfg), ctypes.byref(self._w), B,
+                                tokens.ctypes.data, positions.ctypes.data, tables.ctypes.data,
+                                tables.shape[1], pool.ctypes.data, pool.shape[1],
+                                logits.ctypes.data if logits is not None else None,
+                                nxt.ctypes.data, ctypes.byref(tp) if tp is not None else None)
+        if rc != 0:
+            raise ValueError("oracle rejected the step arguments")
+        return logits, nxt, taps
+
+    def prefill(self, prompt, block_table_row, pool: np.ndarray):
+        """Run the prompt through the decoder one position at a time (0..T-1),
+        filling the pool; returns (logits of the last position, greedy next id)."""
+        prompt = np.asarray(prompt, dtype=np.int32)
+        row = np.ascontiguousarray(np.asarray(block_table_row, dtype=np.int32)[None, :])
+        logits = nxt = None
+        for t in range(len(prompt)):
+            logits, nxt, _ = self.decode_step(prompt[t:t + 1], np.array([t], np.int32), row,
+                                              pool, want_logits=(t == len(prompt) - 1))
+        return logits[0], int(nxt[0])

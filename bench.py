@@ -1,0 +1,275 @@
+"""Decode-step throughput of libqd on one MI355X.
+
+A step is one batched decode step of a Qwen3-style GQA decoder (embedding,
+36 x [RMSNorm + QKV, q/k-norm + RoPE + paged KV append + split-KV attention,
+O + residual, RMSNorm + gate/up + SwiGLU, down + residual], final RMSNorm, LM
+head, on-device argmax) over synthetic seeded weights and paged K/V, replayed
+from one captured hipGraph.  Steps are chained on the device: each step's
+next-token ids are the following step's input (two ping-pong id buffers, so
+the two graphs never change), and the positions advance on the device.
+
+Headline line: Qwen3-4B shape, batch 1, context 512 (value = tokens/s).  The
+same JSON line also carries batch 8 / 16 at context 256 and batch 1 at 8192
+under "workloads", the live roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b]
+                       [--no-cpu-baseline] [--profile-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+from paged_kv_gqa_qwen3_amd import accounting, binding, synth  # noqa: E402
+
+METRIC = "decode tokens/s + achieved HBM GB/s (% of 8 TB/s), Qwen3-4B shape, bs 1/8/16"
+HBM_PEAK_GBPS = 8000.0
+HEADLINE = "4b_bs1_ctx512"
+DEFAULT_WORKLOADS = ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192"]
+WEIGHT_SEED = {"qwen3-4b": 2, "qwen3-8b": 6}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(shape, cls):
+    """Algorithmic bytes one launch of a projection class reads (bf16 weights)."""
+    H, I = shape.hidden, shape.intermediate
+    return {
+        "qkv": (shape.q_dim + 2 * shape.kv_dim) * H * 2,
+        "o_proj": H * shape.q_dim * 2,
+        "gate_up": 2 * I * H * 2,
+        "down": H * I * 2,
+        "lm_head": shape.vocab * H * 2,
+    }[cls]
+
+
+def attention_bytes(shape, ctx):
+    """K/V bytes one attention launch (one layer) reads and appends."""
+    per_tok_layer = 2 * shape.num_kv_heads * shape.head_dim * 2
+    return sum(int(c) for c in ctx) * per_tok_layer
+
+
+class Run:
+    """One workload on one handle: pool, tables and chained device buffers."""
+
+    def __init__(self, torch, dec, w, batch):
+        self.torch, self.dec, self.w, self.batch = torch, dec, w, batch
+        B = w.batch
+        dev = "cuda"
+        self.pool = torch.from_numpy(batch.pool.view(np.int16)).to(dev)
+        self.tab = torch.from_numpy(batch.block_tables).to(dev)
+        self.pos0 = torch.from_numpy(batch.positions).to(dev)
+        self.pos = self.pos0.clone()
+        self.ids = [torch.from_numpy(batch.tokens).to(dev),
+                    torch.zeros(B, dtype=torch.int32, device=dev)]
+        self.k = 0
+
+    def step(self):
+        a, b = self.ids[self.k & 1], self.ids[(self.k + 1) & 1]
+        self.dec.step(a, self.pos, self.tab, self.pool, b, None)
+        self.pos.add_(1)
+        self.k += 1
+
+    def reset(self):
+        self.pos.copy_(self.pos0)
+
+
+def time_workload(torch, dec, w, batch, steps, warmup):
+    run = Run(torch, dec, w, batch)
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    run.reset()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        run.step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    flags = dec.device_status()
+    if flags:
+        raise RuntimeError(f"device input flags {flags} during {w.name}")
+    ctx0 = batch.positions.astype(np.int64) + 1
+    total_bytes = sum(accounting.step_bytes(w.shape, ctx0 + s) for s in range(steps))
+    return run, ms, wall, total_bytes
+
+
+def profile_classes(torch, dec, run, reps=5):
+    """Per-kernel-class times from HIP events recorded on the library's stream."""
+    acc = {c: [0.0, 0] for c in binding.PROF_CLASSES}
+    B = run.w.batch
+    for _ in range(reps):
+        run.reset()
+        a, b = run.ids[0], run.ids[1]
+        res = binding.qd_profile_step(dec.handle, B, a, run.pos, run.tab, run.pool, b, None)
+        for c, (ms, n) in res.items():
+            acc[c][0] += ms
+            acc[c][1] += n
+    return {c: (v[0], v[1]) for c, v in acc.items()}
+
+
+def cpu_baseline(w, W, batch, budget_s=20.0):
+    """The oracle, as it stands, timed on this host on a bounded sample of the
+    same workload: consecutive decode steps of the same batch until about
+    budget_s seconds have passed (at least one)."""
+    import oracle
+
+    orc = oracle.Oracle(w.shape, W)
+    pool = batch.pool.copy()
+    tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        _, nxt, _ = orc.decode_step(tokens, positions, batch.block_tables, pool,
+                                    want_logits=False)
+        steps += 1
+        tokens, positions = nxt.astype(np.int32), positions + 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    ncpu = len(os.sched_getaffinity(0))
+    cores = min(threads, ncpu) if threads > 0 else ncpu
+    return {"value": round(steps * w.batch / dt, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{steps} decode step(s) of {w.name} (batch {w.batch}, context "
+                      f"{int(batch.positions[0])}+), {dt:.1f} s, fp64 C oracle with OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the decode step "
+              "has no multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load_library()
+    names = [n for n in args.workloads.split(",") if n]
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
+    wl = [synth.WORKLOADS[n] for n in names]
+    results = {}
+    headline_extra = {}
+    by_shape = {}
+    for w in wl:
+        by_shape.setdefault(w.shape.name, []).append(w)
+
+    for shape_name, group in by_shape.items():
+        shape = group[0].shape
+        batches = {w.name: synth.make_paged_batch(shape, synth.context_lengths(w), w.steps,
+                                                  w.seed)
+                   for w in group}
+        maxp = max(b.max_pages for b in batches.values())
+        npages = max(b.num_pages for b in batches.values())
+        for w in group:  # one pool shape per handle: pad every pool to npages pages
+            b = batches[w.name]
+            if b.num_pages < npages:
+                batches[w.name] = synth.make_paged_batch(
+                    shape, synth.context_lengths(w), w.steps, w.seed,
+                    spare_pages=npages - b.num_pages)
+            bt = batches[w.name].block_tables
+            if bt.shape[1] < maxp:
+                pad = np.full((bt.shape[0], maxp - bt.shape[1]), batches[w.name].poison_page,
+                              np.int32)
+                batches[w.name].block_tables = np.ascontiguousarray(np.concatenate([bt, pad], 1))
+        log(f"[bench] generating {shape_name} weights")
+        t0 = time.perf_counter()
+        W = synth.make_weights(shape, WEIGHT_SEED[shape_name])
+        log(f"[bench] weights ready in {time.perf_counter() - t0:.1f}s")
+        from paged_kv_gqa_qwen3_amd.decoder import Decoder
+
+        dec = Decoder(shape, max(w.batch for w in group), maxp, npages, use_graphs=True)
+        dec.load_numpy_weights(W)
+        for w in group:
+            batch = batches[w.name]
+            log(f"[bench] {w.name}: timing {args.steps} steps after {args.warmup} warmup")
+            run, ms, wall, nbytes = time_workload(torch, dec, w, batch, args.steps, args.warmup)
+            tok_s = args.steps * w.batch / (ms / 1e3)
+            gbps = nbytes / (ms / 1e3) / 1e9
+            results[w.name] = {
+                "workload": w.name, "batch": w.batch,
+                "context0": [int(c) for c in batch.positions[:4]] + (["..."] if w.batch > 4 else []),
+                "tokens_per_s": round(tok_s, 2), "ms_per_step": round(ms / args.steps, 4),
+                "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "wall_s": round(wall, 4),
+            }
+            log(f"[bench] {w.name}: {tok_s:.1f} tok/s, {ms / args.steps:.4f} ms/step, "
+                f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+            if w.name == HEADLINE:
+                prof = profile_classes(torch, dec, run)
+                ctx_mid = batch.positions.astype(np.int64) + 1
+                per_class = {}
+                for c, (tot_ms, n) in prof.items():
+                    if n == 0:
+                        continue
+                    avg_us = tot_ms / n * 1e3
+                    if c in ("qkv", "o_proj", "gate_up", "down", "lm_head"):
+                        byts = gemv_bytes(shape, c)
+                    elif c == "attention":
+                        byts = attention_bytes(shape, ctx_mid)
+                    else:
+                        byts = w.batch * shape.hidden * 2
+                    per_class[c] = {"launches_per_step": n // 5, "avg_us": round(avg_us, 3),
+                                    "bytes_per_launch": int(byts),
+                                    "GBps": round(byts / (avg_us * 1e-6) / 1e9, 1),
+                                    "ms_per_step": round(tot_ms / 5, 4)}
+                dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
+                d = per_class[dom]
+                headline_extra = {
+                    "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBps"],
+                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
+                                 "traffic": None},
+                    "kernel_classes": per_class,
+                }
+                if not args.no_cpu_baseline:
+                    log("[bench] timing the CPU oracle on a bounded sample")
+                    headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)
+            del run
+            torch.cuda.empty_cache()
+        dec.close()
+        del W
+
+    h = results[HEADLINE]
+    out = {
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 paged K/V)",
+        "config": {"workload": "Qwen3-4B-shaped decode, batch 1, context 512, 16-token pages, "
+                               "shuffled block table", "name": HEADLINE, "batch": 1,
+                   "context0": 512, "parallelism": "single GPU"},
+        "achieved_GBps": h["achieved_GBps"], "hbm_frac": h["hbm_frac"],
+    }
+    out.update(headline_extra)
+    out["workloads"] = [results[n] for n in names if n in results]
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

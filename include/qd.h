@@ -1,0 +1,176 @@
+/*
+ * qd - one batched autoregressive decode step of a Qwen3-style GQA decoder
+ * on AMD MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ types.
+ *
+ * Sources (the pages this library follows, by title):
+ *   [blog]    "GPU 算子与执行优化：从 26 到 100 token/s" (qwen3-runtime)
+ *   [engine]  "从零构建 Qwen3-8B 推理引擎，C++/CUDA 实现性能追平 98%"
+ *   [infer]   "推理引擎里面发生了什么"
+ *   [graphs]  "突破vLLM推理性能瓶颈：CUDA Graph深度优化实战指南"
+ *
+ * The step, for each sequence b of the batch, with token t = token_ids[b]
+ * at position p = positions[b] (context = p + 1 tokens, the new one
+ * included):
+ *   x = E[t]                                          (embedding lookup)
+ *   per layer ([engine] 4.2.2 pre-norm layer; [blog] Part 6 op list):
+ *     h = RMSNorm(x) ; q,k,v = h Wq^T, h Wk^T, h Wv^T (one fused QKV
+ *         projection, [engine] 4.4.3)
+ *     q,k per head: RMSNorm over head_dim, then NeoX RoPE at p ([blog] Part 6)
+ *     k,v (bf16) appended to the paged pool at position p ([blog] Part 4;
+ *         [infer] PagedAttention: 16-token blocks and a per-request table)
+ *     o = softmax(q K^T / sqrt(D)) V over positions 0..p, query head h using
+ *         KV head h / (Hq/Hkv) ([engine] 4.4.2), computed split-KV with a
+ *         log-sum-exp combine ([blog] Part 8)
+ *     x += o Wo^T
+ *     x += (silu(RMSNorm(x) Wg^T) * (RMSNorm(x) Wu^T)) Wd^T   ([blog] Part 6)
+ *   logits = RMSNorm(x) Wlm^T (tied: Wlm = E) ; next = argmax ([blog] Part 3,
+ *   greedy sampling on the device, only the token id leaves the step)
+ * Weights and the KV pool are bf16; all accumulation is fp32.
+ *
+ * Threading: a handle is used by one host thread at a time.  Calls are
+ * asynchronous on the handle's stream unless stated otherwise.
+ */
+#ifndef QD_H
+#define QD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  0 is success; every failure is negative. */
+#define QD_OK 0
+#define QD_EINVAL -1        /* a NULL pointer, a bad size or an unknown name */
+#define QD_EUNSUPPORTED -2  /* a shape or option this build does not handle */
+#define QD_ESTATE -3        /* e.g. decode before every weight was loaded */
+#define QD_EHIP -4          /* a HIP runtime call failed; see qd_last_error */
+#define QD_ENOMEM -5        /* device allocation failed */
+
+/* Bits reported by qd_device_status (input errors the kernels detected). */
+#define QD_DEV_BAD_TOKEN 1     /* a token id outside [0, vocab) (clamped) */
+#define QD_DEV_BAD_POSITION 2  /* a position outside [0, max_pages_per_seq*16) */
+#define QD_DEV_BAD_PAGE 4      /* a block-table entry outside [0, num_pages) */
+
+typedef struct qd_handle qd_handle;
+
+/* Model and capacity.  Shapes follow the HF Qwen3 config names. */
+typedef struct qd_config {
+  int32_t num_layers;          /* L */
+  int32_t hidden;              /* H; multiple of 64 */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 and Hq/Hkv <= 8 */
+  int32_t head_dim;            /* D; 64 or 128 */
+  int32_t intermediate;        /* I; multiple of 32 */
+  int32_t vocab;               /* V; multiple of 64 */
+  int32_t tie_embeddings;      /* 1: the LM head is the embedding matrix */
+  float rms_eps;               /* RMSNorm epsilon (Qwen3: 1e-6) */
+  double rope_theta;           /* RoPE base (Qwen3: 1e6) */
+  int32_t page_size;           /* tokens per KV page; must be 16 */
+  int32_t max_batch;           /* largest batch passed to qd_decode_step (1..64) */
+  int32_t max_pages_per_seq;   /* block-table row length */
+  int32_t num_pages;           /* pages in the caller's pool */
+  int32_t use_graphs;          /* 1: replay one captured hipGraph per batch size */
+} qd_config;
+
+/* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
+ * row-major bf16 array (dtype 0), shape [rows, cols] or [n] for norm gains. */
+typedef struct qd_tensor_desc {
+  const char* name;   /* HF name, e.g. "model.layers.3.self_attn.q_proj.weight" */
+  const void* data;   /* device pointer, bf16 */
+  int32_t ndim;       /* 1 or 2 */
+  int64_t shape[2];
+  int32_t dtype;      /* 0 = bf16 (the only one accepted) */
+} qd_tensor_desc;
+
+/* Create a decoder for `cfg`, bound to HIP stream `hip_stream` (a
+ * hipStream_t; NULL means the null stream) on the current device.  Allocates
+ * the packed-weight arena, activations, split-KV and split-K scratch and the
+ * RoPE table (cos/sin of p * theta^(-2i/D) computed in double, stored fp32).
+ * Returns QD_OK and *out, or an error (then *out is NULL).  Synchronous. */
+int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
+
+/* Copy weights in.  Accepts the HF tensor names of a Qwen3 checkpoint
+ * (model.embed_tokens, model.layers.N.{input_layernorm, self_attn.{q,k,v,o}_proj,
+ * self_attn.{q,k}_norm, post_attention_layernorm, mlp.{gate,up,down}_proj},
+ * model.norm, lm_head when untied) with their HF shapes ([out, in] for
+ * projections).  Tensors may come in several calls.  The library repacks
+ * them into its own tile layout (q|k|v fused, gate and up paired) and keeps
+ * no reference to the caller's memory once the call returns.
+ * QD_EINVAL on an unknown name or a wrong shape.  Synchronous. */
+int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
+
+/* One decode step for `batch` sequences (1 <= batch <= max_batch).  All
+ * pointers are DEVICE pointers:
+ *   token_ids    int32 [batch]       token decoded by each sequence
+ *   positions    int32 [batch]       its position p (= tokens already cached)
+ *   block_tables int32 [batch][max_pages_per_seq]  physical page ids; entries
+ *                                    0 .. p/16 must name pages of kv_pool
+ *   kv_pool      bf16 [L][num_pages][2][Hkv][16][D]  caller-owned paged pool
+ *                                    (index 0 = K, 1 = V); this step writes
+ *                                    K/V of position p of every sequence and
+ *                                    reads positions 0..p
+ *   out_next_ids int32 [batch]       greedy next token (lowest index on ties)
+ *   out_logits   fp32 [batch][vocab] or NULL
+ * Sequences in one call must not write the same pool slot.  Asynchronous;
+ * with use_graphs the first call for a (batch, pointer set) captures a
+ * hipGraph and later calls replay it (new pointers cause a new capture).
+ * Kernels clamp out-of-range ids, positions and page ids instead of reading
+ * out of bounds, and record them for qd_device_status. */
+int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                   const int32_t* positions, const int32_t* block_tables, void* kv_pool,
+                   int32_t* out_next_ids, float* out_logits);
+
+/* Intermediate values of one layer, for checking each stage of the step
+ * (fp32 DEVICE buffers; any may be NULL):
+ *   x_in [B][H]  qkv [B][(Hq+2Hkv)D]  q_rot [B][Hq][D]  k_rot [B][Hkv][D]
+ *   attn [B][Hq][D]  x_mid [B][H]  act [B][I]  x_out [B][H]  final_h [B][H] */
+typedef struct qd_taps {
+  int32_t layer;
+  float *x_in, *qkv, *q_rot, *k_rot, *attn, *x_mid, *act, *x_out, *final_h;
+} qd_taps;
+
+/* qd_decode_step without graphs, also filling `taps` (may be NULL). */
+int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                        const int32_t* positions, const int32_t* block_tables,
+                        void* kv_pool, int32_t* out_next_ids, float* out_logits,
+                        const qd_taps* taps);
+
+/* Kernel classes timed by qd_profile_step. */
+#define QD_PROF_EMBED 0    /* embedding gather */
+#define QD_PROF_QKV 1      /* RMSNorm + fused QKV projection */
+#define QD_PROF_ATTN 2     /* q/k norm + RoPE + KV append + split-KV attention */
+#define QD_PROF_O 3        /* O projection + residual */
+#define QD_PROF_GATE_UP 4  /* RMSNorm + gate/up projection + SwiGLU */
+#define QD_PROF_DOWN 5     /* down projection + residual */
+#define QD_PROF_LM_HEAD 6  /* final RMSNorm + LM head + argmax */
+#define QD_PROF_CLASSES 7
+
+/* Run one step eagerly with a HIP event recorded on the handle's stream
+ * between consecutive kernels, and return per class the summed kernel time
+ * in milliseconds (class_ms[QD_PROF_CLASSES]) and the number of launches
+ * (class_launches[QD_PROF_CLASSES]).  Same arguments and effects as
+ * qd_decode_step.  Synchronous. */
+int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                    const int32_t* positions, const int32_t* block_tables, void* kv_pool,
+                    int32_t* out_next_ids, float* out_logits, float* class_ms,
+                    int32_t* class_launches);
+
+/* Wait for the handle's stream, then return (and clear) the QD_DEV_* bits
+ * the kernels recorded since the last call in *flags.  Synchronous. */
+int qd_device_status(qd_handle* h, int32_t* flags);
+
+/* The handle's stream (a hipStream_t), for callers that time or order work. */
+void* qd_stream(const qd_handle* h);
+
+/* Free everything the handle owns (waits for its stream first). */
+void qd_destroy(qd_handle* h);
+
+/* Text of the last error on this handle (or of the last failed qd_create when
+ * h is NULL).  Valid until the next call on the handle. */
+const char* qd_last_error(const qd_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QD_H */

@@ -1,0 +1,200 @@
+"""ctypes binding of libqd (include/qd.h): the same entry points, argument
+marshalling only.  Every step of the decode path runs in the library's HIP
+kernels; this module never computes anything itself and raises if the
+library is missing.
+
+Device memory and streams come from PyTorch: pass torch tensors (on the GPU)
+or raw integer device pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqd.so")
+
+QD_OK = 0
+QD_EINVAL = -1
+QD_EUNSUPPORTED = -2
+QD_ESTATE = -3
+QD_EHIP = -4
+QD_ENOMEM = -5
+
+QD_DEV_BAD_TOKEN = 1
+QD_DEV_BAD_POSITION = 2
+QD_DEV_BAD_PAGE = 4
+
+EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
+            "qd_profile_step", "qd_device_status", "qd_stream", "qd_destroy", "qd_last_error")
+
+PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
+
+
+class QdConfig(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("tie_embeddings", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("use_graphs", ctypes.c_int32)]
+
+
+class QdTensorDesc(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 2), ("dtype", ctypes.c_int32)]
+
+
+class QdTaps(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act",
+                                       "x_out", "final_h")]
+
+
+TAP_NAMES = ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out", "final_h")
+
+_lib = None
+
+
+class QdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qd error {code}: {msg}")
+        self.code = code
+
+
+def load_library():
+    """Load libqd.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        lib.qd_create.restype = ctypes.c_int
+        lib.qd_create.argtypes = [ctypes.POINTER(QdConfig), P, ctypes.POINTER(P)]
+        lib.qd_load_weights.restype = ctypes.c_int
+        lib.qd_load_weights.argtypes = [P, ctypes.POINTER(QdTensorDesc), ctypes.c_int32]
+        lib.qd_decode_step.restype = ctypes.c_int
+        lib.qd_decode_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
+        lib.qd_decode_step_taps.restype = ctypes.c_int
+        lib.qd_decode_step_taps.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
+                                            ctypes.POINTER(QdTaps)]
+        lib.qd_profile_step.restype = ctypes.c_int
+        lib.qd_profile_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
+                                        ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_int32)]
+        lib.qd_device_status.restype = ctypes.c_int
+        lib.qd_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+        lib.qd_stream.restype = P
+        lib.qd_stream.argtypes = [P]
+        lib.qd_destroy.restype = None
+        lib.qd_destroy.argtypes = [P]
+        lib.qd_last_error.restype = ctypes.c_char_p
+        lib.qd_last_error.argtypes = [P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(rc: int, handle) -> None:
+    if rc != QD_OK:
+        msg = load_library().qd_last_error(handle)
+        raise QdError(rc, msg.decode() if msg else "")
+
+
+def make_config(shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
+                use_graphs: bool = True) -> QdConfig:
+    return QdConfig(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
+                    shape.head_dim, shape.intermediate, shape.vocab, int(shape.tie_embeddings),
+                    shape.rms_eps, shape.rope_theta, 16, max_batch, max_pages_per_seq,
+                    num_pages, int(use_graphs))
+
+
+def qd_create(cfg: QdConfig, stream: int = 0) -> int:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    rc = lib.qd_create(ctypes.byref(cfg), ctypes.c_void_p(stream), ctypes.byref(h))
+    _check(rc, None)
+    return h.value
+
+
+def qd_load_weights(handle: int, tensors: Dict[str, object]) -> None:
+    """tensors: HF name -> bf16 device tensor (torch.bfloat16 on the GPU)."""
+    lib = load_library()
+    descs = (QdTensorDesc * len(tensors))()
+    keep = []
+    for i, (name, t) in enumerate(tensors.items()):
+        nb = name.encode()
+        keep.append(nb)
+        shape = tuple(t.shape)
+        d = descs[i]
+        d.name = nb
+        d.data = _ptr(t)
+        d.ndim = len(shape)
+        d.shape[0] = shape[0]
+        d.shape[1] = shape[1] if len(shape) > 1 else 0
+        d.dtype = 0
+    _check(lib.qd_load_weights(handle, descs, len(tensors)), handle)
+
+
+def qd_decode_step(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,
+                   out_next_ids, out_logits=None) -> None:
+    lib = load_library()
+    _check(lib.qd_decode_step(handle, batch, _ptr(token_ids), _ptr(positions),
+                              _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
+                              _ptr(out_logits)), handle)
+
+
+def qd_decode_step_taps(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,
+                        out_next_ids, out_logits=None, taps: Optional[dict] = None,
+                        tap_layer: int = -1) -> None:
+    lib = load_library()
+    tp = None
+    if taps is not None:
+        tp = QdTaps(tap_layer, *[_ptr(taps.get(n)) for n in TAP_NAMES])
+    _check(lib.qd_decode_step_taps(handle, batch, _ptr(token_ids), _ptr(positions),
+                                   _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
+                                   _ptr(out_logits), ctypes.byref(tp) if tp else None), handle)
+
+
+def qd_profile_step(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,
+                    out_next_ids, out_logits=None):
+    """One eager step timed per kernel class; returns {class: (ms, launches)}."""
+    lib = load_library()
+    n = len(PROF_CLASSES)
+    ms = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(lib.qd_profile_step(handle, batch, _ptr(token_ids), _ptr(positions),
+                               _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
+                               _ptr(out_logits), ms, cnt), handle)
+    return {PROF_CLASSES[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def qd_device_status(handle: int) -> int:
+    lib = load_library()
+    v = ctypes.c_int32(0)
+    _check(lib.qd_device_status(handle, ctypes.byref(v)), handle)
+    return v.value
+
+
+def qd_stream(handle: int) -> int:
+    return load_library().qd_stream(handle) or 0
+
+
+def qd_destroy(handle: int) -> None:
+    load_library().qd_destroy(handle)
+
+
+def qd_last_error(handle: Optional[int] = None) -> str:
+    msg = load_library().qd_last_error(handle)
+    return msg.decode() if msg else ""

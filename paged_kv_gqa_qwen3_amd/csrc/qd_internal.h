@@ -1,0 +1,100 @@
+// Internal interface between the host runtime (qd_runtime.cpp) and the HIP
+// kernels (qd_kernels.hip).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qd {
+
+// Packed weight layout ("tile-major").  A [N][K] bf16 matrix is stored as
+// tiles of 16 rows x 32 columns, tile (rt, kt) at element offset
+// (rt * (K/32) + kt) * 512; inside a tile, lane l of a wave owns the 16 bytes
+// at element offset l * 8: row rt*16 + l%16, columns kt*32 + (l/16)*8 .. +8.
+// One 64-lane 16-byte load therefore reads one whole 1 KB tile, and the lane
+// ownership is exactly the A operand of a 16x16x32 bf16 MFMA.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 32;
+constexpr int kTileElems = kTileRows * kTileCols;  // 512 bf16 = 1 KB
+constexpr int kRowsPerGroup = 64;                  // rows one GEMV workgroup finishes
+constexpr int kPage = 16;                          // tokens per KV page
+constexpr int kMaxBatch = 64;
+
+// Epilogues of the GEMV kernel.
+enum GemvMode : int {
+  kStore = 0,   // out[b][n] = y
+  kResid = 1,   // x[b][n] += y, and partial sums of squares of the new x
+  kSwiGLU = 2,  // act[b][i] = silu(gate_i) * up_i  (row tiles paired gate|up)
+  kArgmax = 3,  // optional logits, then argmax over all rows per batch column
+};
+
+struct GemvArgs {
+  const uint16_t* w;   // packed tiles, N x K
+  int N, K, B, Bmax;
+  int S, kps;          // K split count and k-tiles per split
+  const float* x;      // input activations [B][K] fp32
+  const float* ssq;    // if non-null: RMSNorm the input; [K/64][Bmax] partial sums of squares
+  const float* gain;   // [K] RMSNorm gain
+  float eps;
+  float* part;         // split-K partials [N/64 * S][64][B]
+  unsigned* counters;  // [N/64] split-K arrival counters (zero between launches)
+  float* out;          // kStore: [B][N]; kResid: x [B][N]; kSwiGLU: [B][N/2]
+  float* ssq_out;      // kResid: [N/64][Bmax]
+  float* logits;       // kArgmax: [B][N] or null
+  float* amax_val;     // kArgmax: [N/64][Bmax]
+  int* amax_idx;       // kArgmax: [N/64][Bmax]
+  unsigned* amax_counter;
+  int* next_ids;       // kArgmax: [B]
+};
+
+struct AttnArgs {
+  const float* qkv;        // [B][(Hq+2Hkv)D]
+  const float* q_gain;     // [D]
+  const float* k_gain;     // [D]
+  const float* rope_cos;   // [max_pos][D/2]
+  const float* rope_sin;
+  int max_pos;
+  uint16_t* pool_layer;    // this layer's slice of the pool: [P][2][Hkv][16][D]
+  int num_pages;
+  const int* positions;    // [B]
+  const int* block_tables; // [B][max_pages]
+  int max_pages;
+  int B, Hq, Hkv;
+  float eps, scale;
+  int S_max;               // splits per (sequence, KV head) the grid provides
+  float* o_part;           // [B*Hq][S_max][D]
+  float* ml_part;          // [B*Hq][S_max][2]  (running max, running sum)
+  unsigned* counters;      // [B*Hkv] split arrival counters (zero between launches)
+  float* out;              // [B][Hq][D]
+  float* tap_q;            // optional [B][Hq][D] (after norm and RoPE, unscaled)
+  float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
+  int* dev_flags;
+};
+
+struct EmbedArgs {
+  const uint16_t* table;   // packed [V][H]
+  int V, H, B, Bmax;
+  const int* tokens;
+  float* x;                // [B][H]
+  float* ssq_out;          // [H/64][Bmax]
+  int* dev_flags;
+};
+
+// Minimum pages a split of a sequence covers (one per wave of a workgroup).
+constexpr int kMinPagesPerSplit = 4;
+
+// Launchers (qd_kernels.hip).  All return the launch status.
+hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int tile_mul,
+                         int tile_add, hipStream_t s);
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
+                               int B, int Bmax, float eps, float* out, hipStream_t s);
+
+// LDS bytes a GEMV workgroup needs for its input slice.
+size_t gemv_lds_bytes(int B, int kps);
+
+}  // namespace qd

@@ -1,0 +1,595 @@
+// Host runtime of libqd: handle, weight repack, step orchestration and one
+// captured hipGraph per (batch size, pointer set).
+//
+// The graph design follows the pages' decode-graph pattern ("GPU 算子与执行优化",
+// Part 5: dynamic metadata stays outside, addresses inside the graph are
+// frozen; "突破vLLM推理性能瓶颈", section 2: one graph per batch size) with one
+// change: the split-KV partition count is derived on the device from the
+// positions, so a single graph per batch size serves every context length
+// (the blog's Part 8 had to leave graphs above 2048 tokens because a frozen
+// grid fixed the split count).
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "qd.h"
+#include "qd_internal.h"
+
+using namespace qd;
+
+namespace {
+
+std::string g_create_error;
+
+struct GraphKey {
+  int B;
+  const void* p[6];
+  bool operator<(const GraphKey& o) const {
+    if (B != o.B) return B < o.B;
+    return std::memcmp(p, o.p, sizeof(p)) < 0;
+  }
+};
+
+struct GemvPlan {
+  int S = 1, kps = 1;
+};
+
+struct LayerW {
+  uint16_t *qkv = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr;
+  float *in_norm = nullptr, *post_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+};
+
+}  // namespace
+
+struct qd_handle {
+  qd_config cfg{};
+  hipStream_t stream = nullptr;
+  hipStream_t cap = nullptr;
+  int device = 0;
+  int num_cus = 256;
+  std::string err;
+
+  int L = 0, H = 0, Hq = 0, Hkv = 0, D = 0, I = 0, V = 0, QD = 0, KD = 0, NQKV = 0, G = 0;
+  std::vector<void*> allocs;
+  std::vector<LayerW> lw;
+  uint16_t* embed = nullptr;
+  uint16_t* lm = nullptr;
+  float* final_norm = nullptr;
+  std::map<std::string, int> expected;  // name -> loaded (0/1)
+
+  float *x = nullptr, *ssq = nullptr, *qkv = nullptr, *attn = nullptr, *act = nullptr;
+  float* part = nullptr;
+  unsigned* gemv_cnt = nullptr;
+  float *o_part = nullptr, *ml_part = nullptr;
+  unsigned* attn_cnt = nullptr;
+  float* amax_val = nullptr;
+  int* amax_idx = nullptr;
+  unsigned* amax_cnt = nullptr;
+  int* dev_flags = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  int max_pos = 0;
+  int smax1 = 1;  // attention splits at batch 1 (largest)
+
+  std::map<GraphKey, hipGraphExec_t> graphs;
+  std::map<GraphKey, hipGraph_t> graph_defs;
+};
+
+namespace {
+
+int fail(qd_handle* h, int code, const std::string& msg) {
+  if (h) h->err = msg; else g_create_error = msg;
+  return code;
+}
+
+int hip_fail(qd_handle* h, hipError_t e, const char* what) {
+  return fail(h, QD_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(h, expr)                                  \
+  do {                                                    \
+    hipError_t e_ = (expr);                               \
+    if (e_ != hipSuccess) return hip_fail((h), e_, #expr); \
+  } while (0)
+
+template <typename T>
+int dev_alloc(qd_handle* h, T** p, size_t count) {
+  void* q = nullptr;
+  size_t bytes = count * sizeof(T);
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) return fail(h, QD_ENOMEM, std::string("hipMalloc failed: ") + hipGetErrorString(e));
+  h->allocs.push_back(q);
+  *p = static_cast<T*>(q);
+  return QD_OK;
+}
+
+// Split plan for an N x K projection at batch B: enough workgroups to cover
+// the chip twice (or every K tile split), at most 20 tiles per wave in flight
+// unless the row count alone fills the chip, and an LDS input slice <= 96 KB.
+GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B) {
+  const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
+  const int target = 2 * h->num_cus;
+  GemvPlan p;
+  for (int S = 1; S <= KT; ++S) {
+    const int kps = (KT + S - 1) / S;
+    const int Se = (KT + kps - 1) / kps;
+    if (kps > 20 && NRG < target) continue;
+    if (gemv_lds_bytes(B, kps) > 96 * 1024) continue;
+    p.S = Se;
+    p.kps = kps;
+    if (NRG * Se >= target) return p;
+  }
+  if (p.S == 1 && p.kps == 1 && KT > 1) { p.S = KT; p.kps = 1; }
+  return p;
+}
+
+int attn_splits(const qd_handle* h, int B) {
+  int s = (2 * h->num_cus + B * h->Hkv - 1) / (B * h->Hkv);
+  const int cap = (h->cfg.max_pages_per_seq + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return s;
+}
+
+int validate_config(const qd_config* c) {
+  if (!c) return fail(nullptr, QD_EINVAL, "config is NULL");
+  if (c->num_layers < 1 || c->hidden < 64 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
+      c->head_dim < 1 || c->intermediate < 32 || c->vocab < 64)
+    return fail(nullptr, QD_EINVAL, "model sizes must be positive");
+  if (c->max_batch < 1 || c->max_batch > kMaxBatch)
+    return fail(nullptr, QD_EINVAL, "max_batch must be in 1..64");
+  if (c->max_pages_per_seq < 1 || c->num_pages < 1)
+    return fail(nullptr, QD_EINVAL, "max_pages_per_seq and num_pages must be >= 1");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0))
+    return fail(nullptr, QD_EINVAL, "rms_eps and rope_theta must be > 0");
+  if (c->page_size != kPage) return fail(nullptr, QD_EUNSUPPORTED, "page_size must be 16");
+  if (c->hidden % 64) return fail(nullptr, QD_EUNSUPPORTED, "hidden must be a multiple of 64");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(nullptr, QD_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->num_q_heads % c->num_kv_heads)
+    return fail(nullptr, QD_EUNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4)
+    return fail(nullptr, QD_EUNSUPPORTED, "query heads per KV head must be 1, 2 or 4");
+  if (c->intermediate % 32) return fail(nullptr, QD_EUNSUPPORTED, "intermediate must be a multiple of 32");
+  if (c->vocab % 64) return fail(nullptr, QD_EUNSUPPORTED, "vocab must be a multiple of 64");
+  if ((long long)c->max_pages_per_seq * kPage > (1LL << 30))
+    return fail(nullptr, QD_EUNSUPPORTED, "max_pages_per_seq too large");
+  return QD_OK;
+}
+
+struct StepPtrs {
+  int B;
+  const int32_t* tokens;
+  const int32_t* positions;
+  const int32_t* tables;
+  uint16_t* pool;
+  int32_t* next;
+  float* logits;
+};
+
+// Optional per-launch event recording (qd_profile_step).
+struct Prof {
+  std::vector<hipEvent_t> ev;  // ev[0] before the first launch, ev[i+1] after launch i
+  std::vector<int> cls;        // class of launch i
+};
+
+int prof_mark(qd_handle* h, Prof* pr, int cls, hipStream_t s) {
+  if (!pr) return QD_OK;
+  hipEvent_t e = nullptr;
+  HIP_TRY(h, hipEventCreate(&e));
+  pr->ev.push_back(e);
+  pr->cls.push_back(cls);
+  HIP_TRY(h, hipEventRecord(e, s));
+  return QD_OK;
+}
+
+// Enqueue one step on stream s.
+int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream_t s,
+                Prof* pr = nullptr) {
+  int prc = QD_OK;
+  if (pr && (prc = prof_mark(h, pr, -1, s))) return prc;
+#define PROF(c)                                              \
+  do {                                                       \
+    if (pr && (prc = prof_mark(h, pr, (c), s))) return prc;  \
+  } while (0)
+  const int B = sp.B, L = h->L, H = h->H;
+  const float eps = h->cfg.rms_eps;
+  const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+
+  EmbedArgs ea{};
+  ea.table = h->embed;
+  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch;
+  ea.tokens = sp.tokens; ea.x = h->x; ea.ssq_out = h->ssq; ea.dev_flags = h->dev_flags;
+  HIP_TRY(h, launch_embed(ea, s));
+  PROF(QD_PROF_EMBED);
+
+  auto gemv = [&](const uint16_t* w, int N, int K, const float* xin, const float* gain,
+                  int mode, float* out) -> hipError_t {
+    GemvPlan p = plan_gemv(h, N, K, B);
+    GemvArgs a{};
+    a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
+    a.S = p.S; a.kps = p.kps;
+    a.x = xin;
+    a.ssq = gain ? h->ssq : nullptr;
+    a.gain = gain; a.eps = eps;
+    a.part = h->part; a.counters = h->gemv_cnt;
+    a.out = out;
+    a.ssq_out = h->ssq;
+    a.logits = sp.logits;
+    a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
+    a.next_ids = sp.next;
+    return launch_gemv(a, mode, s);
+  };
+
+  const int smax = attn_splits(h, B);
+  for (int l = 0; l < L; ++l) {
+    const LayerW& w = h->lw[l];
+    const bool tap = taps && taps->layer == l;
+    if (tap && taps->x_in)
+      HIP_TRY(h, hipMemcpyAsync(taps->x_in, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, gemv(w.qkv, h->NQKV, H, h->x, w.in_norm, kStore, h->qkv));
+    PROF(QD_PROF_QKV);
+    if (tap && taps->qkv)
+      HIP_TRY(h, hipMemcpyAsync(taps->qkv, h->qkv, sizeof(float) * B * h->NQKV,
+                                hipMemcpyDeviceToDevice, s));
+    AttnArgs aa{};
+    aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
+    aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
+    aa.pool_layer = sp.pool + (size_t)l * layer_elems;
+    aa.num_pages = h->cfg.num_pages;
+    aa.positions = sp.positions; aa.block_tables = sp.tables;
+    aa.max_pages = h->cfg.max_pages_per_seq;
+    aa.B = B; aa.Hq = h->Hq; aa.Hkv = h->Hkv;
+    aa.eps = eps; aa.scale = (float)(1.0 / std::sqrt((double)h->D));
+    aa.S_max = smax;
+    aa.o_part = h->o_part; aa.ml_part = h->ml_part; aa.counters = h->attn_cnt;
+    aa.out = h->attn;
+    aa.tap_q = tap ? taps->q_rot : nullptr;
+    aa.tap_k = tap ? taps->k_rot : nullptr;
+    aa.dev_flags = h->dev_flags;
+    HIP_TRY(h, launch_attention(aa, h->D, h->G, s));
+    PROF(QD_PROF_ATTN);
+    if (tap && taps->attn)
+      HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,
+                                hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, gemv(w.o, H, h->QD, h->attn, nullptr, kResid, h->x));
+    PROF(QD_PROF_O);
+    if (tap && taps->x_mid)
+      HIP_TRY(h, hipMemcpyAsync(taps->x_mid, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, gemv(w.gu, 2 * h->I, H, h->x, w.post_norm, kSwiGLU, h->act));
+    PROF(QD_PROF_GATE_UP);
+    if (tap && taps->act)
+      HIP_TRY(h, hipMemcpyAsync(taps->act, h->act, sizeof(float) * B * h->I,
+                                hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, gemv(w.down, H, h->I, h->act, nullptr, kResid, h->x));
+    PROF(QD_PROF_DOWN);
+    if (tap && taps->x_out)
+      HIP_TRY(h, hipMemcpyAsync(taps->x_out, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
+  }
+  if (taps && taps->final_h)
+    HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, h->final_norm, H, B, h->cfg.max_batch, eps,
+                                   taps->final_h, s));
+  HIP_TRY(h, gemv(h->lm, h->V, H, h->x, h->final_norm, kArgmax, nullptr));
+  PROF(QD_PROF_LM_HEAD);
+#undef PROF
+  return QD_OK;
+}
+
+bool all_loaded(const qd_handle* h, std::string* missing) {
+  for (auto& kv : h->expected)
+    if (!kv.second) { *missing = kv.first; return false; }
+  return true;
+}
+
+int check_step_args(qd_handle* h, int32_t batch, const void* a, const void* b, const void* c,
+                    const void* d, const void* e) {
+  if (!h) return QD_EINVAL;
+  if (batch < 1 || batch > h->cfg.max_batch) return fail(h, QD_EINVAL, "batch out of range");
+  if (!a || !b || !c || !d || !e) return fail(h, QD_EINVAL, "NULL step pointer");
+  std::string missing;
+  if (!all_loaded(h, &missing)) return fail(h, QD_ESTATE, "weight not loaded: " + missing);
+  return QD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
+  if (!out) return fail(nullptr, QD_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  qd_handle* h = new qd_handle();
+  h->cfg = *cfg;
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  h->L = cfg->num_layers; h->H = cfg->hidden; h->Hq = cfg->num_q_heads;
+  h->Hkv = cfg->num_kv_heads; h->D = cfg->head_dim; h->I = cfg->intermediate;
+  h->V = cfg->vocab; h->QD = h->Hq * h->D; h->KD = h->Hkv * h->D;
+  h->NQKV = h->QD + 2 * h->KD; h->G = h->Hq / h->Hkv;
+
+  auto bail = [&](int code) {
+    g_create_error = h->err;
+    qd_destroy(h);
+    return code;
+  };
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { hip_fail(h, e, "hipGetDevice"); return bail(QD_EHIP); }
+  e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
+  if (e != hipSuccess) { hip_fail(h, e, "hipDeviceGetAttribute"); return bail(QD_EHIP); }
+  e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
+  if (e != hipSuccess) { hip_fail(h, e, "hipStreamCreate"); return bail(QD_EHIP); }
+
+  const int L = h->L, H = h->H, I = h->I, V = h->V, Bm = cfg->max_batch;
+  // packed weights
+  h->lw.resize(L);
+  for (int l = 0; l < L; ++l) {
+    LayerW& w = h->lw[l];
+    if ((rc = dev_alloc(h, &w.qkv, (size_t)h->NQKV * H))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.o, (size_t)H * h->QD))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.gu, (size_t)2 * I * H))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.down, (size_t)H * I))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.in_norm, H))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.post_norm, H))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.q_norm, h->D))) return bail(rc);
+    if ((rc = dev_alloc(h, &w.k_norm, h->D))) return bail(rc);
+    const std::string p = "model.layers." + std::to_string(l) + ".";
+    for (const char* n : {"input_layernorm", "self_attn.q_proj", "self_attn.k_proj",
+                          "self_attn.v_proj", "self_attn.o_proj", "self_attn.q_norm",
+                          "self_attn.k_norm", "post_attention_layernorm", "mlp.gate_proj",
+                          "mlp.up_proj", "mlp.down_proj"})
+      h->expected[p + n + ".weight"] = 0;
+  }
+  if ((rc = dev_alloc(h, &h->embed, (size_t)V * H))) return bail(rc);
+  if (cfg->tie_embeddings) {
+    h->lm = h->embed;
+  } else {
+    if ((rc = dev_alloc(h, &h->lm, (size_t)V * H))) return bail(rc);
+    h->expected["lm_head.weight"] = 0;
+  }
+  if ((rc = dev_alloc(h, &h->final_norm, H))) return bail(rc);
+  h->expected["model.embed_tokens.weight"] = 0;
+  h->expected["model.norm.weight"] = 0;
+
+  // activations and scratch
+  if ((rc = dev_alloc(h, &h->x, (size_t)Bm * H))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / 64) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->qkv, (size_t)Bm * h->NQKV))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->attn, (size_t)Bm * h->QD))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->act, (size_t)Bm * I))) return bail(rc);
+  size_t part_elems = 1;
+  int max_nrg = 1;
+  for (int B = 1; B <= Bm; ++B) {
+    const int dims[5][2] = {{h->NQKV, H}, {H, h->QD}, {2 * I, H}, {H, I}, {V, H}};
+    for (auto& d : dims) {
+      GemvPlan p = plan_gemv(h, d[0], d[1], B);
+      if (p.S > 1) part_elems = std::max(part_elems, (size_t)d[0] * p.S * B);
+      max_nrg = std::max(max_nrg, d[0] / kRowsPerGroup);
+    }
+  }
+  if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg))) return bail(rc);
+  h->smax1 = attn_splits(h, 1);
+  size_t att_rows = 0;
+  for (int B = 1; B <= Bm; ++B) att_rows = std::max(att_rows, (size_t)B * h->Hq * attn_splits(h, B));
+  if ((rc = dev_alloc(h, &h->o_part, att_rows * h->D))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->ml_part, att_rows * 2))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->attn_cnt, (size_t)Bm * h->Hkv))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_val, (size_t)(V / kRowsPerGroup) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_idx, (size_t)(V / kRowsPerGroup) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_cnt, 1))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->dev_flags, 1))) return bail(rc);
+  e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg);
+  if (e == hipSuccess) e = hipMemset(h->attn_cnt, 0, sizeof(unsigned) * Bm * h->Hkv);
+  if (e == hipSuccess) e = hipMemset(h->amax_cnt, 0, sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemset(h->dev_flags, 0, sizeof(int));
+  if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+
+  // RoPE table: angle p * theta^(-2i/D) in double, cos/sin rounded once to fp32.
+  h->max_pos = cfg->max_pages_per_seq * kPage;
+  const int half = h->D / 2;
+  std::vector<float> cs((size_t)h->max_pos * half), sn((size_t)h->max_pos * half);
+  for (int i = 0; i < half; ++i) {
+    const double inv_freq = std::pow(cfg->rope_theta, -2.0 * i / h->D);
+    for (int p = 0; p < h->max_pos; ++p) {
+      const double a = (double)p * inv_freq;
+      cs[(size_t)p * half + i] = (float)std::cos(a);
+      sn[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  }
+  if ((rc = dev_alloc(h, &h->rope_cos, cs.size()))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->rope_sin, sn.size()))) return bail(rc);
+  e = hipMemcpy(h->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(h->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) { hip_fail(h, e, "hipMemcpy"); return bail(QD_EHIP); }
+  *out = h;
+  return QD_OK;
+}
+
+int qd_load_weights(qd_handle* h, const qd_tensor_desc* t, int32_t n) {
+  if (!h) return QD_EINVAL;
+  if (n < 0 || (n > 0 && !t)) return fail(h, QD_EINVAL, "bad tensor list");
+  const int H = h->H, I = h->I, V = h->V, D = h->D;
+  hipStream_t s = h->stream;
+  for (int i = 0; i < n; ++i) {
+    const qd_tensor_desc& d = t[i];
+    if (!d.name || !d.data) return fail(h, QD_EINVAL, "tensor with NULL name or data");
+    const std::string name = d.name;
+    auto it = h->expected.find(name);
+    if (it == h->expected.end()) return fail(h, QD_EINVAL, "unexpected tensor " + name);
+    if (d.dtype != 0) return fail(h, QD_EINVAL, "tensor " + name + " is not bf16");
+    auto need = [&](int64_t r, int64_t c) {
+      if (c < 0) return d.ndim == 1 && d.shape[0] == r;
+      return d.ndim == 2 && d.shape[0] == r && d.shape[1] == c;
+    };
+    const uint16_t* src = static_cast<const uint16_t*>(d.data);
+    hipError_t e = hipSuccess;
+    bool shape_ok = true;
+    if (name == "model.embed_tokens.weight") {
+      shape_ok = need(V, H);
+      if (shape_ok) e = launch_repack(src, V, H, h->embed, 1, 0, s);
+    } else if (name == "lm_head.weight") {
+      shape_ok = need(V, H);
+      if (shape_ok) e = launch_repack(src, V, H, h->lm, 1, 0, s);
+    } else if (name == "model.norm.weight") {
+      shape_ok = need(H, -1);
+      if (shape_ok) e = launch_bf16_to_f32(src, h->final_norm, H, s);
+    } else {
+      const int l = std::atoi(name.c_str() + std::strlen("model.layers."));
+      LayerW& w = h->lw[l];
+      const std::string leaf = name.substr(name.find('.', std::strlen("model.layers.")) + 1);
+      if (leaf == "input_layernorm.weight") {
+        shape_ok = need(H, -1);
+        if (shape_ok) e = launch_bf16_to_f32(src, w.in_norm, H, s);
+      } else if (leaf == "post_attention_layernorm.weight") {
+        shape_ok = need(H, -1);
+        if (shape_ok) e = launch_bf16_to_f32(src, w.post_norm, H, s);
+      } else if (leaf == "self_attn.q_norm.weight") {
+        shape_ok = need(D, -1);
+        if (shape_ok) e = launch_bf16_to_f32(src, w.q_norm, D, s);
+      } else if (leaf == "self_attn.k_norm.weight") {
+        shape_ok = need(D, -1);
+        if (shape_ok) e = launch_bf16_to_f32(src, w.k_norm, D, s);
+      } else if (leaf == "self_attn.q_proj.weight") {
+        shape_ok = need(h->QD, H);
+        if (shape_ok) e = launch_repack(src, h->QD, H, w.qkv, 1, 0, s);
+      } else if (leaf == "self_attn.k_proj.weight") {
+        shape_ok = need(h->KD, H);
+        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 1, h->QD / kTileRows, s);
+      } else if (leaf == "self_attn.v_proj.weight") {
+        shape_ok = need(h->KD, H);
+        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 1, (h->QD + h->KD) / kTileRows, s);
+      } else if (leaf == "self_attn.o_proj.weight") {
+        shape_ok = need(H, h->QD);
+        if (shape_ok) e = launch_repack(src, H, h->QD, w.o, 1, 0, s);
+      } else if (leaf == "mlp.gate_proj.weight") {
+        shape_ok = need(I, H);
+        if (shape_ok) e = launch_repack(src, I, H, w.gu, 2, 0, s);
+      } else if (leaf == "mlp.up_proj.weight") {
+        shape_ok = need(I, H);
+        if (shape_ok) e = launch_repack(src, I, H, w.gu, 2, 1, s);
+      } else if (leaf == "mlp.down_proj.weight") {
+        shape_ok = need(H, I);
+        if (shape_ok) e = launch_repack(src, H, I, w.down, 1, 0, s);
+      } else {
+        return fail(h, QD_EINVAL, "unexpected tensor " + name);
+      }
+    }
+    if (!shape_ok) return fail(h, QD_EINVAL, "tensor " + name + " has the wrong shape");
+    if (e != hipSuccess) return hip_fail(h, e, "repack launch");
+    it->second = 1;
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
+  // weights changed: captured graphs stay valid (same addresses)
+  return QD_OK;
+}
+
+int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                        const int32_t* positions, const int32_t* block_tables, void* kv_pool,
+                        int32_t* out_next_ids, float* out_logits, const qd_taps* taps) {
+  int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
+  if (rc) return rc;
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+              out_next_ids, out_logits};
+  return record_step(h, sp, taps, h->stream);
+}
+
+int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                   const int32_t* positions, const int32_t* block_tables, void* kv_pool,
+                   int32_t* out_next_ids, float* out_logits) {
+  int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
+  if (rc) return rc;
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+              out_next_ids, out_logits};
+  static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
+  if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);
+
+  GraphKey key{batch, {token_ids, positions, block_tables, kv_pool, out_next_ids, out_logits}};
+  auto it = h->graphs.find(key);
+  if (it == h->graphs.end()) {
+    // First call for this key: run it eagerly (this produces the results),
+    // then capture the same launches on the private stream.
+    if ((rc = record_step(h, sp, nullptr, h->stream))) return rc;
+    HIP_TRY(h, hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+    rc = record_step(h, sp, nullptr, h->cap);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(h->cap, &g);
+    if (rc) { if (g) (void)hipGraphDestroy(g); return rc; }
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
+    hipGraphExec_t ge = nullptr;
+    e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) { (void)hipGraphDestroy(g); return hip_fail(h, e, "hipGraphInstantiate"); }
+    h->graphs[key] = ge;
+    h->graph_defs[key] = g;
+    return QD_OK;
+  }
+  HIP_TRY(h, hipGraphLaunch(it->second, h->stream));
+  return QD_OK;
+}
+
+int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
+                    const int32_t* positions, const int32_t* block_tables, void* kv_pool,
+                    int32_t* out_next_ids, float* out_logits, float* class_ms,
+                    int32_t* class_launches) {
+  int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
+  if (rc) return rc;
+  if (!class_ms || !class_launches) return fail(h, QD_EINVAL, "NULL profile output");
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+              out_next_ids, out_logits};
+  Prof pr;
+  rc = record_step(h, sp, nullptr, h->stream, &pr);
+  hipError_t e = hipStreamSynchronize(h->stream);
+  for (int c = 0; c < QD_PROF_CLASSES; ++c) { class_ms[c] = 0.f; class_launches[c] = 0; }
+  if (rc == QD_OK && e == hipSuccess) {
+    for (size_t i = 1; i < pr.ev.size(); ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, pr.ev[i - 1], pr.ev[i]);
+      if (e != hipSuccess) break;
+      const int c = pr.cls[i];
+      if (c >= 0 && c < QD_PROF_CLASSES) { class_ms[c] += ms; class_launches[c] += 1; }
+    }
+  }
+  for (hipEvent_t ev : pr.ev) (void)hipEventDestroy(ev);
+  if (rc) return rc;
+  if (e != hipSuccess) return hip_fail(h, e, "profile events");
+  return QD_OK;
+}
+
+int qd_device_status(qd_handle* h, int32_t* flags) {
+  if (!h || !flags) return QD_EINVAL;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  int v = 0;
+  HIP_TRY(h, hipMemcpy(&v, h->dev_flags, sizeof(int), hipMemcpyDeviceToHost));
+  HIP_TRY(h, hipMemset(h->dev_flags, 0, sizeof(int)));
+  *flags = v;
+  return QD_OK;
+}
+
+void* qd_stream(const qd_handle* h) { return h ? static_cast<void*>(h->stream) : nullptr; }
+
+void qd_destroy(qd_handle* h) {
+  if (!h) return;
+  if (h->stream || h->cap) {
+    (void)hipStreamSynchronize(h->stream);
+  }
+  for (auto& kv : h->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : h->graph_defs) (void)hipGraphDestroy(kv.second);
+  for (void* p : h->allocs) (void)hipFree(p);
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  delete h;
+}
+
+const char* qd_last_error(const qd_handle* h) {
+  return h ? h->err.c_str() : g_create_error.c_str();
+}
+
+}  // extern "C"

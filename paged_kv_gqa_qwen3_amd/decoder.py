@@ -1,0 +1,87 @@
+"""Convenience wrapper over the C ABI for Python callers: owns a qd handle and
+moves numpy inputs into torch device tensors.  Marshalling only; every step
+of the decode path runs in libqd's kernels.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import binding
+
+
+def _torch():
+    import torch  # imported lazily so that CPU-only tools need not load it
+    return torch
+
+
+def to_device_bf16(a: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns -> torch.bfloat16 device tensor (same bits)."""
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def to_device_i32(a: np.ndarray, device="cuda"):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def pool_to_device(pool: np.ndarray, device="cuda"):
+    """Paged KV pool (uint16 bf16 bits, [L][P][2][Hkv][16][D]) -> device int16 tensor."""
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(pool).view(np.int16)).to(device)
+
+
+def pool_to_host(pool_t) -> np.ndarray:
+    return pool_t.cpu().numpy().view(np.uint16)
+
+
+class Decoder:
+    """A qd handle plus the capacity it was created with."""
+
+    def __init__(self, shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
+                 use_graphs: bool = True, stream: Optional[int] = None):
+        torch = _torch()
+        self.shape = shape
+        self.max_batch = max_batch
+        self.max_pages = max_pages_per_seq
+        self.num_pages = num_pages
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        self.cfg = binding.make_config(shape, max_batch, max_pages_per_seq, num_pages,
+                                       use_graphs)
+        self.handle = binding.qd_create(self.cfg, stream)
+
+    def load_numpy_weights(self, weights: Dict[str, np.ndarray], chunk: int = 24) -> None:
+        """Upload HF-named bf16 numpy weights in groups and hand them to the library."""
+        torch = _torch()
+        names = list(weights)
+        for i in range(0, len(names), chunk):
+            group = {n: to_device_bf16(weights[n]) for n in names[i:i + chunk]}
+            binding.qd_load_weights(self.handle, group)
+            del group
+        torch.cuda.synchronize()
+
+    def step(self, tokens, positions, tables, pool, next_ids, logits=None) -> None:
+        binding.qd_decode_step(self.handle, int(tokens.shape[0]), tokens, positions, tables,
+                               pool, next_ids, logits)
+
+    def step_taps(self, tokens, positions, tables, pool, next_ids, logits, taps, layer):
+        binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,
+                                    tables, pool, next_ids, logits, taps, layer)
+
+    def device_status(self) -> int:
+        return binding.qd_device_status(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            binding.qd_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

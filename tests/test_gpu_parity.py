@@ -1,0 +1,354 @@
+"""GPU parity: libqd's decode step against the CPU oracle, through the C ABI.
+
+* Teacher-forced multi-step runs (both sides receive the oracle's token, each
+  keeps its own pool): logits within 2e-2 of max|logit|, greedy ids equal
+  unless the oracle's top-2 gap is within that tolerance.
+* Stage isolation through the library's taps: every stage of one layer is
+  recomputed by the oracle from the GPU's own input to that stage, so each
+  kernel is checked against its own error bound; the KV append must be
+  bit-exact (placement and rounding) and touch nothing else.
+* Graph replay equals eager launches bitwise; physical page placement does
+  not change any bit; two identical steps give identical bits.
+* Full-size shapes (Qwen3-4B batch 1/8/16, 8K context; Qwen3-8B ragged
+  batch 8) in the launch configuration the benchmark times (captured graph).
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_gqa_qwen3_amd import synth
+from paged_kv_gqa_qwen3_amd.decoder import Decoder, pool_to_device, pool_to_host
+from gpu_util import (bf16_rne_of_f32, check_logits, check_next_ids, gemv_tol, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on a CPU host)")
+    return _t
+
+
+def _i32(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+class StepIO:
+    """Static device buffers for repeated steps (so that graphs replay)."""
+
+    def __init__(self, torch, B, max_pages, V, logits=True):
+        self.torch = torch
+        self.tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.tab = torch.zeros(B, max_pages, dtype=torch.int32, device="cuda")
+        self.nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.logits = torch.zeros(B, V, dtype=torch.float32, device="cuda") if logits else None
+
+    def set(self, tokens, positions, tables):
+        t = self.torch
+        self.tok.copy_(t.from_numpy(np.asarray(tokens, dtype=np.int32)))
+        self.pos.copy_(t.from_numpy(np.asarray(positions, dtype=np.int32)))
+        self.tab.copy_(t.from_numpy(np.asarray(tables, dtype=np.int32)))
+
+    def run(self, dec, pool):
+        dec.step(self.tok, self.pos, self.tab, pool, self.nxt, self.logits)
+
+
+def _appended_mask(batch, pairs):
+    """Pool rows (layer, page, K|V, head, slot) written for (sequence, position) pairs."""
+    m = np.zeros(batch.pool.shape[:5], dtype=bool)
+    for b, p in pairs:
+        m[:, batch.block_tables[b, p // 16], :, :, p % 16] = True
+    return m
+
+
+# ----------------------------------------------------------------------------- tiny workload
+
+def test_tiny_workload_teacher_forced(torch):
+    """Tiny GQA decoder: oracle prefill of 64 random tokens, then 16 greedy
+    decode steps on the GPU (graph replay), teacher-forced by the oracle."""
+    w = synth.WORKLOADS["tiny"]
+    shape = w.shape
+    W = synth.make_weights(shape, w.seed)
+    orc = oracle.Oracle(shape, W)
+    batch = synth.make_paged_batch(shape, [0], w.prefill_prompt + w.steps, w.seed, fill_kv=False)
+    prompt = synth.uniform_int(w.seed, "prompt", shape.vocab, w.prefill_prompt)
+    pool_or = batch.pool
+    _, token = orc.prefill(prompt, batch.block_tables[0], pool_or)
+    pool_start = pool_or.copy()
+    pool = pool_to_device(pool_or)
+    dec = Decoder(shape, 1, batch.max_pages, batch.num_pages)
+    dec.load_numpy_weights(W)
+    io = StepIO(torch, 1, batch.max_pages, shape.vocab)
+    pos = w.prefill_prompt
+    worst = 0.0
+    for step in range(w.steps):
+        say(f"tiny step {step} pos {pos}")
+        io.set([token], [pos], batch.block_tables)
+        io.run(dec, pool)
+        lg_or, nx_or, _ = orc.decode_step(np.array([token], np.int32), np.array([pos], np.int32),
+                                          batch.block_tables, pool_or)
+        torch.cuda.synchronize()
+        worst = max(worst, check_logits(io.logits.cpu().numpy(), lg_or, f"step {step}"))
+        check_next_ids(io.nxt.cpu().numpy(), lg_or, f"step {step}")
+        token = int(nx_or[0])
+        pos += 1
+    assert dec.device_status() == 0
+    say(f"tiny worst logit ratio {worst:.3e}")
+    got = pool_to_host(pool)
+    m = _appended_mask(batch, [(0, q) for q in range(w.prefill_prompt, pos)])
+    np.testing.assert_array_equal(got[~m], pool_start[~m])
+    a, b = oracle.bf16_to_f64(got[m]), oracle.bf16_to_f64(pool_or[m])
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-6)
+    dec.close()
+
+
+# ----------------------------------------------------------------------------- stage isolation
+
+def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits, nxt, mfma):
+    B = batch.tokens.shape[0]
+    H, D, Hq, Hkv = shape.hidden, shape.head_dim, shape.num_q_heads, shape.num_kv_heads
+    QD, KD = shape.q_dim, shape.kv_dim
+    eps = shape.rms_eps
+    pos = batch.positions
+    p = f"model.layers.{layer}."
+    t = {k: v.astype(np.float64) for k, v in taps.items()}
+
+    # RMSNorm + fused QKV projection, from the GPU's residual
+    h = oracle.rmsnorm(t["x_in"], W[p + "input_layernorm.weight"], eps)
+    Wqkv = np.concatenate([W[p + "self_attn.q_proj.weight"], W[p + "self_attn.k_proj.weight"],
+                           W[p + "self_attn.v_proj.weight"]])
+    want = oracle.linear(h, Wqkv)
+    assert np.all(np.abs(t["qkv"] - want) <= gemv_tol(Wqkv, h, mfma)), "qkv"
+
+    # q/k RMSNorm + NeoX RoPE, from the GPU's projections
+    for b in range(B):
+        q = t["qkv"][b, :QD].reshape(Hq, D)
+        k = t["qkv"][b, QD:QD + KD].reshape(Hkv, D)
+        qr = oracle.rope_neox(oracle.rmsnorm(q, W[p + "self_attn.q_norm.weight"], eps), pos[b],
+                              shape.rope_theta)
+        kr = oracle.rope_neox(oracle.rmsnorm(k, W[p + "self_attn.k_norm.weight"], eps), pos[b],
+                              shape.rope_theta)
+        assert np.abs(t["q_rot"][b] - qr).max() <= 2e-5 * max(1.0, np.abs(qr).max()), "q_rot"
+        assert np.abs(t["k_rot"][b] - kr).max() <= 2e-5 * max(1.0, np.abs(kr).max()), "k_rot"
+
+    # KV append: bit-exact rounding and placement
+    for b in range(B):
+        page = batch.block_tables[b, pos[b] // 16]
+        slot = pos[b] % 16
+        np.testing.assert_array_equal(pool_after[layer, page, 0, :, slot],
+                                      bf16_rne_of_f32(taps["k_rot"][b]))
+        v = taps["qkv"][b, QD + KD:].reshape(Hkv, D)
+        np.testing.assert_array_equal(pool_after[layer, page, 1, :, slot], bf16_rne_of_f32(v))
+    m = _appended_mask(batch, list(enumerate(pos)))
+    np.testing.assert_array_equal(pool_after[~m], pool_before[~m])
+
+    # paged GQA attention, from the GPU's rotated q and the pool after the append
+    for b in range(B):
+        o = oracle.attention(t["q_rot"][b], pool_after, layer, batch.block_tables[b],
+                             int(pos[b]) + 1, Hkv)
+        vmax = np.abs(oracle.bf16_to_f64(pool_after[layer][:, 1])).max()
+        vmax = vmax if np.isfinite(vmax) else 10.0
+        assert np.abs(t["attn"][b] - o).max() <= 2e-4 * max(1.0, vmax), f"attn seq {b}"
+
+    # O projection + residual
+    a = t["attn"].reshape(B, QD)
+    Wo = W[p + "self_attn.o_proj.weight"]
+    want = t["x_in"] + oracle.linear(a, Wo)
+    tol = gemv_tol(Wo, a, mfma) + 2.0 ** -22 * np.abs(want)
+    assert np.all(np.abs(t["x_mid"] - want) <= tol), "x_mid"
+
+    # RMSNorm + gate/up projection + SwiGLU
+    h2 = oracle.rmsnorm(t["x_mid"], W[p + "post_attention_layernorm.weight"], eps)
+    Wg, Wu = W[p + "mlp.gate_proj.weight"], W[p + "mlp.up_proj.weight"]
+    g, u = oracle.linear(h2, Wg), oracle.linear(h2, Wu)
+    want = oracle.silu(g) * u
+    tg, tu = gemv_tol(Wg, h2, mfma), gemv_tol(Wu, h2, mfma)
+    tol = 1.1 * np.abs(u) * tg + np.abs(oracle.silu(g)) * tu + tg * tu + 1e-6 * np.abs(want)
+    assert np.all(np.abs(t["act"] - want) <= tol), "act"
+
+    # down projection + residual
+    Wd = W[p + "mlp.down_proj.weight"]
+    want = t["x_mid"] + oracle.linear(t["act"], Wd)
+    tol = gemv_tol(Wd, t["act"], mfma) + 2.0 ** -22 * np.abs(want)
+    assert np.all(np.abs(t["x_out"] - want) <= tol), "x_out"
+
+    if layer == shape.num_layers - 1:
+        hf = oracle.rmsnorm(t["x_out"], W["model.norm.weight"], eps)
+        assert np.abs(t["final_h"] - hf).max() <= 1e-5 * max(1.0, np.abs(hf).max()), "final_h"
+        E = W["model.embed_tokens.weight"] if shape.tie_embeddings else W["lm_head.weight"]
+        want = oracle.linear(t["final_h"], E)
+        assert np.all(np.abs(logits - want) <= gemv_tol(E, t["final_h"], mfma) * 1.01 + 1e-6), \
+            "logits"
+        # the on-device argmax is exact on the GPU's own logits (lowest index on ties)
+        np.testing.assert_array_equal(nxt, np.argmax(logits, axis=1))
+
+
+@pytest.mark.parametrize("B,ctx", [
+    (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
+    (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
+])
+def test_tiny_stages(torch, B, ctx):
+    shape = synth.TINY
+    W = synth.make_weights(shape, 100 + B)
+    batch = synth.make_paged_batch(shape, ctx, 1, 200 + B)
+    mfma = B > 4
+    dec = Decoder(shape, max(B, 1), batch.max_pages, batch.num_pages, use_graphs=False)
+    dec.load_numpy_weights(W)
+    QD, KD = shape.q_dim, shape.kv_dim
+    for layer in (0, shape.num_layers - 1):
+        say(f"stages B={B} ctx={ctx} layer={layer}")
+        pool = pool_to_device(batch.pool)
+        taps = {
+            "x_in": torch.zeros(B, shape.hidden, device="cuda"),
+            "qkv": torch.zeros(B, QD + 2 * KD, device="cuda"),
+            "q_rot": torch.zeros(B, shape.num_q_heads, shape.head_dim, device="cuda"),
+            "k_rot": torch.zeros(B, shape.num_kv_heads, shape.head_dim, device="cuda"),
+            "attn": torch.zeros(B, shape.num_q_heads, shape.head_dim, device="cuda"),
+            "x_mid": torch.zeros(B, shape.hidden, device="cuda"),
+            "act": torch.zeros(B, shape.intermediate, device="cuda"),
+            "x_out": torch.zeros(B, shape.hidden, device="cuda"),
+            "final_h": torch.zeros(B, shape.hidden, device="cuda"),
+        }
+        logits = torch.zeros(B, shape.vocab, device="cuda")
+        nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        dec.step_taps(_i32(torch, batch.tokens), _i32(torch, batch.positions),
+                      _i32(torch, batch.block_tables), pool, nxt, logits, taps, layer)
+        torch.cuda.synchronize()
+        tp = {k: v.cpu().numpy() for k, v in taps.items()}
+        _stage_checks(shape, W, batch, tp, batch.pool, pool_to_host(pool), layer,
+                      logits.cpu().numpy(), nxt.cpu().numpy(), mfma)
+    assert dec.device_status() == 0
+    dec.close()
+
+
+# ----------------------------------------------------------------------------- invariances
+
+def test_graph_replay_matches_eager(torch):
+    shape = synth.TINY
+    W = synth.make_weights(shape, 7)
+    batch = synth.make_paged_batch(shape, [5, 40, 77], 6, 8)
+    dg = Decoder(shape, 4, batch.max_pages, batch.num_pages, use_graphs=True)
+    de = Decoder(shape, 4, batch.max_pages, batch.num_pages, use_graphs=False)
+    dg.load_numpy_weights(W)
+    de.load_numpy_weights(W)
+    pg, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
+    ig = StepIO(torch, 3, batch.max_pages, shape.vocab)
+    ie = StepIO(torch, 3, batch.max_pages, shape.vocab)
+    tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    for step in range(6):
+        say(f"graph vs eager step {step}")
+        ig.set(tokens, positions, batch.block_tables)
+        ie.set(tokens, positions, batch.block_tables)
+        ig.run(dg, pg)
+        ie.run(de, pe)
+        torch.cuda.synchronize()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # unrelated eager work
+        assert torch.equal(ig.logits, ie.logits)
+        assert torch.equal(ig.nxt, ie.nxt)
+        tokens = ie.nxt.cpu().numpy()
+        positions = positions + 1
+    assert torch.equal(pg, pe)
+    dg.close()
+    de.close()
+
+
+def test_page_placement_and_determinism(torch):
+    shape = synth.TINY
+    W = synth.make_weights(shape, 9)
+    a = synth.make_paged_batch(shape, [100, 3, 47, 250, 16], 1, 10)
+    b = synth.shuffled_copy(a, 11)
+    dec = Decoder(shape, 5, a.max_pages, a.num_pages, use_graphs=False)
+    dec.load_numpy_weights(W)
+    outs = []
+    for bt in (a, a, b):
+        pool = pool_to_device(bt.pool)
+        io = StepIO(torch, 5, bt.max_pages, shape.vocab)
+        io.set(bt.tokens, bt.positions, bt.block_tables)
+        io.run(dec, pool)
+        torch.cuda.synchronize()
+        outs.append((io.logits.cpu().numpy(), io.nxt.cpu().numpy(), pool_to_host(pool)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][2], outs[1][2])
+    np.testing.assert_array_equal(outs[0][0], outs[2][0])
+    np.testing.assert_array_equal(outs[0][1], outs[2][1])
+
+
+def test_bad_device_inputs_are_flagged_not_faulting(torch):
+    shape = synth.TINY
+    W = synth.make_weights(shape, 12)
+    batch = synth.make_paged_batch(shape, [10, 20, 30], 1, 13)
+    dec = Decoder(shape, 3, batch.max_pages, batch.num_pages, use_graphs=False)
+    dec.load_numpy_weights(W)
+    from paged_kv_gqa_qwen3_amd import binding
+    cases = [
+        ("token", dict(tokens=[shape.vocab + 5, 1, 2]), binding.QD_DEV_BAD_TOKEN),
+        ("position", dict(positions=[10, batch.max_pages * 16 + 3, 30]),
+         binding.QD_DEV_BAD_POSITION),
+        ("page", dict(page=(2, 0, batch.num_pages + 7)), binding.QD_DEV_BAD_PAGE),
+    ]
+    for name, case, bit in cases:
+        say(f"bad input: {name}")
+        tokens = np.array(case.get("tokens", batch.tokens), np.int32)
+        positions = np.array(case.get("positions", batch.positions), np.int32)
+        tables = batch.block_tables.copy()
+        if "page" in case:
+            r, c, v = case["page"]
+            tables[r, c] = v
+        pool = pool_to_device(batch.pool)
+        io = StepIO(torch, 3, batch.max_pages, shape.vocab)
+        io.set(tokens, positions, tables)
+        io.run(dec, pool)
+        assert dec.device_status() & bit
+    assert dec.device_status() == 0
+
+
+# ----------------------------------------------------------------------------- full size
+
+_WEIGHTS = {}
+
+
+def _weights(shape, seed):
+    key = (shape.name, seed)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        gc.collect()
+        say(f"generating {shape.name} weights (seed {seed})")
+        _WEIGHTS[key] = synth.make_weights(shape, seed)
+    return _WEIGHTS[key]
+
+
+@pytest.mark.parametrize("name", ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256",
+                                  "4b_bs1_ctx8192", "8b_bs8_ragged"])
+def test_full_size_steps(torch, name):
+    w = synth.WORKLOADS[name]
+    shape = w.shape
+    W = _weights(shape, 2 if shape is synth.QWEN3_4B else w.seed)
+    ctx0 = synth.context_lengths(w)
+    batch = synth.make_paged_batch(shape, ctx0, w.steps, w.seed)
+    say(f"{name}: B={w.batch} ctx0={ctx0.tolist()} pages={batch.num_pages}")
+    orc = oracle.Oracle(shape, W)
+    dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True)
+    dec.load_numpy_weights(W)
+    pool = pool_to_device(batch.pool)
+    pool_or = batch.pool
+    io = StepIO(torch, w.batch, batch.max_pages, shape.vocab)
+    tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    for step in range(2):
+        say(f"{name}: step {step}")
+        io.set(tokens, positions, batch.block_tables)
+        io.run(dec, pool)
+        lg_or, nx_or, _ = orc.decode_step(tokens, positions, batch.block_tables, pool_or)
+        torch.cuda.synchronize()
+        r = check_logits(io.logits.cpu().numpy(), lg_or, f"{name} step {step}")
+        ex = check_next_ids(io.nxt.cpu().numpy(), lg_or, f"{name} step {step}")
+        say(f"{name}: step {step} logit ratio {r:.3e}, excused ids {ex}")
+        tokens, positions = nx_or.astype(np.int32), positions + 1
+    assert dec.device_status() == 0
+    dec.close()
+    del pool
+    torch.cuda.empty_cache()

@@ -181,7 +181,9 @@ def main():
 
     for shape_name, group in by_shape.items():
         shape = group[0].shape
-        batches = {w.name: synth.make_paged_batch(shape, synth.context_lengths(w), w.steps,
+        # pages for every position the timed and warmup steps reach
+        span = {w.name: max(w.steps, args.steps + args.warmup) for w in group}
+        batches = {w.name: synth.make_paged_batch(shape, synth.context_lengths(w), span[w.name],
                                                   w.seed)
                    for w in group}
         maxp = max(b.max_pages for b in batches.values())
@@ -190,7 +192,7 @@ def main():
             b = batches[w.name]
             if b.num_pages < npages:
                 batches[w.name] = synth.make_paged_batch(
-                    shape, synth.context_lengths(w), w.steps, w.seed,
+                    shape, synth.context_lengths(w), span[w.name], w.seed,
                     spare_pages=npages - b.num_pages)
             bt = batches[w.name].block_tables
             if bt.shape[1] < maxp:

@@ -42,6 +42,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel_class, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    import hashlib
+
+    path = os.path.join(REPO, "profiles", f"traffic_{workload}.json")
+    src = os.path.join(REPO, "paged_kv_gqa_qwen3_amd", "csrc", "qd_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch", {}).get(kernel_class)
+
+
 def gemv_bytes(shape, cls):
     """Algorithmic bytes one launch of a projection class reads (bf16 weights)."""
     H, I = shape.hidden, shape.intermediate
@@ -159,6 +174,9 @@ def main():
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size "
+                         "kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the decode step "
@@ -169,6 +187,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load_library()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
     names = [n for n in args.workloads.split(",") if n]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
@@ -246,7 +272,9 @@ def main():
                     "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBps"],
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
-                                 "traffic": None},
+                                 "traffic": measured_traffic(dom, w.name),
+                                 "algorithmic_bytes": d["bytes_per_launch"],
+                                 "avg_us": d["avg_us"]},
                     "kernel_classes": per_class,
                 }
                 if not args.no_cpu_baseline:

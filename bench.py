@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--mode", choices=("persistent", "graph"), default="graph",
+                    help="one persistent cooperative kernel per step, or one captured "
+                         "hipGraph of per-stage kernels per step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -231,7 +234,8 @@ def main():
         log(f"[bench] weights ready in {time.perf_counter() - t0:.1f}s")
         from paged_kv_gqa_qwen3_amd.decoder import Decoder
 
-        dec = Decoder(shape, max(w.batch for w in group), maxp, npages, use_graphs=True)
+        dec = Decoder(shape, max(w.batch for w in group), maxp, npages, use_graphs=True,
+                      persistent=(args.mode == "persistent"))
         dec.load_numpy_weights(W)
         for w in group:
             batch = batches[w.name]
@@ -293,7 +297,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 paged K/V)",
         "config": {"workload": "Qwen3-4B-shaped decode, batch 1, context 512, 16-token pages, "
                                "shuffled block table", "name": HEADLINE, "batch": 1,
-                   "context0": 512, "parallelism": "single GPU"},
+                   "context0": 512, "parallelism": "single GPU", "mode": args.mode},
         "achieved_GBps": h["achieved_GBps"], "hbm_frac": h["hbm_frac"],
     }
     out.update(headline_extra)

@@ -51,6 +51,7 @@ extern "C" {
 #define QD_DEV_BAD_TOKEN 1     /* a token id outside [0, vocab) (clamped) */
 #define QD_DEV_BAD_POSITION 2  /* a position outside [0, max_pages_per_seq*16) */
 #define QD_DEV_BAD_PAGE 4      /* a block-table entry outside [0, num_pages) */
+#define QD_DEV_TIMEOUT 8       /* a persistent step gave up waiting (results invalid) */
 
 typedef struct qd_handle qd_handle;
 
@@ -59,7 +60,7 @@ typedef struct qd_config {
   int32_t num_layers;          /* L */
   int32_t hidden;              /* H; multiple of 64 */
   int32_t num_q_heads;         /* Hq */
-  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0 and Hq/Hkv <= 8 */
+  int32_t num_kv_heads;        /* Hkv; Hq / Hkv is 1, 2 or 4 */
   int32_t head_dim;            /* D; 64 or 128 */
   int32_t intermediate;        /* I; multiple of 32 */
   int32_t vocab;               /* V; multiple of 64 */
@@ -71,6 +72,9 @@ typedef struct qd_config {
   int32_t max_pages_per_seq;   /* block-table row length */
   int32_t num_pages;           /* pages in the caller's pool */
   int32_t use_graphs;          /* 1: replay one captured hipGraph per batch size */
+  int32_t persistent;          /* 1: run each step as one persistent cooperative kernel
+                                  (head_dim 128 with 4 query heads per KV head, or
+                                  head_dim 64 with 2); otherwise one kernel per stage */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
@@ -112,9 +116,12 @@ int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
  *                                    reads positions 0..p
  *   out_next_ids int32 [batch]       greedy next token (lowest index on ties)
  *   out_logits   fp32 [batch][vocab] or NULL
- * Sequences in one call must not write the same pool slot.  Asynchronous;
- * with use_graphs the first call for a (batch, pointer set) captures a
- * hipGraph and later calls replay it (new pointers cause a new capture).
+ * Sequences in one call must not write the same pool slot.  Asynchronous.
+ * With persistent, the step is one cooperative kernel whose workgroups walk
+ * the stages in order and wait on device counters (every wait is bounded; a
+ * timeout sets QD_DEV_TIMEOUT).  Otherwise, with use_graphs, the first call
+ * for a (batch, pointer set) captures a hipGraph of the per-stage kernels and
+ * later calls replay it (new pointers cause a new capture).
  * Kernels clamp out-of-range ids, positions and page ids instead of reading
  * out of bounds, and record them for qd_device_status. */
 int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,

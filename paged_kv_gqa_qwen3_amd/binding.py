@@ -25,6 +25,7 @@ QD_ENOMEM = -5
 QD_DEV_BAD_TOKEN = 1
 QD_DEV_BAD_POSITION = 2
 QD_DEV_BAD_PAGE = 4
+QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
             "qd_profile_step", "qd_device_status", "qd_stream", "qd_destroy", "qd_last_error")
@@ -40,7 +41,7 @@ class QdConfig(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
                 ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("use_graphs", ctypes.c_int32)]
+                ("use_graphs", ctypes.c_int32), ("persistent", ctypes.c_int32)]
 
 
 class QdTensorDesc(ctypes.Structure):
@@ -113,11 +114,11 @@ def _check(rc: int, handle) -> None:
 
 
 def make_config(shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
-                use_graphs: bool = True) -> QdConfig:
+                use_graphs: bool = True, persistent: bool = False) -> QdConfig:
     return QdConfig(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
                     shape.head_dim, shape.intermediate, shape.vocab, int(shape.tie_embeddings),
                     shape.rms_eps, shape.rope_theta, 16, max_batch, max_pages_per_seq,
-                    num_pages, int(use_graphs))
+                    num_pages, int(use_graphs), int(persistent))
 
 
 def qd_create(cfg: QdConfig, stream: int = 0) -> int:

@@ -1,0 +1,819 @@
+// Device-side building blocks of the decode step (included by the kernel
+// translation units): helpers, the work-item functions and the wait used by
+// the persistent step kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "qd.h"
+#include "qd_internal.h"
+
+namespace qd {
+
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
+  f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
+  f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// (value, index) maximum with the lowest index winning ties; NaN never wins.
+__device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__device__ __forceinline__ void wave_amax(float& bv, int& bi) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float v = __shfl_xor(bv, m);
+    int i = __shfl_xor(bi, m);
+    amax_merge(bv, bi, v, i);
+  }
+}
+
+__device__ __forceinline__ void set_flag(int* flags, int bit) {
+  if (flags) __hip_atomic_fetch_or(flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Data that crosses workgroups inside one launch (split partials, and in the
+// persistent kernel every activation) is written and read with agent-scope
+// relaxed atomic accesses: coherent across the XCDs' L2s on gfx950 without
+// whole-cache writeback or invalidation.  A producer waits until its stores
+// are acknowledged before it increments a counter, so whoever reads the
+// counter's new value and then loads with agent scope sees the data.  (A
+// plain __threadfence() orders the same way but costs an L2 writeback and
+// invalidate per wave, measured at ~0.2 us of serialised device time per
+// workgroup on MI355X.)
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's stores are performed at agent scope.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Returns true in the workgroup that arrives last at `counter` (which then
+// resets it for the next use).
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected,
+                                            unsigned* s_flag) {
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (prev == expected - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// +1 on a "finished" counter once every store of the workgroup is performed.
+__device__ __forceinline__ void signal_done(unsigned* done) {
+  if (done == nullptr) return;
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reset_counter(unsigned* counter) {
+  st_agent(counter, 0u);
+}
+
+// sum_{s < n} p[s * stride] in increasing s, with the loads issued 8 at a
+// time (unconditional, clamped index) so that they overlap.
+__device__ __forceinline__ float sum_strided(const float* p, int n, size_t stride) {
+  float sum = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ld_agent(p + (size_t)min(s0 + j, n - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < n) sum += v[j];
+  }
+  return sum;
+}
+
+// Output row n, batch column b, of a kPartial GEMV (partials laid out
+// [N/64 * S][64][B]): the sum of its S split partials in split order.
+__device__ __forceinline__ float split_sum(const float* part, int S, int B, int n, int b) {
+  const int rg = n / kRowsPerGroup, r = n % kRowsPerGroup;
+  return sum_strided(part + ((size_t)rg * S * kRowsPerGroup + r) * B + b, S,
+                     (size_t)kRowsPerGroup * B);
+}
+
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// ------------------------------------------------------------------ embedding
+
+// x[b] = E[token_b] (exact bf16 -> fp32), read from the packed table, plus
+// the sums of squares of x over each group of 64 columns (the RMSNorm of the
+// first QKV projection consumes them).
+__device__ inline void embed_item(const EmbedArgs& a, unsigned* done, int b) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int tok = a.tokens[b];
+  if (tok < 0 || tok >= a.V) {
+    if (threadIdx.x == 0) set_flag(a.dev_flags, QD_DEV_BAD_TOKEN);
+    tok = tok < 0 ? 0 : a.V - 1;
+  }
+  const int KT = a.H / kTileCols;
+  const int rt = tok / kTileRows, r = tok % kTileRows;
+  for (int base = wave * 64; base < a.H; base += 256) {
+    const int k = base + lane;
+    const int kt = k / kTileCols, q = (k % kTileCols) / 8, e = k % 8;
+    const uint16_t v = a.table[((size_t)rt * KT + kt) * kTileElems + (q * 16 + r) * 8 + e];
+    const float xv = __uint_as_float((unsigned)v << 16);
+    st_agent(a.x + (size_t)b * a.H + k, xv);
+    const float ss = wave_sum(xv * xv);
+    if (lane == 0) st_agent(a.ssq_out + (size_t)(base / 64) * a.Bmax + b, ss);
+  }
+  signal_done(done);
+}
+
+// ------------------------------------------------------------------ GEMV
+
+// LDS of a GEMV item: s_inv [64] f32 | s_res [64][NB] f32 | flag (16 B) |
+// input slice (fp32 [NB][Ks], or bf16 hi [NB][Ks+8] then lo [NB][Ks+8]).
+__host__ __device__ constexpr size_t gemv_head_bytes(int nb) {
+  return 256 + (size_t)kRowsPerGroup * nb * 4 + 16;
+}
+
+__host__ __device__ inline int gemv_nb(int B) {
+  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+}
+
+inline size_t gemv_lds_bytes_impl(int B, int kps) {
+  const int nb = gemv_nb(B);
+  const size_t ks = (size_t)kps * kTileCols;
+  const size_t slice = nb >= 16 ? (size_t)nb * (ks + 8) * 2 * 2 : (size_t)nb * ks * 4;
+  return gemv_head_bytes(nb) + slice;
+}
+
+// y[b][n] = sum_k W[n][k] h[b][k], h = x or RMSNorm(x), W packed bf16.
+//
+// One item = 4 waves = 64 output rows (one 16-row tile per wave) x one K
+// slice of kps tiles.  Each wave streams its slice of weight tiles with one
+// 16-byte load per lane per 1 KB tile, up to CH tiles in flight, issued
+// before the item waits for its input.  The K slice of the
+// (normalised) input sits in LDS.
+//   NB <= 4 : VALU path, fp32 input, NB batch columns, fp32 FMA.
+//   NB >= 16: MFMA path, NB/16 blocks of 16 batch columns,
+//             v_mfma_f32_16x16x32_bf16 with the weight tile as operand A and
+//             the input as a pair of bf16 (hi = bf16(x), lo = bf16(x - hi)),
+//             two MFMAs per tile: ~16 significant bits of input instead of 8
+//             (bf16 inputs alone move a 36-layer model's logits by ~2% of
+//             their maximum, beyond the step's 2e-2 tolerance).
+// With S > 1 splits of K, each item writes its partial tile and the last of
+// the row group's S items to arrive sums the partials in split order
+// (deterministic) and runs the epilogue.
+template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait>
+__device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const float* gain,
+                                 unsigned* done, int item, unsigned char* smem,
+                                 const Wait& wait) {
+  constexpr bool kMfma = NB >= 16;
+  constexpr int NCB = kMfma ? NB / 16 : 1;
+  float* s_inv = reinterpret_cast<float*>(smem);
+  float* s_res = s_inv + kMaxBatch;
+  unsigned* s_flag = reinterpret_cast<unsigned*>(s_res + kRowsPerGroup * NB);
+  unsigned char* xs_base = smem + gemv_head_bytes(NB);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int B = a.B, S = a.S;
+  const int rg = item / S, s = item - rg * S;
+  const int KT = a.K / kTileCols;
+  const int kt0 = s * a.kps;
+  const int kt1 = min(KT, kt0 + a.kps);
+  const int nk = kt1 - kt0;
+  const int Ks = nk * kTileCols;
+  const int rt = rg * 4 + wave;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(w) + ((size_t)rt * KT + kt0) * 64 + lane;
+
+  // First chunk of weight loads goes out before anything waits.  Every load
+  // is issued unconditionally (tile index clamped to the slice) so that the
+  // loads stay in flight together; only the compute is guarded.
+  u32x4 wbuf[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(i, nk - 1) * 64);
+
+  wait();
+  __syncthreads();  // LDS of the previous item is free
+
+  // RMSNorm scale per batch column from the producer's partial sums of
+  // squares: wave w reduces columns w, w+4, ... over its lanes (fixed order).
+  if (a.ssq != nullptr) {
+    const int ng = a.K / 64;
+    for (int b = wave; b < B; b += 4) {
+      float ss = 0.f;
+      for (int g0 = 0; g0 < ng; g0 += 64) {
+        const int g = g0 + lane;
+        ss += g < ng ? ld_agent(a.ssq + (size_t)g * a.Bmax + b) : 0.f;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) s_inv[b] = rsqrtf(ss / (float)a.K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  // Stage the input slice.
+  const int P = kMfma ? Ks + 8 : Ks;
+  for (int b = 0; b < NB; ++b) {
+    const float* xrow = a.x + (size_t)b * a.K + kt0 * kTileCols;
+    const float* grow = gain + kt0 * kTileCols;
+    for (int k = tid; k < Ks; k += 256) {
+      float v = 0.f;
+      if (b < B) {
+        v = ld_agent(xrow + k);
+        if (a.ssq != nullptr) v = v * s_inv[b] * grow[k];
+      }
+      if constexpr (kMfma) {
+        unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
+        const unsigned short hi = f2bf(v);
+        xs[b * P + k] = hi;
+        xs[NB * P + b * P + k] = f2bf(v - __uint_as_float((unsigned)hi << 16));
+      } else {
+        reinterpret_cast<float*>(xs_base)[b * P + k] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc_v[kMfma ? 1 : NB];
+  f32x4 acc_m[NCB];
+#pragma unroll
+  for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[b] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) acc_m[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < nk; c0 += CH) {
+    const int n = min(CH, nk - c0);
+    if (c0 > 0) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(c0 + i, nk - 1) * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (i < n) {
+        const int t = c0 + i;
+        if constexpr (kMfma) {
+          const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
+          const bf16x8 wa = __builtin_bit_cast(bf16x8, wbuf[i]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const int off = (cb * 16 + (lane & 15)) * P + t * kTileCols + (lane >> 4) * 8;
+            const u32x4 xh = *reinterpret_cast<const u32x4*>(xs + off);
+            const u32x4 xl = *reinterpret_cast<const u32x4*>(xs + NB * P + off);
+            acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                wa, __builtin_bit_cast(bf16x8, xh), acc_m[cb], 0, 0, 0);
+            acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                wa, __builtin_bit_cast(bf16x8, xl), acc_m[cb], 0, 0, 0);
+          }
+        } else {
+          const float* xs =
+              reinterpret_cast<const float*>(xs_base) + t * kTileCols + (lane >> 4) * 8;
+          float wf[8];
+          unpack8(wbuf[i], wf);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + b * P);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + b * P + 4);
+            float acc = acc_v[b];
+            acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc);
+            acc = fmaf(wf[2], x0.z, acc); acc = fmaf(wf[3], x0.w, acc);
+            acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
+            acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
+            acc_v[b] = acc;
+          }
+        }
+      }
+    }
+  }
+
+  // Row results of this item -> s_res[64 rows][NB].
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + cb * 16 + (lane & 15)] = acc_m[cb][r];
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float v = acc_v[b];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) s_res[(wave * 16 + lane) * NB + b] = v;
+    }
+  }
+  __syncthreads();
+
+  const int rows = kRowsPerGroup;
+  if constexpr (MODE == kPartial) {
+    // leave the partial for the consumer, which sums the S splits itself
+    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int r = idx / B, b = idx - r * B;
+      st_agent(mine + idx, s_res[r * NB + b]);
+    }
+    signal_done(done);
+    return;
+  }
+  // residual epilogue: every split fetches the old residual of its rows now,
+  // so the one that finishes the row group need not wait for it
+  constexpr int kXold = (kRowsPerGroup * NB + 255) / 256;
+  float x_old[kXold];
+  if constexpr (MODE == kResid) {
+#pragma unroll
+    for (int j = 0; j < kXold; ++j) {
+      const int idx = tid + j * 256;  // = b * rows + r
+      if (idx < rows * B) x_old[j] = ld_agent(a.out + (size_t)(idx / rows) * a.N +
+                                              (size_t)rg * rows + idx % rows);
+    }
+  }
+  if (S > 1) {
+    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int r = idx / B, b = idx - r * B;
+      st_agent(mine + idx, s_res[r * NB + b]);
+    }
+    if (!arrive_last(&a.counters[rg], (unsigned)S, s_flag)) return;
+    const float* all = a.part + (size_t)rg * S * rows * B;
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const float sum = sum_strided(all + idx, S, (size_t)rows * B);
+      const int r = idx / B, b = idx - r * B;
+      s_res[r * NB + b] = sum;
+    }
+    if (tid == 0) reset_counter(&a.counters[rg]);
+    __syncthreads();
+  }
+
+  const int N = a.N;
+  const size_t row0 = (size_t)rg * rows;
+  if constexpr (MODE == kStore) {
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int b = idx / rows, r = idx - b * rows;
+      st_agent(a.out + (size_t)b * N + row0 + r, s_res[r * NB + b]);
+    }
+    signal_done(done);
+  } else if constexpr (MODE == kResid) {
+#pragma unroll
+    for (int j = 0; j < kXold; ++j) {
+      const int base = wave * 64 + j * 256;  // thread tid handles idx = base + lane
+      if (base < rows * B) {
+        const int b = base / rows, r = lane;
+        const float xv = x_old[j] + s_res[r * NB + b];
+        st_agent(a.out + (size_t)b * N + row0 + r, xv);
+        const float ss = wave_sum(xv * xv);
+        if (lane == 0) st_agent(a.ssq_out + (size_t)rg * a.Bmax + b, ss);
+      }
+    }
+    signal_done(done);
+  } else if constexpr (MODE == kSwiGLU) {
+    // rows of this group: [gate j][up j][gate j+1][up j+1], 16 each
+    const int half = N / 2;
+    for (int idx = tid; idx < 32 * B; idx += 256) {
+      const int b = idx / 32, c = idx - b * 32;
+      const int q2 = c / 16, i = c % 16;
+      const float gv = s_res[(q2 * 32 + i) * NB + b];
+      const float uv = s_res[(q2 * 32 + 16 + i) * NB + b];
+      const float sv = gv / (1.f + expf(-gv));
+      st_agent(a.out + (size_t)b * half + (size_t)rg * 32 + c, sv * uv);
+    }
+    signal_done(done);
+  } else {  // kArgmax
+    if (a.logits != nullptr) {
+      for (int idx = tid; idx < rows * B; idx += 256) {
+        const int b = idx / rows, r = idx - b * rows;
+        a.logits[(size_t)b * N + row0 + r] = s_res[r * NB + b];
+      }
+    }
+    for (int b = wave; b < B; b += 4) {
+      float bv = s_res[lane * NB + b];
+      int bi = (int)row0 + lane;
+      wave_amax(bv, bi);
+      if (lane == 0) {
+        st_agent(a.amax_val + (size_t)rg * a.Bmax + b, bv);
+        st_agent(a.amax_idx + (size_t)rg * a.Bmax + b, bi);
+      }
+    }
+    const int NRG = N / rows;
+    if (!arrive_last(a.amax_counter, (unsigned)NRG, s_flag)) return;
+    for (int b = wave; b < B; b += 4) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int g = lane; g < NRG; g += 64)
+        amax_merge(bv, bi, ld_agent(a.amax_val + (size_t)g * a.Bmax + b),
+                   ld_agent(a.amax_idx + (size_t)g * a.Bmax + b));
+      wave_amax(bv, bi);
+      if (lane == 0) a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
+    }
+    if (tid == 0) reset_counter(a.amax_counter);
+  }
+}
+
+// ------------------------------------------------------------------ attention
+
+template <int D, int G>
+struct AttnSmem {
+  static constexpr int LPT = D / 8;       // lanes per token row in one 1 KB load
+  static constexpr int TPI = 64 / LPT;    // tokens per load
+  static constexpr int NI = kPage / TPI;  // loads per 16-token tile
+  static constexpr int NV = NI * G;       // partial scores per lane per page
+  float part[4][NV][64];
+  float acc[4][G * 8][64];
+  alignas(16) float q[G][D];
+  float p[4][64];
+  float m[4][G], l[4][G];
+  alignas(16) unsigned short k[D];
+  alignas(16) unsigned short v[D];
+  unsigned flag;
+};
+
+// One item per (sequence b, KV head g, split s).  Fuses, for the step's
+// token: RMSNorm of the G query heads and of the KV head over head_dim, NeoX
+// RoPE at the token's position, and the bf16 append of k and v into the pool
+// (by the split that owns the last page); then paged attention of the G
+// query heads over the split's pages (K/V read once for the whole group),
+// online softmax, and the log-sum-exp combine of the splits by the last
+// split to arrive.  The split count is derived on the device from the
+// position, so one launch shape (and one captured graph) serves every context.
+//
+// Within a wave, a 16-token page tile of K (or V) for one head is NI loads of
+// 1 KB: in load i lane l holds token i*TPI + l/LPT, dims (l%LPT)*8 .. +8.
+template <int D, int G, class Wait>
+__device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
+                                      const float* k_gain, uint16_t* pool_layer,
+                                      unsigned* done, int item, unsigned char* smem,
+                                      const Wait& wait) {
+  using SM = AttnSmem<D, G>;
+  constexpr int LPT = SM::LPT, TPI = SM::TPI, NI = SM::NI;
+  constexpr int HALF = D / 2;
+  static_assert(16 * G <= 64, "at most 4 query heads per KV head");
+  SM& sm = *reinterpret_cast<SM*>(smem);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int S_max = a.S_max;
+  const int s = item % S_max;
+  const int bg = item / S_max;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+
+  int pos = a.positions[b];
+  const int pos_lim = min(a.max_pages * kPage, a.max_pos);
+  if (pos < 0 || pos >= pos_lim) {
+    if (tid == 0 && s == 0 && g == 0) set_flag(a.dev_flags, QD_DEV_BAD_POSITION);
+    pos = pos < 0 ? 0 : pos_lim - 1;
+  }
+  const int ctx = pos + 1;
+  const int npages = (ctx + kPage - 1) / kPage;
+  int pps = (npages + S_max - 1) / S_max;
+  if (pps < kMinPagesPerSplit) pps = kMinPagesPerSplit;
+  const int nsplit = (npages + pps - 1) / pps;
+  if (s >= nsplit) return;
+  const int pg0 = s * pps, pg1 = min(npages, pg0 + pps);
+  const int* bt = a.block_tables + (size_t)b * a.max_pages;
+  const int Hq = a.Hq, Hkv = a.Hkv;
+  const float* row = a.qkv + (size_t)b * (Hq + 2 * Hkv) * D;  // unused with qkv_part
+  const size_t head_stride = (size_t)kPage * D;  // one (page, K|V, head) tile
+
+  // The cached K/V pages do not depend on this step's projections: the
+  // wave's first page is loaded before waiting for them.
+  auto page_ptr = [&](int pg, int kv) {
+    int phys = bt[pg];
+    if (phys < 0 || phys >= a.num_pages) {
+      if (lane == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
+      phys = 0;
+    }
+    return reinterpret_cast<const u32x4*>(
+        pool_layer + (((size_t)phys * 2 + kv) * Hkv + g) * head_stride);
+  };
+  u32x4 kr[NI], vr[NI];
+  {
+    const int pg = min(pg0 + wave, pg1 - 1);
+    const u32x4* kp = page_ptr(pg, 0);
+    const u32x4* vp = page_ptr(pg, 1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kr[i] = __builtin_nontemporal_load(kp + i * 64 + lane);
+      vr[i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+    }
+  }
+
+  wait();
+  __syncthreads();  // LDS of the previous item is free
+
+  // --- q/k RMSNorm + RoPE, v to bf16 (wave w takes heads w, w+4, ...)
+  for (int hh = wave; hh < G + 2; hh += 4) {
+    int off;  // first row of this head in the QKV projection
+    const float* gain = nullptr;
+    if (hh < G) {
+      off = (g * G + hh) * D;
+      gain = q_gain;
+    } else if (hh == G) {
+      off = Hq * D + g * D;
+      gain = k_gain;
+    } else {
+      off = (Hq + Hkv) * D + g * D;
+    }
+    const bool act = lane < HALF;
+    float x1 = 0.f, x2 = 0.f;
+    if (act) {
+      if (a.qkv_part != nullptr) {
+        x1 = split_sum(a.qkv_part, a.qkv_S, a.B, off + lane, b);
+        x2 = split_sum(a.qkv_part, a.qkv_S, a.B, off + lane + HALF, b);
+      } else {
+        x1 = ld_agent(row + off + lane);
+        x2 = ld_agent(row + off + lane + HALF);
+      }
+    }
+    if (gain != nullptr) {
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float inv = rsqrtf(ss / (float)D + a.eps);
+      if (act) {
+        const float y1 = x1 * inv * gain[lane], y2 = x2 * inv * gain[lane + HALF];
+        const float c = a.rope_cos[(size_t)pos * HALF + lane];
+        const float sn = a.rope_sin[(size_t)pos * HALF + lane];
+        const float r1 = y1 * c - y2 * sn, r2 = y2 * c + y1 * sn;
+        if (hh < G) {
+          sm.q[hh][lane] = r1 * a.scale;
+          sm.q[hh][lane + HALF] = r2 * a.scale;
+          if (a.tap_q != nullptr && s == 0) {
+            float* tq = a.tap_q + ((size_t)b * Hq + g * G + hh) * D;
+            tq[lane] = r1; tq[lane + HALF] = r2;
+          }
+        } else {
+          sm.k[lane] = f2bf(r1);
+          sm.k[lane + HALF] = f2bf(r2);
+          if (a.tap_k != nullptr && s == 0) {
+            float* tk = a.tap_k + ((size_t)b * Hkv + g) * D;
+            tk[lane] = r1; tk[lane + HALF] = r2;
+          }
+        }
+      }
+    } else if (act) {
+      sm.v[lane] = f2bf(x1);
+      sm.v[lane + HALF] = f2bf(x2);
+    }
+  }
+  __syncthreads();
+
+  // --- append k, v of this step (the split owning the last page does it)
+  if (s == nsplit - 1) {
+    const int page = bt[pos / kPage];
+    if (page < 0 || page >= a.num_pages) {
+      if (tid == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
+    } else {
+      uint16_t* kd = pool_layer + (((size_t)page * 2 + 0) * Hkv + g) * head_stride +
+                     (size_t)(pos % kPage) * D;
+      uint16_t* vd = pool_layer + (((size_t)page * 2 + 1) * Hkv + g) * head_stride +
+                     (size_t)(pos % kPage) * D;
+      for (int i = tid; i < D; i += 256) { kd[i] = sm.k[i]; vd[i] = sm.v[i]; }
+    }
+  }
+
+  // --- paged attention over this split's pages, page pg0+wave, +4, ...
+  const int dch = lane % LPT;
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // softmax state of head (lane % G)
+  const u32x4 kcur = *reinterpret_cast<const u32x4*>(&sm.k[dch * 8]);
+  const u32x4 vcur = *reinterpret_cast<const u32x4*>(&sm.v[dch * 8]);
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  for (int pg = pg0 + wave; pg < pg1; pg += 4) {
+    if (pg != pg0 + wave) {
+      const u32x4* kp = page_ptr(pg, 0);
+      const u32x4* vp = page_ptr(pg, 1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kr[i] = __builtin_nontemporal_load(kp + i * 64 + lane);
+        vr[i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+      }
+    }
+    // partial q.k over this lane's 8 dims, for its NI tokens and G heads
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok = pg * kPage + i * TPI + lane / LPT;
+      if (tok == pos) { kr[i] = kcur; vr[i] = vcur; }
+      if (tok >= ctx) { kr[i] = zero4; vr[i] = zero4; }
+      float kf[8];
+      unpack8(kr[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(&sm.q[h][dch * 8]);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&sm.q[h][dch * 8 + 4]);
+        float p = 0.f;
+        p = fmaf(q0.x, kf[0], p); p = fmaf(q0.y, kf[1], p);
+        p = fmaf(q0.z, kf[2], p); p = fmaf(q0.w, kf[3], p);
+        p = fmaf(q1.x, kf[4], p); p = fmaf(q1.y, kf[5], p);
+        p = fmaf(q1.z, kf[6], p); p = fmaf(q1.w, kf[7], p);
+        sm.part[wave][i * G + h][lane] = p;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane u < 16G owns score (token u/G, head u%G): sum the LPT partials
+    float sc = -INFINITY;
+    if (lane < 16 * G) {
+      const int t = lane / G, h = lane % G;
+      const float* src = &sm.part[wave][(t / TPI) * G + h][(t % TPI) * LPT];
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < LPT; j += 4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + j);
+        sum += v4.x; sum += v4.y; sum += v4.z; sum += v4.w;
+      }
+      if (pg * kPage + t < ctx) sc = sum;
+    }
+    float mx = sc;
+#pragma unroll
+    for (int m = G; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const float m_new = fmaxf(m_run, mx);
+    const float p = (sc == -INFINITY) ? 0.f : expf(sc - m_new);
+    const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
+    float psum = p;
+#pragma unroll
+    for (int m = G; m < 64; m <<= 1) psum += __shfl_xor(psum, m);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    sm.p[wave][lane] = p;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = __shfl(alpha, h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = i * TPI + lane / LPT;
+      float vf[8];
+      unpack8(vr[i], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pv = sm.p[wave][t * G + h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // --- combine the 4 waves (and the TPI token groups inside each wave)
+  if (lane < G) { sm.m[wave][lane] = m_run; sm.l[wave][lane] = l_run; }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.acc[wave][h * 8 + e][lane] = acc[h][e];
+  __syncthreads();
+
+  const size_t qh0 = (size_t)b * Hq + (size_t)g * G;  // first query head row of this group
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    const int dc = d / 8, e = d % 8;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][h]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm.m[w][h];
+      const float sc = (mw == -INFINITY) ? 0.f : expf(mw - M);
+      L += sm.l[w][h] * sc;
+      float ow = 0.f;
+#pragma unroll
+      for (int grp = 0; grp < TPI; ++grp) ow += sm.acc[w][h * 8 + e][grp * LPT + dc];
+      o += ow * sc;
+    }
+    if (nsplit == 1) {
+      st_agent(a.out + (qh0 + h) * D + d, o / L);
+    } else {
+      st_agent(a.o_part + ((qh0 + h) * S_max + s) * D + d, o);
+      if (d == 0) {
+        st_agent(a.ml_part + ((qh0 + h) * S_max + s) * 2 + 0, M);
+        st_agent(a.ml_part + ((qh0 + h) * S_max + s) * 2 + 1, L);
+      }
+    }
+  }
+  if (nsplit == 1) {
+    signal_done(done);
+    return;
+  }
+
+  unsigned* cnt = &a.counters[(size_t)b * Hkv + g];
+  if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    const float* ml = a.ml_part + (qh0 + h) * S_max * 2;
+    const float* op = a.o_part + (qh0 + h) * S_max * D + d;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float mv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mv[j] = ld_agent(ml + min(s0 + j, nsplit - 1) * 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);
+    }
+    float L = 0.f, o = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float mv[8], lv[8], ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s2 = min(s0 + j, nsplit - 1);
+        mv[j] = ld_agent(ml + s2 * 2);
+        lv[j] = ld_agent(ml + s2 * 2 + 1);
+        ov[j] = ld_agent(op + (size_t)s2 * D);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (s0 + j < nsplit) {
+          const float sc = expf(mv[j] - M);
+          L += lv[j] * sc;
+          o += ov[j] * sc;
+        }
+      }
+    }
+    st_agent(a.out + (qh0 + h) * D + d, o / L);
+  }
+  if (tid == 0) reset_counter(cnt);
+  signal_done(done);
+}
+
+// ------------------------------------------------------------------ persistent step
+
+// Waits (thread 0 polls, the workgroup then proceeds together) until *c >=
+// target.  Bounded: after `limit` polls it records QD_DEV_TIMEOUT and sets
+// the abort flag, after which every later wait falls through, so every
+// workgroup always reaches the end of the kernel.
+struct Waiter {
+  const unsigned* c;
+  unsigned target;
+  unsigned* abort_flag;
+  int* dev_flags;
+  unsigned limit;
+  __device__ void operator()() const {
+    if (threadIdx.x == 0) {
+      unsigned n = 0;
+      while (ld_agent(c) < target) {
+        if ((n & 63) == 0 && ld_agent(abort_flag) != 0u) break;
+        if (++n > limit) {
+          set_flag(dev_flags, QD_DEV_TIMEOUT);
+          st_agent(abort_flag, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
+};
+
+}  // namespace qd

@@ -20,6 +20,7 @@ constexpr int kTileElems = kTileRows * kTileCols;  // 512 bf16 = 1 KB
 constexpr int kRowsPerGroup = 64;                  // rows one GEMV workgroup finishes
 constexpr int kPage = 16;                          // tokens per KV page
 constexpr int kMaxBatch = 64;
+constexpr int kMaxTilesInFlight = 20;              // weight tiles a wave keeps in flight
 
 // Epilogues of the GEMV kernel.
 enum GemvMode : int {
@@ -27,6 +28,7 @@ enum GemvMode : int {
   kResid = 1,   // x[b][n] += y, and partial sums of squares of the new x
   kSwiGLU = 2,  // act[b][i] = silu(gate_i) * up_i  (row tiles paired gate|up)
   kArgmax = 3,  // optional logits, then argmax over all rows per batch column
+  kPartial = 4, // no reduction: every item leaves its K-split partial for the consumer
 };
 
 struct GemvArgs {
@@ -37,8 +39,8 @@ struct GemvArgs {
   const float* ssq;    // if non-null: RMSNorm the input; [K/64][Bmax] partial sums of squares
   const float* gain;   // [K] RMSNorm gain
   float eps;
-  float* part;         // split-K partials [N/64 * S][64][B]
-  unsigned* counters;  // [N/64] split-K arrival counters (zero between launches)
+  float* part;         // split-K partials [N/64 * S][64][B] (kPartial: the consumer's input)
+  unsigned* counters;  // [N/64] split-K arrival counters (zero between uses)
   float* out;          // kStore: [B][N]; kResid: x [B][N]; kSwiGLU: [B][N/2]
   float* ssq_out;      // kResid: [N/64][Bmax]
   float* logits;       // kArgmax: [B][N] or null
@@ -46,10 +48,13 @@ struct GemvArgs {
   int* amax_idx;       // kArgmax: [N/64][Bmax]
   unsigned* amax_counter;
   int* next_ids;       // kArgmax: [B]
+  unsigned* done;      // if non-null: +1 per row group whose output is final
 };
 
 struct AttnArgs {
-  const float* qkv;        // [B][(Hq+2Hkv)D]
+  const float* qkv;        // [B][(Hq+2Hkv)D], or null when read from qkv_part
+  const float* qkv_part;   // if non-null: the QKV projection's qkv_S split partials
+  int qkv_S;
   const float* q_gain;     // [D]
   const float* k_gain;     // [D]
   const float* rope_cos;   // [max_pos][D/2]
@@ -65,11 +70,12 @@ struct AttnArgs {
   int S_max;               // splits per (sequence, KV head) the grid provides
   float* o_part;           // [B*Hq][S_max][D]
   float* ml_part;          // [B*Hq][S_max][2]  (running max, running sum)
-  unsigned* counters;      // [B*Hkv] split arrival counters (zero between launches)
+  unsigned* counters;      // [B*Hkv] split arrival counters (zero between uses)
   float* out;              // [B][Hq][D]
   float* tap_q;            // optional [B][Hq][D] (after norm and RoPE, unscaled)
   float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
   int* dev_flags;
+  unsigned* done;          // if non-null: +1 per (sequence, KV head) whose output is final
 };
 
 struct EmbedArgs {
@@ -79,6 +85,35 @@ struct EmbedArgs {
   float* x;                // [B][H]
   float* ssq_out;          // [H/64][Bmax]
   int* dev_flags;
+  unsigned* done;          // if non-null: +1 per sequence
+};
+
+// Per-layer pointers for the persistent step kernel (device-resident array).
+struct LayerDev {
+  const uint16_t *qkv, *o, *gu, *down;
+  const float *in_norm, *post_norm, *q_norm, *k_norm;
+};
+
+// Dependency counters of one persistent step, all zero at launch.
+constexpr int kCntEmbed = 0;
+constexpr int kCntPerLayer = 5;  // qkv, attention, o, gate_up, down finalised
+constexpr int cnt_index(int layer, int phase) { return 1 + layer * kCntPerLayer + phase; }
+
+struct StepArgs {
+  // templates: per-layer fields (weights, gains, pool slice, done counters)
+  // are filled in on the device for each layer
+  EmbedArgs embed;
+  GemvArgs qkv, o, gu, down, lm;
+  AttnArgs attn;
+  const LayerDev* layers;
+  int L;
+  size_t pool_layer_elems;   // elements of one layer's slice of the pool
+  unsigned* cnt;             // [1 + L*kCntPerLayer] dependency counters
+  unsigned* exit_cnt;        // workgroups that finished the step
+  unsigned* abort_flag;      // set when a wait times out; later waits fall through
+  int* dev_flags;
+  unsigned spin_limit;       // polls before a wait gives up
+  unsigned long long* trace; // builds with QD_STEP_TRACE only: per-item timestamps
 };
 
 // Minimum pages a split of a sequence covers (one per wave of a workgroup).
@@ -93,6 +128,15 @@ hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
                                int B, int Bmax, float eps, float* out, hipStream_t s);
+
+// Persistent step: which (head_dim, group) shapes it is built for, the LDS
+// bytes it needs, the largest co-resident grid, and the cooperative launch.
+bool step_supported(int head_dim, int group);
+size_t step_lds_bytes(int B, int head_dim, int group, int max_kps);
+hipError_t step_max_grid(int B, int head_dim, int group, size_t lds, int num_cus,
+                         int* grid);
+hipError_t launch_step(const StepArgs& a, int head_dim, int group, int grid, size_t lds,
+                       hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for its input slice.
 size_t gemv_lds_bytes(int B, int kps);

@@ -10,6 +10,7 @@
 // grid fixed the split count).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -64,7 +65,8 @@ struct qd_handle {
   std::map<std::string, int> expected;  // name -> loaded (0/1)
 
   float *x = nullptr, *ssq = nullptr, *qkv = nullptr, *attn = nullptr, *act = nullptr;
-  float* part = nullptr;
+  float* part = nullptr;      // split partials of self-reducing projections (O, down, LM head)
+  float* part_qkv = nullptr;  // split partials of QKV, summed by attention
   unsigned* gemv_cnt = nullptr;
   float *o_part = nullptr, *ml_part = nullptr;
   unsigned* attn_cnt = nullptr;
@@ -78,6 +80,14 @@ struct qd_handle {
 
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::map<GraphKey, hipGraph_t> graph_defs;
+
+  // persistent step
+  bool persistent = false;
+  LayerDev* layers_dev = nullptr;
+  unsigned* step_cnt = nullptr;
+  unsigned* step_exit = nullptr;
+  unsigned* step_abort = nullptr;
+  std::map<int, std::pair<int, size_t>> step_shape;  // batch -> (grid, LDS bytes)
 };
 
 namespace {
@@ -112,15 +122,35 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
 // Split plan for an N x K projection at batch B: enough workgroups to cover
 // the chip twice (or every K tile split), at most 20 tiles per wave in flight
 // unless the row count alone fills the chip, and an LDS input slice <= 96 KB.
+// The persistent step keeps two workgroups per CU, so its GEMV items get a
+// smaller LDS budget.
+constexpr size_t kLdsCapStaged = 96 * 1024;
+constexpr size_t kLdsCapPersistent = 72 * 1024;
+
 GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
   const int target = 2 * h->num_cus;
+  const size_t cap = h->persistent ? kLdsCapPersistent : kLdsCapStaged;
   GemvPlan p;
+  if (h->persistent) {
+    // at most one item per workgroup of the persistent grid (the items of a
+    // stage run concurrently; a wave streams a long K slice in chunks),
+    // more splits only where the input slice would not fit in LDS
+    int S = std::max(1, std::min(KT, target / std::max(1, NRG)));
+    for (;; ++S) {
+      const int kps = (KT + S - 1) / S;
+      if (gemv_lds_bytes(B, kps) <= cap || kps == 1) {
+        p.kps = kps;
+        p.S = (KT + kps - 1) / kps;
+        return p;
+      }
+    }
+  }
   for (int S = 1; S <= KT; ++S) {
     const int kps = (KT + S - 1) / S;
     const int Se = (KT + kps - 1) / kps;
     if (kps > 20 && NRG < target) continue;
-    if (gemv_lds_bytes(B, kps) > 96 * 1024) continue;
+    if (gemv_lds_bytes(B, kps) > cap) continue;
     p.S = Se;
     p.kps = kps;
     if (NRG * Se >= target) return p;
@@ -234,13 +264,27 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     const bool tap = taps && taps->layer == l;
     if (tap && taps->x_in)
       HIP_TRY(h, hipMemcpyAsync(taps->x_in, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, gemv(w.qkv, h->NQKV, H, h->x, w.in_norm, kStore, h->qkv));
+    // Without taps, QKV leaves split partials that attention sums when it
+    // reads q, k, v (same order as the finalising mode, so the bits agree);
+    // with taps the projection is materialised for checking.
+    const bool part_mode = taps == nullptr;
+    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B);
+    if (part_mode) {
+      GemvArgs q{};
+      q.w = w.qkv; q.N = h->NQKV; q.K = H; q.B = B; q.Bmax = h->cfg.max_batch;
+      q.S = pq.S; q.kps = pq.kps; q.x = h->x; q.ssq = h->ssq; q.gain = w.in_norm;
+      q.eps = eps; q.part = h->part_qkv;
+      HIP_TRY(h, launch_gemv(q, kPartial, s));
+    } else {
+      HIP_TRY(h, gemv(w.qkv, h->NQKV, H, h->x, w.in_norm, kStore, h->qkv));
+    }
     PROF(QD_PROF_QKV);
     if (tap && taps->qkv)
       HIP_TRY(h, hipMemcpyAsync(taps->qkv, h->qkv, sizeof(float) * B * h->NQKV,
                                 hipMemcpyDeviceToDevice, s));
     AttnArgs aa{};
     aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
+    if (part_mode) { aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; }
     aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
     aa.pool_layer = sp.pool + (size_t)l * layer_elems;
     aa.num_pages = h->cfg.num_pages;
@@ -279,6 +323,104 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   HIP_TRY(h, gemv(h->lm, h->V, H, h->x, h->final_norm, kArgmax, nullptr));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
+  return QD_OK;
+}
+
+GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const float* xin,
+                       bool norm, float* out) {
+  GemvPlan p = plan_gemv(h, N, K, sp.B);
+  GemvArgs a{};
+  a.N = N; a.K = K; a.B = sp.B; a.Bmax = h->cfg.max_batch;
+  a.S = p.S; a.kps = p.kps;
+  a.x = xin;
+  a.ssq = norm ? h->ssq : nullptr;
+  a.eps = h->cfg.rms_eps;
+  a.part = h->part; a.counters = h->gemv_cnt;
+  a.out = out;
+  a.ssq_out = h->ssq;
+  a.logits = sp.logits;
+  a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
+  a.next_ids = sp.next;
+  return a;
+}
+
+// One step as one persistent cooperative kernel.
+int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
+  const int B = sp.B, H = h->H;
+  StepArgs a{};
+  a.embed.table = h->embed;
+  a.embed.V = h->V; a.embed.H = H; a.embed.B = B; a.embed.Bmax = h->cfg.max_batch;
+  a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
+  a.embed.dev_flags = h->dev_flags;
+  a.qkv = gemv_template(h, sp, h->NQKV, H, h->x, true, h->qkv);
+  a.o = gemv_template(h, sp, H, h->QD, h->attn, false, h->x);
+  a.gu = gemv_template(h, sp, 2 * h->I, H, h->x, true, h->act);
+  a.down = gemv_template(h, sp, H, h->I, h->act, false, h->x);
+  a.lm = gemv_template(h, sp, h->V, H, h->x, true, nullptr);
+  a.lm.w = h->lm;
+  a.lm.gain = h->final_norm;
+  a.qkv.part = h->part_qkv;
+  AttnArgs& at = a.attn;
+  at.qkv = h->qkv;
+  at.qkv_part = h->part_qkv;
+  at.qkv_S = a.qkv.S;
+  at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
+  at.pool_layer = sp.pool;
+  at.num_pages = h->cfg.num_pages;
+  at.positions = sp.positions; at.block_tables = sp.tables;
+  at.max_pages = h->cfg.max_pages_per_seq;
+  at.B = B; at.Hq = h->Hq; at.Hkv = h->Hkv;
+  at.eps = h->cfg.rms_eps; at.scale = (float)(1.0 / std::sqrt((double)h->D));
+  at.S_max = attn_splits(h, B);
+  at.o_part = h->o_part; at.ml_part = h->ml_part; at.counters = h->attn_cnt;
+  at.out = h->attn;
+  at.dev_flags = h->dev_flags;
+  a.layers = h->layers_dev;
+  a.L = h->L;
+  a.pool_layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+  a.cnt = h->step_cnt; a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
+  a.dev_flags = h->dev_flags;
+  a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
+
+  auto it = h->step_shape.find(B);
+  if (it == h->step_shape.end()) {
+    int max_kps = 1;
+    for (const GemvArgs* g : {&a.qkv, &a.o, &a.gu, &a.down, &a.lm})
+      max_kps = std::max(max_kps, g->kps);
+    const size_t lds = step_lds_bytes(B, h->D, h->G, max_kps);
+    int grid = 0;
+    HIP_TRY(h, step_max_grid(B, h->D, h->G, lds, h->num_cus, &grid));
+    if (grid < 1) return fail(h, QD_EUNSUPPORTED, "persistent step does not fit on a CU");
+    const int occupancy_grid = grid;
+    grid = std::min(grid, 2 * h->num_cus);
+    if (const char* g = std::getenv("QD_STEP_GRID")) grid = std::max(1, std::atoi(g));
+    if (std::getenv("QD_DEBUG"))
+      std::fprintf(stderr, "[qd] persistent step B=%d: LDS %zu B, occupancy grid %d, grid %d\n",
+                   B, lds, occupancy_grid, grid);
+    it = h->step_shape.emplace(B, std::make_pair(grid, lds)).first;
+  }
+#ifdef QD_STEP_TRACE
+  static unsigned long long* trace = nullptr;
+  const size_t trace_n = (size_t)it->second.first * 1024 * 3;
+  if (!trace) {
+    HIP_TRY(h, hipMalloc(&trace, trace_n * 8));
+  }
+  HIP_TRY(h, hipMemsetAsync(trace, 0xff, trace_n * 8, s));
+  a.trace = trace;
+#endif
+  HIP_TRY(h, launch_step(a, h->D, h->G, it->second.first, it->second.second, s));
+#ifdef QD_STEP_TRACE
+  if (const char* path = std::getenv("QD_TRACE_OUT")) {
+    HIP_TRY(h, hipStreamSynchronize(s));
+    std::vector<unsigned long long> hostbuf(trace_n);
+    HIP_TRY(h, hipMemcpy(hostbuf.data(), trace, trace_n * 8, hipMemcpyDeviceToHost));
+    FILE* f = std::fopen(path, "wb");
+    if (f) {
+      std::fwrite(hostbuf.data(), 8, trace_n, f);
+      std::fclose(f);
+    }
+  }
+#endif
   return QD_OK;
 }
 
@@ -358,23 +500,30 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->expected["model.embed_tokens.weight"] = 0;
   h->expected["model.norm.weight"] = 0;
 
+  h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
+
   // activations and scratch
   if ((rc = dev_alloc(h, &h->x, (size_t)Bm * H))) return bail(rc);
   if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / 64) * Bm))) return bail(rc);
   if ((rc = dev_alloc(h, &h->qkv, (size_t)Bm * h->NQKV))) return bail(rc);
   if ((rc = dev_alloc(h, &h->attn, (size_t)Bm * h->QD))) return bail(rc);
   if ((rc = dev_alloc(h, &h->act, (size_t)Bm * I))) return bail(rc);
-  size_t part_elems = 1;
+  size_t part_elems = 1, part_qkv_elems = 1;
   int max_nrg = 1;
   for (int B = 1; B <= Bm; ++B) {
-    const int dims[5][2] = {{h->NQKV, H}, {H, h->QD}, {2 * I, H}, {H, I}, {V, H}};
+    const int dims[3][2] = {{H, h->QD}, {H, I}, {V, H}};
     for (auto& d : dims) {
       GemvPlan p = plan_gemv(h, d[0], d[1], B);
       if (p.S > 1) part_elems = std::max(part_elems, (size_t)d[0] * p.S * B);
       max_nrg = std::max(max_nrg, d[0] / kRowsPerGroup);
     }
+    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B), pg = plan_gemv(h, 2 * I, H, B);
+    part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * pq.S * B);
+    if (pg.S > 1) part_elems = std::max(part_elems, (size_t)2 * I * pg.S * B);
+    max_nrg = std::max(max_nrg, std::max(h->NQKV, 2 * I) / kRowsPerGroup);
   }
   if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg))) return bail(rc);
   h->smax1 = attn_splits(h, 1);
   size_t att_rows = 0;
@@ -391,6 +540,26 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (e == hipSuccess) e = hipMemset(h->amax_cnt, 0, sizeof(unsigned));
   if (e == hipSuccess) e = hipMemset(h->dev_flags, 0, sizeof(int));
   if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+
+  // persistent step state
+  h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
+  if (h->persistent) {
+    if ((rc = dev_alloc(h, &h->layers_dev, (size_t)L))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->step_cnt, (size_t)1 + (size_t)L * kCntPerLayer))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->step_exit, 1))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->step_abort, 1))) return bail(rc);
+    e = hipMemset(h->step_cnt, 0, sizeof(unsigned) * (1 + (size_t)L * kCntPerLayer));
+    if (e == hipSuccess) e = hipMemset(h->step_exit, 0, sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(h->step_abort, 0, sizeof(unsigned));
+    std::vector<LayerDev> ld(L);
+    for (int l = 0; l < L; ++l) {
+      const LayerW& w = h->lw[l];
+      ld[l] = LayerDev{w.qkv, w.o, w.gu, w.down, w.in_norm, w.post_norm, w.q_norm, w.k_norm};
+    }
+    if (e == hipSuccess)
+      e = hipMemcpy(h->layers_dev, ld.data(), sizeof(LayerDev) * L, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { hip_fail(h, e, "persistent state"); return bail(QD_EHIP); }
+  }
 
   // RoPE table: angle p * theta^(-2i/D) in double, cos/sin rounded once to fp32.
   h->max_pos = cfg->max_pages_per_seq * kPage;
@@ -510,6 +679,7 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   if (rc) return rc;
   StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits};
+  if (h->persistent) return run_persistent(h, sp, h->stream);
   static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
   if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);
 

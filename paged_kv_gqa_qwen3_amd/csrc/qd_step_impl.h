@@ -1,0 +1,139 @@
+// The persistent decode-step kernel (one cooperative launch per step).
+// Included once per batch-column count by the qd_step_nb*.hip translation
+// units, which instantiate it, so that the large kernels compile in parallel.
+#pragma once
+
+#include "qd_device.h"
+
+namespace qd {
+
+// Weight tiles a wave keeps in flight inside the persistent kernel.
+constexpr int kPersistentTiles = kMaxTilesInFlight;
+
+__device__ __forceinline__ int gemv_items(const GemvArgs& g) {
+  return (g.N / kRowsPerGroup) * g.S;
+}
+
+// The whole decode step in one cooperative launch.  Items are numbered in
+// step order (embedding, then per layer QKV, attention, O, gate/up, down,
+// then the LM head) and workgroup w takes items w, w + grid, w + 2*grid, ...
+// Each stage waits only on counters of earlier stages, and a workgroup takes
+// its items in step order, so the step always makes progress when every
+// workgroup is resident (the cooperative launch guarantees it).
+template <int NB, int D, int G>
+__global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const long nwg = gridDim.x, wg = blockIdx.x;
+  long base = 0;
+#ifdef QD_STEP_TRACE
+  // (phase, start, end) of every item this workgroup runs, 100 MHz clock
+  int phase = 0, nrec = 0;
+  unsigned long long* tr = a.trace + (size_t)wg * 1024 * 3;
+  auto for_items = [&](int n, auto&& fn) {
+    const long first = base + ((wg - base) % nwg + nwg) % nwg;
+    for (long j = first; j < base + n; j += nwg) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      fn((int)(j - base));
+      const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0 && nrec < 1024) {
+        tr[nrec * 3 + 0] = (unsigned long long)phase;
+        tr[nrec * 3 + 1] = t0;
+        tr[nrec * 3 + 2] = t1;
+      }
+      ++nrec;
+    }
+    base += n;
+    ++phase;
+  };
+#else
+  auto for_items = [&](int n, auto&& fn) {
+    const long first = base + ((wg - base) % nwg + nwg) % nwg;
+    for (long j = first; j < base + n; j += nwg) fn((int)(j - base));
+    base += n;
+  };
+#endif
+  const unsigned rg_h = (unsigned)(a.o.N / kRowsPerGroup);
+  // QKV leaves split partials that attention sums: that stage is complete
+  // when every item is
+  const unsigned n_qkv = (unsigned)gemv_items(a.qkv);
+  const unsigned rg_gu = (unsigned)(a.gu.N / kRowsPerGroup);
+  const unsigned n_heads = (unsigned)(a.attn.B * a.attn.Hkv);
+  auto waiter = [&](const unsigned* c, unsigned target) {
+    return Waiter{c, target, a.abort_flag, a.dev_flags, a.spin_limit};
+  };
+
+  for_items(a.embed.B, [&](int b) {
+    __syncthreads();
+    embed_item(a.embed, a.cnt + kCntEmbed, b);
+  });
+
+  for (int l = 0; l < a.L; ++l) {
+    const LayerDev ly = a.layers[l];
+    unsigned* c = a.cnt + cnt_index(l, 0);
+    const unsigned* x_ready = l == 0 ? a.cnt + kCntEmbed : a.cnt + cnt_index(l - 1, 4);
+    const unsigned x_target = l == 0 ? (unsigned)a.embed.B : rg_h;
+
+    for_items(gemv_items(a.qkv), [&](int it) {
+      gemv_item<NB, kPartial, kPersistentTiles>(a.qkv, ly.qkv, ly.in_norm, c + 0, it, smem,
+                                                waiter(x_ready, x_target));
+    });
+    uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
+    for_items(a.attn.B * a.attn.Hkv * a.attn.S_max, [&](int it) {
+      attention_item<D, G>(a.attn, ly.q_norm, ly.k_norm, pool_l, c + 1, it, smem,
+                           waiter(c + 0, n_qkv));
+    });
+    for_items(gemv_items(a.o), [&](int it) {
+      gemv_item<NB, kResid, kPersistentTiles>(a.o, ly.o, nullptr, c + 2, it, smem, waiter(c + 1, n_heads));
+    });
+    for_items(gemv_items(a.gu), [&](int it) {
+      gemv_item<NB, kSwiGLU, kPersistentTiles>(a.gu, ly.gu, ly.post_norm, c + 3, it, smem,
+                                               waiter(c + 2, rg_h));
+    });
+    for_items(gemv_items(a.down), [&](int it) {
+      gemv_item<NB, kResid, kPersistentTiles>(a.down, ly.down, nullptr, c + 4, it, smem,
+                                              waiter(c + 3, rg_gu));
+    });
+  }
+
+  for_items(gemv_items(a.lm), [&](int it) {
+    gemv_item<NB, kArgmax, kPersistentTiles>(a.lm, a.lm.w, a.lm.gain, nullptr, it, smem,
+                           waiter(a.cnt + cnt_index(a.L - 1, 4), rg_h));
+  });
+
+  // The last workgroup out resets the dependency counters for the next step.
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.exit_cnt, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)nwg - 1) {
+      const int n = 1 + a.L * kCntPerLayer;
+      for (int i = 0; i < n; ++i) st_agent(a.cnt + i, 0u);
+      st_agent(a.abort_flag, 0u);
+      st_agent(a.exit_cnt, 0u);
+    }
+  }
+}
+
+
+template <int NB>
+hipError_t step_dispatch(int head_dim, int group, const StepArgs* a, int grid, size_t lds,
+                         hipStream_t s, int* max_grid, int num_cus) {
+  const void* fn = nullptr;
+  if (head_dim == 128 && group == 4) fn = reinterpret_cast<const void*>(&step_kernel<NB, 128, 4>);
+  if (head_dim == 64 && group == 2) fn = reinterpret_cast<const void*>(&step_kernel<NB, 64, 2>);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  if (max_grid != nullptr) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds);
+    if (e != hipSuccess) return e;
+    *max_grid = per_cu * num_cus;
+    return hipSuccess;
+  }
+  void* args[] = {const_cast<StepArgs*>(a)};
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(256), args, (unsigned)lds, s);
+}
+
+}  // namespace qd

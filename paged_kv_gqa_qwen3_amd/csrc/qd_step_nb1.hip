@@ -1,0 +1,7 @@
+// Persistent step kernel instantiated for 1 batch column(s) per GEMV item.
+#include "qd_step_impl.h"
+
+namespace qd {
+template hipError_t step_dispatch<1>(int, int, const StepArgs*, int, size_t, hipStream_t,
+                                       int*, int);
+}  // namespace qd

@@ -42,7 +42,8 @@ class Decoder:
     """A qd handle plus the capacity it was created with."""
 
     def __init__(self, shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
-                 use_graphs: bool = True, stream: Optional[int] = None):
+                 use_graphs: bool = True, stream: Optional[int] = None,
+                 persistent: bool = False):
         torch = _torch()
         self.shape = shape
         self.max_batch = max_batch
@@ -51,7 +52,7 @@ class Decoder:
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
         self.cfg = binding.make_config(shape, max_batch, max_pages_per_seq, num_pages,
-                                       use_graphs)
+                                       use_graphs, persistent)
         self.handle = binding.qd_create(self.cfg, stream)
 
     def load_numpy_weights(self, weights: Dict[str, np.ndarray], chunk: int = 24) -> None:

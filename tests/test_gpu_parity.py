@@ -68,9 +68,11 @@ def _appended_mask(batch, pairs):
 
 # ----------------------------------------------------------------------------- tiny workload
 
-def test_tiny_workload_teacher_forced(torch):
+@pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
+def test_tiny_workload_teacher_forced(torch, persistent):
     """Tiny GQA decoder: oracle prefill of 64 random tokens, then 16 greedy
-    decode steps on the GPU (graph replay), teacher-forced by the oracle."""
+    decode steps on the GPU (graph replay or persistent kernel), teacher-forced
+    by the oracle."""
     w = synth.WORKLOADS["tiny"]
     shape = w.shape
     W = synth.make_weights(shape, w.seed)
@@ -81,7 +83,7 @@ def test_tiny_workload_teacher_forced(torch):
     _, token = orc.prefill(prompt, batch.block_tables[0], pool_or)
     pool_start = pool_or.copy()
     pool = pool_to_device(pool_or)
-    dec = Decoder(shape, 1, batch.max_pages, batch.num_pages)
+    dec = Decoder(shape, 1, batch.max_pages, batch.num_pages, persistent=persistent)
     dec.load_numpy_weights(W)
     io = StepIO(torch, 1, batch.max_pages, shape.vocab)
     pos = w.prefill_prompt
@@ -257,6 +259,39 @@ def test_graph_replay_matches_eager(torch):
     de.close()
 
 
+@pytest.mark.parametrize("B,ctx", [(1, [40]), (3, [5, 40, 77]), (4, [0, 16, 250, 31])])
+def test_persistent_matches_staged_bitwise(torch, B, ctx):
+    """The persistent kernel runs the same items with the same split plans as
+    the per-stage kernels (batch <= 4), so every bit must agree, over chained
+    steps."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 70 + B)
+    batch = synth.make_paged_batch(shape, ctx, 5, 71 + B)
+    dp = Decoder(shape, B, batch.max_pages, batch.num_pages, persistent=True)
+    de = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False)
+    dp.load_numpy_weights(W)
+    de.load_numpy_weights(W)
+    pp, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
+    ip = StepIO(torch, B, batch.max_pages, shape.vocab)
+    ie = StepIO(torch, B, batch.max_pages, shape.vocab)
+    tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    for step in range(5):
+        say(f"persistent vs staged B={B} step {step}")
+        ip.set(tokens, positions, batch.block_tables)
+        ie.set(tokens, positions, batch.block_tables)
+        ip.run(dp, pp)
+        ie.run(de, pe)
+        torch.cuda.synchronize()
+        assert torch.equal(ip.logits, ie.logits)
+        assert torch.equal(ip.nxt, ie.nxt)
+        tokens = ie.nxt.cpu().numpy()
+        positions = positions + 1
+    assert torch.equal(pp, pe)
+    assert dp.device_status() == 0
+    dp.close()
+    de.close()
+
+
 def test_page_placement_and_determinism(torch):
     shape = synth.TINY
     W = synth.make_weights(shape, 9)
@@ -322,17 +357,20 @@ def _weights(shape, seed):
     return _WEIGHTS[key]
 
 
+@pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
 @pytest.mark.parametrize("name", ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256",
                                   "4b_bs1_ctx8192", "8b_bs8_ragged"])
-def test_full_size_steps(torch, name):
+def test_full_size_steps(torch, name, persistent):
     w = synth.WORKLOADS[name]
     shape = w.shape
     W = _weights(shape, 2 if shape is synth.QWEN3_4B else w.seed)
     ctx0 = synth.context_lengths(w)
     batch = synth.make_paged_batch(shape, ctx0, w.steps, w.seed)
-    say(f"{name}: B={w.batch} ctx0={ctx0.tolist()} pages={batch.num_pages}")
+    say(f"{name} persistent={persistent}: B={w.batch} ctx0={ctx0.tolist()} "
+        f"pages={batch.num_pages}")
     orc = oracle.Oracle(shape, W)
-    dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True)
+    dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True,
+                  persistent=persistent)
     dec.load_numpy_weights(W)
     pool = pool_to_device(batch.pool)
     pool_or = batch.pool

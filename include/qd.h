@@ -137,7 +137,9 @@ typedef struct qd_taps {
   float *x_in, *qkv, *q_rot, *k_rot, *attn, *x_mid, *act, *x_out, *final_h;
 } qd_taps;
 
-/* qd_decode_step without graphs, also filling `taps` (may be NULL). */
+/* The step as per-stage kernels launched one by one (no graph, and no
+ * persistent kernel even on a persistent handle, whose split plans it uses),
+ * also filling `taps` (may be NULL). */
 int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
                         const int32_t* positions, const int32_t* block_tables,
                         void* kv_pool, int32_t* out_next_ids, float* out_logits,

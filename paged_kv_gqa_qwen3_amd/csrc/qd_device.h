@@ -110,27 +110,70 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected
   return *s_flag != 0;
 }
 
-// +1 on a "finished" counter once every store of the workgroup is performed.
-__device__ __forceinline__ void signal_done(unsigned* done) {
-  if (done == nullptr) return;
+// Completion of a stage of the persistent step kernel.  Every finished unit
+// of the stage (item, row group, head or sequence) adds 1 to `counter` once
+// its stores are performed; the workgroup whose increment completes the
+// stage raises every workgroup's flag to `phase` (an atomic maximum, so a
+// flag never goes back when two stages finish close together).  Each
+// workgroup polls only its own flag, on a cache line of its own, instead of
+// all of them polling one counter.  counter == nullptr: not in a persistent
+// step, nothing to signal.
+constexpr int kFlagStride = 32;  // unsigned words between two workgroups' flags
+
+struct Done {
+  unsigned* counter;
+  unsigned target;
+  unsigned phase;
+  unsigned* flags;
+  int nflags;
+};
+
+__device__ __forceinline__ void signal_done(const Done& d) {
+  if (d.counter == nullptr) return;
+  __shared__ unsigned s_last;
   stores_done();
   __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(d.counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev + 1 == d.target ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last != 0u)
+    for (int i = threadIdx.x; i < d.nflags; i += blockDim.x)
+      __hip_atomic_fetch_max(d.flags + (size_t)i * kFlagStride, d.phase, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
 }
+
+__device__ __forceinline__ Done no_done() { return Done{nullptr, 0u, 0u, nullptr, 0}; }
 
 __device__ __forceinline__ void reset_counter(unsigned* counter) {
   st_agent(counter, 0u);
 }
 
+// Loads of data written by another workgroup: agent scope when the writer
+// ran in the same launch, plain (cacheable, vectorisable) loads when it was
+// an earlier launch on the stream, whose completion already made it visible.
+template <bool kAgent>
+__device__ __forceinline__ float ld_in(const float* p) {
+  if constexpr (kAgent) return ld_agent(p);
+  else return *p;
+}
+template <bool kAgent>
+__device__ __forceinline__ f32x4 ld_in4(const float* p) {
+  if constexpr (kAgent) return f32x4{ld_agent(p), ld_agent(p + 1), ld_agent(p + 2), ld_agent(p + 3)};
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+
 // sum_{s < n} p[s * stride] in increasing s, with the loads issued 8 at a
 // time (unconditional, clamped index) so that they overlap.
+template <bool kAgent = true>
 __device__ __forceinline__ float sum_strided(const float* p, int n, size_t stride) {
   float sum = 0.f;
   for (int s0 = 0; s0 < n; s0 += 8) {
     float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ld_agent(p + (size_t)min(s0 + j, n - 1) * stride);
+    for (int j = 0; j < 8; ++j) v[j] = ld_in<kAgent>(p + (size_t)min(s0 + j, n - 1) * stride);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (s0 + j < n) sum += v[j];
@@ -138,24 +181,36 @@ __device__ __forceinline__ float sum_strided(const float* p, int n, size_t strid
   return sum;
 }
 
-// Output row n, batch column b, of a kPartial GEMV (partials laid out
-// [N/64 * S][64][B]): the sum of its S split partials in split order.
-__device__ __forceinline__ float split_sum(const float* part, int S, int B, int n, int b) {
-  const int rg = n / kRowsPerGroup, r = n % kRowsPerGroup;
-  return sum_strided(part + ((size_t)rg * S * kRowsPerGroup + r) * B + b, S,
-                     (size_t)kRowsPerGroup * B);
+// Output row n, batch column b, of a kPartial GEMV with `rows` rows per
+// item (partials laid out [N/rows * S][rows][B]): the sum of its S split
+// partials in split order.
+template <bool kAgent>
+__device__ __forceinline__ float split_sum(const float* part, int S, int B, int rows, int n,
+                                           int b) {
+  const int rg = n / rows, r = n % rows;
+  return sum_strided<kAgent>(part + ((size_t)rg * S * rows + r) * B + b, S, (size_t)rows * B);
 }
 
+// Sum of v over aligned groups of n lanes (n a power of two <= 64), in a
+// fixed order; every lane of a group ends with the group's sum.
+__device__ __forceinline__ float group_sum(float v, int n) {
+  for (int m = 1; m < n; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Items of a standalone kernel read their inputs with plain loads (written
+// by an earlier launch); the waits of the persistent kernel set kInLaunch.
 struct NoWait {
+  static constexpr bool kInLaunch = false;
   __device__ void operator()() const {}
 };
 
 // ------------------------------------------------------------------ embedding
 
 // x[b] = E[token_b] (exact bf16 -> fp32), read from the packed table, plus
-// the sums of squares of x over each group of 64 columns (the RMSNorm of the
-// first QKV projection consumes them).
-__device__ inline void embed_item(const EmbedArgs& a, unsigned* done, int b) {
+// the sums of squares of x over each group of ssq_rows columns (the RMSNorm
+// of the first QKV projection consumes them).
+__device__ inline void embed_item(const EmbedArgs& a, const Done& done, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int tok = a.tokens[b];
   if (tok < 0 || tok >= a.V) {
@@ -170,8 +225,8 @@ __device__ inline void embed_item(const EmbedArgs& a, unsigned* done, int b) {
     const uint16_t v = a.table[((size_t)rt * KT + kt) * kTileElems + (q * 16 + r) * 8 + e];
     const float xv = __uint_as_float((unsigned)v << 16);
     st_agent(a.x + (size_t)b * a.H + k, xv);
-    const float ss = wave_sum(xv * xv);
-    if (lane == 0) st_agent(a.ssq_out + (size_t)(base / 64) * a.Bmax + b, ss);
+    const float ss = group_sum(xv * xv, a.ssq_rows);
+    if (k % a.ssq_rows == 0) st_agent(a.ssq_out + (size_t)(k / a.ssq_rows) * a.Bmax + b, ss);
   }
   signal_done(done);
 }
@@ -184,10 +239,6 @@ __host__ __device__ constexpr size_t gemv_head_bytes(int nb) {
   return 256 + (size_t)kRowsPerGroup * nb * 4 + 16;
 }
 
-__host__ __device__ inline int gemv_nb(int B) {
-  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
-}
-
 inline size_t gemv_lds_bytes_impl(int B, int kps) {
   const int nb = gemv_nb(B);
   const size_t ks = (size_t)kps * kTileCols;
@@ -197,11 +248,12 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 
 // y[b][n] = sum_k W[n][k] h[b][k], h = x or RMSNorm(x), W packed bf16.
 //
-// One item = 4 waves = 64 output rows (one 16-row tile per wave) x one K
-// slice of kps tiles.  Each wave streams its slice of weight tiles with one
-// 16-byte load per lane per 1 KB tile, up to CH tiles in flight, issued
-// before the item waits for its input.  The K slice of the
-// (normalised) input sits in LDS.
+// One item = rt row tiles (16 rows each) x one K slice of kps tiles.  Wave w
+// works on row tile w % rt of the item and on every (4/rt)-th k-tile of the
+// slice from w / rt on.  It streams its tiles with one 16-byte load per lane
+// per 1 KB tile and CH tiles in flight: the first CH go out before the item
+// waits for its input, and each later one as soon as the registers it lands
+// in are free.  The K slice of the input (times the RMSNorm gain) sits in LDS.
 //   NB <= 4 : VALU path, fp32 input, NB batch columns, fp32 FMA.
 //   NB >= 16: MFMA path, NB/16 blocks of 16 batch columns,
 //             v_mfma_f32_16x16x32_bf16 with the weight tile as operand A and
@@ -209,14 +261,16 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 //             two MFMAs per tile: ~16 significant bits of input instead of 8
 //             (bf16 inputs alone move a 36-layer model's logits by ~2% of
 //             their maximum, beyond the step's 2e-2 tolerance).
-// With S > 1 splits of K, each item writes its partial tile and the last of
-// the row group's S items to arrive sums the partials in split order
+// Waves that share a row tile add their results in LDS in K order.  With
+// S > 1 splits of K, each item writes its partial rows and the last of the
+// row group's S items to arrive sums the partials in split order
 // (deterministic) and runs the epilogue.
 template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait>
 __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const float* gain,
-                                 unsigned* done, int item, unsigned char* smem,
+                                 const Done& done, int item, unsigned char* smem,
                                  const Wait& wait) {
   constexpr bool kMfma = NB >= 16;
+  constexpr bool kAgent = Wait::kInLaunch;
   constexpr int NCB = kMfma ? NB / 16 : 1;
   float* s_inv = reinterpret_cast<float*>(smem);
   float* s_res = s_inv + kMaxBatch;
@@ -224,61 +278,96 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   unsigned char* xs_base = smem + gemv_head_bytes(NB);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int B = a.B, S = a.S;
+  const int B = a.B, S = a.S, RT = a.rt, WS = 4 / RT;
+  const int rows = RT * kTileRows;
   const int rg = item / S, s = item - rg * S;
   const int KT = a.K / kTileCols;
   const int kt0 = s * a.kps;
   const int kt1 = min(KT, kt0 + a.kps);
   const int nk = kt1 - kt0;
   const int Ks = nk * kTileCols;
-  const int rt = rg * 4 + wave;
-  const u32x4* wp = reinterpret_cast<const u32x4*>(w) + ((size_t)rt * KT + kt0) * 64 + lane;
+  const int tj = wave % RT, kph = wave / RT;  // row tile in the item, K phase
+  const int nkw = kph < nk ? (nk - kph + WS - 1) / WS : 0;  // k-tiles of this wave
+  const int lastw = nkw > 0 ? nkw - 1 : 0;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(w) +
+                    ((size_t)(rg * RT + tj) * KT + kt0 + min(kph, nk - 1)) * 64 + lane;
+  const size_t wstep = (size_t)WS * 64;
 
-  // First chunk of weight loads goes out before anything waits.  Every load
-  // is issued unconditionally (tile index clamped to the slice) so that the
-  // loads stay in flight together; only the compute is guarded.
+  // Every load is issued unconditionally (tile index clamped to the wave's
+  // range) so that the loads stay in flight together; only compute is guarded.
   u32x4 wbuf[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i)
-    wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(i, nk - 1) * 64);
+    wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(i, lastw) * wstep);
 
   wait();
   __syncthreads();  // LDS of the previous item is free
 
-  // RMSNorm scale per batch column from the producer's partial sums of
-  // squares: wave w reduces columns w, w+4, ... over its lanes (fixed order).
-  if (a.ssq != nullptr) {
-    const int ng = a.K / 64;
-    for (int b = wave; b < B; b += 4) {
-      float ss = 0.f;
-      for (int g0 = 0; g0 < ng; g0 += 64) {
-        const int g = g0 + lane;
-        ss += g < ng ? ld_agent(a.ssq + (size_t)g * a.Bmax + b) : 0.f;
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) s_inv[b] = rsqrtf(ss / (float)a.K + a.eps);
+  // RMSNorm: the input is staged as x * gain and each result row is scaled
+  // by 1/rms of its batch column afterwards, so staging does not wait for
+  // the producer's partial sums of squares.  Those are loaded now (wave w
+  // takes columns w, w+4, ...; a lane takes every 64th group) and reduced
+  // after staging.
+  const bool norm = a.ssq != nullptr;
+  constexpr int kSsqCols = (NB + 3) / 4;
+  constexpr int kSsqPer = kMfma ? 2 : 8;  // groups per lane: K/ssq_rows <= 64*kSsqPer
+  float ssv[kSsqCols][kSsqPer];
+  const int ng = a.K / a.ssq_rows;
+  if (norm) {
+#pragma unroll
+    for (int j = 0; j < kSsqCols; ++j) {
+      const int b = min(wave + 4 * j, B - 1);
+#pragma unroll
+      for (int hh = 0; hh < kSsqPer; ++hh)
+        ssv[j][hh] = ld_in<kAgent>(a.ssq + (size_t)min(lane + 64 * hh, ng - 1) * a.Bmax + b);
     }
-    __syncthreads();
   }
 
-  // Stage the input slice.
+  // Stage the input slice, 8 consecutive columns per thread and step.
   const int P = kMfma ? Ks + 8 : Ks;
-  for (int b = 0; b < NB; ++b) {
-    const float* xrow = a.x + (size_t)b * a.K + kt0 * kTileCols;
+  {
+    const int K8 = Ks / 8;
     const float* grow = gain + kt0 * kTileCols;
-    for (int k = tid; k < Ks; k += 256) {
-      float v = 0.f;
-      if (b < B) {
-        v = ld_agent(xrow + k);
-        if (a.ssq != nullptr) v = v * s_inv[b] * grow[k];
+    for (int idx = tid; idx < B * K8; idx += 256) {
+      const int b = idx / K8, c = (idx - b * K8) * 8;
+      const float* xp = a.x + (size_t)b * a.K + kt0 * kTileCols + c;
+      f32x4 v0 = ld_in4<kAgent>(xp), v1 = ld_in4<kAgent>(xp + 4);
+      if (norm) {
+        v0 *= *reinterpret_cast<const f32x4*>(grow + c);
+        v1 *= *reinterpret_cast<const f32x4*>(grow + c + 4);
       }
       if constexpr (kMfma) {
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        unsigned hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = f2bf(v[e]);
+          lo[e] = f2bf(v[e] - __uint_as_float(hi[e] << 16));
+        }
         unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
-        const unsigned short hi = f2bf(v);
-        xs[b * P + k] = hi;
-        xs[NB * P + b * P + k] = f2bf(v - __uint_as_float((unsigned)hi << 16));
+        *reinterpret_cast<u32x4*>(xs + b * P + c) =
+            u32x4{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16,
+                  hi[6] | hi[7] << 16};
+        *reinterpret_cast<u32x4*>(xs + NB * P + b * P + c) =
+            u32x4{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                  lo[6] | lo[7] << 16};
       } else {
-        reinterpret_cast<float*>(xs_base)[b * P + k] = v;
+        float* xs = reinterpret_cast<float*>(xs_base) + b * P + c;
+        *reinterpret_cast<f32x4*>(xs) = v0;
+        *reinterpret_cast<f32x4*>(xs + 4) = v1;
+      }
+    }
+  }
+  if (norm) {
+#pragma unroll
+    for (int j = 0; j < kSsqCols; ++j) {
+      const int b = wave + 4 * j;
+      if (b < B) {
+        float ss = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < kSsqPer; ++hh) ss += lane + 64 * hh < ng ? ssv[j][hh] : 0.f;
+        ss = wave_sum(ss);
+        if (lane == 0) s_inv[b] = rsqrtf(ss / (float)a.K + a.eps);
       }
     }
   }
@@ -291,70 +380,86 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
 #pragma unroll
   for (int c = 0; c < NCB; ++c) acc_m[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < nk; c0 += CH) {
-    const int n = min(CH, nk - c0);
-    if (c0 > 0) {
+  // wave-local tile i is k-tile kph + WS*i of the item's slice
+  auto compute = [&](const u32x4& wv, int i) {
+    const int t = kph + WS * i;
+    if constexpr (kMfma) {
+      const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, wv);
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-        wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(c0 + i, nk - 1) * 64);
-    }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int off = (cb * 16 + (lane & 15)) * P + t * kTileCols + (lane >> 4) * 8;
+        const u32x4 xh = *reinterpret_cast<const u32x4*>(xs + off);
+        const u32x4 xl = *reinterpret_cast<const u32x4*>(xs + NB * P + off);
+        acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wa, __builtin_bit_cast(bf16x8, xh), acc_m[cb], 0, 0, 0);
+        acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wa, __builtin_bit_cast(bf16x8, xl), acc_m[cb], 0, 0, 0);
+      }
+    } else {
+      const float* xs =
+          reinterpret_cast<const float*>(xs_base) + t * kTileCols + (lane >> 4) * 8;
+      float wf[8];
+      unpack8(wv, wf);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < n) {
-        const int t = c0 + i;
-        if constexpr (kMfma) {
-          const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
-          const bf16x8 wa = __builtin_bit_cast(bf16x8, wbuf[i]);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const int off = (cb * 16 + (lane & 15)) * P + t * kTileCols + (lane >> 4) * 8;
-            const u32x4 xh = *reinterpret_cast<const u32x4*>(xs + off);
-            const u32x4 xl = *reinterpret_cast<const u32x4*>(xs + NB * P + off);
-            acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                wa, __builtin_bit_cast(bf16x8, xh), acc_m[cb], 0, 0, 0);
-            acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                wa, __builtin_bit_cast(bf16x8, xl), acc_m[cb], 0, 0, 0);
-          }
-        } else {
-          const float* xs =
-              reinterpret_cast<const float*>(xs_base) + t * kTileCols + (lane >> 4) * 8;
-          float wf[8];
-          unpack8(wbuf[i], wf);
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + b * P);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + b * P + 4);
-            float acc = acc_v[b];
-            acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc);
-            acc = fmaf(wf[2], x0.z, acc); acc = fmaf(wf[3], x0.w, acc);
-            acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
-            acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
-            acc_v[b] = acc;
-          }
-        }
+      for (int b = 0; b < NB; ++b) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + b * P);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + b * P + 4);
+        float acc = acc_v[b];
+        acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc);
+        acc = fmaf(wf[2], x0.z, acc); acc = fmaf(wf[3], x0.w, acc);
+        acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
+        acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
+        acc_v[b] = acc;
       }
     }
+  };
+  // steady state: consume a tile, refill its registers with the tile CH ahead
+  int c0 = 0;
+  for (; c0 + CH < nkw; c0 += CH) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      compute(wbuf[i], c0 + i);
+      wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(c0 + CH + i, lastw) * wstep);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    if (c0 + i < nkw) compute(wbuf[i], c0 + i);
 
-  // Row results of this item -> s_res[64 rows][NB].
+  // Per-wave results (times 1/rms of the batch column under RMSNorm) ->
+  // s_res slot `wave` = [16 rows][NB]; then the waves of a row tile are
+  // added in K order into the slot of its first wave, so that rows 0..rows-1
+  // of s_res hold the item's rows.
   if constexpr (kMfma) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int col = cb * 16 + (lane & 15);
+      const float sc = norm && col < B ? s_inv[col] : 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + cb * 16 + (lane & 15)] = acc_m[cb][r];
+        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = acc_m[cb][r] * sc;
+    }
   } else {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       float v = acc_v[b];
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
+      if (norm && b < B) v *= s_inv[b];
       if (lane < 16) s_res[(wave * 16 + lane) * NB + b] = v;
     }
   }
   __syncthreads();
+  if (WS > 1) {
+    for (int idx = tid; idx < rows * NB; idx += 256) {
+      float v = s_res[idx];
+      for (int k = 1; k < WS; ++k) v += s_res[idx + k * rows * NB];
+      s_res[idx] = v;
+    }
+    __syncthreads();
+  }
 
-  const int rows = kRowsPerGroup;
   if constexpr (MODE == kPartial) {
     // leave the partial for the consumer, which sums the S splits itself
     float* mine = a.part + (size_t)(rg * S + s) * rows * B;
@@ -373,8 +478,8 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
 #pragma unroll
     for (int j = 0; j < kXold; ++j) {
       const int idx = tid + j * 256;  // = b * rows + r
-      if (idx < rows * B) x_old[j] = ld_agent(a.out + (size_t)(idx / rows) * a.N +
-                                              (size_t)rg * rows + idx % rows);
+      if (idx < rows * B) x_old[j] = ld_in<kAgent>(a.out + (size_t)(idx / rows) * a.N +
+                                                     (size_t)rg * rows + idx % rows);
     }
   }
   if (S > 1) {
@@ -403,31 +508,36 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     signal_done(done);
   } else if constexpr (MODE == kResid) {
+    // new residual, and its sums of squares over groups of ssq_rows rows
+    // (ssq_rows divides rows and 64, so a lane group never spans two columns)
+    const int sr = a.ssq_rows;
 #pragma unroll
     for (int j = 0; j < kXold; ++j) {
-      const int base = wave * 64 + j * 256;  // thread tid handles idx = base + lane
-      if (base < rows * B) {
-        const int b = base / rows, r = lane;
-        const float xv = x_old[j] + s_res[r * NB + b];
+      const int idx = tid + j * 256;  // = b * rows + r
+      const bool ok = idx < rows * B;
+      const int b = idx / rows, r = idx - b * rows;
+      float xv = 0.f;
+      if (ok) {
+        xv = x_old[j] + s_res[r * NB + b];
         st_agent(a.out + (size_t)b * N + row0 + r, xv);
-        const float ss = wave_sum(xv * xv);
-        if (lane == 0) st_agent(a.ssq_out + (size_t)rg * a.Bmax + b, ss);
       }
+      const float ss = group_sum(xv * xv, sr);
+      if (ok && r % sr == 0) st_agent(a.ssq_out + ((row0 + r) / sr) * a.Bmax + b, ss);
     }
     signal_done(done);
   } else if constexpr (MODE == kSwiGLU) {
-    // rows of this group: [gate j][up j][gate j+1][up j+1], 16 each
-    const int half = N / 2;
-    for (int idx = tid; idx < 32 * B; idx += 256) {
-      const int b = idx / 32, c = idx - b * 32;
-      const int q2 = c / 16, i = c % 16;
-      const float gv = s_res[(q2 * 32 + i) * NB + b];
-      const float uv = s_res[(q2 * 32 + 16 + i) * NB + b];
+    // row tile j of the item: gate rows 0-7, the matching up rows 8-15
+    const int half = N / 2, nch = RT * 8;
+    for (int idx = tid; idx < nch * B; idx += 256) {
+      const int b = idx / nch, c = idx - b * nch;
+      const int j = c / 8, i = c % 8;
+      const float gv = s_res[(j * 16 + i) * NB + b];
+      const float uv = s_res[(j * 16 + 8 + i) * NB + b];
       const float sv = gv / (1.f + expf(-gv));
-      st_agent(a.out + (size_t)b * half + (size_t)rg * 32 + c, sv * uv);
+      st_agent(a.out + (size_t)b * half + (size_t)rg * nch + c, sv * uv);
     }
     signal_done(done);
-  } else {  // kArgmax
+  } else {  // kArgmax, rows == 64
     if (a.logits != nullptr) {
       for (int idx = tid; idx < rows * B; idx += 256) {
         const int b = idx / rows, r = idx - b * rows;
@@ -435,7 +545,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       }
     }
     for (int b = wave; b < B; b += 4) {
-      float bv = s_res[lane * NB + b];
+      float bv = lane < rows ? s_res[lane * NB + b] : -INFINITY;
       int bi = (int)row0 + lane;
       wave_amax(bv, bi);
       if (lane == 0) {
@@ -445,15 +555,41 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     const int NRG = N / rows;
     if (!arrive_last(a.amax_counter, (unsigned)NRG, s_flag)) return;
-    for (int b = wave; b < B; b += 4) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int g = lane; g < NRG; g += 64)
-        amax_merge(bv, bi, ld_agent(a.amax_val + (size_t)g * a.Bmax + b),
-                   ld_agent(a.amax_idx + (size_t)g * a.Bmax + b));
-      wave_amax(bv, bi);
-      if (lane == 0) a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
+    // tpc threads per batch column, each merging every tpc-th row group's
+    // maximum with 16 loads in flight; the merge is order independent
+    const int Bp = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+    const int tpc = 256 / Bp;
+    const int b = tid / tpc, p = tid - b * tpc;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (b < B) {
+      for (int g0 = p; g0 < NRG; g0 += 16 * tpc) {
+        float v[16];
+        int ix[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int g = min(g0 + j * tpc, NRG - 1);
+          v[j] = ld_agent(a.amax_val + (size_t)g * a.Bmax + b);
+          ix[j] = ld_agent(a.amax_idx + (size_t)g * a.Bmax + b);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax_merge(bv, bi, v[j], ix[j]);
+      }
     }
+    const int wl = tpc < 64 ? tpc : 64;
+    for (int m = 1; m < wl; m <<= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      amax_merge(bv, bi, ov, oi);
+    }
+    if (tpc > 64) {  // a column spans several waves: merge them through LDS
+      int* s_ai = reinterpret_cast<int*>(s_res + 4);
+      if (lane == 0) { s_res[wave] = bv; s_ai[wave] = bi; }
+      __syncthreads();
+      if (p == 0)
+        for (int w2 = 1; w2 < tpc / 64; ++w2) amax_merge(bv, bi, s_res[wave + w2], s_ai[wave + w2]);
+    }
+    if (p == 0 && b < B) a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
     if (tid == 0) reset_counter(a.amax_counter);
   }
 }
@@ -490,9 +626,10 @@ struct AttnSmem {
 template <int D, int G, class Wait>
 __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
                                       const float* k_gain, uint16_t* pool_layer,
-                                      unsigned* done, int item, unsigned char* smem,
+                                      const Done& done, int item, unsigned char* smem,
                                       const Wait& wait) {
   using SM = AttnSmem<D, G>;
+  constexpr bool kAgent = Wait::kInLaunch;
   constexpr int LPT = SM::LPT, TPI = SM::TPI, NI = SM::NI;
   constexpr int HALF = D / 2;
   static_assert(16 * G <= 64, "at most 4 query heads per KV head");
@@ -565,11 +702,11 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     float x1 = 0.f, x2 = 0.f;
     if (act) {
       if (a.qkv_part != nullptr) {
-        x1 = split_sum(a.qkv_part, a.qkv_S, a.B, off + lane, b);
-        x2 = split_sum(a.qkv_part, a.qkv_S, a.B, off + lane + HALF, b);
+        x1 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + lane, b);
+        x2 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + lane + HALF, b);
       } else {
-        x1 = ld_agent(row + off + lane);
-        x2 = ld_agent(row + off + lane + HALF);
+        x1 = ld_in<kAgent>(row + off + lane);
+        x2 = ld_in<kAgent>(row + off + lane + HALF);
       }
     }
     if (gain != nullptr) {
@@ -754,15 +891,9 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     const int h = idx / D, d = idx % D;
     const float* ml = a.ml_part + (qh0 + h) * S_max * 2;
     const float* op = a.o_part + (qh0 + h) * S_max * D + d;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      float mv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mv[j] = ld_agent(ml + min(s0 + j, nsplit - 1) * 2);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);
-    }
-    float L = 0.f, o = 0.f;
+    // one pass over the splits, 8 at a time; sums carried over from earlier
+    // chunks are rescaled to the new running maximum
+    float M = -INFINITY, L = 0.f, o = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += 8) {
       float mv[8], lv[8], ov[8];
 #pragma unroll
@@ -772,14 +903,21 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
         lv[j] = ld_agent(ml + s2 * 2 + 1);
         ov[j] = ld_agent(op + (size_t)s2 * D);
       }
+      float Mc = M;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Mc = fmaxf(Mc, mv[j]);
+      const float r = M == -INFINITY ? 0.f : expf(M - Mc);
+      L *= r;
+      o *= r;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (s0 + j < nsplit) {
-          const float sc = expf(mv[j] - M);
+          const float sc = expf(mv[j] - Mc);
           L += lv[j] * sc;
           o += ov[j] * sc;
         }
       }
+      M = Mc;
     }
     st_agent(a.out + (qh0 + h) * D + d, o / L);
   }
@@ -789,20 +927,22 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
 
 // ------------------------------------------------------------------ persistent step
 
-// Waits (thread 0 polls, the workgroup then proceeds together) until *c >=
-// target.  Bounded: after `limit` polls it records QD_DEV_TIMEOUT and sets
-// the abort flag, after which every later wait falls through, so every
-// workgroup always reaches the end of the kernel.
+// Waits (thread 0 polls, the workgroup then proceeds together) until this
+// workgroup's flag reaches `phase` (see signal_done).  Bounded: after
+// `limit` polls it records QD_DEV_TIMEOUT and sets the abort flag, after
+// which every later wait falls through, so every workgroup always reaches
+// the end of the kernel.
 struct Waiter {
-  const unsigned* c;
-  unsigned target;
+  static constexpr bool kInLaunch = true;
+  const unsigned* flag;
+  unsigned phase;
   unsigned* abort_flag;
   int* dev_flags;
   unsigned limit;
   __device__ void operator()() const {
     if (threadIdx.x == 0) {
       unsigned n = 0;
-      while (ld_agent(c) < target) {
+      while (ld_agent(flag) < phase) {
         if ((n & 63) == 0 && ld_agent(abort_flag) != 0u) break;
         if (++n > limit) {
           set_flag(dev_flags, QD_DEV_TIMEOUT);

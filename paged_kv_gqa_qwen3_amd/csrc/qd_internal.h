@@ -14,6 +14,10 @@ namespace qd {
 // at element offset l * 8: row rt*16 + l%16, columns kt*32 + (l/16)*8 .. +8.
 // One 64-lane 16-byte load therefore reads one whole 1 KB tile, and the lane
 // ownership is exactly the A operand of a 16x16x32 bf16 MFMA.
+// q|k|v are stacked into one matrix; gate and up are interleaved by halves
+// of a row tile: packed row tile t holds gate rows 8t..8t+7 in its rows 0-7
+// and up rows 8t..8t+7 in its rows 8-15, so any row tile yields 8 SwiGLU
+// channels by itself.
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 32;
 constexpr int kTileElems = kTileRows * kTileCols;  // 512 bf16 = 1 KB
@@ -26,35 +30,39 @@ constexpr int kMaxTilesInFlight = 20;              // weight tiles a wave keeps 
 enum GemvMode : int {
   kStore = 0,   // out[b][n] = y
   kResid = 1,   // x[b][n] += y, and partial sums of squares of the new x
-  kSwiGLU = 2,  // act[b][i] = silu(gate_i) * up_i  (row tiles paired gate|up)
+  kSwiGLU = 2,  // act[b][i] = silu(gate_i) * up_i  (gate|up interleaved by half tiles)
   kArgmax = 3,  // optional logits, then argmax over all rows per batch column
   kPartial = 4, // no reduction: every item leaves its K-split partial for the consumer
 };
 
+// One GEMV work item covers rt row tiles (16*rt rows) and one of S slices
+// of K (kps k-tiles); its 4 waves take the row tiles and, when rt < 4,
+// split the item's K slice between them (reduced in LDS).
 struct GemvArgs {
   const uint16_t* w;   // packed tiles, N x K
   int N, K, B, Bmax;
   int S, kps;          // K split count and k-tiles per split
+  int rt;              // row tiles per item: 1, 2 or 4
+  int ssq_rows;        // granularity (16 or 64 rows) of the sums of squares read and written
   const float* x;      // input activations [B][K] fp32
-  const float* ssq;    // if non-null: RMSNorm the input; [K/64][Bmax] partial sums of squares
+  const float* ssq;    // if non-null: RMSNorm the input; [K/ssq_rows][Bmax] partial sums of squares
   const float* gain;   // [K] RMSNorm gain
   float eps;
-  float* part;         // split-K partials [N/64 * S][64][B] (kPartial: the consumer's input)
-  unsigned* counters;  // [N/64] split-K arrival counters (zero between uses)
+  float* part;         // split-K partials [items][16*rt][B] (kPartial: the consumer's input)
+  unsigned* counters;  // [N/(16*rt)] split-K arrival counters (zero between uses)
   float* out;          // kStore: [B][N]; kResid: x [B][N]; kSwiGLU: [B][N/2]
-  float* ssq_out;      // kResid: [N/64][Bmax]
+  float* ssq_out;      // kResid: [N/ssq_rows][Bmax]
   float* logits;       // kArgmax: [B][N] or null
-  float* amax_val;     // kArgmax: [N/64][Bmax]
-  int* amax_idx;       // kArgmax: [N/64][Bmax]
+  float* amax_val;     // kArgmax (rt = 4): [N/64][Bmax]
+  int* amax_idx;       // kArgmax (rt = 4): [N/64][Bmax]
   unsigned* amax_counter;
   int* next_ids;       // kArgmax: [B]
-  unsigned* done;      // if non-null: +1 per row group whose output is final
 };
 
 struct AttnArgs {
   const float* qkv;        // [B][(Hq+2Hkv)D], or null when read from qkv_part
   const float* qkv_part;   // if non-null: the QKV projection's qkv_S split partials
-  int qkv_S;
+  int qkv_S, qkv_rows;     // (qkv_rows rows per QKV item)
   const float* q_gain;     // [D]
   const float* k_gain;     // [D]
   const float* rope_cos;   // [max_pos][D/2]
@@ -75,17 +83,16 @@ struct AttnArgs {
   float* tap_q;            // optional [B][Hq][D] (after norm and RoPE, unscaled)
   float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
   int* dev_flags;
-  unsigned* done;          // if non-null: +1 per (sequence, KV head) whose output is final
 };
 
 struct EmbedArgs {
   const uint16_t* table;   // packed [V][H]
   int V, H, B, Bmax;
+  int ssq_rows;            // 16 or 64
   const int* tokens;
   float* x;                // [B][H]
-  float* ssq_out;          // [H/64][Bmax]
+  float* ssq_out;          // [H/ssq_rows][Bmax]
   int* dev_flags;
-  unsigned* done;          // if non-null: +1 per sequence
 };
 
 // Per-layer pointers for the persistent step kernel (device-resident array).
@@ -109,6 +116,7 @@ struct StepArgs {
   int L;
   size_t pool_layer_elems;   // elements of one layer's slice of the pool
   unsigned* cnt;             // [1 + L*kCntPerLayer] dependency counters
+  unsigned* flags;           // [grid][32]: per-workgroup completed-stage flags
   unsigned* exit_cnt;        // workgroups that finished the step
   unsigned* abort_flag;      // set when a wait times out; later waits fall through
   int* dev_flags;
@@ -116,18 +124,24 @@ struct StepArgs {
   unsigned long long* trace; // builds with QD_STEP_TRACE only: per-item timestamps
 };
 
+// Batch columns a GEMV item is compiled for: VALU up to 4, MFMA blocks of 16 above.
+constexpr int gemv_nb(int B) {
+  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+}
+
 // Minimum pages a split of a sequence covers (one per wave of a workgroup).
 constexpr int kMinPagesPerSplit = 4;
 
 // Launchers (qd_kernels.hip).  All return the launch status.
-hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int tile_mul,
-                         int tile_add, hipStream_t s);
+// Source row r lands in packed row (r / blk) * stride + off + r % blk.
+hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int blk,
+                         int stride, int off, hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
-hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
-                               int B, int Bmax, float eps, float* out, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, int ssq_rows, const float* gain,
+                               int H, int B, int Bmax, float eps, float* out, hipStream_t s);
 
 // Persistent step: which (head_dim, group) shapes it is built for, the LDS
 // bytes it needs, the largest co-resident grid, and the cooperative launch.

@@ -20,24 +20,22 @@ namespace qd {
 
 // ------------------------------------------------------------------ repack
 
-// Row-major [rows][K] bf16 -> tile-major (see qd_internal.h).  Source row
-// tile j lands in destination row tile j * tile_mul + tile_add, which fuses
-// q|k|v (tile_add = row offset / 16) and pairs gate|up (tile_mul = 2).
+// Row-major [rows][K] bf16 -> tile-major (see qd_internal.h).  Source row r
+// lands in packed row (r / blk) * stride + off + r % blk: blk = 16 with
+// stride 16 stacks q|k|v at a row offset, blk = 8 with stride 16 puts gate
+// rows in the first half of each packed row tile (off 0) and up rows in the
+// second (off 8).  One thread moves one 16-byte run of 8 columns.
 __global__ void repack_kernel(const uint16_t* __restrict__ src, int rows, int K,
-                              uint16_t* __restrict__ dst, int tile_mul, int tile_add) {
-  const int KT = K / kTileCols;
-  const size_t n = (size_t)(rows / kTileRows) * KT * 64;
+                              uint16_t* __restrict__ dst, int blk, int stride, int off) {
+  const int KT = K / kTileCols, K8 = K / 8;
+  const size_t n = (size_t)rows * K8;
   for (size_t c = blockIdx.x * (size_t)blockDim.x + threadIdx.x; c < n;
        c += (size_t)gridDim.x * blockDim.x) {
-    const int lane = (int)(c % 64);
-    const size_t t = c / 64;
-    const int kt = (int)(t % KT);
-    const int rt = (int)(t / KT);
-    const uint16_t* s = src + (size_t)(rt * kTileRows + lane % 16) * K + kt * kTileCols +
-                        (lane / 16) * 8;
-    const size_t drt = (size_t)rt * tile_mul + tile_add;
-    uint16_t* d = dst + (drt * KT + kt) * kTileElems + lane * 8;
-    *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+    const int r = (int)(c / K8), k = (int)(c % K8) * 8;
+    const int R = (r / blk) * stride + off + r % blk;
+    const int lane = R % kTileRows + kTileRows * ((k % kTileCols) / 8);
+    uint16_t* d = dst + ((size_t)(R / kTileRows) * KT + k / kTileCols) * kTileElems + lane * 8;
+    *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(src + (size_t)r * K + k);
   }
 }
 
@@ -47,17 +45,17 @@ __global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __re
   if (i < n) dst[i] = __uint_as_float((unsigned)src[i] << 16);
 }
 
-__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) { embed_item(a, a.done, blockIdx.x); }
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) { embed_item(a, no_done(), blockIdx.x); }
 
 // out[b][k] = x[b][k] * rsqrt(sum(ssq partials)/H + eps) * gain[k]
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const float* ssq,
-                                                           const float* gain, int H, int Bmax,
-                                                           float eps, float* out) {
+                                                           int ssq_rows, const float* gain, int H,
+                                                           int Bmax, float eps, float* out) {
   const int b = blockIdx.x;
   __shared__ float s_inv;
   if (threadIdx.x == 0) {
     float ss = 0.f;
-    for (int g = 0; g < H / 64; ++g) ss += ssq[(size_t)g * Bmax + b];
+    for (int g = 0; g < H / ssq_rows; ++g) ss += ssq[(size_t)g * Bmax + b];
     s_inv = rsqrtf(ss / (float)H + eps);
   }
   __syncthreads();
@@ -69,26 +67,26 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const
 template <int NB, int MODE>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  gemv_item<NB, MODE>(a, a.w, a.gain, a.done, blockIdx.x, smem, NoWait{});
+  gemv_item<NB, MODE>(a, a.w, a.gain, no_done(), blockIdx.x, smem, NoWait{});
 }
 
 
 template <int D, int G>
 __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  attention_item<D, G>(a, a.q_gain, a.k_gain, a.pool_layer, a.done, blockIdx.x, smem, NoWait{});
+  attention_item<D, G>(a, a.q_gain, a.k_gain, a.pool_layer, no_done(), blockIdx.x, smem, NoWait{});
 }
 
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int tile_mul,
-                         int tile_add, hipStream_t s) {
-  const size_t n = (size_t)(rows / kTileRows) * (K / kTileCols) * 64;
+hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int blk,
+                         int stride, int off, hipStream_t s) {
+  const size_t n = (size_t)rows * (K / 8);
   int grid = (int)((n + 255) / 256);
   if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(repack_kernel, dim3(grid), dim3(256), 0, s, src, rows, K, dst, tile_mul,
-                     tile_add);
+  hipLaunchKernelGGL(repack_kernel, dim3(grid), dim3(256), 0, s, src, rows, K, dst, blk, stride,
+                     off);
   return hipGetLastError();
 }
 
@@ -102,10 +100,10 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
-                               int B, int Bmax, float eps, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, x, ssq, gain, H, Bmax, eps,
-                     out);
+hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, int ssq_rows, const float* gain,
+                               int H, int B, int Bmax, float eps, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, x, ssq, ssq_rows, gain, H,
+                     Bmax, eps, out);
   return hipGetLastError();
 }
 
@@ -119,7 +117,7 @@ static hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = (a.N / kRowsPerGroup) * a.S;
+  const int grid = (a.N / (kTileRows * a.rt)) * a.S;
   hipLaunchKernelGGL((gemv_kernel<NB, MODE>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }

@@ -38,7 +38,7 @@ struct GraphKey {
 };
 
 struct GemvPlan {
-  int S = 1, kps = 1;
+  int S = 1, kps = 1, rt = 4;
 };
 
 struct LayerW {
@@ -85,9 +85,10 @@ struct qd_handle {
   bool persistent = false;
   LayerDev* layers_dev = nullptr;
   unsigned* step_cnt = nullptr;
+  unsigned* step_flags = nullptr;  // [2 * CUs][32]
   unsigned* step_exit = nullptr;
   unsigned* step_abort = nullptr;
-  std::map<int, std::pair<int, size_t>> step_shape;  // batch -> (grid, LDS bytes)
+  std::map<int, int> step_grid;  // batch -> co-resident grid of the persistent kernel
 };
 
 namespace {
@@ -119,32 +120,72 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
   return QD_OK;
 }
 
-// Split plan for an N x K projection at batch B: enough workgroups to cover
-// the chip twice (or every K tile split), at most 20 tiles per wave in flight
-// unless the row count alone fills the chip, and an LDS input slice <= 96 KB.
-// The persistent step keeps two workgroups per CU, so its GEMV items get a
-// smaller LDS budget.
+// Split plan for an N x K projection at batch B.
+//
+// Batch <= 4 (VALU items, graph path): one 16-row tile per workgroup, its 4
+// waves splitting K, and K itself split only where the input slice would not
+// fit an 80 KB LDS budget or the row tiles alone give fewer than 128
+// workgroups: the projections of a 4B-class model then need no split-K
+// hand-off at batch 1.  The LM head keeps 64-row items (its argmax reduces
+// one partial per row group).
+// Batch >= 5 (MFMA items) and the persistent step: 64-row items, enough
+// workgroups to cover the chip twice, at most 20 tiles per wave unless the
+// row count alone fills the chip, and an LDS input slice <= 96 KB (72 KB in
+// the persistent step, which keeps two workgroups per CU).
+constexpr size_t kLdsCapValu = 80 * 1024;
 constexpr size_t kLdsCapStaged = 96 * 1024;
 constexpr size_t kLdsCapPersistent = 72 * 1024;
+constexpr int kMinValuItems = 128;
 
-GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B) {
+bool row_tile_items(const qd_handle* h, int B) { return !h->persistent && gemv_nb(B) <= 4; }
+
+// Rows per partial sum of squares of the residual stream at batch B.
+int ssq_rows_for(const qd_handle* h, int B) { return row_tile_items(h, B) ? 16 : 64; }
+
+GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
+                   int grid = 0) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
-  const int target = 2 * h->num_cus;
-  const size_t cap = h->persistent ? kLdsCapPersistent : kLdsCapStaged;
+  const int target = grid > 0 ? grid : 2 * h->num_cus;
   GemvPlan p;
-  if (h->persistent) {
-    // at most one item per workgroup of the persistent grid (the items of a
-    // stage run concurrently; a wave streams a long K slice in chunks),
-    // more splits only where the input slice would not fit in LDS
-    int S = std::max(1, std::min(KT, target / std::max(1, NRG)));
-    for (;; ++S) {
+  if (row_tile_items(h, B)) {
+    p.rt = argmax ? 4 : 1;
+    const int groups = N / (kTileRows * p.rt);
+    for (int S = 1; S <= KT; ++S) {
       const int kps = (KT + S - 1) / S;
-      if (gemv_lds_bytes(B, kps) <= cap || kps == 1) {
-        p.kps = kps;
-        p.S = (KT + kps - 1) / kps;
-        return p;
+      const int Se = (KT + kps - 1) / kps;
+      if (gemv_lds_bytes(B, kps) > kLdsCapValu && kps > 1) continue;
+      p.S = Se;
+      p.kps = kps;
+      if (groups * Se >= kMinValuItems) return p;
+    }
+    return p;
+  }
+  const size_t cap = h->persistent ? kLdsCapPersistent : kLdsCapStaged;
+  if (h->persistent) {
+    // The grid's workgroups share each stage: the split count minimises the
+    // items of the busiest workgroup times the k-tiles of an item (rows
+    // alone may give more row groups than workgroups), splits costing a
+    // little for their reduction; the input slice must fit in LDS.
+    int best_S = 1;
+    double best = 1e30;
+    for (int S = 1; S <= std::min(KT, 8); ++S) {
+      const int kps = (KT + S - 1) / S;
+      if (gemv_lds_bytes(B, kps) > cap && kps > 1) continue;
+      const int Se = (KT + kps - 1) / kps;
+      const double rounds = (double)((NRG * Se + target - 1) / target);
+      const double cost = rounds * kps + 2.0 * Se;
+      if (cost < best) { best = cost; best_S = Se; }
+    }
+    p.kps = (KT + best_S - 1) / best_S;
+    p.S = (KT + p.kps - 1) / p.kps;
+    if (gemv_lds_bytes(B, p.kps) > cap) {  // only very long K: split until it fits
+      for (int S = 9; S <= KT; ++S) {
+        p.kps = (KT + S - 1) / S;
+        p.S = (KT + p.kps - 1) / p.kps;
+        if (gemv_lds_bytes(B, p.kps) <= cap) break;
       }
     }
+    return p;
   }
   for (int S = 1; S <= KT; ++S) {
     const int kps = (KT + S - 1) / S;
@@ -179,7 +220,8 @@ int validate_config(const qd_config* c) {
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0))
     return fail(nullptr, QD_EINVAL, "rms_eps and rope_theta must be > 0");
   if (c->page_size != kPage) return fail(nullptr, QD_EUNSUPPORTED, "page_size must be 16");
-  if (c->hidden % 64) return fail(nullptr, QD_EUNSUPPORTED, "hidden must be a multiple of 64");
+  if (c->hidden % 64 || c->hidden > 8192)
+    return fail(nullptr, QD_EUNSUPPORTED, "hidden must be a multiple of 64 and at most 8192");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(nullptr, QD_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (c->num_q_heads % c->num_kv_heads)
@@ -233,19 +275,20 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   const float eps = h->cfg.rms_eps;
   const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
 
+  const int sr = ssq_rows_for(h, B);
   EmbedArgs ea{};
   ea.table = h->embed;
-  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch;
+  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch; ea.ssq_rows = sr;
   ea.tokens = sp.tokens; ea.x = h->x; ea.ssq_out = h->ssq; ea.dev_flags = h->dev_flags;
   HIP_TRY(h, launch_embed(ea, s));
   PROF(QD_PROF_EMBED);
 
   auto gemv = [&](const uint16_t* w, int N, int K, const float* xin, const float* gain,
                   int mode, float* out) -> hipError_t {
-    GemvPlan p = plan_gemv(h, N, K, B);
+    GemvPlan p = plan_gemv(h, N, K, B, mode == kArgmax);
     GemvArgs a{};
     a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
-    a.S = p.S; a.kps = p.kps;
+    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.ssq_rows = sr;
     a.x = xin;
     a.ssq = gain ? h->ssq : nullptr;
     a.gain = gain; a.eps = eps;
@@ -272,7 +315,8 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     if (part_mode) {
       GemvArgs q{};
       q.w = w.qkv; q.N = h->NQKV; q.K = H; q.B = B; q.Bmax = h->cfg.max_batch;
-      q.S = pq.S; q.kps = pq.kps; q.x = h->x; q.ssq = h->ssq; q.gain = w.in_norm;
+      q.S = pq.S; q.kps = pq.kps; q.rt = pq.rt; q.ssq_rows = sr;
+      q.x = h->x; q.ssq = h->ssq; q.gain = w.in_norm;
       q.eps = eps; q.part = h->part_qkv;
       HIP_TRY(h, launch_gemv(q, kPartial, s));
     } else {
@@ -284,7 +328,7 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
                                 hipMemcpyDeviceToDevice, s));
     AttnArgs aa{};
     aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
-    if (part_mode) { aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; }
+    if (part_mode) { aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; aa.qkv_rows = kTileRows * pq.rt; }
     aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
     aa.pool_layer = sp.pool + (size_t)l * layer_elems;
     aa.num_pages = h->cfg.num_pages;
@@ -318,8 +362,8 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
       HIP_TRY(h, hipMemcpyAsync(taps->x_out, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
   }
   if (taps && taps->final_h)
-    HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, h->final_norm, H, B, h->cfg.max_batch, eps,
-                                   taps->final_h, s));
+    HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, sr, h->final_norm, H, B, h->cfg.max_batch,
+                                   eps, taps->final_h, s));
   HIP_TRY(h, gemv(h->lm, h->V, H, h->x, h->final_norm, kArgmax, nullptr));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
@@ -327,11 +371,11 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
 }
 
 GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const float* xin,
-                       bool norm, float* out) {
-  GemvPlan p = plan_gemv(h, N, K, sp.B);
+                       bool norm, float* out, int grid, bool argmax = false) {
+  GemvPlan p = plan_gemv(h, N, K, sp.B, argmax, grid);
   GemvArgs a{};
   a.N = N; a.K = K; a.B = sp.B; a.Bmax = h->cfg.max_batch;
-  a.S = p.S; a.kps = p.kps;
+  a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.ssq_rows = ssq_rows_for(h, sp.B);
   a.x = xin;
   a.ssq = norm ? h->ssq : nullptr;
   a.eps = h->cfg.rms_eps;
@@ -344,19 +388,43 @@ GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const flo
   return a;
 }
 
+// Co-resident grid of the persistent kernel at batch B (at most 2 per CU),
+// for the largest LDS any of its plans may ask for.
+int persistent_grid(qd_handle* h, int B, int* grid) {
+  auto it = h->step_grid.find(B);
+  if (it != h->step_grid.end()) { *grid = it->second; return QD_OK; }
+  const size_t lds_max = step_lds_bytes(B, h->D, h->G, 0) > kLdsCapPersistent
+                             ? step_lds_bytes(B, h->D, h->G, 0) : kLdsCapPersistent;
+  int g = 0;
+  HIP_TRY(h, step_max_grid(B, h->D, h->G, lds_max, h->num_cus, &g));
+  if (g < 1) return fail(h, QD_EUNSUPPORTED, "persistent step does not fit on a CU");
+  const int occupancy_grid = g;
+  g = std::min(g, 2 * h->num_cus);
+  if (const char* e = std::getenv("QD_STEP_GRID")) g = std::min(g, std::max(1, std::atoi(e)));
+  if (std::getenv("QD_DEBUG"))
+    std::fprintf(stderr, "[qd] persistent step B=%d: occupancy grid %d, grid %d\n", B,
+                 occupancy_grid, g);
+  h->step_grid[B] = g;
+  *grid = g;
+  return QD_OK;
+}
+
 // One step as one persistent cooperative kernel.
 int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   const int B = sp.B, H = h->H;
+  int grid = 0;
+  if (int rc = persistent_grid(h, B, &grid)) return rc;
   StepArgs a{};
   a.embed.table = h->embed;
   a.embed.V = h->V; a.embed.H = H; a.embed.B = B; a.embed.Bmax = h->cfg.max_batch;
   a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
   a.embed.dev_flags = h->dev_flags;
-  a.qkv = gemv_template(h, sp, h->NQKV, H, h->x, true, h->qkv);
-  a.o = gemv_template(h, sp, H, h->QD, h->attn, false, h->x);
-  a.gu = gemv_template(h, sp, 2 * h->I, H, h->x, true, h->act);
-  a.down = gemv_template(h, sp, H, h->I, h->act, false, h->x);
-  a.lm = gemv_template(h, sp, h->V, H, h->x, true, nullptr);
+  a.embed.ssq_rows = ssq_rows_for(h, B);
+  a.qkv = gemv_template(h, sp, h->NQKV, H, h->x, true, h->qkv, grid);
+  a.o = gemv_template(h, sp, H, h->QD, h->attn, false, h->x, grid);
+  a.gu = gemv_template(h, sp, 2 * h->I, H, h->x, true, h->act, grid);
+  a.down = gemv_template(h, sp, H, h->I, h->act, false, h->x, grid);
+  a.lm = gemv_template(h, sp, h->V, H, h->x, true, nullptr, grid, true);
   a.lm.w = h->lm;
   a.lm.gain = h->final_norm;
   a.qkv.part = h->part_qkv;
@@ -364,6 +432,7 @@ int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   at.qkv = h->qkv;
   at.qkv_part = h->part_qkv;
   at.qkv_S = a.qkv.S;
+  at.qkv_rows = kTileRows * a.qkv.rt;
   at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
   at.pool_layer = sp.pool;
   at.num_pages = h->cfg.num_pages;
@@ -378,37 +447,24 @@ int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.layers = h->layers_dev;
   a.L = h->L;
   a.pool_layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
-  a.cnt = h->step_cnt; a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
+  a.cnt = h->step_cnt; a.flags = h->step_flags;
+  a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
   a.dev_flags = h->dev_flags;
   a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
 
-  auto it = h->step_shape.find(B);
-  if (it == h->step_shape.end()) {
-    int max_kps = 1;
-    for (const GemvArgs* g : {&a.qkv, &a.o, &a.gu, &a.down, &a.lm})
-      max_kps = std::max(max_kps, g->kps);
-    const size_t lds = step_lds_bytes(B, h->D, h->G, max_kps);
-    int grid = 0;
-    HIP_TRY(h, step_max_grid(B, h->D, h->G, lds, h->num_cus, &grid));
-    if (grid < 1) return fail(h, QD_EUNSUPPORTED, "persistent step does not fit on a CU");
-    const int occupancy_grid = grid;
-    grid = std::min(grid, 2 * h->num_cus);
-    if (const char* g = std::getenv("QD_STEP_GRID")) grid = std::max(1, std::atoi(g));
-    if (std::getenv("QD_DEBUG"))
-      std::fprintf(stderr, "[qd] persistent step B=%d: LDS %zu B, occupancy grid %d, grid %d\n",
-                   B, lds, occupancy_grid, grid);
-    it = h->step_shape.emplace(B, std::make_pair(grid, lds)).first;
-  }
+  int max_kps = 1;
+  for (const GemvArgs* g : {&a.qkv, &a.o, &a.gu, &a.down, &a.lm}) max_kps = std::max(max_kps, g->kps);
+  const size_t lds = step_lds_bytes(B, h->D, h->G, max_kps);
 #ifdef QD_STEP_TRACE
   static unsigned long long* trace = nullptr;
-  const size_t trace_n = (size_t)it->second.first * 1024 * 3;
+  const size_t trace_n = (size_t)grid * 1024 * 4;
   if (!trace) {
     HIP_TRY(h, hipMalloc(&trace, trace_n * 8));
   }
   HIP_TRY(h, hipMemsetAsync(trace, 0xff, trace_n * 8, s));
   a.trace = trace;
 #endif
-  HIP_TRY(h, launch_step(a, h->D, h->G, it->second.first, it->second.second, s));
+  HIP_TRY(h, launch_step(a, h->D, h->G, grid, lds, s));
 #ifdef QD_STEP_TRACE
   if (const char* path = std::getenv("QD_TRACE_OUT")) {
     HIP_TRY(h, hipStreamSynchronize(s));
@@ -504,23 +560,27 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
 
   // activations and scratch
   if ((rc = dev_alloc(h, &h->x, (size_t)Bm * H))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / 64) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / kTileRows) * Bm))) return bail(rc);
   if ((rc = dev_alloc(h, &h->qkv, (size_t)Bm * h->NQKV))) return bail(rc);
   if ((rc = dev_alloc(h, &h->attn, (size_t)Bm * h->QD))) return bail(rc);
   if ((rc = dev_alloc(h, &h->act, (size_t)Bm * I))) return bail(rc);
+  // split partials: N * S * B floats for whichever projection needs most;
+  // arrival counters: one per row group, at most N / 16
   size_t part_elems = 1, part_qkv_elems = 1;
-  int max_nrg = 1;
+  const int max_nrg = std::max(std::max(h->NQKV, 2 * I), std::max(H, V)) / kTileRows;
   for (int B = 1; B <= Bm; ++B) {
-    const int dims[3][2] = {{H, h->QD}, {H, I}, {V, H}};
+    // the same plans the steps will use (persistent plans depend on the grid)
+    int grid = 0;
+    if (h->persistent && (rc = persistent_grid(h, B, &grid))) return bail(rc);
+    const int dims[3][2] = {{H, h->QD}, {H, I}, {2 * I, H}};
     for (auto& d : dims) {
-      GemvPlan p = plan_gemv(h, d[0], d[1], B);
+      GemvPlan p = plan_gemv(h, d[0], d[1], B, false, grid);
       if (p.S > 1) part_elems = std::max(part_elems, (size_t)d[0] * p.S * B);
-      max_nrg = std::max(max_nrg, d[0] / kRowsPerGroup);
     }
-    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B), pg = plan_gemv(h, 2 * I, H, B);
+    const GemvPlan pl = plan_gemv(h, V, H, B, true, grid);
+    if (pl.S > 1) part_elems = std::max(part_elems, (size_t)V * pl.S * B);
+    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B, false, grid);
     part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * pq.S * B);
-    if (pg.S > 1) part_elems = std::max(part_elems, (size_t)2 * I * pg.S * B);
-    max_nrg = std::max(max_nrg, std::max(h->NQKV, 2 * I) / kRowsPerGroup);
   }
   if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
@@ -546,9 +606,11 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (h->persistent) {
     if ((rc = dev_alloc(h, &h->layers_dev, (size_t)L))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_cnt, (size_t)1 + (size_t)L * kCntPerLayer))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->step_flags, (size_t)2 * h->num_cus * 32))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_exit, 1))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_abort, 1))) return bail(rc);
     e = hipMemset(h->step_cnt, 0, sizeof(unsigned) * (1 + (size_t)L * kCntPerLayer));
+    if (e == hipSuccess) e = hipMemset(h->step_flags, 0, sizeof(unsigned) * 2 * h->num_cus * 32);
     if (e == hipSuccess) e = hipMemset(h->step_exit, 0, sizeof(unsigned));
     if (e == hipSuccess) e = hipMemset(h->step_abort, 0, sizeof(unsigned));
     std::vector<LayerDev> ld(L);
@@ -604,10 +666,10 @@ int qd_load_weights(qd_handle* h, const qd_tensor_desc* t, int32_t n) {
     bool shape_ok = true;
     if (name == "model.embed_tokens.weight") {
       shape_ok = need(V, H);
-      if (shape_ok) e = launch_repack(src, V, H, h->embed, 1, 0, s);
+      if (shape_ok) e = launch_repack(src, V, H, h->embed, 16, 16, 0, s);
     } else if (name == "lm_head.weight") {
       shape_ok = need(V, H);
-      if (shape_ok) e = launch_repack(src, V, H, h->lm, 1, 0, s);
+      if (shape_ok) e = launch_repack(src, V, H, h->lm, 16, 16, 0, s);
     } else if (name == "model.norm.weight") {
       shape_ok = need(H, -1);
       if (shape_ok) e = launch_bf16_to_f32(src, h->final_norm, H, s);
@@ -629,25 +691,25 @@ int qd_load_weights(qd_handle* h, const qd_tensor_desc* t, int32_t n) {
         if (shape_ok) e = launch_bf16_to_f32(src, w.k_norm, D, s);
       } else if (leaf == "self_attn.q_proj.weight") {
         shape_ok = need(h->QD, H);
-        if (shape_ok) e = launch_repack(src, h->QD, H, w.qkv, 1, 0, s);
+        if (shape_ok) e = launch_repack(src, h->QD, H, w.qkv, 16, 16, 0, s);
       } else if (leaf == "self_attn.k_proj.weight") {
         shape_ok = need(h->KD, H);
-        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 1, h->QD / kTileRows, s);
+        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 16, 16, h->QD, s);
       } else if (leaf == "self_attn.v_proj.weight") {
         shape_ok = need(h->KD, H);
-        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 1, (h->QD + h->KD) / kTileRows, s);
+        if (shape_ok) e = launch_repack(src, h->KD, H, w.qkv, 16, 16, h->QD + h->KD, s);
       } else if (leaf == "self_attn.o_proj.weight") {
         shape_ok = need(H, h->QD);
-        if (shape_ok) e = launch_repack(src, H, h->QD, w.o, 1, 0, s);
+        if (shape_ok) e = launch_repack(src, H, h->QD, w.o, 16, 16, 0, s);
       } else if (leaf == "mlp.gate_proj.weight") {
         shape_ok = need(I, H);
-        if (shape_ok) e = launch_repack(src, I, H, w.gu, 2, 0, s);
+        if (shape_ok) e = launch_repack(src, I, H, w.gu, 8, 16, 0, s);
       } else if (leaf == "mlp.up_proj.weight") {
         shape_ok = need(I, H);
-        if (shape_ok) e = launch_repack(src, I, H, w.gu, 2, 1, s);
+        if (shape_ok) e = launch_repack(src, I, H, w.gu, 8, 16, 8, s);
       } else if (leaf == "mlp.down_proj.weight") {
         shape_ok = need(H, I);
-        if (shape_ok) e = launch_repack(src, H, I, w.down, 1, 0, s);
+        if (shape_ok) e = launch_repack(src, H, I, w.down, 16, 16, 0, s);
       } else {
         return fail(h, QD_EINVAL, "unexpected tensor " + name);
       }

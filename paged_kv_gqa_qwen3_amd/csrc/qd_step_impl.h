@@ -10,9 +10,23 @@ namespace qd {
 // Weight tiles a wave keeps in flight inside the persistent kernel.
 constexpr int kPersistentTiles = kMaxTilesInFlight;
 
-__device__ __forceinline__ int gemv_items(const GemvArgs& g) {
-  return (g.N / kRowsPerGroup) * g.S;
+#ifdef QD_STEP_TRACE
+// A wait that also records when it was satisfied (trace builds only).
+struct TracedWaiter {
+  static constexpr bool kInLaunch = true;
+  Waiter w;
+  unsigned long long* t;
+  __device__ void operator()() const {
+    w();
+    if (threadIdx.x == 0) *t = __builtin_amdgcn_s_memrealtime();
+  }
+};
+#endif
+
+__device__ __forceinline__ int gemv_row_groups(const GemvArgs& g) {
+  return g.N / (kTileRows * g.rt);
 }
+__device__ __forceinline__ int gemv_items(const GemvArgs& g) { return gemv_row_groups(g) * g.S; }
 
 // The whole decode step in one cooperative launch.  Items are numbered in
 // step order (embedding, then per layer QKV, attention, O, gate/up, down,
@@ -21,29 +35,37 @@ __device__ __forceinline__ int gemv_items(const GemvArgs& g) {
 // its items in step order, so the step always makes progress when every
 // workgroup is resident (the cooperative launch guarantees it).
 template <int NB, int D, int G>
-__global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
+__global__ __launch_bounds__(256, 2) void step_kernel(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const long nwg = gridDim.x, wg = blockIdx.x;
   long base = 0;
 #ifdef QD_STEP_TRACE
-  // (phase, start, end) of every item this workgroup runs, 100 MHz clock
-  int phase = 0, nrec = 0;
-  unsigned long long* tr = a.trace + (size_t)wg * 1024 * 3;
+  // (phase, start, wait satisfied, end) of every item this workgroup runs,
+  // 100 MHz clock
+  __shared__ unsigned long long t_wait;
+  int trace_phase = 0, nrec = 0;
+  unsigned long long* tr = a.trace + (size_t)wg * 1024 * 4;
   auto for_items = [&](int n, auto&& fn) {
     const long first = base + ((wg - base) % nwg + nwg) % nwg;
     for (long j = first; j < base + n; j += nwg) {
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      if (threadIdx.x == 0) t_wait = t0;
       fn((int)(j - base));
       const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
       if (threadIdx.x == 0 && nrec < 1024) {
-        tr[nrec * 3 + 0] = (unsigned long long)phase;
-        tr[nrec * 3 + 1] = t0;
-        tr[nrec * 3 + 2] = t1;
+        tr[nrec * 4 + 0] = (unsigned long long)trace_phase;
+        tr[nrec * 4 + 1] = t0;
+        tr[nrec * 4 + 2] = t_wait;
+        tr[nrec * 4 + 3] = t1;
       }
       ++nrec;
     }
     base += n;
-    ++phase;
+    ++trace_phase;
+  };
+  auto waiter = [&](unsigned phase) {
+    return TracedWaiter{Waiter{a.flags + (size_t)wg * kFlagStride, phase, a.abort_flag,
+                               a.dev_flags, a.spin_limit}, &t_wait};
   };
 #else
   auto for_items = [&](int n, auto&& fn) {
@@ -51,53 +73,60 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
     for (long j = first; j < base + n; j += nwg) fn((int)(j - base));
     base += n;
   };
+  auto waiter = [&](unsigned phase) {
+    return Waiter{a.flags + (size_t)wg * kFlagStride, phase, a.abort_flag, a.dev_flags,
+                  a.spin_limit};
+  };
 #endif
-  const unsigned rg_h = (unsigned)(a.o.N / kRowsPerGroup);
+  const unsigned rg_o = (unsigned)gemv_row_groups(a.o);
+  const unsigned rg_down = (unsigned)gemv_row_groups(a.down);
   // QKV leaves split partials that attention sums: that stage is complete
   // when every item is
   const unsigned n_qkv = (unsigned)gemv_items(a.qkv);
-  const unsigned rg_gu = (unsigned)(a.gu.N / kRowsPerGroup);
+  const unsigned rg_gu = (unsigned)gemv_row_groups(a.gu);
   const unsigned n_heads = (unsigned)(a.attn.B * a.attn.Hkv);
-  auto waiter = [&](const unsigned* c, unsigned target) {
-    return Waiter{c, target, a.abort_flag, a.dev_flags, a.spin_limit};
+  // stage with counter index i completes phase i + 1 (0: nothing done yet)
+  auto done = [&](int i, unsigned target) {
+    return Done{a.cnt + i, target, (unsigned)i + 1u, a.flags, (int)nwg};
   };
+  auto phase = [](int i) { return (unsigned)i + 1u; };
 
   for_items(a.embed.B, [&](int b) {
     __syncthreads();
-    embed_item(a.embed, a.cnt + kCntEmbed, b);
+    embed_item(a.embed, done(kCntEmbed, (unsigned)a.embed.B), b);
   });
 
   for (int l = 0; l < a.L; ++l) {
     const LayerDev ly = a.layers[l];
-    unsigned* c = a.cnt + cnt_index(l, 0);
-    const unsigned* x_ready = l == 0 ? a.cnt + kCntEmbed : a.cnt + cnt_index(l - 1, 4);
-    const unsigned x_target = l == 0 ? (unsigned)a.embed.B : rg_h;
+    const int c = cnt_index(l, 0);
+    const unsigned x_ready = l == 0 ? phase(kCntEmbed) : phase(cnt_index(l - 1, 4));
 
     for_items(gemv_items(a.qkv), [&](int it) {
-      gemv_item<NB, kPartial, kPersistentTiles>(a.qkv, ly.qkv, ly.in_norm, c + 0, it, smem,
-                                                waiter(x_ready, x_target));
+      gemv_item<NB, kPartial, kPersistentTiles>(a.qkv, ly.qkv, ly.in_norm, done(c + 0, n_qkv),
+                                                it, smem, waiter(x_ready));
     });
     uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
     for_items(a.attn.B * a.attn.Hkv * a.attn.S_max, [&](int it) {
-      attention_item<D, G>(a.attn, ly.q_norm, ly.k_norm, pool_l, c + 1, it, smem,
-                           waiter(c + 0, n_qkv));
+      attention_item<D, G>(a.attn, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), it,
+                           smem, waiter(phase(c + 0)));
     });
     for_items(gemv_items(a.o), [&](int it) {
-      gemv_item<NB, kResid, kPersistentTiles>(a.o, ly.o, nullptr, c + 2, it, smem, waiter(c + 1, n_heads));
+      gemv_item<NB, kResid, kPersistentTiles>(a.o, ly.o, nullptr, done(c + 2, rg_o), it, smem,
+                                              waiter(phase(c + 1)));
     });
     for_items(gemv_items(a.gu), [&](int it) {
-      gemv_item<NB, kSwiGLU, kPersistentTiles>(a.gu, ly.gu, ly.post_norm, c + 3, it, smem,
-                                               waiter(c + 2, rg_h));
+      gemv_item<NB, kSwiGLU, kPersistentTiles>(a.gu, ly.gu, ly.post_norm, done(c + 3, rg_gu),
+                                               it, smem, waiter(phase(c + 2)));
     });
     for_items(gemv_items(a.down), [&](int it) {
-      gemv_item<NB, kResid, kPersistentTiles>(a.down, ly.down, nullptr, c + 4, it, smem,
-                                              waiter(c + 3, rg_gu));
+      gemv_item<NB, kResid, kPersistentTiles>(a.down, ly.down, nullptr, done(c + 4, rg_down),
+                                              it, smem, waiter(phase(c + 3)));
     });
   }
 
   for_items(gemv_items(a.lm), [&](int it) {
-    gemv_item<NB, kArgmax, kPersistentTiles>(a.lm, a.lm.w, a.lm.gain, nullptr, it, smem,
-                           waiter(a.cnt + cnt_index(a.L - 1, 4), rg_h));
+    gemv_item<NB, kArgmax, kPersistentTiles>(a.lm, a.lm.w, a.lm.gain, no_done(), it, smem,
+                                             waiter(phase(cnt_index(a.L - 1, 4))));
   });
 
   // The last workgroup out resets the dependency counters for the next step.
@@ -109,6 +138,7 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
     if (prev == (unsigned)nwg - 1) {
       const int n = 1 + a.L * kCntPerLayer;
       for (int i = 0; i < n; ++i) st_agent(a.cnt + i, 0u);
+      for (long i = 0; i < nwg; ++i) st_agent(a.flags + (size_t)i * kFlagStride, 0u);
       st_agent(a.abort_flag, 0u);
       st_agent(a.exit_cnt, 0u);
     }

@@ -261,16 +261,15 @@ def test_graph_replay_matches_eager(torch):
 
 @pytest.mark.parametrize("B,ctx", [(1, [40]), (3, [5, 40, 77]), (4, [0, 16, 250, 31])])
 def test_persistent_matches_staged_bitwise(torch, B, ctx):
-    """The persistent kernel runs the same items with the same split plans as
-    the per-stage kernels (batch <= 4), so every bit must agree, over chained
-    steps."""
+    """The persistent kernel and the per-stage kernels of the same handle run
+    the same items with the same split plans, so every bit must agree, over
+    chained steps (the staged run goes through the taps entry point, which
+    never uses the persistent kernel)."""
     shape = synth.TINY
     W = synth.make_weights(shape, 70 + B)
     batch = synth.make_paged_batch(shape, ctx, 5, 71 + B)
     dp = Decoder(shape, B, batch.max_pages, batch.num_pages, persistent=True)
-    de = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False)
     dp.load_numpy_weights(W)
-    de.load_numpy_weights(W)
     pp, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
     ip = StepIO(torch, B, batch.max_pages, shape.vocab)
     ie = StepIO(torch, B, batch.max_pages, shape.vocab)
@@ -280,7 +279,8 @@ def test_persistent_matches_staged_bitwise(torch, B, ctx):
         ip.set(tokens, positions, batch.block_tables)
         ie.set(tokens, positions, batch.block_tables)
         ip.run(dp, pp)
-        ie.run(de, pe)
+        torch.cuda.synchronize()
+        dp.step_taps(ie.tok, ie.pos, ie.tab, pe, ie.nxt, ie.logits, None, -1)
         torch.cuda.synchronize()
         assert torch.equal(ip.logits, ie.logits)
         assert torch.equal(ip.nxt, ie.nxt)
@@ -289,7 +289,6 @@ def test_persistent_matches_staged_bitwise(torch, B, ctx):
     assert torch.equal(pp, pe)
     assert dp.device_status() == 0
     dp.close()
-    de.close()
 
 
 def test_page_placement_and_determinism(torch):

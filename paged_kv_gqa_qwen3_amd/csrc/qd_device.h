@@ -30,6 +30,13 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// bf16 hi/lo pair of v (hi = bf16(v), lo = bf16(v - hi)).
+__device__ __forceinline__ void split_hilo(float v, uint16_t* hi, uint16_t* lo, size_t i) {
+  const unsigned h = f2bf(v);
+  hi[i] = (uint16_t)h;
+  lo[i] = (uint16_t)f2bf(v - __uint_as_float(h << 16));
+}
+
 __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
   f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
@@ -208,8 +215,9 @@ struct NoWait {
 // ------------------------------------------------------------------ embedding
 
 // x[b] = E[token_b] (exact bf16 -> fp32), read from the packed table, plus
-// the sums of squares of x over each group of ssq_rows columns (the RMSNorm
-// of the first QKV projection consumes them).
+// the sums of squares of x over each group of 16 columns (the RMSNorm of the
+// first QKV projection consumes them) and, for an MFMA consumer, the bf16
+// pair of x times its RMSNorm gain.
 __device__ inline void embed_item(const EmbedArgs& a, const Done& done, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int tok = a.tokens[b];
@@ -225,18 +233,66 @@ __device__ inline void embed_item(const EmbedArgs& a, const Done& done, int b) {
     const uint16_t v = a.table[((size_t)rt * KT + kt) * kTileElems + (q * 16 + r) * 8 + e];
     const float xv = __uint_as_float((unsigned)v << 16);
     st_agent(a.x + (size_t)b * a.H + k, xv);
-    const float ss = group_sum(xv * xv, a.ssq_rows);
-    if (k % a.ssq_rows == 0) st_agent(a.ssq_out + (size_t)(k / a.ssq_rows) * a.Bmax + b, ss);
+    if (a.xo_hi != nullptr) split_hilo(xv * a.xo_gain[k], a.xo_hi, a.xo_lo, (size_t)b * a.H + k);
+    const float ss = group_sum(xv * xv, kSsqRows);
+    if (k % kSsqRows == 0) st_agent(a.ssq_out + (size_t)(k / kSsqRows) * a.Bmax + b, ss);
   }
   signal_done(done);
 }
 
+// Maximum over n (value, index) pairs per batch column (laid out [n][Bmax],
+// written in this launch), lowest index on ties.  tpc = 256/Bp threads per
+// column each merge every tpc-th pair with 16 loads in flight, then the
+// column's threads merge (the merge is order independent).  Returns true in
+// the one thread per column b < B that holds the result.  s_tmp: 8 words of
+// LDS.  Every thread of the workgroup must call it.
+__device__ inline bool merge_amax(const float* val, const int* idx, int n, int B, int Bmax,
+                                  float* s_tmp, float& bv, int& bi, int& b) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int Bp = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+  const int tpc = 256 / Bp;
+  b = tid / tpc;
+  const int p = tid - b * tpc;
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  if (b < B) {
+    for (int g0 = p; g0 < n; g0 += 16 * tpc) {
+      float v[16];
+      int ix[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int g = min(g0 + j * tpc, n - 1);
+        v[j] = ld_agent(val + (size_t)g * Bmax + b);
+        ix[j] = ld_agent(idx + (size_t)g * Bmax + b);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax_merge(bv, bi, v[j], ix[j]);
+    }
+  }
+  const int wl = tpc < 64 ? tpc : 64;
+  for (int m = 1; m < wl; m <<= 1) {
+    const float ov = __shfl_xor(bv, m);
+    const int oi = __shfl_xor(bi, m);
+    amax_merge(bv, bi, ov, oi);
+  }
+  if (tpc > 64) {  // a column spans several waves: merge them through LDS
+    int* s_ai = reinterpret_cast<int*>(s_tmp + 4);
+    __syncthreads();
+    if (lane == 0) { s_tmp[wave] = bv; s_ai[wave] = bi; }
+    __syncthreads();
+    if (p == 0)
+      for (int w2 = 1; w2 < tpc / 64; ++w2) amax_merge(bv, bi, s_tmp[wave + w2], s_ai[wave + w2]);
+  }
+  return p == 0 && b < B;
+}
+
 // ------------------------------------------------------------------ GEMV
 
-// LDS of a GEMV item: s_inv [64] f32 | s_res [64][NB] f32 | flag (16 B) |
-// input slice (fp32 [NB][Ks], or bf16 hi [NB][Ks+8] then lo [NB][Ks+8]).
+// LDS of a GEMV item: s_inv [64] f32 | s_ssq [256] f32 | s_res [64][NB] f32 |
+// flag (16 B) | input slice: VALU fp32 [NB][Ks], MFMA bf16 hi [NB][Ks+8]
+// then lo [NB][Ks+8].
 __host__ __device__ constexpr size_t gemv_head_bytes(int nb) {
-  return 256 + (size_t)kRowsPerGroup * nb * 4 + 16;
+  return 256 + 1024 + (size_t)kRowsPerGroup * nb * 4 + 16;
 }
 
 inline size_t gemv_lds_bytes_impl(int B, int kps) {
@@ -253,14 +309,22 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 // slice from w / rt on.  It streams its tiles with one 16-byte load per lane
 // per 1 KB tile and CH tiles in flight: the first CH go out before the item
 // waits for its input, and each later one as soon as the registers it lands
-// in are free.  The K slice of the input (times the RMSNorm gain) sits in LDS.
-//   NB <= 4 : VALU path, fp32 input, NB batch columns, fp32 FMA.
+// in are free.
+//   NB <= 4 : VALU path, fp32 FMA; the K slice of the input (times the
+//             RMSNorm gain) is staged in LDS.
 //   NB >= 16: MFMA path, NB/16 blocks of 16 batch columns,
 //             v_mfma_f32_16x16x32_bf16 with the weight tile as operand A and
 //             the input as a pair of bf16 (hi = bf16(x), lo = bf16(x - hi)),
 //             two MFMAs per tile: ~16 significant bits of input instead of 8
 //             (bf16 inputs alone move a 36-layer model's logits by ~2% of
-//             their maximum, beyond the step's 2e-2 tolerance).
+//             their maximum, beyond the step's 2e-2 tolerance).  The producer
+//             of the input wrote the pairs once (xh, xl: [64][K] bf16, times
+//             the RMSNorm gain); the item copies its K slice of them to LDS,
+//             once for its 4 row tiles (reading the B operand per wave from
+//             L2 instead would pass twice the weight bytes through each CU's
+//             load unit at 16 columns, one row tile per item).
+// Under RMSNorm each result row is scaled by 1/rms of its batch column at
+// the end, so the input does not wait for the producer's sums of squares.
 // Waves that share a row tile add their results in LDS in K order.  With
 // S > 1 splits of K, each item writes its partial rows and the last of the
 // row group's S items to arrive sums the partials in split order
@@ -272,8 +336,10 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   constexpr bool kMfma = NB >= 16;
   constexpr bool kAgent = Wait::kInLaunch;
   constexpr int NCB = kMfma ? NB / 16 : 1;
+  static_assert(!kMfma || !kAgent, "the MFMA path reads inputs of an earlier launch");
   float* s_inv = reinterpret_cast<float*>(smem);
-  float* s_res = s_inv + kMaxBatch;
+  float* s_ssq = s_inv + kMaxBatch;
+  float* s_res = s_ssq + 256;
   unsigned* s_flag = reinterpret_cast<unsigned*>(s_res + kRowsPerGroup * NB);
   unsigned char* xs_base = smem + gemv_head_bytes(NB);
 
@@ -289,8 +355,9 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   const int tj = wave % RT, kph = wave / RT;  // row tile in the item, K phase
   const int nkw = kph < nk ? (nk - kph + WS - 1) / WS : 0;  // k-tiles of this wave
   const int lastw = nkw > 0 ? nkw - 1 : 0;
+  const int kw0 = kt0 + min(kph, nk - 1);  // first k-tile of this wave
   const u32x4* wp = reinterpret_cast<const u32x4*>(w) +
-                    ((size_t)(rg * RT + tj) * KT + kt0 + min(kph, nk - 1)) * 64 + lane;
+                    ((size_t)(rg * RT + tj) * KT + kw0) * 64 + lane;
   const size_t wstep = (size_t)WS * 64;
 
   // Every load is issued unconditionally (tile index clamped to the wave's
@@ -303,29 +370,37 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   wait();
   __syncthreads();  // LDS of the previous item is free
 
-  // RMSNorm: the input is staged as x * gain and each result row is scaled
-  // by 1/rms of its batch column afterwards, so staging does not wait for
-  // the producer's partial sums of squares.  Those are loaded now (wave w
-  // takes columns w, w+4, ...; a lane takes every 64th group) and reduced
-  // after staging.
+  // RMSNorm sums of squares: one partial per 16 rows of the producer,
+  // [K/16][Bmax].  Thread t adds batch column t % NB's partials t / NB,
+  // t / NB + 256/NB, ... in order, 16 loads in flight, the first batch
+  // issued before the input is staged; the 256/NB parts are then added in
+  // order.
   const bool norm = a.ssq != nullptr;
-  constexpr int kSsqCols = (NB + 3) / 4;
-  constexpr int kSsqPer = kMfma ? 2 : 8;  // groups per lane: K/ssq_rows <= 64*kSsqPer
-  float ssv[kSsqCols][kSsqPer];
-  const int ng = a.K / a.ssq_rows;
+  constexpr int kParts = 256 / NB;
+  const int ng = a.K / kSsqRows;
+  const int sb = tid % NB, sp = tid / NB;
+  float sv[16];
   if (norm) {
 #pragma unroll
-    for (int j = 0; j < kSsqCols; ++j) {
-      const int b = min(wave + 4 * j, B - 1);
-#pragma unroll
-      for (int hh = 0; hh < kSsqPer; ++hh)
-        ssv[j][hh] = ld_in<kAgent>(a.ssq + (size_t)min(lane + 64 * hh, ng - 1) * a.Bmax + b);
-    }
+    for (int j = 0; j < 16; ++j)
+      sv[j] = ld_in<kAgent>(a.ssq + (size_t)min(sp + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1));
   }
 
   // Stage the input slice, 8 consecutive columns per thread and step.
   const int P = kMfma ? Ks + 8 : Ks;
-  {
+  if constexpr (kMfma) {
+    // copy the pairs of columns 0..NB-1 (columns >= B only feed unused
+    // outputs); hi rows first, then lo rows
+    const int K8 = Ks / 8, n = NB * K8;
+    unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
+    for (int idx = tid; idx < 2 * n; idx += 256) {
+      const int hl = idx >= n, rem = idx - hl * n;
+      const int b = rem / K8, c = (rem - b * K8) * 8;
+      const uint16_t* src = (hl ? a.xl : a.xh) + (size_t)b * a.K + kt0 * kTileCols + c;
+      *reinterpret_cast<u32x4*>(xs + hl * NB * P + b * P + c) =
+          *reinterpret_cast<const u32x4*>(src);
+    }
+  } else {
     const int K8 = Ks / 8;
     const float* grow = gain + kt0 * kTileCols;
     for (int idx = tid; idx < B * K8; idx += 256) {
@@ -336,40 +411,29 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
         v0 *= *reinterpret_cast<const f32x4*>(grow + c);
         v1 *= *reinterpret_cast<const f32x4*>(grow + c + 4);
       }
-      if constexpr (kMfma) {
-        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        unsigned hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[e] = f2bf(v[e]);
-          lo[e] = f2bf(v[e] - __uint_as_float(hi[e] << 16));
-        }
-        unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
-        *reinterpret_cast<u32x4*>(xs + b * P + c) =
-            u32x4{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16,
-                  hi[6] | hi[7] << 16};
-        *reinterpret_cast<u32x4*>(xs + NB * P + b * P + c) =
-            u32x4{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
-                  lo[6] | lo[7] << 16};
-      } else {
-        float* xs = reinterpret_cast<float*>(xs_base) + b * P + c;
-        *reinterpret_cast<f32x4*>(xs) = v0;
-        *reinterpret_cast<f32x4*>(xs + 4) = v1;
-      }
+      float* xs = reinterpret_cast<float*>(xs_base) + b * P + c;
+      *reinterpret_cast<f32x4*>(xs) = v0;
+      *reinterpret_cast<f32x4*>(xs + 4) = v1;
     }
   }
   if (norm) {
+    float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < kSsqCols; ++j) {
-      const int b = wave + 4 * j;
-      if (b < B) {
-        float ss = 0.f;
+    for (int j = 0; j < 16; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;
+    for (int g0 = sp + 16 * kParts; g0 < ng; g0 += 16 * kParts) {
 #pragma unroll
-        for (int hh = 0; hh < kSsqPer; ++hh) ss += lane + 64 * hh < ng ? ssv[j][hh] : 0.f;
-        ss = wave_sum(ss);
-        if (lane == 0) s_inv[b] = rsqrtf(ss / (float)a.K + a.eps);
-      }
+      for (int j = 0; j < 16; ++j)
+        sv[j] = ld_in<kAgent>(a.ssq + (size_t)min(g0 + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss += g0 + j * kParts < ng ? sv[j] : 0.f;
     }
+    s_ssq[tid] = ss;
+  }
+  __syncthreads();
+  if (norm && tid < B) {
+    float ss = 0.f;
+    for (int p = 0; p < kParts; ++p) ss += s_ssq[p * NB + tid];
+    s_inv[tid] = rsqrtf(ss / (float)a.K + a.eps);
   }
   __syncthreads();
 
@@ -488,14 +552,36 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       const int r = idx / B, b = idx - r * B;
       st_agent(mine + idx, s_res[r * NB + b]);
     }
-    if (!arrive_last(&a.counters[rg], (unsigned)S, s_flag)) return;
+    if (!arrive_last(&a.counters[(size_t)rg * kCntStride], (unsigned)S, s_flag)) return;
+    // sum the S partials of each output in split order; a thread keeps 4
+    // outputs x 8 splits of loads in flight (indices clamped, extras unused)
     const float* all = a.part + (size_t)rg * S * rows * B;
-    for (int idx = tid; idx < rows * B; idx += 256) {
-      const float sum = sum_strided(all + idx, S, (size_t)rows * B);
-      const int r = idx / B, b = idx - r * B;
-      s_res[r * NB + b] = sum;
+    const int n = rows * B;
+    constexpr int J = 4;
+    for (int i0 = tid; i0 < n; i0 += 256 * J) {
+      float acc[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) acc[j] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float v[J][8];
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            v[j][k] = ld_agent(all + (size_t)min(s0 + k, S - 1) * n + min(i0 + j * 256, n - 1));
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (s0 + k < S) acc[j] += v[j][k];
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int idx = i0 + j * 256;
+        if (idx < n) s_res[(idx / B) * NB + idx % B] = acc[j];
+      }
     }
-    if (tid == 0) reset_counter(&a.counters[rg]);
+    if (tid == 0) reset_counter(&a.counters[(size_t)rg * kCntStride]);
     __syncthreads();
   }
 
@@ -508,9 +594,9 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     signal_done(done);
   } else if constexpr (MODE == kResid) {
-    // new residual, and its sums of squares over groups of ssq_rows rows
-    // (ssq_rows divides rows and 64, so a lane group never spans two columns)
-    const int sr = a.ssq_rows;
+    // new residual, its sums of squares over groups of 16 rows (a group of
+    // 16 lanes never spans two batch columns), and for an MFMA consumer the
+    // bf16 pair of x times the consumer's RMSNorm gain
 #pragma unroll
     for (int j = 0; j < kXold; ++j) {
       const int idx = tid + j * 256;  // = b * rows + r
@@ -520,9 +606,12 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       if (ok) {
         xv = x_old[j] + s_res[r * NB + b];
         st_agent(a.out + (size_t)b * N + row0 + r, xv);
+        if (a.xo_hi != nullptr)
+          split_hilo(xv * a.xo_gain[row0 + r], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
       }
-      const float ss = group_sum(xv * xv, sr);
-      if (ok && r % sr == 0) st_agent(a.ssq_out + ((row0 + r) / sr) * a.Bmax + b, ss);
+      const float ss = group_sum(xv * xv, kSsqRows);
+      if (ok && r % kSsqRows == 0)
+        st_agent(a.ssq_out + ((row0 + r) / kSsqRows) * a.Bmax + b, ss);
     }
     signal_done(done);
   } else if constexpr (MODE == kSwiGLU) {
@@ -534,7 +623,9 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       const float gv = s_res[(j * 16 + i) * NB + b];
       const float uv = s_res[(j * 16 + 8 + i) * NB + b];
       const float sv = gv / (1.f + expf(-gv));
-      st_agent(a.out + (size_t)b * half + (size_t)rg * nch + c, sv * uv);
+      const size_t o = (size_t)b * half + (size_t)rg * nch + c;
+      st_agent(a.out + o, sv * uv);
+      if (a.xo_hi != nullptr) split_hilo(sv * uv, a.xo_hi, a.xo_lo, o);
     }
     signal_done(done);
   } else {  // kArgmax, rows == 64
@@ -553,44 +644,31 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
         st_agent(a.amax_idx + (size_t)rg * a.Bmax + b, bi);
       }
     }
-    const int NRG = N / rows;
-    if (!arrive_last(a.amax_counter, (unsigned)NRG, s_flag)) return;
-    // tpc threads per batch column, each merging every tpc-th row group's
-    // maximum with 16 loads in flight; the merge is order independent
-    const int Bp = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
-    const int tpc = 256 / Bp;
-    const int b = tid / tpc, p = tid - b * tpc;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    if (b < B) {
-      for (int g0 = p; g0 < NRG; g0 += 16 * tpc) {
-        float v[16];
-        int ix[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int g = min(g0 + j * tpc, NRG - 1);
-          v[j] = ld_agent(a.amax_val + (size_t)g * a.Bmax + b);
-          ix[j] = ld_agent(a.amax_idx + (size_t)g * a.Bmax + b);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) amax_merge(bv, bi, v[j], ix[j]);
+    // two levels of "last to arrive": groups of 64 row groups, then the
+    // groups (no single counter takes every row group's atomic)
+    const int NRG = N / rows, gq = rg / 64, ng2 = (NRG + 63) / 64;
+    const int in_group = min(64, NRG - gq * 64);
+    unsigned* cnt1 = a.amax_counter + (size_t)gq * kCntStride;
+    if (!arrive_last(cnt1, (unsigned)in_group, s_flag)) return;
+    {
+      float bv;
+      int bi, b;
+      if (merge_amax(a.amax_val + (size_t)gq * 64 * a.Bmax, a.amax_idx + (size_t)gq * 64 * a.Bmax,
+                     in_group, B, a.Bmax, s_res, bv, bi, b)) {
+        st_agent(a.amax_val2 + (size_t)gq * a.Bmax + b, bv);
+        st_agent(a.amax_idx2 + (size_t)gq * a.Bmax + b, bi);
       }
     }
-    const int wl = tpc < 64 ? tpc : 64;
-    for (int m = 1; m < wl; m <<= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      amax_merge(bv, bi, ov, oi);
+    if (tid == 0) reset_counter(cnt1);
+    unsigned* cnt2 = a.amax_counter + (size_t)ng2 * kCntStride;
+    if (!arrive_last(cnt2, (unsigned)ng2, s_flag)) return;
+    {
+      float bv;
+      int bi, b;
+      if (merge_amax(a.amax_val2, a.amax_idx2, ng2, B, a.Bmax, s_res, bv, bi, b))
+        a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
     }
-    if (tpc > 64) {  // a column spans several waves: merge them through LDS
-      int* s_ai = reinterpret_cast<int*>(s_res + 4);
-      if (lane == 0) { s_res[wave] = bv; s_ai[wave] = bi; }
-      __syncthreads();
-      if (p == 0)
-        for (int w2 = 1; w2 < tpc / 64; ++w2) amax_merge(bv, bi, s_res[wave + w2], s_ai[wave + w2]);
-    }
-    if (p == 0 && b < B) a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
-    if (tid == 0) reset_counter(a.amax_counter);
+    if (tid == 0) reset_counter(cnt2);
   }
 }
 
@@ -872,6 +950,7 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     }
     if (nsplit == 1) {
       st_agent(a.out + (qh0 + h) * D + d, o / L);
+      if (a.out_hi != nullptr) split_hilo(o / L, a.out_hi, a.out_lo, (qh0 + h) * D + d);
     } else {
       st_agent(a.o_part + ((qh0 + h) * S_max + s) * D + d, o);
       if (d == 0) {
@@ -885,7 +964,7 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     return;
   }
 
-  unsigned* cnt = &a.counters[(size_t)b * Hkv + g];
+  unsigned* cnt = &a.counters[((size_t)b * Hkv + g) * kCntStride];
   if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
@@ -920,6 +999,7 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
       M = Mc;
     }
     st_agent(a.out + (qh0 + h) * D + d, o / L);
+    if (a.out_hi != nullptr) split_hilo(o / L, a.out_hi, a.out_lo, (qh0 + h) * D + d);
   }
   if (tid == 0) reset_counter(cnt);
   signal_done(done);

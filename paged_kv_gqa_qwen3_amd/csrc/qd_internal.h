@@ -25,6 +25,9 @@ constexpr int kRowsPerGroup = 64;                  // rows one GEMV workgroup fi
 constexpr int kPage = 16;                          // tokens per KV page
 constexpr int kMaxBatch = 64;
 constexpr int kMaxTilesInFlight = 20;              // weight tiles a wave keeps in flight
+constexpr int kSsqRows = 16;    // rows per partial sum of squares of the residual stream
+constexpr int kCntStride = 32;  // words between arrival counters: one 128-byte line each
+                                // (atomics on one line serialise at the memory side)
 
 // Epilogues of the GEMV kernel.
 enum GemvMode : int {
@@ -43,19 +46,25 @@ struct GemvArgs {
   int N, K, B, Bmax;
   int S, kps;          // K split count and k-tiles per split
   int rt;              // row tiles per item: 1, 2 or 4
-  int ssq_rows;        // granularity (16 or 64 rows) of the sums of squares read and written
-  const float* x;      // input activations [B][K] fp32
-  const float* ssq;    // if non-null: RMSNorm the input; [K/ssq_rows][Bmax] partial sums of squares
+  const float* x;      // VALU input activations [B][K] fp32
+  const uint16_t* xh;  // MFMA input: bf16 pairs [64][K] of the input (times the RMSNorm gain)
+  const uint16_t* xl;
+  const float* ssq;    // if non-null: RMSNorm the input; [K/16][Bmax] partial sums of squares
   const float* gain;   // [K] RMSNorm gain
   float eps;
   float* part;         // split-K partials [items][16*rt][B] (kPartial: the consumer's input)
-  unsigned* counters;  // [N/(16*rt)] split-K arrival counters (zero between uses)
+  unsigned* counters;  // [N/(16*rt)] split-K arrival counters, kCntStride apart (zero between uses)
   float* out;          // kStore: [B][N]; kResid: x [B][N]; kSwiGLU: [B][N/2]
-  float* ssq_out;      // kResid: [N/ssq_rows][Bmax]
+  float* ssq_out;      // kResid: [N/16][Bmax]
+  uint16_t* xo_hi;     // kResid, kSwiGLU: if non-null, also the bf16 pairs [64][cols] of the
+  uint16_t* xo_lo;     // output (kResid: times xo_gain) for an MFMA consumer
+  const float* xo_gain;
   float* logits;       // kArgmax: [B][N] or null
-  float* amax_val;     // kArgmax (rt = 4): [N/64][Bmax]
-  int* amax_idx;       // kArgmax (rt = 4): [N/64][Bmax]
-  unsigned* amax_counter;
+  float* amax_val;     // kArgmax (rt = 4): [N/64][Bmax] row-group maxima
+  int* amax_idx;
+  float* amax_val2;    // kArgmax: [ceil(N/64/64)][Bmax] maxima of groups of 64 row groups
+  int* amax_idx2;
+  unsigned* amax_counter;  // kArgmax: ceil(N/64/64) + 1 counters, kCntStride apart
   int* next_ids;       // kArgmax: [B]
 };
 
@@ -78,8 +87,10 @@ struct AttnArgs {
   int S_max;               // splits per (sequence, KV head) the grid provides
   float* o_part;           // [B*Hq][S_max][D]
   float* ml_part;          // [B*Hq][S_max][2]  (running max, running sum)
-  unsigned* counters;      // [B*Hkv] split arrival counters (zero between uses)
+  unsigned* counters;      // [B*Hkv] split arrival counters, kCntStride apart (zero between uses)
   float* out;              // [B][Hq][D]
+  uint16_t* out_hi;        // if non-null: bf16 pairs of out for an MFMA consumer
+  uint16_t* out_lo;
   float* tap_q;            // optional [B][Hq][D] (after norm and RoPE, unscaled)
   float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
   int* dev_flags;
@@ -88,10 +99,12 @@ struct AttnArgs {
 struct EmbedArgs {
   const uint16_t* table;   // packed [V][H]
   int V, H, B, Bmax;
-  int ssq_rows;            // 16 or 64
   const int* tokens;
   float* x;                // [B][H]
-  float* ssq_out;          // [H/ssq_rows][Bmax]
+  float* ssq_out;          // [H/16][Bmax]
+  uint16_t* xo_hi;         // if non-null: bf16 pairs [64][H] of x times xo_gain
+  uint16_t* xo_lo;
+  const float* xo_gain;
   int* dev_flags;
 };
 
@@ -140,8 +153,8 @@ hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
-hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, int ssq_rows, const float* gain,
-                               int H, int B, int Bmax, float eps, float* out, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
+                               int B, int Bmax, float eps, float* out, hipStream_t s);
 
 // Persistent step: which (head_dim, group) shapes it is built for, the LDS
 // bytes it needs, the largest co-resident grid, and the cooperative launch.

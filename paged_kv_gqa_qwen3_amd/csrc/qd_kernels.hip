@@ -49,13 +49,13 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) { embed_item(a,
 
 // out[b][k] = x[b][k] * rsqrt(sum(ssq partials)/H + eps) * gain[k]
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const float* ssq,
-                                                           int ssq_rows, const float* gain, int H,
-                                                           int Bmax, float eps, float* out) {
+                                                           const float* gain, int H, int Bmax,
+                                                           float eps, float* out) {
   const int b = blockIdx.x;
   __shared__ float s_inv;
   if (threadIdx.x == 0) {
     float ss = 0.f;
-    for (int g = 0; g < H / ssq_rows; ++g) ss += ssq[(size_t)g * Bmax + b];
+    for (int g = 0; g < H / kSsqRows; ++g) ss += ssq[(size_t)g * Bmax + b];
     s_inv = rsqrtf(ss / (float)H + eps);
   }
   __syncthreads();
@@ -100,10 +100,10 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, int ssq_rows, const float* gain,
-                               int H, int B, int Bmax, float eps, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, x, ssq, ssq_rows, gain, H,
-                     Bmax, eps, out);
+hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
+                               int B, int Bmax, float eps, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(B), dim3(256), 0, s, x, ssq, gain, H, Bmax, eps,
+                     out);
   return hipGetLastError();
 }
 
@@ -186,15 +186,14 @@ size_t step_lds_bytes(int B, int head_dim, int group, int max_kps) {
   return att > gm ? att : gm;
 }
 
+// The persistent step serves batches <= 4 only.
 static hipError_t step_call(int B, int head_dim, int group, const StepArgs* a, int grid,
                             size_t lds, hipStream_t s, int* max_grid, int num_cus) {
   switch (gemv_nb(B)) {
     case 1: return step_dispatch<1>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
     case 2: return step_dispatch<2>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
     case 4: return step_dispatch<4>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    case 16: return step_dispatch<16>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    case 32: return step_dispatch<32>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    default: return step_dispatch<64>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -65,6 +65,9 @@ struct qd_handle {
   std::map<std::string, int> expected;  // name -> loaded (0/1)
 
   float *x = nullptr, *ssq = nullptr, *qkv = nullptr, *attn = nullptr, *act = nullptr;
+  // bf16 pairs [64][cols] for MFMA consumers (batch >= 5)
+  uint16_t *xg_hi = nullptr, *xg_lo = nullptr, *attn_hi = nullptr, *attn_lo = nullptr;
+  uint16_t *act_hi = nullptr, *act_lo = nullptr;
   float* part = nullptr;      // split partials of self-reducing projections (O, down, LM head)
   float* part_qkv = nullptr;  // split partials of QKV, summed by attention
   unsigned* gemv_cnt = nullptr;
@@ -72,6 +75,8 @@ struct qd_handle {
   unsigned* attn_cnt = nullptr;
   float* amax_val = nullptr;
   int* amax_idx = nullptr;
+  float* amax_val2 = nullptr;
+  int* amax_idx2 = nullptr;
   unsigned* amax_cnt = nullptr;
   int* dev_flags = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
@@ -129,25 +134,28 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
 // hand-off at batch 1.  The LM head keeps 64-row items (its argmax reduces
 // one partial per row group).
 // Batch >= 5 (MFMA items) and the persistent step: 64-row items, enough
-// workgroups to cover the chip twice, at most 20 tiles per wave unless the
-// row count alone fills the chip, and an LDS input slice <= 96 KB (72 KB in
-// the persistent step, which keeps two workgroups per CU).
+// workgroups to cover the chip twice (the persistent step: its grid), at
+// most 20 tiles per wave unless the row count alone fills the chip, and an
+// LDS input slice <= 48 KB so that three workgroups fit a CU (72 KB in the
+// persistent step).
 constexpr size_t kLdsCapValu = 80 * 1024;
-constexpr size_t kLdsCapStaged = 96 * 1024;
+constexpr size_t kLdsCapStaged = 48 * 1024;
 constexpr size_t kLdsCapPersistent = 72 * 1024;
 constexpr int kMinValuItems = 128;
 
-bool row_tile_items(const qd_handle* h, int B) { return !h->persistent && gemv_nb(B) <= 4; }
-
-// Rows per partial sum of squares of the residual stream at batch B.
-int ssq_rows_for(const qd_handle* h, int B) { return row_tile_items(h, B) ? 16 : 64; }
+// The persistent kernel serves batches <= 4 (VALU items); larger batches
+// always take the per-stage kernels.
+bool use_persistent(const qd_handle* h, int B) { return h->persistent && gemv_nb(B) <= 4; }
 
 GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
                    int grid = 0) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
   const int target = grid > 0 ? grid : 2 * h->num_cus;
+  const int nb = gemv_nb(B);
   GemvPlan p;
-  if (row_tile_items(h, B)) {
+  if (!use_persistent(h, B) && nb <= 4) {
+    // batch <= 4: one 16-row tile per item (the LM head: four), K split
+    // only when needed (LDS budget, or fewer than 128 items)
     p.rt = argmax ? 4 : 1;
     const int groups = N / (kTileRows * p.rt);
     for (int S = 1; S <= KT; ++S) {
@@ -160,8 +168,8 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
     }
     return p;
   }
-  const size_t cap = h->persistent ? kLdsCapPersistent : kLdsCapStaged;
-  if (h->persistent) {
+  const size_t cap = use_persistent(h, B) ? kLdsCapPersistent : kLdsCapStaged;
+  if (use_persistent(h, B)) {
     // The grid's workgroups share each stage: the split count minimises the
     // items of the busiest workgroup times the k-tiles of an item (rows
     // alone may give more row groups than workgroups), splits costing a
@@ -275,21 +283,31 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   const float eps = h->cfg.rms_eps;
   const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
 
-  const int sr = ssq_rows_for(h, B);
+  // MFMA consumers (batch >= 5) read bf16 pairs that each producer writes
+  // once: x times the next RMSNorm gain (xg), the attention output, act
+  const bool mfma = gemv_nb(B) >= 16;
   EmbedArgs ea{};
   ea.table = h->embed;
-  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch; ea.ssq_rows = sr;
+  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch;
   ea.tokens = sp.tokens; ea.x = h->x; ea.ssq_out = h->ssq; ea.dev_flags = h->dev_flags;
+  if (mfma) { ea.xo_hi = h->xg_hi; ea.xo_lo = h->xg_lo; ea.xo_gain = h->lw[0].in_norm; }
   HIP_TRY(h, launch_embed(ea, s));
   PROF(QD_PROF_EMBED);
 
-  auto gemv = [&](const uint16_t* w, int N, int K, const float* xin, const float* gain,
-                  int mode, float* out) -> hipError_t {
+  // xin_hl: the MFMA input pairs; out_hl/out_gain: pairs this projection
+  // writes for the next MFMA consumer
+  auto gemv = [&](const uint16_t* w, int N, int K, const float* xin, uint16_t* const* xin_hl,
+                  const float* gain, int mode, float* out, uint16_t* const* out_hl = nullptr,
+                  const float* out_gain = nullptr) -> hipError_t {
     GemvPlan p = plan_gemv(h, N, K, B, mode == kArgmax);
     GemvArgs a{};
     a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
-    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.ssq_rows = sr;
+    a.S = p.S; a.kps = p.kps; a.rt = p.rt;
     a.x = xin;
+    if (mfma) {
+      a.xh = xin_hl[0]; a.xl = xin_hl[1];
+      if (out_hl) { a.xo_hi = out_hl[0]; a.xo_lo = out_hl[1]; a.xo_gain = out_gain; }
+    }
     a.ssq = gain ? h->ssq : nullptr;
     a.gain = gain; a.eps = eps;
     a.part = h->part; a.counters = h->gemv_cnt;
@@ -297,10 +315,15 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     a.ssq_out = h->ssq;
     a.logits = sp.logits;
     a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
+  a.amax_val2 = h->amax_val2; a.amax_idx2 = h->amax_idx2;
+    a.amax_val2 = h->amax_val2; a.amax_idx2 = h->amax_idx2;
     a.next_ids = sp.next;
     return launch_gemv(a, mode, s);
   };
 
+  uint16_t* const xg[2] = {h->xg_hi, h->xg_lo};
+  uint16_t* const attn_hl[2] = {h->attn_hi, h->attn_lo};
+  uint16_t* const act_hl[2] = {h->act_hi, h->act_lo};
   const int smax = attn_splits(h, B);
   for (int l = 0; l < L; ++l) {
     const LayerW& w = h->lw[l];
@@ -315,12 +338,13 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     if (part_mode) {
       GemvArgs q{};
       q.w = w.qkv; q.N = h->NQKV; q.K = H; q.B = B; q.Bmax = h->cfg.max_batch;
-      q.S = pq.S; q.kps = pq.kps; q.rt = pq.rt; q.ssq_rows = sr;
+      q.S = pq.S; q.kps = pq.kps; q.rt = pq.rt;
       q.x = h->x; q.ssq = h->ssq; q.gain = w.in_norm;
+      if (mfma) { q.xh = h->xg_hi; q.xl = h->xg_lo; }
       q.eps = eps; q.part = h->part_qkv;
       HIP_TRY(h, launch_gemv(q, kPartial, s));
     } else {
-      HIP_TRY(h, gemv(w.qkv, h->NQKV, H, h->x, w.in_norm, kStore, h->qkv));
+      HIP_TRY(h, gemv(w.qkv, h->NQKV, H, h->x, xg, w.in_norm, kStore, h->qkv));
     }
     PROF(QD_PROF_QKV);
     if (tap && taps->qkv)
@@ -339,6 +363,7 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.S_max = smax;
     aa.o_part = h->o_part; aa.ml_part = h->ml_part; aa.counters = h->attn_cnt;
     aa.out = h->attn;
+    if (mfma) { aa.out_hi = h->attn_hi; aa.out_lo = h->attn_lo; }
     aa.tap_q = tap ? taps->q_rot : nullptr;
     aa.tap_k = tap ? taps->k_rot : nullptr;
     aa.dev_flags = h->dev_flags;
@@ -347,24 +372,25 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     if (tap && taps->attn)
       HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,
                                 hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, gemv(w.o, H, h->QD, h->attn, nullptr, kResid, h->x));
+    HIP_TRY(h, gemv(w.o, H, h->QD, h->attn, attn_hl, nullptr, kResid, h->x, xg, w.post_norm));
     PROF(QD_PROF_O);
     if (tap && taps->x_mid)
       HIP_TRY(h, hipMemcpyAsync(taps->x_mid, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, gemv(w.gu, 2 * h->I, H, h->x, w.post_norm, kSwiGLU, h->act));
+    HIP_TRY(h, gemv(w.gu, 2 * h->I, H, h->x, xg, w.post_norm, kSwiGLU, h->act, act_hl));
     PROF(QD_PROF_GATE_UP);
     if (tap && taps->act)
       HIP_TRY(h, hipMemcpyAsync(taps->act, h->act, sizeof(float) * B * h->I,
                                 hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, gemv(w.down, H, h->I, h->act, nullptr, kResid, h->x));
+    const float* next_gain = l + 1 < L ? h->lw[l + 1].in_norm : h->final_norm;
+    HIP_TRY(h, gemv(w.down, H, h->I, h->act, act_hl, nullptr, kResid, h->x, xg, next_gain));
     PROF(QD_PROF_DOWN);
     if (tap && taps->x_out)
       HIP_TRY(h, hipMemcpyAsync(taps->x_out, h->x, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s));
   }
   if (taps && taps->final_h)
-    HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, sr, h->final_norm, H, B, h->cfg.max_batch,
-                                   eps, taps->final_h, s));
-  HIP_TRY(h, gemv(h->lm, h->V, H, h->x, h->final_norm, kArgmax, nullptr));
+    HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, h->final_norm, H, B, h->cfg.max_batch, eps,
+                                   taps->final_h, s));
+  HIP_TRY(h, gemv(h->lm, h->V, H, h->x, xg, h->final_norm, kArgmax, nullptr));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
   return QD_OK;
@@ -375,7 +401,7 @@ GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const flo
   GemvPlan p = plan_gemv(h, N, K, sp.B, argmax, grid);
   GemvArgs a{};
   a.N = N; a.K = K; a.B = sp.B; a.Bmax = h->cfg.max_batch;
-  a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.ssq_rows = ssq_rows_for(h, sp.B);
+  a.S = p.S; a.kps = p.kps; a.rt = p.rt;
   a.x = xin;
   a.ssq = norm ? h->ssq : nullptr;
   a.eps = h->cfg.rms_eps;
@@ -384,6 +410,7 @@ GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const flo
   a.ssq_out = h->ssq;
   a.logits = sp.logits;
   a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
+  a.amax_val2 = h->amax_val2; a.amax_idx2 = h->amax_idx2;
   a.next_ids = sp.next;
   return a;
 }
@@ -419,7 +446,6 @@ int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.embed.V = h->V; a.embed.H = H; a.embed.B = B; a.embed.Bmax = h->cfg.max_batch;
   a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
   a.embed.dev_flags = h->dev_flags;
-  a.embed.ssq_rows = ssq_rows_for(h, B);
   a.qkv = gemv_template(h, sp, h->NQKV, H, h->x, true, h->qkv, grid);
   a.o = gemv_template(h, sp, H, h->QD, h->attn, false, h->x, grid);
   a.gu = gemv_template(h, sp, 2 * h->I, H, h->x, true, h->act, grid);
@@ -560,10 +586,22 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
 
   // activations and scratch
   if ((rc = dev_alloc(h, &h->x, (size_t)Bm * H))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / kTileRows) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->ssq, (size_t)(H / kSsqRows) * Bm))) return bail(rc);
   if ((rc = dev_alloc(h, &h->qkv, (size_t)Bm * h->NQKV))) return bail(rc);
   if ((rc = dev_alloc(h, &h->attn, (size_t)Bm * h->QD))) return bail(rc);
   if ((rc = dev_alloc(h, &h->act, (size_t)Bm * I))) return bail(rc);
+  if (gemv_nb(Bm) >= 16) {
+    // MFMA operands cover whole blocks of 16 batch columns: rows up to the
+    // block are allocated and zeroed (rows >= B only feed unused outputs)
+    const size_t rows = (size_t)gemv_nb(Bm);
+    uint16_t** bufs[6] = {&h->xg_hi, &h->xg_lo, &h->attn_hi, &h->attn_lo, &h->act_hi, &h->act_lo};
+    const size_t cols[6] = {(size_t)H, (size_t)H, (size_t)h->QD, (size_t)h->QD, (size_t)I, (size_t)I};
+    for (int i = 0; i < 6; ++i) {
+      if ((rc = dev_alloc(h, bufs[i], rows * cols[i]))) return bail(rc);
+      e = hipMemset(*bufs[i], 0, rows * cols[i] * sizeof(uint16_t));
+      if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+    }
+  }
   // split partials: N * S * B floats for whichever projection needs most;
   // arrival counters: one per row group, at most N / 16
   size_t part_elems = 1, part_qkv_elems = 1;
@@ -571,7 +609,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   for (int B = 1; B <= Bm; ++B) {
     // the same plans the steps will use (persistent plans depend on the grid)
     int grid = 0;
-    if (h->persistent && (rc = persistent_grid(h, B, &grid))) return bail(rc);
+    if (use_persistent(h, B) && (rc = persistent_grid(h, B, &grid))) return bail(rc);
     const int dims[3][2] = {{H, h->QD}, {H, I}, {2 * I, H}};
     for (auto& d : dims) {
       GemvPlan p = plan_gemv(h, d[0], d[1], B, false, grid);
@@ -584,20 +622,23 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   }
   if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg * kCntStride))) return bail(rc);
   h->smax1 = attn_splits(h, 1);
   size_t att_rows = 0;
   for (int B = 1; B <= Bm; ++B) att_rows = std::max(att_rows, (size_t)B * h->Hq * attn_splits(h, B));
   if ((rc = dev_alloc(h, &h->o_part, att_rows * h->D))) return bail(rc);
   if ((rc = dev_alloc(h, &h->ml_part, att_rows * 2))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->attn_cnt, (size_t)Bm * h->Hkv))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->amax_val, (size_t)(V / kRowsPerGroup) * Bm))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->amax_idx, (size_t)(V / kRowsPerGroup) * Bm))) return bail(rc);
-  if ((rc = dev_alloc(h, &h->amax_cnt, 1))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->attn_cnt, (size_t)Bm * h->Hkv * kCntStride))) return bail(rc);
+  const size_t nrg_v = V / kRowsPerGroup, ng2_v = (nrg_v + 63) / 64;
+  if ((rc = dev_alloc(h, &h->amax_val, nrg_v * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_idx, nrg_v * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_val2, ng2_v * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_idx2, ng2_v * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->amax_cnt, (ng2_v + 1) * kCntStride))) return bail(rc);
   if ((rc = dev_alloc(h, &h->dev_flags, 1))) return bail(rc);
-  e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg);
-  if (e == hipSuccess) e = hipMemset(h->attn_cnt, 0, sizeof(unsigned) * Bm * h->Hkv);
-  if (e == hipSuccess) e = hipMemset(h->amax_cnt, 0, sizeof(unsigned));
+  e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg * kCntStride);
+  if (e == hipSuccess) e = hipMemset(h->attn_cnt, 0, sizeof(unsigned) * Bm * h->Hkv * kCntStride);
+  if (e == hipSuccess) e = hipMemset(h->amax_cnt, 0, sizeof(unsigned) * (ng2_v + 1) * kCntStride);
   if (e == hipSuccess) e = hipMemset(h->dev_flags, 0, sizeof(int));
   if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
 
@@ -741,7 +782,7 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   if (rc) return rc;
   StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits};
-  if (h->persistent) return run_persistent(h, sp, h->stream);
+  if (use_persistent(h, batch)) return run_persistent(h, sp, h->stream);
   static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
   if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);
 

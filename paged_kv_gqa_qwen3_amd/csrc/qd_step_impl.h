@@ -35,7 +35,7 @@ __device__ __forceinline__ int gemv_items(const GemvArgs& g) { return gemv_row_g
 // its items in step order, so the step always makes progress when every
 // workgroup is resident (the cooperative launch guarantees it).
 template <int NB, int D, int G>
-__global__ __launch_bounds__(256, 2) void step_kernel(const StepArgs a) {
+__global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const long nwg = gridDim.x, wg = blockIdx.x;
   long base = 0;

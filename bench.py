@@ -42,17 +42,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("qd_device.h", "qd_kernels.hip")
+
+
+def kernel_source_sha256():
+    """sha256 over the device-code sources of the per-stage kernels, in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(REPO, "paged_kv_gqa_qwen3_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel_class, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
-    import hashlib
-
     path = os.path.join(REPO, "profiles", f"traffic_{workload}.json")
-    src = os.path.join(REPO, "paged_kv_gqa_qwen3_amd", "csrc", "qd_kernels.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return rec.get("traffic_bytes_per_launch", {}).get(kernel_class)
 
@@ -253,23 +263,32 @@ def main():
             log(f"[bench] {w.name}: {tok_s:.1f} tok/s, {ms / args.steps:.4f} ms/step, "
                 f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
             if w.name == HEADLINE:
+                # Projections: each class's launches for all layers replayed
+                # alone as a graph between two events on the library's stream
+                # (avg_us).  Every class, attention included: the step run
+                # with an event between kernels (events_us; event records add
+                # a few us per kernel).
                 prof = profile_classes(torch, dec, run)
                 ctx_mid = batch.positions.astype(np.int64) + 1
                 per_class = {}
                 for c, (tot_ms, n) in prof.items():
                     if n == 0:
                         continue
-                    avg_us = tot_ms / n * 1e3
+                    ev_us = tot_ms / n * 1e3
                     if c in ("qkv", "o_proj", "gate_up", "down", "lm_head"):
                         byts = gemv_bytes(shape, c)
+                        avg_us = binding.qd_profile_class(dec.handle, w.batch, c, reps=20)
                     elif c == "attention":
                         byts = attention_bytes(shape, ctx_mid)
+                        avg_us = ev_us
                     else:
                         byts = w.batch * shape.hidden * 2
+                        avg_us = ev_us
                     per_class[c] = {"launches_per_step": n // 5, "avg_us": round(avg_us, 3),
+                                    "events_us": round(ev_us, 3),
                                     "bytes_per_launch": int(byts),
                                     "GBps": round(byts / (avg_us * 1e-6) / 1e9, 1),
-                                    "ms_per_step": round(tot_ms / 5, 4)}
+                                    "ms_per_step": round(avg_us * (n // 5) / 1e3, 4)}
                 dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
                 d = per_class[dom]
                 headline_extra = {

@@ -155,15 +155,29 @@ int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
 #define QD_PROF_LM_HEAD 6  /* final RMSNorm + LM head + argmax */
 #define QD_PROF_CLASSES 7
 
-/* Run one step eagerly with a HIP event recorded on the handle's stream
- * between consecutive kernels, and return per class the summed kernel time
- * in milliseconds (class_ms[QD_PROF_CLASSES]) and the number of launches
+/* Run the step as the per-stage kernels twice on the handle's stream, the
+ * second time with a HIP event between consecutive kernels (enqueued while
+ * the GPU runs the first, so its kernels run back to back), and return per
+ * class the summed time between the events around its kernels in
+ * milliseconds (class_ms[QD_PROF_CLASSES]) and the number of launches
  * (class_launches[QD_PROF_CLASSES]).  Same arguments and effects as
- * qd_decode_step.  Synchronous. */
+ * qd_decode_step (the repeat rewrites the same KV slots with the same
+ * values).  Synchronous. */
 int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
                     const int32_t* positions, const int32_t* block_tables, void* kv_pool,
                     int32_t* out_next_ids, float* out_logits, float* class_ms,
                     int32_t* class_launches);
+
+/* Time one projection class alone (QD_PROF_QKV, _O, _GATE_UP, _DOWN or
+ * _LM_HEAD): its kernels for every layer (the LM head: once), launched as in
+ * qd_decode_step at this batch size with the real per-layer weights, are
+ * captured into a graph that is replayed `reps` times between two HIP events
+ * on the handle's stream; *avg_us is the mean time per launch.  Inputs are
+ * whatever the handle's scratch activations hold; the kernels overwrite that
+ * scratch (the next qd_decode_step recomputes it) and touch no caller
+ * buffer and no KV pool.  QD_EUNSUPPORTED for the other classes.
+ * Synchronous. */
+int qd_profile_class(qd_handle* h, int32_t batch, int32_t cls, int32_t reps, float* avg_us);
 
 /* Wait for the handle's stream, then return (and clear) the QD_DEV_* bits
  * the kernels recorded since the last call in *flags.  Synchronous. */

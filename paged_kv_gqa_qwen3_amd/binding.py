@@ -28,7 +28,8 @@ QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
-            "qd_profile_step", "qd_device_status", "qd_stream", "qd_destroy", "qd_last_error")
+            "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream", "qd_destroy",
+            "qd_last_error")
 
 PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
 
@@ -87,6 +88,9 @@ def load_library():
         lib.qd_profile_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
                                         ctypes.POINTER(ctypes.c_float),
                                         ctypes.POINTER(ctypes.c_int32)]
+        lib.qd_profile_class.restype = ctypes.c_int
+        lib.qd_profile_class.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float)]
         lib.qd_device_status.restype = ctypes.c_int
         lib.qd_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
         lib.qd_stream.restype = P
@@ -179,6 +183,15 @@ def qd_profile_step(handle: int, batch: int, token_ids, positions, block_tables,
                                _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
                                _ptr(out_logits), ms, cnt), handle)
     return {PROF_CLASSES[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def qd_profile_class(handle: int, batch: int, cls: str, reps: int = 20) -> float:
+    """Mean microseconds per launch of one projection class replayed alone."""
+    lib = load_library()
+    v = ctypes.c_float(0.0)
+    _check(lib.qd_profile_class(handle, batch, PROF_CLASSES.index(cls), reps, ctypes.byref(v)),
+           handle)
+    return float(v.value)
 
 
 def qd_device_status(handle: int) -> int:

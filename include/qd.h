@@ -58,7 +58,7 @@ typedef struct qd_handle qd_handle;
 /* Model and capacity.  Shapes follow the HF Qwen3 config names. */
 typedef struct qd_config {
   int32_t num_layers;          /* L */
-  int32_t hidden;              /* H; multiple of 64 */
+  int32_t hidden;              /* H; multiple of 64, at most 8192 */
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv; Hq / Hkv is 1, 2 or 4 */
   int32_t head_dim;            /* D; 64 or 128 */
@@ -69,12 +69,13 @@ typedef struct qd_config {
   double rope_theta;           /* RoPE base (Qwen3: 1e6) */
   int32_t page_size;           /* tokens per KV page; must be 16 */
   int32_t max_batch;           /* largest batch passed to qd_decode_step (1..64) */
-  int32_t max_pages_per_seq;   /* block-table row length */
+  int32_t max_pages_per_seq;   /* block-table row length; at most 4096 (65536 tokens) */
   int32_t num_pages;           /* pages in the caller's pool */
   int32_t use_graphs;          /* 1: replay one captured hipGraph per batch size */
-  int32_t persistent;          /* 1: run each step as one persistent cooperative kernel
-                                  (head_dim 128 with 4 query heads per KV head, or
-                                  head_dim 64 with 2); otherwise one kernel per stage */
+  int32_t persistent;          /* 1: run each step of batch <= 4 as one persistent
+                                  cooperative kernel (head_dim 128 with 4 query heads per
+                                  KV head, or head_dim 64 with 2); larger batches, and
+                                  other shapes, take the per-stage kernels */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a

@@ -674,127 +674,232 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
 
 // ------------------------------------------------------------------ attention
 
-template <int D, int G>
+// LDS of an attention item with NW waves.  part (partial q.k sums of the
+// page being scored) and acc (the waves' outputs, for the final merge) are
+// never live at the same time.
+template <int D, int G, int NW>
 struct AttnSmem {
   static constexpr int LPT = D / 8;       // lanes per token row in one 1 KB load
   static constexpr int TPI = 64 / LPT;    // tokens per load
   static constexpr int NI = kPage / TPI;  // loads per 16-token tile
   static constexpr int NV = NI * G;       // partial scores per lane per page
-  float part[4][NV][64];
-  float acc[4][G * 8][64];
+  static constexpr int ACC = G * 8 + 1;  // per-lane accumulators, padded against bank conflicts
+  union {
+    float part[NW][NV][64];
+    float acc[NW][64][ACC];  // every lane's G x 8 output partials
+    float ml[2][G][kMaxSplitsStaged];  // combine: (max, sum) of the splits
+  };
   alignas(16) float q[G][D];
-  float p[4][64];
-  float m[4][G], l[4][G];
+  float p[NW][64];
+  float m[NW][G], l[NW][G];
+  float wsc[NW][G];        // per-wave rescale factors of the merge
+  float mx[G], lsum[G];    // per head: overall max and sum of the item (or of all splits)
   alignas(16) unsigned short k[D];
   alignas(16) unsigned short v[D];
   unsigned flag;
 };
 
-// One item per (sequence b, KV head g, split s).  Fuses, for the step's
-// token: RMSNorm of the G query heads and of the KV head over head_dim, NeoX
-// RoPE at the token's position, and the bf16 append of k and v into the pool
-// (by the split that owns the last page); then paged attention of the G
-// query heads over the split's pages (K/V read once for the whole group),
-// online softmax, and the log-sum-exp combine of the splits by the last
-// split to arrive.  The split count is derived on the device from the
-// position, so one launch shape (and one captured graph) serves every context.
+// Pages one split of a sequence covers: every wave of an NW-wave workgroup
+// holds PW pages in flight.
+template <int NW, int PW>
+__host__ __device__ constexpr int attn_pages_per_split() { return NW * PW; }
+
+// The attention work of one step, held in registers by every wave: lane b
+// (< B) has sequence b's position (clamped; an out-of-range one is flagged),
+// its split count and its range [first, end) of item numbers.  Items are
+// numbered sequence by sequence, (KV head, split) inside, so the count
+// follows from the positions and no launch slot goes to an item that does
+// not exist.
+struct AttnList {
+  int pos, nsplit, first, end;
+};
+
+template <int PPS>
+__device__ inline AttnList attn_list(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  AttnList l{0, 0, 0, 0};
+  int items = 0;
+  if (lane < a.B) {
+    int pos = a.positions[lane];
+    const int pos_lim = min(a.max_pages * kPage, a.max_pos);
+    if (pos < 0 || pos >= pos_lim) {
+      if (threadIdx.x == lane) set_flag(a.dev_flags, QD_DEV_BAD_POSITION);
+      pos = pos < 0 ? 0 : pos_lim - 1;
+    }
+    const int npages = (pos + 1 + kPage - 1) / kPage;
+    l.pos = pos;
+    l.nsplit = (npages + PPS - 1) / PPS;
+    items = a.Hkv * l.nsplit;
+  }
+  int inc = items;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int v = __shfl_up(inc, m);
+    if (lane >= m) inc += v;
+  }
+  l.end = inc;
+  l.first = inc - items;
+  return l;
+}
+
+// Items of the step (the same in every wave).
+__device__ __forceinline__ int attn_items(const AttnList& l, int B) { return __shfl(l.end, B - 1); }
+
+// One item per (sequence b, KV head g, split s) of NW waves.  Fuses, for the
+// step's token: RMSNorm of the G query heads and of the KV head over
+// head_dim, NeoX RoPE at the token's position, and the bf16 append of k and
+// v into the pool (by the split that owns the last page); then paged
+// attention of the G query heads over the split's pages (K/V read once for
+// the whole group), online softmax per wave, the waves merged in LDS, and
+// for contexts longer than one split the log-sum-exp combine of the splits
+// by the last split to arrive.
+//
+// A split covers NW*PW pages (page s*NW*PW + w + NW*j for wave w, j < PW):
+// each wave issues all of its pages' K/V loads at once, before waiting for
+// the q, k, v inputs.
 //
 // Within a wave, a 16-token page tile of K (or V) for one head is NI loads of
 // 1 KB: in load i lane l holds token i*TPI + l/LPT, dims (l%LPT)*8 .. +8.
-template <int D, int G, class Wait>
-__device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
-                                      const float* k_gain, uint16_t* pool_layer,
-                                      const Done& done, int item, unsigned char* smem,
-                                      const Wait& wait) {
-  using SM = AttnSmem<D, G>;
+template <int D, int G, int NW, int PW, class Wait>
+__device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
+                                      const float* q_gain, const float* k_gain,
+                                      uint16_t* pool_layer, const Done& done, int item,
+                                      unsigned char* smem, const Wait& wait) {
+  using SM = AttnSmem<D, G, NW>;
   constexpr bool kAgent = Wait::kInLaunch;
   constexpr int LPT = SM::LPT, TPI = SM::TPI, NI = SM::NI;
   constexpr int HALF = D / 2;
+  constexpr int PPS = attn_pages_per_split<NW, PW>();
   static_assert(16 * G <= 64, "at most 4 query heads per KV head");
   SM& sm = *reinterpret_cast<SM*>(smem);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int S_max = a.S_max;
-  const int s = item % S_max;
-  const int bg = item / S_max;
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
-
-  int pos = a.positions[b];
-  const int pos_lim = min(a.max_pages * kPage, a.max_pos);
-  if (pos < 0 || pos >= pos_lim) {
-    if (tid == 0 && s == 0 && g == 0) set_flag(a.dev_flags, QD_DEV_BAD_POSITION);
-    pos = pos < 0 ? 0 : pos_lim - 1;
-  }
+  const int Hq = a.Hq, Hkv = a.Hkv;
+  // this item's sequence: the lane whose item range holds it
+  const unsigned long long mine =
+      __ballot(lane < a.B && item >= list.first && item < list.end);
+  const int b = __ffsll((long long)mine) - 1;
+  const int pos = __shfl(list.pos, b);
+  const int nsplit = __shfl(list.nsplit, b);
+  const int u = item - __shfl(list.first, b);
+  const int g = u % Hkv, s = u / Hkv;
   const int ctx = pos + 1;
   const int npages = (ctx + kPage - 1) / kPage;
-  int pps = (npages + S_max - 1) / S_max;
-  if (pps < kMinPagesPerSplit) pps = kMinPagesPerSplit;
-  const int nsplit = (npages + pps - 1) / pps;
-  if (s >= nsplit) return;
-  const int pg0 = s * pps, pg1 = min(npages, pg0 + pps);
   const int* bt = a.block_tables + (size_t)b * a.max_pages;
-  const int Hq = a.Hq, Hkv = a.Hkv;
-  const float* row = a.qkv + (size_t)b * (Hq + 2 * Hkv) * D;  // unused with qkv_part
   const size_t head_stride = (size_t)kPage * D;  // one (page, K|V, head) tile
+  const int pg0 = s * PPS;
+  const bool act = lane < HALF;
+  constexpr int HPW = (G + 2 + NW - 1) / NW;  // q/k/v heads per wave in the prologue
 
-  // The cached K/V pages do not depend on this step's projections: the
-  // wave's first page is loaded before waiting for them.
-  auto page_ptr = [&](int pg, int kv) {
-    int phys = bt[pg];
-    if (phys < 0 || phys >= a.num_pages) {
-      if (lane == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
-      phys = 0;
-    }
-    return reinterpret_cast<const u32x4*>(
-        pool_layer + (((size_t)phys * 2 + kv) * Hkv + g) * head_stride);
+  // Loads are issued in dependency order (they complete in order for the
+  // wait counter): the block-table entries of the wave's pages, the inputs
+  // of its q/k/v heads and their gains and the RoPE row, then the K/V pages.
+  int phys[PW];
+#pragma unroll
+  for (int j = 0; j < PW; ++j) phys[j] = bt[min(pg0 + wave + NW * j, npages - 1)];
+
+  // q/k/v head hh = wave + NW*u of the group: rows off..off+D of the QKV
+  // projection; lane takes dims lane and lane + D/2.  The split partials
+  // (up to 8) are loaded now and summed in order in the prologue.
+  // (Inside the persistent kernel the projection is produced by the same
+  // launch, so these loads wait for it: see load_inputs below.)
+  auto head_row = [&](int hh) {
+    return hh < G ? (g * G + hh) * D : hh == G ? Hq * D + g * D : (Hq + Hkv) * D + g * D;
   };
-  u32x4 kr[NI], vr[NI];
-  {
-    const int pg = min(pg0 + wave, pg1 - 1);
-    const u32x4* kp = page_ptr(pg, 0);
-    const u32x4* vp = page_ptr(pg, 1);
+  const bool early = a.qkv_part == nullptr || a.qkv_S <= 8;
+  float xp1[HPW][8], xp2[HPW][8], gn1[HPW], gn2[HPW];
+  auto load_inputs = [&]() {
+#pragma unroll
+    for (int uu = 0; uu < HPW; ++uu) {
+      const int hh = min(wave + NW * uu, G + 1);
+      const int off = head_row(hh);
+      const int l2 = act ? lane : 0;
+      if (a.qkv_part != nullptr) {
+        if (early) {
+          const int rows = a.qkv_rows, S = a.qkv_S;
+          const int n1 = off + l2, n2 = off + l2 + HALF;
+          const float* p1 = a.qkv_part + ((size_t)(n1 / rows) * S * rows + n1 % rows) * a.B + b;
+          const float* p2 = a.qkv_part + ((size_t)(n2 / rows) * S * rows + n2 % rows) * a.B + b;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            xp1[uu][j] = ld_in<kAgent>(p1 + (size_t)min(j, S - 1) * rows * a.B);
+            xp2[uu][j] = ld_in<kAgent>(p2 + (size_t)min(j, S - 1) * rows * a.B);
+          }
+        }
+      } else {
+        const float* row = a.qkv + (size_t)b * (Hq + 2 * Hkv) * D;
+        xp1[uu][0] = ld_in<kAgent>(row + off + l2);
+        xp2[uu][0] = ld_in<kAgent>(row + off + l2 + HALF);
+      }
+    }
+  };
+  if constexpr (!kAgent) load_inputs();  // written by an earlier launch
+#pragma unroll
+  for (int uu = 0; uu < HPW; ++uu) {
+    const int hh = min(wave + NW * uu, G + 1);
+    const float* gain = hh < G ? q_gain : k_gain;
+    const int l2 = act ? lane : 0;
+    gn1[uu] = gain[l2];
+    gn2[uu] = gain[l2 + HALF];
+  }
+  const float cs1 = a.rope_cos[(size_t)pos * HALF + (act ? lane : 0)];
+  const float sn1 = a.rope_sin[(size_t)pos * HALF + (act ? lane : 0)];
+
+  // --- the cached K/V pages of this wave (they do not depend on this
+  // step's projections, so they go out before the wait).  Every load is
+  // issued unconditionally: a page past the context repeats the last page
+  // (its scores are masked), so no wait is forced between pages.
+  u32x4 kr[PW][NI], vr[PW][NI];
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    const int pg = pg0 + wave + NW * j;
+    int ph = phys[j];
+    if (ph < 0 || ph >= a.num_pages) {
+      if (lane == 0 && pg < npages) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
+      ph = 0;
+    }
+    const u32x4* kp = reinterpret_cast<const u32x4*>(
+        pool_layer + (((size_t)ph * 2 + 0) * Hkv + g) * head_stride);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(
+        pool_layer + (((size_t)ph * 2 + 1) * Hkv + g) * head_stride);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kr[i] = __builtin_nontemporal_load(kp + i * 64 + lane);
-      vr[i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+      kr[j][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
+      vr[j][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
     }
   }
 
   wait();
   __syncthreads();  // LDS of the previous item is free
+  if constexpr (kAgent) load_inputs();  // written in this launch: after the wait
 
-  // --- q/k RMSNorm + RoPE, v to bf16 (wave w takes heads w, w+4, ...)
-  for (int hh = wave; hh < G + 2; hh += 4) {
-    int off;  // first row of this head in the QKV projection
-    const float* gain = nullptr;
-    if (hh < G) {
-      off = (g * G + hh) * D;
-      gain = q_gain;
-    } else if (hh == G) {
-      off = Hq * D + g * D;
-      gain = k_gain;
-    } else {
-      off = (Hq + Hkv) * D + g * D;
-    }
-    const bool act = lane < HALF;
+  // --- q/k RMSNorm + RoPE, v to bf16 (wave w takes heads w, w+NW, ...)
+#pragma unroll
+  for (int uu = 0; uu < HPW; ++uu) {
+    const int hh = wave + NW * uu;
+    if (hh >= G + 2) break;  // wave-uniform
     float x1 = 0.f, x2 = 0.f;
-    if (act) {
-      if (a.qkv_part != nullptr) {
-        x1 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + lane, b);
-        x2 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + lane + HALF, b);
-      } else {
-        x1 = ld_in<kAgent>(row + off + lane);
-        x2 = ld_in<kAgent>(row + off + lane + HALF);
-      }
+    if (a.qkv_part == nullptr) {
+      x1 = xp1[uu][0];
+      x2 = xp2[uu][0];
+    } else if (early) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < a.qkv_S) { x1 += xp1[uu][j]; x2 += xp2[uu][j]; }
+    } else {
+      const int off = head_row(hh), l2 = act ? lane : 0;
+      x1 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + l2, b);
+      x2 = split_sum<kAgent>(a.qkv_part, a.qkv_S, a.B, a.qkv_rows, off + l2 + HALF, b);
     }
-    if (gain != nullptr) {
+    if (!act) { x1 = 0.f; x2 = 0.f; }
+    if (hh <= G) {  // q heads and k: RMSNorm over head_dim, gain, RoPE
       const float ss = wave_sum(x1 * x1 + x2 * x2);
       const float inv = rsqrtf(ss / (float)D + a.eps);
       if (act) {
-        const float y1 = x1 * inv * gain[lane], y2 = x2 * inv * gain[lane + HALF];
-        const float c = a.rope_cos[(size_t)pos * HALF + lane];
-        const float sn = a.rope_sin[(size_t)pos * HALF + lane];
-        const float r1 = y1 * c - y2 * sn, r2 = y2 * c + y1 * sn;
+        const float y1 = x1 * inv * gn1[uu], y2 = x2 * inv * gn2[uu];
+        const float r1 = y1 * cs1 - y2 * sn1, r2 = y2 * cs1 + y1 * sn1;
         if (hh < G) {
           sm.q[hh][lane] = r1 * a.scale;
           sm.q[hh][lane + HALF] = r2 * a.scale;
@@ -828,11 +933,11 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
                      (size_t)(pos % kPage) * D;
       uint16_t* vd = pool_layer + (((size_t)page * 2 + 1) * Hkv + g) * head_stride +
                      (size_t)(pos % kPage) * D;
-      for (int i = tid; i < D; i += 256) { kd[i] = sm.k[i]; vd[i] = sm.v[i]; }
+      for (int i = tid; i < D; i += NW * 64) { kd[i] = sm.k[i]; vd[i] = sm.v[i]; }
     }
   }
 
-  // --- paged attention over this split's pages, page pg0+wave, +4, ...
+  // --- paged attention over this wave's pages
   const int dch = lane % LPT;
   float acc[G][8];
 #pragma unroll
@@ -842,26 +947,20 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
   float m_run = -INFINITY, l_run = 0.f;  // softmax state of head (lane % G)
   const u32x4 kcur = *reinterpret_cast<const u32x4*>(&sm.k[dch * 8]);
   const u32x4 vcur = *reinterpret_cast<const u32x4*>(&sm.v[dch * 8]);
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
-  for (int pg = pg0 + wave; pg < pg1; pg += 4) {
-    if (pg != pg0 + wave) {
-      const u32x4* kp = page_ptr(pg, 0);
-      const u32x4* vp = page_ptr(pg, 1);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kr[i] = __builtin_nontemporal_load(kp + i * 64 + lane);
-        vr[i] = __builtin_nontemporal_load(vp + i * 64 + lane);
-      }
-    }
+  for (int j = 0; j < PW; ++j) {
+    const int pg = pg0 + wave + NW * j;
+    if (pg >= npages) break;  // wave-uniform (pages past the context were loaded, not used)
     // partial q.k over this lane's 8 dims, for its NI tokens and G heads
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = pg * kPage + i * TPI + lane / LPT;
-      if (tok == pos) { kr[i] = kcur; vr[i] = vcur; }
-      if (tok >= ctx) { kr[i] = zero4; vr[i] = zero4; }
+      u32x4 kk = kr[j][i];
+      if (tok == pos) { kk = kcur; vr[j][i] = vcur; }
+      if (tok >= ctx) { kk = zero4; vr[j][i] = zero4; }
       float kf[8];
-      unpack8(kr[i], kf);
+      unpack8(kk, kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const f32x4 q0 = *reinterpret_cast<const f32x4*>(&sm.q[h][dch * 8]);
@@ -882,8 +981,8 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
       const float* src = &sm.part[wave][(t / TPI) * G + h][(t % TPI) * LPT];
       float sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < LPT; j += 4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + j);
+      for (int jj = 0; jj < LPT; jj += 4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + jj);
         sum += v4.x; sum += v4.y; sum += v4.z; sum += v4.w;
       }
       if (pg * kPage + t < ctx) sc = sum;
@@ -911,7 +1010,7 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     for (int i = 0; i < NI; ++i) {
       const int t = i * TPI + lane / LPT;
       float vf[8];
-      unpack8(vr[i], vf);
+      unpack8(vr[j][i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float pv = sm.p[wave][t * G + h];
@@ -922,32 +1021,47 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
     __builtin_amdgcn_wave_barrier();
   }
 
-  // --- combine the 4 waves (and the TPI token groups inside each wave)
+  // --- merge the waves (and the TPI token groups inside each) through LDS:
+  // every lane stores its partials, one thread per (wave, head) the factor
+  // exp(m_w - M), then each output sums its NW * TPI partials
+  __syncthreads();  // every wave is done with part (acc aliases it)
   if (lane < G) { sm.m[wave][lane] = m_run; sm.l[wave][lane] = l_run; }
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.acc[wave][h * 8 + e][lane] = acc[h][e];
+    for (int e = 0; e < 8; ++e) sm.acc[wave][lane][h * 8 + e] = acc[h][e];
+  __syncthreads();
+  if (tid < NW * G) {
+    const int w = tid / G, h = tid % G;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, sm.m[w2][h]);
+    const float mw = sm.m[w][h];
+    sm.wsc[w][h] = mw == -INFINITY ? 0.f : expf(mw - M);
+    if (w == 0) sm.mx[h] = M;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += sm.l[w][tid] * sm.wsc[w][tid];
+    sm.lsum[tid] = L;
+  }
   __syncthreads();
 
   const size_t qh0 = (size_t)b * Hq + (size_t)g * G;  // first query head row of this group
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
     const int h = idx / D, d = idx % D;
     const int dc = d / 8, e = d % 8;
-    float M = -INFINITY;
+    float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][h]);
-    float L = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = sm.m[w][h];
-      const float sc = (mw == -INFINITY) ? 0.f : expf(mw - M);
-      L += sm.l[w][h] * sc;
+    for (int w = 0; w < NW; ++w) {
       float ow = 0.f;
 #pragma unroll
-      for (int grp = 0; grp < TPI; ++grp) ow += sm.acc[w][h * 8 + e][grp * LPT + dc];
-      o += ow * sc;
+      for (int grp = 0; grp < TPI; ++grp) ow += sm.acc[w][grp * LPT + dc][h * 8 + e];
+      o += ow * sm.wsc[w][h];
     }
+    const float M = sm.mx[h], L = sm.lsum[h];
     if (nsplit == 1) {
       st_agent(a.out + (qh0 + h) * D + d, o / L);
       if (a.out_hi != nullptr) split_hilo(o / L, a.out_hi, a.out_lo, (qh0 + h) * D + d);
@@ -966,40 +1080,63 @@ __device__ inline void attention_item(const AttnArgs& a, const float* q_gain,
 
   unsigned* cnt = &a.counters[((size_t)b * Hkv + g) * kCntStride];
   if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
-    const float* ml = a.ml_part + (qh0 + h) * S_max * 2;
-    const float* op = a.o_part + (qh0 + h) * S_max * D + d;
-    // one pass over the splits, 8 at a time; sums carried over from earlier
-    // chunks are rescaled to the new running maximum
-    float M = -INFINITY, L = 0.f, o = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      float mv[8], lv[8], ov[8];
+  // (max, sum) of every split into LDS, and (for up to 16 splits) each
+  // output's split partials into registers in the same round trip; then
+  // per head the overall max and the splits' factors exp(m_s - M)
+  constexpr int kOut = (G * D + NW * 64 - 1) / (NW * 64);  // outputs per thread
+  float ov[kOut][16];
+  if (nsplit <= 16) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s2 = min(s0 + j, nsplit - 1);
-        mv[j] = ld_agent(ml + s2 * 2);
-        lv[j] = ld_agent(ml + s2 * 2 + 1);
-        ov[j] = ld_agent(op + (size_t)s2 * D);
-      }
-      float Mc = M;
+    for (int k = 0; k < kOut; ++k) {
+      const int idx = min(tid + k * NW * 64, G * D - 1);
+      const float* op = a.o_part + (qh0 + idx / D) * S_max * D + idx % D;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Mc = fmaxf(Mc, mv[j]);
-      const float r = M == -INFINITY ? 0.f : expf(M - Mc);
-      L *= r;
-      o *= r;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (s0 + j < nsplit) {
-          const float sc = expf(mv[j] - Mc);
-          L += lv[j] * sc;
-          o += ov[j] * sc;
-        }
-      }
-      M = Mc;
+      for (int j = 0; j < 16; ++j) ov[k][j] = ld_agent(op + (size_t)min(j, nsplit - 1) * D);
     }
-    st_agent(a.out + (qh0 + h) * D + d, o / L);
-    if (a.out_hi != nullptr) split_hilo(o / L, a.out_hi, a.out_lo, (qh0 + h) * D + d);
+  }
+  for (int i = tid; i < G * nsplit; i += NW * 64) {
+    const int h = i / nsplit, s2 = i % nsplit;
+    const float* ml = a.ml_part + ((qh0 + h) * S_max + s2) * 2;
+    sm.ml[0][h][s2] = ld_agent(ml);
+    sm.ml[1][h][s2] = ld_agent(ml + 1);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, sm.ml[0][tid][s2]);
+    float L = 0.f;
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+      const float f = expf(sm.ml[0][tid][s2] - M);
+      sm.ml[0][tid][s2] = f;
+      L += sm.ml[1][tid][s2] * f;
+    }
+    sm.lsum[tid] = L;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOut; ++k) {
+    const int idx = tid + k * NW * 64;
+    if (idx >= G * D) break;
+    const int h = idx / D, d = idx % D;
+    float o = 0.f;
+    if (nsplit <= 16) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < nsplit) o += ov[k][j] * sm.ml[0][h][j];
+    } else {
+      const float* op = a.o_part + (qh0 + h) * S_max * D + d;
+      for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float w16[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w16[j] = ld_agent(op + (size_t)min(s0 + j, nsplit - 1) * D);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (s0 + j < nsplit) o += w16[j] * sm.ml[0][h][s0 + j];
+      }
+    }
+    const float r = o / sm.lsum[h];
+    st_agent(a.out + (qh0 + h) * D + d, r);
+    if (a.out_hi != nullptr) split_hilo(r, a.out_hi, a.out_lo, (qh0 + h) * D + d);
   }
   if (tid == 0) reset_counter(cnt);
   signal_done(done);

@@ -84,7 +84,8 @@ struct AttnArgs {
   int max_pages;
   int B, Hq, Hkv;
   float eps, scale;
-  int S_max;               // splits per (sequence, KV head) the grid provides
+  int S_max;               // most splits a sequence can have (sizes o_part, ml_part)
+  int grid;                // workgroups of the standalone kernel (they share the items)
   float* o_part;           // [B*Hq][S_max][D]
   float* ml_part;          // [B*Hq][S_max][2]  (running max, running sum)
   unsigned* counters;      // [B*Hkv] split arrival counters, kCntStride apart (zero between uses)
@@ -142,8 +143,21 @@ constexpr int gemv_nb(int B) {
   return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
 }
 
-// Minimum pages a split of a sequence covers (one per wave of a workgroup).
-constexpr int kMinPagesPerSplit = 4;
+// Attention workgroups: the standalone kernel has 8 waves with 1 KV page
+// each in flight at batch <= 4 and 3 at larger batches (more, busier
+// workgroups are worth an extra page per wave over a split combine); the
+// persistent kernel's workgroups have 4 waves with 2 pages.  A split of a
+// sequence covers waves * pages.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnWavesPersistent = 4;
+constexpr int attn_pages_per_wave(int B, bool persistent) {
+  return persistent ? 2 : B <= 4 ? 1 : 3;
+}
+constexpr int attn_pages_per_split(int B, bool persistent) {
+  return (persistent ? kAttnWavesPersistent : kAttnWaves) * attn_pages_per_wave(B, persistent);
+}
+// Splits of one sequence the final combine can hold (its (max, sum) pairs sit in LDS).
+constexpr int kMaxSplitsStaged = 512;
 
 // Launchers (qd_kernels.hip).  All return the launch status.
 // Source row r lands in packed row (r / blk) * stride + off + r % blk.
@@ -152,7 +166,11 @@ hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, in
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
+// waves, pages: kAttnWaves with 1 or 3 pages per wave, or the persistent
+// kernel's item shape (kAttnWavesPersistent, 2; head shapes the persistent
+// kernel supports only).
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
+                            hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
                                int B, int Bmax, float eps, float* out, hipStream_t s);
 

@@ -71,10 +71,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 }
 
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+// The workgroups take the step's attention items round robin.
+template <int D, int G, int NW, int PW>
+__global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  attention_item<D, G>(a, a.q_gain, a.k_gain, a.pool_layer, no_done(), blockIdx.x, smem, NoWait{});
+  const AttnList list = attn_list<NW * PW>(a);
+  const int items = attn_items(list, a.B);
+  for (int t = blockIdx.x; t < items; t += gridDim.x)
+    attention_item<D, G, NW, PW>(a, list, a.q_gain, a.k_gain, a.pool_layer, no_done(), t, smem,
+                                 NoWait{});
 }
 
 
@@ -144,23 +149,36 @@ hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, int NW, int PW>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  const int grid = a.B * a.Hkv * a.S_max;
-  hipLaunchKernelGGL((attention_kernel<D, G>), dim3(grid), dim3(256), sizeof(AttnSmem<D, G>),
-                     s, a);
+  hipLaunchKernelGGL((attention_kernel<D, G, NW, PW>), dim3(a.grid), dim3(NW * 64),
+                     sizeof(AttnSmem<D, G, NW>), s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s) {
+template <int D, int G>
+static hipError_t launch_attention_dg(const AttnArgs& a, int pages, hipStream_t s) {
+  return pages == 1 ? launch_attention_t<D, G, kAttnWaves, 1>(a, s)
+                    : launch_attention_t<D, G, kAttnWaves, 3>(a, s);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
+                            hipStream_t s) {
+  if (waves == kAttnWavesPersistent) {  // the persistent kernel's item shape
+    if (pages != 2) return hipErrorInvalidValue;
+    if (head_dim == 128 && group == 4) return launch_attention_t<128, 4, kAttnWavesPersistent, 2>(a, s);
+    if (head_dim == 64 && group == 2) return launch_attention_t<64, 2, kAttnWavesPersistent, 2>(a, s);
+    return hipErrorInvalidValue;
+  }
+  if (waves != kAttnWaves || (pages != 1 && pages != 3)) return hipErrorInvalidValue;
   if (head_dim == 128) {
-    if (group == 4) return launch_attention_t<128, 4>(a, s);
-    if (group == 2) return launch_attention_t<128, 2>(a, s);
-    if (group == 1) return launch_attention_t<128, 1>(a, s);
+    if (group == 4) return launch_attention_dg<128, 4>(a, pages, s);
+    if (group == 2) return launch_attention_dg<128, 2>(a, pages, s);
+    if (group == 1) return launch_attention_dg<128, 1>(a, pages, s);
   } else if (head_dim == 64) {
-    if (group == 4) return launch_attention_t<64, 4>(a, s);
-    if (group == 2) return launch_attention_t<64, 2>(a, s);
-    if (group == 1) return launch_attention_t<64, 1>(a, s);
+    if (group == 4) return launch_attention_dg<64, 4>(a, pages, s);
+    if (group == 2) return launch_attention_dg<64, 2>(a, pages, s);
+    if (group == 1) return launch_attention_dg<64, 1>(a, pages, s);
   }
   return hipErrorInvalidValue;
 }
@@ -180,8 +198,8 @@ bool step_supported(int head_dim, int group) {
 
 size_t step_lds_bytes(int B, int head_dim, int group, int max_kps) {
   size_t att = 0;
-  if (head_dim == 128 && group == 4) att = sizeof(AttnSmem<128, 4>);
-  if (head_dim == 64 && group == 2) att = sizeof(AttnSmem<64, 2>);
+  if (head_dim == 128 && group == 4) att = sizeof(AttnSmem<128, 4, kAttnWavesPersistent>);
+  if (head_dim == 64 && group == 2) att = sizeof(AttnSmem<64, 2, kAttnWavesPersistent>);
   const size_t gm = gemv_lds_bytes(B, max_kps);
   return att > gm ? att : gm;
 }

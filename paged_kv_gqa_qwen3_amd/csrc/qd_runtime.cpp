@@ -209,12 +209,16 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
   return p;
 }
 
+// Most splits of one sequence (its longest table) at batch B.
 int attn_splits(const qd_handle* h, int B) {
-  int s = (2 * h->num_cus + B * h->Hkv - 1) / (B * h->Hkv);
-  const int cap = (h->cfg.max_pages_per_seq + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return s;
+  const int pps = attn_pages_per_split(B, use_persistent(h, B));
+  return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
+}
+
+// Workgroups of the standalone attention kernel: they take the step's items
+// round robin; at most two per CU.
+int attn_grid(const qd_handle* h, int B) {
+  return std::max(1, std::min(2 * h->num_cus, B * h->Hkv * attn_splits(h, B)));
 }
 
 int validate_config(const qd_config* c) {
@@ -240,8 +244,8 @@ int validate_config(const qd_config* c) {
     return fail(nullptr, QD_EUNSUPPORTED, "query heads per KV head must be 1, 2 or 4");
   if (c->intermediate % 32) return fail(nullptr, QD_EUNSUPPORTED, "intermediate must be a multiple of 32");
   if (c->vocab % 64) return fail(nullptr, QD_EUNSUPPORTED, "vocab must be a multiple of 64");
-  if ((long long)c->max_pages_per_seq * kPage > (1LL << 30))
-    return fail(nullptr, QD_EUNSUPPORTED, "max_pages_per_seq too large");
+  if ((long long)c->max_pages_per_seq > (long long)kMaxSplitsStaged * attn_pages_per_split(1, false))
+    return fail(nullptr, QD_EUNSUPPORTED, "max_pages_per_seq too large (at most 4096 pages)");
   return QD_OK;
 }
 
@@ -378,13 +382,18 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.B = B; aa.Hq = h->Hq; aa.Hkv = h->Hkv;
     aa.eps = eps; aa.scale = (float)(1.0 / std::sqrt((double)h->D));
     aa.S_max = smax;
+    aa.grid = attn_grid(h, B);
     aa.o_part = h->o_part; aa.ml_part = h->ml_part; aa.counters = h->attn_cnt;
     aa.out = h->attn;
     if (mfma) { aa.out_hi = h->attn_hi; aa.out_lo = h->attn_lo; }
     aa.tap_q = tap ? taps->q_rot : nullptr;
     aa.tap_k = tap ? taps->k_rot : nullptr;
     aa.dev_flags = h->dev_flags;
-    HIP_TRY(h, launch_attention(aa, h->D, h->G, s));
+    // a persistent handle's batches <= 4 use the persistent kernel's item
+    // shape here too, so both launch modes compute the same bits
+    const bool pers = use_persistent(h, B);
+    HIP_TRY(h, launch_attention(aa, h->D, h->G, pers ? kAttnWavesPersistent : kAttnWaves,
+                                attn_pages_per_wave(B, pers), s));
     PROF(QD_PROF_ATTN);
     if (tap && taps->attn)
       HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,

@@ -85,6 +85,9 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
   const unsigned n_qkv = (unsigned)gemv_items(a.qkv);
   const unsigned rg_gu = (unsigned)gemv_row_groups(a.gu);
   const unsigned n_heads = (unsigned)(a.attn.B * a.attn.Hkv);
+  // the attention work list (positions are inputs of the step)
+  const AttnList alist = attn_list<attn_pages_per_split(1, true)>(a.attn);
+  const int attn_n = attn_items(alist, a.attn.B);
   // stage with counter index i completes phase i + 1 (0: nothing done yet)
   auto done = [&](int i, unsigned target) {
     return Done{a.cnt + i, target, (unsigned)i + 1u, a.flags, (int)nwg};
@@ -106,9 +109,10 @@ __global__ __launch_bounds__(256) void step_kernel(const StepArgs a) {
                                                 it, smem, waiter(x_ready));
     });
     uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
-    for_items(a.attn.B * a.attn.Hkv * a.attn.S_max, [&](int it) {
-      attention_item<D, G>(a.attn, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), it,
-                           smem, waiter(phase(c + 0)));
+    for_items(attn_n, [&](int it) {
+      attention_item<D, G, kAttnWavesPersistent, attn_pages_per_wave(1, true)>(
+          a.attn, alist, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), it, smem,
+          waiter(phase(c + 0)));
     });
     for_items(gemv_items(a.o), [&](int it) {
       gemv_item<NB, kResid, kPersistentTiles>(a.o, ly.o, nullptr, done(c + 2, rg_o), it, smem,

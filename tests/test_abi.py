@@ -53,6 +53,8 @@ def _cfg(**kw):
     ("num_pages", 0, binding.QD_EINVAL),
     ("rms_eps", 0.0, binding.QD_EINVAL),
     ("num_layers", 0, binding.QD_EINVAL),
+    ("hidden", 8256, binding.QD_EUNSUPPORTED),
+    ("max_pages_per_seq", 4097, binding.QD_EUNSUPPORTED),
 ])
 def test_create_rejects_bad_config(lib, field, value, code):
     h = ctypes.c_void_p()

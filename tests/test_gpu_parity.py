@@ -193,6 +193,9 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
 @pytest.mark.parametrize("B,ctx", [
     (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
     (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
+    # splits of 8 pages (batch <= 4) or 24 pages: one to 17 of them, and a
+    # combine of more than 16 splits (2100)
+    (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]),
 ])
 def test_tiny_stages(torch, B, ctx):
     shape = synth.TINY
@@ -259,7 +262,8 @@ def test_graph_replay_matches_eager(torch):
     de.close()
 
 
-@pytest.mark.parametrize("B,ctx", [(1, [40]), (3, [5, 40, 77]), (4, [0, 16, 250, 31])])
+@pytest.mark.parametrize("B,ctx", [(1, [40]), (3, [5, 40, 77]), (4, [0, 16, 250, 31]),
+                                   (2, [700, 1300])])
 def test_persistent_matches_staged_bitwise(torch, B, ctx):
     """The persistent kernel and the per-stage kernels of the same handle run
     the same items with the same split plans, so every bit must agree, over

@@ -138,6 +138,45 @@ struct StepArgs {
   unsigned long long* trace; // builds with QD_STEP_TRACE only: per-item timestamps
 };
 
+// Arguments of the batch-1 streaming step kernel (qd_stream.hip): the whole
+// step in one cooperative launch whose waves stream their share of every
+// projection's weights through rings in LDS.
+constexpr int kStreamRing = 24;  // 1 KB weight tiles a wave keeps loaded or in flight
+constexpr int kStreamMaxLayers = 64;
+constexpr int kStreamStageVec = 16;  // 4-float groups of a staged input per thread
+struct StreamArgs {
+  EmbedArgs embed;
+  AttnArgs attn;             // attention at batch 1; pool_layer is layer 0's slice
+  const LayerDev* layers;
+  // packed weights of layer l, projection p (QKV, O, gate/up, down) at
+  // [4*l + p]: read with scalar loads from the kernel arguments
+  const uint16_t* w[4 * kStreamMaxLayers];
+  int L, H, QD, I, V, NQKV, Bmax;
+  const uint16_t* lm;        // packed [V][H]
+  const float* final_norm;
+  float eps;
+  float* x;                  // [H] residual stream
+  float* ssq;                // [H/16][Bmax] partial sums of squares of x (column 0)
+  float* qkv;                // [NQKV] q|k|v
+  float* attn_out;           // [Hq*D]
+  float* act;                // [I]
+  float* logits;             // [V] or null
+  float* amax_val;           // [grid] per-workgroup maxima of the LM head
+  int* amax_idx;
+  int* next_ids;             // [1]
+  size_t pool_layer_elems;   // elements of one layer's slice of the pool
+  int in_floats;             // LDS floats for a stage input plus the old residual rows
+  int res_off;               // float offset of the old residual rows in that region
+  int rt_max;                // most row tiles of one projection a workgroup owns
+  unsigned* cnt;             // [2 + L*kCntPerLayer] dependency counters (zero at launch)
+  unsigned* flags;           // [grid][32] per-workgroup completed-stage flags
+  unsigned* exit_cnt;
+  unsigned* abort_flag;
+  int* dev_flags;
+  unsigned spin_limit;
+  unsigned long long* trace;  // builds with QD_STEP_TRACE only: per-stage timestamps
+};
+
 // Batch columns a GEMV item is compiled for: VALU up to 4, MFMA blocks of 16 above.
 constexpr int gemv_nb(int B) {
   return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
@@ -182,6 +221,14 @@ hipError_t step_max_grid(int B, int head_dim, int group, size_t lds, int num_cus
                          int* grid);
 hipError_t launch_step(const StepArgs& a, int head_dim, int group, int grid, size_t lds,
                        hipStream_t s);
+
+// Batch-1 streaming step: LDS bytes, largest co-resident grid (0 when it
+// does not fit), cooperative launch; the (head_dim, group) shapes of the
+// persistent step only.
+size_t stream_lds_bytes(int head_dim, int group, int in_floats, int rt_max);
+hipError_t stream_max_grid(int head_dim, int group, size_t lds, int num_cus, int* grid);
+hipError_t launch_stream(const StreamArgs& a, int head_dim, int group, int grid, size_t lds,
+                         hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for its input slice.
 size_t gemv_lds_bytes(int B, int kps);

@@ -95,6 +95,13 @@ struct qd_handle {
   unsigned* step_exit = nullptr;
   unsigned* step_abort = nullptr;
   std::map<int, int> step_grid;  // batch -> co-resident grid of the persistent kernel
+  // batch-1 streaming step (persistent handles whose shapes fit it)
+  bool stream_ok = false;
+  int stream_grid = 0;
+  size_t stream_lds = 0;
+  int stream_in_floats = 0, stream_rt_max = 0, stream_res_off = 0;
+  float* stream_amax_val = nullptr;  // [stream_grid]
+  int* stream_amax_idx = nullptr;
 };
 
 namespace {
@@ -147,6 +154,10 @@ constexpr int kMinValuItems = 128;
 // The persistent kernel serves batches <= 4 (VALU items); larger batches
 // always take the per-stage kernels.
 bool use_persistent(const qd_handle* h, int B) { return h->persistent && gemv_nb(B) <= 4; }
+
+// A persistent handle runs batch 1 as the streaming step kernel when its
+// shapes fit (decided in qd_create).
+bool use_stream(const qd_handle* h, int B) { return h->stream_ok && B == 1; }
 
 GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
                    int grid = 0) {
@@ -531,6 +542,111 @@ int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   return QD_OK;
 }
 
+// Decide whether batch 1 runs as the streaming step kernel and size it: one
+// workgroup per CU (its rings take most of the LDS), each owning about
+// 1/grid of every projection's row tiles.
+int setup_stream(qd_handle* h) {
+  // (inputs under an RMSNorm gain are the hidden size: at most 8192)
+  if (!h->persistent || h->L > kStreamMaxLayers || h->H > 8192) return QD_OK;
+  const int kmax = std::max(h->H, std::max(h->QD, h->I));
+  if (kmax > 4 * 256 * kStreamStageVec) return QD_OK;  // staged input: 16 floats per thread
+  auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
+  int W = h->num_cus;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const int rt_max = std::max(cdiv(h->NQKV / kTileRows, W),
+                                std::max(cdiv(h->H / kTileRows, W), cdiv(2 * h->I / kTileRows, W)));
+    // inputs are staged in whole KB (256 floats), the old residual rows after them
+    const int res_off = cdiv(kmax, 256) * 256;
+    const int in_floats = res_off + cdiv(h->H / kTileRows, W) * kTileRows;
+    const size_t lds = stream_lds_bytes(h->D, h->G, in_floats, rt_max);
+    if (lds == 0) return QD_OK;
+    int g = 0;
+    if (stream_max_grid(h->D, h->G, lds, h->num_cus, &g) != hipSuccess || g < 1) {
+      (void)hipGetLastError();  // LDS beyond the device limit: no streaming step
+      return QD_OK;
+    }
+    if (g >= W) {
+      h->stream_ok = true;
+      h->stream_grid = W;
+      h->stream_lds = lds;
+      h->stream_in_floats = in_floats;
+      h->stream_res_off = res_off;
+      h->stream_rt_max = rt_max;
+      if (std::getenv("QD_DEBUG"))
+        std::fprintf(stderr, "[qd] streaming step: grid %d, LDS %zu, rt_max %d\n", W, lds, rt_max);
+      return QD_OK;
+    }
+    W = g;
+  }
+  return QD_OK;
+}
+
+// One batch-1 step as the streaming cooperative kernel.
+int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
+  const int H = h->H;
+  StreamArgs a{};
+  a.embed.table = h->embed;
+  a.embed.V = h->V; a.embed.H = H; a.embed.B = 1; a.embed.Bmax = h->cfg.max_batch;
+  a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
+  a.embed.dev_flags = h->dev_flags;
+  AttnArgs& at = a.attn;
+  at.qkv = h->qkv;  // q|k|v in full, as the per-stage path with taps reads it
+  at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
+  at.pool_layer = sp.pool;
+  at.num_pages = h->cfg.num_pages;
+  at.positions = sp.positions; at.block_tables = sp.tables;
+  at.max_pages = h->cfg.max_pages_per_seq;
+  at.B = 1; at.Hq = h->Hq; at.Hkv = h->Hkv;
+  at.eps = h->cfg.rms_eps; at.scale = (float)(1.0 / std::sqrt((double)h->D));
+  at.S_max = attn_splits(h, 1);
+  at.o_part = h->o_part; at.ml_part = h->ml_part; at.counters = h->attn_cnt;
+  at.out = h->attn;
+  at.dev_flags = h->dev_flags;
+  a.layers = h->layers_dev;
+  for (int l = 0; l < h->L; ++l) {
+    const LayerW& w = h->lw[l];
+    a.w[4 * l + 0] = w.qkv; a.w[4 * l + 1] = w.o; a.w[4 * l + 2] = w.gu; a.w[4 * l + 3] = w.down;
+  }
+  a.L = h->L; a.H = H; a.QD = h->QD; a.I = h->I; a.V = h->V; a.NQKV = h->NQKV;
+  a.Bmax = h->cfg.max_batch;
+  a.lm = h->lm; a.final_norm = h->final_norm; a.eps = h->cfg.rms_eps;
+  a.x = h->x; a.ssq = h->ssq; a.qkv = h->qkv; a.attn_out = h->attn; a.act = h->act;
+  a.logits = sp.logits;
+  a.amax_val = h->stream_amax_val; a.amax_idx = h->stream_amax_idx;
+  a.next_ids = sp.next;
+  a.pool_layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+  a.in_floats = h->stream_in_floats;
+  a.res_off = h->stream_res_off;
+  a.rt_max = h->stream_rt_max;
+  a.cnt = h->step_cnt; a.flags = h->step_flags;
+  a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
+  a.dev_flags = h->dev_flags;
+  a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
+#ifdef QD_STEP_TRACE
+  static unsigned long long* trace = nullptr;
+  const size_t trace_n = (size_t)h->stream_grid * 1024;
+  if (!trace) {
+    HIP_TRY(h, hipMalloc(&trace, trace_n * 8));
+  }
+  HIP_TRY(h, hipMemsetAsync(trace, 0xff, trace_n * 8, s));
+  a.trace = trace;
+#endif
+  HIP_TRY(h, launch_stream(a, h->D, h->G, h->stream_grid, h->stream_lds, s));
+#ifdef QD_STEP_TRACE
+  if (const char* path = std::getenv("QD_TRACE_OUT")) {
+    HIP_TRY(h, hipStreamSynchronize(s));
+    std::vector<unsigned long long> hostbuf(trace_n);
+    HIP_TRY(h, hipMemcpy(hostbuf.data(), trace, trace_n * 8, hipMemcpyDeviceToHost));
+    FILE* f = std::fopen(path, "wb");
+    if (f) {
+      std::fwrite(hostbuf.data(), 8, trace_n, f);
+      std::fclose(f);
+    }
+  }
+#endif
+  return QD_OK;
+}
+
 bool all_loaded(const qd_handle* h, std::string* missing) {
   for (auto& kv : h->expected)
     if (!kv.second) { *missing = kv.first; return false; }
@@ -608,6 +724,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->expected["model.norm.weight"] = 0;
 
   h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
+  if ((rc = setup_stream(h))) return bail(rc);
 
   // activations and scratch
   if ((rc = dev_alloc(h, &h->x, (size_t)Bm * H))) return bail(rc);
@@ -672,11 +789,16 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
   if (h->persistent) {
     if ((rc = dev_alloc(h, &h->layers_dev, (size_t)L))) return bail(rc);
-    if ((rc = dev_alloc(h, &h->step_cnt, (size_t)1 + (size_t)L * kCntPerLayer))) return bail(rc);
+    // (the streaming step also counts the LM head's workgroups)
+    if ((rc = dev_alloc(h, &h->step_cnt, (size_t)2 + (size_t)L * kCntPerLayer))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_flags, (size_t)2 * h->num_cus * 32))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_exit, 1))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_abort, 1))) return bail(rc);
-    e = hipMemset(h->step_cnt, 0, sizeof(unsigned) * (1 + (size_t)L * kCntPerLayer));
+    if (h->stream_ok) {
+      if ((rc = dev_alloc(h, &h->stream_amax_val, (size_t)h->stream_grid))) return bail(rc);
+      if ((rc = dev_alloc(h, &h->stream_amax_idx, (size_t)h->stream_grid))) return bail(rc);
+    }
+    e = hipMemset(h->step_cnt, 0, sizeof(unsigned) * (2 + (size_t)L * kCntPerLayer));
     if (e == hipSuccess) e = hipMemset(h->step_flags, 0, sizeof(unsigned) * 2 * h->num_cus * 32);
     if (e == hipSuccess) e = hipMemset(h->step_exit, 0, sizeof(unsigned));
     if (e == hipSuccess) e = hipMemset(h->step_abort, 0, sizeof(unsigned));
@@ -808,6 +930,7 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   if (rc) return rc;
   StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits};
+  if (use_stream(h, batch)) return run_stream(h, sp, h->stream);
   if (use_persistent(h, batch)) return run_persistent(h, sp, h->stream);
   static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
   if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);

@@ -1,0 +1,540 @@
+// The batch-1 decode step as one persistent cooperative kernel that streams
+// weights continuously (included by qd_stream.hip).
+//
+// At batch 1 every projection is one of a chain of dependent stages, and each
+// stage boundary costs a few microseconds of hand-off latency (stores
+// performed, completion counted, waiting workgroups released).  If the
+// weights of a stage only started to stream once its input was ready, HBM
+// would idle for every one of those hand-offs.  Here every wave owns a fixed
+// share of every projection's weight tiles (its workgroup's row tiles, every
+// 4th k-tile of each) and streams them in step order into a private ring of
+// kStreamRing 1 KB slots in LDS with direct global-to-LDS loads, as far ahead as the
+// ring allows and independently of the stage it is computing: while a
+// workgroup waits for a stage's input its rings hold the next tiles it will
+// need.  The compute side consumes the ring in the same order.
+//
+// Each 1 KB weight tile is two 16x16x32 bf16 MFMAs against the input split
+// into a bf16 pair (hi = bf16(x), lo = bf16(x - hi), about 16 significant
+// bits), the input broadcast to all 16 columns: a wave runs alone on its
+// SIMD, where every instruction costs an issue slot, and this takes 5
+// instructions per tile (one ring read, two input reads, two MFMAs) where
+// unpacking and FMAs in fp32 take over 20.  Attention is the item function
+// of the per-stage kernels.
+#pragma once
+
+#include "qd_device.h"
+#include "qd_stream_plan.h"
+
+namespace qd {
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr unsigned vmcnt_imm(int n) {
+  return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | 0x70u | 0xF00u;
+}
+// ... and until every LDS / scalar-memory operation is done (vmcnt at its maximum).
+constexpr unsigned kLgkmZero = 15u | (3u << 14) | 0x70u;
+// Cache-policy operand of a direct-to-LDS load at device scope (sc1): the
+// data was written by other workgroups of the same launch.
+constexpr int kDeviceScope = 16;
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+// 4-float groups of a staged input per thread: inputs up to 16384 floats.
+constexpr int kStageVec = kStreamStageVec;
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// makes global stores visible, and even a fence limited to LDS counts the
+// ring's direct-to-LDS loads as LDS writes: both wait for every outstanding
+// vector memory operation of the wave, which would drain the ring.  The
+// stream kernel's barriers only hand data written with ds_write between
+// waves (each ring slot is read only by the wave that loads it), so waiting
+// for the wave's LDS operations is enough; the signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The wave's ring: its slots, the loader (position and counts) and the
+// slot the consumer reads next.
+struct StreamRing {
+  unsigned char* slots;  // kStreamRing slots of 1 KB
+  StreamLoader ld;
+  int cs_slot;
+  int W, wg;             // grid size and this workgroup
+#ifdef QD_STEP_TRACE
+  unsigned long long t_wait, t_dot;  // (trace builds) shader cycles waiting for tiles / in ring_mfma
+#endif
+};
+
+// Top the ring up (stream_refill) with direct global-to-LDS loads: lane l's
+// 16 bytes of a tile land at byte 16*l of its slot, i.e. in the order of
+// the packed tile.
+__device__ __forceinline__ void ring_top_up(const StreamArgs& a, StreamRing& rg, int wave,
+                                            int lane, int u_limit) {
+  unsigned char* const slots = rg.slots;
+  stream_refill(a, rg.ld, wave, rg.W, rg.wg, u_limit,
+                [&](const unsigned char* tile, int slot) {
+                  __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(tile) + lane,
+                                                   slots + (size_t)slot * 1024, 16, 0, 0);
+                });
+}
+
+// Wait until the next N (1..kBatch) tiles of the ring have landed.  A
+// wave's vector-memory loads complete in issue order, so they are in LDS
+// once at most (loads issued after them) operations are outstanding; any
+// other memory operation issued since only makes the wait stricter.
+template <int N>
+__device__ __forceinline__ void ring_wait(const StreamRing& rg) {
+  static_assert(N >= 1 && N <= kBatch, "batch size");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (rg.ld.issued - rg.ld.consumed == kStreamRing)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStreamRing - N));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// This lane's 16 bytes of the i-th unconsumed tile.
+__device__ __forceinline__ u32x4 ring_read(const StreamRing& rg, int i, int lane) {
+  int slot = rg.cs_slot + i;
+  if (slot >= kStreamRing) slot -= kStreamRing;
+  return *reinterpret_cast<const u32x4*>(rg.slots + (size_t)slot * 1024 + lane * 16);
+}
+
+// The next n tiles have been read (their LDS reads completed): their slots
+// may be refilled.
+__device__ __forceinline__ void ring_release(StreamRing& rg, int n) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  rg.ld.consumed += n;
+  rg.cs_slot += n;
+  if (rg.cs_slot >= kStreamRing) rg.cs_slot -= kStreamRing;
+}
+
+// Two accumulators of a wave's 16-row tile sums: the hi and the lo halves
+// of the input (added at the end); lane l holds rows 4*(l/16) .. +3 (all 16
+// columns are the same).
+struct Acc2 {
+  f32x4 h, l;
+};
+
+// acc += the next N tiles of the stream in order, the i-th against input
+// columns kcol(i) .. +8 of the staged bf16 pair (xh, xl); the freed slots
+// are refilled before the arithmetic.
+template <int N, class KCol>
+__device__ __forceinline__ void ring_mfma(const StreamArgs& a, StreamRing& rg, int wave, int lane,
+                                          int u_limit, const KCol& kcol,
+                                          const unsigned short* xh, const unsigned short* xl,
+                                          Acc2& acc) {
+#ifdef QD_STEP_TRACE
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+#endif
+  ring_top_up(a, rg, wave, lane, u_limit);
+#ifdef QD_STEP_TRACE
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+#endif
+  ring_wait<N>(rg);
+#ifdef QD_STEP_TRACE
+  rg.t_wait += __builtin_amdgcn_s_memtime() - t1;
+#endif
+  u32x4 wv[N], vh[N], vl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    wv[i] = ring_read(rg, i, lane);
+    const int c = kcol(i);
+    vh[i] = *reinterpret_cast<const u32x4*>(xh + c);
+    vl[i] = *reinterpret_cast<const u32x4*>(xl + c);
+  }
+  ring_release(rg, N);
+  ring_top_up(a, rg, wave, lane, u_limit);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 w8 = __builtin_bit_cast(bf16x8, wv[i]);
+    acc.h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vh[i]), acc.h,
+                                                    0, 0, 0);
+    acc.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vl[i]), acc.l,
+                                                    0, 0, 0);
+  }
+#ifdef QD_STEP_TRACE
+  rg.t_dot += __builtin_amdgcn_s_memtime() - t0;
+#endif
+}
+
+// acc += tiles j = 0 .. n-1 of the stream (column of tile j: kcol(j)), in
+// full batches, then one by one.
+template <class KCol>
+__device__ __forceinline__ void ring_mfma_run(const StreamArgs& a, StreamRing& rg, int wave,
+                                              int lane, int u_limit, int n, const KCol& kcol,
+                                              const unsigned short* xh, const unsigned short* xl,
+                                              Acc2& acc) {
+  int j0 = 0;
+  for (; j0 + kBatch <= n; j0 += kBatch)
+    ring_mfma<kBatch>(a, rg, wave, lane, u_limit, [&](int i) { return kcol(j0 + i); }, xh, xl,
+                      acc);
+  for (; j0 < n; ++j0)
+    ring_mfma<1>(a, rg, wave, lane, u_limit, [&](int) { return kcol(j0); }, xh, xl, acc);
+}
+
+// Wait until the step reached `phase` (every wave polls its workgroup's
+// flag, topping up its ring meanwhile).  Bounded like Waiter: after
+// spin_limit polls it records QD_DEV_TIMEOUT and sets the abort flag, after
+// which every later wait falls through.
+__device__ __forceinline__ void stream_wait(const StreamArgs& a, StreamRing& rg, int wave, int lane,
+                                   unsigned phase, int u_limit) {
+  const unsigned* flag = a.flags + (size_t)blockIdx.x * kFlagStride;
+  ring_top_up(a, rg, wave, lane, u_limit);
+  // the flag values are read into scalar registers, so that the loop (and
+  // the ring state it updates) stays uniform across the wave
+  for (unsigned n = 0;; ++n) {
+    if (__builtin_amdgcn_readfirstlane(ld_agent(flag)) >= phase) break;
+    ring_top_up(a, rg, wave, lane, u_limit);
+    if ((n & 63) == 0 && __builtin_amdgcn_readfirstlane(ld_agent(a.abort_flag)) != 0u) break;
+    if (n >= a.spin_limit) {
+      if (lane == 0) set_flag(a.dev_flags, QD_DEV_TIMEOUT);
+      st_agent(a.abort_flag, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Completion of this workgroup's share of a stage.  Only wave 0 stores
+// results, so only it waits for its stores to be performed (its ring holds
+// no load beyond the stage it just finished, see stream_step_kernel); then
+// the counter and, from the last workgroup to arrive, every flag.
+__device__ __forceinline__ void stream_signal(const Done& d, unsigned* s_last) {
+  if ((threadIdx.x >> 6) == 0) stores_done();
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(d.counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = prev + 1 == d.target ? 1u : 0u;
+  }
+  lds_barrier();
+  if (*s_last != 0u)
+    for (int i = threadIdx.x; i < d.nflags; i += blockDim.x)
+      __hip_atomic_fetch_max(d.flags + (size_t)i * kFlagStride, d.phase, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS after the rings: the stage input (first in fp32 as loaded, then as
+// its bf16 pair: hi [K] and lo [K]) and the old residual of the
+// workgroup's rows at float offset res_off (or an attention item's LDS,
+// never live at the same time), then the waves' row sums (rt_max row tiles
+// x 4 waves x 16 rows) and a few scalars.
+struct StreamMisc {
+  float s_ssq[4];
+  unsigned s_last;
+  float amax_v[4];
+  int amax_i[4];
+  float tmp[8];
+};
+
+template <int D, int G>
+constexpr size_t stream_in_bytes_t(int in_floats) {
+  const size_t x = (size_t)in_floats * 4;
+  const size_t att = sizeof(AttnSmem<D, G, kAttnWavesPersistent>);
+  return ((x > att ? x : att) + 15) / 16 * 16;
+}
+
+template <int D, int G>
+constexpr size_t stream_lds_bytes_t(int in_floats, int rt_max) {
+  return (size_t)4 * kStreamRing * 1024 + stream_in_bytes_t<D, G>(in_floats) +
+         (size_t)rt_max * 4 * kTileRows * 4 + sizeof(StreamMisc);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = gridDim.x, wg = blockIdx.x;
+  const int u_end = a.L * kUnitsPerLayer + 1;
+  unsigned char* in_lds = smem + (size_t)4 * kStreamRing * 1024;
+  float* xs = reinterpret_cast<float*>(in_lds);
+  float* red = reinterpret_cast<float*>(in_lds + stream_in_bytes_t<D, G>(a.in_floats));
+  StreamMisc& sm = *reinterpret_cast<StreamMisc*>(red + (size_t)a.rt_max * 4 * kTileRows);
+
+  // Wave 0 stores every stage's results and must then wait for its stores,
+  // which also waits for every load it issued before them: its ring never
+  // runs ahead of the unit it computes or waits for (u_lim), so that wait
+  // costs no more than the stores.  The other waves stream ahead freely.
+  StreamRing rg;
+  rg.slots = smem + (size_t)wave * kStreamRing * 1024;
+  rg.cs_slot = 0;
+  rg.W = W;
+  rg.wg = wg;
+#ifdef QD_STEP_TRACE
+  rg.t_wait = rg.t_dot = 0;
+#endif
+  stream_start(a, rg.ld, wave, W, wg);
+  auto u_lim = [&](int u) { return wave == 0 ? u : u_end; };
+  ring_top_up(a, rg, wave, lane, u_lim(0));
+
+  auto done = [&](int i, unsigned target) {
+    return Done{a.cnt + i, target, (unsigned)i + 1u, a.flags, W};
+  };
+#ifdef QD_STEP_TRACE
+  // (trace builds) event e of this workgroup: 100 MHz clock, from thread 0
+  auto mark = [&](int e) {
+    if (tid == 0) a.trace[(size_t)wg * 1024 + e] = __builtin_amdgcn_s_memrealtime();
+  };
+#else
+  auto mark = [](int) {};
+#endif
+  mark(1023);
+  auto phase = [](int i) { return (unsigned)i + 1u; };
+
+  // embedding (workgroup 0)
+  if (wg == 0) embed_item(a.embed, done(kCntEmbed, 1u), 0);
+
+  // The input of a projection in LDS as the bf16 pair of x (times the
+  // RMSNorm gain), 1/rms of it from the producer's partial sums of squares
+  // (s_inv, the same in every thread) and, for a residual epilogue, the old
+  // residual of the workgroup's row tiles [r0, r1) at xres.  Every thread
+  // loads its own 4-float groups with device-scope 16-byte loads (the data
+  // was written in this launch; past the end they return zeros).
+  float* const xres = xs + a.res_off;
+  unsigned short* const xsh = reinterpret_cast<unsigned short*>(xs);
+  float s_inv = 1.f;
+  auto stage_input = [&](const float* in, int K, const float* gain, int r0, int r1) {
+    const int nj = (K + 1023) / 1024;
+    const __amdgpu_buffer_rsrc_t rin =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(in), 0, K * 4, kBufferWord3);
+    f32x4 xv[kStageVec], gv[kStageVec];
+#pragma unroll
+    for (int j = 0; j < kStageVec; ++j) {
+      if (j < nj) {
+        xv[j] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, 16 * (tid + 256 * j), 0, kDeviceScope));
+        if (gain != nullptr) {
+          const int i = min(4 * (tid + 256 * j), K - 4);
+          gv[j] = *reinterpret_cast<const f32x4*>(gain + i);
+        }
+      }
+    }
+    for (int i = tid; i < (r1 - r0) * kTileRows; i += 256)
+      xres[i] = ld_agent(a.x + r0 * kTileRows + i);
+    if (gain != nullptr) {
+      const int ng = K / kSsqRows;
+      float ss = 0.f;
+      for (int g = tid; g < ng; g += 256) ss += ld_agent(a.ssq + (size_t)g * a.Bmax);
+      ss = wave_sum(ss);
+      if (lane == 0) sm.s_ssq[wave] = ss;
+    }
+#pragma unroll
+    for (int j = 0; j < kStageVec; ++j) {
+      const int i = 4 * (tid + 256 * j);
+      if (j < nj && i < K) {
+        f32x4 v = xv[j];
+        if (gain != nullptr) v *= gv[j];
+        unsigned short h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = f2bf(v[e]);
+          l[e] = f2bf(v[e] - __uint_as_float((unsigned)h[e] << 16));
+        }
+        *reinterpret_cast<uint2*>(xsh + i) =
+            make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
+        *reinterpret_cast<uint2*>(xsh + K + i) =
+            make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
+      }
+    }
+    lds_barrier();
+    if (gain != nullptr)
+      s_inv = rsqrtf((sm.s_ssq[0] + sm.s_ssq[1] + sm.s_ssq[2] + sm.s_ssq[3]) / (float)K + a.eps);
+  };
+
+  // The workgroup's rows of unit u: every wave adds its k-tiles of each row
+  // tile (k-tiles wave, wave + 4, ...) and leaves the 16 row sums in
+  // red[row tile][wave]; then wave 0 adds the waves in K order, scales by
+  // 1/rms under RMSNorm and runs epi(row tile in the workgroup, row tile, y)
+  // with 16 lanes per row tile (lane: row lane % 16).
+  auto project = [&](int u, bool norm, auto&& epi) {
+    const StreamShare s = stream_share(a, u, wave, W, wg);
+    const int K = s.KT * kTileCols;
+    const int nkw = stream_row_tiles(s);
+    for (int r = s.r0; r < s.r1; ++r) {
+      Acc2 acc{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      ring_mfma_run(a, rg, wave, lane, u_lim(u), nkw, [&](int j) {
+        return (s.kstart + 4 * j) * kTileCols + (lane >> 4) * 8;
+      }, xsh, xsh + K, acc);
+      if ((lane & 15) == 0)
+        *reinterpret_cast<f32x4*>(red + ((r - s.r0) * 4 + wave) * kTileRows + (lane >> 4) * 4) =
+            acc.h + acc.l;
+    }
+    lds_barrier();
+    if (wave == 0) {
+      for (int rr = lane >> 4; rr < s.r1 - s.r0; rr += 4) {
+        const float* rp = red + (size_t)rr * 4 * kTileRows + (lane & 15);
+        float y = rp[0];
+        for (int w2 = 1; w2 < 4; ++w2) y += rp[w2 * kTileRows];
+        if (norm) y *= s_inv;
+        epi(rr, s.r0 + rr, y);
+      }
+    }
+  };
+
+  // residual epilogue: x += y, and the sum of squares of each 16 new rows
+  auto resid = [&](int rr, int rt, float y) {
+    const int n = rt * kTileRows + (lane & 15);
+    const float xv = xres[rr * kTileRows + (lane & 15)] + y;
+    st_agent(a.x + n, xv);
+    const float ss = group_sum(xv * xv, kSsqRows);
+    if ((lane & 15) == 0) st_agent(a.ssq + (size_t)(n / kSsqRows) * a.Bmax, ss);
+  };
+
+  const unsigned n_heads = (unsigned)a.attn.Hkv;
+  const AttnList alist = attn_list<attn_pages_per_split(1, true)>(a.attn);
+  const int attn_n = __builtin_amdgcn_readfirstlane(attn_items(alist, 1));
+
+  for (int l = 0; l < a.L; ++l) {
+    const LayerDev ly = a.layers[l];
+    const int c = cnt_index(l, 0);
+    const int u = l * kUnitsPerLayer;
+    const unsigned x_ready = l == 0 ? phase(kCntEmbed) : phase(cnt_index(l - 1, 4));
+
+    // QKV: its result is q|k|v, which attention reads as the partials of a
+    // single K split
+    stream_wait(a, rg, wave, lane, x_ready, u_lim(u + kPrQkv));
+    mark(l * 20 + 0);
+    stage_input(a.x, a.H, ly.in_norm, 0, 0);
+    mark(l * 20 + 1);
+    project(u + kPrQkv, true, [&](int, int rt, float y) {
+      st_agent(a.qkv + rt * kTileRows + (lane & 15), y);
+    });
+    mark(l * 20 + 2);
+    stream_signal(done(c + 0, (unsigned)W), &sm.s_last);
+    mark(l * 20 + 3);
+
+    // attention (the items read q|k|v, RMSNorm and rotate q and k, append
+    // k and v to the pool and attend over it)
+    ring_top_up(a, rg, wave, lane, u_lim(u + kPrO));
+    uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
+    for (int t = wg; t < attn_n; t += W)
+      attention_item<D, G, kAttnWavesPersistent, attn_pages_per_wave(1, true)>(
+          a.attn, alist, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), t, in_lds,
+          Waiter{a.flags + (size_t)wg * kFlagStride, phase(c + 0), a.abort_flag, a.dev_flags,
+                 a.spin_limit});
+    mark(l * 20 + 4);
+
+    // O projection + residual
+    {
+      const StreamShare so = stream_share(a, u + kPrO, 0, W, wg);
+      stream_wait(a, rg, wave, lane, phase(c + 1), u_lim(u + kPrO));
+      mark(l * 20 + 5);
+      stage_input(a.attn_out, a.QD, nullptr, so.r0, so.r1);
+      mark(l * 20 + 6);
+      project(u + kPrO, false, resid);
+      mark(l * 20 + 7);
+      stream_signal(done(c + 2, (unsigned)W), &sm.s_last);
+      mark(l * 20 + 8);
+    }
+
+    // gate/up + SwiGLU (rows 0-7 of a packed tile are gate channels, rows
+    // 8-15 the matching up channels)
+    stream_wait(a, rg, wave, lane, phase(c + 2), u_lim(u + kPrGu));
+    mark(l * 20 + 9);
+    stage_input(a.x, a.H, ly.post_norm, 0, 0);
+    mark(l * 20 + 10);
+    project(u + kPrGu, true, [&](int, int rt, float y) {
+      const float uv = __shfl(y, 8 + (lane & 7), 16);
+      if ((lane & 15) < 8)
+        st_agent(a.act + rt * 8 + (lane & 7), y / (1.f + expf(-y)) * uv);
+    });
+    mark(l * 20 + 11);
+    stream_signal(done(c + 3, (unsigned)W), &sm.s_last);
+    mark(l * 20 + 12);
+
+    // down projection + residual
+    {
+      const StreamShare sd = stream_share(a, u + kPrDown, 0, W, wg);
+      stream_wait(a, rg, wave, lane, phase(c + 3), u_lim(u + kPrDown));
+      mark(l * 20 + 13);
+      stage_input(a.act, a.I, nullptr, sd.r0, sd.r1);
+      mark(l * 20 + 14);
+      project(u + kPrDown, false, resid);
+      mark(l * 20 + 15);
+      stream_signal(done(c + 4, (unsigned)W), &sm.s_last);
+      mark(l * 20 + 16);
+    }
+  }
+
+  // LM head: every wave one row tile of each of the workgroup's 64-row
+  // groups, all k-tiles; logits, the argmax of the workgroup's rows, then,
+  // in the last workgroup to finish, of all workgroups
+  const int u_lm = a.L * kUnitsPerLayer;
+  stream_wait(a, rg, wave, lane, phase(cnt_index(a.L - 1, 4)), u_end);
+  mark(1000);
+  stage_input(a.x, a.H, a.final_norm, 0, 0);
+  mark(1001);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  {
+    const StreamShare s = stream_share(a, u_lm, wave, W, wg);
+    for (int g = s.r0; g < s.r1; ++g) {
+      Acc2 acc{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      ring_mfma_run(a, rg, wave, lane, u_end, s.KT, [&](int j) {
+        return j * kTileCols + (lane >> 4) * 8;
+      }, xsh, xsh + a.H, acc);
+      const f32x4 y = (acc.h + acc.l) * s_inv;
+      const int row0 = (4 * g + wave) * kTileRows + (lane >> 4) * 4;
+      if ((lane & 15) == 0 && a.logits != nullptr) *reinterpret_cast<f32x4*>(a.logits + row0) = y;
+      float v = y[0];
+      int i = row0;
+#pragma unroll
+      for (int q = 1; q < 4; ++q) amax_merge(v, i, y[q], row0 + q);
+      wave_amax(v, i);
+      amax_merge(bv, bi, v, i);
+    }
+  }
+  mark(1002);
+  if (lane == 0) { sm.amax_v[wave] = bv; sm.amax_i[wave] = bi; }
+  lds_barrier();
+  if (tid == 0) {
+    for (int w2 = 1; w2 < 4; ++w2) amax_merge(bv, bi, sm.amax_v[w2], sm.amax_i[w2]);
+    st_agent(a.amax_val + wg, bv);
+    st_agent(a.amax_idx + wg, bi);
+  }
+  stores_done();
+  lds_barrier();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.cnt + cnt_index(a.L, 0), 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.s_last = prev + 1 == (unsigned)W ? 1u : 0u;
+  }
+  lds_barrier();
+  if (sm.s_last != 0u) {
+    float v;
+    int i, b;
+    if (merge_amax(a.amax_val, a.amax_idx, W, 1, 1, sm.tmp, v, i, b))
+      a.next_ids[0] = i == 0x7fffffff ? -1 : i;
+  }
+
+#ifdef QD_STEP_TRACE
+  if (lane == 0) {
+    a.trace[(size_t)wg * 1024 + 1008 + 2 * wave] = rg.t_wait;
+    a.trace[(size_t)wg * 1024 + 1009 + 2 * wave] = rg.t_dot;
+  }
+#endif
+  // The last workgroup out resets the dependency counters for the next step.
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.exit_cnt, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)W - 1) {
+      const int n = cnt_index(a.L, 0) + 1;
+      for (int i = 0; i < n; ++i) st_agent(a.cnt + i, 0u);
+      for (int i = 0; i < W; ++i) st_agent(a.flags + (size_t)i * kFlagStride, 0u);
+      st_agent(a.abort_flag, 0u);
+      st_agent(a.exit_cnt, 0u);
+    }
+  }
+}
+
+}  // namespace qd

@@ -37,6 +37,13 @@ __device__ __forceinline__ void split_hilo(float v, uint16_t* hi, uint16_t* lo, 
   lo[i] = (uint16_t)f2bf(v - __uint_as_float(h << 16));
 }
 
+// Cache-policy operand of a device-scope load (sc1): the data was written by
+// other workgroups of the same launch.
+constexpr int kDeviceScope = 16;
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle); loads
+// past its size return zeros.
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
   f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
@@ -767,6 +774,14 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
                                       unsigned char* smem, const Wait& wait) {
   using SM = AttnSmem<D, G, NW>;
   constexpr bool kAgent = Wait::kInLaunch;
+#ifdef QD_STEP_TRACE
+  auto mark = [&](int e) {
+    if (a.trace != nullptr && threadIdx.x == 0) a.trace[e] = __builtin_amdgcn_s_memrealtime();
+  };
+#else
+  auto mark = [](int) {};
+#endif
+  mark(0);
   constexpr int LPT = SM::LPT, TPI = SM::TPI, NI = SM::NI;
   constexpr int HALF = D / 2;
   constexpr int PPS = attn_pages_per_split<NW, PW>();
@@ -873,6 +888,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
 
   wait();
   __syncthreads();  // LDS of the previous item is free
+  mark(1);
   if constexpr (kAgent) load_inputs();  // written in this launch: after the wait
 
   // --- q/k RMSNorm + RoPE, v to bf16 (wave w takes heads w, w+NW, ...)
@@ -937,6 +953,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     }
   }
 
+  mark(2);
   // --- paged attention over this wave's pages
   const int dch = lane % LPT;
   float acc[G][8];
@@ -1021,6 +1038,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     __builtin_amdgcn_wave_barrier();
   }
 
+  mark(3);
   // --- merge the waves (and the TPI token groups inside each) through LDS:
   // every lane stores its partials, one thread per (wave, head) the factor
   // exp(m_w - M), then each output sums its NW * TPI partials
@@ -1079,7 +1097,9 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   }
 
   unsigned* cnt = &a.counters[((size_t)b * Hkv + g) * kCntStride];
+  mark(4);
   if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
+  mark(5);
   // (max, sum) of every split into LDS, and (for up to 16 splits) each
   // output's split partials into registers in the same round trip; then
   // per head the overall max and the splits' factors exp(m_s - M)
@@ -1139,7 +1159,9 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     if (a.out_hi != nullptr) split_hilo(r, a.out_hi, a.out_lo, (qh0 + h) * D + d);
   }
   if (tid == 0) reset_counter(cnt);
+  mark(6);
   signal_done(done);
+  mark(7);
 }
 
 // ------------------------------------------------------------------ persistent step

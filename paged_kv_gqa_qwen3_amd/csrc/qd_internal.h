@@ -95,6 +95,7 @@ struct AttnArgs {
   float* tap_q;            // optional [B][Hq][D] (after norm and RoPE, unscaled)
   float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
   int* dev_flags;
+  unsigned long long* trace;  // builds with QD_STEP_TRACE only: item event timestamps, or null
 };
 
 struct EmbedArgs {
@@ -138,6 +139,8 @@ struct StepArgs {
   unsigned long long* trace; // builds with QD_STEP_TRACE only: per-item timestamps
 };
 
+struct StreamRun;
+
 // Arguments of the batch-1 streaming step kernel (qd_stream.hip): the whole
 // step in one cooperative launch whose waves stream their share of every
 // projection's weights through rings in LDS.
@@ -165,6 +168,10 @@ struct StreamArgs {
   int* amax_idx;
   int* next_ids;             // [1]
   size_t pool_layer_elems;   // elements of one layer's slice of the pool
+  const struct StreamRun* runs;  // every wave's weight-tile runs (see qd_stream_plan.h)
+  const int* run_off;        // [grid][4] first run of each wave
+  int qkv_S;                 // K splits of each QKV row tile (attention sums the partials)
+  float* qkv_part;           // [NQKV/16][qkv_S][16] QKV split partials
   int in_floats;             // LDS floats for a stage input plus the old residual rows
   int res_off;               // float offset of the old residual rows in that region
   int rt_max;                // most row tiles of one projection a workgroup owns

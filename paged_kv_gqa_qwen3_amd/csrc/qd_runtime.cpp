@@ -21,6 +21,7 @@
 
 #include "qd.h"
 #include "qd_internal.h"
+#include "qd_stream_plan.h"
 
 using namespace qd;
 
@@ -99,7 +100,9 @@ struct qd_handle {
   bool stream_ok = false;
   int stream_grid = 0;
   size_t stream_lds = 0;
-  int stream_in_floats = 0, stream_rt_max = 0, stream_res_off = 0;
+  int stream_in_floats = 0, stream_rt_max = 0, stream_res_off = 0, stream_qkv_S = 1;
+  StreamRun* stream_runs = nullptr;  // every wave's weight-tile runs
+  int* stream_run_off = nullptr;     // [stream_grid][4]
   float* stream_amax_val = nullptr;  // [stream_grid]
   int* stream_amax_idx = nullptr;
 };
@@ -553,7 +556,13 @@ int setup_stream(qd_handle* h) {
   auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
   int W = h->num_cus;
   for (int attempt = 0; attempt < 2; ++attempt) {
-    const int rt_max = std::max(cdiv(h->NQKV / kTileRows, W),
+    // QKV K splits (the kernel supports any count; attention sums the
+    // partials).  Measured on the 4B shape, 2 splits balance the workgroups'
+    // shares (3 half tiles each instead of 1 or 2 tiles) but lose as much to
+    // the shorter runs and the extra epilogues: one split.
+    const int Rq = h->NQKV / kTileRows;
+    const int qS = 1;
+    const int rt_max = std::max(cdiv(Rq * qS, W),
                                 std::max(cdiv(h->H / kTileRows, W), cdiv(2 * h->I / kTileRows, W)));
     // inputs are staged in whole KB (256 floats), the old residual rows after them
     const int res_off = cdiv(kmax, 256) * 256;
@@ -566,14 +575,41 @@ int setup_stream(qd_handle* h) {
       return QD_OK;
     }
     if (g >= W) {
+      // the waves' tile runs, from the same partition the kernel consumes
+      StreamArgs sa{};
+      sa.L = h->L; sa.H = h->H; sa.QD = h->QD; sa.I = h->I; sa.V = h->V; sa.NQKV = h->NQKV;
+      sa.qkv_S = qS;
+      for (int l = 0; l < h->L; ++l) {
+        const LayerW& w = h->lw[l];
+        sa.w[4 * l + 0] = w.qkv; sa.w[4 * l + 1] = w.o; sa.w[4 * l + 2] = w.gu; sa.w[4 * l + 3] = w.down;
+      }
+      sa.lm = h->lm;
+      std::vector<StreamRun> runs;
+      std::vector<int> off((size_t)W * 4);
+      for (int wg = 0; wg < W; ++wg)
+        for (int wave = 0; wave < 4; ++wave) {
+          off[(size_t)wg * 4 + wave] = (int)runs.size();
+          stream_runs(sa, W, wg, wave, [&](const unsigned char* p, int n, int stride, int u) {
+            runs.push_back(StreamRun{p, (uint32_t)n | ((uint32_t)u << 16), (uint32_t)stride});
+          });
+        }
+      int rc = dev_alloc(h, &h->stream_runs, runs.size());
+      if (!rc) rc = dev_alloc(h, &h->stream_run_off, off.size());
+      if (rc) return rc;
+      HIP_TRY(h, hipMemcpy(h->stream_runs, runs.data(), runs.size() * sizeof(StreamRun),
+                           hipMemcpyHostToDevice));
+      HIP_TRY(h, hipMemcpy(h->stream_run_off, off.data(), off.size() * sizeof(int),
+                           hipMemcpyHostToDevice));
       h->stream_ok = true;
       h->stream_grid = W;
       h->stream_lds = lds;
       h->stream_in_floats = in_floats;
       h->stream_res_off = res_off;
       h->stream_rt_max = rt_max;
+      h->stream_qkv_S = qS;
       if (std::getenv("QD_DEBUG"))
-        std::fprintf(stderr, "[qd] streaming step: grid %d, LDS %zu, rt_max %d\n", W, lds, rt_max);
+        std::fprintf(stderr, "[qd] streaming step: grid %d, LDS %zu, rt_max %d, QKV splits %d\n",
+                     W, lds, rt_max, qS);
       return QD_OK;
     }
     W = g;
@@ -590,7 +626,10 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
   a.embed.dev_flags = h->dev_flags;
   AttnArgs& at = a.attn;
-  at.qkv = h->qkv;  // q|k|v in full, as the per-stage path with taps reads it
+  at.qkv = h->qkv;
+  at.qkv_part = h->part_qkv;
+  at.qkv_S = h->stream_qkv_S;
+  at.qkv_rows = kTileRows;
   at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
   at.pool_layer = sp.pool;
   at.num_pages = h->cfg.num_pages;
@@ -615,6 +654,10 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.amax_val = h->stream_amax_val; a.amax_idx = h->stream_amax_idx;
   a.next_ids = sp.next;
   a.pool_layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+  a.runs = h->stream_runs;
+  a.run_off = h->stream_run_off;
+  a.qkv_S = h->stream_qkv_S;
+  a.qkv_part = h->part_qkv;
   a.in_floats = h->stream_in_floats;
   a.res_off = h->stream_res_off;
   a.rt_max = h->stream_rt_max;
@@ -763,6 +806,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * pq.S * B);
   }
   if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
+  if (h->stream_ok) part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * h->stream_qkv_S);
   if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg * kCntStride))) return bail(rc);
   h->smax1 = attn_splits(h, 1);

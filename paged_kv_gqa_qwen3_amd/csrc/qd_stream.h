@@ -34,13 +34,11 @@ constexpr unsigned vmcnt_imm(int n) {
 }
 // ... and until every LDS / scalar-memory operation is done (vmcnt at its maximum).
 constexpr unsigned kLgkmZero = 15u | (3u << 14) | 0x70u;
-// Cache-policy operand of a direct-to-LDS load at device scope (sc1): the
-// data was written by other workgroups of the same launch.
-constexpr int kDeviceScope = 16;
-// Word 3 of a raw buffer resource (32-bit data format, no swizzle).
-constexpr int kBufferWord3 = 0x00020000;
+
 // 4-float groups of a staged input per thread: inputs up to 16384 floats.
 constexpr int kStageVec = kStreamStageVec;
+// ... and of an RMSNorm gain (the hidden size: at most 8192 floats).
+constexpr int kGainVec = 8;
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // makes global stores visible, and even a fence limited to LDS counts the
@@ -75,8 +73,7 @@ struct StreamRing {
 __device__ __forceinline__ void ring_top_up(const StreamArgs& a, StreamRing& rg, int wave,
                                             int lane, int u_limit) {
   unsigned char* const slots = rg.slots;
-  stream_refill(a, rg.ld, wave, rg.W, rg.wg, u_limit,
-                [&](const unsigned char* tile, int slot) {
+  stream_refill(rg.ld, u_limit, [&](const unsigned char* tile, int slot) {
                   __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(tile) + lane,
                                                    slots + (size_t)slot * 1024, 16, 0, 0);
                 });
@@ -115,11 +112,22 @@ __device__ __forceinline__ void ring_release(StreamRing& rg, int n) {
   if (rg.cs_slot >= kStreamRing) rg.cs_slot -= kStreamRing;
 }
 
-// Two accumulators of a wave's 16-row tile sums: the hi and the lo halves
-// of the input (added at the end); lane l holds rows 4*(l/16) .. +3 (all 16
-// columns are the same).
+// Accumulators of a wave's 16-row tile sums: for each position of a batch,
+// the hi and the lo halves of the input (so that the MFMAs of a batch do not
+// wait on each other); lane l holds rows 4*(l/16) .. +3 (all 16 columns are
+// the same).
 struct Acc2 {
-  f32x4 h, l;
+  f32x4 h[kBatch], l[kBatch];
+  __device__ __forceinline__ Acc2() {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) h[i] = l[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ f32x4 total() const {
+    f32x4 t = h[0] + l[0];
+#pragma unroll
+    for (int i = 1; i < kBatch; ++i) t += h[i] + l[i];
+    return t;
+  }
 };
 
 // acc += the next N tiles of the stream in order, the i-th against input
@@ -154,10 +162,10 @@ __device__ __forceinline__ void ring_mfma(const StreamArgs& a, StreamRing& rg, i
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const bf16x8 w8 = __builtin_bit_cast(bf16x8, wv[i]);
-    acc.h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vh[i]), acc.h,
-                                                    0, 0, 0);
-    acc.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vl[i]), acc.l,
-                                                    0, 0, 0);
+    acc.h[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vh[i]),
+                                                       acc.h[i], 0, 0, 0);
+    acc.l[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vl[i]),
+                                                       acc.l[i], 0, 0, 0);
   }
 #ifdef QD_STEP_TRACE
   rg.t_dot += __builtin_amdgcn_s_memtime() - t0;
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
 #ifdef QD_STEP_TRACE
   rg.t_wait = rg.t_dot = 0;
 #endif
-  stream_start(a, rg.ld, wave, W, wg);
+  stream_start(rg.ld, a.runs + __builtin_amdgcn_readfirstlane(a.run_off[wg * 4 + wave]));
   auto u_lim = [&](int u) { return wave == 0 ? u : u_end; };
   ring_top_up(a, rg, wave, lane, u_lim(0));
 
@@ -302,24 +310,23 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   unsigned short* const xsh = reinterpret_cast<unsigned short*>(xs);
   float s_inv = 1.f;
   auto stage_input = [&](const float* in, int K, const float* gain, int r0, int r1) {
+    const bool norm = gain != nullptr;
     const int nj = (K + 1023) / 1024;
     const __amdgpu_buffer_rsrc_t rin =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(in), 0, K * 4, kBufferWord3);
-    f32x4 xv[kStageVec], gv[kStageVec];
+    f32x4 xv[kStageVec], gv[kGainVec];
 #pragma unroll
     for (int j = 0; j < kStageVec; ++j) {
       if (j < nj) {
         xv[j] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, 16 * (tid + 256 * j), 0, kDeviceScope));
-        if (gain != nullptr) {
-          const int i = min(4 * (tid + 256 * j), K - 4);
-          gv[j] = *reinterpret_cast<const f32x4*>(gain + i);
-        }
+        if (norm && j < kGainVec)  // (under a norm K is the hidden size: j < kGainVec)
+          gv[j] = *reinterpret_cast<const f32x4*>(gain + min(4 * (tid + 256 * j), K - 4));
       }
     }
     for (int i = tid; i < (r1 - r0) * kTileRows; i += 256)
       xres[i] = ld_agent(a.x + r0 * kTileRows + i);
-    if (gain != nullptr) {
+    if (norm) {
       const int ng = K / kSsqRows;
       float ss = 0.f;
       for (int g = tid; g < ng; g += 256) ss += ld_agent(a.ssq + (size_t)g * a.Bmax);
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       const int i = 4 * (tid + 256 * j);
       if (j < nj && i < K) {
         f32x4 v = xv[j];
-        if (gain != nullptr) v *= gv[j];
+        if (norm && j < kGainVec) v *= gv[j];
         unsigned short h[4], l[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -345,27 +352,29 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       }
     }
     lds_barrier();
-    if (gain != nullptr)
+    if (norm)
       s_inv = rsqrtf((sm.s_ssq[0] + sm.s_ssq[1] + sm.s_ssq[2] + sm.s_ssq[3]) / (float)K + a.eps);
   };
 
-  // The workgroup's rows of unit u: every wave adds its k-tiles of each row
-  // tile (k-tiles wave, wave + 4, ...) and leaves the 16 row sums in
-  // red[row tile][wave]; then wave 0 adds the waves in K order, scales by
-  // 1/rms under RMSNorm and runs epi(row tile in the workgroup, row tile, y)
-  // with 16 lanes per row tile (lane: row lane % 16).
-  auto project = [&](int u, bool norm, auto&& epi) {
+  // The workgroup's pieces of unit u: every wave adds its k-tiles of each
+  // piece (k-tiles kb + wave, kb + wave + 4, ...) and leaves the 16 row sums
+  // in red[piece][wave]; then wave 0 adds the waves in K order, scales by
+  // 1/rms under RMSNorm and runs epi(piece in the workgroup, piece, y) with
+  // 16 lanes per piece (lane: row lane % 16).  Without a K split a piece is
+  // a row tile.
+  auto project = [&](int u, int u_limit, bool norm, auto&& epi) {
     const StreamShare s = stream_share(a, u, wave, W, wg);
     const int K = s.KT * kTileCols;
-    const int nkw = stream_row_tiles(s);
     for (int r = s.r0; r < s.r1; ++r) {
-      Acc2 acc{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      ring_mfma_run(a, rg, wave, lane, u_lim(u), nkw, [&](int j) {
-        return (s.kstart + 4 * j) * kTileCols + (lane >> 4) * 8;
+      int kb, ke;
+      stream_piece(s, r, kb, ke);
+      Acc2 acc;
+      ring_mfma_run(a, rg, wave, lane, u_limit, stream_piece_tiles(s, r), [&](int j) {
+        return (kb + s.kstart + 4 * j) * kTileCols + (lane >> 4) * 8;
       }, xsh, xsh + K, acc);
       if ((lane & 15) == 0)
         *reinterpret_cast<f32x4*>(red + ((r - s.r0) * 4 + wave) * kTileRows + (lane >> 4) * 4) =
-            acc.h + acc.l;
+            acc.total();
     }
     lds_barrier();
     if (wave == 0) {
@@ -391,6 +400,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   const unsigned n_heads = (unsigned)a.attn.Hkv;
   const AttnList alist = attn_list<attn_pages_per_split(1, true)>(a.attn);
   const int attn_n = __builtin_amdgcn_readfirstlane(attn_items(alist, 1));
+  const bool attn_wg = wg < attn_n;  // this workgroup runs attention items
 
   for (int l = 0; l < a.L; ++l) {
     const LayerDev ly = a.layers[l];
@@ -398,14 +408,18 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     const int u = l * kUnitsPerLayer;
     const unsigned x_ready = l == 0 ? phase(kCntEmbed) : phase(cnt_index(l - 1, 4));
 
-    // QKV: its result is q|k|v, which attention reads as the partials of a
-    // single K split
-    stream_wait(a, rg, wave, lane, x_ready, u_lim(u + kPrQkv));
+    // QKV, as qkv_S split partials per row that attention sums.  A
+    // workgroup that runs attention items loads no tile past the
+    // QKV unit meanwhile: its K/V page loads, issued when its item starts,
+    // would otherwise complete only after those tiles (loads complete in
+    // order); it fetches its next tiles while it waits for the other items.
+    const int lim_qkv = attn_wg ? u + kPrQkv : u_lim(u + kPrQkv);
+    stream_wait(a, rg, wave, lane, x_ready, lim_qkv);
     mark(l * 20 + 0);
     stage_input(a.x, a.H, ly.in_norm, 0, 0);
     mark(l * 20 + 1);
-    project(u + kPrQkv, true, [&](int, int rt, float y) {
-      st_agent(a.qkv + rt * kTileRows + (lane & 15), y);
+    project(u + kPrQkv, lim_qkv, true, [&](int, int piece, float y) {
+      st_agent(a.qkv_part + piece * kTileRows + (lane & 15), y);  // = [rt][split][row]
     });
     mark(l * 20 + 2);
     stream_signal(done(c + 0, (unsigned)W), &sm.s_last);
@@ -413,11 +427,17 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
 
     // attention (the items read q|k|v, RMSNorm and rotate q and k, append
     // k and v to the pool and attend over it)
-    ring_top_up(a, rg, wave, lane, u_lim(u + kPrO));
+    if (!attn_wg) ring_top_up(a, rg, wave, lane, u_lim(u + kPrO));
     uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
+#ifdef QD_STEP_TRACE
+    AttnArgs at = a.attn;  // (trace builds) the item's events of layer 17 at slots 960..967
+    at.trace = l == 17 ? a.trace + (size_t)wg * 1024 + 960 : nullptr;
+#else
+    const AttnArgs& at = a.attn;
+#endif
     for (int t = wg; t < attn_n; t += W)
       attention_item<D, G, kAttnWavesPersistent, attn_pages_per_wave(1, true)>(
-          a.attn, alist, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), t, in_lds,
+          at, alist, ly.q_norm, ly.k_norm, pool_l, done(c + 1, n_heads), t, in_lds,
           Waiter{a.flags + (size_t)wg * kFlagStride, phase(c + 0), a.abort_flag, a.dev_flags,
                  a.spin_limit});
     mark(l * 20 + 4);
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       mark(l * 20 + 5);
       stage_input(a.attn_out, a.QD, nullptr, so.r0, so.r1);
       mark(l * 20 + 6);
-      project(u + kPrO, false, resid);
+      project(u + kPrO, u_lim(u + kPrO), false, resid);
       mark(l * 20 + 7);
       stream_signal(done(c + 2, (unsigned)W), &sm.s_last);
       mark(l * 20 + 8);
@@ -441,7 +461,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     mark(l * 20 + 9);
     stage_input(a.x, a.H, ly.post_norm, 0, 0);
     mark(l * 20 + 10);
-    project(u + kPrGu, true, [&](int, int rt, float y) {
+    project(u + kPrGu, u_lim(u + kPrGu), true, [&](int, int rt, float y) {
       const float uv = __shfl(y, 8 + (lane & 7), 16);
       if ((lane & 15) < 8)
         st_agent(a.act + rt * 8 + (lane & 7), y / (1.f + expf(-y)) * uv);
@@ -457,7 +477,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       mark(l * 20 + 13);
       stage_input(a.act, a.I, nullptr, sd.r0, sd.r1);
       mark(l * 20 + 14);
-      project(u + kPrDown, false, resid);
+      project(u + kPrDown, u_lim(u + kPrDown), false, resid);
       mark(l * 20 + 15);
       stream_signal(done(c + 4, (unsigned)W), &sm.s_last);
       mark(l * 20 + 16);
@@ -477,11 +497,11 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   {
     const StreamShare s = stream_share(a, u_lm, wave, W, wg);
     for (int g = s.r0; g < s.r1; ++g) {
-      Acc2 acc{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      Acc2 acc;
       ring_mfma_run(a, rg, wave, lane, u_end, s.KT, [&](int j) {
         return j * kTileCols + (lane >> 4) * 8;
       }, xsh, xsh + a.H, acc);
-      const f32x4 y = (acc.h + acc.l) * s_inv;
+      const f32x4 y = acc.total() * s_inv;
       const int row0 = (4 * g + wave) * kTileRows + (lane >> 4) * 4;
       if ((lane & 15) == 0 && a.logits != nullptr) *reinterpret_cast<f32x4*>(a.logits + row0) = y;
       float v = y[0];

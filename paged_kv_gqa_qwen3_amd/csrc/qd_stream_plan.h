@@ -31,115 +31,152 @@ enum StreamProj : int { kPrQkv = 0, kPrO = 1, kPrGu = 2, kPrDown = 3 };
 
 QD_HD int stream_u_end(const StreamArgs& a) { return a.L * kUnitsPerLayer + 1; }
 
-// One wave's share of one unit: the workgroup's row tiles (the LM head:
-// 64-row groups) [r0, r1), and of each the k-tiles kstart, kstart + kstep,
-// ... (the LM head: row tile 4*g + wave of group g, every k-tile).
+// One wave's share of one unit.  A unit of R row tiles (the LM head: 64-row
+// groups) with S K-splits has R*S pieces, piece r being k-tiles
+// [(r%S)*kps, min(KT, (r%S+1)*kps)) of row tile r/S; the workgroup owns
+// pieces [r0, r1), and of each the wave takes k-tiles kb + kstart, kb +
+// kstart + kstep, ... (the LM head: row tile 4*g + wave of group g, every
+// k-tile).
 struct StreamShare {
   const uint16_t* w;
-  int KT, R, r0, r1, kstart, kstep;
+  int KT, R, S, kps, r0, r1, kstart, kstep;
   bool lm;
 };
 
-// Workgroup wg of W owns rows [wg*R/W, (wg+1)*R/W) of a unit with R row
-// tiles (groups).
+// Workgroup wg of W owns pieces [wg*P/W, (wg+1)*P/W) of a unit with P
+// pieces.
 QD_HD StreamShare stream_share(const StreamArgs& a, int u, int wave, int W, int wg) {
   StreamShare s;
   if (u >= a.L * kUnitsPerLayer) {
-    s.w = a.lm; s.KT = a.H / kTileCols; s.R = a.V / kRowsPerGroup;
+    s.w = a.lm; s.KT = a.H / kTileCols; s.R = a.V / kRowsPerGroup; s.S = 1;
     s.kstart = 0; s.kstep = 1; s.lm = true;
   } else {
     const int p = u % kUnitsPerLayer;
     s.w = a.w[u];
     s.KT = (p == kPrO ? a.QD : p == kPrDown ? a.I : a.H) / kTileCols;
     s.R = (p == kPrQkv ? a.NQKV : p == kPrGu ? 2 * a.I : a.H) / kTileRows;
+    s.S = p == kPrQkv ? a.qkv_S : 1;
     s.kstart = wave; s.kstep = 4; s.lm = false;
   }
-  s.r0 = (int)((unsigned)wg * (unsigned)s.R / (unsigned)W);
-  s.r1 = (int)((unsigned)(wg + 1) * (unsigned)s.R / (unsigned)W);
+  s.kps = (s.KT + s.S - 1) / s.S;
+  const unsigned P = (unsigned)s.R * (unsigned)s.S;
+  s.r0 = (int)((unsigned)wg * P / (unsigned)W);
+  s.r1 = (int)((unsigned)(wg + 1) * P / (unsigned)W);
   return s;
 }
 
-// k-tiles of one row tile (group) that the wave takes.
-QD_HD int stream_row_tiles(const StreamShare& s) {
-  return s.kstart < s.KT ? (s.KT - s.kstart + s.kstep - 1) / s.kstep : 0;
+// k-tile range [kb, ke) of piece r.
+QD_HD void stream_piece(const StreamShare& s, int r, int& kb, int& ke) {
+  kb = (r % s.S) * s.kps;
+  ke = kb + s.kps < s.KT ? kb + s.kps : s.KT;
+}
+
+// k-tiles of piece r that the wave takes.
+QD_HD int stream_piece_tiles(const StreamShare& s, int r) {
+  int kb, ke;
+  stream_piece(s, r, kb, ke);
+  return kb + s.kstart < ke ? (ke - kb - s.kstart + s.kstep - 1) / s.kstep : 0;
 }
 
 QD_HD const unsigned char* stream_tile(const StreamShare& s, int r, int k, int wave) {
-  const int rt = s.lm ? 4 * r + wave : r;
+  const int rt = s.lm ? 4 * r + wave : r / s.S;
   return reinterpret_cast<const unsigned char*>(s.w) + ((size_t)rt * s.KT + k) * 1024;
 }
 
-// The loader's position in the wave's tile stream and the ring counts:
-// tiles issued and consumed so far, the slot the next load goes to.
+// One run of a wave's tile stream: n tiles at p, p + stride, ... (bytes),
+// all of unit u.  The host lists each wave's runs in stream order
+// (stream_runs), ending with a run of no tiles in unit u_end; the kernel's
+// loader walks them with scalar loads, so that its state stays small.
+struct StreamRun {
+  const unsigned char* p;
+  uint32_t n_u;     // n | u << 16
+  uint32_t stride;
+};
+static_assert(sizeof(StreamRun) == 16, "16-byte runs");
+
+// Host: emit(p, n, stride, u) for the runs of wave `wave` of workgroup wg,
+// in stream order, then the terminating run.
+template <class Emit>
+inline void stream_runs(const StreamArgs& a, int W, int wg, int wave, const Emit& emit) {
+  const int u_end = stream_u_end(a);
+  for (int u = 0; u < u_end; ++u) {
+    const StreamShare s = stream_share(a, u, wave, W, wg);
+    for (int r = s.r0; r < s.r1; ++r) {
+      int kb, ke;
+      stream_piece(s, r, kb, ke);
+      const int n = stream_piece_tiles(s, r);
+      if (n > 0) emit(stream_tile(s, r, kb + s.kstart, wave), n, s.kstep * 1024, u);
+    }
+  }
+  emit(static_cast<const unsigned char*>(nullptr), 0, 0, u_end);
+}
+
+// The loader: the current run, the next tile of it and the tiles left in
+// it, and the ring counts (tiles issued and consumed so far, the slot the
+// next load goes to).
 struct StreamLoader {
-  int u, r, k;               // unit (u_end: the stream has ended), row tile or group, k-tile
-  const unsigned char* p;    // tile (r, k) of this wave; null once the stream has ended
-  StreamShare s;
+  const StreamRun* run;
+  const unsigned char* p;
+  int n, u, stride;
   int issued, consumed, slot;
 };
 
-// The first tile of unit u or, when the wave has no share in it, of the
-// next unit where it has one.
-QD_HD void stream_seek(const StreamArgs& a, StreamLoader& c, int u, int wave, int W, int wg) {
-  const int u_end = stream_u_end(a);
-  for (; u < u_end; ++u) {
-    c.s = stream_share(a, u, wave, W, wg);
-    if (c.s.r0 < c.s.r1 && c.s.kstart < c.s.KT) break;
-  }
-  c.u = u;
-  c.r = c.s.r0;
-  c.k = c.s.kstart;
-  c.p = u < u_end ? stream_tile(c.s, c.r, c.k, wave) : nullptr;
-  if (u >= u_end) c.k = c.s.KT;  // no k-tile left: nothing matches a batch
+QD_HD void stream_fetch(StreamLoader& c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // constant address space: read with scalar loads (the runs never change)
+  const __attribute__((address_space(4))) StreamRun* r =
+      (const __attribute__((address_space(4))) StreamRun*)c.run;
+  c.p = r->p;
+  const uint32_t nu = r->n_u;
+  c.stride = (int)r->stride;
+#else
+  c.p = c.run->p;
+  const uint32_t nu = c.run->n_u;
+  c.stride = (int)c.run->stride;
+#endif
+  c.n = (int)(nu & 0xffffu);
+  c.u = (int)(nu >> 16);
 }
 
-QD_HD void stream_advance(const StreamArgs& a, StreamLoader& c, int wave, int W, int wg) {
-  c.k += c.s.kstep;
-  c.p += (size_t)c.s.kstep * 1024;
-  if (c.k < c.s.KT) return;
-  c.k = c.s.kstart;
-  if (++c.r < c.s.r1) {
-    c.p = stream_tile(c.s, c.r, c.k, wave);
-    return;
-  }
-  stream_seek(a, c, c.u + 1, wave, W, wg);
-}
-
-QD_HD void stream_start(const StreamArgs& a, StreamLoader& c, int wave, int W, int wg) {
+QD_HD void stream_start(StreamLoader& c, const StreamRun* runs) {
+  c.run = runs;
   c.issued = c.consumed = c.slot = 0;
-  stream_seek(a, c, 0, wave, W, wg);
+  stream_fetch(c);
 }
 
 // Issue loads (issue(tile, slot)) until kStreamRing tiles are loaded or in
 // flight ahead of the consumer, but none of a unit after u_limit and none
-// past the end of the stream.  The common case, a batch of kBatch slots
-// freed and as many tiles left in the current row, takes a straight-line
-// path.
+// past the end of the stream (the terminating run has no tiles).  The
+// common case, a batch of kBatch slots freed and as many tiles left in the
+// current run, takes a straight-line path.
 template <class Issue>
-QD_HD void stream_refill(const StreamArgs& a, StreamLoader& c, int wave, int W, int wg,
-                         int u_limit, const Issue& issue) {
-  const int u_end = stream_u_end(a);
-  if (c.issued - c.consumed <= kStreamRing - kBatch && c.u <= u_limit && c.u < u_end &&
-      c.k + (kBatch - 1) * c.s.kstep < c.s.KT) {
-    const size_t step = (size_t)c.s.kstep * 1024;
+QD_HD void stream_refill(StreamLoader& c, int u_limit, const Issue& issue) {
+  if (c.issued - c.consumed <= kStreamRing - kBatch && c.u <= u_limit && c.n >= kBatch) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       int slot = c.slot + i;
       if (slot >= kStreamRing) slot -= kStreamRing;
-      issue(c.p + i * step, slot);
+      issue(c.p + (size_t)i * c.stride, slot);
     }
     c.issued += kBatch;
     c.slot += kBatch;
     if (c.slot >= kStreamRing) c.slot -= kStreamRing;
-    c.k += (kBatch - 1) * c.s.kstep;
-    c.p += (kBatch - 1) * step;
-    stream_advance(a, c, wave, W, wg);
+    c.p += (size_t)kBatch * c.stride;
+    c.n -= kBatch;
+    if (c.n == 0) {
+      ++c.run;
+      stream_fetch(c);
+    }
   }
-  while (c.issued - c.consumed < kStreamRing && c.u <= u_limit && c.u < u_end) {
+  while (c.issued - c.consumed < kStreamRing && c.u <= u_limit && c.n > 0) {
     issue(c.p, c.slot);
     ++c.issued;
     c.slot = c.slot + 1 == kStreamRing ? 0 : c.slot + 1;
-    stream_advance(a, c, wave, W, wg);
+    c.p += c.stride;
+    if (--c.n == 0) {
+      ++c.run;
+      stream_fetch(c);
+    }
   }
 }
 

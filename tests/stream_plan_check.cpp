@@ -1,6 +1,7 @@
 // CPU replay of the batch-1 streaming step kernel's weight loader
-// (qd_stream_plan.h): for every wave of every workgroup, the refill and
-// consume calls are made in the kernel's order, and each issued tile must be
+// (qd_stream_plan.h): for every wave of every workgroup the host builds its
+// tile runs as the runtime does, the refill and consume calls are made in
+// the kernel's order, and each issued tile must be
 // the next tile of the wave's expected stream (hence inside its matrix),
 // land in the slot the consumer reads it from, be issued before it is
 // consumed, never overfill the ring, and the stream must end with every
@@ -41,13 +42,15 @@ const uint16_t* fake_base(int u) {
 }
 
 // The wave's tiles in consumption order, from the partition's definition:
-// unit by unit, the workgroup's rows [wg*R/W, (wg+1)*R/W), k-tiles wave,
-// wave + 4, ... (the LM head: row tile 4g + wave, every k-tile).
-std::vector<const unsigned char*> expected(const Shape& sh, int W, int wg, int wave) {
+// unit by unit, the workgroup's pieces [wg*P/W, (wg+1)*P/W) of the unit's P
+// = R*S pieces (piece r: row tile r/S, k-tiles [(r%S)*kps, ...+kps) within
+// K), of each the k-tiles kb + wave, kb + wave + 4, ... (the LM head: row
+// tile 4g + wave, every k-tile).
+std::vector<const unsigned char*> expected(const Shape& sh, int qS, int W, int wg, int wave) {
   std::vector<const unsigned char*> out;
   const int QD = sh.Hq * sh.D, NQKV = (sh.Hq + 2 * sh.Hkv) * sh.D;
   for (int u = 0; u <= 4 * sh.L; ++u) {
-    int R, KT, k0, ks;
+    int R, KT, k0, ks, S = 1;
     bool lm = u == 4 * sh.L;
     if (lm) {
       R = sh.V / 64; KT = sh.H / 32; k0 = 0; ks = 1;
@@ -56,29 +59,39 @@ std::vector<const unsigned char*> expected(const Shape& sh, int W, int wg, int w
       const int N = p == 0 ? NQKV : p == 1 ? sh.H : p == 2 ? 2 * sh.I : sh.H;
       const int K = p == 0 ? sh.H : p == 1 ? QD : p == 2 ? sh.H : sh.I;
       R = N / 16; KT = K / 32; k0 = wave; ks = 4;
+      if (p == 0) S = qS;
     }
-    const long r0 = (long)wg * R / W, r1 = (long)(wg + 1) * R / W;
+    const int kps = (KT + S - 1) / S;
+    const long P = (long)R * S;
+    const long r0 = (long)wg * P / W, r1 = (long)(wg + 1) * P / W;
     const unsigned char* base = reinterpret_cast<const unsigned char*>(fake_base(u));
     const long rows_total = lm ? 4L * R : R;  // row tiles of the matrix
-    for (long r = r0; r < r1; ++r)
-      for (int k = k0; k < KT; k += ks) {
-        const long rt = lm ? 4 * r + wave : r;
-        if (rt >= rows_total) std::abort();
+    for (long r = r0; r < r1; ++r) {
+      const int kb = (int)(r % S) * kps, ke = kb + kps < KT ? kb + kps : KT;
+      for (int k = kb + k0; k < ke; k += ks) {
+        const long rt = lm ? 4 * r + wave : r / S;
+        if (rt >= rows_total || k >= KT) std::abort();
         out.push_back(base + (rt * KT + k) * 1024);
       }
+    }
   }
   return out;
 }
 
-void run_wave(const Shape& sh, const StreamArgs& a, int W, int wg, int wave) {
-  const std::vector<const unsigned char*> want = expected(sh, W, wg, wave);
+void run_wave(const Shape& sh, const StreamArgs& a, int W, int wg, int wave, bool attn_wg) {
+  const std::vector<const unsigned char*> want = expected(sh, a.qkv_S, W, wg, wave);
   std::vector<Tile> got;
+  std::vector<StreamRun> runs;
+  stream_runs(a, W, wg, wave, [&](const unsigned char* p, int n, int stride, int u) {
+    if (n > 0xffff || u > 0xffff) fail(sh.name, W, wg, wave, "run fields overflow", n);
+    runs.push_back(StreamRun{p, (uint32_t)n | ((uint32_t)u << 16), (uint32_t)stride});
+  });
   StreamLoader ld;
-  stream_start(a, ld, wave, W, wg);
+  stream_start(ld, runs.data());
   const int u_end = stream_u_end(a);
   auto lim = [&](int u) { return wave == 0 ? u : u_end; };
   auto refill = [&](int u_limit) {
-    stream_refill(a, ld, wave, W, wg, u_limit, [&](const unsigned char* p, int slot) {
+    stream_refill(ld, u_limit, [&](const unsigned char* p, int slot) {
       got.push_back(Tile{p, slot});
     });
     if (ld.issued - ld.consumed > kStreamRing) fail(sh.name, W, wg, wave, "ring overfilled", ld.issued);
@@ -104,11 +117,11 @@ void run_wave(const Shape& sh, const StreamArgs& a, int W, int wg, int wave) {
     if (cs_slot >= kStreamRing) cs_slot -= kStreamRing;
     refill(u_limit);
   };
-  // the kernel's projection: per row tile (group), full batches, then singles
+  // the kernel's projection: per piece (row tile, group), full batches, then singles
   auto project = [&](int u, int u_limit) {
     const StreamShare s = stream_share(a, u, wave, W, wg);
-    const int n = stream_row_tiles(s);
     for (int r = s.r0; r < s.r1; ++r) {
+      const int n = stream_piece_tiles(s, r);
       int j = 0;
       for (; j + kBatch <= n; j += kBatch) consume(kBatch, u_limit);
       for (; j < n; ++j) consume(1, u_limit);
@@ -117,9 +130,11 @@ void run_wave(const Shape& sh, const StreamArgs& a, int W, int wg, int wave) {
   refill(lim(0));
   for (int l = 0; l < a.L; ++l) {
     const int u = 4 * l;
-    refill(lim(u + kPrQkv));  // wait for the layer's input
-    project(u + kPrQkv, lim(u + kPrQkv));
-    refill(lim(u + kPrO));    // attention
+    // a workgroup with attention items loads nothing past QKV until its items ran
+    const int lim_qkv = attn_wg ? u + kPrQkv : lim(u + kPrQkv);
+    refill(lim_qkv);          // wait for the layer's input
+    project(u + kPrQkv, lim_qkv);
+    if (!attn_wg) refill(lim(u + kPrO));  // before attention
     refill(lim(u + kPrO));    // wait for attention
     project(u + kPrO, lim(u + kPrO));
     refill(lim(u + kPrGu));
@@ -131,7 +146,8 @@ void run_wave(const Shape& sh, const StreamArgs& a, int W, int wg, int wave) {
   project(u_end - 1, u_end);
   if (ld.issued != ld.consumed) fail(sh.name, W, wg, wave, "tiles left unconsumed", ld.issued);
   if (ld.consumed != (long)want.size()) fail(sh.name, W, wg, wave, "stream length", ld.consumed);
-  if (ld.u != u_end || ld.p != nullptr) fail(sh.name, W, wg, wave, "loader not at the end", ld.u);
+  if (ld.u != u_end || ld.n != 0 || ld.run != &runs.back())
+    fail(sh.name, W, wg, wave, "loader not at the end", ld.u);
 }
 
 }  // namespace
@@ -147,18 +163,22 @@ int main() {
   const int grids[] = {256, 255, 64, 7, 1};
   long cases = 0;
   for (const Shape& sh : shapes) {
-    StreamArgs a{};
-    a.L = sh.L; a.H = sh.H; a.QD = sh.Hq * sh.D; a.I = sh.I; a.V = sh.V;
-    a.NQKV = (sh.Hq + 2 * sh.Hkv) * sh.D;
-    for (int u = 0; u < 4 * sh.L; ++u) a.w[u] = fake_base(u);
-    a.lm = fake_base(4 * sh.L);
-    for (int W : grids) {
-      if (sh.L > 4 && W < 64) continue;  // large models: realistic grids only
-      for (int wg = 0; wg < W; ++wg)
-        for (int wave = 0; wave < 4; ++wave) {
-          run_wave(sh, a, W, wg, wave);
-          ++cases;
-        }
+    for (int qS : {1, 2, 4}) {
+      StreamArgs a{};
+      a.L = sh.L; a.H = sh.H; a.QD = sh.Hq * sh.D; a.I = sh.I; a.V = sh.V;
+      a.NQKV = (sh.Hq + 2 * sh.Hkv) * sh.D;
+      a.qkv_S = qS;
+      for (int u = 0; u < 4 * sh.L; ++u) a.w[u] = fake_base(u);
+      a.lm = fake_base(4 * sh.L);
+      for (int W : grids) {
+        if (sh.L > 4 && (W < 64 || qS == 4)) continue;  // large models: realistic cases only
+        for (int wg = 0; wg < W; ++wg)
+          for (int wave = 0; wave < 4; ++wave)
+            for (int attn_wg = 0; attn_wg < 2; ++attn_wg) {
+              run_wave(sh, a, W, wg, wave, attn_wg != 0);
+              ++cases;
+            }
+      }
     }
   }
   std::printf("%ld wave streams checked, %d failures\n", cases, g_fail);

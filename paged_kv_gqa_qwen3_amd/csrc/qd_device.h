@@ -396,9 +396,10 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // Stage the input slice, 8 consecutive columns per thread and step.
   const int P = kMfma ? Ks + 8 : Ks;
   if constexpr (kMfma) {
-    // copy the pairs of columns 0..NB-1 (columns >= B only feed unused
-    // outputs); hi rows first, then lo rows
-    const int K8 = Ks / 8, n = NB * K8;
+    // copy the pairs of the B live columns, hi rows first, then lo rows
+    // (LDS columns B..NB-1 keep whatever they held: they only feed outputs
+    // that are never stored)
+    const int K8 = Ks / 8, n = B * K8;
     unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
     for (int idx = tid; idx < 2 * n; idx += 256) {
       const int hl = idx >= n, rem = idx - hl * n;

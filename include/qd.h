@@ -75,7 +75,14 @@ typedef struct qd_config {
   int32_t persistent;          /* 1: run each step of batch <= 4 as one persistent
                                   cooperative kernel (head_dim 128 with 4 query heads per
                                   KV head, or head_dim 64 with 2); larger batches, and
-                                  other shapes, take the per-stage kernels */
+                                  other shapes, take the per-stage kernels.  Batch 1
+                                  (with at most 64 layers, hidden <= 8192 and every
+                                  projection input <= 16384) runs as a kernel that
+                                  streams each wave's share of the weights through LDS
+                                  across stage boundaries and computes the projections
+                                  with MFMA on a bf16 hi/lo split of their input (about
+                                  16 significant bits; the per-stage batch-1 kernels
+                                  keep the input in fp32) */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a

@@ -172,18 +172,71 @@ __device__ __forceinline__ void ring_mfma(const StreamArgs& a, StreamRing& rg, i
 #endif
 }
 
-// acc += tiles j = 0 .. n-1 of the stream (column of tile j: kcol(j)), in
-// full batches, then one by one.
+// One batch of kBatch tiles as read from LDS: this lane's 16 bytes of each
+// weight tile and of the matching hi and lo input columns.
+struct StreamBatch {
+  u32x4 w[kBatch], h[kBatch], l[kBatch];
+};
+
+// Issue the LDS reads of the batch at tiles j0 .. j0+kBatch-1 of the run
+// (ring slots from the consumer's position on).
+template <class KCol>
+__device__ __forceinline__ void batch_read(const StreamRing& rg, int lane, int j0, const KCol& kcol,
+                                           const unsigned short* xh, const unsigned short* xl,
+                                           StreamBatch& bt) {
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    bt.w[i] = ring_read(rg, i, lane);
+    const int c = kcol(j0 + i);
+    bt.h[i] = *reinterpret_cast<const u32x4*>(xh + c);
+    bt.l[i] = *reinterpret_cast<const u32x4*>(xl + c);
+  }
+}
+
+__device__ __forceinline__ void batch_mfma(const StreamBatch& bt, Acc2& acc) {
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const bf16x8 w8 = __builtin_bit_cast(bf16x8, bt.w[i]);
+    acc.h[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bt.h[i]),
+                                                       acc.h[i], 0, 0, 0);
+    acc.l[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bt.l[i]),
+                                                       acc.l[i], 0, 0, 0);
+  }
+}
+
+// acc += tiles j = 0 .. n-1 of the stream (column of tile j: kcol(j)).  Full
+// batches are software-pipelined: the next batch's wait and LDS reads are
+// issued before the current batch's MFMAs, so that the LDS round trip
+// overlaps them and the refill; the tail goes one tile at a time.
 template <class KCol>
 __device__ __forceinline__ void ring_mfma_run(const StreamArgs& a, StreamRing& rg, int wave,
                                               int lane, int u_limit, int n, const KCol& kcol,
                                               const unsigned short* xh, const unsigned short* xl,
                                               Acc2& acc) {
-  int j0 = 0;
-  for (; j0 + kBatch <= n; j0 += kBatch)
-    ring_mfma<kBatch>(a, rg, wave, lane, u_limit, [&](int i) { return kcol(j0 + i); }, xh, xl,
-                      acc);
-  for (; j0 < n; ++j0)
+  const int nfull = n / kBatch;
+  if (nfull > 0) {
+#ifdef QD_STEP_TRACE
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+#endif
+    StreamBatch cur, nxt;
+    ring_top_up(a, rg, wave, lane, u_limit);
+    ring_wait<kBatch>(rg);
+    batch_read(rg, lane, 0, kcol, xh, xl, cur);
+    for (int b = 0; b < nfull; ++b) {
+      ring_release(rg, kBatch);  // (waits for this batch's reads)
+      ring_top_up(a, rg, wave, lane, u_limit);
+      if (b + 1 < nfull) {
+        ring_wait<kBatch>(rg);
+        batch_read(rg, lane, (b + 1) * kBatch, kcol, xh, xl, nxt);
+      }
+      batch_mfma(cur, acc);
+      cur = nxt;
+    }
+#ifdef QD_STEP_TRACE
+    rg.t_dot += __builtin_amdgcn_s_memtime() - t0;
+#endif
+  }
+  for (int j0 = nfull * kBatch; j0 < n; ++j0)
     ring_mfma<1>(a, rg, wave, lane, u_limit, [&](int) { return kcol(j0); }, xh, xl, acc);
 }
 

@@ -77,8 +77,14 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const AttnList list = attn_list<NW * PW>(a);
   const int items = attn_items(list, a.B);
+#ifdef QD_STEP_TRACE
+  AttnArgs at = a;  // (trace builds) 8 event slots per workgroup
+  if (a.trace != nullptr) at.trace = a.trace + (size_t)blockIdx.x * 8;
+#else
+  const AttnArgs& at = a;
+#endif
   for (int t = blockIdx.x; t < items; t += gridDim.x)
-    attention_item<D, G, NW, PW>(a, list, a.q_gain, a.k_gain, a.pool_layer, no_done(), t, smem,
+    attention_item<D, G, NW, PW>(at, list, a.q_gain, a.k_gain, a.pool_layer, no_done(), t, smem,
                                  NoWait{});
 }
 

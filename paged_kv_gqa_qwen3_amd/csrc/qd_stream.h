@@ -75,7 +75,8 @@ __device__ __forceinline__ void ring_top_up(const StreamArgs& a, StreamRing& rg,
   unsigned char* const slots = rg.slots;
   stream_refill(rg.ld, u_limit, [&](const unsigned char* tile, int slot) {
                   __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(tile) + lane,
-                                                   slots + (size_t)slot * 1024, 16, 0, 0);
+                                                   slots + (size_t)slot * 1024, 16, 0,
+                                                   kNonTemporal);
                 });
 }
 

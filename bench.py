@@ -3,10 +3,12 @@
 A step is one batched decode step of a Qwen3-style GQA decoder (embedding,
 36 x [RMSNorm + QKV, q/k-norm + RoPE + paged KV append + split-KV attention,
 O + residual, RMSNorm + gate/up + SwiGLU, down + residual], final RMSNorm, LM
-head, on-device argmax) over synthetic seeded weights and paged K/V, replayed
-from one captured hipGraph.  Steps are chained on the device: each step's
-next-token ids are the following step's input (two ping-pong id buffers, so
-the two graphs never change), and the positions advance on the device.
+head, on-device argmax) over synthetic seeded weights and paged K/V, run
+as the library runs it on a handle sized for the workload (qd_step_path: the
+batch-1 weight-streaming kernel, or the per-stage kernels replayed from one
+captured hipGraph).  Steps are chained on the device: each step's next-token
+ids are the following step's input (two ping-pong id buffers, so the graphs
+never change), and the positions advance on the device.
 
 Headline line: Qwen3-4B shape, batch 1, context 512 (value = tokens/s).  The
 same JSON line also carries batch 8 / 16 at context 256 and batch 1 at 8192
@@ -42,15 +44,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("qd_device.h", "qd_kernels.hip")
+KERNEL_SOURCES = {
+    "per_stage": ("qd_device.h", "qd_kernels.hip"),
+    "stream_step": ("qd_device.h", "qd_stream_plan.h", "qd_stream.h", "qd_stream.hip"),
+}
 
 
-def kernel_source_sha256():
-    """sha256 over the device-code sources of the per-stage kernels, in order."""
+def kernel_source_sha256(kind="per_stage"):
+    """sha256 over the device-code sources of the per-stage kernels, or of the
+    batch-1 streaming kernel, in order."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(REPO, "paged_kv_gqa_qwen3_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -58,11 +64,12 @@ def kernel_source_sha256():
 def measured_traffic(kernel_class, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
-    path = os.path.join(REPO, "profiles", f"traffic_{workload}.json")
+    kind = "stream_step" if kernel_class == "stream_step" else "per_stage"
+    path = os.path.join(REPO, "profiles", f"traffic_{workload}_{kind}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256(kind):
         return None
     return rec.get("traffic_bytes_per_launch", {}).get(kernel_class)
 
@@ -176,6 +183,62 @@ def cpu_baseline(w, W, batch, budget_s=20.0):
                       f"{int(batch.positions[0])}+), {dt:.1f} s, fp64 C oracle with OpenMP"}
 
 
+def stream_roofline(w, ms, steps, nbytes):
+    """The batch-1 step is one kernel launch: its algorithmic bytes (weights
+    plus the K/V read and appended) per launch over its mean duration, timed
+    with HIP events on the library's stream over the timed steps."""
+    avg_us = ms / steps * 1e3
+    per_launch = nbytes / steps
+    gbps = per_launch / (avg_us * 1e-6) / 1e9
+    return {
+        "roofline": {"bound": "hbm", "kernel": "stream_step", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("stream_step", w.name),
+                     "algorithmic_bytes": int(per_launch), "avg_us": round(avg_us, 3)},
+    }
+
+
+def per_stage_roofline(torch, dec, run, shape, w, batch):
+    """Per-stage path: every class's time (projections replayed alone as a
+    graph between two events on the library's stream: avg_us; every class,
+    attention included, from the step run with an event between kernels:
+    events_us, which adds a few us per kernel); the roofline is that of the
+    class with the largest share of the step."""
+    prof = profile_classes(torch, dec, run)
+    ctx_mid = batch.positions.astype(np.int64) + 1
+    per_class = {}
+    for c, (tot_ms, n) in prof.items():
+        if n == 0:
+            continue
+        ev_us = tot_ms / n * 1e3
+        if c in ("qkv", "o_proj", "gate_up", "down", "lm_head"):
+            byts = gemv_bytes(shape, c)
+            avg_us = binding.qd_profile_class(dec.handle, w.batch, c, reps=20)
+        elif c == "attention":
+            byts = attention_bytes(shape, ctx_mid)
+            avg_us = ev_us
+        else:
+            byts = w.batch * shape.hidden * 2
+            avg_us = ev_us
+        per_class[c] = {"launches_per_step": n // 5, "avg_us": round(avg_us, 3),
+                        "events_us": round(ev_us, 3),
+                        "bytes_per_launch": int(byts),
+                        "GBps": round(byts / (avg_us * 1e-6) / 1e9, 1),
+                        "ms_per_step": round(avg_us * (n // 5) / 1e3, 4)}
+    dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
+    d = per_class[dom]
+    return {
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom, w.name),
+                     "algorithmic_bytes": d["bytes_per_launch"],
+                     "avg_us": d["avg_us"]},
+        "kernel_classes": per_class,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,16 +247,17 @@ def main():
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--mode", choices=("persistent", "graph"), default="graph",
-                    help="one persistent cooperative kernel per step, or one captured "
-                         "hipGraph of per-stage kernels per step")
+    ap.add_argument("--mode", choices=("auto", "graph"), default="auto",
+                    help="auto: a persistent handle, on which the library runs each step as "
+                         "the batch-1 streaming kernel, the persistent kernel or the per-stage "
+                         "graph (qd_step_path); graph: the per-stage graph only")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the decode step "
-              "has no multi-GPU path in this build", file=sys.stderr)
+              "has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -220,41 +284,28 @@ def main():
 
     for shape_name, group in by_shape.items():
         shape = group[0].shape
-        # pages for every position the timed and warmup steps reach
-        span = {w.name: max(w.steps, args.steps + args.warmup) for w in group}
-        batches = {w.name: synth.make_paged_batch(shape, synth.context_lengths(w), span[w.name],
-                                                  w.seed)
-                   for w in group}
-        maxp = max(b.max_pages for b in batches.values())
-        npages = max(b.num_pages for b in batches.values())
-        for w in group:  # one pool shape per handle: pad every pool to npages pages
-            b = batches[w.name]
-            if b.num_pages < npages:
-                batches[w.name] = synth.make_paged_batch(
-                    shape, synth.context_lengths(w), span[w.name], w.seed,
-                    spare_pages=npages - b.num_pages)
-            bt = batches[w.name].block_tables
-            if bt.shape[1] < maxp:
-                pad = np.full((bt.shape[0], maxp - bt.shape[1]), batches[w.name].poison_page,
-                              np.int32)
-                batches[w.name].block_tables = np.ascontiguousarray(np.concatenate([bt, pad], 1))
         log(f"[bench] generating {shape_name} weights")
         t0 = time.perf_counter()
         W = synth.make_weights(shape, WEIGHT_SEED[shape_name])
         log(f"[bench] weights ready in {time.perf_counter() - t0:.1f}s")
         from paged_kv_gqa_qwen3_amd.decoder import Decoder
 
-        dec = Decoder(shape, max(w.batch for w in group), maxp, npages, use_graphs=True,
-                      persistent=(args.mode == "persistent"))
-        dec.load_numpy_weights(W)
         for w in group:
-            batch = batches[w.name]
-            log(f"[bench] {w.name}: timing {args.steps} steps after {args.warmup} warmup")
+            # one handle per workload, sized for the positions its timed and
+            # warmup steps reach
+            span = max(w.steps, args.steps + args.warmup)
+            batch = synth.make_paged_batch(shape, synth.context_lengths(w), span, w.seed)
+            dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True,
+                          persistent=(args.mode == "auto"))
+            dec.load_numpy_weights(W)
+            path = dec.step_path(w.batch)
+            log(f"[bench] {w.name}: {path} path, timing {args.steps} steps after "
+                f"{args.warmup} warmup")
             run, ms, wall, nbytes = time_workload(torch, dec, w, batch, args.steps, args.warmup)
             tok_s = args.steps * w.batch / (ms / 1e3)
             gbps = nbytes / (ms / 1e3) / 1e9
             results[w.name] = {
-                "workload": w.name, "batch": w.batch,
+                "workload": w.name, "batch": w.batch, "path": path,
                 "context0": [int(c) for c in batch.positions[:4]] + (["..."] if w.batch > 4 else []),
                 "tokens_per_s": round(tok_s, 2), "ms_per_step": round(ms / args.steps, 4),
                 "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -263,49 +314,16 @@ def main():
             log(f"[bench] {w.name}: {tok_s:.1f} tok/s, {ms / args.steps:.4f} ms/step, "
                 f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
             if w.name == HEADLINE:
-                # Projections: each class's launches for all layers replayed
-                # alone as a graph between two events on the library's stream
-                # (avg_us).  Every class, attention included: the step run
-                # with an event between kernels (events_us; event records add
-                # a few us per kernel).
-                prof = profile_classes(torch, dec, run)
-                ctx_mid = batch.positions.astype(np.int64) + 1
-                per_class = {}
-                for c, (tot_ms, n) in prof.items():
-                    if n == 0:
-                        continue
-                    ev_us = tot_ms / n * 1e3
-                    if c in ("qkv", "o_proj", "gate_up", "down", "lm_head"):
-                        byts = gemv_bytes(shape, c)
-                        avg_us = binding.qd_profile_class(dec.handle, w.batch, c, reps=20)
-                    elif c == "attention":
-                        byts = attention_bytes(shape, ctx_mid)
-                        avg_us = ev_us
-                    else:
-                        byts = w.batch * shape.hidden * 2
-                        avg_us = ev_us
-                    per_class[c] = {"launches_per_step": n // 5, "avg_us": round(avg_us, 3),
-                                    "events_us": round(ev_us, 3),
-                                    "bytes_per_launch": int(byts),
-                                    "GBps": round(byts / (avg_us * 1e-6) / 1e9, 1),
-                                    "ms_per_step": round(avg_us * (n // 5) / 1e3, 4)}
-                dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
-                d = per_class[dom]
-                headline_extra = {
-                    "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["GBps"],
-                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                 "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
-                                 "traffic": measured_traffic(dom, w.name),
-                                 "algorithmic_bytes": d["bytes_per_launch"],
-                                 "avg_us": d["avg_us"]},
-                    "kernel_classes": per_class,
-                }
+                if path == "stream":
+                    headline_extra = stream_roofline(w, ms, args.steps, nbytes)
+                else:
+                    headline_extra = per_stage_roofline(torch, dec, run, shape, w, batch)
                 if not args.no_cpu_baseline:
                     log("[bench] timing the CPU oracle on a bounded sample")
                     headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)
             del run
+            dec.close()
             torch.cuda.empty_cache()
-        dec.close()
         del W
 
     h = results[HEADLINE]
@@ -316,7 +334,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 paged K/V)",
         "config": {"workload": "Qwen3-4B-shaped decode, batch 1, context 512, 16-token pages, "
                                "shuffled block table", "name": HEADLINE, "batch": 1,
-                   "context0": 512, "parallelism": "single GPU", "mode": args.mode},
+                   "context0": 512, "parallelism": "single GPU", "mode": args.mode,
+                   "path": h["path"]},
         "achieved_GBps": h["achieved_GBps"], "hbm_frac": h["hbm_frac"],
     }
     out.update(headline_extra)

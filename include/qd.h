@@ -69,20 +69,22 @@ typedef struct qd_config {
   double rope_theta;           /* RoPE base (Qwen3: 1e6) */
   int32_t page_size;           /* tokens per KV page; must be 16 */
   int32_t max_batch;           /* largest batch passed to qd_decode_step (1..64) */
-  int32_t max_pages_per_seq;   /* block-table row length; at most 4096 (65536 tokens) */
+  int32_t max_pages_per_seq;   /* block-table row length; at most 2048 (32768 tokens) */
   int32_t num_pages;           /* pages in the caller's pool */
   int32_t use_graphs;          /* 1: replay one captured hipGraph per batch size */
   int32_t persistent;          /* 1: run each step of batch <= 4 as one persistent
                                   cooperative kernel (head_dim 128 with 4 query heads per
                                   KV head, or head_dim 64 with 2); larger batches, and
                                   other shapes, take the per-stage kernels.  Batch 1
-                                  (with at most 64 layers, hidden <= 8192 and every
-                                  projection input <= 16384) runs as a kernel that
-                                  streams each wave's share of the weights through LDS
-                                  across stage boundaries and computes the projections
-                                  with MFMA on a bf16 hi/lo split of their input (about
-                                  16 significant bits; the per-stage batch-1 kernels
-                                  keep the input in fp32) */
+                                  (with max_pages_per_seq <= 128, at most 64 layers,
+                                  hidden <= 8192 and every projection input <= 16384)
+                                  runs as a kernel that streams each wave's share of
+                                  the weights through LDS across stage boundaries and
+                                  computes the projections with MFMA on a bf16 hi/lo
+                                  split of their input (about 16 significant bits; the
+                                  per-stage batch-1 kernels keep the input in fp32); on
+                                  a handle with longer block-table rows batch 1 takes
+                                  the per-stage kernels (qd_step_path tells which) */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
@@ -193,6 +195,16 @@ int qd_device_status(qd_handle* h, int32_t* flags);
 
 /* The handle's stream (a hipStream_t), for callers that time or order work. */
 void* qd_stream(const qd_handle* h);
+
+/* How qd_decode_step runs a step of `batch` sequences on this handle. */
+#define QD_PATH_STAGED 0      /* per-stage kernels launched one by one */
+#define QD_PATH_GRAPH 1       /* per-stage kernels replayed from a captured hipGraph */
+#define QD_PATH_PERSISTENT 2  /* one persistent cooperative kernel per step */
+#define QD_PATH_STREAM 3      /* batch 1: the weight-streaming persistent kernel */
+
+/* One of QD_PATH_*, or QD_EINVAL for a NULL handle or a batch outside
+ * 1..max_batch.  No GPU work. */
+int qd_step_path(const qd_handle* h, int32_t batch);
 
 /* Free everything the handle owns (waits for its stream first). */
 void qd_destroy(qd_handle* h);

@@ -28,8 +28,8 @@ QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
-            "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream", "qd_destroy",
-            "qd_last_error")
+            "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
+            "qd_step_path", "qd_destroy", "qd_last_error")
 
 PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
 
@@ -95,6 +95,8 @@ def load_library():
         lib.qd_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
         lib.qd_stream.restype = P
         lib.qd_stream.argtypes = [P]
+        lib.qd_step_path.restype = ctypes.c_int
+        lib.qd_step_path.argtypes = [P, ctypes.c_int32]
         lib.qd_destroy.restype = None
         lib.qd_destroy.argtypes = [P]
         lib.qd_last_error.restype = ctypes.c_char_p
@@ -203,6 +205,16 @@ def qd_device_status(handle: int) -> int:
 
 def qd_stream(handle: int) -> int:
     return load_library().qd_stream(handle) or 0
+
+
+STEP_PATHS = ("staged", "graph", "persistent", "stream")
+
+
+def qd_step_path(handle: int, batch: int) -> str:
+    """How a step of `batch` sequences runs on this handle (see STEP_PATHS)."""
+    v = load_library().qd_step_path(handle, batch)
+    _check(v if v < 0 else 0, handle)
+    return STEP_PATHS[v]
 
 
 def qd_destroy(handle: int) -> None:

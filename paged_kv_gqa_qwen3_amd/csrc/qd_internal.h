@@ -146,6 +146,10 @@ struct StreamRun;
 // projection's weights through rings in LDS.
 constexpr int kStreamRing = 24;  // 1 KB weight tiles a wave keeps loaded or in flight
 constexpr int kStreamMaxLayers = 64;
+// Longest block-table row (pages) of a handle that runs batch 1 as the
+// streaming kernel: its attention runs on few workgroups while the others
+// hold their weight rings, which pays for short contexts only.
+constexpr int kStreamMaxPages = 128;
 constexpr int kStreamStageVec = 16;  // 4-float groups of a staged input per thread
 struct StreamArgs {
   EmbedArgs embed;
@@ -196,8 +200,9 @@ constexpr int gemv_nb(int B) {
 // sequence covers waves * pages.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnWavesPersistent = 4;
+constexpr int kAttnPagesPersistent = 1;
 constexpr int attn_pages_per_wave(int B, bool persistent) {
-  return persistent ? 2 : B <= 4 ? 1 : 3;
+  return persistent ? kAttnPagesPersistent : B <= 4 ? 1 : 3;
 }
 constexpr int attn_pages_per_split(int B, bool persistent) {
   return (persistent ? kAttnWavesPersistent : kAttnWaves) * attn_pages_per_wave(B, persistent);
@@ -213,7 +218,7 @@ hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
 // waves, pages: kAttnWaves with 1 or 3 pages per wave, or the persistent
-// kernel's item shape (kAttnWavesPersistent, 2; head shapes the persistent
+// kernel's item shape (kAttnWavesPersistent, kAttnPagesPersistent; head shapes the persistent
 // kernel supports only).
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s);

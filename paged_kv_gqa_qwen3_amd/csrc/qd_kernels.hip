@@ -171,9 +171,11 @@ static hipError_t launch_attention_dg(const AttnArgs& a, int pages, hipStream_t 
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s) {
   if (waves == kAttnWavesPersistent) {  // the persistent kernel's item shape
-    if (pages != 2) return hipErrorInvalidValue;
-    if (head_dim == 128 && group == 4) return launch_attention_t<128, 4, kAttnWavesPersistent, 2>(a, s);
-    if (head_dim == 64 && group == 2) return launch_attention_t<64, 2, kAttnWavesPersistent, 2>(a, s);
+    if (pages != kAttnPagesPersistent) return hipErrorInvalidValue;
+    if (head_dim == 128 && group == 4)
+      return launch_attention_t<128, 4, kAttnWavesPersistent, kAttnPagesPersistent>(a, s);
+    if (head_dim == 64 && group == 2)
+      return launch_attention_t<64, 2, kAttnWavesPersistent, kAttnPagesPersistent>(a, s);
     return hipErrorInvalidValue;
   }
   if (waves != kAttnWaves || (pages != 1 && pages != 3)) return hipErrorInvalidValue;

@@ -90,6 +90,7 @@ struct qd_handle {
 
   // persistent step
   bool persistent = false;
+  bool long_ctx = false;  // max_pages_per_seq > kStreamMaxPages: batch 1 takes the per-stage kernels
   LayerDev* layers_dev = nullptr;
   unsigned* step_cnt = nullptr;
   unsigned* step_flags = nullptr;  // [2 * CUs][32]
@@ -155,8 +156,12 @@ constexpr size_t kLdsCapPersistent = 72 * 1024;
 constexpr int kMinValuItems = 128;
 
 // The persistent kernel serves batches <= 4 (VALU items); larger batches
-// always take the per-stage kernels.
-bool use_persistent(const qd_handle* h, int B) { return h->persistent && gemv_nb(B) <= 4; }
+// always take the per-stage kernels, and so does batch 1 on a handle sized
+// for long contexts (there the per-stage attention kernel, which spreads a
+// long sequence over many more workgroups, is faster).
+bool use_persistent(const qd_handle* h, int B) {
+  return h->persistent && gemv_nb(B) <= 4 && !(B == 1 && h->long_ctx);
+}
 
 // A persistent handle runs batch 1 as the streaming step kernel when its
 // shapes fit (decided in qd_create).
@@ -258,8 +263,11 @@ int validate_config(const qd_config* c) {
     return fail(nullptr, QD_EUNSUPPORTED, "query heads per KV head must be 1, 2 or 4");
   if (c->intermediate % 32) return fail(nullptr, QD_EUNSUPPORTED, "intermediate must be a multiple of 32");
   if (c->vocab % 64) return fail(nullptr, QD_EUNSUPPORTED, "vocab must be a multiple of 64");
-  if ((long long)c->max_pages_per_seq > (long long)kMaxSplitsStaged * attn_pages_per_split(1, false))
-    return fail(nullptr, QD_EUNSUPPORTED, "max_pages_per_seq too large (at most 4096 pages)");
+  // (every split's (max, sum) pair of one sequence is staged in LDS by the combine)
+  constexpr int kMaxPages =
+      kMaxSplitsStaged * std::min(attn_pages_per_split(1, false), attn_pages_per_split(1, true));
+  if ((long long)c->max_pages_per_seq > (long long)kMaxPages)
+    return fail(nullptr, QD_EUNSUPPORTED, "max_pages_per_seq too large");
   return QD_OK;
 }
 
@@ -550,7 +558,7 @@ int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
 // 1/grid of every projection's row tiles.
 int setup_stream(qd_handle* h) {
   // (inputs under an RMSNorm gain are the hidden size: at most 8192)
-  if (!h->persistent || h->L > kStreamMaxLayers || h->H > 8192) return QD_OK;
+  if (!h->persistent || h->long_ctx || h->L > kStreamMaxLayers || h->H > 8192) return QD_OK;
   const int kmax = std::max(h->H, std::max(h->QD, h->I));
   if (kmax > 4 * 256 * kStreamStageVec) return QD_OK;  // staged input: 16 floats per thread
   auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
@@ -767,6 +775,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->expected["model.norm.weight"] = 0;
 
   h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
+  h->long_ctx = cfg->max_pages_per_seq > kStreamMaxPages;
   if ((rc = setup_stream(h))) return bail(rc);
 
   // activations and scratch
@@ -1087,6 +1096,14 @@ int qd_device_status(qd_handle* h, int32_t* flags) {
 }
 
 void* qd_stream(const qd_handle* h) { return h ? static_cast<void*>(h->stream) : nullptr; }
+
+int qd_step_path(const qd_handle* h, int32_t batch) {
+  if (!h || batch < 1 || batch > h->cfg.max_batch) return QD_EINVAL;
+  if (use_stream(h, batch)) return QD_PATH_STREAM;
+  if (use_persistent(h, batch)) return QD_PATH_PERSISTENT;
+  static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
+  return h->cfg.use_graphs && !no_graph ? QD_PATH_GRAPH : QD_PATH_STAGED;
+}
 
 void qd_destroy(qd_handle* h) {
   if (!h) return;

@@ -113,32 +113,46 @@ __device__ __forceinline__ void ring_release(StreamRing& rg, int n) {
   if (rg.cs_slot >= kStreamRing) rg.cs_slot -= kStreamRing;
 }
 
-// Accumulators of a wave's 16-row tile sums: for each position of a batch,
-// the hi and the lo halves of the input (so that the MFMAs of a batch do not
-// wait on each other); lane l holds rows 4*(l/16) .. +3 (all 16 columns are
-// the same).
+// Accumulators of a wave's 16-row tile sums.  The input's bf16 pair is
+// spread over the MFMA's 16 columns: the lanes of columns 0..7 supply hi,
+// those of columns 8..15 lo, so that one MFMA per tile yields both products
+// (columns 0..7 hold W*hi, 8..15 W*lo); kBatch accumulators keep the MFMAs of
+// a batch independent.  Lane l holds rows 4*(l/16) .. +3 of column l % 16.
 struct Acc2 {
-  f32x4 h[kBatch], l[kBatch];
+  f32x4 a[kBatch];
   __device__ __forceinline__ Acc2() {
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) h[i] = l[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kBatch; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // W*(hi + lo) of the lane's 4 rows, the same in all 16 lanes of a row
+  // group (every lane takes part: a column's partner is lane ^ 8)
   __device__ __forceinline__ f32x4 total() const {
-    f32x4 t = h[0] + l[0];
+    f32x4 t = a[0];
 #pragma unroll
-    for (int i = 1; i < kBatch; ++i) t += h[i] + l[i];
-    return t;
+    for (int i = 1; i < kBatch; ++i) t += a[i];
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = t[e] + __shfl_xor(t[e], 8);
+    return r;
   }
 };
 
-// acc += the next N tiles of the stream in order, the i-th against input
-// columns kcol(i) .. +8 of the staged bf16 pair (xh, xl); the freed slots
-// are refilled before the arithmetic.
-template <int N, class KCol>
-__device__ __forceinline__ void ring_mfma(const StreamArgs& a, StreamRing& rg, int wave, int lane,
-                                          int u_limit, const KCol& kcol,
-                                          const unsigned short* xh, const unsigned short* xl,
-                                          Acc2& acc) {
+// This lane's input column pointer: hi for columns 0..7, lo for 8..15 (the
+// pair is hi [K] then lo [K]), at k-group lane / 16 of a tile.
+__device__ __forceinline__ const unsigned short* stream_in_lane(const unsigned short* xsh, int K,
+                                                               int lane) {
+  return xsh + ((lane & 8) ? K : 0) + (lane >> 4) * 8;
+}
+
+__device__ __forceinline__ f32x4 tile_mfma(u32x4 w, u32x4 x, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                 __builtin_bit_cast(bf16x8, x), acc, 0, 0, 0);
+}
+
+// acc += the next tile of the stream against the input at xk (this lane's
+// 16 bytes of it); the freed slot is refilled before the arithmetic.
+__device__ __forceinline__ void ring_mfma1(const StreamArgs& a, StreamRing& rg, int wave, int lane,
+                                           int u_limit, const unsigned short* xk, Acc2& acc) {
 #ifdef QD_STEP_TRACE
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
 #endif
@@ -146,99 +160,95 @@ __device__ __forceinline__ void ring_mfma(const StreamArgs& a, StreamRing& rg, i
 #ifdef QD_STEP_TRACE
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
 #endif
-  ring_wait<N>(rg);
+  ring_wait<1>(rg);
 #ifdef QD_STEP_TRACE
   rg.t_wait += __builtin_amdgcn_s_memtime() - t1;
 #endif
-  u32x4 wv[N], vh[N], vl[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    wv[i] = ring_read(rg, i, lane);
-    const int c = kcol(i);
-    vh[i] = *reinterpret_cast<const u32x4*>(xh + c);
-    vl[i] = *reinterpret_cast<const u32x4*>(xl + c);
-  }
-  ring_release(rg, N);
+  const u32x4 w = ring_read(rg, 0, lane);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(xk);
+  ring_release(rg, 1);
   ring_top_up(a, rg, wave, lane, u_limit);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const bf16x8 w8 = __builtin_bit_cast(bf16x8, wv[i]);
-    acc.h[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vh[i]),
-                                                       acc.h[i], 0, 0, 0);
-    acc.l[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, vl[i]),
-                                                       acc.l[i], 0, 0, 0);
-  }
+  acc.a[0] = tile_mfma(w, x, acc.a[0]);
 #ifdef QD_STEP_TRACE
   rg.t_dot += __builtin_amdgcn_s_memtime() - t0;
 #endif
 }
 
 // One batch of kBatch tiles as read from LDS: this lane's 16 bytes of each
-// weight tile and of the matching hi and lo input columns.
+// weight tile and of its input columns.
 struct StreamBatch {
-  u32x4 w[kBatch], h[kBatch], l[kBatch];
+  u32x4 w[kBatch], x[kBatch];
 };
 
-// Issue the LDS reads of the batch at tiles j0 .. j0+kBatch-1 of the run
-// (ring slots from the consumer's position on).
-template <class KCol>
-__device__ __forceinline__ void batch_read(const StreamRing& rg, int lane, int j0, const KCol& kcol,
-                                           const unsigned short* xh, const unsigned short* xl,
-                                           StreamBatch& bt) {
+// Issue the LDS reads of the batch at the consumer's next kBatch slots, the
+// tiles' inputs at xk + i * KSTEP k-tiles.  Slots that do not wrap around the
+// ring are addressed from one base with immediate offsets.
+template <int KSTEP>
+__device__ __forceinline__ void batch_read(const StreamRing& rg, int lane,
+                                           const unsigned short* xk, StreamBatch& bt) {
+  if (rg.cs_slot <= kStreamRing - kBatch) {
+    const unsigned char* base = rg.slots + (size_t)rg.cs_slot * 1024 + lane * 16;
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    bt.w[i] = ring_read(rg, i, lane);
-    const int c = kcol(j0 + i);
-    bt.h[i] = *reinterpret_cast<const u32x4*>(xh + c);
-    bt.l[i] = *reinterpret_cast<const u32x4*>(xl + c);
+    for (int i = 0; i < kBatch; ++i) bt.w[i] = *reinterpret_cast<const u32x4*>(base + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) bt.w[i] = ring_read(rg, i, lane);
   }
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i)
+    bt.x[i] = *reinterpret_cast<const u32x4*>(xk + i * KSTEP * kTileCols);
 }
 
 __device__ __forceinline__ void batch_mfma(const StreamBatch& bt, Acc2& acc) {
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    const bf16x8 w8 = __builtin_bit_cast(bf16x8, bt.w[i]);
-    acc.h[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bt.h[i]),
-                                                       acc.h[i], 0, 0, 0);
-    acc.l[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bt.l[i]),
-                                                       acc.l[i], 0, 0, 0);
-  }
+  for (int i = 0; i < kBatch; ++i) acc.a[i] = tile_mfma(bt.w[i], bt.x[i], acc.a[i]);
 }
 
-// acc += tiles j = 0 .. n-1 of the stream (column of tile j: kcol(j)).  Full
-// batches are software-pipelined: the next batch's wait and LDS reads are
-// issued before the current batch's MFMAs, so that the LDS round trip
-// overlaps them and the refill; the tail goes one tile at a time.
-template <class KCol>
+// acc += tiles j = 0 .. n-1 of the stream, tile j against the input at
+// xk + j * KSTEP k-tiles.  Full batches are software-pipelined over two
+// register sets: the next batch's wait and LDS reads are issued before the
+// current batch's MFMAs, so that the LDS round trip overlaps them and the
+// refill; the tail goes one tile at a time.
+template <int KSTEP>
 __device__ __forceinline__ void ring_mfma_run(const StreamArgs& a, StreamRing& rg, int wave,
-                                              int lane, int u_limit, int n, const KCol& kcol,
-                                              const unsigned short* xh, const unsigned short* xl,
-                                              Acc2& acc) {
+                                              int lane, int u_limit, int n,
+                                              const unsigned short* xk, Acc2& acc) {
+  constexpr int kStep = kBatch * KSTEP * kTileCols;  // input elements between batches
   const int nfull = n / kBatch;
   if (nfull > 0) {
 #ifdef QD_STEP_TRACE
     const unsigned long long t0 = __builtin_amdgcn_s_memtime();
 #endif
-    StreamBatch cur, nxt;
+    StreamBatch A, B;
     ring_top_up(a, rg, wave, lane, u_limit);
     ring_wait<kBatch>(rg);
-    batch_read(rg, lane, 0, kcol, xh, xl, cur);
-    for (int b = 0; b < nfull; ++b) {
-      ring_release(rg, kBatch);  // (waits for this batch's reads)
+    batch_read<KSTEP>(rg, lane, xk, A);
+    // batches 2p (in A) and 2p + 1 (in B)
+    for (int p = 0; p < nfull / 2; ++p) {
+      ring_release(rg, kBatch);  // (waits for batch 2p's reads)
       ring_top_up(a, rg, wave, lane, u_limit);
-      if (b + 1 < nfull) {
+      ring_wait<kBatch>(rg);
+      batch_read<KSTEP>(rg, lane, xk + (2 * p + 1) * kStep, B);
+      batch_mfma(A, acc);
+      ring_release(rg, kBatch);  // (waits for batch 2p + 1's reads)
+      ring_top_up(a, rg, wave, lane, u_limit);
+      if (2 * p + 2 < nfull) {
         ring_wait<kBatch>(rg);
-        batch_read(rg, lane, (b + 1) * kBatch, kcol, xh, xl, nxt);
+        batch_read<KSTEP>(rg, lane, xk + (2 * p + 2) * kStep, A);
       }
-      batch_mfma(cur, acc);
-      cur = nxt;
+      batch_mfma(B, acc);
+    }
+    if (nfull & 1) {  // the last batch, in A
+      ring_release(rg, kBatch);
+      ring_top_up(a, rg, wave, lane, u_limit);
+      batch_mfma(A, acc);
     }
 #ifdef QD_STEP_TRACE
     rg.t_dot += __builtin_amdgcn_s_memtime() - t0;
 #endif
   }
-  for (int j0 = nfull * kBatch; j0 < n; ++j0)
-    ring_mfma<1>(a, rg, wave, lane, u_limit, [&](int) { return kcol(j0); }, xh, xl, acc);
+  for (int j = nfull * kBatch; j < n; ++j)
+    ring_mfma1(a, rg, wave, lane, u_limit, xk + j * KSTEP * kTileCols, acc);
 }
 
 // Wait until the step reached `phase` (every wave polls its workgroup's
@@ -418,17 +428,16 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   // a row tile.
   auto project = [&](int u, int u_limit, bool norm, auto&& epi) {
     const StreamShare s = stream_share(a, u, wave, W, wg);
-    const int K = s.KT * kTileCols;
+    const unsigned short* const xin = stream_in_lane(xsh, s.KT * kTileCols, lane);
     for (int r = s.r0; r < s.r1; ++r) {
       int kb, ke;
       stream_piece(s, r, kb, ke);
       Acc2 acc;
-      ring_mfma_run(a, rg, wave, lane, u_limit, stream_piece_tiles(s, r), [&](int j) {
-        return (kb + s.kstart + 4 * j) * kTileCols + (lane >> 4) * 8;
-      }, xsh, xsh + K, acc);
+      ring_mfma_run<kStreamKStep>(a, rg, wave, lane, u_limit, stream_piece_tiles(s, r),
+                                  xin + (kb + s.kstart) * kTileCols, acc);
+      const f32x4 t = acc.total();
       if ((lane & 15) == 0)
-        *reinterpret_cast<f32x4*>(red + ((r - s.r0) * 4 + wave) * kTileRows + (lane >> 4) * 4) =
-            acc.total();
+        *reinterpret_cast<f32x4*>(red + ((r - s.r0) * 4 + wave) * kTileRows + (lane >> 4) * 4) = t;
     }
     lds_barrier();
     if (wave == 0) {
@@ -550,11 +559,10 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   int bi = 0x7fffffff;
   {
     const StreamShare s = stream_share(a, u_lm, wave, W, wg);
+    const unsigned short* const xin = stream_in_lane(xsh, a.H, lane);
     for (int g = s.r0; g < s.r1; ++g) {
       Acc2 acc;
-      ring_mfma_run(a, rg, wave, lane, u_end, s.KT, [&](int j) {
-        return j * kTileCols + (lane >> 4) * 8;
-      }, xsh, xsh + a.H, acc);
+      ring_mfma_run<1>(a, rg, wave, lane, u_end, s.KT, xin, acc);
       const f32x4 y = acc.total() * s_inv;
       const int row0 = (4 * g + wave) * kTileRows + (lane >> 4) * 4;
       if ((lane & 15) == 0 && a.logits != nullptr) *reinterpret_cast<f32x4*>(a.logits + row0) = y;

@@ -27,6 +27,8 @@ constexpr int kBatch = 4;
 // (QKV, O, gate/up, down) in layer order, then the LM head; u_end (=
 // 4*L + 1) marks its end.
 constexpr int kUnitsPerLayer = 4;
+// A projection's k-tiles are dealt round robin to the workgroup's 4 waves.
+constexpr int kStreamKStep = 4;
 enum StreamProj : int { kPrQkv = 0, kPrO = 1, kPrGu = 2, kPrDown = 3 };
 
 QD_HD int stream_u_end(const StreamArgs& a) { return a.L * kUnitsPerLayer + 1; }
@@ -56,7 +58,7 @@ QD_HD StreamShare stream_share(const StreamArgs& a, int u, int wave, int W, int 
     s.KT = (p == kPrO ? a.QD : p == kPrDown ? a.I : a.H) / kTileCols;
     s.R = (p == kPrQkv ? a.NQKV : p == kPrGu ? 2 * a.I : a.H) / kTileRows;
     s.S = p == kPrQkv ? a.qkv_S : 1;
-    s.kstart = wave; s.kstep = 4; s.lm = false;
+    s.kstart = wave; s.kstep = kStreamKStep; s.lm = false;
   }
   s.kps = (s.KT + s.S - 1) / s.S;
   const unsigned P = (unsigned)s.R * (unsigned)s.S;

@@ -73,6 +73,10 @@ class Decoder:
         binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,
                                     tables, pool, next_ids, logits, taps, layer)
 
+    def step_path(self, batch: int) -> str:
+        """'stream', 'persistent', 'graph' or 'staged': how a step of `batch` runs."""
+        return binding.qd_step_path(self.handle, batch)
+
     def device_status(self) -> int:
         return binding.qd_device_status(self.handle)
 

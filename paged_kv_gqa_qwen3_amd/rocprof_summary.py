@@ -1,0 +1,143 @@
+"""Text summaries of rocprofv3 output for the profiles/ directory.
+
+Two inputs, both CSV directories written by rocprofv3 on the GPU machine:
+
+* a kernel trace (``--kernel-trace --stats``): per-dispatch durations of the
+  decode-step kernels, grouped into classes;
+* two counter runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, one
+  counter per run) of a command that also runs one plain 1 GiB device copy
+  (bench.py --copy-calibration-mib 1024): the copy's counter values give the
+  factor from counter units to bytes, which then scales every kernel's
+  counters into HBM bytes per dispatch.
+
+Usage (repo root):
+  python -m paged_kv_gqa_qwen3_amd.rocprof_summary trace <trace_dir> <prefix> <workload> <out.txt> <command...>
+  python -m paged_kv_gqa_qwen3_amd.rocprof_summary traffic <fetch_dir> <write_dir> <workload> <kind> <out_prefix>
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import json
+import os
+import sys
+
+# Kernel-name substrings -> class (first match wins).
+CLASSES = (
+    ("stream_step_kernel", "stream_step"),
+    ("step_kernel", "persistent_step"),
+    ("gemv_kernel<1, 4>", "qkv"),
+    ("gemv_kernel<1, 2>", "gate_up"),
+    ("gemv_kernel<1, 3>", "lm_head"),
+    ("gemv_kernel<1, 1>", "o_proj+down"),
+    ("attention_kernel", "attention"),
+    ("embed_kernel", "embed"),
+)
+
+
+def kernel_class(name: str):
+    for key, cls in CLASSES:
+        if key in name:
+            return cls
+    return None
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def trace_summary(trace_dir: str, prefix: str, workload: str, out_txt: str, command: str) -> None:
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, f"{prefix}_kernel_trace.csv")))))
+    dur = collections.defaultdict(list)
+    for r in rows:
+        c = kernel_class(r["Kernel_Name"])
+        if c is not None:
+            dur[c].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = list(csv.DictReader(open(_one(os.path.join(trace_dir, f"{prefix}_kernel_stats.csv")))))
+    lines = [f"# Kernel durations, workload {workload}", "", "command (repo root, MI355X):",
+             "  " + command, "", f'{"class":16s} {"dispatches":>10s} {"mean_us":>10s} {"median_us":>10s}']
+    for c in sorted(dur):
+        v = sorted(dur[c])
+        lines.append(f"{c:16s} {len(v):10d} {sum(v) / len(v):10.2f} {v[len(v) // 2]:10.2f}")
+    lines += ["", "rocprofv3 --stats (kernel_stats.csv), top rows:",
+              f'{"kernel":64s} {"calls":>6s} {"avg_us":>10s}']
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        lines.append(f'{r["Name"][:64]:64s} {r["Calls"]:>6s} {float(r["AverageNs"]) / 1e3:10.2f}')
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
+def _counter_rows(run_dir: str, counter: str):
+    path = _one(os.path.join(run_dir, "*counter_collection.csv"))
+    return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+
+def _calibration(rows) -> float:
+    """Counter value of the 1 GiB copy (the copy kernel with the largest grid)."""
+    copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    if not copies:
+        raise ValueError("no device copy in the counter run")
+    big = max(copies, key=lambda r: int(r["Grid_Size"]))
+    return float(big["Counter_Value"])
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, workload: str, kind: str,
+                    out_prefix: str) -> dict:
+    """Scaled HBM bytes per dispatch of each kernel class; writes
+    <out_prefix>.txt and <out_prefix>.json (with the kernel source sha256 that
+    bench.py checks before it reports the figure)."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench  # the repo-root benchmark: source hash and algorithmic bytes
+
+    f, w = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    gib_kib = 1024.0 * 1024.0
+    fs, ws = gib_kib / _calibration(f), gib_kib / _calibration(w)
+
+    def per_class(rows):
+        d = collections.defaultdict(list)
+        for r in rows:
+            c = kernel_class(r["Kernel_Name"])
+            if c:
+                d[c].append(float(r["Counter_Value"]))
+        return d
+
+    fc, wc = per_class(f), per_class(w)
+    sha = bench.kernel_source_sha256(kind)
+    lines = [f"# HBM traffic per dispatch (rocprofv3 --pmc), workload {workload}", "",
+             f"kernel source sha256 ({' + '.join(bench.KERNEL_SOURCES[kind])}): {sha}", "",
+             f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {_calibration(f):.1f} KiB and "
+             f"WRITE_SIZE = {_calibration(w):.1f} KiB",
+             f"for 1,048,576 KiB moved each way: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}.", "",
+             f'{"kernel class":16s} {"dispatches":>10s} {"fetch_KiB":>12s} {"write_KiB":>10s} {"scaled_MB":>10s}']
+    traffic = {}
+    for c in sorted(fc):
+        if c not in wc:
+            continue
+        fk = sum(fc[c]) / len(fc[c])
+        wk = sum(wc[c]) / len(wc[c])
+        b = (fk * fs + wk * ws) * 1024.0
+        lines.append(f"{c:16s} {len(fc[c]):10d} {fk:12.1f} {wk:10.1f} {b / 1e6:10.2f}")
+        traffic[c] = int(round(b))
+    rec = {"kernel_source_sha256": sha, "workload": workload, "traffic_bytes_per_launch": traffic,
+           "fetch_scale": fs, "write_scale": ws}
+    open(out_prefix + ".txt", "w").write("\n".join(lines) + "\n")
+    json.dump(rec, open(out_prefix + ".json", "w"), indent=1)
+    return rec
+
+
+def main(argv):
+    if len(argv) >= 6 and argv[1] == "trace":
+        trace_summary(argv[2], argv[3], argv[4], argv[5], " ".join(argv[6:]))
+    elif len(argv) == 7 and argv[1] == "traffic":
+        print(json.dumps(traffic_summary(argv[2], argv[3], argv[4], argv[5], argv[6]), indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

@@ -566,8 +566,9 @@ int setup_stream(qd_handle* h) {
   for (int attempt = 0; attempt < 2; ++attempt) {
     // QKV K splits (the kernel supports any count; attention sums the
     // partials).  Measured on the 4B shape, 2 splits balance the workgroups'
-    // shares (3 half tiles each instead of 1 or 2 tiles) but lose as much to
-    // the shorter runs and the extra epilogues: one split.
+    // shares (3 half tiles each instead of 1 or 2 tiles) but lose more to the
+    // shorter runs, the extra epilogues and attention's extra input loads
+    // (2.44 and, with 4 splits, 2.51 ms per step against 2.37): one split.
     const int Rq = h->NQKV / kTileRows;
     const int qS = 1;
     const int rt_max = std::max(cdiv(Rq * qS, W),
@@ -675,7 +676,7 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
 #ifdef QD_STEP_TRACE
   static unsigned long long* trace = nullptr;
-  const size_t trace_n = (size_t)h->stream_grid * 1024;
+  const size_t trace_n = (size_t)h->stream_grid * 1024 * 3;
   if (!trace) {
     HIP_TRY(h, hipMalloc(&trace, trace_n * 8));
   }

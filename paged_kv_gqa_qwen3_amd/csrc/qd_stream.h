@@ -354,6 +354,11 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   // (trace builds) event e of this workgroup: 100 MHz clock, from thread 0
   auto mark = [&](int e) {
     if (tid == 0) a.trace[(size_t)wg * 1024 + e] = __builtin_amdgcn_s_memrealtime();
+    // ... and wave 1's time and weight tiles issued so far, in two more blocks
+    if (tid == 64) {
+      a.trace[(size_t)gridDim.x * 1024 + (size_t)wg * 1024 + e] = __builtin_amdgcn_s_memrealtime();
+      a.trace[(size_t)gridDim.x * 2048 + (size_t)wg * 1024 + e] = (unsigned long long)rg.ld.issued;
+    }
   };
 #else
   auto mark = [](int) {};

@@ -1107,18 +1107,21 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
   mark(5);
   // (max, sum) of every split into LDS, and (for up to 16 splits) each
-  // output's split partials into registers in the same round trip; then
-  // per head the overall max and the splits' factors exp(m_s - M)
-  constexpr int kOut = (G * D + NW * 64 - 1) / (NW * 64);  // outputs per thread
-  float ov[kOut][16];
-  if (nsplit <= 16) {
+  // 4-output chunk's split partials into registers with one 16-byte
+  // device-scope load per split, in the same round trip; then per head the
+  // overall max and the splits' factors exp(m_s - M)
+  constexpr int kChunks = G * D / 4;  // 4-float output chunks, one per thread
+  static_assert(kChunks <= NW * 64, "one chunk per thread");
+  f32x4 ov[16];
+  if (nsplit <= 16 && tid < kChunks) {
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        a.o_part, 0, (int)((size_t)a.B * Hq * S_max * D * 4), kBufferWord3);
+    const int base = (int)(((qh0 + (4 * tid) / D) * S_max) * D + (4 * tid) % D) * 4;
 #pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-      const int idx = min(tid + k * NW * 64, G * D - 1);
-      const float* op = a.o_part + (qh0 + idx / D) * S_max * D + idx % D;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ov[k][j] = ld_agent(op + (size_t)min(j, nsplit - 1) * D);
-    }
+    for (int j = 0; j < 16; ++j)
+      if (j < nsplit)
+        ov[j] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, base + j * D * 4, 0, kDeviceScope));
   }
   for (int i = tid; i < G * nsplit; i += NW * 64) {
     const int h = i / nsplit, s2 = i % nsplit;
@@ -1139,17 +1142,28 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     sm.lsum[tid] = L;
   }
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kOut; ++k) {
-    const int idx = tid + k * NW * 64;
-    if (idx >= G * D) break;
-    const int h = idx / D, d = idx % D;
-    float o = 0.f;
-    if (nsplit <= 16) {
+  if (nsplit <= 16) {
+    if (tid < kChunks) {
+      const int h = (4 * tid) / D, d0 = (4 * tid) % D;
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (j < nsplit) o += ov[k][j] * sm.ml[0][h][j];
-    } else {
+        if (j < nsplit) o += ov[j] * sm.ml[0][h][j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r = o[e] / sm.lsum[h];
+        st_agent(a.out + (qh0 + h) * D + d0 + e, r);
+        if (a.out_hi != nullptr) split_hilo(r, a.out_hi, a.out_lo, (qh0 + h) * D + d0 + e);
+      }
+    }
+  } else {
+    constexpr int kOut = (G * D + NW * 64 - 1) / (NW * 64);  // outputs per thread
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+      const int idx = tid + k * NW * 64;
+      if (idx >= G * D) break;
+      const int h = idx / D, d = idx % D;
+      float o = 0.f;
       const float* op = a.o_part + (qh0 + h) * S_max * D + d;
       for (int s0 = 0; s0 < nsplit; s0 += 16) {
         float w16[16];
@@ -1159,10 +1173,10 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
         for (int j = 0; j < 16; ++j)
           if (s0 + j < nsplit) o += w16[j] * sm.ml[0][h][s0 + j];
       }
+      const float r = o / sm.lsum[h];
+      st_agent(a.out + (qh0 + h) * D + d, r);
+      if (a.out_hi != nullptr) split_hilo(r, a.out_hi, a.out_lo, (qh0 + h) * D + d);
     }
-    const float r = o / sm.lsum[h];
-    st_agent(a.out + (qh0 + h) * D + d, r);
-    if (a.out_hi != nullptr) split_hilo(r, a.out_hi, a.out_lo, (qh0 + h) * D + d);
   }
   if (tid == 0) reset_counter(cnt);
   mark(6);

@@ -308,7 +308,7 @@ __host__ __device__ constexpr size_t gemv_head_bytes(int nb) {
 inline size_t gemv_lds_bytes_impl(int B, int kps) {
   const int nb = gemv_nb(B);
   const size_t ks = (size_t)kps * kTileCols;
-  const size_t slice = nb >= 16 ? (size_t)nb * (ks + 8) * 2 * 2 : (size_t)nb * ks * 4;
+  const size_t slice = nb >= 8 ? (size_t)nb * (ks + 8) * 2 * 2 : (size_t)nb * ks * 4;
   return gemv_head_bytes(nb) + slice;
 }
 
@@ -322,10 +322,12 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 // in are free.
 //   NB <= 4 : VALU path, fp32 FMA; the K slice of the input (times the
 //             RMSNorm gain) is staged in LDS.
-//   NB >= 16: MFMA path, NB/16 blocks of 16 batch columns,
-//             v_mfma_f32_16x16x32_bf16 with the weight tile as operand A and
-//             the input as a pair of bf16 (hi = bf16(x), lo = bf16(x - hi)),
-//             two MFMAs per tile: ~16 significant bits of input instead of 8
+//   NB >= 8 : MFMA path, v_mfma_f32_16x16x32_bf16 with the weight tile as
+//             operand A and the input as a pair of bf16 (hi = bf16(x), lo =
+//             bf16(x - hi)): at NB = 8 one MFMA per tile, columns 0..7 the
+//             hi halves and 8..15 the lo halves of the 8 batch columns
+//             (added at the end); at NB >= 16 NB/16 blocks of 16 batch
+//             columns, two MFMAs per tile: ~16 significant bits of input instead of 8
 //             (bf16 inputs alone move a 36-layer model's logits by ~2% of
 //             their maximum, beyond the step's 2e-2 tolerance).  The producer
 //             of the input wrote the pairs once (xh, xl: [64][K] bf16, times
@@ -343,9 +345,10 @@ template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait>
 __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const float* gain,
                                  const Done& done, int item, unsigned char* smem,
                                  const Wait& wait) {
-  constexpr bool kMfma = NB >= 16;
+  constexpr bool kMfma = NB >= 8;
+  constexpr bool kSplitCols = NB == 8;  // hi and lo side by side in one operand
   constexpr bool kAgent = Wait::kInLaunch;
-  constexpr int NCB = kMfma ? NB / 16 : 1;
+  constexpr int NCB = kMfma && !kSplitCols ? NB / 16 : 1;
   static_assert(!kMfma || !kAgent, "the MFMA path reads inputs of an earlier launch");
   float* s_inv = reinterpret_cast<float*>(smem);
   float* s_ssq = s_inv + kMaxBatch;
@@ -458,7 +461,15 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // wave-local tile i is k-tile kph + WS*i of the item's slice
   auto compute = [&](const u32x4& wv, int i) {
     const int t = kph + WS * i;
-    if constexpr (kMfma) {
+    if constexpr (kSplitCols) {
+      // LDS rows 0..7 hold the hi halves, 8..15 the lo halves: operand
+      // column (lane % 16) reads row lane % 16
+      const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(
+          xs + (lane & 15) * P + t * kTileCols + (lane >> 4) * 8);
+      acc_m[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, xv), acc_m[0], 0, 0, 0);
+    } else if constexpr (kMfma) {
       const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
       const bf16x8 wa = __builtin_bit_cast(bf16x8, wv);
 #pragma unroll
@@ -506,7 +517,19 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // s_res slot `wave` = [16 rows][NB]; then the waves of a row tile are
   // added in K order into the slot of its first wave, so that rows 0..rows-1
   // of s_res hold the item's rows.
-  if constexpr (kMfma) {
+  if constexpr (kSplitCols) {
+    // column c < 8 (hi) plus its partner c + 8 (lo), lane ^ 8
+    f32x4 tot;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tot[r] = acc_m[0][r] + __shfl_xor(acc_m[0][r], 8);
+    const int col = lane & 15;
+    if (col < 8) {
+      const float sc = norm && col < B ? s_inv[col] : 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = tot[r] * sc;
+    }
+  } else if constexpr (kMfma) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int col = cb * 16 + (lane & 15);

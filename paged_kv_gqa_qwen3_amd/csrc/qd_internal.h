@@ -188,10 +188,13 @@ struct StreamArgs {
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: per-stage timestamps
 };
 
-// Batch columns a GEMV item is compiled for: VALU up to 4, MFMA blocks of 16 above.
+// Batch columns a GEMV item is compiled for: VALU up to 4; MFMA above, 8
+// columns (the input's hi and lo halves side by side in one 16-column
+// operand) up to 8, blocks of 16 beyond.
 constexpr int gemv_nb(int B) {
-  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
 }
+constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 
 // Attention workgroups: the standalone kernel has 8 waves with 1 KV page
 // each in flight at batch <= 4 and 3 at larger batches (more, busier

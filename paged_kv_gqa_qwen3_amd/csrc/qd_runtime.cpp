@@ -305,7 +305,7 @@ int prof_mark(qd_handle* h, Prof* pr, int cls, hipStream_t s) {
 hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode, float* logits,
                              int32_t* next, hipStream_t s) {
   const int H = h->H, L = h->L;
-  const bool mfma = gemv_nb(B) >= 16;
+  const bool mfma = gemv_mfma(B);
   uint16_t* const xg[2] = {h->xg_hi, h->xg_lo};
   uint16_t* const attn_hl[2] = {h->attn_hi, h->attn_lo};
   uint16_t* const act_hl[2] = {h->act_hi, h->act_lo};
@@ -364,7 +364,7 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   const int B = sp.B, L = h->L, H = h->H;
   const float eps = h->cfg.rms_eps;
   const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
-  const bool mfma = gemv_nb(B) >= 16;
+  const bool mfma = gemv_mfma(B);
 
   EmbedArgs ea{};
   ea.table = h->embed;
@@ -785,9 +785,9 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if ((rc = dev_alloc(h, &h->qkv, (size_t)Bm * h->NQKV))) return bail(rc);
   if ((rc = dev_alloc(h, &h->attn, (size_t)Bm * h->QD))) return bail(rc);
   if ((rc = dev_alloc(h, &h->act, (size_t)Bm * I))) return bail(rc);
-  if (gemv_nb(Bm) >= 16) {
-    // MFMA operands cover whole blocks of 16 batch columns: rows up to the
-    // block are allocated and zeroed (rows >= B only feed unused outputs)
+  if (gemv_mfma(Bm)) {
+    // MFMA operands cover whole blocks of 8 or 16 batch columns: rows up to
+    // the block are allocated and zeroed (rows >= B only feed unused outputs)
     const size_t rows = (size_t)gemv_nb(Bm);
     uint16_t** bufs[6] = {&h->xg_hi, &h->xg_lo, &h->attn_hi, &h->attn_lo, &h->act_hi, &h->act_lo};
     const size_t cols[6] = {(size_t)H, (size_t)H, (size_t)h->QD, (size_t)h->QD, (size_t)I, (size_t)I};

@@ -64,6 +64,7 @@ struct StreamRing {
   int W, wg;             // grid size and this workgroup
 #ifdef QD_STEP_TRACE
   unsigned long long t_wait, t_dot;  // (trace builds) shader cycles waiting for tiles / in ring_mfma
+  unsigned long long t_top, t_rel;   // ... refilling / waiting for a batch's LDS reads
 #endif
 };
 
@@ -224,16 +225,37 @@ __device__ __forceinline__ void ring_mfma_run(const StreamArgs& a, StreamRing& r
     ring_wait<kBatch>(rg);
     batch_read<KSTEP>(rg, lane, xk, A);
     // batches 2p (in A) and 2p + 1 (in B)
-    for (int p = 0; p < nfull / 2; ++p) {
-      ring_release(rg, kBatch);  // (waits for batch 2p's reads)
-      ring_top_up(a, rg, wave, lane, u_limit);
+#ifdef QD_STEP_TRACE
+    // (trace builds) shader cycles spent waiting for tiles, releasing, refilling
+    auto timed_wait = [&]() {
+      const unsigned long long tw = __builtin_amdgcn_s_memtime();
       ring_wait<kBatch>(rg);
+      rg.t_wait += __builtin_amdgcn_s_memtime() - tw;
+    };
+    auto rel_top = [&]() {
+      const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+      ring_release(rg, kBatch);
+      const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+      ring_top_up(a, rg, wave, lane, u_limit);
+      const unsigned long long t2 = __builtin_amdgcn_s_memtime();
+      rg.t_rel += t1 - t0;
+      rg.t_top += t2 - t1;
+    };
+#else
+    auto timed_wait = [&]() { ring_wait<kBatch>(rg); };
+    auto rel_top = [&]() {
+      ring_release(rg, kBatch);
+      ring_top_up(a, rg, wave, lane, u_limit);
+    };
+#endif
+    for (int p = 0; p < nfull / 2; ++p) {
+      rel_top();  // (the release waits for batch 2p's reads)
+      timed_wait();
       batch_read<KSTEP>(rg, lane, xk + (2 * p + 1) * kStep, B);
       batch_mfma(A, acc);
-      ring_release(rg, kBatch);  // (waits for batch 2p + 1's reads)
-      ring_top_up(a, rg, wave, lane, u_limit);
+      rel_top();  // (waits for batch 2p + 1's reads)
       if (2 * p + 2 < nfull) {
-        ring_wait<kBatch>(rg);
+        timed_wait();
         batch_read<KSTEP>(rg, lane, xk + (2 * p + 2) * kStep, A);
       }
       batch_mfma(B, acc);
@@ -341,7 +363,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   rg.W = W;
   rg.wg = wg;
 #ifdef QD_STEP_TRACE
-  rg.t_wait = rg.t_dot = 0;
+  rg.t_wait = rg.t_dot = rg.t_top = rg.t_rel = 0;
 #endif
   stream_start(rg.ld, a.runs + __builtin_amdgcn_readfirstlane(a.run_off[wg * 4 + wave]));
   auto u_lim = [&](int u) { return wave == 0 ? u : u_end; };
@@ -606,6 +628,8 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   if (lane == 0) {
     a.trace[(size_t)wg * 1024 + 1008 + 2 * wave] = rg.t_wait;
     a.trace[(size_t)wg * 1024 + 1009 + 2 * wave] = rg.t_dot;
+    a.trace[(size_t)wg * 1024 + 980 + 2 * wave] = rg.t_top;
+    a.trace[(size_t)wg * 1024 + 981 + 2 * wave] = rg.t_rel;
   }
 #endif
   // The last workgroup out resets the dependency counters for the next step.

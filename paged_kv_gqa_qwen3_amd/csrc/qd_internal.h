@@ -197,20 +197,22 @@ constexpr int gemv_nb(int B) {
 constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 
 // Attention workgroups: the standalone kernel has 8 waves with 1 KV page
-// each in flight up to batch 8 and 3 at larger batches (there more, busier
-// workgroups are worth the extra pages per wave over a split combine:
-// batch 16, context 256, 4.00 against 4.44 ms per step with 1 page; batch 8
-// 3.39 with 1 page against 3.44 with 3); the persistent kernels'
-// workgroups have 4 waves with 1 page.  A split of a sequence covers
-// waves * pages.
+// each in flight up to batch 8 on handles sized for short contexts, and 3
+// at larger batches or for long contexts (there fewer, busier workgroups are
+// worth the extra pages per wave: batch 16, context 256, 4.00 against
+// 4.44 ms per step with 1 page; batch 1, context 8192, 2.95 against 3.45;
+// but batch 8, context 256, 3.39 with 1 page against 3.44 with 3); the
+// persistent kernels' workgroups have 4 waves with 1 page.  A split of a
+// sequence covers waves * pages.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnWavesPersistent = 4;
 constexpr int kAttnPagesPersistent = 1;
-constexpr int attn_pages_per_wave(int B, bool persistent) {
-  return persistent ? kAttnPagesPersistent : B <= 8 ? 1 : 3;
+constexpr int attn_pages_per_wave(int B, bool persistent, bool long_ctx = false) {
+  return persistent ? kAttnPagesPersistent : B <= 8 && !long_ctx ? 1 : 3;
 }
-constexpr int attn_pages_per_split(int B, bool persistent) {
-  return (persistent ? kAttnWavesPersistent : kAttnWaves) * attn_pages_per_wave(B, persistent);
+constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false) {
+  return (persistent ? kAttnWavesPersistent : kAttnWaves) *
+         attn_pages_per_wave(B, persistent, long_ctx);
 }
 // Splits of one sequence the final combine can hold (its (max, sum) pairs sit in LDS).
 constexpr int kMaxSplitsStaged = 512;

@@ -235,7 +235,7 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
 
 // Most splits of one sequence (its longest table) at batch B.
 int attn_splits(const qd_handle* h, int B) {
-  const int pps = attn_pages_per_split(B, use_persistent(h, B));
+  const int pps = attn_pages_per_split(B, use_persistent(h, B), h->long_ctx);
   return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
 }
 
@@ -420,7 +420,7 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     // shape here too, so both launch modes compute the same bits
     const bool pers = use_persistent(h, B);
     HIP_TRY(h, launch_attention(aa, h->D, h->G, pers ? kAttnWavesPersistent : kAttnWaves,
-                                attn_pages_per_wave(B, pers), s));
+                                attn_pages_per_wave(B, pers, h->long_ctx), s));
     PROF(QD_PROF_ATTN);
     if (tap && taps->attn)
       HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from paged_kv_gqa_qwen3_amd import synth
+from paged_kv_gqa_qwen3_amd import binding, synth
 from paged_kv_gqa_qwen3_amd.decoder import Decoder, pool_to_device, pool_to_host
 from gpu_util import (bf16_rne_of_f32, check_logits, check_next_ids, gemv_tol, say)
 
@@ -313,19 +313,21 @@ def test_persistent_matches_staged_bitwise(torch, B, ctx):
     dp.close()
 
 
-@pytest.mark.parametrize("ctx", [[40], [700], [2100], [0]])
+@pytest.mark.parametrize("ctx", [[40], [700], [2000], [0]])
 def test_stream_step_matches_staged(torch, ctx):
     """Batch 1 on a persistent handle runs the weight-streaming kernel (MFMA
     tiles against a bf16 pair of the input); the per-stage kernels of the
     same handle (VALU, fp32 input) must agree within the logit tolerance
     over chained steps, greedy ids must agree unless near a tie, and the KV
     rows both append must agree to bf16 rounding.  Short, split and long
-    contexts (one split, several, the combine over many); a repeated step
-    must give the same bits."""
+    contexts (one split, several, the combine over more than 16 splits: the
+    longest a streaming handle takes, 128 pages); a repeated step must give
+    the same bits."""
     shape = synth.TINY
     W = synth.make_weights(shape, 80 + ctx[0] % 7)
     batch = synth.make_paged_batch(shape, ctx, 5, 81)
     dp = Decoder(shape, 1, batch.max_pages, batch.num_pages, persistent=True)
+    assert dp.step_path(1) == "stream", batch.max_pages
     dp.load_numpy_weights(W)
     pp, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
     ip = StepIO(torch, 1, batch.max_pages, shape.vocab)
@@ -356,6 +358,25 @@ def test_stream_step_matches_staged(torch, ctx):
                      "stream vs staged appended KV")
     assert dp.device_status() == 0
     dp.close()
+
+
+def test_step_paths(torch):
+    """qd_step_path: a persistent handle streams batch 1 only when sized for
+    at most 128 pages per sequence, runs batches 2-4 as the persistent step
+    and larger ones as the graph; a non-persistent handle always takes the
+    graph; batches outside 1..max_batch are rejected."""
+    shape = synth.TINY
+    for pages, persistent, want in ((128, True, ["stream", "persistent", "persistent",
+                                                  "persistent", "graph", "graph"]),
+                                    (129, True, ["graph", "persistent", "persistent",
+                                                 "persistent", "graph", "graph"]),
+                                    (16, False, ["graph"] * 6)):
+        dec = Decoder(shape, 6, pages, pages + 1, persistent=persistent)
+        assert [dec.step_path(b) for b in range(1, 7)] == want, (pages, persistent)
+        for bad in (0, 7):
+            with pytest.raises(binding.QdError):
+                dec.step_path(bad)
+        dec.close()
 
 
 def test_page_placement_and_determinism(torch):

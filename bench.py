@@ -248,9 +248,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=("auto", "graph"), default="auto",
-                    help="auto: a persistent handle, on which the library runs each step as "
-                         "the batch-1 streaming kernel, the persistent kernel or the per-stage "
-                         "graph (qd_step_path); graph: the per-stage graph only")
+                    help="auto: a persistent handle, on which the library runs batch 1 as "
+                         "the streaming kernel where the handle allows it and every other step "
+                         "as the per-stage graph (qd_step_path); graph: the per-stage graph "
+                         "only")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel for scaling hardware byte counters)")

@@ -51,7 +51,7 @@ extern "C" {
 #define QD_DEV_BAD_TOKEN 1     /* a token id outside [0, vocab) (clamped) */
 #define QD_DEV_BAD_POSITION 2  /* a position outside [0, max_pages_per_seq*16) */
 #define QD_DEV_BAD_PAGE 4      /* a block-table entry outside [0, num_pages) */
-#define QD_DEV_TIMEOUT 8       /* a persistent step gave up waiting (results invalid) */
+#define QD_DEV_TIMEOUT 8       /* the streaming step gave up waiting (results invalid) */
 
 typedef struct qd_handle qd_handle;
 
@@ -72,19 +72,17 @@ typedef struct qd_config {
   int32_t max_pages_per_seq;   /* block-table row length; at most 2048 (32768 tokens) */
   int32_t num_pages;           /* pages in the caller's pool */
   int32_t use_graphs;          /* 1: replay one captured hipGraph per batch size */
-  int32_t persistent;          /* 1: run each step of batch <= 4 as one persistent
-                                  cooperative kernel (head_dim 128 with 4 query heads per
-                                  KV head, or head_dim 64 with 2); larger batches, and
-                                  other shapes, take the per-stage kernels.  Batch 1
-                                  (with max_pages_per_seq <= 128, at most 64 layers,
-                                  hidden <= 8192 and every projection input <= 16384)
-                                  runs as a kernel that streams each wave's share of
-                                  the weights through LDS across stage boundaries and
-                                  computes the projections with MFMA on a bf16 hi/lo
-                                  split of their input (about 16 significant bits; the
-                                  per-stage batch-1 kernels keep the input in fp32); on
-                                  a handle with longer block-table rows batch 1 takes
-                                  the per-stage kernels (qd_step_path tells which) */
+  int32_t persistent;          /* 1: run batch 1 as one cooperative kernel that
+                                  streams each wave's share of the weights through LDS
+                                  across stage boundaries and computes the projections
+                                  with MFMA on a bf16 hi/lo split of their input (about
+                                  16 significant bits; the per-stage batch-1 kernels
+                                  keep the input in fp32).  Needs head_dim 128 with 4
+                                  query heads per KV head or head_dim 64 with 2,
+                                  max_pages_per_seq <= 128, at most 64 layers, hidden
+                                  <= 8192 and every projection input <= 16384; other
+                                  handles, and every batch above 1, take the per-stage
+                                  kernels (qd_step_path tells which) */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
@@ -127,9 +125,10 @@ int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
  *   out_next_ids int32 [batch]       greedy next token (lowest index on ties)
  *   out_logits   fp32 [batch][vocab] or NULL
  * Sequences in one call must not write the same pool slot.  Asynchronous.
- * With persistent, the step is one cooperative kernel whose workgroups walk
- * the stages in order and wait on device counters (every wait is bounded; a
- * timeout sets QD_DEV_TIMEOUT).  Otherwise, with use_graphs, the first call
+ * On the streaming path (see persistent) the step is one cooperative kernel
+ * whose workgroups walk the stages in order and wait on device counters
+ * (every wait is bounded; a timeout sets QD_DEV_TIMEOUT).  Otherwise, with
+ * use_graphs, the first call
  * for a (batch, pointer set) captures a hipGraph of the per-stage kernels and
  * later calls replay it (new pointers cause a new capture).
  * Kernels clamp out-of-range ids, positions and page ids instead of reading
@@ -148,8 +147,8 @@ typedef struct qd_taps {
 } qd_taps;
 
 /* The step as per-stage kernels launched one by one (no graph, and no
- * persistent kernel even on a persistent handle, whose split plans it uses),
- * also filling `taps` (may be NULL). */
+ * streaming kernel even on a persistent handle), also filling `taps` (may be
+ * NULL). */
 int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
                         const int32_t* positions, const int32_t* block_tables,
                         void* kv_pool, int32_t* out_next_ids, float* out_logits,
@@ -199,8 +198,7 @@ void* qd_stream(const qd_handle* h);
 /* How qd_decode_step runs a step of `batch` sequences on this handle. */
 #define QD_PATH_STAGED 0      /* per-stage kernels launched one by one */
 #define QD_PATH_GRAPH 1       /* per-stage kernels replayed from a captured hipGraph */
-#define QD_PATH_PERSISTENT 2  /* one persistent cooperative kernel per step */
-#define QD_PATH_STREAM 3      /* batch 1: the weight-streaming persistent kernel */
+#define QD_PATH_STREAM 3      /* batch 1: the weight-streaming cooperative kernel */
 
 /* One of QD_PATH_*, or QD_EINVAL for a NULL handle or a batch outside
  * 1..max_batch.  No GPU work. */

@@ -207,7 +207,7 @@ def qd_stream(handle: int) -> int:
     return load_library().qd_stream(handle) or 0
 
 
-STEP_PATHS = ("staged", "graph", "persistent", "stream")
+STEP_PATHS = {0: "staged", 1: "graph", 3: "stream"}  # QD_PATH_* values
 
 
 def qd_step_path(handle: int, batch: int) -> str:

@@ -110,34 +110,16 @@ struct EmbedArgs {
   int* dev_flags;
 };
 
-// Per-layer pointers for the persistent step kernel (device-resident array).
+// Per-layer pointers for the streaming step kernel (device-resident array).
 struct LayerDev {
   const uint16_t *qkv, *o, *gu, *down;
   const float *in_norm, *post_norm, *q_norm, *k_norm;
 };
 
-// Dependency counters of one persistent step, all zero at launch.
+// Dependency counters of one streaming step, all zero at launch.
 constexpr int kCntEmbed = 0;
 constexpr int kCntPerLayer = 5;  // qkv, attention, o, gate_up, down finalised
 constexpr int cnt_index(int layer, int phase) { return 1 + layer * kCntPerLayer + phase; }
-
-struct StepArgs {
-  // templates: per-layer fields (weights, gains, pool slice, done counters)
-  // are filled in on the device for each layer
-  EmbedArgs embed;
-  GemvArgs qkv, o, gu, down, lm;
-  AttnArgs attn;
-  const LayerDev* layers;
-  int L;
-  size_t pool_layer_elems;   // elements of one layer's slice of the pool
-  unsigned* cnt;             // [1 + L*kCntPerLayer] dependency counters
-  unsigned* flags;           // [grid][32]: per-workgroup completed-stage flags
-  unsigned* exit_cnt;        // workgroups that finished the step
-  unsigned* abort_flag;      // set when a wait times out; later waits fall through
-  int* dev_flags;
-  unsigned spin_limit;       // polls before a wait gives up
-  unsigned long long* trace; // builds with QD_STEP_TRACE only: per-item timestamps
-};
 
 struct StreamRun;
 
@@ -188,11 +170,13 @@ struct StreamArgs {
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: per-stage timestamps
 };
 
-// Batch columns a GEMV item is compiled for: VALU up to 4; MFMA above, 8
+// Batch columns a GEMV item is compiled for: VALU at batch 1; MFMA above, 8
 // columns (the input's hi and lo halves side by side in one 16-column
-// operand) up to 8, blocks of 16 beyond.
+// operand) up to batch 8, blocks of 16 beyond.  (Batches 2-4 as VALU items
+// were measured slower on the 4B shape: 3.08, 3.51, 3.60 ms per step against
+// 2.75, 2.80, 2.88 with the 8-column MFMA items.)
 constexpr int gemv_nb(int B) {
-  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+  return B <= 1 ? 1 : B <= 8 ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
 }
 constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 
@@ -202,7 +186,7 @@ constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 // worth the extra pages per wave: batch 16, context 256, 4.00 against
 // 4.44 ms per step with 1 page; batch 1, context 8192, 2.95 against 3.45;
 // but batch 8, context 256, 3.39 with 1 page against 3.44 with 3); the
-// persistent kernels' workgroups have 4 waves with 1 page.  A split of a
+// streaming kernel's attention items have 4 waves with 1 page.  A split of a
 // sequence covers waves * pages.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnWavesPersistent = 4;
@@ -224,26 +208,15 @@ hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, in
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
-// waves, pages: kAttnWaves with 1 or 3 pages per wave, or the persistent
-// kernel's item shape (kAttnWavesPersistent, kAttnPagesPersistent; head shapes the persistent
-// kernel supports only).
+// waves, pages: kAttnWaves with 1 or 3 pages per wave.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,
                                int B, int Bmax, float eps, float* out, hipStream_t s);
 
-// Persistent step: which (head_dim, group) shapes it is built for, the LDS
-// bytes it needs, the largest co-resident grid, and the cooperative launch.
-bool step_supported(int head_dim, int group);
-size_t step_lds_bytes(int B, int head_dim, int group, int max_kps);
-hipError_t step_max_grid(int B, int head_dim, int group, size_t lds, int num_cus,
-                         int* grid);
-hipError_t launch_step(const StepArgs& a, int head_dim, int group, int grid, size_t lds,
-                       hipStream_t s);
-
 // Batch-1 streaming step: LDS bytes, largest co-resident grid (0 when it
-// does not fit), cooperative launch; the (head_dim, group) shapes of the
-// persistent step only.
+// does not fit), cooperative launch; built for (head_dim, group) = (128, 4)
+// and (64, 2) only (stream_lds_bytes returns 0 for other shapes).
 size_t stream_lds_bytes(int head_dim, int group, int in_floats, int rt_max);
 hipError_t stream_max_grid(int head_dim, int group, size_t lds, int num_cus, int* grid);
 hipError_t launch_stream(const StreamArgs& a, int head_dim, int group, int grid, size_t lds,

@@ -9,9 +9,11 @@
 //
 // Every piece of work is an "item" function (one GEMV row group x K split,
 // one (sequence, KV head, split) of attention, one embedding row).  The same
-// items run either one kernel per step stage (standalone kernels, captured in
-// a hipGraph) or inside one persistent cooperative kernel that walks the
-// whole step and resolves the dependencies between stages with counters.
+// items run as one kernel per step stage here (captured in a hipGraph per
+// batch size); the attention and embedding items also run inside the batch-1
+// streaming kernel (qd_stream.h), which walks the whole step in one
+// cooperative launch and resolves the dependencies between stages with
+// counters.
 #include <hip/hip_runtime.h>
 
 #include "qd_device.h"
@@ -171,14 +173,6 @@ static hipError_t launch_attention_dg(const AttnArgs& a, int pages, hipStream_t 
 
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s) {
-  if (waves == kAttnWavesPersistent) {  // the persistent kernel's item shape
-    if (pages != kAttnPagesPersistent) return hipErrorInvalidValue;
-    if (head_dim == 128 && group == 4)
-      return launch_attention_t<128, 4, kAttnWavesPersistent, kAttnPagesPersistent>(a, s);
-    if (head_dim == 64 && group == 2)
-      return launch_attention_t<64, 2, kAttnWavesPersistent, kAttnPagesPersistent>(a, s);
-    return hipErrorInvalidValue;
-  }
   if (waves != kAttnWaves || (pages != 1 && pages != 3)) return hipErrorInvalidValue;
   if (head_dim == 128) {
     if (group == 4) return launch_attention_dg<128, 4>(a, pages, s);
@@ -193,44 +187,5 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int wave
 }
 
 size_t gemv_lds_bytes(int B, int kps) { return gemv_lds_bytes_impl(B, kps); }
-
-// -------------------------------------------------------- persistent step
-
-// Instantiated in qd_step_nb*.hip.
-template <int NB>
-hipError_t step_dispatch(int head_dim, int group, const StepArgs* a, int grid, size_t lds,
-                         hipStream_t s, int* max_grid, int num_cus);
-
-bool step_supported(int head_dim, int group) {
-  return (head_dim == 128 && group == 4) || (head_dim == 64 && group == 2);
-}
-
-size_t step_lds_bytes(int B, int head_dim, int group, int max_kps) {
-  size_t att = 0;
-  if (head_dim == 128 && group == 4) att = sizeof(AttnSmem<128, 4, kAttnWavesPersistent>);
-  if (head_dim == 64 && group == 2) att = sizeof(AttnSmem<64, 2, kAttnWavesPersistent>);
-  const size_t gm = gemv_lds_bytes(B, max_kps);
-  return att > gm ? att : gm;
-}
-
-// The persistent step serves batches <= 4 only.
-static hipError_t step_call(int B, int head_dim, int group, const StepArgs* a, int grid,
-                            size_t lds, hipStream_t s, int* max_grid, int num_cus) {
-  switch (gemv_nb(B)) {
-    case 1: return step_dispatch<1>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    case 2: return step_dispatch<2>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    case 4: return step_dispatch<4>(head_dim, group, a, grid, lds, s, max_grid, num_cus);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t step_max_grid(int B, int head_dim, int group, size_t lds, int num_cus, int* grid) {
-  return step_call(B, head_dim, group, nullptr, 0, lds, nullptr, grid, num_cus);
-}
-
-hipError_t launch_step(const StepArgs& a, int head_dim, int group, int grid, size_t lds,
-                       hipStream_t s) {
-  return step_call(a.qkv.B, head_dim, group, &a, grid, lds, s, nullptr, 0);
-}
 
 }  // namespace qd

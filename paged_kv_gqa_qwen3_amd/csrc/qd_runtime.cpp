@@ -83,7 +83,6 @@ struct qd_handle {
   int* dev_flags = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   int max_pos = 0;
-  int smax1 = 1;  // attention splits at batch 1 (largest)
 
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::map<GraphKey, hipGraph_t> graph_defs;
@@ -96,7 +95,6 @@ struct qd_handle {
   unsigned* step_flags = nullptr;  // [2 * CUs][32]
   unsigned* step_exit = nullptr;
   unsigned* step_abort = nullptr;
-  std::map<int, int> step_grid;  // batch -> co-resident grid of the persistent kernel
   // batch-1 streaming step (persistent handles whose shapes fit it)
   bool stream_ok = false;
   int stream_grid = 0;
@@ -148,33 +146,22 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
 // Batch >= 5 (MFMA items) and the persistent step: 64-row items, enough
 // workgroups to cover the chip twice (the persistent step: its grid), at
 // most 20 tiles per wave unless the row count alone fills the chip, and an
-// LDS input slice <= 48 KB so that three workgroups fit a CU (72 KB in the
-// persistent step).
+// LDS input slice <= 48 KB so that three workgroups fit a CU.
 constexpr size_t kLdsCapValu = 80 * 1024;
 constexpr size_t kLdsCapStaged = 48 * 1024;
-constexpr size_t kLdsCapPersistent = 72 * 1024;
 constexpr int kMinValuItems = 128;
 
-// The persistent kernel serves batches <= 4 (VALU items); larger batches
-// always take the per-stage kernels, and so does batch 1 on a handle sized
-// for long contexts (there the per-stage attention kernel, which spreads a
-// long sequence over many more workgroups, is faster).
-bool use_persistent(const qd_handle* h, int B) {
-  return h->persistent && gemv_nb(B) <= 4 && !(B == 1 && h->long_ctx);
-}
-
-// A persistent handle runs batch 1 as the streaming step kernel when its
-// shapes fit (decided in qd_create).
+// A persistent handle runs batch 1 as the weight-streaming step kernel when
+// its shapes fit and it is sized for short contexts (decided in qd_create);
+// every other step takes the per-stage kernels.
 bool use_stream(const qd_handle* h, int B) { return h->stream_ok && B == 1; }
 
-GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
-                   int grid = 0) {
+GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
-  const int target = grid > 0 ? grid : 2 * h->num_cus;
   const int nb = gemv_nb(B);
   GemvPlan p;
-  if (!use_persistent(h, B) && nb <= 4) {
-    // batch <= 4: one 16-row tile per item (the LM head: four), K split
+  if (nb == 1) {
+    // batch 1 (VALU): one 16-row tile per item (the LM head: four), K split
     // only when needed (LDS budget, or fewer than 128 items)
     p.rt = argmax ? 4 : 1;
     const int groups = N / (kTileRows * p.rt);
@@ -188,43 +175,16 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
     }
     return p;
   }
-  const size_t cap = use_persistent(h, B) ? kLdsCapPersistent : kLdsCapStaged;
-  if (use_persistent(h, B)) {
-    // The grid's workgroups share each stage: the split count minimises the
-    // items of the busiest workgroup times the k-tiles of an item (rows
-    // alone may give more row groups than workgroups), splits costing a
-    // little for their reduction; the input slice must fit in LDS.
-    int best_S = 1;
-    double best = 1e30;
-    for (int S = 1; S <= std::min(KT, 8); ++S) {
-      const int kps = (KT + S - 1) / S;
-      if (gemv_lds_bytes(B, kps) > cap && kps > 1) continue;
-      const int Se = (KT + kps - 1) / kps;
-      const double rounds = (double)((NRG * Se + target - 1) / target);
-      const double cost = rounds * kps + 2.0 * Se;
-      if (cost < best) { best = cost; best_S = Se; }
-    }
-    p.kps = (KT + best_S - 1) / best_S;
-    p.S = (KT + p.kps - 1) / p.kps;
-    if (gemv_lds_bytes(B, p.kps) > cap) {  // only very long K: split until it fits
-      for (int S = 9; S <= KT; ++S) {
-        p.kps = (KT + S - 1) / S;
-        p.S = (KT + p.kps - 1) / p.kps;
-        if (gemv_lds_bytes(B, p.kps) <= cap) break;
-      }
-    }
-    return p;
-  }
-  // MFMA items (batch >= 5): the fewest K splits that give every CU an item,
+  // MFMA items (batch >= 2): the fewest K splits that give every CU an item,
   // slices of at most 16 k-tiles while row groups alone do not (measured on
   // the 4B shape: batch 8 3.39 -> 3.19 ms per step against two items per CU
   // and 20-tile slices; batch 16 4.00 -> 3.93)
-  const int mtarget = grid > 0 ? grid : h->num_cus;
+  const int mtarget = h->num_cus;
   for (int S = 1; S <= KT; ++S) {
     const int kps = (KT + S - 1) / S;
     const int Se = (KT + kps - 1) / kps;
     if (kps > 16 && NRG < mtarget) continue;
-    if (gemv_lds_bytes(B, kps) > cap) continue;
+    if (gemv_lds_bytes(B, kps) > kLdsCapStaged) continue;
     p.S = Se;
     p.kps = kps;
     if (NRG * Se >= mtarget) return p;
@@ -233,9 +193,14 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
   return p;
 }
 
-// Most splits of one sequence (its longest table) at batch B.
+// Most splits of one sequence (its longest table) at batch B in the
+// per-stage attention kernel, and in the streaming kernel's items.
 int attn_splits(const qd_handle* h, int B) {
-  const int pps = attn_pages_per_split(B, use_persistent(h, B), h->long_ctx);
+  const int pps = attn_pages_per_split(B, false, h->long_ctx);
+  return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
+}
+int stream_attn_splits(const qd_handle* h) {
+  const int pps = attn_pages_per_split(1, true);
   return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
 }
 
@@ -416,11 +381,8 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.tap_q = tap ? taps->q_rot : nullptr;
     aa.tap_k = tap ? taps->k_rot : nullptr;
     aa.dev_flags = h->dev_flags;
-    // a persistent handle's batches <= 4 use the persistent kernel's item
-    // shape here too, so both launch modes compute the same bits
-    const bool pers = use_persistent(h, B);
-    HIP_TRY(h, launch_attention(aa, h->D, h->G, pers ? kAttnWavesPersistent : kAttnWaves,
-                                attn_pages_per_wave(B, pers, h->long_ctx), s));
+    HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
+                                attn_pages_per_wave(B, false, h->long_ctx), s));
     PROF(QD_PROF_ATTN);
     if (tap && taps->attn)
       HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,
@@ -445,116 +407,6 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   HIP_TRY(h, proj(QD_PROF_LM_HEAD, 0, true));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
-  return QD_OK;
-}
-
-GemvArgs gemv_template(qd_handle* h, const StepPtrs& sp, int N, int K, const float* xin,
-                       bool norm, float* out, int grid, bool argmax = false) {
-  GemvPlan p = plan_gemv(h, N, K, sp.B, argmax, grid);
-  GemvArgs a{};
-  a.N = N; a.K = K; a.B = sp.B; a.Bmax = h->cfg.max_batch;
-  a.S = p.S; a.kps = p.kps; a.rt = p.rt;
-  a.x = xin;
-  a.ssq = norm ? h->ssq : nullptr;
-  a.eps = h->cfg.rms_eps;
-  a.part = h->part; a.counters = h->gemv_cnt;
-  a.out = out;
-  a.ssq_out = h->ssq;
-  a.logits = sp.logits;
-  a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
-  a.amax_val2 = h->amax_val2; a.amax_idx2 = h->amax_idx2;
-  a.next_ids = sp.next;
-  return a;
-}
-
-// Co-resident grid of the persistent kernel at batch B (at most 2 per CU),
-// for the largest LDS any of its plans may ask for.
-int persistent_grid(qd_handle* h, int B, int* grid) {
-  auto it = h->step_grid.find(B);
-  if (it != h->step_grid.end()) { *grid = it->second; return QD_OK; }
-  const size_t lds_max = step_lds_bytes(B, h->D, h->G, 0) > kLdsCapPersistent
-                             ? step_lds_bytes(B, h->D, h->G, 0) : kLdsCapPersistent;
-  int g = 0;
-  HIP_TRY(h, step_max_grid(B, h->D, h->G, lds_max, h->num_cus, &g));
-  if (g < 1) return fail(h, QD_EUNSUPPORTED, "persistent step does not fit on a CU");
-  const int occupancy_grid = g;
-  g = std::min(g, 2 * h->num_cus);
-  if (const char* e = std::getenv("QD_STEP_GRID")) g = std::min(g, std::max(1, std::atoi(e)));
-  if (std::getenv("QD_DEBUG"))
-    std::fprintf(stderr, "[qd] persistent step B=%d: occupancy grid %d, grid %d\n", B,
-                 occupancy_grid, g);
-  h->step_grid[B] = g;
-  *grid = g;
-  return QD_OK;
-}
-
-// One step as one persistent cooperative kernel.
-int run_persistent(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
-  const int B = sp.B, H = h->H;
-  int grid = 0;
-  if (int rc = persistent_grid(h, B, &grid)) return rc;
-  StepArgs a{};
-  a.embed.table = h->embed;
-  a.embed.V = h->V; a.embed.H = H; a.embed.B = B; a.embed.Bmax = h->cfg.max_batch;
-  a.embed.tokens = sp.tokens; a.embed.x = h->x; a.embed.ssq_out = h->ssq;
-  a.embed.dev_flags = h->dev_flags;
-  a.qkv = gemv_template(h, sp, h->NQKV, H, h->x, true, h->qkv, grid);
-  a.o = gemv_template(h, sp, H, h->QD, h->attn, false, h->x, grid);
-  a.gu = gemv_template(h, sp, 2 * h->I, H, h->x, true, h->act, grid);
-  a.down = gemv_template(h, sp, H, h->I, h->act, false, h->x, grid);
-  a.lm = gemv_template(h, sp, h->V, H, h->x, true, nullptr, grid, true);
-  a.lm.w = h->lm;
-  a.lm.gain = h->final_norm;
-  a.qkv.part = h->part_qkv;
-  AttnArgs& at = a.attn;
-  at.qkv = h->qkv;
-  at.qkv_part = h->part_qkv;
-  at.qkv_S = a.qkv.S;
-  at.qkv_rows = kTileRows * a.qkv.rt;
-  at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
-  at.pool_layer = sp.pool;
-  at.num_pages = h->cfg.num_pages;
-  at.positions = sp.positions; at.block_tables = sp.tables;
-  at.max_pages = h->cfg.max_pages_per_seq;
-  at.B = B; at.Hq = h->Hq; at.Hkv = h->Hkv;
-  at.eps = h->cfg.rms_eps; at.scale = (float)(1.0 / std::sqrt((double)h->D));
-  at.S_max = attn_splits(h, B);
-  at.o_part = h->o_part; at.ml_part = h->ml_part; at.counters = h->attn_cnt;
-  at.out = h->attn;
-  at.dev_flags = h->dev_flags;
-  a.layers = h->layers_dev;
-  a.L = h->L;
-  a.pool_layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
-  a.cnt = h->step_cnt; a.flags = h->step_flags;
-  a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
-  a.dev_flags = h->dev_flags;
-  a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
-
-  int max_kps = 1;
-  for (const GemvArgs* g : {&a.qkv, &a.o, &a.gu, &a.down, &a.lm}) max_kps = std::max(max_kps, g->kps);
-  const size_t lds = step_lds_bytes(B, h->D, h->G, max_kps);
-#ifdef QD_STEP_TRACE
-  static unsigned long long* trace = nullptr;
-  const size_t trace_n = (size_t)grid * 1024 * 4;
-  if (!trace) {
-    HIP_TRY(h, hipMalloc(&trace, trace_n * 8));
-  }
-  HIP_TRY(h, hipMemsetAsync(trace, 0xff, trace_n * 8, s));
-  a.trace = trace;
-#endif
-  HIP_TRY(h, launch_step(a, h->D, h->G, grid, lds, s));
-#ifdef QD_STEP_TRACE
-  if (const char* path = std::getenv("QD_TRACE_OUT")) {
-    HIP_TRY(h, hipStreamSynchronize(s));
-    std::vector<unsigned long long> hostbuf(trace_n);
-    HIP_TRY(h, hipMemcpy(hostbuf.data(), trace, trace_n * 8, hipMemcpyDeviceToHost));
-    FILE* f = std::fopen(path, "wb");
-    if (f) {
-      std::fwrite(hostbuf.data(), 8, trace_n, f);
-      std::fclose(f);
-    }
-  }
-#endif
   return QD_OK;
 }
 
@@ -651,7 +503,7 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   at.max_pages = h->cfg.max_pages_per_seq;
   at.B = 1; at.Hq = h->Hq; at.Hkv = h->Hkv;
   at.eps = h->cfg.rms_eps; at.scale = (float)(1.0 / std::sqrt((double)h->D));
-  at.S_max = attn_splits(h, 1);
+  at.S_max = stream_attn_splits(h);
   at.o_part = h->o_part; at.ml_part = h->ml_part; at.counters = h->attn_cnt;
   at.out = h->attn;
   at.dev_flags = h->dev_flags;
@@ -780,7 +632,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->expected["model.embed_tokens.weight"] = 0;
   h->expected["model.norm.weight"] = 0;
 
-  h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
+  h->persistent = cfg->persistent != 0;
   h->long_ctx = cfg->max_pages_per_seq > kStreamMaxPages;
   if ((rc = setup_stream(h))) return bail(rc);
 
@@ -807,26 +659,24 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   size_t part_elems = 1, part_qkv_elems = 1;
   const int max_nrg = std::max(std::max(h->NQKV, 2 * I), std::max(H, V)) / kTileRows;
   for (int B = 1; B <= Bm; ++B) {
-    // the same plans the steps will use (persistent plans depend on the grid)
-    int grid = 0;
-    if (use_persistent(h, B) && (rc = persistent_grid(h, B, &grid))) return bail(rc);
+    // the same plans the steps will use
     const int dims[3][2] = {{H, h->QD}, {H, I}, {2 * I, H}};
     for (auto& d : dims) {
-      GemvPlan p = plan_gemv(h, d[0], d[1], B, false, grid);
+      GemvPlan p = plan_gemv(h, d[0], d[1], B);
       if (p.S > 1) part_elems = std::max(part_elems, (size_t)d[0] * p.S * B);
     }
-    const GemvPlan pl = plan_gemv(h, V, H, B, true, grid);
+    const GemvPlan pl = plan_gemv(h, V, H, B, true);
     if (pl.S > 1) part_elems = std::max(part_elems, (size_t)V * pl.S * B);
-    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B, false, grid);
+    const GemvPlan pq = plan_gemv(h, h->NQKV, H, B);
     part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * pq.S * B);
   }
   if ((rc = dev_alloc(h, &h->part, part_elems))) return bail(rc);
   if (h->stream_ok) part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * h->stream_qkv_S);
   if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg * kCntStride))) return bail(rc);
-  h->smax1 = attn_splits(h, 1);
   size_t att_rows = 0;
   for (int B = 1; B <= Bm; ++B) att_rows = std::max(att_rows, (size_t)B * h->Hq * attn_splits(h, B));
+  if (h->stream_ok) att_rows = std::max(att_rows, (size_t)h->Hq * stream_attn_splits(h));
   if ((rc = dev_alloc(h, &h->o_part, att_rows * h->D))) return bail(rc);
   if ((rc = dev_alloc(h, &h->ml_part, att_rows * 2))) return bail(rc);
   if ((rc = dev_alloc(h, &h->attn_cnt, (size_t)Bm * h->Hkv * kCntStride))) return bail(rc);
@@ -844,19 +694,16 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (e == hipSuccess) e = hipMemset(h->dev_flags, 0, sizeof(int));
   if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
 
-  // persistent step state
-  h->persistent = cfg->persistent != 0 && step_supported(h->D, h->G);
-  if (h->persistent) {
+  // streaming step state
+  if (h->stream_ok) {
     if ((rc = dev_alloc(h, &h->layers_dev, (size_t)L))) return bail(rc);
     // (the streaming step also counts the LM head's workgroups)
     if ((rc = dev_alloc(h, &h->step_cnt, (size_t)2 + (size_t)L * kCntPerLayer))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_flags, (size_t)2 * h->num_cus * 32))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_exit, 1))) return bail(rc);
     if ((rc = dev_alloc(h, &h->step_abort, 1))) return bail(rc);
-    if (h->stream_ok) {
-      if ((rc = dev_alloc(h, &h->stream_amax_val, (size_t)h->stream_grid))) return bail(rc);
-      if ((rc = dev_alloc(h, &h->stream_amax_idx, (size_t)h->stream_grid))) return bail(rc);
-    }
+    if ((rc = dev_alloc(h, &h->stream_amax_val, (size_t)h->stream_grid))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->stream_amax_idx, (size_t)h->stream_grid))) return bail(rc);
     e = hipMemset(h->step_cnt, 0, sizeof(unsigned) * (2 + (size_t)L * kCntPerLayer));
     if (e == hipSuccess) e = hipMemset(h->step_flags, 0, sizeof(unsigned) * 2 * h->num_cus * 32);
     if (e == hipSuccess) e = hipMemset(h->step_exit, 0, sizeof(unsigned));
@@ -990,7 +837,6 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits};
   if (use_stream(h, batch)) return run_stream(h, sp, h->stream);
-  if (use_persistent(h, batch)) return run_persistent(h, sp, h->stream);
   static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
   if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);
 
@@ -1106,7 +952,6 @@ void* qd_stream(const qd_handle* h) { return h ? static_cast<void*>(h->stream) :
 int qd_step_path(const qd_handle* h, int32_t batch) {
   if (!h || batch < 1 || batch > h->cfg.max_batch) return QD_EINVAL;
   if (use_stream(h, batch)) return QD_PATH_STREAM;
-  if (use_persistent(h, batch)) return QD_PATH_PERSISTENT;
   static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
   return h->cfg.use_graphs && !no_graph ? QD_PATH_GRAPH : QD_PATH_STAGED;
 }

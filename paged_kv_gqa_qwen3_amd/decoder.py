@@ -74,7 +74,7 @@ class Decoder:
                                     tables, pool, next_ids, logits, taps, layer)
 
     def step_path(self, batch: int) -> str:
-        """'stream', 'persistent', 'graph' or 'staged': how a step of `batch` runs."""
+        """'stream', 'graph' or 'staged': how a step of `batch` runs."""
         return binding.qd_step_path(self.handle, batch)
 
     def device_status(self) -> int:

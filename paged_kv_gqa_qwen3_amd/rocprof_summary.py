@@ -26,7 +26,6 @@ import sys
 # Kernel-name substrings -> class (first match wins).
 CLASSES = (
     ("stream_step_kernel", "stream_step"),
-    ("step_kernel", "persistent_step"),
     ("gemv_kernel<1, 4>", "qkv"),
     ("gemv_kernel<1, 2>", "gate_up"),
     ("gemv_kernel<1, 3>", "lm_head"),

@@ -90,8 +90,8 @@ def _appended_mask(batch, pairs):
 @pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
 def test_tiny_workload_teacher_forced(torch, persistent):
     """Tiny GQA decoder: oracle prefill of 64 random tokens, then 16 greedy
-    decode steps on the GPU (graph replay or persistent kernel), teacher-forced
-    by the oracle."""
+    decode steps on the GPU (graph replay, or on a persistent handle the
+    weight-streaming kernel), teacher-forced by the oracle."""
     w = synth.WORKLOADS["tiny"]
     shape = w.shape
     W = synth.make_weights(shape, w.seed)
@@ -212,15 +212,15 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
 @pytest.mark.parametrize("B,ctx", [
     (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
     (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
-    # splits of 8 pages (batch <= 4) or 24 pages: one to 17 of them, and a
-    # combine of more than 16 splits (2100)
+    # splits of 8 pages (batch <= 8, at most 128 pages per sequence) or 24
+    # pages: one to 17 of them, and a combine of more than 16 splits (2100)
     (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]),
 ])
 def test_tiny_stages(torch, B, ctx):
     shape = synth.TINY
     W = synth.make_weights(shape, 100 + B)
     batch = synth.make_paged_batch(shape, ctx, 1, 200 + B)
-    mfma = B > 4
+    mfma = B > 1
     dec = Decoder(shape, max(B, 1), batch.max_pages, batch.num_pages, use_graphs=False)
     dec.load_numpy_weights(W)
     QD, KD = shape.q_dim, shape.kv_dim
@@ -282,35 +282,48 @@ def test_graph_replay_matches_eager(torch):
 
 
 @pytest.mark.parametrize("B,ctx", [(3, [5, 40, 77]), (4, [0, 16, 250, 31]), (2, [700, 1300])])
-def test_persistent_matches_staged_bitwise(torch, B, ctx):
-    """At batch 2-4 the persistent kernel and the per-stage kernels of the
-    same handle run the same items with the same split plans, so every bit
-    must agree, over chained steps (the staged run goes through the taps
-    entry point, which never uses the persistent kernel)."""
+def test_persistent_handle_mixed_batches(torch, B, ctx):
+    """A persistent handle runs batch 1 as the streaming kernel and larger
+    batches as the per-stage graph, sharing its scratch between the two.
+    Steps of both sizes interleaved on one handle must give the same bits as
+    the same steps on a graph-only handle (batch B) and on a batch-1
+    streaming handle (the first sequence alone, on a pool of its own)."""
     shape = synth.TINY
     W = synth.make_weights(shape, 70 + B)
     batch = synth.make_paged_batch(shape, ctx, 5, 71 + B)
-    dp = Decoder(shape, B, batch.max_pages, batch.num_pages, persistent=True)
-    dp.load_numpy_weights(W)
-    pp, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
-    ip = StepIO(torch, B, batch.max_pages, shape.vocab)
-    ie = StepIO(torch, B, batch.max_pages, shape.vocab)
+    mp, npg = batch.max_pages, batch.num_pages
+    dp = Decoder(shape, B, mp, npg, persistent=True)
+    dg = Decoder(shape, B, mp, npg, persistent=False)
+    ds = Decoder(shape, 1, mp, npg, persistent=True)
+    assert [dp.step_path(b) for b in (1, B)] == ["stream", "graph"]
+    assert ds.step_path(1) == "stream"
+    for d in (dp, dg, ds):
+        d.load_numpy_weights(W)
+    pools = [pool_to_device(batch.pool) for _ in range(4)]  # dp batch B, dg, dp batch 1, ds
+    io = [StepIO(torch, B, mp, shape.vocab), StepIO(torch, B, mp, shape.vocab),
+          StepIO(torch, 1, mp, shape.vocab), StepIO(torch, 1, mp, shape.vocab)]
     tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    tok1, pos1 = batch.tokens[:1].copy(), batch.positions[:1].copy()
     for step in range(5):
-        say(f"persistent vs staged B={B} step {step}")
-        ip.set(tokens, positions, batch.block_tables)
-        ie.set(tokens, positions, batch.block_tables)
-        ip.run(dp, pp)
+        say(f"mixed batches B={B} step {step}")
+        for i, d in ((0, dp), (2, dp), (1, dg), (3, ds)):
+            if i < 2:
+                io[i].set(tokens, positions, batch.block_tables)
+            else:
+                io[i].set(tok1, pos1, batch.block_tables[:1])
+            io[i].run(d, pools[i])
         torch.cuda.synchronize()
-        dp.step_taps(ie.tok, ie.pos, ie.tab, pe, ie.nxt, ie.logits, None, -1)
-        torch.cuda.synchronize()
-        assert torch.equal(ip.logits, ie.logits)
-        assert torch.equal(ip.nxt, ie.nxt)
-        tokens = ie.nxt.cpu().numpy()
-        positions = positions + 1
-    assert torch.equal(pp, pe)
-    assert dp.device_status() == 0
-    dp.close()
+        assert torch.equal(io[0].logits, io[1].logits)
+        assert torch.equal(io[0].nxt, io[1].nxt)
+        assert torch.equal(io[2].logits, io[3].logits)
+        assert torch.equal(io[2].nxt, io[3].nxt)
+        tokens, positions = io[1].nxt.cpu().numpy(), positions + 1
+        tok1, pos1 = io[3].nxt.cpu().numpy(), pos1 + 1
+    assert torch.equal(pools[0], pools[1])
+    assert torch.equal(pools[2], pools[3])
+    for d in (dp, dg, ds):
+        assert d.device_status() == 0
+        d.close()
 
 
 @pytest.mark.parametrize("ctx", [[40], [700], [2000], [0]])
@@ -362,14 +375,12 @@ def test_stream_step_matches_staged(torch, ctx):
 
 def test_step_paths(torch):
     """qd_step_path: a persistent handle streams batch 1 only when sized for
-    at most 128 pages per sequence, runs batches 2-4 as the persistent step
-    and larger ones as the graph; a non-persistent handle always takes the
-    graph; batches outside 1..max_batch are rejected."""
+    at most 128 pages per sequence and runs every larger batch as the graph;
+    a non-persistent handle always takes the graph; batches outside
+    1..max_batch are rejected."""
     shape = synth.TINY
-    for pages, persistent, want in ((128, True, ["stream", "persistent", "persistent",
-                                                  "persistent", "graph", "graph"]),
-                                    (129, True, ["graph", "persistent", "persistent",
-                                                 "persistent", "graph", "graph"]),
+    for pages, persistent, want in ((128, True, ["stream"] + ["graph"] * 5),
+                                    (129, True, ["graph"] * 6),
                                     (16, False, ["graph"] * 6)):
         dec = Decoder(shape, 6, pages, pages + 1, persistent=persistent)
         assert [dec.step_path(b) for b in range(1, 7)] == want, (pages, persistent)
@@ -444,9 +455,13 @@ def _weights(shape, seed):
     return _WEIGHTS[key]
 
 
-@pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
-@pytest.mark.parametrize("name", ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256",
-                                  "4b_bs1_ctx8192", "8b_bs8_ragged"])
+# Every workload through the per-stage graph; the one that a persistent
+# handle runs differently (batch 1 at a short context: the streaming kernel)
+# also on such a handle.
+@pytest.mark.parametrize("name,persistent", [
+    (n, False) for n in ("4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
+                         "8b_bs8_ragged")] + [("4b_bs1_ctx512", True)],
+    ids=lambda v: v if isinstance(v, str) else ("persistent" if v else "graph"))
 def test_full_size_steps(torch, name, persistent):
     w = synth.WORKLOADS[name]
     shape = w.shape
@@ -458,6 +473,7 @@ def test_full_size_steps(torch, name, persistent):
     orc = oracle.Oracle(shape, W)
     dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True,
                   persistent=persistent)
+    assert dec.step_path(w.batch) == ("stream" if persistent else "graph")
     dec.load_numpy_weights(W)
     pool = pool_to_device(batch.pool)
     pool_or = batch.pool

@@ -209,23 +209,17 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
         np.testing.assert_array_equal(nxt, np.argmax(logits, axis=1))
 
 
-@pytest.mark.parametrize("B,ctx", [
-    (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
-    (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
-    # splits of 8 pages (batch <= 8, at most 128 pages per sequence) or 24
-    # pages: one to 17 of them, and a combine of more than 16 splits (2100)
-    (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]),
-])
-def test_tiny_stages(torch, B, ctx):
-    shape = synth.TINY
-    W = synth.make_weights(shape, 100 + B)
-    batch = synth.make_paged_batch(shape, ctx, 1, 200 + B)
+def _run_stage_checks(torch, shape, W, batch, what):
+    """One step through the taps entry point (per-stage kernels, no graph),
+    stopping at the first and last layer, each stage checked by the oracle
+    from the GPU's own input to it."""
+    B = batch.tokens.shape[0]
     mfma = B > 1
-    dec = Decoder(shape, max(B, 1), batch.max_pages, batch.num_pages, use_graphs=False)
+    dec = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False)
     dec.load_numpy_weights(W)
     QD, KD = shape.q_dim, shape.kv_dim
     for layer in (0, shape.num_layers - 1):
-        say(f"stages B={B} ctx={ctx} layer={layer}")
+        say(f"stages {what} layer={layer}")
         pool = pool_to_device(batch.pool)
         taps = {
             "x_in": torch.zeros(B, shape.hidden, device="cuda"),
@@ -248,6 +242,47 @@ def test_tiny_stages(torch, B, ctx):
                       logits.cpu().numpy(), nxt.cpu().numpy(), mfma)
     assert dec.device_status() == 0
     dec.close()
+
+
+@pytest.mark.parametrize("B,ctx", [
+    (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
+    (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
+    # splits of 8 pages (batch <= 8, at most 128 pages per sequence) or 24
+    # pages: one to 17 of them, and a combine of more than 16 splits (2100)
+    (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]),
+    # 32- and 64-column MFMA items, up to the largest batch a handle takes
+    (24, [(37 * i) % 400 for i in range(24)]), (33, [(53 * i) % 300 for i in range(33)]),
+    (64, [(29 * i) % 200 for i in range(64)]),
+])
+def test_tiny_stages(torch, B, ctx):
+    shape = synth.TINY
+    W = synth.make_weights(shape, 100 + B)
+    batch = synth.make_paged_batch(shape, ctx, 1, 200 + B)
+    _run_stage_checks(torch, shape, W, batch, f"B={B} ctx={ctx}")
+
+
+# Every (head_dim, query heads per KV head) pair the attention kernel is
+# built for, on small models (2 layers, hidden 256, 2 KV heads), at batch 1
+# (the fp32-input GEMV items) and batch 5 (MFMA items), with one split, a
+# few and a combine over more than 16.
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 2), (64, 4), (128, 1), (128, 2), (128, 4)])
+@pytest.mark.parametrize("ctx", [[700], [0, 17, 300, 40, 1100]], ids=["b1", "b5"])
+def test_head_shapes_stages(torch, D, G, ctx):
+    shape = synth.ModelShape(f"d{D}g{G}", 2, 256, 2 * G, 2, D, 704, 4096, True)
+    seed = 300 + D + G
+    W = synth.make_weights(shape, seed)
+    batch = synth.make_paged_batch(shape, ctx, 1, seed)
+    _run_stage_checks(torch, shape, W, batch, f"D={D} G={G} ctx={ctx}")
+
+
+def test_max_context_stages(torch):
+    """The longest block-table row a handle takes (2048 pages, 32768 tokens):
+    the step at position 32767, a combine over 86 splits of 24 pages."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 91)
+    batch = synth.make_paged_batch(shape, [32767], 1, 92)
+    assert batch.max_pages == 2048
+    _run_stage_checks(torch, shape, W, batch, "ctx=32767")
 
 
 # ----------------------------------------------------------------------------- invariances

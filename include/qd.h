@@ -137,6 +137,32 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
                    const int32_t* positions, const int32_t* block_tables, void* kv_pool,
                    int32_t* out_next_ids, float* out_logits);
 
+/* Sample the next token of each sequence from a step's logits on the
+ * device, so that only the token id leaves the GPU (the yuzheng310 page,
+ * "GPU 算子与执行优化", part 3: argmax and the top-p/top-k filters run on
+ * the device; the rkmt page, "从零构建 Qwen3-8B 推理引擎", section 4.1.2:
+ * temperature and top_p travel with a request).  All pointers are DEVICE
+ * buffers of `batch` entries (logits: [batch][vocab] fp32, as qd_decode_step
+ * writes them to out_logits), owned by the caller:
+ *   temperature  fp32   <= 0 or NaN: greedy (lowest index among the largest)
+ *   top_k        int32  keep the top_k highest logits (ties: lower id first);
+ *                       <= 0 or >= vocab: no limit; 1: greedy
+ *   top_p        fp32   then keep the shortest run of those, highest first,
+ *                       whose weight reaches top_p of their total; >= 1 or
+ *                       NaN: no limit; <= 0: greedy
+ *   uniform      fp32   the caller's draw in [0, 1) (below 0 or NaN: 0)
+ *   out_ids      int32  the sampled token ids
+ * Weights are exp((logit - max) / temperature) in fp32, each counted as the
+ * integer floor(w * 2^32) so that every sum is exact; the sampled token is
+ * the kept one, in increasing id order, at which the running weight first
+ * exceeds floor(uniform * total).  Logits must be finite and 16-byte
+ * aligned.  Asynchronous on the handle's stream; no allocation (scratch
+ * owned by the handle: calls on one handle must not overlap).  QD_EINVAL for
+ * a NULL or misaligned pointer or a batch outside 1..max_batch. */
+int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* temperature,
+              const int32_t* top_k, const float* top_p, const float* uniform,
+              int32_t* out_ids);
+
 /* Intermediate values of one layer, for checking each stage of the step
  * (fp32 DEVICE buffers; any may be NULL):
  *   x_in [B][H]  qkv [B][(Hq+2Hkv)D]  q_rot [B][Hq][D]  k_rot [B][Hkv][D]

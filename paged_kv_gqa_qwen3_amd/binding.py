@@ -29,7 +29,7 @@ QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
-            "qd_step_path", "qd_destroy", "qd_last_error")
+            "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error")
 
 PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
 
@@ -91,6 +91,8 @@ def load_library():
         lib.qd_profile_class.restype = ctypes.c_int
         lib.qd_profile_class.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_float)]
+        lib.qd_sample.restype = ctypes.c_int
+        lib.qd_sample.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
         lib.qd_device_status.restype = ctypes.c_int
         lib.qd_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
         lib.qd_stream.restype = P
@@ -194,6 +196,15 @@ def qd_profile_class(handle: int, batch: int, cls: str, reps: int = 20) -> float
     _check(lib.qd_profile_class(handle, batch, PROF_CLASSES.index(cls), reps, ctypes.byref(v)),
            handle)
     return float(v.value)
+
+
+def qd_sample(handle: int, batch: int, logits, temperature, top_k, top_p, uniform,
+              out_ids) -> None:
+    """Sampled next token per sequence from device logits [batch][vocab]; every
+    argument is a device tensor of `batch` entries (see include/qd.h)."""
+    lib = load_library()
+    _check(lib.qd_sample(handle, batch, _ptr(logits), _ptr(temperature), _ptr(top_k),
+                         _ptr(top_p), _ptr(uniform), _ptr(out_ids)), handle)
 
 
 def qd_device_status(handle: int) -> int:

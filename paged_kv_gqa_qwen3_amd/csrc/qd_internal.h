@@ -201,6 +201,28 @@ constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false
 // Splits of one sequence the final combine can hold (its (max, sum) pairs sit in LDS).
 constexpr int kMaxSplitsStaged = 512;
 
+// On-device sampling (qd_sample.hip): G workgroups per row of logits, each
+// owning C of them; top_k up to kFastTopK is merged from per-chunk lists of
+// 64 candidates, anything else runs over the whole row in one workgroup.
+constexpr int kFastTopK = 64;
+constexpr int kSampleChunk = 8192;  // most logits per workgroup
+struct SampleArgs {
+  const float* logits;       // [B][V]
+  int V;
+  const float* temperature;  // [B]
+  const int* top_k;          // [B]
+  const float* top_p;        // [B]
+  const float* uniform;      // [B] draws in [0, 1)
+  int* out;                  // [B] sampled token ids
+  int G, C;                  // workgroups per row, logits per workgroup (sample_split)
+  float* part_max;           // [B][G] chunk maxima and their ids
+  int* part_idx;
+  unsigned long long* cand;  // [B][G][64] each chunk's first 64 tokens in rank order
+  unsigned* counters;        // [B] at stride kCntStride, zero between calls
+};
+void sample_split(int V, int* G, int* C);
+hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s);
+
 // Launchers (qd_kernels.hip).  All return the launch status.
 // Source row r lands in packed row (r / blk) * stride + off + r % blk.
 hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, int blk,

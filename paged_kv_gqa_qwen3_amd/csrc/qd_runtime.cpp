@@ -80,6 +80,12 @@ struct qd_handle {
   int* amax_idx2 = nullptr;
   unsigned* amax_cnt = nullptr;
   int32_t* prof_ids = nullptr;  // next-token output of qd_profile_class's LM head launches
+  // qd_sample scratch: chunk maxima, chunk candidates, per-row arrival counters
+  int sample_G = 1, sample_C = 0;
+  float* sample_max = nullptr;
+  int* sample_idx = nullptr;
+  unsigned long long* sample_cand = nullptr;
+  unsigned* sample_cnt = nullptr;
   int* dev_flags = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   int max_pos = 0;
@@ -688,6 +694,21 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if ((rc = dev_alloc(h, &h->amax_cnt, (ng2_v + 1) * kCntStride))) return bail(rc);
   if ((rc = dev_alloc(h, &h->dev_flags, 1))) return bail(rc);
   if ((rc = dev_alloc(h, &h->prof_ids, (size_t)Bm))) return bail(rc);
+  sample_split(V, &h->sample_G, &h->sample_C);
+  if ((size_t)h->sample_G * 512 > (size_t)h->sample_C * 4)  // the merge reuses the chunk's LDS
+  {
+    fail(h, QD_EUNSUPPORTED, "vocab too large for on-device sampling (at most 524288)");
+    return bail(QD_EUNSUPPORTED);
+  }
+  {
+    const size_t slots = (size_t)Bm * h->sample_G;
+    if ((rc = dev_alloc(h, &h->sample_max, slots))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_idx, slots))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_cand, slots * 64))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_cnt, (size_t)Bm * kCntStride))) return bail(rc);
+    e = hipMemset(h->sample_cnt, 0, sizeof(unsigned) * Bm * kCntStride);
+    if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+  }
   e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg * kCntStride);
   if (e == hipSuccess) e = hipMemset(h->attn_cnt, 0, sizeof(unsigned) * Bm * h->Hkv * kCntStride);
   if (e == hipSuccess) e = hipMemset(h->amax_cnt, 0, sizeof(unsigned) * (ng2_v + 1) * kCntStride);
@@ -935,6 +956,22 @@ int qd_profile_class(qd_handle* h, int32_t batch, int32_t cls, int32_t reps, flo
   if (ge) (void)hipGraphExecDestroy(ge);
   if (g) (void)hipGraphDestroy(g);
   return rc;
+}
+
+int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* temperature,
+              const int32_t* top_k, const float* top_p, const float* uniform,
+              int32_t* out_ids) {
+  if (!h) return QD_EINVAL;
+  if (batch < 1 || batch > h->cfg.max_batch) return fail(h, QD_EINVAL, "batch out of range");
+  if (!logits || !temperature || !top_k || !top_p || !uniform || !out_ids)
+    return fail(h, QD_EINVAL, "NULL sampling pointer");
+  if (reinterpret_cast<uintptr_t>(logits) % 16)
+    return fail(h, QD_EINVAL, "logits must be 16-byte aligned");
+  SampleArgs a{logits, h->V, temperature, top_k, top_p, uniform, out_ids,
+               h->sample_G, h->sample_C, h->sample_max, h->sample_idx,
+               h->sample_cand, h->sample_cnt};
+  HIP_TRY(h, launch_sample(a, batch, h->stream));
+  return QD_OK;
 }
 
 int qd_device_status(qd_handle* h, int32_t* flags) {

@@ -1,0 +1,476 @@
+// On-device sampling of the next token from one row of logits per
+// workgroup: temperature, top-k and top-p, with a uniform draw the caller
+// supplies, so that only the token id leaves the GPU (the yuzheng310 page,
+// "GPU 算子与执行优化", part 3: argmax and the top-p/top-k filters stay on
+// the device; the rkmt page, section 4.1.2: temperature and top_p travel with
+// a request, the sampled token comes back).
+//
+// The pages fix no algorithm; the kernel follows the plain definitions:
+//   * temperature <= 0 (or NaN): the greedy token, lowest index on ties;
+//   * weights w_i = exp((l_i - max l) / T) in fp32, held as integers
+//     q_i = floor(w_i * 2^32) (kept in doubles: every sum stays below 2^53,
+//     so sums are exact and independent of order);
+//   * rank order: logit descending, then token id ascending;
+//   * top_k in 1..V-1 keeps the first top_k tokens in rank order;
+//   * top_p < 1 keeps, of those, the shortest rank-order prefix whose weight
+//     reaches ceil(top_p * Q) (Q: the weight top-k kept; top_p <= 0: the
+//     first token alone);
+//   * the draw: t = min(floor(u * R), R - 1) over the kept weight R, and the
+//     token is the kept one, in increasing id order, whose running weight
+//     first exceeds t.
+//
+// One launch per call, G workgroups per row (G = ceil(V / 8192)), each
+// owning a chunk of at most 8192 logits that it loads into LDS once.  Every
+// chunk leaves its (max, argmax) and, when 2 <= top_k <= kFastTopK, its 64
+// first tokens in rank order (each wave sorts batches of 64 across its lanes
+// and keeps the best 64; then the lists are merged); the last workgroup of
+// the row to arrive merges them: the greedy token from the maxima, and the
+// row's first 64 tokens from the lists, then top-k, top-p and the draw in one
+// wave.  Any other setting (top_k 0 or above kFastTopK with temperature > 0)
+// takes the whole-row path in that last workgroup: cut points in rank order
+// by radix selection over a 32-bit key that orders floats (four passes of 8
+// bits: token counts for top-k, weight for top-p), then one pass in id order
+// among the tokens whose key equals the cut key; every pass re-reads the row
+// from L2 (608 KB for a 151,936 token vocabulary) and recomputes the weights
+// it needs.
+#include <hip/hip_runtime.h>
+
+#include "qd_device.h"
+
+namespace qd {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleWaves = kSampleThreads / 64;
+
+// Larger float -> larger key; -0 and +0 share a key (they rank as equals).
+__device__ __forceinline__ unsigned sample_key(float x) {
+  const unsigned b = __float_as_uint(x + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+struct SampleSmem {
+  double mass[256];
+  double wd[kSampleWaves];
+  float wv[kSampleWaves];
+  int wi[kSampleWaves];
+  unsigned key;       // a selected cut key
+  double need;        // count or weight still to take at that key
+  int id;             // last id kept at the cut key
+};
+
+__device__ __forceinline__ float key_value(unsigned key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Add val to histogram bin `bin` of sm.mass for the lanes where `on` (call
+// in wave-uniform control flow): lanes of one bin are summed first while at
+// least 8 share it (the top byte of the key puts most tokens of a row in a
+// few bins), the rest add one by one.
+__device__ __forceinline__ void hist_add(SampleSmem& sm, unsigned bin, double val, bool on) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long pending = __ballot(on);
+  while (pending) {
+    const int leader = __ffsll((long long)pending) - 1;
+    const unsigned lb = __shfl(bin, leader);
+    const bool same = ((pending >> lane) & 1ull) && bin == lb;
+    const unsigned long long m = __ballot(same);
+    if (__popcll(m) < 8) {
+      if ((pending >> lane) & 1ull) atomicAdd(&sm.mass[bin], val);
+      break;
+    }
+    double sum = same ? val : 0.0;
+#pragma unroll
+    for (int s2 = 32; s2 >= 1; s2 >>= 1) sum += __shfl_xor(sum, s2);
+    if (lane == leader) atomicAdd(&sm.mass[lb], sum);
+    pending &= ~m;
+  }
+}
+
+// After a histogram pass of a radix selection: the bin (from the top) whose
+// running total reaches `need`, into sm.key (with the digits fixed so far)
+// and what remains to take inside it into sm.need.  Threads 0-63 only.
+__device__ __forceinline__ void pick_bin(SampleSmem& sm, unsigned prefix, int shift, double need) {
+  const int lane = threadIdx.x & 63;
+  double m4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m4[e] = sm.mass[255 - (4 * lane + e)];
+  const double s4 = m4[0] + m4[1] + m4[2] + m4[3];
+  double inc = s4;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  double before = inc - s4;
+  const unsigned long long hit = __ballot(before < need && need <= inc);
+  const int first = hit ? __ffsll((long long)hit) - 1 : 63;
+  if (lane == first) {
+    int e = 0;
+    while (e < 3 && before + m4[e] < need) { before += m4[e]; ++e; }
+    const unsigned bin = 255u - (unsigned)(4 * lane + e);
+    sm.key = prefix | (bin << shift);
+    sm.need = need - before;
+  }
+}
+
+// Sum over the block (exact: the values are integers below 2^53).
+__device__ __forceinline__ double block_sum(double v, SampleSmem& sm) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sm.wd[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSampleWaves; ++w) s += sm.wd[w];
+  return s;
+}
+
+// Exclusive prefix over threads in thread order (exact, as block_sum).
+__device__ __forceinline__ double block_exclusive(double v, SampleSmem& sm) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) sm.wd[wave] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += sm.wd[w];
+  return base + inc - v;
+}
+
+// The whole-row path for row b (one workgroup of kSampleThreads), given
+// the row's max M (T > 0, top_p > 0, top_k not 1).
+__device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, float p,
+                           float u, SampleSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int V = a.V, V4 = a.V >> 2;
+  const f32x4* __restrict__ row4 = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V);
+
+  // Passes over the row.  strided: float4 groups tid, tid + 1024, ...
+  // (coalesced), four loads in flight per thread; chunked: the thread's own
+  // run of consecutive groups, so that thread order is id order.  fn(id,
+  // logit, valid) is called in wave-uniform control flow (valid false past
+  // the end), so it may use cross-lane operations.
+  auto strided = [&](auto&& fn) {
+    for (int j0 = tid; j0 < V4; j0 += 4 * kSampleThreads) {
+      f32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q * kSampleThreads;
+        v[q] = j < V4 ? row4[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q * kSampleThreads;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fn(4 * j + e, v[q][e], j < V4);
+      }
+    }
+  };
+  const int c4 = (V4 + kSampleThreads - 1) / kSampleThreads;
+  const int g_lo = min(V4, tid * c4), g_hi = min(V4, g_lo + c4);
+  auto chunked = [&](auto&& fn) {  // no cross-lane operations in fn
+    for (int j0 = g_lo; j0 < g_hi; j0 += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q < g_hi) v[q] = row4[j0 + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q < g_hi) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fn(4 * (j0 + q) + e, v[q][e]);
+        }
+    }
+  };
+
+  auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
+
+  // The cut in rank order: the key at which the running total of unit(l)
+  // over tokens passing `in`, taken from the largest key down, reaches
+  // need(total) (total: the sum over all of them, known after the first
+  // pass); leaves the key in sm.key and in sm.need what remains to take
+  // among the tokens of that key.  Returns the total.
+  auto select = [&](auto&& in, auto&& unit, auto&& need_of) {
+    unsigned prefix = 0u, mask = 0u;
+    double need = 0.0, total = 0.0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
+      __syncthreads();
+      strided([&](int i, float l, bool ok) {
+        const unsigned key = sample_key(l);
+        const bool on = ok && (key & mask) == prefix && in(i, l, key);
+        double val = 0.0;
+        if (on) val = unit(l);
+        hist_add(sm, (key >> shift) & 255u, val, on);
+      });
+      __syncthreads();
+      if (shift == 24) {
+        double t4 = 0.0;
+        for (int j = 0; j < 256; ++j) t4 += sm.mass[j];  // exact: integers < 2^53
+        total = t4;
+        need = need_of(total);
+      }
+      if (tid < 64) pick_bin(sm, prefix, shift, need);
+      __syncthreads();
+      prefix = sm.key;
+      need = sm.need;
+      mask |= 255u << shift;
+    }
+    return total;
+  };
+
+  // The last id (in id order) among tokens with key kc passing `in` at
+  // which the running unit total reaches need.
+  auto cut_id = [&](unsigned kc, auto&& in, auto&& unit, double need) {
+    if (tid == 0) sm.id = V - 1;
+    double mine = 0.0;
+    chunked([&](int i, float l) {
+      if (sample_key(l) == kc && in(i, l, kc)) mine += unit(l);
+    });
+    double run = block_exclusive(mine, sm);
+    if (run < need && need <= run + mine) {
+      bool found = false;
+      chunked([&](int i, float l) {
+        if (!found && sample_key(l) == kc && in(i, l, kc)) {
+          run += unit(l);
+          if (run >= need) { sm.id = i; found = true; }
+        }
+      });
+    }
+    __syncthreads();
+    return sm.id;
+  };
+
+  // --- top-k
+  const bool use_k = k > 0 && k < V;
+  unsigned kk = 0u;
+  int ik = V;
+  auto all = [](int, float, unsigned) { return true; };
+  auto one = [](float) { return 1.0; };
+  if (use_k) {
+    select(all, one, [&](double) { return (double)k; });
+    kk = sm.key;
+    ik = cut_id(kk, all, one, sm.need);
+  }
+  auto in_k = [&](int i, float, unsigned key) { return !use_k || key > kk || (key == kk && i <= ik); };
+
+  // --- top-p (the target is formed from the total weight top-k kept)
+  const bool use_p = p < 1.f;
+  unsigned kp = 0u;
+  int ip = V;
+  if (use_p) {
+    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); });
+    kp = sm.key;
+    ip = cut_id(kp, in_k, weight, sm.need);
+  }
+  auto kept = [&](int i, float l) {
+    const unsigned key = sample_key(l);
+    return in_k(i, l, key) && (!use_p || key > kp || (key == kp && i <= ip));
+  };
+
+  // --- the draw, in id order
+  double mine = 0.0;
+  chunked([&](int i, float l) { if (kept(i, l)) mine += weight(l); });
+  double run = block_exclusive(mine, sm);
+  const double R = block_sum(mine, sm);
+  const double t = fmin(floor((double)u * R), R - 1.0);
+  if (run <= t && t < run + mine) {
+    bool found = false;
+    chunked([&](int i, float l) {
+      if (!found && kept(i, l)) {
+        run += weight(l);
+        if (t < run) { a.out[b] = i; found = true; }
+      }
+    });
+  }
+}
+
+// Top-64 lists, one value per lane, sorted descending across the lanes of a
+// wave.  A token is the 64-bit value key << 32 | (2^32 - 1 - id): larger
+// for a larger logit, then a lower id (the rank order); 0 is "no token".
+typedef unsigned long long u64;
+static_assert(kFastTopK <= 64, "the fast path keeps 64 candidates per chunk");
+
+__device__ __forceinline__ u64 shfl64(u64 v, int src) {
+  const unsigned lo = __shfl((unsigned)v, src), hi = __shfl((unsigned)(v >> 32), src);
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
+  const unsigned lo = __shfl_xor((unsigned)v, m), hi = __shfl_xor((unsigned)(v >> 32), m);
+  return ((u64)hi << 32) | lo;
+}
+
+// Bitonic sort of the wave's 64 values, descending across lanes.
+__device__ __forceinline__ u64 sort64(u64 x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const u64 y = shfl_xor64(x, stride);
+      const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+      x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  return x;
+}
+
+// The 64 largest of two sorted lists, sorted: the lane-wise larger of one
+// list and the other reversed is bitonic and holds them; a bitonic merge
+// orders it.
+__device__ __forceinline__ u64 merge64(u64 a, u64 b) {
+  const int lane = threadIdx.x & 63;
+  const u64 br = shfl64(b, 63 - lane);
+  u64 x = a > br ? a : br;
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const u64 y = shfl_xor64(x, stride);
+    x = (lane & stride) == 0 ? (x > y ? x : y) : (x < y ? x : y);
+  }
+  return x;
+}
+
+__device__ __forceinline__ u64 token_value(float l, int id) {
+  return ((u64)sample_key(l) << 32) | (0xffffffffu - (unsigned)id);
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ SampleSmem sm;
+  __shared__ u64 lists[kSampleWaves][64];
+  __shared__ unsigned s_flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
+  const int V = a.V;
+  const float T = a.temperature[b];
+  const int k = a.top_k[b];
+  const float p = a.top_p[b];
+  float u = a.uniform[b];
+  if (!(u >= 0.f)) u = 0.f;  // negative or NaN draws count as 0
+  const bool greedy = !(T > 0.f) || p <= 0.f || k == 1;
+  const bool fast = !greedy && k > 1 && k <= kFastTopK;
+
+  // --- this workgroup's chunk of the row into LDS (n is a multiple of 4)
+  float* const xs = reinterpret_cast<float*>(dyn);
+  const int c0 = g * a.C, n = max(0, min(a.C, V - c0));
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V + c0);
+  for (int j = tid; j < n / 4; j += kSampleThreads) reinterpret_cast<f32x4*>(xs)[j] = src[j];
+  __syncthreads();
+
+  // --- the chunk's max (lowest index on ties)
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = tid; i < n; i += kSampleThreads) amax_merge(bv, bi, xs[i], c0 + i);
+  wave_amax(bv, bi);
+  if (lane == 0) { sm.wv[wave] = bv; sm.wi[wave] = bi; }
+  __syncthreads();
+  for (int w = 0; w < kSampleWaves; ++w) amax_merge(bv, bi, sm.wv[w], sm.wi[w]);
+  const size_t slot = (size_t)b * G + g;
+  if (tid == 0) { st_agent(a.part_max + slot, bv); st_agent(a.part_idx + slot, bi); }
+
+  // --- the chunk's 64 first tokens in rank order: every wave sorts batches
+  // of 64 of its share and keeps the best 64, then wave 0 merges the waves
+  if (fast) {
+    const int per = (n + kSampleWaves - 1) / kSampleWaves;
+    const int w_lo = min(n, wave * per), w_hi = min(n, w_lo + per);
+    u64 best = 0ull;
+    for (int s0 = w_lo; s0 < w_hi; s0 += 64) {
+      const int i = s0 + lane;
+      best = merge64(best, sort64(i < w_hi ? token_value(xs[i], c0 + i) : 0ull));
+    }
+    lists[wave][lane] = best;
+    __syncthreads();
+    if (wave == 0) {
+      u64 acc = lists[0][lane];
+      for (int w = 1; w < kSampleWaves; ++w) acc = merge64(acc, lists[w][lane]);
+      __hip_atomic_store(a.cand + slot * 64 + lane, acc, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // --- the last workgroup of the row to arrive finishes it
+  unsigned* const cnt = a.counters + (size_t)b * kCntStride;
+  if (!arrive_last(cnt, (unsigned)G, &s_flag)) return;
+  if (tid == 0) reset_counter(cnt);
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  for (int w = tid; w < G; w += kSampleThreads)
+    amax_merge(bv, bi, ld_agent(a.part_max + (size_t)b * G + w), ld_agent(a.part_idx + (size_t)b * G + w));
+  wave_amax(bv, bi);
+  __syncthreads();
+  if (lane == 0) { sm.wv[wave] = bv; sm.wi[wave] = bi; }
+  __syncthreads();
+  for (int w = 0; w < kSampleWaves; ++w) amax_merge(bv, bi, sm.wv[w], sm.wi[w]);
+  if (tid == 0) a.out[b] = bi;  // greedy, and the fallback of the draws below
+  if (greedy) return;
+  if (!fast) {
+    sample_row(a, b, bv, T, k, p, u, sm);
+    return;
+  }
+
+  // Fast path: the chunks' lists into LDS (all loads in flight at once; the
+  // chunk is no longer needed: G * 512 bytes <= 4 * C), then wave 0 merges
+  // them into the row's 64 first tokens in rank order, lane r holding rank
+  // r, and takes the weights of the first k, the top-p cut in rank order
+  // and the draw in id order.
+  const u64* lst = a.cand + (size_t)b * G * 64;
+  u64* const cl = reinterpret_cast<u64*>(dyn);
+  __syncthreads();  // every thread is done with the chunk
+  for (int i = tid; i < G * 64; i += kSampleThreads)
+    cl[i] = __hip_atomic_load(lst + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (wave != 0) return;
+  u64 c = cl[lane];
+  for (int w = 1; w < G; ++w) c = merge64(c, cl[w * 64 + lane]);
+  const bool in = lane < k && c != 0ull;
+  const int id = (int)(0xffffffffu - (unsigned)c);
+  const float l = key_value((unsigned)(c >> 32));
+  const double w = in ? floor((double)expf((l - bv) / T) * 4294967296.0) : 0.0;
+  double incl = w;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const double Q = __shfl(incl, 63);
+  int nkeep = k;
+  if (p < 1.f) {
+    const double target = ceil((double)p * Q);
+    const unsigned long long hit = __ballot(in && incl >= target);
+    if (hit) nkeep = __ffsll((long long)hit);
+  }
+  const double wk = lane < nkeep ? w : 0.0;
+  double R = wk;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) R += __shfl_xor(R, m);
+  const double t = fmin(floor((double)u * R), R - 1.0);
+  double before = 0.0;
+  for (int j = 0; j < 64; ++j) {
+    const int idj = __shfl(id, j);
+    const double wj = __shfl(wk, j);
+    if (idj < id) before += wj;
+  }
+  if (wk > 0.0 && before <= t && t < before + wk) a.out[b] = id;
+}
+
+void sample_split(int V, int* G, int* C) {
+  int g = (V + kSampleChunk - 1) / kSampleChunk;
+  if (g < 1) g = 1;
+  *G = g;
+  *C = ((V + g - 1) / g + 3) / 4 * 4;
+}
+
+hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s) {
+  const size_t lds = (size_t)a.C * 4;
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_kernel, dim3(B * a.G), dim3(kSampleThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qd

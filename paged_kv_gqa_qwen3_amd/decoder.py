@@ -73,6 +73,11 @@ class Decoder:
         binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,
                                     tables, pool, next_ids, logits, taps, layer)
 
+    def sample(self, logits, temperature, top_k, top_p, uniform, out_ids) -> None:
+        """Sample each sequence's next token on the device (qd_sample)."""
+        binding.qd_sample(self.handle, int(logits.shape[0]), logits, temperature, top_k, top_p,
+                          uniform, out_ids)
+
     def step_path(self, batch: int) -> str:
         """'stream', 'graph' or 'staged': how a step of `batch` runs."""
         return binding.qd_step_path(self.handle, batch)

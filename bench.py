@@ -239,6 +239,37 @@ def per_stage_roofline(torch, dec, run, shape, w, batch):
     }
 
 
+SAMPLING_SETTINGS = (("greedy", 0.0, 0, 1.0), ("T0.6_top_k20_top_p0.95", 0.6, 20, 0.95),
+                     ("T1_no_limit", 1.0, 0, 1.0))
+
+
+def time_sampling(torch, dec, B, V, reps=50):
+    """Microseconds per qd_sample call on seeded N(0, 2) logits [B][V] for a few
+    settings (HIP events on the library's stream, which is torch's current
+    stream here)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    lg = torch.randn(B, V, device="cuda", generator=g) * 2.0
+    u = torch.rand(B, device="cuda", generator=g)
+    out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, T, k, p in SAMPLING_SETTINGS:
+        t_ = torch.full((B,), T, device="cuda")
+        k_ = torch.full((B,), k, dtype=torch.int32, device="cuda")
+        p_ = torch.full((B,), p, device="cuda")
+        for _ in range(3):
+            dec.sample(lg, t_, k_, p_, u, out)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            dec.sample(lg, t_, k_, p_, u, out)
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = round(s.elapsed_time(e) / reps * 1e3, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +345,9 @@ def main():
             }
             log(f"[bench] {w.name}: {tok_s:.1f} tok/s, {ms / args.steps:.4f} ms/step, "
                 f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+            # on-device sampling of the next token (not part of the step)
+            results[w.name]["sampling_us_per_call"] = time_sampling(torch, dec, w.batch, shape.vocab)
+            log(f"[bench] {w.name}: qd_sample us per call {results[w.name]['sampling_us_per_call']}")
             if w.name == HEADLINE:
                 if path == "stream":
                     headline_extra = stream_roofline(w, ms, args.steps, nbytes)

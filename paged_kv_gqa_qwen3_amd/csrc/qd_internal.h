@@ -206,6 +206,7 @@ constexpr int kMaxSplitsStaged = 512;
 // 64 candidates, anything else runs over the whole row in one workgroup.
 constexpr int kFastTopK = 64;
 constexpr int kSampleChunk = 8192;  // most logits per workgroup
+constexpr int kMaxSampleChunks = 64;  // most workgroups per row (vocab <= 524288)
 struct SampleArgs {
   const float* logits;       // [B][V]
   int V;
@@ -219,6 +220,8 @@ struct SampleArgs {
   int* part_idx;
   unsigned long long* cand;  // [B][G][64] each chunk's first 64 tokens in rank order
   unsigned* counters;        // [B] at stride kCntStride, zero between calls
+  double* part_sum;          // [B][G] chunk weight sums (rows without limits)
+  unsigned* counters2;       // [B] at stride kCntStride, for the second launch
 };
 void sample_split(int V, int* G, int* C);
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s);

@@ -86,6 +86,8 @@ struct qd_handle {
   int* sample_idx = nullptr;
   unsigned long long* sample_cand = nullptr;
   unsigned* sample_cnt = nullptr;
+  double* sample_sum = nullptr;
+  unsigned* sample_cnt2 = nullptr;
   int* dev_flags = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   int max_pos = 0;
@@ -695,7 +697,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if ((rc = dev_alloc(h, &h->dev_flags, 1))) return bail(rc);
   if ((rc = dev_alloc(h, &h->prof_ids, (size_t)Bm))) return bail(rc);
   sample_split(V, &h->sample_G, &h->sample_C);
-  if ((size_t)h->sample_G * 512 > (size_t)h->sample_C * 4)  // the merge reuses the chunk's LDS
+  if (h->sample_G > kMaxSampleChunks ||
+      (size_t)h->sample_G * 512 > (size_t)h->sample_C * 4)  // the merge reuses the chunk's LDS
   {
     fail(h, QD_EUNSUPPORTED, "vocab too large for on-device sampling (at most 524288)");
     return bail(QD_EUNSUPPORTED);
@@ -706,7 +709,10 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     if ((rc = dev_alloc(h, &h->sample_idx, slots))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_cand, slots * 64))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_cnt, (size_t)Bm * kCntStride))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_sum, slots))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_cnt2, (size_t)Bm * kCntStride))) return bail(rc);
     e = hipMemset(h->sample_cnt, 0, sizeof(unsigned) * Bm * kCntStride);
+    if (e == hipSuccess) e = hipMemset(h->sample_cnt2, 0, sizeof(unsigned) * Bm * kCntStride);
     if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
   }
   e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg * kCntStride);
@@ -969,7 +975,7 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
     return fail(h, QD_EINVAL, "logits must be 16-byte aligned");
   SampleArgs a{logits, h->V, temperature, top_k, top_p, uniform, out_ids,
                h->sample_G, h->sample_C, h->sample_max, h->sample_idx,
-               h->sample_cand, h->sample_cnt};
+               h->sample_cand, h->sample_cnt, h->sample_sum, h->sample_cnt2};
   HIP_TRY(h, launch_sample(a, batch, h->stream));
   return QD_OK;
 }

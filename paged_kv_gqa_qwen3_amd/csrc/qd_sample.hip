@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   if (!(u >= 0.f)) u = 0.f;  // negative or NaN draws count as 0
   const bool greedy = !(T > 0.f) || p <= 0.f || k == 1;
   const bool fast = !greedy && k > 1 && k <= kFastTopK;
+  const bool plain = !greedy && (k <= 0 || k >= V) && !(p < 1.f);  // sample_sum_kernel
 
   // --- this workgroup's chunk of the row into LDS (n is a multiple of 4)
   float* const xs = reinterpret_cast<float*>(dyn);
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   for (int w = 0; w < kSampleWaves; ++w) amax_merge(bv, bi, sm.wv[w], sm.wi[w]);
   if (tid == 0) a.out[b] = bi;  // greedy, and the fallback of the draws below
   if (greedy) return;
+  if (plain) return;  // the draw is taken by the second launch
   if (!fast) {
     sample_row(a, b, bv, T, k, p, u, sm);
     return;
@@ -459,6 +461,105 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   if (wk > 0.0 && before <= t && t < before + wk) a.out[b] = id;
 }
 
+// Second launch, for rows with no top-k or top-p limit: every chunk's
+// weight sum against the row's max (from the first launch's chunk maxima),
+// then, in the last workgroup of the row to arrive, the chunk holding the
+// draw target and the walk through it in id order.
+constexpr int kSumThreads = 256;
+
+__global__ __launch_bounds__(kSumThreads) void sample_sum_kernel(SampleArgs a) {
+  __shared__ double wsum[kSumThreads / 64];
+  __shared__ double s_run[kSumThreads / 64];
+  __shared__ unsigned s_flag;
+  __shared__ double s_sums[kMaxSampleChunks];
+  __shared__ int s_chunk;
+  __shared__ double s_t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
+  const int V = a.V;
+  const float T = a.temperature[b];
+  const int k = a.top_k[b];
+  const float p = a.top_p[b];
+  if (!(T > 0.f) || p <= 0.f || k == 1 || !((k <= 0 || k >= V) && !(p < 1.f))) return;
+  float u = a.uniform[b];
+  if (!(u >= 0.f)) u = 0.f;
+
+  // the row's max: the chunk maxima, written by the first launch
+  float M = -INFINITY;
+  for (int w = 0; w < G; ++w) M = fmaxf(M, a.part_max[(size_t)b * G + w]);
+  auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
+  auto block_total = [&](double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    __syncthreads();
+    if (lane == 0) wsum[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSumThreads / 64; ++w) t += wsum[w];
+    return t;
+  };
+
+  const int c0 = g * a.C, n = max(0, min(a.C, V - c0));
+  const float* row = a.logits + (size_t)b * V;
+  const f32x4* src = reinterpret_cast<const f32x4*>(row + c0);
+  double mine = 0.0;
+  for (int j = tid; j < n / 4; j += kSumThreads) {
+    const f32x4 v = src[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mine += weight(v[e]);
+  }
+  const double S = block_total(mine);
+  const size_t slot = (size_t)b * G + g;
+  if (tid == 0) __hip_atomic_store(a.part_sum + slot, S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  unsigned* const cnt = a.counters2 + (size_t)b * kCntStride;
+  if (!arrive_last(cnt, (unsigned)G, &s_flag)) return;
+  for (int w = tid; w < G; w += kSumThreads)  // every chunk sum in one round trip
+    s_sums[w] = __hip_atomic_load(a.part_sum + (size_t)b * G + w, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid == 0) {
+    reset_counter(cnt);
+    double R = 0.0;
+    for (int w = 0; w < G; ++w) R += s_sums[w];
+    const double t = fmin(floor((double)u * R), R - 1.0);
+    double run = 0.0;
+    int gc = G - 1;
+    for (int w = 0; w < G; ++w) {
+      if (t < run + s_sums[w]) { gc = w; break; }
+      run += s_sums[w];
+    }
+    s_chunk = gc;
+    s_t = t - run;  // the target inside that chunk
+  }
+  __syncthreads();
+  // walk chunk s_chunk in id order: threads own consecutive runs of logits
+  const int cg = s_chunk, cc0 = cg * a.C, cn = max(0, min(a.C, V - cc0));
+  const double tt = s_t;
+  const int per = (cn + kSumThreads - 1) / kSumThreads;
+  const int lo = min(cn, tid * per), hi = min(cn, lo + per);
+  double own = 0.0;
+  for (int i = lo; i < hi; ++i) own += weight(row[cc0 + i]);
+  double inc = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) s_run[wave] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += s_run[w];
+  double run = base + inc - own;
+  if (run <= tt && tt < run + own) {
+    for (int i = lo; i < hi; ++i) {
+      run += weight(row[cc0 + i]);
+      if (tt < run) { a.out[b] = cc0 + i; break; }
+    }
+  }
+}
+
 void sample_split(int V, int* G, int* C) {
   int g = (V + kSampleChunk - 1) / kSampleChunk;
   if (g < 1) g = 1;
@@ -470,6 +571,9 @@ hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s) {
   const size_t lds = (size_t)a.C * 4;
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sample_kernel, dim3(B * a.G), dim3(kSampleThreads), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sample_sum_kernel, dim3(B * a.G), dim3(kSumThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -297,6 +297,7 @@ __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, 
 // for a larger logit, then a lower id (the rank order); 0 is "no token".
 typedef unsigned long long u64;
 static_assert(kFastTopK <= 64, "the fast path keeps 64 candidates per chunk");
+constexpr int kSurvivors = 1024;  // tokens of a chunk the fast path gathers past its bound
 
 __device__ __forceinline__ u64 shfl64(u64 v, int src) {
   const unsigned lo = __shfl((unsigned)v, src), hi = __shfl((unsigned)(v >> 32), src);
@@ -336,6 +337,18 @@ __device__ __forceinline__ u64 merge64(u64 a, u64 b) {
   return x;
 }
 
+// Merge cnt sorted lists of 64 (list j at L + 64 * j, in LDS) into the
+// first, pairwise in rounds, the waves of the workgroup taking the pairs of
+// a round in parallel.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void merge_lists(u64* L, int cnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int step = 1; step < cnt; step <<= 1) {
+    for (int j = wave * 2 * step; j + step < cnt; j += kSampleWaves * 2 * step)
+      L[64 * j + lane] = merge64(L[64 * j + lane], L[64 * (j + step) + lane]);
+    __syncthreads();
+  }
+}
+
 __device__ __forceinline__ u64 token_value(float l, int id) {
   return ((u64)sample_key(l) << 32) | (0xffffffffu - (unsigned)id);
 }
@@ -344,6 +357,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SampleSmem sm;
   __shared__ u64 lists[kSampleWaves][64];
+  __shared__ u64 surv[kSurvivors];
+  __shared__ u64 s_bound;
+  __shared__ unsigned s_nsurv;
   __shared__ unsigned s_flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
@@ -375,24 +391,65 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   const size_t slot = (size_t)b * G + g;
   if (tid == 0) { st_agent(a.part_max + slot, bv); st_agent(a.part_idx + slot, bi); }
 
-  // --- the chunk's 64 first tokens in rank order: every wave sorts batches
-  // of 64 of its share and keeps the best 64, then wave 0 merges the waves
+  // --- the chunk's 64 first tokens in rank order.  A bound first: thread
+  // t's tokens are t, t + 1024, ...; the tokens of one lane index across the
+  // waves form 64 disjoint groups, and the least of the 64 group maxima is
+  // at most the chunk's 64th largest, so only tokens at or above it can be
+  // among the first 64.  Those (a few hundred in practice) are gathered and
+  // every wave sorts batches of 64 of them across its lanes, keeping the
+  // best 64; the waves' lists are then merged.  If more than kSurvivors pass
+  // the bound, every token of the chunk goes through the sorts instead.
   if (fast) {
-    const int per = (n + kSampleWaves - 1) / kSampleWaves;
-    const int w_lo = min(n, wave * per), w_hi = min(n, w_lo + per);
-    u64 best = 0ull;
-    for (int s0 = w_lo; s0 < w_hi; s0 += 64) {
-      const int i = s0 + lane;
-      best = merge64(best, sort64(i < w_hi ? token_value(xs[i], c0 + i) : 0ull));
+    u64 gm = 0ull;
+    for (int i = tid; i < n; i += kSampleThreads) {
+      const u64 v = token_value(xs[i], c0 + i);
+      gm = v > gm ? v : gm;
     }
-    lists[wave][lane] = best;
+    lists[wave][lane] = gm;
+    if (tid == 0) s_nsurv = 0u;
     __syncthreads();
     if (wave == 0) {
-      u64 acc = lists[0][lane];
-      for (int w = 1; w < kSampleWaves; ++w) acc = merge64(acc, lists[w][lane]);
-      __hip_atomic_store(a.cand + slot * 64 + lane, acc, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int w = 1; w < kSampleWaves; ++w) gm = lists[w][lane] > gm ? lists[w][lane] : gm;
+      u64 lo = gm;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const u64 o = shfl_xor64(lo, m);
+        lo = o < lo ? o : lo;
+      }
+      if (lane == 0) s_bound = lo;
     }
+    __syncthreads();
+    const u64 bound = s_bound;
+    for (int i = tid; i < n; i += kSampleThreads) {
+      const u64 v = token_value(xs[i], c0 + i);
+      if (v >= bound) {
+        const unsigned at = atomicAdd(&s_nsurv, 1u);
+        if (at < (unsigned)kSurvivors) surv[at] = v;
+      }
+    }
+    __syncthreads();
+    const int ns = (int)s_nsurv;
+    u64 best = 0ull;
+    if (ns <= kSurvivors) {
+      for (int s0 = wave * 64; s0 < ns; s0 += kSampleWaves * 64) {
+        const int i = s0 + lane;
+        best = merge64(best, sort64(i < ns ? surv[i] : 0ull));
+      }
+    } else {
+      const int per = (n + kSampleWaves - 1) / kSampleWaves;
+      const int w_lo = min(n, wave * per), w_hi = min(n, w_lo + per);
+      for (int s0 = w_lo; s0 < w_hi; s0 += 64) {
+        const int i = s0 + lane;
+        best = merge64(best, sort64(i < w_hi ? token_value(xs[i], c0 + i) : 0ull));
+      }
+    }
+    __syncthreads();  // every wave is done with the group maxima in lists
+    lists[wave][lane] = best;
+    __syncthreads();
+    merge_lists(&lists[0][0], kSampleWaves);
+    if (wave == 0)
+      __hip_atomic_store(a.cand + slot * 64 + lane, lists[0][lane], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // --- the last workgroup of the row to arrive finishes it
@@ -417,19 +474,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   }
 
   // Fast path: the chunks' lists into LDS (all loads in flight at once; the
-  // chunk is no longer needed: G * 512 bytes <= 4 * C), then wave 0 merges
-  // them into the row's 64 first tokens in rank order, lane r holding rank
-  // r, and takes the weights of the first k, the top-p cut in rank order
-  // and the draw in id order.
+  // chunk is no longer needed: G * 512 bytes <= 4 * C), merged pairwise by
+  // all waves into the row's 64 first tokens in rank order; then wave 0,
+  // lane r holding rank r, takes the weights of the first k, the top-p cut
+  // in rank order and the draw in id order.
   const u64* lst = a.cand + (size_t)b * G * 64;
   u64* const cl = reinterpret_cast<u64*>(dyn);
   __syncthreads();  // every thread is done with the chunk
   for (int i = tid; i < G * 64; i += kSampleThreads)
     cl[i] = __hip_atomic_load(lst + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  merge_lists(cl, G);
   if (wave != 0) return;
-  u64 c = cl[lane];
-  for (int w = 1; w < G; ++w) c = merge64(c, cl[w * 64 + lane]);
+  const u64 c = cl[lane];
   const bool in = lane < k && c != 0ull;
   const int id = (int)(0xffffffffu - (unsigned)c);
   const float l = key_value((unsigned)(c >> 32));

@@ -240,7 +240,7 @@ def per_stage_roofline(torch, dec, run, shape, w, batch):
 
 
 SAMPLING_SETTINGS = (("greedy", 0.0, 0, 1.0), ("T0.6_top_k20_top_p0.95", 0.6, 20, 0.95),
-                     ("T1_no_limit", 1.0, 0, 1.0))
+                     ("T1_no_limit", 1.0, 0, 1.0), ("T0.3_top_p0.9", 0.3, 0, 0.9))
 
 
 def time_sampling(torch, dec, B, V, reps=50):

@@ -371,7 +371,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   if (!(u >= 0.f)) u = 0.f;  // negative or NaN draws count as 0
   const bool greedy = !(T > 0.f) || p <= 0.f || k == 1;
   const bool fast = !greedy && k > 1 && k <= kFastTopK;
-  const bool plain = !greedy && (k <= 0 || k >= V) && !(p < 1.f);  // sample_sum_kernel
+  // rows the second launch finishes: no limit, or top-p alone
+  const bool plain = !greedy && (k <= 0 || k >= V) && !(p < 1.f);
+  const bool topp = !greedy && (k <= 0 || k >= V) && p < 1.f;
 
   // --- this workgroup's chunk of the row into LDS (n is a multiple of 4)
   float* const xs = reinterpret_cast<float*>(dyn);
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   // every wave sorts batches of 64 of them across its lanes, keeping the
   // best 64; the waves' lists are then merged.  If more than kSurvivors pass
   // the bound, every token of the chunk goes through the sorts instead.
-  if (fast) {
+  if (fast || topp) {
     u64 gm = 0ull;
     for (int i = tid; i < n; i += kSampleThreads) {
       const u64 v = token_value(xs[i], c0 + i);
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   for (int w = 0; w < kSampleWaves; ++w) amax_merge(bv, bi, sm.wv[w], sm.wi[w]);
   if (tid == 0) a.out[b] = bi;  // greedy, and the fallback of the draws below
   if (greedy) return;
-  if (plain) return;  // the draw is taken by the second launch
+  if (plain || topp) return;  // finished by the second launch
   if (!fast) {
     sample_row(a, b, bv, T, k, p, u, sm);
     return;
@@ -518,26 +520,31 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   if (wk > 0.0 && before <= t && t < before + wk) a.out[b] = id;
 }
 
-// Second launch, for rows with no top-k or top-p limit: every chunk's
-// weight sum against the row's max (from the first launch's chunk maxima),
-// then, in the last workgroup of the row to arrive, the chunk holding the
-// draw target and the walk through it in id order.
-constexpr int kSumThreads = 256;
-
-__global__ __launch_bounds__(kSumThreads) void sample_sum_kernel(SampleArgs a) {
-  __shared__ double wsum[kSumThreads / 64];
-  __shared__ double s_run[kSumThreads / 64];
+// Second launch, for rows with no top-k limit and either no top-p limit or
+// top-p alone: every chunk's weight sum against the row's max (from the
+// first launch's chunk maxima); then, in the last workgroup of the row to
+// arrive, with no limit, the chunk holding the draw target and the walk
+// through it in id order; with top-p, the total weight gives the target,
+// and if the row's first 64 tokens (merged from the first launch's chunk
+// lists) reach it, the cut and the draw are taken over them in one wave,
+// else over the whole row (sample_row).
+__global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ SampleSmem sm;
+  __shared__ double s_run[kSampleWaves];
   __shared__ unsigned s_flag;
   __shared__ double s_sums[kMaxSampleChunks];
   __shared__ int s_chunk;
   __shared__ double s_t;
+  __shared__ int s_whole;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
   const int V = a.V;
   const float T = a.temperature[b];
   const int k = a.top_k[b];
   const float p = a.top_p[b];
-  if (!(T > 0.f) || p <= 0.f || k == 1 || !((k <= 0 || k >= V) && !(p < 1.f))) return;
+  if (!(T > 0.f) || p <= 0.f || k == 1 || !(k <= 0 || k >= V)) return;
+  const bool topp = p < 1.f;
   float u = a.uniform[b];
   if (!(u >= 0.f)) u = 0.f;
 
@@ -545,41 +552,74 @@ __global__ __launch_bounds__(kSumThreads) void sample_sum_kernel(SampleArgs a) {
   float M = -INFINITY;
   for (int w = 0; w < G; ++w) M = fmaxf(M, a.part_max[(size_t)b * G + w]);
   auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
-  auto block_total = [&](double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    __syncthreads();
-    if (lane == 0) wsum[wave] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kSumThreads / 64; ++w) t += wsum[w];
-    return t;
-  };
 
   const int c0 = g * a.C, n = max(0, min(a.C, V - c0));
   const float* row = a.logits + (size_t)b * V;
   const f32x4* src = reinterpret_cast<const f32x4*>(row + c0);
   double mine = 0.0;
-  for (int j = tid; j < n / 4; j += kSumThreads) {
+  for (int j = tid; j < n / 4; j += kSampleThreads) {
     const f32x4 v = src[j];
 #pragma unroll
     for (int e = 0; e < 4; ++e) mine += weight(v[e]);
   }
-  const double S = block_total(mine);
+  const double S = block_sum(mine, sm);
   const size_t slot = (size_t)b * G + g;
   if (tid == 0) __hip_atomic_store(a.part_sum + slot, S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   unsigned* const cnt = a.counters2 + (size_t)b * kCntStride;
   if (!arrive_last(cnt, (unsigned)G, &s_flag)) return;
-  for (int w = tid; w < G; w += kSumThreads)  // every chunk sum in one round trip
+  for (int w = tid; w < G; w += kSampleThreads)  // every chunk sum in one round trip
     s_sums[w] = __hip_atomic_load(a.part_sum + (size_t)b * G + w, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  if (tid == 0) reset_counter(cnt);
+  double R = 0.0;
+  for (int w = 0; w < G; ++w) R += s_sums[w];
+
+  if (topp) {
+    // the row's first 64 tokens in rank order from the chunk lists
+    const u64* lst = a.cand + (size_t)b * G * 64;
+    u64* const cl = reinterpret_cast<u64*>(dyn);
+    for (int i = tid; i < G * 64; i += kSampleThreads)
+      cl[i] = __hip_atomic_load(lst + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    merge_lists(cl, G);
+    if (wave == 0) {
+      const u64 c = cl[lane];
+      const bool in = c != 0ull;
+      const int id = (int)(0xffffffffu - (unsigned)c);
+      const double w = in ? weight(key_value((unsigned)(c >> 32))) : 0.0;
+      double incl = w;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const double o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      const double target = ceil((double)p * R);
+      const unsigned long long hit = __ballot(in && incl >= target);
+      if (lane == 0) s_whole = hit ? 0 : 1;
+      if (hit) {
+        const int nkeep = __ffsll((long long)hit);
+        const double wk = lane < nkeep ? w : 0.0;
+        double Rk = wk;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) Rk += __shfl_xor(Rk, m);
+        const double t = fmin(floor((double)u * Rk), Rk - 1.0);
+        double before = 0.0;
+        for (int j = 0; j < 64; ++j) {
+          const int idj = __shfl(id, j);
+          const double wj = __shfl(wk, j);
+          if (idj < id) before += wj;
+        }
+        if (wk > 0.0 && before <= t && t < before + wk) a.out[b] = id;
+      }
+    }
+    __syncthreads();
+    if (s_whole) sample_row(a, b, M, T, k, p, u, sm);
+    return;
+  }
+
   if (tid == 0) {
-    reset_counter(cnt);
-    double R = 0.0;
-    for (int w = 0; w < G; ++w) R += s_sums[w];
     const double t = fmin(floor((double)u * R), R - 1.0);
     double run = 0.0;
     int gc = G - 1;
@@ -594,7 +634,7 @@ __global__ __launch_bounds__(kSumThreads) void sample_sum_kernel(SampleArgs a) {
   // walk chunk s_chunk in id order: threads own consecutive runs of logits
   const int cg = s_chunk, cc0 = cg * a.C, cn = max(0, min(a.C, V - cc0));
   const double tt = s_t;
-  const int per = (cn + kSumThreads - 1) / kSumThreads;
+  const int per = (cn + kSampleThreads - 1) / kSampleThreads;
   const int lo = min(cn, tid * per), hi = min(cn, lo + per);
   double own = 0.0;
   for (int i = lo; i < hi; ++i) own += weight(row[cc0 + i]);
@@ -630,7 +670,8 @@ hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL(sample_kernel, dim3(B * a.G), dim3(kSampleThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_sum_kernel, dim3(B * a.G), dim3(kSumThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_sum_kernel, dim3(B * a.G), dim3(kSampleThreads),
+                     (size_t)a.G * 64 * sizeof(unsigned long long), s, a);
   return hipGetLastError();
 }
 

@@ -21,24 +21,29 @@ import csv
 import glob
 import json
 import os
+import re
 import sys
 
-# Kernel-name substrings -> class (first match wins).
+# Kernel-name substrings -> class (first match wins); GEMV launches are
+# classed by their epilogue (the second template argument, any batch width).
 CLASSES = (
     ("stream_step_kernel", "stream_step"),
-    ("gemv_kernel<1, 4>", "qkv"),
-    ("gemv_kernel<1, 2>", "gate_up"),
-    ("gemv_kernel<1, 3>", "lm_head"),
-    ("gemv_kernel<1, 1>", "o_proj+down"),
+    ("sample_sum_kernel", "sample_sum"),
+    ("sample_kernel", "sample"),
     ("attention_kernel", "attention"),
     ("embed_kernel", "embed"),
 )
+GEMV_MODES = {"4": "qkv", "2": "gate_up", "3": "lm_head", "1": "o_proj+down", "0": "gemv_store"}
+_GEMV = re.compile(r"gemv_kernel<(\d+), (\d+)>")
 
 
 def kernel_class(name: str):
     for key, cls in CLASSES:
         if key in name:
             return cls
+    m = _GEMV.search(name)
+    if m:
+        return GEMV_MODES.get(m.group(2))
     return None
 
 

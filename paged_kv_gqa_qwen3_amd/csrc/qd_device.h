@@ -1,6 +1,6 @@
 // Device-side building blocks of the decode step (included by the kernel
 // translation units): helpers, the work-item functions and the wait used by
-// the persistent step kernel.
+// the batch-1 streaming step kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -127,7 +127,7 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected
   return *s_flag != 0;
 }
 
-// Completion of a stage of the persistent step kernel.  Every finished unit
+// Completion of a stage of the streaming step kernel.  Every finished unit
 // of the stage (item, row group, head or sequence) adds 1 to `counter` once
 // its stores are performed; the workgroup whose increment completes the
 // stage raises every workgroup's flag to `phase` (an atomic maximum, so a
@@ -320,7 +320,7 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 // per 1 KB tile and CH tiles in flight: the first CH go out before the item
 // waits for its input, and each later one as soon as the registers it lands
 // in are free.
-//   NB <= 4 : VALU path, fp32 FMA; the K slice of the input (times the
+//   NB = 1  : VALU path, fp32 FMA; the K slice of the input (times the
 //             RMSNorm gain) is staged in LDS.
 //   NB >= 8 : MFMA path, v_mfma_f32_16x16x32_bf16 with the weight tile as
 //             operand A and the input as a pair of bf16 (hi = bf16(x), lo =
@@ -1207,7 +1207,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   mark(7);
 }
 
-// ------------------------------------------------------------------ persistent step
+// ------------------------------------------------------------------ streaming step
 
 // Waits (thread 0 polls, the workgroup then proceeds together) until this
 // workgroup's flag reaches `phase` (see signal_done).  Bounded: after

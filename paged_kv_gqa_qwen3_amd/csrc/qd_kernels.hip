@@ -139,8 +139,6 @@ template <int MODE>
 static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
   switch (gemv_nb(a.B)) {
     case 1: return launch_gemv_t<1, MODE>(a, s);
-    case 2: return launch_gemv_t<2, MODE>(a, s);
-    case 4: return launch_gemv_t<4, MODE>(a, s);
     case 8: return launch_gemv_t<8, MODE>(a, s);
     case 16: return launch_gemv_t<16, MODE>(a, s);
     case 32: return launch_gemv_t<32, MODE>(a, s);

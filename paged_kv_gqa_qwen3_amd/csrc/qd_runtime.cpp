@@ -66,7 +66,7 @@ struct qd_handle {
   std::map<std::string, int> expected;  // name -> loaded (0/1)
 
   float *x = nullptr, *ssq = nullptr, *qkv = nullptr, *attn = nullptr, *act = nullptr;
-  // bf16 pairs [64][cols] for MFMA consumers (batch >= 5)
+  // bf16 pairs [64][cols] for MFMA consumers (batch >= 2)
   uint16_t *xg_hi = nullptr, *xg_lo = nullptr, *attn_hi = nullptr, *attn_lo = nullptr;
   uint16_t *act_hi = nullptr, *act_lo = nullptr;
   float* part = nullptr;      // split partials of self-reducing projections (O, down, LM head)
@@ -95,7 +95,7 @@ struct qd_handle {
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::map<GraphKey, hipGraph_t> graph_defs;
 
-  // persistent step
+  // batch-1 streaming step (persistent handles)
   bool persistent = false;
   bool long_ctx = false;  // max_pages_per_seq > kStreamMaxPages: batch 1 takes the per-stage kernels
   LayerDev* layers_dev = nullptr;
@@ -145,16 +145,15 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
 
 // Split plan for an N x K projection at batch B.
 //
-// Batch <= 4 (VALU items, graph path): one 16-row tile per workgroup, its 4
-// waves splitting K, and K itself split only where the input slice would not
-// fit an 80 KB LDS budget or the row tiles alone give fewer than 128
-// workgroups: the projections of a 4B-class model then need no split-K
-// hand-off at batch 1.  The LM head keeps 64-row items (its argmax reduces
-// one partial per row group).
-// Batch >= 5 (MFMA items) and the persistent step: 64-row items, enough
-// workgroups to cover the chip twice (the persistent step: its grid), at
-// most 20 tiles per wave unless the row count alone fills the chip, and an
-// LDS input slice <= 48 KB so that three workgroups fit a CU.
+// Batch 1 (VALU items): one 16-row tile per workgroup, its 4 waves splitting
+// K, and K itself split only where the input slice would not fit an 80 KB
+// LDS budget or the row tiles alone give fewer than 128 workgroups: the
+// projections of a 4B-class model then need no split-K hand-off at batch 1.
+// The LM head keeps 64-row items (its argmax reduces one partial per row
+// group).
+// Batch >= 2 (MFMA items): 64-row items, the fewest K splits that give every
+// CU an item, slices of at most 16 k-tiles while the row groups alone do
+// not, and an LDS input slice <= 48 KB so that three workgroups fit a CU.
 constexpr size_t kLdsCapValu = 80 * 1024;
 constexpr size_t kLdsCapStaged = 48 * 1024;
 constexpr int kMinValuItems = 128;
@@ -278,7 +277,7 @@ int prof_mark(qd_handle* h, Prof* pr, int cls, hipStream_t s) {
 // Launch the projection of class cls (QD_PROF_QKV, _O, _GATE_UP, _DOWN or
 // _LM_HEAD) of layer l at batch B on stream s, as the step does.  QKV leaves
 // split partials for attention when part_mode (else it stores q|k|v).
-// MFMA consumers (batch >= 5) read the bf16 pairs their producer wrote once:
+// MFMA consumers (batch >= 2) read the bf16 pairs their producer wrote once:
 // x times the next RMSNorm gain (xg), the attention output, act.
 hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode, float* logits,
                              int32_t* next, hipStream_t s) {

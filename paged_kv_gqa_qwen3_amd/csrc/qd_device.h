@@ -373,6 +373,34 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
                     ((size_t)(rg * RT + tj) * KT + kw0) * 64 + lane;
   const size_t wstep = (size_t)WS * 64;
 
+  // MFMA path: the input slice (written by an earlier launch) is loaded
+  // first, up to kStageLoads 16-byte pieces per thread in flight together,
+  // so that staging does not wait behind the weight tiles (loads complete
+  // in order) one piece at a time; further pieces are copied after them.
+  // (12 pieces cost a third workgroup per CU in registers: batch 8 and 16
+  // took 3.50 and 4.22 ms per step; 8 pieces 3.16 and 3.88; 6 pieces 3.15
+  // and 3.94; the one-piece loop 3.19 and 3.94.)
+  constexpr int kStageLoads = 8;
+  const int K8 = Ks / 8, n_in = kMfma ? B * K8 : 0;
+  u32x4 inb[kMfma ? kStageLoads : 1];
+  auto in_src = [&](int idx) {
+    const int hl = idx >= n_in, rem = idx - hl * n_in;
+    const int b = rem / K8, c = (rem - b * K8) * 8;
+    return (hl ? a.xl : a.xh) + (size_t)b * a.K + kt0 * kTileCols + c;
+  };
+  auto in_dst = [&](int idx) {
+    const int hl = idx >= n_in, rem = idx - hl * n_in;
+    const int b = rem / K8, c = (rem - b * K8) * 8;
+    return hl * NB * (Ks + 8) + b * (Ks + 8) + c;
+  };
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int idx = tid + j * 256;
+      if (idx < 2 * n_in) inb[j] = *reinterpret_cast<const u32x4*>(in_src(idx));
+    }
+  }
+
   // Every load is issued unconditionally (tile index clamped to the wave's
   // range) so that the loads stay in flight together; only compute is guarded.
   u32x4 wbuf[CH];
@@ -402,20 +430,18 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // Stage the input slice, 8 consecutive columns per thread and step.
   const int P = kMfma ? Ks + 8 : Ks;
   if constexpr (kMfma) {
-    // copy the pairs of the B live columns, hi rows first, then lo rows
-    // (LDS columns B..NB-1 keep whatever they held: they only feed outputs
-    // that are never stored)
-    const int K8 = Ks / 8, n = B * K8;
+    // the pairs of the B live columns, hi rows first, then lo rows (LDS
+    // columns B..NB-1 keep whatever they held: they only feed outputs that
+    // are never stored)
     unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
-    for (int idx = tid; idx < 2 * n; idx += 256) {
-      const int hl = idx >= n, rem = idx - hl * n;
-      const int b = rem / K8, c = (rem - b * K8) * 8;
-      const uint16_t* src = (hl ? a.xl : a.xh) + (size_t)b * a.K + kt0 * kTileCols + c;
-      *reinterpret_cast<u32x4*>(xs + hl * NB * P + b * P + c) =
-          *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int idx = tid + j * 256;
+      if (idx < 2 * n_in) *reinterpret_cast<u32x4*>(xs + in_dst(idx)) = inb[j];
     }
+    for (int idx = tid + kStageLoads * 256; idx < 2 * n_in; idx += 256)
+      *reinterpret_cast<u32x4*>(xs + in_dst(idx)) = *reinterpret_cast<const u32x4*>(in_src(idx));
   } else {
-    const int K8 = Ks / 8;
     const float* grow = gain + kt0 * kTileCols;
     for (int idx = tid; idx < B * K8; idx += 256) {
       const int b = idx / K8, c = (idx - b * K8) * 8;

@@ -408,6 +408,42 @@ def test_stream_step_matches_staged(torch, ctx):
     dp.close()
 
 
+def test_profiling_entry_points(torch):
+    """qd_profile_step runs the same step as qd_decode_step (same logits,
+    ids and pool bits, for the graph handle's per-stage plan) and reports a
+    positive time for every class it launched; qd_profile_class times one
+    projection class alone and leaves the next step's results unchanged."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 55)
+    batch = synth.make_paged_batch(shape, [5, 40, 77], 2, 56)
+    B = 3
+    dp = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False)
+    dp.load_numpy_weights(W)
+    pa, pb = pool_to_device(batch.pool), pool_to_device(batch.pool)
+    ia = StepIO(torch, B, batch.max_pages, shape.vocab)
+    ib = StepIO(torch, B, batch.max_pages, shape.vocab)
+    for io in (ia, ib):
+        io.set(batch.tokens, batch.positions, batch.block_tables)
+    ia.run(dp, pa)
+    prof = binding.qd_profile_step(dp.handle, B, ib.tok, ib.pos, ib.tab, pb, ib.nxt, ib.logits)
+    torch.cuda.synchronize()
+    assert torch.equal(ia.logits, ib.logits) and torch.equal(ia.nxt, ib.nxt)
+    assert torch.equal(pa, pb)
+    for cls, (ms, n) in prof.items():
+        assert n >= 1 and ms > 0.0, (cls, ms, n)
+    for cls in ("qkv", "o_proj", "gate_up", "down", "lm_head"):
+        us = binding.qd_profile_class(dp.handle, B, cls, reps=3)
+        assert us > 0.0, cls
+    with pytest.raises(binding.QdError):
+        binding.qd_profile_class(dp.handle, B, "attention", reps=3)
+    ia.run(dp, pa)  # the classes overwrote only scratch: the next step is unchanged
+    ib.run(dp, pb)
+    torch.cuda.synchronize()
+    assert torch.equal(ia.logits, ib.logits)
+    assert dp.device_status() == 0
+    dp.close()
+
+
 def test_step_paths(torch):
     """qd_step_path: a persistent handle streams batch 1 only when sized for
     at most 128 pages per sequence and runs every larger batch as the graph;

@@ -230,6 +230,54 @@ void* qd_stream(const qd_handle* h);
  * 1..max_batch.  No GPU work. */
 int qd_step_path(const qd_handle* h, int32_t batch);
 
+/* ---- Page manager for the paged KV pool (host only, no GPU work) ----
+ * Fixed 16-token pages taken from and returned to a free pool in O(1), one
+ * page list per sequence (its block-table row for qd_decode_step), forks
+ * that share full pages, and a prefix cache: full pages registered under
+ * their token prefix are kept after their sequences end and handed to a
+ * new sequence whose tokens start the same way (the rkmt page, "从零构建
+ * Qwen3-8B 推理引擎", sections 4.3.1 paged KV cache and 4.4.4 automatic
+ * prefix cache).  A page is shared only while full; cached pages nobody
+ * references are evicted, least recently released first (a sequence's
+ * pages from its last to its first), when the free pool is empty.  Pages
+ * are ids 0..num_pages-1 of the caller's pool; the first page taken is 0.
+ * Not thread-safe.  Errors: QD_EINVAL (NULL pointer, unknown or duplicate
+ * sequence id, bad size), QD_ENOMEM (not enough pages: nothing changed),
+ * QD_EUNSUPPORTED (more than max_pages_per_seq pages). */
+typedef struct qd_blocks qd_blocks;
+
+int qd_blocks_create(int32_t num_pages, int32_t max_pages_per_seq, qd_blocks** out);
+void qd_blocks_destroy(qd_blocks* m);
+/* A new sequence with no pages. */
+int qd_blocks_add(qd_blocks* m, int64_t seq);
+/* Make the sequence's pages cover token positions [0, n_tokens) (a step
+ * at position p needs n_tokens = p + 1); never shrinks. */
+int qd_blocks_reserve(qd_blocks* m, int64_t seq, int32_t n_tokens);
+/* End the sequence: its pages return to the pool, or to the cache. */
+int qd_blocks_release(qd_blocks* m, int64_t seq);
+/* New sequence dst with src's positions: it shares src's full pages; if src
+ * has a partly filled page, dst gets a fresh page that the caller must fill
+ * by copying page *copy_src to page *copy_dst on the device (both -1 when
+ * there is none).  Returns the number of copies (0 or 1). */
+int qd_blocks_fork(qd_blocks* m, int64_t src, int64_t dst, int32_t* copy_src,
+                   int32_t* copy_dst);
+/* Block-table rows [n][max_pages_per_seq] (host int32) of the listed
+ * sequences, unused entries set to pad_page. */
+int qd_blocks_tables(const qd_blocks* m, const int64_t* seqs, int32_t n, int32_t pad_page,
+                     int32_t* out);
+/* Token positions the sequence's pages cover. */
+int qd_blocks_length(const qd_blocks* m, int64_t seq);
+/* Pages obtainable now (free plus cached and unreferenced). */
+int qd_blocks_available(const qd_blocks* m);
+/* Register the sequence's full pages for tokens[0, n) (n <= its length;
+ * the KV of those positions must be in the pages) in the prefix cache;
+ * returns the number of pages newly registered. */
+int qd_blocks_publish(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t n);
+/* For a sequence with no pages: take the cached full pages whose prefix
+ * matches tokens[0, n), longest first; returns the positions they cover
+ * (a multiple of 16), which need no prefill. */
+int qd_blocks_match(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t n);
+
 /* Free everything the handle owns (waits for its stream first). */
 void qd_destroy(qd_handle* h);
 

@@ -12,6 +12,8 @@ import ctypes
 import os
 from typing import Dict, Optional
 
+import numpy as np
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqd.so")
 
@@ -29,7 +31,10 @@ QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
-            "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error")
+            "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
+            "qd_blocks_create", "qd_blocks_destroy", "qd_blocks_add", "qd_blocks_reserve",
+            "qd_blocks_release", "qd_blocks_fork", "qd_blocks_tables", "qd_blocks_length",
+            "qd_blocks_available", "qd_blocks_publish", "qd_blocks_match")
 
 PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
 
@@ -91,6 +96,18 @@ def load_library():
         lib.qd_profile_class.restype = ctypes.c_int
         lib.qd_profile_class.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_float)]
+        I32, I64 = ctypes.c_int32, ctypes.c_int64
+        for name, args in (("qd_blocks_create", [I32, I32, ctypes.POINTER(P)]),
+                           ("qd_blocks_add", [P, I64]), ("qd_blocks_reserve", [P, I64, I32]),
+                           ("qd_blocks_release", [P, I64]), ("qd_blocks_fork", [P, I64, I64, P, P]),
+                           ("qd_blocks_tables", [P, P, I32, I32, P]),
+                           ("qd_blocks_length", [P, I64]), ("qd_blocks_available", [P]),
+                           ("qd_blocks_publish", [P, I64, P, I32]),
+                           ("qd_blocks_match", [P, I64, P, I32])):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = args
+        lib.qd_blocks_destroy.restype = None
+        lib.qd_blocks_destroy.argtypes = [P]
         lib.qd_sample.restype = ctypes.c_int
         lib.qd_sample.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
         lib.qd_device_status.restype = ctypes.c_int
@@ -235,3 +252,70 @@ def qd_destroy(handle: int) -> None:
 def qd_last_error(handle: Optional[int] = None) -> str:
     msg = load_library().qd_last_error(handle)
     return msg.decode() if msg else ""
+
+
+class PageManager:
+    """Host-side page manager of a paged KV pool (qd_blocks_* in include/qd.h).
+    Methods return the C call's non-negative result and raise QdError on an
+    error code (QD_ENOMEM: not enough pages, nothing changed)."""
+
+    def __init__(self, num_pages: int, max_pages_per_seq: int):
+        self.lib = load_library()
+        h = ctypes.c_void_p()
+        rc = self.lib.qd_blocks_create(num_pages, max_pages_per_seq, ctypes.byref(h))
+        if rc != QD_OK:
+            raise QdError(rc, "qd_blocks_create failed")
+        self.h = h.value
+        self.max_pages = max_pages_per_seq
+
+    def _rc(self, rc: int) -> int:
+        if rc < 0:
+            raise QdError(rc, "page manager call failed")
+        return rc
+
+    def add(self, seq: int) -> None:
+        self._rc(self.lib.qd_blocks_add(self.h, seq))
+
+    def reserve(self, seq: int, n_tokens: int) -> None:
+        self._rc(self.lib.qd_blocks_reserve(self.h, seq, n_tokens))
+
+    def release(self, seq: int) -> None:
+        self._rc(self.lib.qd_blocks_release(self.h, seq))
+
+    def fork(self, src: int, dst: int):
+        """(copy_src, copy_dst): the page to copy on the device, or (-1, -1)."""
+        a, b = ctypes.c_int32(), ctypes.c_int32()
+        self._rc(self.lib.qd_blocks_fork(self.h, src, dst, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def tables(self, seqs, pad_page: int) -> np.ndarray:
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        out = np.empty((len(ids), self.max_pages), dtype=np.int32)
+        self._rc(self.lib.qd_blocks_tables(self.h, ids.ctypes.data, len(ids), pad_page,
+                                           out.ctypes.data))
+        return out
+
+    def length(self, seq: int) -> int:
+        return self._rc(self.lib.qd_blocks_length(self.h, seq))
+
+    def available(self) -> int:
+        return self._rc(self.lib.qd_blocks_available(self.h))
+
+    def publish(self, seq: int, tokens) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        return self._rc(self.lib.qd_blocks_publish(self.h, seq, t.ctypes.data, len(t)))
+
+    def match(self, seq: int, tokens) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        return self._rc(self.lib.qd_blocks_match(self.h, seq, t.ctypes.data, len(t)))
+
+    def close(self) -> None:
+        if self.h:
+            self.lib.qd_blocks_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -564,3 +564,103 @@ def test_full_size_steps(torch, name, persistent):
     dec.close()
     del pool
     torch.cuda.empty_cache()
+
+
+def test_prefix_shared_pages_match_private_copies(torch):
+    """Sequences built with the page manager: A prefilled (by the oracle) and
+    its 48-token prompt prefix published; B takes those three pages from the
+    prefix cache and prefills only its own suffix; C holds B's tokens in
+    pages of its own.  Decode steps of [A, B, C] on the GPU give B and C the
+    same bits, and leave the shared pages untouched."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 41)
+    orc = oracle.Oracle(shape, W)
+    rng = np.random.default_rng(42)
+    prefix = rng.integers(0, shape.vocab, 48).astype(np.int32)
+    pa = np.concatenate([prefix, rng.integers(0, shape.vocab, 10).astype(np.int32)])
+    pb = np.concatenate([prefix, rng.integers(0, shape.vocab, 7).astype(np.int32)])
+    steps, max_pages, num_pages = 4, 8, 24
+    pad = num_pages  # an extra page, never used, as the table filler
+    L, Hkv, D = shape.num_layers, shape.num_kv_heads, shape.head_dim
+    pool = np.zeros((L, num_pages + 1, 2, Hkv, 16, D), dtype=np.uint16)
+    mgr = binding.PageManager(num_pages, max_pages)
+    mgr.add(0)
+    mgr.reserve(0, len(pa) + steps)
+    row_a = mgr.tables([0], pad)[0]
+    _, tok_a = orc.prefill(pa, row_a, pool)
+    assert mgr.publish(0, pa) == 3
+    mgr.add(1)
+    assert mgr.match(1, pb) == 48
+    mgr.reserve(1, len(pb) + steps)
+    mgr.add(2)
+    mgr.reserve(2, len(pb) + steps)
+    rows = mgr.tables([0, 1, 2], pad)
+    assert list(rows[1][:3]) == list(row_a[:3]) and not set(rows[2]) & set(row_a[:3])
+    for t in range(48, len(pb)):  # B: only its suffix
+        orc.decode_step(pb[t:t + 1], np.array([t], np.int32), rows[1:2], pool, want_logits=False)
+    _, tok_c = orc.prefill(pb, rows[2], pool)
+    shared = [int(p) for p in row_a[:3]]
+    before = pool[:, shared].copy()
+    dec = Decoder(shape, 3, max_pages, num_pages + 1)
+    dec.load_numpy_weights(W)
+    dpool = pool_to_device(pool)
+    io = StepIO(torch, 3, max_pages, shape.vocab)
+    tokens = np.array([tok_a, tok_c, tok_c], np.int32)
+    positions = np.array([len(pa), len(pb), len(pb)], np.int32)
+    for step in range(steps):
+        say(f"prefix sharing step {step}")
+        io.set(tokens, positions, rows)
+        io.run(dec, dpool)
+        torch.cuda.synchronize()
+        assert torch.equal(io.logits[1], io.logits[2]), step
+        assert torch.equal(io.nxt[1], io.nxt[2]), step
+        tokens = io.nxt.cpu().numpy()
+        tokens[2] = tokens[1]
+        positions = positions + 1
+    np.testing.assert_array_equal(pool_to_host(dpool)[:, shared], before)
+    assert dec.device_status() == 0
+    dec.close()
+    mgr.close()
+
+
+def test_forked_sequence_matches_its_source(torch):
+    """A sequence forked by the page manager (full pages shared, the partly
+    filled page copied on the device) decodes the same tokens to the same
+    bits as its source, and diverging tokens leave the shared pages as they
+    were."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 43)
+    orc = oracle.Oracle(shape, W)
+    prompt = np.random.default_rng(44).integers(0, shape.vocab, 40).astype(np.int32)
+    steps, max_pages, num_pages = 3, 6, 16
+    L, Hkv, D = shape.num_layers, shape.num_kv_heads, shape.head_dim
+    pool = np.zeros((L, num_pages + 1, 2, Hkv, 16, D), dtype=np.uint16)
+    mgr = binding.PageManager(num_pages, max_pages)
+    mgr.add(0)
+    mgr.reserve(0, len(prompt))
+    _, tok = orc.prefill(prompt, mgr.tables([0], num_pages)[0], pool)
+    cs, cd = mgr.fork(0, 1)
+    assert cs >= 0 and cd >= 0
+    for s in (0, 1):
+        mgr.reserve(s, len(prompt) + steps)
+    rows = mgr.tables([0, 1], num_pages)
+    shared = [int(p) for p in rows[0][:2]]
+    assert list(rows[1][:2]) == shared
+    dpool = pool_to_device(pool)
+    dpool[:, cd] = dpool[:, cs]  # the device copy the fork asks for
+    before = pool_to_host(dpool)[:, shared].copy()
+    dec = Decoder(shape, 2, max_pages, num_pages + 1)
+    dec.load_numpy_weights(W)
+    io = StepIO(torch, 2, max_pages, shape.vocab)
+    io.set([tok, tok], [len(prompt)] * 2, rows)
+    io.run(dec, dpool)
+    torch.cuda.synchronize()
+    assert torch.equal(io.logits[0], io.logits[1])
+    nxt = io.nxt.cpu().numpy()
+    io.set([nxt[0], (nxt[0] + 1) % shape.vocab], [len(prompt) + 1] * 2, rows)
+    io.run(dec, dpool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pool_to_host(dpool)[:, shared], before)
+    assert dec.device_status() == 0
+    dec.close()
+    mgr.close()

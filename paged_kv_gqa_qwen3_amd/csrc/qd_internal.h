@@ -222,6 +222,7 @@ struct SampleArgs {
   unsigned* counters;        // [B] at stride kCntStride, zero between calls
   double* part_sum;          // [B][G] chunk weight sums (rows without limits)
   unsigned* counters2;       // [B] at stride kCntStride, for the second launch
+  double* row_hist;          // [B][256] weight per top key byte (top-p rows), zero between calls
 };
 void sample_split(int V, int* G, int* C);
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s);

@@ -88,6 +88,7 @@ struct qd_handle {
   unsigned* sample_cnt = nullptr;
   double* sample_sum = nullptr;
   unsigned* sample_cnt2 = nullptr;
+  double* sample_hist = nullptr;
   int* dev_flags = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   int max_pos = 0;
@@ -710,8 +711,10 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     if ((rc = dev_alloc(h, &h->sample_cnt, (size_t)Bm * kCntStride))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_sum, slots))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_cnt2, (size_t)Bm * kCntStride))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_hist, (size_t)Bm * 256))) return bail(rc);
     e = hipMemset(h->sample_cnt, 0, sizeof(unsigned) * Bm * kCntStride);
     if (e == hipSuccess) e = hipMemset(h->sample_cnt2, 0, sizeof(unsigned) * Bm * kCntStride);
+    if (e == hipSuccess) e = hipMemset(h->sample_hist, 0, sizeof(double) * Bm * 256);
     if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
   }
   e = hipMemset(h->gemv_cnt, 0, sizeof(unsigned) * max_nrg * kCntStride);
@@ -974,7 +977,8 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
     return fail(h, QD_EINVAL, "logits must be 16-byte aligned");
   SampleArgs a{logits, h->V, temperature, top_k, top_p, uniform, out_ids,
                h->sample_G, h->sample_C, h->sample_max, h->sample_idx,
-               h->sample_cand, h->sample_cnt, h->sample_sum, h->sample_cnt2};
+               h->sample_cand, h->sample_cnt, h->sample_sum, h->sample_cnt2,
+               h->sample_hist};
   HIP_TRY(h, launch_sample(a, batch, h->stream));
   return QD_OK;
 }

@@ -145,9 +145,11 @@ __device__ __forceinline__ double block_exclusive(double v, SampleSmem& sm) {
 }
 
 // The whole-row path for row b (one workgroup of kSampleThreads), given
-// the row's max M (T > 0, top_p > 0, top_k not 1).
+// the row's max M (T > 0, top_p > 0, top_k not 1).  pre_top: sm.mass holds
+// the row's weight per top key byte already (top-p without top-k), so the
+// top-p selection starts at its second byte.
 __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, float p,
-                           float u, SampleSmem& sm) {
+                           float u, SampleSmem& sm, bool pre_top = false) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int V = a.V, V4 = a.V >> 2;
   const f32x4* __restrict__ row4 = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V);
@@ -197,19 +199,22 @@ __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, 
   // need(total) (total: the sum over all of them, known after the first
   // pass); leaves the key in sm.key and in sm.need what remains to take
   // among the tokens of that key.  Returns the total.
-  auto select = [&](auto&& in, auto&& unit, auto&& need_of) {
+  auto select = [&](auto&& in, auto&& unit, auto&& need_of, bool pre = false) {
     unsigned prefix = 0u, mask = 0u;
     double need = 0.0, total = 0.0;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
-      __syncthreads();
-      strided([&](int i, float l, bool ok) {
-        const unsigned key = sample_key(l);
-        const bool on = ok && (key & mask) == prefix && in(i, l, key);
-        double val = 0.0;
-        if (on) val = unit(l);
-        hist_add(sm, (key >> shift) & 255u, val, on);
-      });
+      if (!(pre && shift == 24)) {
+        __syncthreads();
+        for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
+        __syncthreads();
+        strided([&](int i, float l, bool ok) {
+          const unsigned key = sample_key(l);
+          const bool on = ok && (key & mask) == prefix && in(i, l, key);
+          double val = 0.0;
+          if (on) val = unit(l);
+          hist_add(sm, (key >> shift) & 255u, val, on);
+        });
+      }
       __syncthreads();
       if (shift == 24) {
         double t4 = 0.0;
@@ -266,7 +271,7 @@ __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, 
   unsigned kp = 0u;
   int ip = V;
   if (use_p) {
-    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); });
+    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); }, pre_top && !use_k);
     kp = sm.key;
     ip = cut_id(kp, in_k, weight, sm.need);
   }
@@ -557,10 +562,31 @@ __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a
   const float* row = a.logits + (size_t)b * V;
   const f32x4* src = reinterpret_cast<const f32x4*>(row + c0);
   double mine = 0.0;
-  for (int j = tid; j < n / 4; j += kSampleThreads) {
-    const f32x4 v = src[j];
+  if (topp) {
+    // the chunk's weight per top key byte too, added into the row's
+    // histogram (exact: integers below 2^53), for a nucleus beyond the
+    // first 64 tokens
+    for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
+    __syncthreads();
+    for (int j0 = 0; j0 < n / 4; j0 += kSampleThreads) {
+      const int j = j0 + tid;
+      const f32x4 v = j < n / 4 ? src[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) mine += weight(v[e]);
+      for (int e = 0; e < 4; ++e) {
+        const double w = j < n / 4 ? weight(v[e]) : 0.0;
+        mine += w;
+        hist_add(sm, sample_key(v[e]) >> 24, w, w > 0.0);
+      }
+    }
+    __syncthreads();
+    for (int j = tid; j < 256; j += kSampleThreads)
+      if (sm.mass[j] != 0.0) atomicAdd(a.row_hist + (size_t)b * 256 + j, sm.mass[j]);
+  } else {
+    for (int j = tid; j < n / 4; j += kSampleThreads) {
+      const f32x4 v = src[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine += weight(v[e]);
+    }
   }
   const double S = block_sum(mine, sm);
   const size_t slot = (size_t)b * G + g;
@@ -615,7 +641,14 @@ __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a
       }
     }
     __syncthreads();
-    if (s_whole) sample_row(a, b, M, T, k, p, u, sm);
+    // the row's top-byte histogram into LDS (and cleared for the next call)
+    for (int j = tid; j < 256; j += kSampleThreads) {
+      double* hp = a.row_hist + (size_t)b * 256 + j;
+      sm.mass[j] = __hip_atomic_load(hp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(hp, 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_whole) sample_row(a, b, M, T, k, p, u, sm, true);
     return;
   }
 

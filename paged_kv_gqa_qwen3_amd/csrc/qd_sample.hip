@@ -19,20 +19,29 @@
 //     token is the kept one, in increasing id order, whose running weight
 //     first exceeds t.
 //
-// One launch per call, G workgroups per row (G = ceil(V / 8192)), each
-// owning a chunk of at most 8192 logits that it loads into LDS once.  Every
-// chunk leaves its (max, argmax) and, when 2 <= top_k <= kFastTopK, its 64
-// first tokens in rank order (each wave sorts batches of 64 across its lanes
-// and keeps the best 64; then the lists are merged); the last workgroup of
-// the row to arrive merges them: the greedy token from the maxima, and the
-// row's first 64 tokens from the lists, then top-k, top-p and the draw in one
-// wave.  Any other setting (top_k 0 or above kFastTopK with temperature > 0)
-// takes the whole-row path in that last workgroup: cut points in rank order
-// by radix selection over a 32-bit key that orders floats (four passes of 8
-// bits: token counts for top-k, weight for top-p), then one pass in id order
-// among the tokens whose key equals the cut key; every pass re-reads the row
-// from L2 (608 KB for a 151,936 token vocabulary) and recomputes the weights
-// it needs.
+// Two launches per call, G workgroups per row (G = ceil(V / 8192)), each
+// owning a chunk of at most 8192 logits.
+//   First launch: every chunk loads its logits into LDS once and leaves its
+//   (max, argmax) and, for 2 <= top_k <= kFastTopK or for top-p without
+//   top_k, its 64 first tokens in rank order (each wave sorts batches of 64
+//   across its lanes and keeps the best 64; the waves' lists are merged).
+//   The last workgroup of the row to arrive takes the greedy token from the
+//   maxima, or, with 2 <= top_k <= kFastTopK, merges the chunks' lists into
+//   the row's first 64 tokens and takes top-k, top-p and the draw in one
+//   wave.
+//   Second launch, rows without top_k: every chunk sums its weights against
+//   the row's max (with top-p also its weight per top key byte, added into
+//   the row's histogram); the last workgroup then walks the chunk holding
+//   the draw target (no limit), or takes the top-p cut and the draw over
+//   the row's first 64 tokens when they reach the target.
+// Anything else (top_k above kFastTopK, or a top-p nucleus beyond 64
+// tokens) runs over the whole row in one workgroup (sample_row): cut points
+// in rank order by radix selection over a 32-bit key that orders floats
+// (four passes of 8 bits: token counts for top-k, weight for top-p; the
+// first top-p pass from the row histogram when there is one), then one pass
+// in id order among the tokens whose key equals the cut key; every pass
+// re-reads the row from L2 (608 KB for a 151,936 token vocabulary) and
+// recomputes the weights it needs.
 #include <hip/hip_runtime.h>
 
 #include "qd_device.h"

@@ -493,12 +493,16 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   // Attention items go to workgroups that own no row of the O projection
   // (so no O tiles wait for them meanwhile), when there are enough of those
   // (4B shape: 96 of 256; batch 1, context 512: 2.374 -> 2.358 ms per step
-  // against items on workgroups 0..71).
+  // against items on workgroups 0..71).  Ownership is decided on the
+  // XCD-major place (stream_place), which spreads the idle workgroups, like
+  // every unit's pieces, evenly over the XCDs (2.354 -> 2.343 ms per step
+  // against the plain order, where O owners sat on 5 of the 8 XCDs).
   const unsigned R_o = (unsigned)(a.H / kTileRows);
   const int n_idle = (unsigned)W > R_o ? W - (int)R_o : 0;
-  const int o_before = (int)((unsigned)wg * R_o / (unsigned)W);
-  const bool o_idle = (int)((unsigned)(wg + 1) * R_o / (unsigned)W) == o_before;
-  const int a_first = n_idle >= attn_n ? (o_idle ? wg - o_before : attn_n) : wg;
+  const int wq = stream_place(wg, W);
+  const int o_before = (int)((unsigned)wq * R_o / (unsigned)W);
+  const bool o_idle = (int)((unsigned)(wq + 1) * R_o / (unsigned)W) == o_before;
+  const int a_first = n_idle >= attn_n ? (o_idle ? wq - o_before : attn_n) : wg;
   const bool attn_wg = a_first < attn_n;  // this workgroup runs attention items
 
   for (int l = 0; l < a.L; ++l) {

@@ -45,8 +45,13 @@ struct StreamShare {
   bool lm;
 };
 
-// Workgroup wg of W owns pieces [wg*P/W, (wg+1)*P/W) of a unit with P
-// pieces.
+// Workgroups are dealt to the chip's 8 XCDs round robin (wg % 8); a
+// workgroup's place in every partition is its index in XCD-major order, so
+// that each XCD gets a balanced share of every unit.
+QD_HD int stream_place(int wg, int W) { return W % 8 == 0 ? (wg % 8) * (W / 8) + wg / 8 : wg; }
+
+// Workgroup wg of W owns pieces [q*P/W, (q+1)*P/W) of a unit with P
+// pieces, q = stream_place(wg, W).
 QD_HD StreamShare stream_share(const StreamArgs& a, int u, int wave, int W, int wg) {
   StreamShare s;
   if (u >= a.L * kUnitsPerLayer) {
@@ -62,8 +67,9 @@ QD_HD StreamShare stream_share(const StreamArgs& a, int u, int wave, int W, int 
   }
   s.kps = (s.KT + s.S - 1) / s.S;
   const unsigned P = (unsigned)s.R * (unsigned)s.S;
-  s.r0 = (int)((unsigned)wg * P / (unsigned)W);
-  s.r1 = (int)((unsigned)(wg + 1) * P / (unsigned)W);
+  const unsigned q = (unsigned)stream_place(wg, W);
+  s.r0 = (int)(q * P / (unsigned)W);
+  s.r1 = (int)((q + 1) * P / (unsigned)W);
   return s;
 }
 

@@ -42,8 +42,10 @@ const uint16_t* fake_base(int u) {
 }
 
 // The wave's tiles in consumption order, from the partition's definition:
-// unit by unit, the workgroup's pieces [wg*P/W, (wg+1)*P/W) of the unit's P
-// = R*S pieces (piece r: row tile r/S, k-tiles [(r%S)*kps, ...+kps) within
+// unit by unit, the workgroup's pieces [q*P/W, (q+1)*P/W) of the unit's P
+// = R*S pieces, q its index when the W workgroups are listed XCD by XCD
+// (workgroup wg runs on XCD wg % 8; q = (wg % 8) * W/8 + wg / 8 when W is a
+// multiple of 8, else wg) (piece r: row tile r/S, k-tiles [(r%S)*kps, ...+kps) within
 // K), of each the k-tiles kb + wave, kb + wave + 4, ... (the LM head: row
 // tile 4g + wave, every k-tile).
 std::vector<const unsigned char*> expected(const Shape& sh, int qS, int W, int wg, int wave) {
@@ -63,7 +65,12 @@ std::vector<const unsigned char*> expected(const Shape& sh, int qS, int W, int w
     }
     const int kps = (KT + S - 1) / S;
     const long P = (long)R * S;
-    const long r0 = (long)wg * P / W, r1 = (long)(wg + 1) * P / W;
+    long q = wg;
+    if (W % 8 == 0) {
+      const int per_xcd = W / 8, xcd = wg % 8, slot = wg / 8;
+      q = (long)xcd * per_xcd + slot;
+    }
+    const long r0 = q * P / W, r1 = (q + 1) * P / W;
     const unsigned char* base = reinterpret_cast<const unsigned char*>(fake_base(u));
     const long rows_total = lm ? 4L * R : R;  // row tiles of the matrix
     for (long r = r0; r < r1; ++r) {

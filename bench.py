@@ -270,6 +270,53 @@ def time_sampling(torch, dec, B, V, reps=50):
     return res
 
 
+def time_prefill(torch, shape, W, n_tokens=512, chunk=32, reps=3):
+    """Milliseconds to prefill one n_tokens prompt from an empty pool through
+    qd_prefill: chunks of `chunk` rows in position order, logits for the last
+    row only (HIP events on the library's stream, torch's current stream).
+    Every chunk streams the weights once."""
+    from paged_kv_gqa_qwen3_amd.decoder import Decoder
+    pages = -(-n_tokens // 16)
+    dec = Decoder(shape, chunk, pages, pages, use_graphs=False)
+    dec.load_numpy_weights(W)
+    pool = torch.zeros(shape.num_layers, pages, 2, shape.num_kv_heads, 16, shape.head_dim,
+                       dtype=torch.int16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    prompt = torch.randint(0, shape.vocab, (n_tokens,), dtype=torch.int32, device="cuda",
+                           generator=g)
+    table = torch.arange(pages, dtype=torch.int32, device="cuda")
+    calls = []
+    for c0 in range(0, n_tokens, chunk):
+        pos = torch.arange(c0, min(c0 + chunk, n_tokens), dtype=torch.int32, device="cuda")
+        last = c0 + chunk >= n_tokens
+        if last:  # the prompt's last token first: it gets the logits
+            pos = torch.cat([pos[-1:], pos[:-1]])
+        calls.append((prompt[pos.long()].contiguous(), pos,
+                      table[None].expand(len(pos), pages).contiguous(), 1 if last else 0))
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+
+    def run():
+        for tok, pos, tab, n in calls:
+            dec.prefill(tok, pos, tab, pool, n, nxt if n else None, lg if n else None)
+    run()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    assert dec.device_status() == 0
+    dec.close()
+    del pool
+    torch.cuda.empty_cache()
+    return {"prompt_tokens": n_tokens, "chunk_rows": chunk, "chunks": len(calls),
+            "ms": round(ms, 3), "tokens_per_s": round(n_tokens / (ms / 1e3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +400,11 @@ def main():
                     headline_extra = stream_roofline(w, ms, args.steps, nbytes)
                 else:
                     headline_extra = per_stage_roofline(torch, dec, run, shape, w, batch)
+                # prompt processing (qd_prefill) of a 512-token prompt, the
+                # headline's context, on a handle of its own
+                results[w.name]["prefill"] = time_prefill(torch, shape, W)
+                log(f"[bench] {w.name}: qd_prefill of 512 prompt tokens "
+                    f"{results[w.name]['prefill']}")
                 if not args.no_cpu_baseline:
                     log("[bench] timing the CPU oracle on a bounded sample")
                     headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)

@@ -112,6 +112,36 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
  * QD_EINVAL on an unknown name or a wrong shape.  Synchronous. */
 int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
 
+/* One chunk of prompt tokens (chunked prefill; the blog "GPU 算子与执行优化：
+ * 从 26 到 100 token/s", Part 7: only the positions whose next token is
+ * wanted reach the LM head, and chunks that end no prompt compute no logits).
+ * `rows` (1 <= rows <= max_batch) prompt tokens, from one or several
+ * sequences, each row laid out as a decode step's row (DEVICE pointers):
+ *   token_ids    int32 [rows]        the prompt token at that position
+ *   positions    int32 [rows]        its position; a sequence's rows may come
+ *                                    in any order but must not repeat a position
+ *   block_tables int32 [rows][max_pages_per_seq]  the row's sequence's pages
+ *                                    (the same row content for every row of
+ *                                    one sequence)
+ *   kv_pool      as for qd_decode_step; every row's K/V is written
+ *   n_logits     0 .. rows: rows 0 .. n_logits-1 get the final RMSNorm, the
+ *                                    LM head and the greedy next id (put each
+ *                                    prompt's last token there); 0 = none
+ *   out_next_ids int32 [n_logits]    or NULL when n_logits is 0
+ *   out_logits   fp32 [n_logits][vocab] or NULL
+ * Attention is causal across the chunk: a row attends to every position of
+ * its sequence up to its own, including rows of this same chunk (each layer
+ * appends all rows' K/V in one launch, then attends in a second).  Positions
+ * before the chunk must already be in the pool.  The result equals running
+ * the rows one position at a time through qd_decode_step, up to rounding.
+ * Kernels are launched directly on the handle's stream (no graph), always
+ * the per-stage kernels (also on a persistent handle).  Asynchronous.
+ * QD_EINVAL on a NULL pointer, rows out of range or n_logits outside
+ * 0..rows; QD_ESTATE before all weights are loaded. */
+int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32_t* positions,
+               const int32_t* block_tables, void* kv_pool, int32_t n_logits,
+               int32_t* out_next_ids, float* out_logits);
+
 /* One decode step for `batch` sequences (1 <= batch <= max_batch).  All
  * pointers are DEVICE pointers:
  *   token_ids    int32 [batch]       token decoded by each sequence

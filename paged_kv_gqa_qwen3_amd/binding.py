@@ -29,7 +29,7 @@ QD_DEV_BAD_POSITION = 2
 QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
-EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_decode_step_taps",
+EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_decode_step_taps",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
             "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
             "qd_blocks_create", "qd_blocks_destroy", "qd_blocks_add", "qd_blocks_reserve",
@@ -86,6 +86,8 @@ def load_library():
         lib.qd_load_weights.argtypes = [P, ctypes.POINTER(QdTensorDesc), ctypes.c_int32]
         lib.qd_decode_step.restype = ctypes.c_int
         lib.qd_decode_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
+        lib.qd_prefill.restype = ctypes.c_int
+        lib.qd_prefill.argtypes = [P, ctypes.c_int32, P, P, P, P, ctypes.c_int32, P, P]
         lib.qd_decode_step_taps.restype = ctypes.c_int
         lib.qd_decode_step_taps.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
                                             ctypes.POINTER(QdTaps)]
@@ -179,6 +181,13 @@ def qd_decode_step(handle: int, batch: int, token_ids, positions, block_tables, 
     _check(lib.qd_decode_step(handle, batch, _ptr(token_ids), _ptr(positions),
                               _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
                               _ptr(out_logits)), handle)
+
+
+def qd_prefill(handle: int, rows: int, token_ids, positions, block_tables, kv_pool,
+               n_logits: int, out_next_ids=None, out_logits=None) -> None:
+    lib = load_library()
+    _check(lib.qd_prefill(handle, rows, _ptr(token_ids), _ptr(positions), _ptr(block_tables),
+                          _ptr(kv_pool), n_logits, _ptr(out_next_ids), _ptr(out_logits)), handle)
 
 
 def qd_decode_step_taps(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,

@@ -992,8 +992,12 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   }
   __syncthreads();
 
-  // --- append k, v of this step (the split owning the last page does it)
-  if (s == nsplit - 1) {
+  // --- append k, v of this step (the split owning the last page does it).
+  // A prefill chunk's rows attend to one another's K/V, so its layer runs
+  // two launches: the first only appends, the second only attends (its own
+  // k, v come from LDS, the same bits the first launch wrote).
+  const int kv_mode = kAgent ? kAppendAttend : a.kv_mode;
+  if (kv_mode != kAttendOnly && s == nsplit - 1) {
     const int page = bt[pos / kPage];
     if (page < 0 || page >= a.num_pages) {
       if (tid == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
@@ -1005,6 +1009,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
       for (int i = tid; i < D; i += NW * 64) { kd[i] = sm.k[i]; vd[i] = sm.v[i]; }
     }
   }
+  if (kv_mode == kAppendOnly) return;  // uniform over the workgroup
 
   mark(2);
   // --- paged attention over this wave's pages

@@ -38,6 +38,13 @@ enum GemvMode : int {
   kPartial = 4, // no reduction: every item leaves its K-split partial for the consumer
 };
 
+// What an attention launch does with the step's K/V rows.
+enum KvMode : int {
+  kAppendAttend = 0,  // decode: append each row's k, v and attend
+  kAppendOnly = 1,    // prefill, first launch of a layer: append only
+  kAttendOnly = 2,    // prefill, second launch: attend over the filled pages
+};
+
 // One GEMV work item covers rt row tiles (16*rt rows) and one of S slices
 // of K (kps k-tiles); its 4 waves take the row tiles and, when rt < 4,
 // split the item's K slice between them (reduced in LDS).
@@ -96,6 +103,8 @@ struct AttnArgs {
   float* tap_k;            // optional [B][Hkv][D] (before bf16 rounding)
   int* dev_flags;
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: item event timestamps, or null
+  int kv_mode;             // kAppendAttend (decode), or a prefill layer's kAppendOnly then
+                           // kAttendOnly launch (standalone kernel only)
 };
 
 struct EmbedArgs {

@@ -157,6 +157,14 @@ int dev_alloc(qd_handle* h, T** p, size_t count) {
 // not, and an LDS input slice <= 48 KB so that three workgroups fit a CU.
 constexpr size_t kLdsCapValu = 80 * 1024;
 constexpr size_t kLdsCapStaged = 48 * 1024;
+// Wider batches stage more input columns per k-tile: a 48 KB cap would cut K
+// into slices of 3 k-tiles at 64 columns, and the split partials (S x N x 64
+// floats, written and read back) would outweigh the weights.  Larger caps
+// (fewer workgroups per CU) keep the slices at 9-13 k-tiles (4B shape,
+// 512-token prompt in 64-row chunks: 249 -> 137 ms; 32-row: 131 -> 116 ms).
+constexpr size_t gemv_lds_cap(int nb) {
+  return nb >= 64 ? (size_t)124 * 1024 : nb >= 32 ? (size_t)96 * 1024 : kLdsCapStaged;
+}
 constexpr int kMinValuItems = 128;
 
 // A persistent handle runs batch 1 as the weight-streaming step kernel when
@@ -192,7 +200,7 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false)
     const int kps = (KT + S - 1) / S;
     const int Se = (KT + kps - 1) / kps;
     if (kps > 16 && NRG < mtarget) continue;
-    if (gemv_lds_bytes(B, kps) > kLdsCapStaged) continue;
+    if (gemv_lds_bytes(B, kps) > gemv_lds_cap(nb)) continue;
     p.S = Se;
     p.kps = kps;
     if (NRG * Se >= mtarget) return p;
@@ -257,6 +265,7 @@ struct StepPtrs {
   uint16_t* pool;
   int32_t* next;
   float* logits;
+  int n_logits = -1;  // a prefill chunk: rows [0, n_logits) get the LM head; -1: a decode step
 };
 
 // Optional per-launch event recording (qd_profile_step).
@@ -389,6 +398,12 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.tap_q = tap ? taps->q_rot : nullptr;
     aa.tap_k = tap ? taps->k_rot : nullptr;
     aa.dev_flags = h->dev_flags;
+    if (sp.n_logits >= 0) {  // prefill: every row's k, v in the pool before any row attends
+      aa.kv_mode = kAppendOnly;
+      HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
+                                  attn_pages_per_wave(B, false, h->long_ctx), s));
+      aa.kv_mode = kAttendOnly;
+    }
     HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
                                 attn_pages_per_wave(B, false, h->long_ctx), s));
     PROF(QD_PROF_ATTN);
@@ -412,7 +427,11 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   if (taps && taps->final_h)
     HIP_TRY(h, launch_rmsnorm_rows(h->x, h->ssq, h->final_norm, H, B, h->cfg.max_batch, eps,
                                    taps->final_h, s));
-  HIP_TRY(h, proj(QD_PROF_LM_HEAD, 0, true));
+  // the LM head over the leading rows: all of a decode step's, a prefill
+  // chunk's first n_logits (none for a chunk that ends no prompt)
+  const int B_lm = sp.n_logits < 0 ? B : sp.n_logits;
+  if (B_lm > 0)
+    HIP_TRY(h, launch_projection(h, B_lm, QD_PROF_LM_HEAD, 0, true, sp.logits, sp.next, s));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
   return QD_OK;
@@ -890,6 +909,19 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   }
   HIP_TRY(h, hipGraphLaunch(it->second, h->stream));
   return QD_OK;
+}
+
+int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32_t* positions,
+               const int32_t* block_tables, void* kv_pool, int32_t n_logits,
+               int32_t* out_next_ids, float* out_logits) {
+  if (!h) return QD_EINVAL;
+  if (n_logits < 0 || n_logits > rows) return fail(h, QD_EINVAL, "n_logits must be in 0..rows");
+  if (n_logits > 0 && !out_next_ids) return fail(h, QD_EINVAL, "NULL out_next_ids");
+  int rc = check_step_args(h, rows, token_ids, positions, block_tables, kv_pool, token_ids);
+  if (rc) return rc;
+  StepPtrs sp{rows, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+              out_next_ids, out_logits, n_logits};
+  return record_step(h, sp, nullptr, h->stream);
 }
 
 int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,

@@ -69,6 +69,13 @@ class Decoder:
         binding.qd_decode_step(self.handle, int(tokens.shape[0]), tokens, positions, tables,
                                pool, next_ids, logits)
 
+    def prefill(self, tokens, positions, tables, pool, n_logits=0, next_ids=None,
+                logits=None) -> None:
+        """One chunk of prompt rows (qd_prefill): causal across the chunk; rows
+        0..n_logits-1 get logits and greedy next ids."""
+        binding.qd_prefill(self.handle, int(tokens.shape[0]), tokens, positions, tables, pool,
+                           int(n_logits), next_ids, logits)
+
     def step_taps(self, tokens, positions, tables, pool, next_ids, logits, taps, layer):
         binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,
                                     tables, pool, next_ids, logits, taps, layer)

@@ -72,4 +72,5 @@ def test_null_arguments(lib):
     assert lib.qd_decode_step(None, 1, None, None, None, None, None, None) == binding.QD_EINVAL
     assert lib.qd_load_weights(None, None, 0) == binding.QD_EINVAL
     assert lib.qd_sample(None, 1, None, None, None, None, None, None) == binding.QD_EINVAL
+    assert lib.qd_prefill(None, 1, None, None, None, None, 0, None, None) == binding.QD_EINVAL
     lib.qd_destroy(None)

@@ -20,7 +20,8 @@ import pytest
 import oracle
 from paged_kv_gqa_qwen3_amd import binding, synth
 from paged_kv_gqa_qwen3_amd.decoder import Decoder, pool_to_device, pool_to_host
-from gpu_util import (bf16_rne_of_f32, check_logits, check_next_ids, gemv_tol, say)
+from gpu_util import (LOGIT_RTOL, bf16_rne_of_f32, check_logits, check_next_ids, gemv_tol,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -664,3 +665,101 @@ def test_forked_sequence_matches_its_source(torch):
     assert dec.device_status() == 0
     dec.close()
     mgr.close()
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def _prefill_chunks(prompts, chunk, seed):
+    """The prompts' (sequence, position) rows in chunks of `chunk`, positions
+    in order across chunks (so a chunk's earlier positions are in the pool),
+    sequences interleaved; in each chunk the rows holding a prompt's last
+    token come first (they get logits), the others in a seeded random order.
+    Returns [(rows, n_logits)]."""
+    rng = np.random.default_rng(seed)
+    rows = sorted((p, s) for s, pr in enumerate(prompts) for p in range(len(pr)))
+    out = []
+    for i in range(0, len(rows), chunk):
+        c = [(s, p) for p, s in rows[i:i + chunk]]
+        last = [r for r in c if r[1] == len(prompts[r[0]]) - 1]
+        rest = [r for r in c if r[1] != len(prompts[r[0]]) - 1]
+        order = rng.permutation(len(rest))
+        out.append((last + [rest[j] for j in order], len(last)))
+    return out
+
+
+def _check_prefill(torch, shape, W, prompts, chunk, persistent, seed):
+    """GPU chunked prefill (qd_prefill) against the oracle running each prompt
+    one position at a time: the last position's logits and greedy id, every
+    appended K/V row, and no other pool row touched."""
+    V = shape.vocab
+    batch = synth.make_paged_batch(shape, [0] * len(prompts), max(len(p) for p in prompts),
+                                   seed, fill_kv=False)
+    tables = batch.block_tables
+    pool_start = batch.pool.copy()
+    pool = pool_to_device(batch.pool)
+    dec = Decoder(shape, chunk, batch.max_pages, batch.num_pages, persistent=persistent)
+    dec.load_numpy_weights(W)
+    got = {}
+    for ci, (rows, n) in enumerate(_prefill_chunks(prompts, chunk, seed)):
+        say(f"prefill {shape.name} chunk {ci}: {len(rows)} rows, {n} with logits")
+        tok = _i32(torch, [prompts[s][p] for s, p in rows])
+        pos = _i32(torch, [p for _, p in rows])
+        tab = _i32(torch, tables[[s for s, _ in rows]])
+        nxt = torch.full((max(n, 1),), -1, dtype=torch.int32, device="cuda")
+        lg = torch.zeros(max(n, 1), V, dtype=torch.float32, device="cuda")
+        dec.prefill(tok, pos, tab, pool, n, nxt if n else None, lg if n else None)
+        torch.cuda.synchronize()
+        for i in range(n):
+            got[rows[i][0]] = (lg[i].cpu().numpy(), nxt[i:i + 1].cpu().numpy())
+    assert dec.device_status() == 0
+    dec.close()
+    orc = oracle.Oracle(shape, W)
+    pool_or = batch.pool
+    for s, pr in enumerate(prompts):
+        say(f"prefill {shape.name}: oracle, prompt {s} ({len(pr)} tokens)")
+        lg_or, _ = orc.prefill(pr, tables[s], pool_or)
+        r = check_logits(got[s][0][None], lg_or[None], f"prompt {s}")
+        check_next_ids(got[s][1], lg_or[None], f"prompt {s}")
+        say(f"prefill prompt {s}: logit ratio {r:.3e}")
+    host = pool_to_host(pool)
+    m = _appended_mask(batch, [(s, p) for s, pr in enumerate(prompts) for p in range(len(pr))])
+    np.testing.assert_array_equal(host[~m], pool_start[~m])
+    # Layer 0's K/V come from the embedding through one projection: the
+    # one-stage bound of the decode step's append.  Deeper layers' K/V are
+    # outputs of the whole stack below them, like the logits, and take the
+    # logits' end-to-end bound (LOGIT_RTOL of the row's largest magnitude)
+    # plus either side's bf16 rounding.
+    _assert_kv_close(oracle.bf16_to_f64(host[0][m[0]]), oracle.bf16_to_f64(pool_or[0][m[0]]),
+                     "prefill KV, layer 0")
+    worst = 0.0
+    for l in range(1, shape.num_layers):
+        a, b = oracle.bf16_to_f64(host[l][m[l]]), oracle.bf16_to_f64(pool_or[l][m[l]])
+        scale = np.abs(b).max(axis=-1, keepdims=True) + 1e-30
+        r = np.abs(a - b) / (2.0 ** -7 * np.abs(b) + LOGIT_RTOL * scale)
+        worst = max(worst, float(r.max()))
+        assert np.all(r <= 1.0), f"prefill KV, layer {l}: worst ratio {float(r.max()):.3f}"
+    say(f"prefill KV: worst end-to-end ratio {worst:.3f} (layers 1..{shape.num_layers - 1})")
+
+
+@pytest.mark.parametrize("lens,chunk,persistent", [
+    ([70, 45], 24, False),      # rows from two prompts, one logit row per ending chunk
+    ([33, 33, 20], 64, False),  # a 64-row chunk, then two prompts ending in one chunk
+    ([17, 9], 8, True),         # persistent handle: prefill still runs the staged kernels
+    ([1], 1, True),             # one-token prompt: the batch-1 kernels
+])
+def test_tiny_prefill_matches_oracle(torch, lens, chunk, persistent):
+    shape = synth.TINY
+    seed = 300 + sum(lens) + chunk
+    W = synth.make_weights(shape, seed)
+    prompts = [synth.uniform_int(seed + i, "prompt", shape.vocab, n) for i, n in enumerate(lens)]
+    _check_prefill(torch, shape, W, prompts, chunk, persistent, seed)
+
+
+def test_full_size_prefill_matches_oracle(torch):
+    """Qwen3-4B shape: two prompts (20 and 12 tokens) in 16-row chunks; the
+    second chunk ends both prompts (logits for two rows)."""
+    shape = synth.QWEN3_4B
+    W = _weights(shape, 2)
+    prompts = [synth.uniform_int(500 + i, "prompt", shape.vocab, n) for i, n in enumerate([20, 12])]
+    _check_prefill(torch, shape, W, prompts, 16, False, 5)
+    torch.cuda.empty_cache()

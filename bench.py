@@ -324,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing qd_prefill on a 512-token prompt (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=("auto", "graph"), default="auto",
                     help="auto: a persistent handle, on which the library runs batch 1 as "
@@ -402,9 +404,10 @@ def main():
                     headline_extra = per_stage_roofline(torch, dec, run, shape, w, batch)
                 # prompt processing (qd_prefill) of a 512-token prompt, the
                 # headline's context, on a handle of its own
-                results[w.name]["prefill"] = time_prefill(torch, shape, W)
-                log(f"[bench] {w.name}: qd_prefill of 512 prompt tokens "
-                    f"{results[w.name]['prefill']}")
+                if not args.no_prefill:
+                    results[w.name]["prefill"] = time_prefill(torch, shape, W)
+                    log(f"[bench] {w.name}: qd_prefill of 512 prompt tokens "
+                        f"{results[w.name]['prefill']}")
                 if not args.no_cpu_baseline:
                     log("[bench] timing the CPU oracle on a bounded sample")
                     headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)

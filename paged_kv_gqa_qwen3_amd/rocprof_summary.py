@@ -110,7 +110,14 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, kind: str,
 
     fc, wc = per_class(f), per_class(w)
     sha = bench.kernel_source_sha256(kind)
+    run = (f"python -u bench.py --workloads {workload} --steps 4 --warmup 1 --no-cpu-baseline "
+           f"--no-prefill --copy-calibration-mib 1024")
     lines = [f"# HBM traffic per dispatch (rocprofv3 --pmc), workload {workload}", "",
+             "commands (repo root, MI355X), one counter per run, then this summary:",
+             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- {run}",
+             f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- {run}",
+             f"  python -m paged_kv_gqa_qwen3_amd.rocprof_summary traffic {fetch_dir} {write_dir} "
+             f"{workload} {kind} {out_prefix}", "",
              f"kernel source sha256 ({' + '.join(bench.KERNEL_SOURCES[kind])}): {sha}", "",
              f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {_calibration(f):.1f} KiB and "
              f"WRITE_SIZE = {_calibration(w):.1f} KiB",

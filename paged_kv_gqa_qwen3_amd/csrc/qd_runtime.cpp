@@ -159,12 +159,12 @@ constexpr size_t kLdsCapValu = 80 * 1024;
 constexpr size_t kLdsCapStaged = 48 * 1024;
 // Wider batches stage more input columns per k-tile: a 48 KB cap would cut K
 // into slices of 3 k-tiles at 64 columns, and the split partials (S x N x 64
-// floats, written and read back) would outweigh the weights.  Larger caps
-// (fewer workgroups per CU) keep the slices at 9-13 k-tiles (4B shape,
-// 512-token prompt in 64-row chunks: 249 -> 137 ms; 32-row: 131 -> 116 ms).
-constexpr size_t gemv_lds_cap(int nb) {
-  return nb >= 64 ? (size_t)124 * 1024 : nb >= 32 ? (size_t)96 * 1024 : kLdsCapStaged;
-}
+// floats, written and read back) would outweigh the weights.  A 76 KB cap
+// keeps two workgroups per CU and slices of 7-16 k-tiles (4B shape,
+// 512-token prompt in 64-row chunks: 249 -> 126 ms, 32-row: 131 -> 100 ms;
+// one workgroup per CU with 124 KB: 137 and 112 ms; 16 columns stay best at
+// 48 KB).
+constexpr size_t gemv_lds_cap(int nb) { return nb >= 32 ? (size_t)76 * 1024 : kLdsCapStaged; }
 constexpr int kMinValuItems = 128;
 
 // A persistent handle runs batch 1 as the weight-streaming step kernel when

@@ -763,3 +763,48 @@ def test_full_size_prefill_matches_oracle(torch):
     prompts = [synth.uniform_int(500 + i, "prompt", shape.vocab, n) for i, n in enumerate([20, 12])]
     _check_prefill(torch, shape, W, prompts, 16, False, 5)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
+def test_prefill_then_decode_end_to_end(torch, persistent):
+    """The whole request on the GPU: a 40-token prompt prefilled in 16-row
+    chunks (qd_prefill), then 8 greedy decode steps from the prefill's own
+    next id, each teacher-forced by the oracle (which prefills one position
+    at a time), logits and ids checked at every step."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 77)
+    n, steps = 40, 8
+    prompt = synth.uniform_int(77, "prompt", shape.vocab, n)
+    batch = synth.make_paged_batch(shape, [0], n + steps, 77, fill_kv=False)
+    table = batch.block_tables
+    pool = pool_to_device(batch.pool)
+    pool_or = batch.pool.copy()
+    dec = Decoder(shape, 16, batch.max_pages, batch.num_pages, persistent=persistent)
+    dec.load_numpy_weights(W)
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+    for c0 in range(0, n, 16):
+        pos = list(range(c0, min(c0 + 16, n)))
+        last = pos[-1] == n - 1
+        if last:
+            pos = [pos[-1]] + pos[:-1]
+        dec.prefill(_i32(torch, prompt[pos]), _i32(torch, pos), _i32(torch, table[[0] * len(pos)]),
+                    pool, 1 if last else 0, nxt if last else None, lg if last else None)
+    orc = oracle.Oracle(shape, W)
+    lg_or, token = orc.prefill(prompt, table[0], pool_or)
+    torch.cuda.synchronize()
+    check_logits(lg.cpu().numpy(), lg_or[None], "prefill")
+    check_next_ids(nxt.cpu().numpy(), lg_or[None], "prefill")
+    io = StepIO(torch, 1, batch.max_pages, shape.vocab)
+    for step in range(steps):
+        say(f"prefill+decode persistent={persistent} step {step}")
+        io.set([token], [n + step], table)
+        io.run(dec, pool)
+        lg_or, nx_or, _ = orc.decode_step(np.array([token], np.int32),
+                                          np.array([n + step], np.int32), table, pool_or)
+        torch.cuda.synchronize()
+        check_logits(io.logits.cpu().numpy(), lg_or, f"step {step}")
+        check_next_ids(io.nxt.cpu().numpy(), lg_or, f"step {step}")
+        token = int(nx_or[0])
+    assert dec.device_status() == 0
+    dec.close()

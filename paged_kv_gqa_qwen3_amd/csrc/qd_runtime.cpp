@@ -917,6 +917,7 @@ int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32
   if (!h) return QD_EINVAL;
   if (n_logits < 0 || n_logits > rows) return fail(h, QD_EINVAL, "n_logits must be in 0..rows");
   if (n_logits > 0 && !out_next_ids) return fail(h, QD_EINVAL, "NULL out_next_ids");
+  // (out_next_ids may be NULL here: token_ids stands in for it in the check)
   int rc = check_step_args(h, rows, token_ids, positions, block_tables, kv_pool, token_ids);
   if (rc) return rc;
   StepPtrs sp{rows, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),

@@ -808,3 +808,27 @@ def test_prefill_then_decode_end_to_end(torch, persistent):
         token = int(nx_or[0])
     assert dec.device_status() == 0
     dec.close()
+
+
+def test_prefill_rejects_bad_arguments(torch):
+    """Argument errors come back as codes and launch nothing: rows outside
+    1..max_batch, n_logits outside 0..rows, no next-id output while logits
+    are asked for, weights not loaded."""
+    shape = synth.TINY
+    batch = synth.make_paged_batch(shape, [0], 32, 3, fill_kv=False)
+    dec = Decoder(shape, 4, batch.max_pages, batch.num_pages)
+    pool = pool_to_device(batch.pool)
+    tok, pos = _i32(torch, [1, 2, 3, 4]), _i32(torch, [0, 1, 2, 3])
+    tab = _i32(torch, np.repeat(batch.block_tables, 4, axis=0))
+    nxt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    h = dec.handle
+    with pytest.raises(binding.QdError):  # weights not loaded
+        binding.qd_prefill(h, 4, tok, pos, tab, pool, 1, nxt)
+    dec.load_numpy_weights(synth.make_weights(shape, 3))
+    for rows, n, out in ((0, 0, nxt), (5, 1, nxt), (4, 5, nxt), (4, -1, nxt), (4, 1, None)):
+        with pytest.raises(binding.QdError):
+            binding.qd_prefill(h, rows, tok, pos, tab, pool, n, out)
+    binding.qd_prefill(h, 4, tok, pos, tab, pool, 0)  # a chunk without logits is fine
+    torch.cuda.synchronize()
+    assert dec.device_status() == 0
+    dec.close()

@@ -27,6 +27,11 @@
  *   greedy sampling on the device, only the token id leaves the step)
  * Weights and the KV pool are bf16; all accumulation is fp32.
  *
+ * Around the step: qd_prefill runs a chunk of prompt tokens through the same
+ * layers (causal across the chunk, logits only where asked), qd_sample draws
+ * the next token on the device (temperature, top-k, top-p), and qd_blocks_*
+ * manage the pool's pages on the host (free pool, forks, prefix cache).
+ *
  * Threading: a handle is used by one host thread at a time.  Calls are
  * asynchronous on the handle's stream unless stated otherwise.
  */

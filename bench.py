@@ -10,13 +10,15 @@ captured hipGraph).  Steps are chained on the device: each step's next-token
 ids are the following step's input (two ping-pong id buffers, so the graphs
 never change), and the positions advance on the device.
 
-Headline line: Qwen3-4B shape, batch 1, context 512 (value = tokens/s).  The
-same JSON line also carries batch 8 / 16 at context 256 and batch 1 at 8192
-under "workloads", the live roofline of the dominant kernel and the CPU
-oracle timed on a bounded sample.
+Headline line: Qwen3-4B shape, batch 1, context 512 (value = tokens/s, the
+median over --reps repetitions of K timed steps).  The same JSON line also
+carries batch 8 / 16 at context 256, batch 1 at 8192 and the Qwen3-8B ragged
+batch 8 under "workloads", the live roofline of the dominant kernel, the
+measured streaming-read ceiling of the device and the CPU oracle timed on a
+bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b]
-                       [--no-cpu-baseline] [--profile-only]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
+                       [--workloads a,b] [--no-cpu-baseline] [--no-prefill]
 """
 from __future__ import annotations
 
@@ -36,7 +38,8 @@ from paged_kv_gqa_qwen3_amd import accounting, binding, synth  # noqa: E402
 METRIC = "decode tokens/s + achieved HBM GB/s (% of 8 TB/s), Qwen3-4B shape, bs 1/8/16"
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "4b_bs1_ctx512"
-DEFAULT_WORKLOADS = ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192"]
+DEFAULT_WORKLOADS = ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
+                     "8b_bs8_ragged"]
 WEIGHT_SEED = {"qwen3-4b": 2, "qwen3-8b": 6}
 
 
@@ -117,28 +120,35 @@ class Run:
         self.pos.copy_(self.pos0)
 
 
-def time_workload(torch, dec, w, batch, steps, warmup):
+def time_workload(torch, dec, w, batch, steps, warmup, reps):
+    """`reps` repetitions of `steps` chained steps from the same start
+    positions, each bracketed by HIP events on the library's stream (torch's
+    current stream here); returns the run, every repetition's milliseconds,
+    the wall time of all of them and the algorithmic bytes of one
+    repetition."""
     run = Run(torch, dec, w, batch)
     for _ in range(warmup):
         run.step()
     torch.cuda.synchronize()
-    run.reset()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
-        run.step()
-    end.record()
-    torch.cuda.synchronize()
+    for _ in range(reps):
+        run.reset()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            run.step()
+        end.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end)
     flags = dec.device_status()
     if flags:
         raise RuntimeError(f"device input flags {flags} during {w.name}")
     ctx0 = batch.positions.astype(np.int64) + 1
     total_bytes = sum(accounting.step_bytes(w.shape, ctx0 + s) for s in range(steps))
-    return run, ms, wall, total_bytes
+    return run, times, wall, total_bytes
 
 
 def profile_classes(torch, dec, run, reps=5):
@@ -178,9 +188,34 @@ def cpu_baseline(w, W, batch, budget_s=20.0):
     ncpu = len(os.sched_getaffinity(0))
     cores = min(threads, ncpu) if threads > 0 else ncpu
     return {"value": round(steps * w.batch / dt, 4), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{steps} decode step(s) of {w.name} (batch {w.batch}, context "
                       f"{int(batch.positions[0])}+), {dt:.1f} s, fp64 C oracle with OpenMP"}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling(torch, gib=2, reps=10):
+    """The device's plain streaming-read rate (qd_read_ceiling: 16-byte
+    nontemporal loads over a gib GiB buffer, the weight-streaming pattern),
+    GB/s: the practical ceiling next to the nominal 8 TB/s."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    torch.cuda.synchronize()
+    gbps = binding.qd_read_ceiling(buf, buf.numel(), reps,
+                                   torch.cuda.current_stream().cuda_stream)
+    del buf
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
 
 
 def stream_roofline(w, ms, steps, nbytes):
@@ -322,6 +357,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed repetitions of --steps steps per workload (median reported)")
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
@@ -345,6 +382,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load_library()
+    ceiling = read_ceiling(torch)
+    log(f"[bench] streaming-read ceiling {ceiling} GB/s")
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -382,14 +421,20 @@ def main():
             path = dec.step_path(w.batch)
             log(f"[bench] {w.name}: {path} path, timing {args.steps} steps after "
                 f"{args.warmup} warmup")
-            run, ms, wall, nbytes = time_workload(torch, dec, w, batch, args.steps, args.warmup)
+            run, times, wall, nbytes = time_workload(torch, dec, w, batch, args.steps,
+                                                     args.warmup, args.reps)
+            ms = float(np.median(times))
             tok_s = args.steps * w.batch / (ms / 1e3)
             gbps = nbytes / (ms / 1e3) / 1e9
             results[w.name] = {
                 "workload": w.name, "batch": w.batch, "path": path,
                 "context0": [int(c) for c in batch.positions[:4]] + (["..."] if w.batch > 4 else []),
                 "tokens_per_s": round(tok_s, 2), "ms_per_step": round(ms / args.steps, 4),
+                "ms_per_step_min_max": [round(min(times) / args.steps, 4),
+                                        round(max(times) / args.steps, 4)],
+                "reps": args.reps,
                 "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "ceiling_frac": round(gbps / ceiling, 4) if ceiling else None,
                 "wall_s": round(wall, 4),
             }
             log(f"[bench] {w.name}: {tok_s:.1f} tok/s, {ms / args.steps:.4f} ms/step, "
@@ -427,10 +472,16 @@ def main():
                    "context0": 512, "parallelism": "single GPU", "mode": args.mode,
                    "path": h["path"]},
         "achieved_GBps": h["achieved_GBps"], "hbm_frac": h["hbm_frac"],
+        "reps": args.reps, "ms_per_step_min_max": h["ms_per_step_min_max"],
     }
     out.update(headline_extra)
+    if "roofline" in out:
+        out["roofline"]["ceiling_GBps"] = ceiling
     out["workloads"] = [results[n] for n in names if n in results]
     print(json.dumps(out), flush=True)
+    # every handle is closed above; let the device finish before the
+    # interpreter and the runtime tear down
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -104,6 +104,11 @@ typedef struct qd_tensor_desc {
  * hipStream_t; NULL means the null stream) on the current device.  Allocates
  * the packed-weight arena, activations, split-KV and split-K scratch and the
  * RoPE table (cos/sin of p * theta^(-2i/D) computed in double, stored fp32).
+ * Everything a step touches besides the caller's buffers is allocated here,
+ * once, so that its addresses stay fixed for every later step and captured
+ * graph (the blog "GPU 算子与执行优化：从 26 到 100 token/s", Part 5: the
+ * decode-graph runner allocates its static buffers before capture and the
+ * graph freezes every address it uses).
  * Returns QD_OK and *out, or an error (then *out is NULL).  Synchronous. */
 int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
 
@@ -111,10 +116,13 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
  * (model.embed_tokens, model.layers.N.{input_layernorm, self_attn.{q,k,v,o}_proj,
  * self_attn.{q,k}_norm, post_attention_layernorm, mlp.{gate,up,down}_proj},
  * model.norm, lm_head when untied) with their HF shapes ([out, in] for
- * projections).  Tensors may come in several calls.  The library repacks
- * them into its own tile layout (q|k|v fused, gate and up paired) and keeps
- * no reference to the caller's memory once the call returns.
- * QD_EINVAL on an unknown name or a wrong shape.  Synchronous. */
+ * projections), as a checkpoint's tensors come, with no offline conversion,
+ * and lays them out in the order the step reads them (the rkmt page "从零构建
+ * Qwen3-8B 推理引擎", 4.2.1 tensors and weight loading; 4.4.3 fused QKV).
+ * Tensors may come in several calls.  The library repacks them into its own
+ * tile layout (q|k|v fused, gate and up paired) and keeps no reference to
+ * the caller's memory once the call returns.  QD_EINVAL on an unknown name
+ * or a wrong shape; QD_EHIP if a repack launch fails.  Synchronous. */
 int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
 
 /* One chunk of prompt tokens (chunked prefill; the blog "GPU 算子与执行优化：
@@ -147,7 +155,13 @@ int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32
                const int32_t* block_tables, void* kv_pool, int32_t n_logits,
                int32_t* out_next_ids, float* out_logits);
 
-/* One decode step for `batch` sequences (1 <= batch <= max_batch).  All
+/* One decode step for `batch` sequences (1 <= batch <= max_batch): token
+ * ids and positions in, one next token id per sequence out, and nothing but
+ * ids and control crosses the call (the rkmt page "从零构建 Qwen3-8B 推理引擎",
+ * 4.1.2: DecodeStep returns the sampled next token; the blog "GPU 算子与执行优化：
+ * 从 26 到 100 token/s", Part 5: replay copies the dynamic ids and positions
+ * into frozen buffers and launches the captured step once; Part 3: the argmax
+ * runs on the device and logits leave only when asked for).  All
  * pointers are DEVICE pointers:
  *   token_ids    int32 [batch]       token decoded by each sequence
  *   positions    int32 [batch]       its position p (= tokens already cached)
@@ -165,7 +179,9 @@ int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32
  * (every wait is bounded; a timeout sets QD_DEV_TIMEOUT).  Otherwise, with
  * use_graphs, the first call
  * for a (batch, pointer set) captures a hipGraph of the per-stage kernels and
- * later calls replay it (new pointers cause a new capture).
+ * later calls replay it (new pointers cause a new capture).  A handle keeps
+ * at most 64 graphs: beyond that the least recently replayed one is
+ * destroyed (after its stream drains) to make room.
  * Kernels clamp out-of-range ids, positions and page ids instead of reading
  * out of bounds, and record them for qd_device_status. */
 int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
@@ -215,6 +231,17 @@ int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
                         void* kv_pool, int32_t* out_next_ids, float* out_logits,
                         const qd_taps* taps);
 
+/* Checking only: one batch-1 step as the weight-streaming kernel (the one
+ * qd_decode_step runs at batch 1 on a handle whose qd_step_path is
+ * QD_PATH_STREAM), also filling `taps` (may be NULL): workgroup 0 copies
+ * each stage's result of layer taps->layer out of the running kernel once
+ * every workgroup has finished that stage.  Same arguments and effects as
+ * qd_decode_step at batch 1.  QD_EUNSUPPORTED on a handle that does not
+ * stream batch 1. */
+int qd_stream_step_taps(qd_handle* h, const int32_t* token_ids, const int32_t* positions,
+                        const int32_t* block_tables, void* kv_pool, int32_t* out_next_ids,
+                        float* out_logits, const qd_taps* taps);
+
 /* Kernel classes timed by qd_profile_step. */
 #define QD_PROF_EMBED 0    /* embedding gather */
 #define QD_PROF_QKV 1      /* RMSNorm + fused QKV projection */
@@ -248,6 +275,20 @@ int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
  * buffer and no KV pool.  QD_EUNSUPPORTED for the other classes.
  * Synchronous. */
 int qd_profile_class(qd_handle* h, int32_t batch, int32_t cls, int32_t reps, float* avg_us);
+
+/* Measurement: the device's plain streaming-read rate in GB/s (*gbps), the
+ * practical ceiling of the weight-streaming pattern that the step's kernels
+ * follow, for comparison with the nominal HBM peak (the locsic page
+ * "推理引擎里面发生了什么", HBM bandwidth wall: decode is bound by the rate
+ * at which weights stream from HBM).  Reads the first floor(bytes/1024) KB
+ * of the DEVICE buffer `buf` (caller-owned, contents irrelevant, >= 1 GiB
+ * recommended so that the caches do not hold it) `reps` times with 16-byte
+ * nontemporal loads, 1, 2 and 4 workgroups per CU, and reports the best
+ * rate; timed with HIP events on `hip_stream` (a hipStream_t, NULL = null
+ * stream).  Needs no handle and allocates nothing.  Synchronous.  QD_EINVAL
+ * for a NULL pointer, bytes < 1024 or reps < 1; QD_EHIP on a launch error
+ * (message in qd_last_error(NULL)). */
+int qd_read_ceiling(const void* buf, int64_t bytes, int32_t reps, void* hip_stream, float* gbps);
 
 /* Wait for the handle's stream, then return (and clear) the QD_DEV_* bits
  * the kernels recorded since the last call in *flags.  Synchronous. */
@@ -313,11 +354,17 @@ int qd_blocks_publish(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t 
  * (a multiple of 16), which need no prefill. */
 int qd_blocks_match(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t n);
 
-/* Free everything the handle owns (waits for its stream first). */
+/* Free everything the handle owns: captured graphs, packed weights,
+ * scratch (it waits for its stream first; the caller's pool and buffers are
+ * untouched).  Call it before the HIP runtime is torn down (before process
+ * exit), like any other release of device memory.  NULL is a no-op.  The
+ * pages name no teardown; this is the counterpart of qd_create. */
 void qd_destroy(qd_handle* h);
 
 /* Text of the last error on this handle (or of the last failed qd_create when
- * h is NULL).  Valid until the next call on the handle. */
+ * h is NULL).  Valid until the next call on the handle.  Errors never cross
+ * the ABI as exceptions (the rkmt page "从零构建 Qwen3-8B 推理引擎", 4.1.1: a
+ * fault of the compute layer must not take down the layer above it). */
 const char* qd_last_error(const qd_handle* h);
 
 #ifdef __cplusplus

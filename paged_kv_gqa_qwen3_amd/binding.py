@@ -30,6 +30,7 @@ QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_decode_step_taps",
+            "qd_stream_step_taps", "qd_read_ceiling",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
             "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
             "qd_blocks_create", "qd_blocks_destroy", "qd_blocks_add", "qd_blocks_reserve",
@@ -91,6 +92,11 @@ def load_library():
         lib.qd_decode_step_taps.restype = ctypes.c_int
         lib.qd_decode_step_taps.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
                                             ctypes.POINTER(QdTaps)]
+        lib.qd_stream_step_taps.restype = ctypes.c_int
+        lib.qd_stream_step_taps.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(QdTaps)]
+        lib.qd_read_ceiling.restype = ctypes.c_int
+        lib.qd_read_ceiling.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P,
+                                        ctypes.POINTER(ctypes.c_float)]
         lib.qd_profile_step.restype = ctypes.c_int
         lib.qd_profile_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
                                         ctypes.POINTER(ctypes.c_float),
@@ -200,6 +206,26 @@ def qd_decode_step_taps(handle: int, batch: int, token_ids, positions, block_tab
     _check(lib.qd_decode_step_taps(handle, batch, _ptr(token_ids), _ptr(positions),
                                    _ptr(block_tables), _ptr(kv_pool), _ptr(out_next_ids),
                                    _ptr(out_logits), ctypes.byref(tp) if tp else None), handle)
+
+
+def qd_stream_step_taps(handle: int, token_ids, positions, block_tables, kv_pool,
+                        out_next_ids, out_logits=None, taps: Optional[dict] = None,
+                        tap_layer: int = -1) -> None:
+    lib = load_library()
+    tp = None
+    if taps is not None:
+        tp = QdTaps(tap_layer, *[_ptr(taps.get(n)) for n in TAP_NAMES])
+    _check(lib.qd_stream_step_taps(handle, _ptr(token_ids), _ptr(positions), _ptr(block_tables),
+                                   _ptr(kv_pool), _ptr(out_next_ids), _ptr(out_logits),
+                                   ctypes.byref(tp) if tp else None), handle)
+
+
+def qd_read_ceiling(buf, nbytes: int, reps: int, stream: Optional[int] = None) -> float:
+    """Plain streaming-read rate (GB/s) over the first nbytes of a device buffer."""
+    lib = load_library()
+    out = ctypes.c_float()
+    _check(lib.qd_read_ceiling(_ptr(buf), int(nbytes), int(reps), stream, ctypes.byref(out)), None)
+    return float(out.value)
 
 
 def qd_profile_step(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,

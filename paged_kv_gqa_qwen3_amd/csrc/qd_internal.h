@@ -177,6 +177,13 @@ struct StreamArgs {
   int* dev_flags;
   unsigned spin_limit;
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: per-stage timestamps
+  // Stage taps (checking only): at layer tap_layer (-1: none) workgroup 0
+  // copies each stage's result out once every workgroup has finished it
+  // (fp32, the qd_taps layouts; any pointer may be null), and the attention
+  // items run with attn_tap (attn plus tap_q / tap_k).
+  int tap_layer;
+  float *tap_x_in, *tap_qkv, *tap_attn, *tap_x_mid, *tap_act, *tap_x_out, *tap_final_h;
+  AttnArgs attn_tap;
 };
 
 // Batch columns a GEMV item is compiled for: VALU at batch 1; MFMA above, 8
@@ -256,6 +263,9 @@ size_t stream_lds_bytes(int head_dim, int group, int in_floats, int rt_max);
 hipError_t stream_max_grid(int head_dim, int group, size_t lds, int num_cus, int* grid);
 hipError_t launch_stream(const StreamArgs& a, int head_dim, int group, int grid, size_t lds,
                          hipStream_t s);
+
+// Plain streaming read of the first bytes/1024 KB of src (measurement).
+hipError_t launch_read_ceiling(const void* src, size_t bytes, int grid, hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for its input slice.
 size_t gemv_lds_bytes(int B, int kps);

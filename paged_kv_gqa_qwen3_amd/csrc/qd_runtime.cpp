@@ -38,6 +38,9 @@ struct GraphKey {
   }
 };
 
+// Captured graphs a handle keeps (one per batch size and pointer set).
+constexpr int kMaxGraphs = 64;
+
 struct GemvPlan {
   int S = 1, kps = 1, rt = 4;
 };
@@ -95,6 +98,8 @@ struct qd_handle {
 
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::map<GraphKey, hipGraph_t> graph_defs;
+  std::map<GraphKey, unsigned long long> graph_use;  // last replay, for eviction at the cap
+  unsigned long long graph_clock = 0;
 
   // batch-1 streaming step (persistent handles)
   bool persistent = false;
@@ -500,9 +505,6 @@ int setup_stream(qd_handle* h) {
       h->stream_res_off = res_off;
       h->stream_rt_max = rt_max;
       h->stream_qkv_S = qS;
-      if (std::getenv("QD_DEBUG"))
-        std::fprintf(stderr, "[qd] streaming step: grid %d, LDS %zu, rt_max %d, QKV splits %d\n",
-                     W, lds, rt_max, qS);
       return QD_OK;
     }
     W = g;
@@ -510,8 +512,9 @@ int setup_stream(qd_handle* h) {
   return QD_OK;
 }
 
-// One batch-1 step as the streaming cooperative kernel.
-int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
+// One batch-1 step as the streaming cooperative kernel (taps: copy one
+// layer's intermediates out, for checking; may be null).
+int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s, const qd_taps* taps = nullptr) {
   const int H = h->H;
   StreamArgs a{};
   a.embed.table = h->embed;
@@ -558,6 +561,16 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   a.exit_cnt = h->step_exit; a.abort_flag = h->step_abort;
   a.dev_flags = h->dev_flags;
   a.spin_limit = 1u << 22;  // polls; a few seconds, far beyond any real wait
+  a.tap_layer = -1;
+  a.attn_tap = a.attn;
+  if (taps != nullptr) {
+    a.tap_layer = taps->layer;
+    a.tap_x_in = taps->x_in; a.tap_qkv = taps->qkv; a.tap_attn = taps->attn;
+    a.tap_x_mid = taps->x_mid; a.tap_act = taps->act; a.tap_x_out = taps->x_out;
+    a.tap_final_h = taps->final_h;
+    a.attn_tap.tap_q = taps->q_rot;
+    a.attn_tap.tap_k = taps->k_rot;
+  }
 #ifdef QD_STEP_TRACE
   static unsigned long long* trace = nullptr;
   const size_t trace_n = (size_t)h->stream_grid * 1024 * 3;
@@ -877,6 +890,18 @@ int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
   return record_step(h, sp, taps, h->stream);
 }
 
+int qd_stream_step_taps(qd_handle* h, const int32_t* token_ids, const int32_t* positions,
+                        const int32_t* block_tables, void* kv_pool, int32_t* out_next_ids,
+                        float* out_logits, const qd_taps* taps) {
+  int rc = check_step_args(h, 1, token_ids, positions, block_tables, kv_pool, out_next_ids);
+  if (rc) return rc;
+  if (!use_stream(h, 1))
+    return fail(h, QD_EUNSUPPORTED, "this handle does not run batch 1 as the streaming kernel");
+  StepPtrs sp{1, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+              out_next_ids, out_logits};
+  return run_stream(h, sp, h->stream, taps);
+}
+
 int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
                    const int32_t* positions, const int32_t* block_tables, void* kv_pool,
                    int32_t* out_next_ids, float* out_logits) {
@@ -885,12 +910,24 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits};
   if (use_stream(h, batch)) return run_stream(h, sp, h->stream);
-  static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
-  if (!h->cfg.use_graphs || no_graph) return record_step(h, sp, nullptr, h->stream);
+  if (!h->cfg.use_graphs) return record_step(h, sp, nullptr, h->stream);
 
   GraphKey key{batch, {token_ids, positions, block_tables, kv_pool, out_next_ids, out_logits}};
   auto it = h->graphs.find(key);
   if (it == h->graphs.end()) {
+    if (h->graphs.size() >= (size_t)kMaxGraphs) {
+      // at the cap: destroy the least recently replayed graph (once the
+      // stream has finished with it)
+      auto old = h->graphs.begin();
+      for (auto g = h->graphs.begin(); g != h->graphs.end(); ++g)
+        if (h->graph_use[g->first] < h->graph_use[old->first]) old = g;
+      HIP_TRY(h, hipStreamSynchronize(h->stream));
+      (void)hipGraphExecDestroy(old->second);
+      (void)hipGraphDestroy(h->graph_defs[old->first]);
+      h->graph_defs.erase(old->first);
+      h->graph_use.erase(old->first);
+      h->graphs.erase(old);
+    }
     // First call for this key: run it eagerly (this produces the results),
     // then capture the same launches on the private stream.
     if ((rc = record_step(h, sp, nullptr, h->stream))) return rc;
@@ -905,8 +942,10 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
     if (e != hipSuccess) { (void)hipGraphDestroy(g); return hip_fail(h, e, "hipGraphInstantiate"); }
     h->graphs[key] = ge;
     h->graph_defs[key] = g;
+    h->graph_use[key] = ++h->graph_clock;
     return QD_OK;
   }
+  h->graph_use[key] = ++h->graph_clock;
   HIP_TRY(h, hipGraphLaunch(it->second, h->stream));
   return QD_OK;
 }
@@ -1016,6 +1055,38 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
   return QD_OK;
 }
 
+int qd_read_ceiling(const void* buf, int64_t bytes, int32_t reps, void* hip_stream,
+                    float* gbps) {
+  if (!buf || !gbps || bytes < 1024 || reps < 1) return fail(nullptr, QD_EINVAL, "bad arguments");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  float best = 0.f;
+  for (int per_cu = 1; per_cu <= 4 && e == hipSuccess; per_cu *= 2) {
+    const int grid = per_cu * cus;
+    e = launch_read_ceiling(buf, (size_t)bytes, grid, s);  // warm-up
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch_read_ceiling(buf, (size_t)bytes, grid, s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess && ms > 0.f) {
+      const float g = (float)((double)(bytes / 1024 * 1024) * reps / (ms * 1e-3) / 1e9);
+      best = g > best ? g : best;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "qd_read_ceiling");
+  *gbps = best;
+  return QD_OK;
+}
+
 int qd_device_status(qd_handle* h, int32_t* flags) {
   if (!h || !flags) return QD_EINVAL;
   HIP_TRY(h, hipStreamSynchronize(h->stream));
@@ -1031,8 +1102,7 @@ void* qd_stream(const qd_handle* h) { return h ? static_cast<void*>(h->stream) :
 int qd_step_path(const qd_handle* h, int32_t batch) {
   if (!h || batch < 1 || batch > h->cfg.max_batch) return QD_EINVAL;
   if (use_stream(h, batch)) return QD_PATH_STREAM;
-  static const bool no_graph = std::getenv("QD_NO_GRAPH") && std::atoi(std::getenv("QD_NO_GRAPH"));
-  return h->cfg.use_graphs && !no_graph ? QD_PATH_GRAPH : QD_PATH_STAGED;
+  return h->cfg.use_graphs ? QD_PATH_GRAPH : QD_PATH_STAGED;
 }
 
 void qd_destroy(qd_handle* h) {

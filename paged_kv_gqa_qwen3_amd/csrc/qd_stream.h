@@ -487,6 +487,14 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     if ((lane & 15) == 0) st_agent(a.ssq + (size_t)(n / kSsqRows) * a.Bmax, ss);
   };
 
+  // Stage taps (checking only): workgroup 0 copies a stage's result out
+  // once every workgroup has finished that stage (it is read here before
+  // workgroup 0 itself finishes the next stage, so nothing overwrites it).
+  auto tap_copy = [&](float* dst, const float* src, int n) {
+    if (dst != nullptr && wg == 0)
+      for (int i = tid; i < n; i += 256) dst[i] = ld_agent(src + i);
+  };
+
   const unsigned n_heads = (unsigned)a.attn.Hkv;
   const AttnList alist = attn_list<attn_pages_per_split(1, true)>(a.attn);
   const int attn_n = __builtin_amdgcn_readfirstlane(attn_items(alist, 1));
@@ -519,6 +527,8 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     const int lim_qkv = attn_wg ? u + kPrQkv : u_lim(u + kPrQkv);
     stream_wait(a, rg, wave, lane, x_ready, lim_qkv);
     mark(l * 20 + 0);
+    if (l == a.tap_layer) tap_copy(a.tap_x_in, a.x, a.H);
+    if (l - 1 == a.tap_layer) tap_copy(a.tap_x_out, a.x, a.H);
     stage_input(a.x, a.H, ly.in_norm, 0, 0);
     mark(l * 20 + 1);
     project(u + kPrQkv, lim_qkv, true, [&](int, int piece, float y) {
@@ -533,10 +543,10 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     if (!attn_wg) ring_top_up(a, rg, wave, lane, u_lim(u + kPrO));
     uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
 #ifdef QD_STEP_TRACE
-    AttnArgs at = a.attn;  // (trace builds) the item's events of layer 17 at slots 960..967
-    at.trace = l == 17 ? a.trace + (size_t)wg * 1024 + 960 : nullptr;
+    AttnArgs at = l == a.tap_layer ? a.attn_tap : a.attn;  // (trace builds) the item's
+    at.trace = l == 17 ? a.trace + (size_t)wg * 1024 + 960 : nullptr;  // events of layer 17
 #else
-    const AttnArgs& at = a.attn;
+    const AttnArgs& at = l == a.tap_layer ? a.attn_tap : a.attn;
 #endif
     for (int t = a_first; t < attn_n; t += W)
       attention_item<D, G, kAttnWavesPersistent, attn_pages_per_wave(1, true)>(
@@ -550,6 +560,17 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       const StreamShare so = stream_share(a, u + kPrO, 0, W, wg);
       stream_wait(a, rg, wave, lane, phase(c + 1), u_lim(u + kPrO));
       mark(l * 20 + 5);
+      if (l == a.tap_layer) {
+        tap_copy(a.tap_attn, a.attn_out, a.QD);
+        if (a.tap_qkv != nullptr && wg == 0)  // q|k|v: the sum of the split partials
+          for (int n = tid; n < a.NQKV; n += 256) {
+            const float* p = a.qkv_part + (size_t)(n / kTileRows) * a.qkv_S * kTileRows +
+                             n % kTileRows;
+            float v = 0.f;
+            for (int s2 = 0; s2 < a.qkv_S; ++s2) v += ld_agent(p + (size_t)s2 * kTileRows);
+            a.tap_qkv[n] = v;
+          }
+      }
       stage_input(a.attn_out, a.QD, nullptr, so.r0, so.r1);
       mark(l * 20 + 6);
       project(u + kPrO, u_lim(u + kPrO), false, resid);
@@ -562,6 +583,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     // 8-15 the matching up channels)
     stream_wait(a, rg, wave, lane, phase(c + 2), u_lim(u + kPrGu));
     mark(l * 20 + 9);
+    if (l == a.tap_layer) tap_copy(a.tap_x_mid, a.x, a.H);
     stage_input(a.x, a.H, ly.post_norm, 0, 0);
     mark(l * 20 + 10);
     project(u + kPrGu, u_lim(u + kPrGu), true, [&](int, int rt, float y) {
@@ -578,6 +600,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
       const StreamShare sd = stream_share(a, u + kPrDown, 0, W, wg);
       stream_wait(a, rg, wave, lane, phase(c + 3), u_lim(u + kPrDown));
       mark(l * 20 + 13);
+      if (l == a.tap_layer) tap_copy(a.tap_act, a.act, a.I);
       stage_input(a.act, a.I, nullptr, sd.r0, sd.r1);
       mark(l * 20 + 14);
       project(u + kPrDown, u_lim(u + kPrDown), false, resid);
@@ -593,8 +616,11 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
   const int u_lm = a.L * kUnitsPerLayer;
   stream_wait(a, rg, wave, lane, phase(cnt_index(a.L - 1, 4)), u_end);
   mark(1000);
+  if (a.L - 1 == a.tap_layer) tap_copy(a.tap_x_out, a.x, a.H);
   stage_input(a.x, a.H, a.final_norm, 0, 0);
   mark(1001);
+  if (a.tap_final_h != nullptr && wg == 0)  // the final RMSNorm, as the LM head applies it
+    for (int i = tid; i < a.H; i += 256) a.tap_final_h[i] = ld_agent(a.x + i) * s_inv * a.final_norm[i];
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   {

@@ -80,6 +80,12 @@ class Decoder:
         binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,
                                     tables, pool, next_ids, logits, taps, layer)
 
+    def stream_step_taps(self, tokens, positions, tables, pool, next_ids, logits, taps, layer):
+        """Batch 1 through the weight-streaming kernel, copying one layer's
+        intermediates out (qd_stream_step_taps)."""
+        binding.qd_stream_step_taps(self.handle, tokens, positions, tables, pool, next_ids,
+                                    logits, taps, layer)
+
     def sample(self, logits, temperature, top_k, top_p, uniform, out_ids) -> None:
         """Sample each sequence's next token on the device (qd_sample)."""
         binding.qd_sample(self.handle, int(logits.shape[0]), logits, temperature, top_k, top_p,

@@ -10,9 +10,15 @@ Two inputs, both CSV directories written by rocprofv3 on the GPU machine:
   factor from counter units to bytes, which then scales every kernel's
   counters into HBM bytes per dispatch.
 
+A third summary reads a counter run of the MFMA metrics (``--pmc MfmaUtil
+MfmaFlopsBF16 SQ_BUSY_CYCLES``: the share of cycles the matrix cores are busy,
+and the bf16 matrix FLOPs per dispatch), with the mean dispatch durations of
+a kernel trace of the same workload, into bf16 MFMA TFLOP/s per class.
+
 Usage (repo root):
   python -m paged_kv_gqa_qwen3_amd.rocprof_summary trace <trace_dir> <prefix> <workload> <out.txt> <command...>
   python -m paged_kv_gqa_qwen3_amd.rocprof_summary traffic <fetch_dir> <write_dir> <workload> <kind> <out_prefix>
+  python -m paged_kv_gqa_qwen3_amd.rocprof_summary mfma <pmc_dir> <trace_dir> <prefix> <workload> <out.txt> <command...>
 """
 from __future__ import annotations
 
@@ -139,11 +145,59 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, kind: str,
     return rec
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def mfma_summary(pmc_dir: str, trace_dir: str, prefix: str, workload: str, out_txt: str,
+                 command: str) -> None:
+    """Per kernel class: mean MfmaUtil (% of matrix-core cycles busy over the
+    dispatch), bf16 MFMA FLOPs per dispatch and, over the class's mean
+    duration in the kernel trace, bf16 MFMA TFLOP/s and its share of the
+    2.5 PFLOP/s dense peak."""
+    path = _one(os.path.join(pmc_dir, "*counter_collection.csv"))
+    rows = list(csv.DictReader(open(path)))
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        c = kernel_class(r["Kernel_Name"])
+        if c is not None:
+            vals[c][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    trace = list(csv.DictReader(open(_one(os.path.join(trace_dir, f"{prefix}_kernel_trace.csv")))))
+    dur = collections.defaultdict(list)
+    for r in trace:
+        c = kernel_class(r["Kernel_Name"])
+        if c is not None:
+            dur[c].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# MFMA activity per dispatch (rocprofv3 --pmc), workload {workload}", "",
+             "commands (repo root, MI355X):", "  " + command, "",
+             "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), in %;",
+             "MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (one 16x16x32 bf16 MFMA = 16384);",
+             "TFLOP/s = MfmaFlopsBF16 / mean duration of the class in the kernel trace.", "",
+             f'{"class":16s} {"dispatches":>10s} {"MfmaUtil_%":>10s} {"GFLOP":>10s} '
+             f'{"mean_us":>9s} {"TFLOP/s":>9s} {"of_peak":>8s} {"SQ_BUSY_Mcyc":>12s}']
+    for c in sorted(vals):
+        v = vals[c]
+        util = v.get("MfmaUtil", [])
+        fl = v.get("MfmaFlopsBF16", [])
+        busy = v.get("SQ_BUSY_CYCLES", [])
+        if not fl:
+            continue
+        mf = sum(fl) / len(fl)
+        mu = sum(util) / len(util) if util else float("nan")
+        sb = sum(busy) / len(busy) / 1e6 if busy else float("nan")
+        d = sum(dur[c]) / len(dur[c]) if dur.get(c) else float("nan")
+        tf = mf / (d * 1e-6) / 1e12 if dur.get(c) else float("nan")
+        lines.append(f"{c:16s} {len(fl):10d} {mu:10.2f} {mf / 1e9:10.2f} {d:9.2f} {tf:9.2f} "
+                     f"{tf / MFMA_BF16_PEAK_TFLOPS:8.4f} {sb:12.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 6 and argv[1] == "trace":
         trace_summary(argv[2], argv[3], argv[4], argv[5], " ".join(argv[6:]))
     elif len(argv) == 7 and argv[1] == "traffic":
         print(json.dumps(traffic_summary(argv[2], argv[3], argv[4], argv[5], argv[6]), indent=1))
+    elif len(argv) >= 7 and argv[1] == "mfma":
+        mfma_summary(argv[2], argv[3], argv[4], argv[5], argv[6], " ".join(argv[7:]))
     else:
         print(__doc__)
         return 2

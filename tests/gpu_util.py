@@ -50,9 +50,12 @@ def gemv_tol(w_bf16: np.ndarray, h: np.ndarray, mfma: bool) -> np.ndarray:
     (K 2^-24 + d) sum_k |w||h|, d covering the input's own rounding (a bf16
     hi/lo pair, 16 significant bits, on the MFMA path; fp32 normalisation
     otherwise)."""
-    K = w_bf16.shape[1]
-    wa = np.abs(oracle.bf16_to_f64(w_bf16))
-    mag = np.abs(np.atleast_2d(h)) @ wa.T
+    N, K = w_bf16.shape
+    ha = np.abs(np.atleast_2d(h))
+    mag = np.empty((ha.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, 16384):  # row blocks: an LM head's |W| is GBs in fp64
+        wa = np.abs(oracle.bf16_to_f64(w_bf16[n0:n0 + 16384]))
+        mag[:, n0:n0 + 16384] = ha @ wa.T
     d = 2.0 ** -15 if mfma else 2.0 ** -20
     return (K * 2.0 ** -24 + d) * mag + 1e-30
 

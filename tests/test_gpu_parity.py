@@ -140,6 +140,10 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
     p = f"model.layers.{layer}."
     t = {k: v.astype(np.float64) for k, v in taps.items()}
 
+    if layer == 0:  # the embedding gather: exactly the tokens' bf16 rows
+        np.testing.assert_array_equal(
+            t["x_in"], oracle.bf16_to_f64(W["model.embed_tokens.weight"][batch.tokens]))
+
     # RMSNorm + fused QKV projection, from the GPU's residual
     h = oracle.rmsnorm(t["x_in"], W[p + "input_layernorm.weight"], eps)
     Wqkv = np.concatenate([W[p + "self_attn.q_proj.weight"], W[p + "self_attn.k_proj.weight"],
@@ -210,13 +214,17 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
         np.testing.assert_array_equal(nxt, np.argmax(logits, axis=1))
 
 
-def _run_stage_checks(torch, shape, W, batch, what):
-    """One step through the taps entry point (per-stage kernels, no graph),
-    stopping at the first and last layer, each stage checked by the oracle
-    from the GPU's own input to it."""
+def _run_stage_checks(torch, shape, W, batch, what, stream=False):
+    """One step through a taps entry point, stopping at the first and last
+    layer, each stage checked by the oracle from the GPU's own input to it:
+    the per-stage kernels (no graph), or with stream=True the batch-1
+    weight-streaming kernel (MFMA tiles on a bf16 pair of the input)."""
     B = batch.tokens.shape[0]
-    mfma = B > 1
-    dec = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False)
+    mfma = B > 1 or stream
+    dec = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False,
+                  persistent=stream)
+    if stream:
+        assert B == 1 and dec.step_path(1) == "stream"
     dec.load_numpy_weights(W)
     QD, KD = shape.q_dim, shape.kv_dim
     for layer in (0, shape.num_layers - 1):
@@ -235,8 +243,9 @@ def _run_stage_checks(torch, shape, W, batch, what):
         }
         logits = torch.zeros(B, shape.vocab, device="cuda")
         nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
-        dec.step_taps(_i32(torch, batch.tokens), _i32(torch, batch.positions),
-                      _i32(torch, batch.block_tables), pool, nxt, logits, taps, layer)
+        run = dec.stream_step_taps if stream else dec.step_taps
+        run(_i32(torch, batch.tokens), _i32(torch, batch.positions),
+            _i32(torch, batch.block_tables), pool, nxt, logits, taps, layer)
         torch.cuda.synchronize()
         tp = {k: v.cpu().numpy() for k, v in taps.items()}
         _stage_checks(shape, W, batch, tp, batch.pool, pool_to_host(pool), layer,
@@ -284,6 +293,28 @@ def test_max_context_stages(torch):
     batch = synth.make_paged_batch(shape, [32767], 1, 92)
     assert batch.max_pages == 2048
     _run_stage_checks(torch, shape, W, batch, "ctx=32767")
+
+
+@pytest.mark.parametrize("ctx", [[0], [15], [16], [40], [700], [2047]])
+def test_tiny_stream_stages(torch, ctx):
+    """The batch-1 weight-streaming kernel, stage by stage (its taps entry
+    point): one split, several, and the longest context a streaming handle
+    takes (128 pages, a combine over 32 splits)."""
+    shape = synth.TINY
+    W = synth.make_weights(shape, 400 + ctx[0] % 13)
+    batch = synth.make_paged_batch(shape, ctx, 1, 401 + ctx[0] % 7)
+    _run_stage_checks(torch, shape, W, batch, f"stream ctx={ctx}", stream=True)
+
+
+def test_full_size_stream_stages(torch):
+    """The headline's kernel at the Qwen3-4B shape, context 512, stage by
+    stage at the first and the last layer (the LM head and argmax included)."""
+    w = synth.WORKLOADS["4b_bs1_ctx512"]
+    shape = w.shape
+    W = _weights(shape, 2)
+    batch = synth.make_paged_batch(shape, synth.context_lengths(w), 2, w.seed)
+    _run_stage_checks(torch, shape, W, batch, "stream 4b ctx=512", stream=True)
+    torch.cuda.empty_cache()
 
 
 # ----------------------------------------------------------------------------- invariances

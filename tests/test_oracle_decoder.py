@@ -6,6 +6,9 @@
   it decodes the same prompt one position at a time through the paged pool.
   This pins the layer wiring (pre-norm residuals, q/k norm before RoPE, KV
   append before attention, causal inclusive context, tied LM head, final norm).
+  ``Oracle.prefill`` is pinned by the same forward: its logits and greedy id
+  are those of the prompt's last position, and the pool it fills holds the
+  same bytes as the step-by-step loop's.
 * With the attention output and MLP output projections zeroed, the residual
   stream is the embedding, so logits reduce to E . rmsnorm(E[t]).
 * Sequences in a batch are independent, and physical page placement does not
@@ -92,6 +95,13 @@ def test_stepwise_paged_decode_equals_causal_forward(tied):
     want = _library_forward(shape, W, prompt)
     scale = np.abs(want).max()
     assert np.abs(got - want).max() <= 1e-10 * scale
+    # Oracle.prefill: the last position's logits and greedy id, the same pool
+    pool_p = _fresh(shape, [0], T, 3, fill=False).pool
+    lg_p, nxt_p = orc.prefill(prompt, batch.block_tables[0], pool_p)
+    assert lg_p.shape == (shape.vocab,)
+    assert np.abs(lg_p - want[-1]).max() <= 1e-10 * scale
+    assert nxt_p == int(np.argmax(want[-1]))
+    np.testing.assert_array_equal(pool_p, batch.pool)
 
 
 def test_zeroed_blocks_reduce_to_embedding_logits():

@@ -214,6 +214,25 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
               const int32_t* top_k, const float* top_p, const float* uniform,
               int32_t* out_ids);
 
+/* qd_sample without a handle and without allocating anything: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments and
+ * results as qd_sample (DEVICE pointers, `batch` rows of `vocab` fp32
+ * logits, 16-byte aligned), plus the vocabulary size and the HIP stream
+ * (a hipStream_t; NULL = null stream) the two sampling launches and one
+ * small fill launch go to.  Scratch is one static device array of ~1.2 MB
+ * per GPU (held until the process ends), sized for batch <= 64 and vocab <=
+ * 262144: larger sizes return QD_EINVAL with a message in qd_last_error(NULL).
+ * Every call on a GPU shares that GPU's array (its counters are cleared at
+ * the start of each call): calls that overlap on one GPU (different streams
+ * or threads) race and must be serialised by the caller.  No hipMalloc,
+ * hipFree or hipMemset is called.  Asynchronous.  QD_EINVAL also for a NULL
+ * or misaligned pointer; QD_EUNSUPPORTED for a vocab too small to chunk;
+ * QD_EHIP on a launch error. */
+int qd_sample_noalloc(int32_t batch, int32_t vocab, const float* logits, const float* temperature,
+                      const int32_t* top_k, const float* top_p, const float* uniform,
+                      int32_t* out_ids, void* hip_stream);
+
 /* Intermediate values of one layer, for checking each stage of the step
  * (fp32 DEVICE buffers; any may be NULL):
  *   x_in [B][H]  qkv [B][(Hq+2Hkv)D]  q_rot [B][Hq][D]  k_rot [B][Hkv][D]

@@ -30,7 +30,7 @@ QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
 EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_decode_step_taps",
-            "qd_stream_step_taps", "qd_read_ceiling",
+            "qd_stream_step_taps", "qd_read_ceiling", "qd_sample_noalloc",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
             "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
             "qd_blocks_create", "qd_blocks_destroy", "qd_blocks_add", "qd_blocks_reserve",
@@ -94,6 +94,8 @@ def load_library():
                                             ctypes.POINTER(QdTaps)]
         lib.qd_stream_step_taps.restype = ctypes.c_int
         lib.qd_stream_step_taps.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(QdTaps)]
+        lib.qd_sample_noalloc.restype = ctypes.c_int
+        lib.qd_sample_noalloc.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P]
         lib.qd_read_ceiling.restype = ctypes.c_int
         lib.qd_read_ceiling.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P,
                                         ctypes.POINTER(ctypes.c_float)]
@@ -218,6 +220,14 @@ def qd_stream_step_taps(handle: int, token_ids, positions, block_tables, kv_pool
     _check(lib.qd_stream_step_taps(handle, _ptr(token_ids), _ptr(positions), _ptr(block_tables),
                                    _ptr(kv_pool), _ptr(out_next_ids), _ptr(out_logits),
                                    ctypes.byref(tp) if tp else None), handle)
+
+
+def qd_sample_noalloc(batch: int, vocab: int, logits, temperature, top_k, top_p, uniform,
+                      out_ids, stream: Optional[int] = None) -> None:
+    """qd_sample without a handle; scratch is the library's static device array."""
+    lib = load_library()
+    _check(lib.qd_sample_noalloc(batch, vocab, _ptr(logits), _ptr(temperature), _ptr(top_k),
+                                 _ptr(top_p), _ptr(uniform), _ptr(out_ids), stream), None)
 
 
 def qd_read_ceiling(buf, nbytes: int, reps: int, stream: Optional[int] = None) -> float:

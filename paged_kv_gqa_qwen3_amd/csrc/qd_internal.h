@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace qd {
 
 // Packed weight layout ("tile-major").  A [N][K] bf16 matrix is stored as
@@ -263,6 +265,10 @@ size_t stream_lds_bytes(int head_dim, int group, int in_floats, int rt_max);
 hipError_t stream_max_grid(int head_dim, int group, size_t lds, int num_cus, int* grid);
 hipError_t launch_stream(const StreamArgs& a, int head_dim, int group, int grid, size_t lds,
                          hipStream_t s);
+
+// Records msg as the error qd_last_error(NULL) reports (entry points without
+// a handle); returns code.
+int set_global_error(int code, const std::string& msg);
 
 // Plain streaming read of the first bytes/1024 KB of src (measurement).
 hipError_t launch_read_ceiling(const void* src, size_t bytes, int grid, hipStream_t s);

@@ -614,6 +614,11 @@ int check_step_args(qd_handle* h, int32_t batch, const void* a, const void* b, c
 
 }  // namespace
 
+int qd::set_global_error(int code, const std::string& msg) {
+  g_create_error = msg;
+  return code;
+}
+
 extern "C" {
 
 int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {

@@ -44,6 +44,9 @@
 // recomputes the weights it needs.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <string>
+
 #include "qd_device.h"
 
 namespace qd {
@@ -717,4 +720,103 @@ hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ no-allocation entry point
+
+// qd_sample_noalloc runs the same two launches with its scratch in one
+// file-scope device array instead of a handle's buffers, so that callers
+// that cannot allocate (code under graph capture, tight serving loops) can
+// sample.  The array is sized for batch <= kNoAllocBatch and vocab <=
+// kNoAllocVocab and carved at fixed 256-byte aligned offsets (strides of the
+// largest batch and chunk count).  Each GPU holds its own copy until the
+// process ends; in host code its address is taken once per device with
+// hipGetSymbolAddress (the array's name is not a device address there).
+constexpr int kNoAllocBatch = 64;
+constexpr int kNoAllocVocab = 262144;
+constexpr int kNoAllocChunks = (kNoAllocVocab + kSampleChunk - 1) / kSampleChunk;
+constexpr size_t na_align(size_t x) { return (x + 255) / 256 * 256; }
+constexpr size_t kNaSlots = (size_t)kNoAllocBatch * kNoAllocChunks;
+constexpr size_t kNaMax = 0;                                             // float [B][G]
+constexpr size_t kNaIdx = kNaMax + na_align(kNaSlots * 4);               // int [B][G]
+constexpr size_t kNaCand = kNaIdx + na_align(kNaSlots * 4);              // u64 [B][G][64]
+constexpr size_t kNaSum = kNaCand + na_align(kNaSlots * 64 * 8);         // double [B][G]
+// (counters, second counters and row histograms are contiguous: one fill
+// clears them at the start of every call)
+constexpr size_t kNaCnt = kNaSum + na_align(kNaSlots * 8);               // u32 [B][kCntStride]
+constexpr size_t kNaCnt2 = kNaCnt + na_align((size_t)kNoAllocBatch * kCntStride * 4);
+constexpr size_t kNaHist = kNaCnt2 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
+constexpr size_t kNaBytes = kNaHist + na_align((size_t)kNoAllocBatch * 256 * 8);  // ~1.2 MB
+
+static __device__ __align__(256) unsigned char scratch[kNaBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_na_mutex;
+unsigned char* g_na_ptr[kMaxDevices];
+
+// The device address of this device's copy of `scratch` (looked up once per
+// device, with the device current), or null with the error in *e.
+unsigned char* noalloc_scratch(int dev, hipError_t* e) {
+  std::lock_guard<std::mutex> lock(g_na_mutex);
+  if (g_na_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    *e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*e != hipSuccess) return nullptr;
+    g_na_ptr[dev] = static_cast<unsigned char*>(ptr);
+  }
+  return g_na_ptr[dev];
+}
+}  // namespace
+
 }  // namespace qd
+
+extern "C" int qd_sample_noalloc(int32_t batch, int32_t vocab, const float* logits,
+                                 const float* temperature, const int32_t* top_k,
+                                 const float* top_p, const float* uniform, int32_t* out_ids,
+                                 void* hip_stream) {
+  using namespace qd;
+  if (!logits || !temperature || !top_k || !top_p || !uniform || !out_ids)
+    return set_global_error(QD_EINVAL, "qd_sample_noalloc: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(logits) % 16)
+    return set_global_error(QD_EINVAL, "qd_sample_noalloc: logits must be 16-byte aligned");
+  if (batch < 1 || batch > kNoAllocBatch)
+    return set_global_error(QD_EINVAL,
+                            "qd_sample_noalloc: batch must be in 1..64 (the static scratch's limit)");
+  if (vocab < 64 || vocab > kNoAllocVocab)
+    return set_global_error(QD_EINVAL,
+                            "qd_sample_noalloc: vocab must be in 64..262144 (the static scratch's limit)");
+  int G = 1, C = 0;
+  sample_split(vocab, &G, &C);
+  if ((size_t)G * 512 > (size_t)C * 4)  // the merge reuses a chunk's LDS
+    return set_global_error(QD_EUNSUPPORTED, "qd_sample_noalloc: vocab too small to chunk");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_global_error(QD_EHIP, "qd_sample_noalloc: no usable current device");
+  unsigned char* p = noalloc_scratch(dev, &e);
+  if (p == nullptr)
+    return set_global_error(QD_EHIP, std::string("qd_sample_noalloc: hipGetSymbolAddress: ") +
+                                         hipGetErrorString(e));
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  // counters and row histograms start at zero in every call (a fill kernel,
+  // so the call can be captured into a graph)
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s,
+                     reinterpret_cast<unsigned*>(p + kNaCnt), (kNaBytes - kNaCnt) / 4);
+  e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_global_error(QD_EHIP, std::string("qd_sample_noalloc: ") + hipGetErrorString(e));
+  SampleArgs a{logits, vocab, temperature, top_k, top_p, uniform, out_ids, G, C,
+               reinterpret_cast<float*>(p + kNaMax), reinterpret_cast<int*>(p + kNaIdx),
+               reinterpret_cast<unsigned long long*>(p + kNaCand),
+               reinterpret_cast<unsigned*>(p + kNaCnt), reinterpret_cast<double*>(p + kNaSum),
+               reinterpret_cast<unsigned*>(p + kNaCnt2), reinterpret_cast<double*>(p + kNaHist)};
+  e = launch_sample(a, batch, s);
+  if (e != hipSuccess)
+    return set_global_error(QD_EHIP, std::string("qd_sample_noalloc: ") + hipGetErrorString(e));
+  return QD_OK;
+}

@@ -30,11 +30,13 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   return (unsigned short)(u >> 16);
 }
 
-// bf16 hi/lo pair of v (hi = bf16(v), lo = bf16(v - hi)).
+// bf16 hi/lo pair of v (hi = bf16(v), lo = bf16(v - hi)), stored with agent
+// scope: a consumer may run in the same launch, on another XCD.
 __device__ __forceinline__ void split_hilo(float v, uint16_t* hi, uint16_t* lo, size_t i) {
   const unsigned h = f2bf(v);
-  hi[i] = (uint16_t)h;
-  lo[i] = (uint16_t)f2bf(v - __uint_as_float(h << 16));
+  __hip_atomic_store(hi + i, (uint16_t)h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(lo + i, (uint16_t)f2bf(v - __uint_as_float(h << 16)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Cache-policy operand of a device-scope load (sc1): the data was written by
@@ -222,6 +224,40 @@ struct NoWait {
   __device__ void operator()() const {}
 };
 
+// Bounded poll (thread 0; the workgroup then proceeds together) until the
+// counter reaches target; past `limit` polls it records QD_DEV_TIMEOUT and
+// gives up (the results are then invalid, but the launch drains).
+__device__ __forceinline__ void poll_counter(const unsigned* c, unsigned target, int* dev_flags,
+                                             unsigned limit) {
+  unsigned k = 0;
+  while (ld_agent(c) < target) {
+    if (++k > limit) {
+      set_flag(dev_flags, QD_DEV_TIMEOUT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The wait of an item of a fused launch whose inputs come from items of the
+// same launch: n completion counters (kCntStride apart) must each reach
+// target.  Producers sit at lower workgroup indices, which are dispatched
+// first, so a waiting workgroup only waits for running or finished ones.
+struct CounterWait {
+  static constexpr bool kInLaunch = true;
+  const unsigned* cnt;
+  int n;
+  unsigned target;
+  int* dev_flags;
+  unsigned limit;
+  __device__ void operator()() const {
+    if (threadIdx.x == 0)
+      for (int i = 0; i < n; ++i) poll_counter(cnt + (size_t)i * kCntStride, target, dev_flags, limit);
+    __syncthreads();
+  }
+};
+
+
 // ------------------------------------------------------------------ embedding
 
 // x[b] = E[token_b] (exact bf16 -> fp32), read from the packed table, plus
@@ -230,6 +266,8 @@ struct NoWait {
 // pair of x times its RMSNorm gain.
 __device__ inline void embed_item(const EmbedArgs& a, const Done& done, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (b == 0 && a.zero != nullptr)
+    for (int i = threadIdx.x; i < a.nzero; i += blockDim.x) st_agent(a.zero + (size_t)i * kCntStride, 0u);
   int tok = a.tokens[b];
   if (tok < 0 || tok >= a.V) {
     if (threadIdx.x == 0) set_flag(a.dev_flags, QD_DEV_BAD_TOKEN);
@@ -345,11 +383,19 @@ template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait>
 __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const float* gain,
                                  const Done& done, int item, unsigned char* smem,
                                  const Wait& wait) {
+#ifdef QD_STEP_TRACE
+  auto mark = [&](int e) {
+    if (a.trace != nullptr && threadIdx.x == 0 && item < kTraceItems)
+      a.trace[(size_t)item * 8 + e] = __builtin_amdgcn_s_memrealtime();
+  };
+#else
+  auto mark = [](int) {};
+#endif
+  mark(0);
   constexpr bool kMfma = NB >= 8;
   constexpr bool kSplitCols = NB == 8;  // hi and lo side by side in one operand
   constexpr bool kAgent = Wait::kInLaunch;
   constexpr int NCB = kMfma && !kSplitCols ? NB / 16 : 1;
-  static_assert(!kMfma || !kAgent, "the MFMA path reads inputs of an earlier launch");
   float* s_inv = reinterpret_cast<float*>(smem);
   float* s_ssq = s_inv + kMaxBatch;
   float* s_res = s_ssq + 256;
@@ -371,16 +417,21 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   const int kw0 = kt0 + min(kph, nk - 1);  // first k-tile of this wave
   const u32x4* wp = reinterpret_cast<const u32x4*>(w) +
                     ((size_t)(rg * RT + tj) * KT + kw0) * 64 + lane;
-  const size_t wstep = (size_t)WS * 64;
 
-  // MFMA path: the input slice (written by an earlier launch) is loaded
-  // first, up to kStageLoads 16-byte pieces per thread in flight together,
-  // so that staging does not wait behind the weight tiles (loads complete
-  // in order) one piece at a time; further pieces are copied after them.
-  // (12 pieces cost a third workgroup per CU in registers: batch 8 and 16
-  // took 3.50 and 4.22 ms per step; 8 pieces 3.16 and 3.88; 6 pieces 3.15
-  // and 3.94; the one-piece loop 3.19 and 3.94.)
+  // Loads go out in the order their data is needed, so that waiting for
+  // one never waits for a later one (a wave's loads complete in issue
+  // order): the input slice, the RMSNorm sums of squares, then the first CH
+  // weight tiles.  When the input is produced in the same launch (kAgent:
+  // a fused launch), the weight tiles go out first and the input only
+  // after the wait, with device-scope loads.
+  //
+  // MFMA path: up to kStageLoads 16-byte pieces of the input slice per
+  // thread in registers (12 pieces cost a third workgroup per CU in
+  // registers: batch 8 and 16 took 3.50 and 4.22 ms per step against 3.16
+  // and 3.88 with 8); further pieces are copied after the weight tiles.
+  // VALU path: up to kValuPre 4-float groups of the input and of the gain.
   constexpr int kStageLoads = 8;
+  constexpr int kValuPre = 2;
   const int K8 = Ks / 8, n_in = kMfma ? B * K8 : 0;
   u32x4 inb[kMfma ? kStageLoads : 1];
   auto in_src = [&](int idx) {
@@ -393,46 +444,87 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     const int b = rem / K8, c = (rem - b * K8) * 8;
     return hl * NB * (Ks + 8) + b * (Ks + 8) + c;
   };
-  if constexpr (kMfma) {
+  const int K4 = Ks / 4, n_v4 = kMfma ? 0 : B * K4;  // VALU: 4-float groups of the slice
+  f32x4 xpre[kMfma ? 1 : kValuPre], gpre[kMfma ? 1 : kValuPre];
+  const bool norm = a.ssq != nullptr;
+  // device-scope 16-byte loads of in-launch input pieces
+  const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.xh), 0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.xl), 0, 0x7fffffff, kBufferWord3);
+  auto in_load = [&](int idx) -> u32x4 {
+    if constexpr (!kAgent) return *reinterpret_cast<const u32x4*>(in_src(idx));
+    const int hl = idx >= n_in, rem = idx - hl * n_in;
+    const int b = rem / K8, c = (rem - b * K8) * 8;
+    const int off = (b * a.K + kt0 * kTileCols + c) * 2;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hl ? rs_lo : rs_hi, off,
+                                                                           0, kDeviceScope));
+  };
+  if constexpr (kAgent) {
+    // (issued after the wait below)
+  } else if constexpr (kMfma) {
 #pragma unroll
     for (int j = 0; j < kStageLoads; ++j) {
       const int idx = tid + j * 256;
-      if (idx < 2 * n_in) inb[j] = *reinterpret_cast<const u32x4*>(in_src(idx));
+      if (idx < 2 * n_in) inb[j] = in_load(idx);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kValuPre; ++j) {
+      const int g4 = tid + j * 256;
+      if (g4 < n_v4) {
+        const int b = g4 / K4, c = (g4 - b * K4) * 4;
+        xpre[j] = *reinterpret_cast<const f32x4*>(a.x + (size_t)b * a.K + kt0 * kTileCols + c);
+        if (norm) gpre[j] = *reinterpret_cast<const f32x4*>(gain + kt0 * kTileCols + c);
+      }
     }
   }
 
-  // Every load is issued unconditionally (tile index clamped to the wave's
-  // range) so that the loads stay in flight together; only compute is guarded.
-  u32x4 wbuf[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i)
-    wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(i, lastw) * wstep);
-
-  wait();
-  __syncthreads();  // LDS of the previous item is free
-
   // RMSNorm sums of squares: one partial per 16 rows of the producer,
   // [K/16][Bmax].  Thread t adds batch column t % NB's partials t / NB,
-  // t / NB + 256/NB, ... in order, 16 loads in flight, the first batch
-  // issued before the input is staged; the 256/NB parts are then added in
-  // order.
-  const bool norm = a.ssq != nullptr;
+  // t / NB + 256/NB, ... in order (kSsq loads in flight: hidden sizes up
+  // to 16 * kSsq * 256/NB; beyond that the rest after the weight tiles);
+  // the 256/NB parts are then added in order.
   constexpr int kParts = 256 / NB;
+  constexpr int kSsq = NB >= 16 ? 16 : 8;
   const int ng = a.K / kSsqRows;
   const int sb = tid % NB, sp = tid / NB;
-  float sv[16];
-  if (norm) {
+  float sv[kSsq];
+  auto load_ssq = [&](int g0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      sv[j] = ld_in<kAgent>(a.ssq + (size_t)min(sp + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1));
+    for (int j = 0; j < kSsq; ++j)
+      sv[j] = ld_in<kAgent>(a.ssq + (size_t)min(g0 + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1));
+  };
+  if (norm && !kAgent) load_ssq(sp);
+
+  // Weight tiles: every load is issued unconditionally (tile index clamped
+  // to the wave's range) so that the loads stay in flight together; only
+  // compute is guarded.  Offsets in 32 bits (a wave's tiles lie within one
+  // projection).
+  const unsigned wstep = (unsigned)WS * 64u;
+  auto wtile = [&](int i) { return wp + (unsigned)min(i, lastw) * wstep; };
+  u32x4 wbuf[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) wbuf[i] = __builtin_nontemporal_load(wtile(i));
+
+  wait();
+  mark(1);
+  if constexpr (kAgent) {
+    if (norm) load_ssq(sp);
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int j = 0; j < kStageLoads; ++j) {
+        const int idx = tid + j * 256;
+        if (idx < 2 * n_in) inb[j] = in_load(idx);
+      }
+    }
   }
 
-  // Stage the input slice, 8 consecutive columns per thread and step.
+  // Stage the input slice: MFMA, the pairs of the B live columns, hi rows
+  // first, then lo rows (LDS columns B..NB-1 keep whatever they held: they
+  // only feed outputs that are never stored); VALU, x times the gain.
   const int P = kMfma ? Ks + 8 : Ks;
   if constexpr (kMfma) {
-    // the pairs of the B live columns, hi rows first, then lo rows (LDS
-    // columns B..NB-1 keep whatever they held: they only feed outputs that
-    // are never stored)
     unsigned short* xs = reinterpret_cast<unsigned short*>(xs_base);
 #pragma unroll
     for (int j = 0; j < kStageLoads; ++j) {
@@ -440,32 +532,33 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       if (idx < 2 * n_in) *reinterpret_cast<u32x4*>(xs + in_dst(idx)) = inb[j];
     }
     for (int idx = tid + kStageLoads * 256; idx < 2 * n_in; idx += 256)
-      *reinterpret_cast<u32x4*>(xs + in_dst(idx)) = *reinterpret_cast<const u32x4*>(in_src(idx));
+      *reinterpret_cast<u32x4*>(xs + in_dst(idx)) = in_load(idx);
   } else {
     const float* grow = gain + kt0 * kTileCols;
-    for (int idx = tid; idx < B * K8; idx += 256) {
-      const int b = idx / K8, c = (idx - b * K8) * 8;
-      const float* xp = a.x + (size_t)b * a.K + kt0 * kTileCols + c;
-      f32x4 v0 = ld_in4<kAgent>(xp), v1 = ld_in4<kAgent>(xp + 4);
-      if (norm) {
-        v0 *= *reinterpret_cast<const f32x4*>(grow + c);
-        v1 *= *reinterpret_cast<const f32x4*>(grow + c + 4);
+#pragma unroll
+    for (int j = 0; j < kValuPre; ++j) {
+      const int g4 = tid + j * 256;
+      if (!kAgent && g4 < n_v4) {
+        const int b = g4 / K4, c = (g4 - b * K4) * 4;
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(xs_base) + b * P + c) =
+            norm ? xpre[j] * gpre[j] : xpre[j];
       }
-      float* xs = reinterpret_cast<float*>(xs_base) + b * P + c;
-      *reinterpret_cast<f32x4*>(xs) = v0;
-      *reinterpret_cast<f32x4*>(xs + 4) = v1;
+    }
+    for (int g4 = tid + (kAgent ? 0 : kValuPre * 256); g4 < n_v4; g4 += 256) {
+      const int b = g4 / K4, c = (g4 - b * K4) * 4;
+      f32x4 v = ld_in4<kAgent>(a.x + (size_t)b * a.K + kt0 * kTileCols + c);
+      if (norm) v *= *reinterpret_cast<const f32x4*>(grow + c);
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(xs_base) + b * P + c) = v;
     }
   }
   if (norm) {
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;
-    for (int g0 = sp + 16 * kParts; g0 < ng; g0 += 16 * kParts) {
+    for (int j = 0; j < kSsq; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;
+    for (int g0 = sp + kSsq * kParts; g0 < ng; g0 += kSsq * kParts) {
+      load_ssq(g0);
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        sv[j] = ld_in<kAgent>(a.ssq + (size_t)min(g0 + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1));
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ss += g0 + j * kParts < ng ? sv[j] : 0.f;
+      for (int j = 0; j < kSsq; ++j) ss += g0 + j * kParts < ng ? sv[j] : 0.f;
     }
     s_ssq[tid] = ss;
   }
@@ -476,68 +569,131 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     s_inv[tid] = rsqrtf(ss / (float)a.K + a.eps);
   }
   __syncthreads();
+  mark(2);
 
-  float acc_v[kMfma ? 1 : NB];
-  f32x4 acc_m[NCB];
+  // Tiles are consumed in batches of KB: the batch's input operands are
+  // read from LDS first, then its MFMAs (or FMAs) run on KB independent
+  // accumulators, so neither the LDS round trip nor the accumulation chain
+  // is paid per tile; each consumed tile's registers are refilled with the
+  // tile CH ahead at once.
+  constexpr int KB = kSplitCols ? 4 : kMfma ? (NCB == 1 ? 2 : 1) : 2;
+  static_assert(CH % KB == 0, "whole batches of tiles in flight");
+  float acc_v[KB][kMfma ? 1 : NB];
+  f32x4 acc_m[KB][NCB];
 #pragma unroll
-  for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[b] = 0.f;
+  for (int q = 0; q < KB; ++q) {
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) acc_m[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[q][b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) acc_m[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // wave-local tile i is k-tile kph + WS*i of the item's slice
-  auto compute = [&](const u32x4& wv, int i) {
+  const unsigned short* xsh = reinterpret_cast<const unsigned short*>(xs_base);
+  const float* xsf = reinterpret_cast<const float*>(xs_base);
+  struct BIn { u32x4 h[NCB], l[NCB]; f32x4 f0[NB], f1[NB]; };
+  auto read_in = [&](int i, BIn& bi) {
     const int t = kph + WS * i;
     if constexpr (kSplitCols) {
       // LDS rows 0..7 hold the hi halves, 8..15 the lo halves: operand
       // column (lane % 16) reads row lane % 16
-      const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(
-          xs + (lane & 15) * P + t * kTileCols + (lane >> 4) * 8);
-      acc_m[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, xv), acc_m[0], 0, 0, 0);
+      bi.h[0] = *reinterpret_cast<const u32x4*>(xsh + (lane & 15) * P + t * kTileCols +
+                                                (lane >> 4) * 8);
     } else if constexpr (kMfma) {
-      const unsigned short* xs = reinterpret_cast<const unsigned short*>(xs_base);
-      const bf16x8 wa = __builtin_bit_cast(bf16x8, wv);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int off = (cb * 16 + (lane & 15)) * P + t * kTileCols + (lane >> 4) * 8;
-        const u32x4 xh = *reinterpret_cast<const u32x4*>(xs + off);
-        const u32x4 xl = *reinterpret_cast<const u32x4*>(xs + NB * P + off);
-        acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wa, __builtin_bit_cast(bf16x8, xh), acc_m[cb], 0, 0, 0);
-        acc_m[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wa, __builtin_bit_cast(bf16x8, xl), acc_m[cb], 0, 0, 0);
+        bi.h[cb] = *reinterpret_cast<const u32x4*>(xsh + off);
+        bi.l[cb] = *reinterpret_cast<const u32x4*>(xsh + NB * P + off);
       }
     } else {
-      const float* xs =
-          reinterpret_cast<const float*>(xs_base) + t * kTileCols + (lane >> 4) * 8;
+      const float* xp = xsf + t * kTileCols + (lane >> 4) * 8;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        bi.f0[b] = *reinterpret_cast<const f32x4*>(xp + b * P);
+        bi.f1[b] = *reinterpret_cast<const f32x4*>(xp + b * P + 4);
+      }
+    }
+  };
+  auto mac = [&](const u32x4& wv, const BIn& bi, int q) {
+    if constexpr (kSplitCols) {
+      acc_m[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, wv), __builtin_bit_cast(bf16x8, bi.h[0]), acc_m[q][0], 0, 0, 0);
+    } else if constexpr (kMfma) {
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, wv);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        acc_m[q][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wa, __builtin_bit_cast(bf16x8, bi.h[cb]), acc_m[q][cb], 0, 0, 0);
+        acc_m[q][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wa, __builtin_bit_cast(bf16x8, bi.l[cb]), acc_m[q][cb], 0, 0, 0);
+      }
+    } else {
       float wf[8];
       unpack8(wv, wf);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + b * P);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + b * P + 4);
-        float acc = acc_v[b];
-        acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc);
-        acc = fmaf(wf[2], x0.z, acc); acc = fmaf(wf[3], x0.w, acc);
-        acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
-        acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
-        acc_v[b] = acc;
+        float acc = acc_v[q][b];
+        acc = fmaf(wf[0], bi.f0[b].x, acc); acc = fmaf(wf[1], bi.f0[b].y, acc);
+        acc = fmaf(wf[2], bi.f0[b].z, acc); acc = fmaf(wf[3], bi.f0[b].w, acc);
+        acc = fmaf(wf[4], bi.f1[b].x, acc); acc = fmaf(wf[5], bi.f1[b].y, acc);
+        acc = fmaf(wf[6], bi.f1[b].z, acc); acc = fmaf(wf[7], bi.f1[b].w, acc);
+        acc_v[q][b] = acc;
       }
     }
   };
-  // steady state: consume a tile, refill its registers with the tile CH ahead
+  // steady state: consume a batch, refill its registers with the tiles CH ahead
   int c0 = 0;
   for (; c0 + CH < nkw; c0 += CH) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      compute(wbuf[i], c0 + i);
-      wbuf[i] = __builtin_nontemporal_load(wp + (size_t)min(c0 + CH + i, lastw) * wstep);
+    for (int i0 = 0; i0 < CH; i0 += KB) {
+      BIn bi[KB];
+#pragma unroll
+      for (int q = 0; q < KB; ++q) read_in(c0 + i0 + q, bi[q]);
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        mac(wbuf[i0 + q], bi[q], q);
+        wbuf[i0 + q] = __builtin_nontemporal_load(wtile(c0 + CH + i0 + q));
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < CH; ++i)
-    if (c0 + i < nkw) compute(wbuf[i], c0 + i);
+  for (int i0 = 0; i0 < CH; i0 += KB) {
+    if (c0 + i0 >= nkw) break;
+    BIn bi[KB];
+#pragma unroll
+    for (int q = 0; q < KB; ++q) read_in(min(c0 + i0 + q, nkw - 1), bi[q]);
+#pragma unroll
+    for (int q = 0; q < KB; ++q)
+      if (c0 + i0 + q < nkw) mac(wbuf[i0 + q], bi[q], q);
+  }
+  // the batch accumulators, added in a fixed order
+#pragma unroll
+  for (int q = 1; q < KB; ++q) {
+#pragma unroll
+    for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[0][b] += acc_v[q][b];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) acc_m[0][c] += acc_m[q][c];
+  }
+
+  // The residual epilogue's old residual and the next consumer's gain
+  // (thread: outputs idx = tid + 256 j, idx = b * rows + r), loaded while
+  // the waves' results are reduced.  Every split fetches them; only the one
+  // that finishes the row group uses them.
+  constexpr int kXold = (kRowsPerGroup * NB + 255) / 256;
+  float x_old[kXold], xo_g[kXold];
+  if constexpr (MODE == kResid) {
+#pragma unroll
+    for (int j = 0; j < kXold; ++j) {
+      const int idx = tid + j * 256;
+      if (idx < rows * B) {
+        const size_t n = (size_t)rg * rows + idx % rows;
+        x_old[j] = (a.res_in != nullptr ? a.res_in : a.out)[(size_t)(idx / rows) * a.N + n];
+        xo_g[j] = a.xo_hi != nullptr ? a.xo_gain[n] : 0.f;
+      }
+    }
+  }
+  mark(3);
 
   // Per-wave results (times 1/rms of the batch column under RMSNorm) ->
   // s_res slot `wave` = [16 rows][NB]; then the waves of a row tile are
@@ -547,7 +703,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     // column c < 8 (hi) plus its partner c + 8 (lo), lane ^ 8
     f32x4 tot;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tot[r] = acc_m[0][r] + __shfl_xor(acc_m[0][r], 8);
+    for (int r = 0; r < 4; ++r) tot[r] = acc_m[0][0][r] + __shfl_xor(acc_m[0][0][r], 8);
     const int col = lane & 15;
     if (col < 8) {
       const float sc = norm && col < B ? s_inv[col] : 1.f;
@@ -562,12 +718,12 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       const float sc = norm && col < B ? s_inv[col] : 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = acc_m[cb][r] * sc;
+        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = acc_m[0][cb][r] * sc;
     }
   } else {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      float v = acc_v[b];
+      float v = acc_v[0][b];
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
       if (norm && b < B) v *= s_inv[b];
@@ -583,6 +739,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     __syncthreads();
   }
+  mark(4);
 
   if constexpr (MODE == kPartial) {
     // leave the partial for the consumer, which sums the S splits itself
@@ -591,20 +748,9 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       const int r = idx / B, b = idx - r * B;
       st_agent(mine + idx, s_res[r * NB + b]);
     }
+    mark(7);
     signal_done(done);
     return;
-  }
-  // residual epilogue: every split fetches the old residual of its rows now,
-  // so the one that finishes the row group need not wait for it
-  constexpr int kXold = (kRowsPerGroup * NB + 255) / 256;
-  float x_old[kXold];
-  if constexpr (MODE == kResid) {
-#pragma unroll
-    for (int j = 0; j < kXold; ++j) {
-      const int idx = tid + j * 256;  // = b * rows + r
-      if (idx < rows * B) x_old[j] = ld_in<kAgent>(a.out + (size_t)(idx / rows) * a.N +
-                                                     (size_t)rg * rows + idx % rows);
-    }
   }
   if (S > 1) {
     float* mine = a.part + (size_t)(rg * S + s) * rows * B;
@@ -613,6 +759,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       st_agent(mine + idx, s_res[r * NB + b]);
     }
     if (!arrive_last(&a.counters[(size_t)rg * kCntStride], (unsigned)S, s_flag)) return;
+    mark(5);
     // sum the S partials of each output in split order; a thread keeps 4
     // outputs x 8 splits of loads in flight (indices clamped, extras unused)
     const float* all = a.part + (size_t)rg * S * rows * B;
@@ -643,6 +790,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     if (tid == 0) reset_counter(&a.counters[(size_t)rg * kCntStride]);
     __syncthreads();
+    mark(6);
   }
 
   const int N = a.N;
@@ -652,6 +800,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       const int b = idx / rows, r = idx - b * rows;
       st_agent(a.out + (size_t)b * N + row0 + r, s_res[r * NB + b]);
     }
+    mark(7);
     signal_done(done);
   } else if constexpr (MODE == kResid) {
     // new residual, its sums of squares over groups of 16 rows (a group of
@@ -667,12 +816,13 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
         xv = x_old[j] + s_res[r * NB + b];
         st_agent(a.out + (size_t)b * N + row0 + r, xv);
         if (a.xo_hi != nullptr)
-          split_hilo(xv * a.xo_gain[row0 + r], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
+          split_hilo(xv * xo_g[j], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
       }
       const float ss = group_sum(xv * xv, kSsqRows);
       if (ok && r % kSsqRows == 0)
         st_agent(a.ssq_out + ((row0 + r) / kSsqRows) * a.Bmax + b, ss);
     }
+    mark(7);
     signal_done(done);
   } else if constexpr (MODE == kSwiGLU) {
     // row tile j of the item: gate rows 0-7, the matching up rows 8-15
@@ -687,6 +837,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       st_agent(a.out + o, sv * uv);
       if (a.xo_hi != nullptr) split_hilo(sv * uv, a.xo_hi, a.xo_lo, o);
     }
+    mark(7);
     signal_done(done);
   } else {  // kArgmax, rows == 64
     if (a.logits != nullptr) {
@@ -853,6 +1004,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   const int u = item - __shfl(list.first, b);
   const int g = u % Hkv, s = u / Hkv;
   const int ctx = pos + 1;
+
   const int npages = (ctx + kPage - 1) / kPage;
   const int* bt = a.block_tables + (size_t)b * a.max_pages;
   const size_t head_stride = (size_t)kPage * D;  // one (page, K|V, head) tile

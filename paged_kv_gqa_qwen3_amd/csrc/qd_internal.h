@@ -28,6 +28,7 @@ constexpr int kPage = 16;                          // tokens per KV page
 constexpr int kMaxBatch = 64;
 constexpr int kMaxTilesInFlight = 20;              // weight tiles a wave keeps in flight
 constexpr int kSsqRows = 16;    // rows per partial sum of squares of the residual stream
+constexpr int kTraceItems = 4096;  // (trace builds) items with event slots per launch
 constexpr int kCntStride = 32;  // words between arrival counters: one 128-byte line each
                                 // (atomics on one line serialise at the memory side)
 
@@ -64,6 +65,8 @@ struct GemvArgs {
   float* part;         // split-K partials [items][16*rt][B] (kPartial: the consumer's input)
   unsigned* counters;  // [N/(16*rt)] split-K arrival counters, kCntStride apart (zero between uses)
   float* out;          // kStore: [B][N]; kResid: x [B][N]; kSwiGLU: [B][N/2]
+  const float* res_in; // kResid: the old residual [B][N] if not out (fused launches
+                       // write the new residual to another buffer)
   float* ssq_out;      // kResid: [N/16][Bmax]
   uint16_t* xo_hi;     // kResid, kSwiGLU: if non-null, also the bf16 pairs [64][cols] of the
   uint16_t* xo_lo;     // output (kResid: times xo_gain) for an MFMA consumer
@@ -75,6 +78,7 @@ struct GemvArgs {
   int* amax_idx2;
   unsigned* amax_counter;  // kArgmax: ceil(N/64/64) + 1 counters, kCntStride apart
   int* next_ids;       // kArgmax: [B]
+  unsigned long long* trace;  // builds with QD_STEP_TRACE only: 8 event timestamps per item, or null
 };
 
 struct AttnArgs {
@@ -119,6 +123,26 @@ struct EmbedArgs {
   uint16_t* xo_lo;
   const float* xo_gain;
   int* dev_flags;
+  unsigned* zero;          // if non-null: counters (kCntStride apart) the first row clears
+  int nzero;
+};
+
+// The MLP half of a layer as one launch at batches 2-16 (MFMA items):
+// [gate/up items | down items].  A finished gate/up row group counts in
+// cnt_g[the K slice of down its SwiGLU channels feed] (kCntStride apart);
+// a down item issues its weight tiles, then waits until its slice's count
+// is complete, so that down's weights stream while gate/up finishes.
+// Gate/up items sit at lower workgroup indices, which are dispatched first:
+// a waiting down item only waits for running or finished ones.  The launch
+// clears the counters it does not use (cnt_other) for the next one.
+struct FusedMlpArgs {
+  GemvArgs gu, d;      // gate/up (kSwiGLU) and down (kResid)
+  int ng, nd;
+  unsigned* cnt_g;     // [down K slices]
+  unsigned* cnt_other; // the next launch's counters, cleared here: [n_other]
+  int n_other;
+  int* dev_flags;
+  unsigned spin_limit;
 };
 
 // Per-layer pointers for the streaming step kernel (device-resident array).
@@ -272,6 +296,10 @@ int set_global_error(int code, const std::string& msg);
 
 // Plain streaming read of the first bytes/1024 KB of src (measurement).
 hipError_t launch_read_ceiling(const void* src, size_t bytes, int grid, hipStream_t s);
+
+// The fused MLP launch (batches 2-16).
+bool fused_supported(int B);
+hipError_t launch_fused_mlp(const FusedMlpArgs& a, size_t lds, hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for its input slice.
 size_t gemv_lds_bytes(int B, int kps);

@@ -66,8 +66,11 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const
 }
 
 
+// Occupancy floor per batch width: four workgroups per CU for the fp32
+// (batch 1) items, three for the MFMA items up to 32 columns (the LDS cap
+// of their input slices allows three), two above.
 template <int NB, int MODE>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   gemv_item<NB, MODE>(a, a.w, a.gain, no_done(), blockIdx.x, smem, NoWait{});
 }
@@ -90,6 +93,43 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
                                  NoWait{});
 }
 
+
+// ------------------------------------------------------------------ fused layer launches
+
+// Occupancy floor of the fused MLP launch: the GEMV items' (three
+// workgroups per CU up to 32 batch columns).
+constexpr int fused_min_blocks(int NB) { return NB == 1 ? 4 : 3; }
+
+// MLP block of one layer: [gate/up items | down items] (see FusedMlpArgs).
+template <int NB>
+__global__ __launch_bounds__(256, fused_min_blocks(NB)) void fused_mlp_kernel(FusedMlpArgs f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wg = blockIdx.x;
+  if (wg == 0)  // the attention block's counters, for its next launch
+    for (int i = threadIdx.x; i < f.n_other; i += blockDim.x)
+      st_agent(f.cnt_other + (size_t)i * kCntStride, 0u);
+  if (wg < f.ng) {
+    // a gate/up row group yields rows/2 SwiGLU channels: down k-tile
+    // rg * rows/2 / 32, in down's K slice (that) / kps
+    const int rows = kTileRows * f.gu.rt;
+    const int rg = wg / f.gu.S;
+    const int sd = (rg * (rows / 2) / kTileCols) / f.d.kps;
+    gemv_item<NB, kSwiGLU>(f.gu, f.gu.w, f.gu.gain,
+                           Done{f.cnt_g + (size_t)sd * kCntStride, 0u, 0u, nullptr, 0}, wg, smem,
+                           NoWait{});
+    return;
+  }
+  // down item: waits for the gate/up row groups that feed its K slice
+  const int item = wg - f.ng;
+  const int s = item % f.d.S;
+  const int KT = f.d.K / kTileCols;
+  const int nk = min(KT, (s + 1) * f.d.kps) - s * f.d.kps;
+  const int rows_gu = kTileRows * f.gu.rt;
+  const unsigned target = (unsigned)(nk * kTileCols / (rows_gu / 2));
+  gemv_item<NB, kResid>(f.d, f.d.w, nullptr, no_done(), item, smem,
+                        CounterWait{f.cnt_g + (size_t)s * kCntStride, 1, target, f.dev_flags,
+                                    f.spin_limit});
+}
 
 // ------------------------------------------------------------------ read ceiling
 
@@ -131,6 +171,32 @@ __global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4* __restri
 }
 
 // ------------------------------------------------------------------ launchers
+
+bool fused_supported(int B) {
+  const int nb = gemv_nb(B);
+  return nb == 8 || nb == 16;
+}
+
+template <int NB>
+static hipError_t launch_fused_mlp_t(const FusedMlpArgs& a, size_t lds, hipStream_t s) {
+  static bool attr_set = false;
+  const void* fn = reinterpret_cast<const void*>(&fused_mlp_kernel<NB>);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fused_mlp_kernel<NB>), dim3(a.ng + a.nd), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_mlp(const FusedMlpArgs& a, size_t lds, hipStream_t s) {
+  switch (gemv_nb(a.gu.B)) {
+    case 8: return launch_fused_mlp_t<8>(a, lds, s);
+    case 16: return launch_fused_mlp_t<16>(a, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_read_ceiling(const void* src, size_t bytes, int grid, hipStream_t s) {
   hipLaunchKernelGGL(read_ceiling_kernel, dim3(grid), dim3(256), 0, s,

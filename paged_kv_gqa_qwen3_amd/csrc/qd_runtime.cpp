@@ -72,6 +72,16 @@ struct qd_handle {
   // bf16 pairs [64][cols] for MFMA consumers (batch >= 2)
   uint16_t *xg_hi = nullptr, *xg_lo = nullptr, *attn_hi = nullptr, *attn_lo = nullptr;
   uint16_t *act_hi = nullptr, *act_lo = nullptr;
+  // the fused MLP launch: the second residual / norm / MFMA-pair set (down
+  // writes the next layer's while gate/up items of the same launch still
+  // read this layer's), down's own split partials and counters, and two
+  // alternating sets of completion counters, kCntStride apart
+  float *x_b = nullptr, *ssq_b = nullptr;
+  uint16_t *xg_b_hi = nullptr, *xg_b_lo = nullptr;
+  float* part_b = nullptr;
+  unsigned* gemv_cnt_b = nullptr;
+  unsigned* fused_cnt = nullptr;
+  int fused_cnt_n = 0;
   float* part = nullptr;      // split partials of self-reducing projections (O, down, LM head)
   float* part_qkv = nullptr;  // split partials of QKV, summed by attention
   unsigned* gemv_cnt = nullptr;
@@ -289,6 +299,14 @@ int prof_mark(qd_handle* h, Prof* pr, int cls, hipStream_t s) {
   return QD_OK;
 }
 
+#ifdef QD_STEP_TRACE
+// (trace builds) per-item event timestamps of layer kTraceLayer's launches of
+// an eager step, by class (QD_PROF_*), written to QD_TRACE_OUT after it
+constexpr int kTraceLayer = 17;
+constexpr size_t kTraceSlots = (size_t)kTraceItems * 8;
+unsigned long long* g_trace[QD_PROF_CLASSES];
+#endif
+
 // Launch the projection of class cls (QD_PROF_QKV, _O, _GATE_UP, _DOWN or
 // _LM_HEAD) of layer l at batch B on stream s, as the step does.  QKV leaves
 // split partials for attention when part_mode (else it stores q|k|v).
@@ -325,6 +343,10 @@ hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode
     a.amax_val = h->amax_val; a.amax_idx = h->amax_idx; a.amax_counter = h->amax_cnt;
     a.amax_val2 = h->amax_val2; a.amax_idx2 = h->amax_idx2;
     a.next_ids = next;
+#ifdef QD_STEP_TRACE
+    if (l == kTraceLayer || (cls == QD_PROF_LM_HEAD && g_trace[cls] != nullptr))
+      a.trace = g_trace[cls];
+#endif
     return launch_gemv(a, mode, s);
   };
   if (cls == QD_PROF_LM_HEAD) return gemv(h->lm, h->V, H, h->x, xg, h->final_norm, kArgmax, nullptr);
@@ -345,8 +367,15 @@ hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode
 }
 
 // Enqueue one step on stream s.
+int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s);
+
 int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream_t s,
                 Prof* pr = nullptr) {
+  // a decode step at batches 2-16 runs the MLP half of every layer as one
+  // fused launch (the taps, profiling and prefill paths keep one launch per
+  // stage)
+  if (taps == nullptr && pr == nullptr && sp.n_logits < 0 && fused_supported(sp.B))
+    return record_step_fused(h, sp, s);
   int prc = QD_OK;
   if (pr && (prc = prof_mark(h, pr, -1, s))) return prc;
 #define PROF(c)                                              \
@@ -357,6 +386,17 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
   const float eps = h->cfg.rms_eps;
   const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
   const bool mfma = gemv_mfma(B);
+#ifdef QD_STEP_TRACE
+  hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+  (void)hipStreamIsCapturing(s, &cap_st);
+  const bool tracing = std::getenv("QD_TRACE_OUT") != nullptr && cap_st == hipStreamCaptureStatusNone;
+  for (int c = 0; c < QD_PROF_CLASSES; ++c) {
+    if (tracing && g_trace[c] == nullptr) HIP_TRY(h, hipMalloc(&g_trace[c], kTraceSlots * 8));
+    if (tracing) HIP_TRY(h, hipMemsetAsync(g_trace[c], 0xff, kTraceSlots * 8, s));
+  }
+  if (!tracing)
+    for (int c = 0; c < QD_PROF_CLASSES; ++c) g_trace[c] = nullptr;
+#endif
 
   EmbedArgs ea{};
   ea.table = h->embed;
@@ -403,6 +443,9 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.tap_q = tap ? taps->q_rot : nullptr;
     aa.tap_k = tap ? taps->k_rot : nullptr;
     aa.dev_flags = h->dev_flags;
+#ifdef QD_STEP_TRACE
+    if (l == kTraceLayer) aa.trace = g_trace[QD_PROF_ATTN];
+#endif
     if (sp.n_logits >= 0) {  // prefill: every row's k, v in the pool before any row attends
       aa.kv_mode = kAppendOnly;
       HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
@@ -439,6 +482,118 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     HIP_TRY(h, launch_projection(h, B_lm, QD_PROF_LM_HEAD, 0, true, sp.logits, sp.next, s));
   PROF(QD_PROF_LM_HEAD);
 #undef PROF
+#ifdef QD_STEP_TRACE
+  if (tracing) {
+    HIP_TRY(h, hipStreamSynchronize(s));
+    std::vector<unsigned long long> buf(kTraceSlots);
+    FILE* f = std::fopen(std::getenv("QD_TRACE_OUT"), "wb");
+    for (int c = 0; c < QD_PROF_CLASSES && f; ++c) {
+      HIP_TRY(h, hipMemcpy(buf.data(), g_trace[c], kTraceSlots * 8, hipMemcpyDeviceToHost));
+      std::fwrite(buf.data(), 8, kTraceSlots, f);
+    }
+    if (f) std::fclose(f);
+  }
+#endif
+  return QD_OK;
+}
+
+// A decode step at batches 2-16 with the MLP half of every layer as one
+// fused launch (FusedMlpArgs): embedding; per layer the QKV, attention and
+// O launches of the per-stage path, then [gate/up | down]; the LM head.
+// The items and split plans are those of the per-stage kernels.  Down
+// writes the next layer's residual, norm sums and MFMA input pairs to the
+// other buffer set (gate/up items of the same launch still read this
+// one's), so the sets alternate from layer to layer; the completion
+// counters alternate too (each launch clears the next one's; the embedding
+// launch clears both at the start of the step).
+int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
+  const int B = sp.B, L = h->L, H = h->H, I = h->I;
+  const float eps = h->cfg.rms_eps;
+  const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+  struct Set { float *x, *ssq; uint16_t *hi, *lo; };
+  const Set set[2] = {{h->x, h->ssq, h->xg_hi, h->xg_lo}, {h->x_b, h->ssq_b, h->xg_b_hi, h->xg_b_lo}};
+  const GemvPlan pq = plan_gemv(h, h->NQKV, H, B), po = plan_gemv(h, H, h->QD, B);
+  const GemvPlan pg = plan_gemv(h, 2 * I, H, B), pd = plan_gemv(h, H, I, B);
+  const size_t lds_m = std::max(gemv_lds_bytes(B, pg.kps), gemv_lds_bytes(B, pd.kps));
+  const int ncnt = h->fused_cnt_n / 2;  // counters per set
+  unsigned* const cnt_set[2] = {h->fused_cnt, h->fused_cnt + (size_t)ncnt * kCntStride};
+
+  EmbedArgs ea{};
+  ea.table = h->embed;
+  ea.V = h->V; ea.H = H; ea.B = B; ea.Bmax = h->cfg.max_batch;
+  ea.tokens = sp.tokens; ea.x = h->x; ea.ssq_out = h->ssq; ea.dev_flags = h->dev_flags;
+  ea.xo_hi = h->xg_hi; ea.xo_lo = h->xg_lo; ea.xo_gain = h->lw[0].in_norm;
+  ea.zero = h->fused_cnt; ea.nzero = 2 * ncnt;
+  HIP_TRY(h, launch_embed(ea, s));
+
+  auto gemv_args = [&](const uint16_t* w, int N, int K, const GemvPlan& p) {
+    GemvArgs a{};
+    a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
+    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.eps = eps;
+    return a;
+  };
+  const int smax = attn_splits(h, B);
+  for (int l = 0; l < L; ++l) {
+    const LayerW& w = h->lw[l];
+    const Set& P = set[l & 1];
+    const Set& Q = set[(l + 1) & 1];
+    GemvArgs q = gemv_args(w.qkv, h->NQKV, H, pq);
+    q.x = P.x; q.xh = P.hi; q.xl = P.lo; q.ssq = P.ssq; q.gain = w.in_norm;
+    q.part = h->part_qkv; q.counters = h->gemv_cnt;
+    HIP_TRY(h, launch_gemv(q, kPartial, s));
+
+    AttnArgs aa{};
+    aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
+    aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; aa.qkv_rows = kTileRows * pq.rt;
+    aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
+    aa.pool_layer = sp.pool + (size_t)l * layer_elems;
+    aa.num_pages = h->cfg.num_pages;
+    aa.positions = sp.positions; aa.block_tables = sp.tables;
+    aa.max_pages = h->cfg.max_pages_per_seq;
+    aa.B = B; aa.Hq = h->Hq; aa.Hkv = h->Hkv;
+    aa.eps = eps; aa.scale = (float)(1.0 / std::sqrt((double)h->D));
+    aa.S_max = smax;
+    aa.grid = attn_grid(h, B);
+    aa.o_part = h->o_part; aa.ml_part = h->ml_part; aa.counters = h->attn_cnt;
+    aa.out = h->attn; aa.out_hi = h->attn_hi; aa.out_lo = h->attn_lo;
+    aa.dev_flags = h->dev_flags;
+    HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
+                                attn_pages_per_wave(B, false, h->long_ctx), s));
+
+    GemvArgs o = gemv_args(w.o, H, h->QD, po);  // residual in place on this set
+    o.x = h->attn; o.xh = h->attn_hi; o.xl = h->attn_lo;
+    o.part = h->part; o.counters = h->gemv_cnt;
+    o.out = P.x; o.ssq_out = P.ssq; o.xo_hi = P.hi; o.xo_lo = P.lo; o.xo_gain = w.post_norm;
+    HIP_TRY(h, launch_gemv(o, kResid, s));
+
+    FusedMlpArgs fm{};
+    fm.gu = gemv_args(w.gu, 2 * I, H, pg);
+    fm.gu.x = P.x; fm.gu.xh = P.hi; fm.gu.xl = P.lo; fm.gu.ssq = P.ssq; fm.gu.gain = w.post_norm;
+    fm.gu.part = h->part; fm.gu.counters = h->gemv_cnt; fm.gu.out = h->act;
+    fm.gu.xo_hi = h->act_hi; fm.gu.xo_lo = h->act_lo;
+    fm.d = gemv_args(w.down, H, I, pd);
+    fm.d.x = h->act; fm.d.xh = h->act_hi; fm.d.xl = h->act_lo;
+    fm.d.part = h->part_b; fm.d.counters = h->gemv_cnt_b;
+    fm.d.res_in = P.x; fm.d.out = Q.x; fm.d.ssq_out = Q.ssq; fm.d.xo_hi = Q.hi; fm.d.xo_lo = Q.lo;
+    fm.d.xo_gain = l + 1 < L ? h->lw[l + 1].in_norm : h->final_norm;
+    fm.ng = 2 * I / (kTileRows * pg.rt) * pg.S;
+    fm.nd = H / (kTileRows * pd.rt) * pd.S;
+    fm.cnt_g = cnt_set[l & 1];
+    fm.cnt_other = cnt_set[(l + 1) & 1]; fm.n_other = pd.S;
+    fm.dev_flags = h->dev_flags;
+    fm.spin_limit = 1u << 22;
+    HIP_TRY(h, launch_fused_mlp(fm, lds_m, s));
+  }
+  // the LM head on the last layer's output set
+  const Set& F = set[L & 1];
+  GemvArgs lm = gemv_args(h->lm, h->V, H, plan_gemv(h, h->V, H, B, true));
+  lm.x = F.x; lm.xh = F.hi; lm.xl = F.lo; lm.ssq = F.ssq; lm.gain = h->final_norm;
+  lm.part = h->part; lm.counters = h->gemv_cnt;
+  lm.logits = sp.logits;
+  lm.amax_val = h->amax_val; lm.amax_idx = h->amax_idx; lm.amax_counter = h->amax_cnt;
+  lm.amax_val2 = h->amax_val2; lm.amax_idx2 = h->amax_idx2;
+  lm.next_ids = sp.next;
+  HIP_TRY(h, launch_gemv(lm, kArgmax, s));
   return QD_OK;
 }
 
@@ -691,9 +846,11 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     // MFMA operands cover whole blocks of 8 or 16 batch columns: rows up to
     // the block are allocated and zeroed (rows >= B only feed unused outputs)
     const size_t rows = (size_t)gemv_nb(Bm);
-    uint16_t** bufs[6] = {&h->xg_hi, &h->xg_lo, &h->attn_hi, &h->attn_lo, &h->act_hi, &h->act_lo};
-    const size_t cols[6] = {(size_t)H, (size_t)H, (size_t)h->QD, (size_t)h->QD, (size_t)I, (size_t)I};
-    for (int i = 0; i < 6; ++i) {
+    uint16_t** bufs[8] = {&h->xg_hi, &h->xg_lo, &h->attn_hi, &h->attn_lo, &h->act_hi, &h->act_lo,
+                          &h->xg_b_hi, &h->xg_b_lo};
+    const size_t cols[8] = {(size_t)H, (size_t)H, (size_t)h->QD, (size_t)h->QD, (size_t)I, (size_t)I,
+                            (size_t)H, (size_t)H};
+    for (int i = 0; i < 8; ++i) {
       if ((rc = dev_alloc(h, bufs[i], rows * cols[i]))) return bail(rc);
       e = hipMemset(*bufs[i], 0, rows * cols[i] * sizeof(uint16_t));
       if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
@@ -719,8 +876,24 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (h->stream_ok) part_qkv_elems = std::max(part_qkv_elems, (size_t)h->NQKV * h->stream_qkv_S);
   if ((rc = dev_alloc(h, &h->part_qkv, part_qkv_elems))) return bail(rc);
   if ((rc = dev_alloc(h, &h->gemv_cnt, (size_t)max_nrg * kCntStride))) return bail(rc);
+  // fused launches (see record_step_fused)
+  if ((rc = dev_alloc(h, &h->x_b, (size_t)Bm * H))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->ssq_b, (size_t)(H / kSsqRows) * Bm))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->part_b, part_elems))) return bail(rc);
+  if ((rc = dev_alloc(h, &h->gemv_cnt_b, (size_t)max_nrg * kCntStride))) return bail(rc);
+  {
+    int max_down_splits = 1;
+    for (int B = 1; B <= Bm; ++B) max_down_splits = std::max(max_down_splits, plan_gemv(h, H, I, B).S);
+    h->fused_cnt_n = 2 * max_down_splits;  // two alternating sets
+    if ((rc = dev_alloc(h, &h->fused_cnt, (size_t)h->fused_cnt_n * kCntStride))) return bail(rc);
+    e = hipMemset(h->fused_cnt, 0, sizeof(unsigned) * h->fused_cnt_n * kCntStride);
+    if (e == hipSuccess)
+      e = hipMemset(h->gemv_cnt_b, 0, sizeof(unsigned) * max_nrg * kCntStride);
+    if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+  }
   size_t att_rows = 0;
-  for (int B = 1; B <= Bm; ++B) att_rows = std::max(att_rows, (size_t)B * h->Hq * attn_splits(h, B));
+  for (int B = 1; B <= Bm; ++B)
+    att_rows = std::max(att_rows, (size_t)B * h->Hq * attn_splits(h, B));
   if (h->stream_ok) att_rows = std::max(att_rows, (size_t)h->Hq * stream_attn_splits(h));
   if ((rc = dev_alloc(h, &h->o_part, att_rows * h->D))) return bail(rc);
   if ((rc = dev_alloc(h, &h->ml_part, att_rows * 2))) return bail(rc);

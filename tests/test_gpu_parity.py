@@ -441,8 +441,9 @@ def test_stream_step_matches_staged(torch, ctx):
 
 
 def test_profiling_entry_points(torch):
-    """qd_profile_step runs the same step as qd_decode_step (same logits,
-    ids and pool bits, for the graph handle's per-stage plan) and reports a
+    """qd_profile_step runs the step as the per-stage kernels, the same items
+    and split plans as qd_decode_step (whose MLP half is one fused launch
+    at this batch): the same logits, ids and pool bits; it reports a
     positive time for every class it launched; qd_profile_class times one
     projection class alone and leaves the next step's results unchanged."""
     shape = synth.TINY
@@ -468,12 +469,54 @@ def test_profiling_entry_points(torch):
         assert us > 0.0, cls
     with pytest.raises(binding.QdError):
         binding.qd_profile_class(dp.handle, B, "attention", reps=3)
-    ia.run(dp, pa)  # the classes overwrote only scratch: the next step is unchanged
+    ib.tok.copy_(ia.tok)  # the classes overwrote only scratch: the next step is unchanged
+    pb.copy_(pa)
+    ia.run(dp, pa)
     ib.run(dp, pb)
     torch.cuda.synchronize()
     assert torch.equal(ia.logits, ib.logits)
     assert dp.device_status() == 0
     dp.close()
+
+
+@pytest.mark.parametrize("shape_name,B,ctx", [
+    ("tiny", 1, [37]), ("tiny", 3, [5, 40, 300]), ("tiny", 8, [0, 16, 31, 100, 255, 256, 700, 2]),
+    ("tiny", 16, [(41 * i) % 900 for i in range(16)]), ("tiny", 17, [(13 * i) % 200 for i in range(17)]),
+    ("d128g4", 5, [3, 17, 200, 513, 64]), ("d128g4", 1, [2000]),
+])
+def test_fused_step_matches_per_stage(torch, shape_name, B, ctx):
+    """At batches 2-16 qd_decode_step runs the MLP half of every layer as one
+    launch (gate/up items, then down items that wait on completion
+    counters) with alternating residual buffer sets; the items and split
+    plans are the per-stage kernels', so over chained steps the logits,
+    ids and the whole pool must equal the per-stage path's
+    (qd_decode_step_taps) bit for bit.  Batches 1 and 17 take the
+    per-stage launches either way."""
+    shape = synth.TINY if shape_name == "tiny" else \
+        synth.ModelShape("d128g4", 2, 256, 8, 2, 128, 704, 4096, True)
+    W = synth.make_weights(shape, 600 + B)
+    batch = synth.make_paged_batch(shape, ctx, 4, 601 + B)
+    dec = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=True)
+    dec.load_numpy_weights(W)
+    pf, pe = pool_to_device(batch.pool), pool_to_device(batch.pool)
+    io_f = StepIO(torch, B, batch.max_pages, shape.vocab)
+    io_e = StepIO(torch, B, batch.max_pages, shape.vocab)
+    tokens, positions = batch.tokens.copy(), batch.positions.copy()
+    for step in range(4):
+        say(f"fused vs per-stage {shape_name} B={B} step {step}")
+        io_f.set(tokens, positions, batch.block_tables)
+        io_e.set(tokens, positions, batch.block_tables)
+        io_f.run(dec, pf)
+        dec.step_taps(io_e.tok, io_e.pos, io_e.tab, pe, io_e.nxt, io_e.logits, None, -1)
+        torch.cuda.synchronize()
+        assert torch.isfinite(io_f.logits).all()
+        assert torch.equal(io_f.logits, io_e.logits), step
+        assert torch.equal(io_f.nxt, io_e.nxt), step
+        tokens, positions = io_e.nxt.cpu().numpy(), positions + 1
+    torch.cuda.synchronize()
+    assert torch.equal(pf, pe)
+    assert dec.device_status() == 0
+    dec.close()
 
 
 def test_step_paths(torch):

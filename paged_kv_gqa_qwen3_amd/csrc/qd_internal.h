@@ -131,13 +131,11 @@ struct EmbedArgs {
 // [gate/up items | down items].  A finished gate/up row group counts in
 // cnt_g[the K slice of down its SwiGLU channels feed] (kCntStride apart);
 // a down item issues its weight tiles, then waits until its slice's count
-// is complete, so that down's weights stream while gate/up finishes.
-// Gate/up items sit at lower workgroup indices, which are dispatched first:
-// a waiting down item only waits for running or finished ones.  The launch
-// clears the counters it does not use (cnt_other) for the next one.
+// is complete, so that down's weights stream while gate/up finishes.  The
+// launch clears the counters it does not use (cnt_other) for the next one.
 struct FusedMlpArgs {
   GemvArgs gu, d;      // gate/up (kSwiGLU) and down (kResid)
-  int ng, nd;
+  int ng, nd;          // items of each
   unsigned* cnt_g;     // [down K slices]
   unsigned* cnt_other; // the next launch's counters, cleared here: [n_other]
   int n_other;

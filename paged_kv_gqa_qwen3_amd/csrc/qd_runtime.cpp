@@ -517,6 +517,16 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   const size_t lds_m = std::max(gemv_lds_bytes(B, pg.kps), gemv_lds_bytes(B, pd.kps));
   const int ncnt = h->fused_cnt_n / 2;  // counters per set
   unsigned* const cnt_set[2] = {h->fused_cnt, h->fused_cnt + (size_t)ncnt * kCntStride};
+#ifdef QD_STEP_TRACE
+  hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+  (void)hipStreamIsCapturing(s, &cap_st);
+  const bool tracing = std::getenv("QD_TRACE_OUT") != nullptr && cap_st == hipStreamCaptureStatusNone;
+  for (int c = 0; c < QD_PROF_CLASSES; ++c) {
+    if (tracing && g_trace[c] == nullptr) HIP_TRY(h, hipMalloc(&g_trace[c], kTraceSlots * 8));
+    if (tracing) HIP_TRY(h, hipMemsetAsync(g_trace[c], 0xff, kTraceSlots * 8, s));
+  }
+  auto tr = [&](int c, int l) { return tracing && l == kTraceLayer ? g_trace[c] : nullptr; };
+#endif
 
   EmbedArgs ea{};
   ea.table = h->embed;
@@ -540,6 +550,9 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     GemvArgs q = gemv_args(w.qkv, h->NQKV, H, pq);
     q.x = P.x; q.xh = P.hi; q.xl = P.lo; q.ssq = P.ssq; q.gain = w.in_norm;
     q.part = h->part_qkv; q.counters = h->gemv_cnt;
+#ifdef QD_STEP_TRACE
+    q.trace = tr(QD_PROF_QKV, l);
+#endif
     HIP_TRY(h, launch_gemv(q, kPartial, s));
 
     AttnArgs aa{};
@@ -557,6 +570,9 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     aa.o_part = h->o_part; aa.ml_part = h->ml_part; aa.counters = h->attn_cnt;
     aa.out = h->attn; aa.out_hi = h->attn_hi; aa.out_lo = h->attn_lo;
     aa.dev_flags = h->dev_flags;
+#ifdef QD_STEP_TRACE
+    aa.trace = tr(QD_PROF_ATTN, l);
+#endif
     HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
                                 attn_pages_per_wave(B, false, h->long_ctx), s));
 
@@ -564,6 +580,9 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     o.x = h->attn; o.xh = h->attn_hi; o.xl = h->attn_lo;
     o.part = h->part; o.counters = h->gemv_cnt;
     o.out = P.x; o.ssq_out = P.ssq; o.xo_hi = P.hi; o.xo_lo = P.lo; o.xo_gain = w.post_norm;
+#ifdef QD_STEP_TRACE
+    o.trace = tr(QD_PROF_O, l);
+#endif
     HIP_TRY(h, launch_gemv(o, kResid, s));
 
     FusedMlpArgs fm{};
@@ -582,6 +601,10 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     fm.cnt_other = cnt_set[(l + 1) & 1]; fm.n_other = pd.S;
     fm.dev_flags = h->dev_flags;
     fm.spin_limit = 1u << 22;
+#ifdef QD_STEP_TRACE
+    fm.gu.trace = tr(QD_PROF_GATE_UP, l);
+    fm.d.trace = tr(QD_PROF_DOWN, l);
+#endif
     HIP_TRY(h, launch_fused_mlp(fm, lds_m, s));
   }
   // the LM head on the last layer's output set
@@ -593,7 +616,22 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   lm.amax_val = h->amax_val; lm.amax_idx = h->amax_idx; lm.amax_counter = h->amax_cnt;
   lm.amax_val2 = h->amax_val2; lm.amax_idx2 = h->amax_idx2;
   lm.next_ids = sp.next;
+#ifdef QD_STEP_TRACE
+  lm.trace = tracing ? g_trace[QD_PROF_LM_HEAD] : nullptr;
+#endif
   HIP_TRY(h, launch_gemv(lm, kArgmax, s));
+#ifdef QD_STEP_TRACE
+  if (tracing) {
+    HIP_TRY(h, hipStreamSynchronize(s));
+    std::vector<unsigned long long> buf(kTraceSlots);
+    FILE* f = std::fopen(std::getenv("QD_TRACE_OUT"), "wb");
+    for (int c = 0; c < QD_PROF_CLASSES && f; ++c) {
+      HIP_TRY(h, hipMemcpy(buf.data(), g_trace[c], kTraceSlots * 8, hipMemcpyDeviceToHost));
+      std::fwrite(buf.data(), 8, kTraceSlots, f);
+    }
+    if (f) std::fclose(f);
+  }
+#endif
   return QD_OK;
 }
 

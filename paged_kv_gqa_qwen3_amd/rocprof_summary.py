@@ -34,6 +34,8 @@ import sys
 # classed by their epilogue (the second template argument, any batch width).
 CLASSES = (
     ("stream_step_kernel", "stream_step"),
+    ("fused_mlp_kernel", "gate_up+down"),
+    ("read_ceiling_kernel", "read_ceiling"),
     ("sample_sum_kernel", "sample_sum"),
     ("sample_kernel", "sample"),
     ("attention_kernel", "attention"),

@@ -352,6 +352,51 @@ def time_prefill(torch, shape, W, n_tokens=512, chunk=32, reps=3):
             "ms": round(ms, 3), "tokens_per_s": round(n_tokens / (ms / 1e3), 1)}
 
 
+def time_prefill_prompts(torch, shape, W, n_tokens=512, reps=5):
+    """Milliseconds to prefill one n_tokens prompt from an empty pool through
+    qd_prefill_prompts: one chunk, projections as GEMMs on the matrix cores,
+    tiled causal attention, logits for the last row (HIP events on the
+    library's stream, torch's current stream; median of `reps`).  Also the
+    projections' algorithmic FLOP rate over the whole prefill time."""
+    from paged_kv_gqa_qwen3_amd.decoder import Decoder
+    pages = -(-n_tokens // 16)
+    dec = Decoder(shape, 1, pages, pages, use_graphs=False, max_prefill_rows=n_tokens)
+    dec.load_numpy_weights(W)
+    pool = torch.zeros(shape.num_layers, pages, 2, shape.num_kv_heads, 16, shape.head_dim,
+                       dtype=torch.int16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    prompt = torch.randint(0, shape.vocab, (n_tokens,), dtype=torch.int32, device="cuda",
+                           generator=g)
+    table = torch.arange(pages, dtype=torch.int32, device="cuda")[None].contiguous()
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+
+    def run():
+        dec.prefill_prompts([n_tokens], [0], prompt, table, pool, 1, nxt, lg)
+    run()
+    times = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        run()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    ms = float(np.median(times))
+    assert dec.device_status() == 0
+    dec.close()
+    del pool
+    torch.cuda.empty_cache()
+    H, I, QD, KD = shape.hidden, shape.intermediate, shape.q_dim, shape.kv_dim
+    proj_flop = 2.0 * n_tokens * shape.num_layers * H * (QD + 2 * KD + QD + 3 * I)
+    return {"prompt_tokens": n_tokens, "chunk_rows": n_tokens, "chunks": 1,
+            "ms": round(ms, 3), "ms_min_max": [round(min(times), 3), round(max(times), 3)],
+            "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
+            "projection_tflops": round(proj_flop / (ms / 1e3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,9 +495,13 @@ def main():
                 # prompt processing (qd_prefill) of a 512-token prompt, the
                 # headline's context, on a handle of its own
                 if not args.no_prefill:
-                    results[w.name]["prefill"] = time_prefill(torch, shape, W)
-                    log(f"[bench] {w.name}: qd_prefill of 512 prompt tokens "
+                    results[w.name]["prefill"] = time_prefill_prompts(torch, shape, W)
+                    log(f"[bench] {w.name}: qd_prefill_prompts of 512 prompt tokens "
                         f"{results[w.name]['prefill']}")
+                    results[w.name]["prefill_decode_kernels"] = time_prefill(torch, shape, W)
+                    log(f"[bench] {w.name}: qd_prefill (32-row chunks on the decode "
+                        f"kernels) of 512 prompt tokens "
+                        f"{results[w.name]['prefill_decode_kernels']}")
                 if not args.no_cpu_baseline:
                     log("[bench] timing the CPU oracle on a bounded sample")
                     headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)

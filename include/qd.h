@@ -88,6 +88,13 @@ typedef struct qd_config {
                                   <= 8192 and every projection input <= 16384; other
                                   handles, and every batch above 1, take the per-stage
                                   kernels (qd_step_path tells which) */
+  int32_t max_prefill_rows;    /* largest chunk passed to qd_prefill_prompts (rows of
+                                  all its prompts together, at most 16384); the handle
+                                  keeps a workspace of at most rows * (8*hidden +
+                                  12*q_dim + 8*kv_dim + 4*intermediate) bytes for it
+                                  (q_dim = Hq*D, kv_dim = Hkv*D; 60 MB for 512 rows of
+                                  Qwen3-4B).  0: no workspace, and qd_prefill_prompts
+                                  is refused */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
@@ -154,6 +161,43 @@ int qd_load_weights(qd_handle* h, const qd_tensor_desc* tensors, int32_t n);
 int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32_t* positions,
                const int32_t* block_tables, void* kv_pool, int32_t n_logits,
                int32_t* out_next_ids, float* out_logits);
+
+/* Prompts on the matrix cores: n_seqs prompt segments, packed back to back
+ * into one chunk of rows = sum(seq_rows) <= max_prefill_rows, run through
+ * the layers as one batch, causally masked, with only each prompt's last
+ * position reaching the LM head (the blog "GPU 算子与执行优化：从 26 到 100
+ * token/s", Part 7; the rkmt page "从零构建 Qwen3-8B 推理引擎", 4.1.2: a
+ * prefill writes the prompt's K/V into the cache, then decoding starts from
+ * its last logits).  The projections run as GEMMs (bf16 weights times a
+ * bf16 hi/lo pair of the input, fp32 accumulation), attention as a tiled
+ * causal kernel over the pool's pages.  Segment s holds the tokens of
+ * positions start_pos[s] .. start_pos[s] + seq_rows[s] - 1 of one sequence;
+ * positions below start_pos[s] (an earlier chunk of the same prompt, or a
+ * shared prefix) must already be in the pool.
+ *   n_seqs       1 .. 64
+ *   seq_rows     int32 [n_seqs]  HOST: rows of each segment, >= 1
+ *   start_pos    int32 [n_seqs]  HOST: position of each segment's first row;
+ *                                start_pos[s] + seq_rows[s] <= max_pages_per_seq*16
+ *   token_ids    int32 [rows]    DEVICE: segment 0's tokens, then segment 1's, ...
+ *   block_tables int32 [n_seqs][max_pages_per_seq]  DEVICE: each segment's pages
+ *   kv_pool      as for qd_decode_step; every row's K/V is written at its slot
+ *   n_logits     0 .. min(n_seqs, max_batch): segments 0 .. n_logits-1 get
+ *                the final RMSNorm, the LM head and the greedy next id of
+ *                their last row (put the segments that end a prompt first)
+ *   out_next_ids int32 [n_logits] DEVICE, or NULL when n_logits is 0
+ *   out_logits   fp32 [n_logits][vocab] DEVICE, or NULL
+ * The result equals running each segment's rows one position at a time
+ * through qd_decode_step, up to rounding.  Kernels are launched directly on
+ * the handle's stream (no graph); the host arrays are read before the call
+ * returns.  Asynchronous.  QD_EINVAL on a NULL pointer or a size out of
+ * range; QD_EUNSUPPORTED on a handle created with max_prefill_rows = 0;
+ * QD_ESTATE before all weights are loaded.  Block-table entries outside the
+ * pool and token ids outside the vocabulary are clamped and reported by
+ * qd_device_status. */
+int qd_prefill_prompts(qd_handle* h, int32_t n_seqs, const int32_t* seq_rows,
+                       const int32_t* start_pos, const int32_t* token_ids,
+                       const int32_t* block_tables, void* kv_pool, int32_t n_logits,
+                       int32_t* out_next_ids, float* out_logits);
 
 /* One decode step for `batch` sequences (1 <= batch <= max_batch): token
  * ids and positions in, one next token id per sequence out, and nothing but

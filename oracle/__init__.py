@@ -87,6 +87,10 @@ def _load():
                                      ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P]
         lib.or_silu.restype = ctypes.c_double
         lib.or_silu.argtypes = [ctypes.c_double]
+        lib.or_f64_to_bf16_n.restype = None
+        lib.or_f64_to_bf16_n.argtypes = [_P, ctypes.c_int64, _P]
+        lib.or_silu_n.restype = None
+        lib.or_silu_n.argtypes = [_P, ctypes.c_int64, _P]
         lib.or_argmax.restype = ctypes.c_int
         lib.or_argmax.argtypes = [_P, ctypes.c_int]
         lib.or_decode_step.restype = ctypes.c_int
@@ -119,12 +123,10 @@ def bf16_to_f64(bits) -> np.ndarray:
 def f64_to_bf16(x) -> np.ndarray:
     """float64 -> nearest bf16 bit pattern (ties to even), one rounding step."""
     lib = _load()
-    x = np.asarray(x, dtype=np.float64)
-    flat = x.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint16)
-    for i, v in enumerate(flat):
-        out[i] = lib.or_f64_to_bf16(float(v))
-    return out.reshape(x.shape)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.or_f64_to_bf16_n(x.ctypes.data, x.size, out.ctypes.data)
+    return out
 
 
 def rmsnorm(x, gain_bf16, eps: float = 1e-6) -> np.ndarray:
@@ -181,8 +183,10 @@ def attention(q, pool, layer: int, table_row, ctx: int, num_kv_heads: int) -> np
 
 def silu(z) -> np.ndarray:
     lib = _load()
-    z = np.asarray(z, dtype=np.float64)
-    return np.vectorize(lib.or_silu, otypes=[np.float64])(z)
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    out = np.empty(z.shape, dtype=np.float64)
+    lib.or_silu_n(z.ctypes.data, z.size, out.ctypes.data)
+    return out
 
 
 def argmax(v) -> int:
@@ -198,6 +202,7 @@ class Oracle:
 
     def __init__(self, shape, weights: Dict[str, np.ndarray]):
         self.shape = shape
+        self._weights = weights
         self._keep = []
         c = _Config(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
                     shape.head_dim, shape.intermediate, shape.vocab,
@@ -276,3 +281,63 @@ class Oracle:
             logits, nxt, _ = self.decode_step(prompt[t:t + 1], np.array([t], np.int32), row,
                                               pool, want_logits=(t == len(prompt) - 1))
         return logits[0], int(nxt[0])
+
+    def prefill_chunk(self, tokens, positions, block_tables, pool: np.ndarray, n_head: int):
+        """The rows of a chunk through the layers as one batch, as
+        ``decode_step`` runs its rows: per layer every row's K/V is appended at
+        its position before any row attends, so rows of one sequence at
+        consecutive positions get the causal prefill of that stretch (the blog
+        "GPU 算子与执行优化：从 26 到 100 token/s", Part 7).  The steps are
+        ``decode_step``'s; only the projections differ, as fp64 matrix
+        products (numpy) of the bf16 weights, whose summation order is the
+        library's, so the two agree to fp64 rounding.  Norms, RoPE, attention,
+        SwiGLU and bf16 rounding are the C routines.  Only rows 0..n_head-1
+        get the final norm, the LM head and the greedy id (the same Part 7:
+        the LM head runs on the positions whose next token is wanted).
+        Appends to ``pool`` in place; returns (logits [n_head, V], next
+        [n_head])."""
+        s = self.shape
+        W = self._weights
+        tokens = np.asarray(tokens, dtype=np.int32)
+        positions = np.asarray(positions, dtype=np.int32)
+        tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        pool = _req(pool, np.uint16)
+        B = tokens.shape[0]
+        H, Hq, Hkv, D = s.hidden, s.num_q_heads, s.num_kv_heads, s.head_dim
+        eps, theta = s.rms_eps, s.rope_theta
+        assert positions.shape == (B,) and tables.shape[0] == B and 0 <= n_head <= B
+
+        def mat(name):
+            return bf16_to_f64(W[name])
+
+        x = bf16_to_f64(W["model.embed_tokens.weight"][tokens])
+        for l in range(s.num_layers):
+            p = f"model.layers.{l}."
+            h = rmsnorm(x, W[p + "input_layernorm.weight"], eps)
+            q = (h @ mat(p + "self_attn.q_proj.weight").T).reshape(B, Hq, D)
+            k = (h @ mat(p + "self_attn.k_proj.weight").T).reshape(B, Hkv, D)
+            v = (h @ mat(p + "self_attn.v_proj.weight").T).reshape(B, Hkv, D)
+            q = rmsnorm(q, W[p + "self_attn.q_norm.weight"], eps)
+            k = rmsnorm(k, W[p + "self_attn.k_norm.weight"], eps)
+            for b in range(B):
+                q[b] = rope_neox(q[b], int(positions[b]), theta)
+                k[b] = rope_neox(k[b], int(positions[b]), theta)
+            kb, vb = f64_to_bf16(k), f64_to_bf16(v)
+            for b in range(B):
+                pos = int(positions[b])
+                page = int(tables[b][pos // PAGE])
+                if not 0 <= page < pool.shape[1]:
+                    raise ValueError("block-table entry outside the pool")
+                pool[l, page, 0, :, pos % PAGE, :] = kb[b]
+                pool[l, page, 1, :, pos % PAGE, :] = vb[b]
+            att = np.stack([attention(q[b], pool, l, tables[b], int(positions[b]) + 1, Hkv)
+                            for b in range(B)]).reshape(B, Hq * D)
+            x = x + att @ mat(p + "self_attn.o_proj.weight").T
+            h2 = rmsnorm(x, W[p + "post_attention_layernorm.weight"], eps)
+            a = silu(h2 @ mat(p + "mlp.gate_proj.weight").T) * (h2 @ mat(p + "mlp.up_proj.weight").T)
+            x = x + a @ mat(p + "mlp.down_proj.weight").T
+        head = W["model.embed_tokens.weight"] if s.tie_embeddings else W["lm_head.weight"]
+        hf = rmsnorm(x[:n_head], W["model.norm.weight"], eps)
+        logits = linear(hf, head) if n_head else np.zeros((0, s.vocab))
+        nxt = np.array([argmax(r) for r in logits], dtype=np.int32)
+        return logits, nxt

@@ -158,6 +158,17 @@ void or_attention(const double* q, int Hq, int Hkv, int D, const uint16_t* pool,
 
 double or_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Element-wise forms of or_f64_to_bf16 and or_silu over arrays (the same
+ * scalar functions applied in a loop, so that callers need not cross into
+ * C once per element). */
+void or_f64_to_bf16_n(const double* x, int64_t n, uint16_t* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = or_f64_to_bf16(x[i]);
+}
+
+void or_silu_n(const double* z, int64_t n, double* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = or_silu(z[i]);
+}
+
 /* Index of the largest value, lowest index among equals; -1 if any NaN. */
 int or_argmax(const double* v, int n) {
   int best = -1;

@@ -29,7 +29,8 @@ QD_DEV_BAD_POSITION = 2
 QD_DEV_BAD_PAGE = 4
 QD_DEV_TIMEOUT = 8
 
-EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_decode_step_taps",
+EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_prefill_prompts",
+            "qd_decode_step_taps",
             "qd_stream_step_taps", "qd_read_ceiling", "qd_sample_noalloc",
             "qd_profile_step", "qd_profile_class", "qd_device_status", "qd_stream",
             "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
@@ -48,7 +49,8 @@ class QdConfig(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
                 ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("use_graphs", ctypes.c_int32), ("persistent", ctypes.c_int32)]
+                ("use_graphs", ctypes.c_int32), ("persistent", ctypes.c_int32),
+                ("max_prefill_rows", ctypes.c_int32)]
 
 
 class QdTensorDesc(ctypes.Structure):
@@ -89,6 +91,8 @@ def load_library():
         lib.qd_decode_step.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
         lib.qd_prefill.restype = ctypes.c_int
         lib.qd_prefill.argtypes = [P, ctypes.c_int32, P, P, P, P, ctypes.c_int32, P, P]
+        lib.qd_prefill_prompts.restype = ctypes.c_int
+        lib.qd_prefill_prompts.argtypes = [P, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
         lib.qd_decode_step_taps.restype = ctypes.c_int
         lib.qd_decode_step_taps.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P,
                                             ctypes.POINTER(QdTaps)]
@@ -149,11 +153,12 @@ def _check(rc: int, handle) -> None:
 
 
 def make_config(shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
-                use_graphs: bool = True, persistent: bool = False) -> QdConfig:
+                use_graphs: bool = True, persistent: bool = False,
+                max_prefill_rows: int = 0) -> QdConfig:
     return QdConfig(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
                     shape.head_dim, shape.intermediate, shape.vocab, int(shape.tie_embeddings),
                     shape.rms_eps, shape.rope_theta, 16, max_batch, max_pages_per_seq,
-                    num_pages, int(use_graphs), int(persistent))
+                    num_pages, int(use_graphs), int(persistent), int(max_prefill_rows))
 
 
 def qd_create(cfg: QdConfig, stream: int = 0) -> int:
@@ -196,6 +201,20 @@ def qd_prefill(handle: int, rows: int, token_ids, positions, block_tables, kv_po
     lib = load_library()
     _check(lib.qd_prefill(handle, rows, _ptr(token_ids), _ptr(positions), _ptr(block_tables),
                           _ptr(kv_pool), n_logits, _ptr(out_next_ids), _ptr(out_logits)), handle)
+
+
+def qd_prefill_prompts(handle: int, seq_rows, start_pos, token_ids, block_tables, kv_pool,
+                       n_logits: int, out_next_ids=None, out_logits=None) -> None:
+    """seq_rows, start_pos: host int sequences (one entry per prompt segment)."""
+    lib = load_library()
+    n = len(seq_rows)
+    rows = np.ascontiguousarray(seq_rows, dtype=np.int32)
+    pos = np.ascontiguousarray(start_pos, dtype=np.int32)
+    if pos.shape != (n,):
+        raise ValueError("seq_rows and start_pos differ in length")
+    _check(lib.qd_prefill_prompts(handle, n, rows.ctypes.data, pos.ctypes.data, _ptr(token_ids),
+                                  _ptr(block_tables), _ptr(kv_pool), n_logits,
+                                  _ptr(out_next_ids), _ptr(out_logits)), handle)
 
 
 def qd_decode_step_taps(handle: int, batch: int, token_ids, positions, block_tables, kv_pool,

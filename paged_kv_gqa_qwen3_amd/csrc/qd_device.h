@@ -30,6 +30,29 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   return (unsigned short)(u >> 16);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr unsigned vmcnt_imm(int n) {
+  return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | 0x70u | 0xF00u;
+}
+// ... and until every LDS / scalar-memory operation is done (vmcnt at its maximum).
+constexpr unsigned kLgkmZero = 15u | (3u << 14) | 0x70u;
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// makes global stores visible, and even a fence limited to LDS counts
+// direct-to-LDS loads as LDS writes: both wait for every outstanding vector
+// memory operation of the wave, which would drain a pipeline of such loads.
+// This one waits only for the wave's own LDS reads and writes.  Tiles that
+// direct-to-LDS loads bring in are handed to other waves only after each
+// loading wave has waited (vmcnt) for its loads before the barrier.  The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // bf16 hi/lo pair of v (hi = bf16(v), lo = bf16(v - hi)), stored with agent
 // scope: a consumer may run in the same launch, on another XCD.
 __device__ __forceinline__ void split_hilo(float v, uint16_t* hi, uint16_t* lo, size_t i) {

@@ -302,4 +302,81 @@ hipError_t launch_fused_mlp(const FusedMlpArgs& a, size_t lds, hipStream_t s);
 // LDS bytes a GEMV workgroup needs for its input slice.
 size_t gemv_lds_bytes(int B, int kps);
 
+// ------------------------------------------------------------------ prefill
+// A prompt chunk of M rows on the GEMM path (qd_prefill_prompts).  The chunk
+// holds nseg segments back to back: segment s is rows [row0[s], row0[s+1])
+// and holds the tokens at positions pos0[s], pos0[s]+1, ... of the sequence
+// whose block-table row is s.  Activations that feed a matrix-core
+// projection are stored as "operand tiles": a [M][K] matrix as bf16 hi/lo
+// pairs in tiles of 16 rows x 32 columns, tile (mt, kt) holding hi at
+// element offset ((mt * (K/32) + kt) * 2) * 512 and lo 512 elements further,
+// with element (m, k) at ((k%32)/8 * 16 + m%16) * 8 + k%8 inside a tile: the
+// lane layout of the weight tiles, so that lane l's 16 bytes are the B
+// operand of a 16x16x32 MFMA (rows m%16 = l%16, columns k = 8*(l/16)..+7).
+constexpr int kPfMaxSegs = 64;
+constexpr int kPfMaxRows = 16384;
+constexpr int kPfRowAlign = 128;  // operand-tile buffers hold whole 128-row blocks
+
+struct PfSegs {
+  int n;
+  int row0[kPfMaxSegs + 1];
+  int pos0[kPfMaxSegs];
+  int qb0[kPfMaxSegs + 1];  // first 16-row query block of each segment; qb0[n] = all blocks
+};
+
+// Element offset of (m, k) in operand tiles with KT = K/32 k-tiles (hi; lo is +512).
+__host__ __device__ constexpr size_t pf_tile_off(int m, int k, int KT) {
+  return (((size_t)(m >> 4) * KT + (k >> 5)) * 2) * kTileElems +
+         (size_t)((((k & 31) >> 3) << 4) + (m & 15)) * 8 + (k & 7);
+}
+
+// Epilogues of the prefill GEMM.
+enum PfMode : int {
+  kPfStore = 0,   // out[m][n] = y
+  kPfResid = 1,   // out[m][n] += y (the residual stream)
+  kPfSwiGLU = 2,  // act operand tiles of silu(gate) * up (gate|up interleaved by half tiles)
+};
+
+struct PfGemmArgs {
+  const uint16_t* w;   // packed weight tiles, N x K
+  const uint16_t* x;   // operand tiles of the input, [Mp/16][K/32]
+  int N, K, M;
+  int nb_n, nb_m;      // workgroup tiles along N and along M
+  float* out;          // kPfStore / kPfResid: [M][ldo]
+  int ldo;
+  uint16_t* act;       // kPfSwiGLU: operand tiles [Mp/16][N/2/32]
+};
+
+struct PfAttnArgs {
+  const float* qkv;         // [M][(Hq+2Hkv)D] projection output
+  const float* q_gain;      // [D]
+  const float* k_gain;
+  const float* rope_cos;    // [max_pos][D/2]
+  const float* rope_sin;
+  uint16_t* pool_layer;     // this layer's slice of the pool: [P][2][Hkv][16][D]
+  int num_pages;
+  const int* block_tables;  // [nseg][max_pages]
+  int max_pages;
+  int M, Hq, Hkv;
+  float eps, scale;
+  uint16_t* q_hi;           // [M][Hq][D] q after norm, RoPE and scale, bf16 pair
+  uint16_t* q_lo;
+  uint16_t* out;            // attention output as operand tiles, K = Hq*D
+  int* dev_flags;
+  PfSegs seg;
+};
+
+// Prefill launchers (qd_prefill.hip).  wn, wm: the GEMM workgroup tile is
+// 32*wn weight rows x 32*wm input rows (4 waves of 16*wn x 16*wm).
+hipError_t launch_pf_embed(const uint16_t* table, int V, int H, const int* tokens, int M,
+                           float* x, int* dev_flags, hipStream_t s);
+hipError_t launch_pf_norm(const float* x, const float* gain, int K, int M, int Mpad, float eps,
+                          uint16_t* out, hipStream_t s);
+hipError_t launch_pf_gemm(const PfGemmArgs& a, int mode, int wn, int wm, hipStream_t s);
+hipError_t launch_pf_qk(const PfAttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_pf_attn(const PfAttnArgs& a, int head_dim, int group, hipStream_t s);
+hipError_t launch_pf_head_rows(const float* x, int H, const PfSegs& seg, int n, const float* gain,
+                               float* x_out, float* ssq_out, int Bmax, uint16_t* xo_hi,
+                               uint16_t* xo_lo, hipStream_t s);
+
 }  // namespace qd

@@ -128,6 +128,16 @@ struct qd_handle {
   int* stream_run_off = nullptr;     // [stream_grid][4]
   float* stream_amax_val = nullptr;  // [stream_grid]
   int* stream_amax_idx = nullptr;
+
+  // prompt chunks on the matrix cores (qd_prefill_prompts): pf_rows rows of
+  // residual stream, QKV output, q pairs and operand tiles (norm outputs and
+  // the attention output share pf_tin; the SwiGLU output is pf_tact)
+  int pf_rows = 0;
+  float* pf_x = nullptr;
+  float* pf_qkv = nullptr;
+  uint16_t *pf_q_hi = nullptr, *pf_q_lo = nullptr;
+  uint16_t* pf_tin = nullptr;
+  uint16_t* pf_tact = nullptr;
 };
 
 namespace {
@@ -253,6 +263,8 @@ int validate_config(const qd_config* c) {
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0))
     return fail(nullptr, QD_EINVAL, "rms_eps and rope_theta must be > 0");
   if (c->page_size != kPage) return fail(nullptr, QD_EUNSUPPORTED, "page_size must be 16");
+  if (c->max_prefill_rows < 0 || c->max_prefill_rows > kPfMaxRows)
+    return fail(nullptr, QD_EINVAL, "max_prefill_rows must be in 0..16384");
   if (c->hidden % 64 || c->hidden > 8192)
     return fail(nullptr, QD_EUNSUPPORTED, "hidden must be a multiple of 64 and at most 8192");
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -805,6 +817,75 @@ int check_step_args(qd_handle* h, int32_t batch, const void* a, const void* b, c
   return QD_OK;
 }
 
+// GEMM workgroup tile of an N-row projection over M input rows: the
+// largest of 128x128, 128x64, 64x128 and 64x64 (weight rows x input rows)
+// that still gives every CU a workgroup, else 64x64.
+void pf_tile(const qd_handle* h, int N, int M, int* wn, int* wm) {
+  static const int cand[4][2] = {{4, 4}, {4, 2}, {2, 4}, {2, 2}};
+  for (const auto& c : cand) {
+    const long long tiles = (long long)((N + 32 * c[0] - 1) / (32 * c[0])) * ((M + 32 * c[1] - 1) / (32 * c[1]));
+    if (tiles >= h->num_cus) { *wn = c[0]; *wm = c[1]; return; }
+  }
+  *wn = 2; *wm = 2;
+}
+
+hipError_t pf_gemm(qd_handle* h, int mode, const uint16_t* w, int N, int K, const uint16_t* x,
+                   int M, float* out, int ldo, uint16_t* act, hipStream_t s) {
+  int wn = 4, wm = 4;
+  pf_tile(h, N, M, &wn, &wm);
+  PfGemmArgs a{};
+  a.w = w; a.x = x; a.N = N; a.K = K; a.M = M;
+  a.nb_n = (N + 32 * wn - 1) / (32 * wn);
+  a.nb_m = (M + 32 * wm - 1) / (32 * wm);
+  a.out = out; a.ldo = ldo; a.act = act;
+  return launch_pf_gemm(a, mode, wn, wm, s);
+}
+
+// Enqueue a prompt chunk (qd_prefill_prompts) on the handle's stream.
+int record_prefill_prompts(qd_handle* h, const PfSegs& sg, const int32_t* tokens,
+                           const int32_t* tables, uint16_t* pool, int n_logits, int32_t* next,
+                           float* logits) {
+  hipStream_t s = h->stream;
+  const int L = h->L, H = h->H, I = h->I, M = sg.row0[sg.n];
+  const int Mt = (M + 15) / 16 * 16;
+  const float eps = h->cfg.rms_eps;
+  const size_t layer_elems = (size_t)h->cfg.num_pages * 2 * h->Hkv * kPage * h->D;
+  HIP_TRY(h, launch_pf_embed(h->embed, h->V, H, tokens, M, h->pf_x, h->dev_flags, s));
+  PfAttnArgs aa{};
+  aa.qkv = h->pf_qkv;
+  aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin;
+  aa.num_pages = h->cfg.num_pages;
+  aa.block_tables = tables; aa.max_pages = h->cfg.max_pages_per_seq;
+  aa.M = M; aa.Hq = h->Hq; aa.Hkv = h->Hkv;
+  aa.eps = eps; aa.scale = (float)(1.0 / std::sqrt((double)h->D));
+  aa.q_hi = h->pf_q_hi; aa.q_lo = h->pf_q_lo;
+  aa.out = h->pf_tin;
+  aa.dev_flags = h->dev_flags;
+  aa.seg = sg;
+  for (int l = 0; l < L; ++l) {
+    const LayerW& w = h->lw[l];
+    HIP_TRY(h, launch_pf_norm(h->pf_x, w.in_norm, H, M, Mt, eps, h->pf_tin, s));
+    HIP_TRY(h, pf_gemm(h, kPfStore, w.qkv, h->NQKV, H, h->pf_tin, M, h->pf_qkv, h->NQKV, nullptr, s));
+    aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
+    aa.pool_layer = pool + (size_t)l * layer_elems;
+    HIP_TRY(h, launch_pf_qk(aa, h->D, s));
+    HIP_TRY(h, launch_pf_attn(aa, h->D, h->G, s));
+    HIP_TRY(h, pf_gemm(h, kPfResid, w.o, H, h->QD, h->pf_tin, M, h->pf_x, H, nullptr, s));
+    HIP_TRY(h, launch_pf_norm(h->pf_x, w.post_norm, H, M, Mt, eps, h->pf_tin, s));
+    HIP_TRY(h, pf_gemm(h, kPfSwiGLU, w.gu, 2 * I, H, h->pf_tin, M, nullptr, 0, h->pf_tact, s));
+    HIP_TRY(h, pf_gemm(h, kPfResid, w.down, H, I, h->pf_tact, M, h->pf_x, H, nullptr, s));
+  }
+  if (n_logits > 0) {
+    // each segment's last row, in the decode step's buffers, then the step's LM head
+    const bool mfma = gemv_mfma(n_logits);
+    HIP_TRY(h, launch_pf_head_rows(h->pf_x, H, sg, n_logits, h->final_norm, h->x, h->ssq,
+                                   h->cfg.max_batch, mfma ? h->xg_hi : nullptr,
+                                   mfma ? h->xg_lo : nullptr, s));
+    HIP_TRY(h, launch_projection(h, n_logits, QD_PROF_LM_HEAD, 0, true, logits, next, s));
+  }
+  return QD_OK;
+}
+
 }  // namespace
 
 int qd::set_global_error(int code, const std::string& msg) {
@@ -995,6 +1076,23 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     if (e != hipSuccess) { hip_fail(h, e, "persistent state"); return bail(QD_EHIP); }
   }
 
+  // prompt-chunk workspace, zeroed once (operand-tile rows past a chunk's
+  // last are read by the GEMMs and must hold finite values)
+  if (cfg->max_prefill_rows > 0) {
+    const size_t Mp = (size_t)((cfg->max_prefill_rows + kPfRowAlign - 1) / kPfRowAlign) * kPfRowAlign;
+    h->pf_rows = (int)Mp;
+    const size_t tin = Mp * std::max(H, h->QD) * 2, tact = Mp * I * 2;
+    if ((rc = dev_alloc(h, &h->pf_x, Mp * H))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->pf_qkv, Mp * h->NQKV))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->pf_q_hi, Mp * h->QD))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->pf_q_lo, Mp * h->QD))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->pf_tin, tin))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->pf_tact, tact))) return bail(rc);
+    e = hipMemset(h->pf_tin, 0, tin * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMemset(h->pf_tact, 0, tact * sizeof(uint16_t));
+    if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
+  }
+
   // RoPE table: angle p * theta^(-2i/D) in double, cos/sin rounded once to fp32.
   h->max_pos = cfg->max_pages_per_seq * kPage;
   const int half = h->D / 2;
@@ -1178,6 +1276,42 @@ int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32
   StepPtrs sp{rows, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
               out_next_ids, out_logits, n_logits};
   return record_step(h, sp, nullptr, h->stream);
+}
+
+int qd_prefill_prompts(qd_handle* h, int32_t n_seqs, const int32_t* seq_rows,
+                       const int32_t* start_pos, const int32_t* token_ids,
+                       const int32_t* block_tables, void* kv_pool, int32_t n_logits,
+                       int32_t* out_next_ids, float* out_logits) {
+  if (!h) return QD_EINVAL;
+  if (h->pf_rows == 0)
+    return fail(h, QD_EUNSUPPORTED, "handle created with max_prefill_rows = 0");
+  if (n_seqs < 1 || n_seqs > kPfMaxSegs) return fail(h, QD_EINVAL, "n_seqs must be in 1..64");
+  if (!seq_rows || !start_pos || !token_ids || !block_tables || !kv_pool)
+    return fail(h, QD_EINVAL, "NULL prefill pointer");
+  if (n_logits < 0 || n_logits > n_seqs || n_logits > h->cfg.max_batch)
+    return fail(h, QD_EINVAL, "n_logits must be in 0..min(n_seqs, max_batch)");
+  if (n_logits > 0 && !out_next_ids) return fail(h, QD_EINVAL, "NULL out_next_ids");
+  std::string missing;
+  if (!all_loaded(h, &missing)) return fail(h, QD_ESTATE, "weight not loaded: " + missing);
+  PfSegs sg{};
+  sg.n = n_seqs;
+  long long rows = 0, qb = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (seq_rows[s] < 1) return fail(h, QD_EINVAL, "seq_rows must be >= 1");
+    if (start_pos[s] < 0 || (long long)start_pos[s] + seq_rows[s] > h->max_pos)
+      return fail(h, QD_EINVAL, "segment positions past max_pages_per_seq * 16");
+    sg.row0[s] = (int)rows;
+    sg.pos0[s] = start_pos[s];
+    sg.qb0[s] = (int)qb;
+    rows += seq_rows[s];
+    qb += (seq_rows[s] + 15) / 16;
+    if (rows > h->cfg.max_prefill_rows)
+      return fail(h, QD_EINVAL, "rows of all segments exceed max_prefill_rows");
+  }
+  sg.row0[n_seqs] = (int)rows;
+  sg.qb0[n_seqs] = (int)qb;
+  return record_prefill_prompts(h, sg, token_ids, block_tables, static_cast<uint16_t*>(kv_pool),
+                                n_logits, out_next_ids, out_logits);
 }
 
 int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,

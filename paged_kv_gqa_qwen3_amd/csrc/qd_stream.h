@@ -27,33 +27,11 @@
 
 namespace qd {
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// the wave are outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr unsigned vmcnt_imm(int n) {
-  return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | 0x70u | 0xF00u;
-}
-// ... and until every LDS / scalar-memory operation is done (vmcnt at its maximum).
-constexpr unsigned kLgkmZero = 15u | (3u << 14) | 0x70u;
-
 // 4-float groups of a staged input per thread: inputs up to 16384 floats.
 constexpr int kStageVec = kStreamStageVec;
 // ... and of an RMSNorm gain (the hidden size: at most 8192 floats).
 constexpr int kGainVec = 8;
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// makes global stores visible, and even a fence limited to LDS counts the
-// ring's direct-to-LDS loads as LDS writes: both wait for every outstanding
-// vector memory operation of the wave, which would drain the ring.  The
-// stream kernel's barriers only hand data written with ds_write between
-// waves (each ring slot is read only by the wave that loads it), so waiting
-// for the wave's LDS operations is enough; the signal fences keep the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(kLgkmZero);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // The wave's ring: its slots, the loader (position and counts) and the
 // slot the consumer reads next.

@@ -43,7 +43,7 @@ class Decoder:
 
     def __init__(self, shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
                  use_graphs: bool = True, stream: Optional[int] = None,
-                 persistent: bool = False):
+                 persistent: bool = False, max_prefill_rows: int = 0):
         torch = _torch()
         self.shape = shape
         self.max_batch = max_batch
@@ -52,7 +52,7 @@ class Decoder:
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
         self.cfg = binding.make_config(shape, max_batch, max_pages_per_seq, num_pages,
-                                       use_graphs, persistent)
+                                       use_graphs, persistent, max_prefill_rows)
         self.handle = binding.qd_create(self.cfg, stream)
 
     def load_numpy_weights(self, weights: Dict[str, np.ndarray], chunk: int = 24) -> None:
@@ -75,6 +75,15 @@ class Decoder:
         0..n_logits-1 get logits and greedy next ids."""
         binding.qd_prefill(self.handle, int(tokens.shape[0]), tokens, positions, tables, pool,
                            int(n_logits), next_ids, logits)
+
+    def prefill_prompts(self, seq_rows, start_pos, tokens, tables, pool, n_logits=0,
+                        next_ids=None, logits=None) -> None:
+        """Prompt segments packed back to back (qd_prefill_prompts): segment s
+        is seq_rows[s] tokens at positions start_pos[s].. with block-table row
+        tables[s]; segments 0..n_logits-1 get their last row's logits and
+        greedy next id."""
+        binding.qd_prefill_prompts(self.handle, seq_rows, start_pos, tokens, tables, pool,
+                                   int(n_logits), next_ids, logits)
 
     def step_taps(self, tokens, positions, tables, pool, next_ids, logits, taps, layer):
         binding.qd_decode_step_taps(self.handle, int(tokens.shape[0]), tokens, positions,

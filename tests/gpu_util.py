@@ -65,3 +65,30 @@ def bf16_rne_of_f32(x: np.ndarray) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def kv_tol(b):
+    """Appended K/V rows (one head_dim row each): bf16 rounding of either side
+    (2^-7 relative) plus the projection's own error, which the MFMA path's
+    bf16-pair input (about 2^-17 relative per term) can amplify by
+    cancellation in small entries: 2^-10 of the row's largest entry."""
+    return 2.0 ** -7 * np.abs(b) + 2.0 ** -10 * np.abs(b).max(axis=-1, keepdims=True) + 1e-6
+
+
+def assert_kv_close(a, b, what=""):
+    """a within kv_tol(b) of b; on failure, name the worst entry."""
+    tol = kv_tol(b)
+    r = np.abs(a - b) / tol
+    if not np.all(r <= 1.0):
+        i = np.unravel_index(int(np.argmax(r)), r.shape)
+        raise AssertionError(f"{what}: KV entry {tuple(int(v) for v in i)} got {a[i]!r} "
+                             f"want {b[i]!r} (tol {tol[i]:.3g}); "
+                             f"{int((r > 1).sum())} entries out of tolerance")
+
+
+def appended_mask(batch, pairs):
+    """Pool rows (layer, page, K|V, head, slot) written for (sequence, position) pairs."""
+    m = np.zeros(batch.pool.shape[:5], dtype=bool)
+    for b, p in pairs:
+        m[:, batch.block_tables[b, p // 16], :, :, p % 16] = True
+    return m

@@ -55,6 +55,8 @@ def _cfg(**kw):
     ("num_layers", 0, binding.QD_EINVAL),
     ("hidden", 8256, binding.QD_EUNSUPPORTED),
     ("max_pages_per_seq", 4097, binding.QD_EUNSUPPORTED),
+    ("max_prefill_rows", -1, binding.QD_EINVAL),
+    ("max_prefill_rows", 16385, binding.QD_EINVAL),
 ])
 def test_create_rejects_bad_config(lib, field, value, code):
     h = ctypes.c_void_p()
@@ -73,4 +75,6 @@ def test_null_arguments(lib):
     assert lib.qd_load_weights(None, None, 0) == binding.QD_EINVAL
     assert lib.qd_sample(None, 1, None, None, None, None, None, None) == binding.QD_EINVAL
     assert lib.qd_prefill(None, 1, None, None, None, None, 0, None, None) == binding.QD_EINVAL
+    assert lib.qd_prefill_prompts(None, 1, None, None, None, None, None, 0, None,
+                                  None) == binding.QD_EINVAL
     lib.qd_destroy(None)

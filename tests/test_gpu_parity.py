@@ -20,8 +20,9 @@ import pytest
 import oracle
 from paged_kv_gqa_qwen3_amd import binding, synth
 from paged_kv_gqa_qwen3_amd.decoder import Decoder, pool_to_device, pool_to_host
-from gpu_util import (LOGIT_RTOL, bf16_rne_of_f32, check_logits, check_next_ids, gemv_tol,
-                      say)
+from gpu_util import (LOGIT_RTOL, appended_mask as _appended_mask,
+                      assert_kv_close as _assert_kv_close, bf16_rne_of_f32, check_logits,
+                      check_next_ids, gemv_tol, kv_tol as _kv_tol, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,33 +58,6 @@ class StepIO:
 
     def run(self, dec, pool):
         dec.step(self.tok, self.pos, self.tab, pool, self.nxt, self.logits)
-
-
-def _kv_tol(b):
-    """Appended K/V rows (one head_dim row each): bf16 rounding of either side
-    (2^-7 relative) plus the projection's own error, which the MFMA path's
-    bf16-pair input (about 2^-17 relative per term) can amplify by
-    cancellation in small entries: 2^-10 of the row's largest entry."""
-    return 2.0 ** -7 * np.abs(b) + 2.0 ** -10 * np.abs(b).max(axis=-1, keepdims=True) + 1e-6
-
-
-def _assert_kv_close(a, b, what=""):
-    """a within _kv_tol(b) of b; on failure, name the worst entry."""
-    tol = _kv_tol(b)
-    r = np.abs(a - b) / tol
-    if not np.all(r <= 1.0):
-        i = np.unravel_index(int(np.argmax(r)), r.shape)
-        raise AssertionError(f"{what}: KV entry {tuple(int(v) for v in i)} got {a[i]!r} "
-                             f"want {b[i]!r} (tol {tol[i]:.3g}); "
-                             f"{int((r > 1).sum())} entries out of tolerance")
-
-
-def _appended_mask(batch, pairs):
-    """Pool rows (layer, page, K|V, head, slot) written for (sequence, position) pairs."""
-    m = np.zeros(batch.pool.shape[:5], dtype=bool)
-    for b, p in pairs:
-        m[:, batch.block_tables[b, p // 16], :, :, p % 16] = True
-    return m
 
 
 # ----------------------------------------------------------------------------- tiny workload

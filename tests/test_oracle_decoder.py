@@ -8,7 +8,10 @@
   append before attention, causal inclusive context, tied LM head, final norm).
   ``Oracle.prefill`` is pinned by the same forward: its logits and greedy id
   are those of the prompt's last position, and the pool it fills holds the
-  same bytes as the step-by-step loop's.
+  same bytes as the step-by-step loop's.  ``Oracle.prefill_chunk`` (a chunk's
+  rows as one batch, projections as numpy matrix products) gives every row's
+  logits of that forward, and agrees with ``decode_step`` on a continuation
+  chunk of shuffled rows from two sequences.
 * With the attention output and MLP output projections zeroed, the residual
   stream is the embedding, so logits reduce to E . rmsnorm(E[t]).
 * Sequences in a batch are independent, and physical page placement does not
@@ -102,6 +105,58 @@ def test_stepwise_paged_decode_equals_causal_forward(tied):
     assert np.abs(lg_p - want[-1]).max() <= 1e-10 * scale
     assert nxt_p == int(np.argmax(want[-1]))
     np.testing.assert_array_equal(pool_p, batch.pool)
+
+
+@pytest.mark.parametrize("tied", [True, False])
+def test_prefill_chunk_equals_causal_forward(tied):
+    """Oracle.prefill_chunk with a whole prompt as one chunk (every row a head
+    row) gives every position's logits of the library causal forward, and
+    fills the pool with the bytes of the one-position-at-a-time loop."""
+    shape = synth.ModelShape("t", 2, 128, 4, 2, 32, 192, 512, tied)
+    W = _weights(23, shape)
+    T = 37
+    prompt = synth.uniform_int(6, "prompt", shape.vocab, T)
+    batch = _fresh(shape, [0], T, 3, fill=False)
+    orc = oracle.Oracle(shape, W)
+    tables = np.repeat(batch.block_tables, T, axis=0)
+    lg, nxt = orc.prefill_chunk(prompt, np.arange(T, dtype=np.int32), tables, batch.pool, T)
+    want = _library_forward(shape, W, prompt)
+    scale = np.abs(want).max()
+    assert lg.shape == want.shape
+    assert np.abs(lg - want).max() <= 1e-10 * scale
+    np.testing.assert_array_equal(nxt, np.argmax(want, axis=1))
+    pool_s = _fresh(shape, [0], T, 3, fill=False).pool
+    orc.prefill(prompt, batch.block_tables[0], pool_s)
+    np.testing.assert_array_equal(batch.pool, pool_s)
+
+
+def test_prefill_chunk_matches_decode_step_rows():
+    """A continuation chunk: shuffled rows of two sequences whose earlier
+    positions are already in the pool.  prefill_chunk and decode_step (which
+    also appends every row before any row attends) agree on the head rows'
+    logits to fp64 rounding, on their ids, and on every pool byte; a smaller
+    n_head gives the leading rows' logits alone."""
+    W = _weights(61)
+    orc = oracle.Oracle(SHAPE, W)
+    batch = _fresh(SHAPE, [9, 20], 12, 7)
+    rows = [(0, 9 + i) for i in range(12)] + [(1, 20 + i) for i in range(7)]
+    order = np.random.default_rng(3).permutation(len(rows))
+    rows = [rows[i] for i in order]
+    tok = synth.uniform_int(8, "chunk", SHAPE.vocab, len(rows))
+    pos = np.array([p for _, p in rows], dtype=np.int32)
+    tab = batch.block_tables[[s for s, _ in rows]]
+    pool_a, pool_b = batch.pool.copy(), batch.pool.copy()
+    lg_a, nx_a, _ = orc.decode_step(tok, pos, tab, pool_a)
+    lg_b, nx_b = orc.prefill_chunk(tok, pos, tab, pool_b, len(rows))
+    assert np.abs(lg_b - lg_a).max() <= 1e-10 * np.abs(lg_a).max()
+    np.testing.assert_array_equal(nx_b, nx_a)
+    np.testing.assert_array_equal(pool_b, pool_a)
+    pool_c = batch.pool.copy()
+    lg_c, nx_c = orc.prefill_chunk(tok, pos, tab, pool_c, 3)
+    assert lg_c.shape == (3, SHAPE.vocab)
+    np.testing.assert_array_equal(lg_c, lg_b[:3])
+    np.testing.assert_array_equal(nx_c, nx_b[:3])
+    np.testing.assert_array_equal(pool_c, pool_a)
 
 
 def test_zeroed_blocks_reduce_to_embedding_logits():

@@ -408,6 +408,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing qd_prefill on a 512-token prompt (profiling runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time qd_prefill_prompts on a 512-token prompt of the headline "
+                         "model only, print its record and stop (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=("auto", "graph"), default="auto",
                     help="auto: a persistent handle, on which the library runs batch 1 as "
@@ -437,6 +440,14 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
+    if args.prefill_only:
+        shape = synth.WORKLOADS[HEADLINE].shape
+        W = synth.make_weights(shape, WEIGHT_SEED[shape.name])
+        rec = time_prefill_prompts(torch, shape, W, reps=args.reps)
+        log(f"[bench] qd_prefill_prompts of 512 prompt tokens {rec}")
+        print(json.dumps({"prefill": rec, "model": shape.name}))
+        torch.cuda.synchronize()
+        return
     names = [n for n in args.workloads.split(",") if n]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)

@@ -122,19 +122,28 @@ __global__ __launch_bounds__(256) void pf_norm_kernel(const float* x, const floa
 // 16x16).  K advances one 32-column k-tile per stage.  A stage is the
 // workgroup's 2*WN weight tiles and 2*WM input tiles (hi and lo), 1 KB
 // each, brought into LDS by direct global-to-LDS loads (the waves share
-// them out); S stages are in flight.  Each wave waits for its own loads of
-// a stage, then an LDS barrier makes every wave's tiles of that stage
-// visible and tells that the slot read in the previous stage is free.
+// them out); S stages are in flight, one workgroup per CU.  Each wave waits
+// for its own loads of the next stage, then an LDS barrier makes every
+// wave's tiles of that stage visible and tells that the stage just read
+// into registers is free for the loads S stages ahead.  A wave reads the
+// next stage's operands from LDS while its MFMAs consume the current one's
+// (two register sets, alternating).
 // Workgroups are laid out so that each XCD (workgroup w runs on XCD w mod 8)
 // takes a contiguous range of tiles, weight block by weight block: the
 // input-row blocks of one weight block run together on one XCD and the
 // later ones find the weight tiles in its L2.
+template <int WN, int WM>
+struct PfFrag {
+  bf16x8 a[WN];
+  bf16x8 b[WM][2];
+};
+
 template <int MODE, int WN, int WM, int S>
 __global__ __launch_bounds__(256) void pf_gemm_kernel(PfGemmArgs a) {
   constexpr int TA = 2 * WN, TB = 4 * WM, T = TA + TB;
   static_assert(T % 4 == 0, "the 4 waves share a stage's tiles evenly");
   constexpr int LPW = T / 4;
-  static_assert((S - 2) * LPW <= 63, "vmcnt range");
+  static_assert(S >= 2 && (S - 1) * LPW <= 63, "vmcnt range");
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
@@ -169,40 +178,69 @@ __global__ __launch_bounds__(256) void pf_gemm_kernel(PfGemmArgs a) {
           reinterpret_cast<const u32x4*>(src[u] + (size_t)kt * step[u]) + lane,
           smem + ((size_t)slot * T + wave + 4 * u) * 1024, 16, 0, 0);
   };
+  auto read_frag = [&](PfFrag<WN, WM>& f, int slot) {
+    const unsigned char* st = smem + (size_t)slot * T * 1024 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WN; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8*>(st + (wn * WN + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < WM; ++j)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        f.b[j][hl] = *reinterpret_cast<const bf16x8*>(st + (TA + (wm * WM + j) * 2 + hl) * 1024);
+  };
 
   f32x4 acc[WN][WM];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  auto mma = [&](const PfFrag<WN, WM>& f) {
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue(s, s);
-  for (int kt = 0; kt < KT; ++kt) {
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+      for (int j = 0; j < WM; ++j)
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j][hl], acc[i][j], 0, 0, 0);
+  };
+  // one k-tile kt < KT-1: make stage kt+1 visible, refill the slot of stage
+  // kt (already read into cur) with stage kt+S, read stage kt+1 into nxt,
+  // multiply cur.  (The last k-tile only multiplies: no branch inside the
+  // loop body, so the compiler sees that cur's LDS reads have completed.)
+  auto step_k = [&](int kt, const PfFrag<WN, WM>& cur, PfFrag<WN, WM>& nxt) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + S - 2 < KT)
+    if (kt + S - 1 <= KT - 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPW));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
-    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
-    const unsigned char* st = smem + (size_t)(kt % S) * T * 1024;
-    bf16x8 af[WN];
+    if (kt + S < KT) issue(kt + S, kt % S);
+    read_frag(nxt, (kt + 1) % S);
+    mma(cur);
+  };
+
 #pragma unroll
-    for (int i = 0; i < WN; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(st + (wn * WN + i) * 1024 + lane * 16);
-#pragma unroll
-    for (int j = 0; j < WM; ++j) {
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        const bf16x8 bf =
-            *reinterpret_cast<const bf16x8*>(st + (TA + (wm * WM + j) * 2 + hl) * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < WN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
-      }
-    }
+  for (int s = 0; s < S; ++s)
+    if (s < KT) issue(s, s);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (KT >= S)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * LPW));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  PfFrag<WN, WM> f0, f1;
+  read_frag(f0, 0);
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    step_k(kt, f0, f1);
+    step_k(kt + 1, f1, f0);
+  }
+  if (kt + 2 == KT) {
+    step_k(kt, f0, f1);
+    mma(f1);
+  } else {
+    mma(f0);
   }
 
   // epilogue: acc[i][j] lane l holds rows 4*(l/16)..+3 of weight row tile
@@ -355,8 +393,24 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     qf[kk][1] = *reinterpret_cast<const bf16x8*>(a.q_lo + o);
   }
 
+  // the item's page ids 64 at a time in a register (lane l: page 64c + l of
+  // chunk c), so that finding a page in the loop needs no memory round trip
+  // (a load there would have to wait for every K/V load in flight)
+  int tab_chunk = 0;
+  int tab_reg = lane < npages ? table[lane] : 0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // q fragments and page ids in registers
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   auto issue = [&](int pg, int slot) {
-    int page = table[pg];
+    if ((pg >> 6) != tab_chunk) {
+      tab_chunk = pg >> 6;
+      const int i = 64 * tab_chunk + lane;
+      tab_reg = i < npages ? table[i] : 0;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // once per 64 pages
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    int page = __builtin_amdgcn_readlane(tab_reg, pg & 63);
     if (page < 0 || page >= a.num_pages) {
       if (lane == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
       page = page < 0 ? 0 : a.num_pages - 1;
@@ -512,20 +566,27 @@ hipError_t launch_pf_norm(const float* x, const float* gain, int K, int M, int M
   return hipGetLastError();
 }
 
-constexpr int kPfStages = 3;
+// Stages of a GEMM workgroup: as many as 72 KB of LDS hold (two workgroups
+// per CU), within the vmcnt range.
+constexpr int pf_stages(int WN, int WM) {
+  const int T = 2 * WN + 4 * WM, lpw = T / 4;
+  const int by_lds = 72 / T, by_cnt = 63 / lpw + 1;
+  return by_lds < by_cnt ? by_lds : by_cnt;
+}
 
 template <int MODE, int WN, int WM>
 static hipError_t launch_pf_gemm_t(const PfGemmArgs& a, hipStream_t s) {
-  constexpr size_t lds = (size_t)kPfStages * (2 * WN + 4 * WM) * 1024;
+  constexpr int kStages = pf_stages(WN, WM);
+  constexpr size_t lds = (size_t)kStages * (2 * WN + 4 * WM) * 1024;
   static bool attr_set = false;
-  const void* fn = reinterpret_cast<const void*>(&pf_gemm_kernel<MODE, WN, WM, kPfStages>);
+  const void* fn = reinterpret_cast<const void*>(&pf_gemm_kernel<MODE, WN, WM, kStages>);
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = a.nb_n * a.nb_m;
-  hipLaunchKernelGGL((pf_gemm_kernel<MODE, WN, WM, kPfStages>), dim3(8 * ((tiles + 7) / 8)),
+  hipLaunchKernelGGL((pf_gemm_kernel<MODE, WN, WM, kStages>), dim3(8 * ((tiles + 7) / 8)),
                      dim3(256), lds, s, a);
   return hipGetLastError();
 }

@@ -33,6 +33,14 @@ import sys
 # Kernel-name substrings -> class (first match wins); GEMV launches are
 # classed by their epilogue (the second template argument, any batch width).
 CLASSES = (
+    ("pf_gemm_kernel<0", "pf_qkv"),
+    ("pf_gemm_kernel<1", "pf_o+down"),
+    ("pf_gemm_kernel<2", "pf_gate_up"),
+    ("pf_attn_kernel", "pf_attention"),
+    ("pf_qk_kernel", "pf_qk_rope"),
+    ("pf_norm_kernel", "pf_norm"),
+    ("pf_embed_kernel", "pf_embed"),
+    ("pf_head_rows_kernel", "pf_head_rows"),
     ("stream_step_kernel", "stream_step"),
     ("fused_mlp_kernel", "gate_up+down"),
     ("read_ceiling_kernel", "read_ceiling"),

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` may use it; the GPU library never does.  It
 shares no code with the GPU path.  The arithmetic lives in ``qd_oracle.c``
 (plain loops, fp64 throughout; only the weights and the KV pool are bf16, as
-the pages fix); this module marshals numpy arrays into it.
+the pages fix, or the pool is OCP E4M3 with per-tensor K and V scales for the
+FP8 variant); this module marshals numpy arrays into it.
 
 Every function here is pinned by tests under ``tests/`` against closed forms,
 invariants, library routines or brute force (see the test module docstrings).
@@ -57,6 +58,28 @@ class _Weights(ctypes.Structure):
                 ("layers", ctypes.POINTER(_Layer))]
 
 
+class _Kv(ctypes.Structure):
+    _fields_ = [("fp8", ctypes.c_int), ("k_scale", ctypes.c_double), ("v_scale", ctypes.c_double)]
+
+
+class KvFormat:
+    """Element type of a KV pool: bf16 (the default), or OCP E4M3 ("fp8")
+    with one scale for K and one for V (stored code = E4M3(value / scale))."""
+
+    def __init__(self, fp8: bool = False, k_scale: float = 1.0, v_scale: float = 1.0):
+        self.fp8, self.k_scale, self.v_scale = bool(fp8), float(k_scale), float(v_scale)
+
+    def _c(self):
+        return _Kv(int(self.fp8), self.k_scale, self.v_scale)
+
+    @property
+    def dtype(self):
+        return np.uint8 if self.fp8 else np.uint16
+
+
+BF16 = KvFormat()
+
+
 class _Taps(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_int)] + [
         (n, _P) for n in ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out",
@@ -84,7 +107,16 @@ def _load():
         lib.or_rope_neox.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.or_attention.restype = None
         lib.or_attention.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P,
-                                     ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P]
+                                     ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P,
+                                     ctypes.POINTER(_Kv)]
+        lib.or_e4m3_to_f64.restype = ctypes.c_double
+        lib.or_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.or_f64_to_e4m3.restype = ctypes.c_uint8
+        lib.or_f64_to_e4m3.argtypes = [ctypes.c_double]
+        lib.or_f64_to_e4m3_n.restype = None
+        lib.or_f64_to_e4m3_n.argtypes = [_P, ctypes.c_int64, _P]
+        lib.or_e4m3_to_f64_n.restype = None
+        lib.or_e4m3_to_f64_n.argtypes = [_P, ctypes.c_int64, _P]
         lib.or_silu.restype = ctypes.c_double
         lib.or_silu.argtypes = [ctypes.c_double]
         lib.or_f64_to_bf16_n.restype = None
@@ -96,7 +128,8 @@ def _load():
         lib.or_decode_step.restype = ctypes.c_int
         lib.or_decode_step.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights),
                                        ctypes.c_int, _P, _P, _P, ctypes.c_int, _P,
-                                       ctypes.c_int, _P, _P, ctypes.POINTER(_Taps)]
+                                       ctypes.c_int, _P, _P, ctypes.POINTER(_Taps),
+                                       ctypes.POINTER(_Kv)]
         _lib = lib
     return _lib
 
@@ -127,6 +160,34 @@ def f64_to_bf16(x) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint16)
     lib.or_f64_to_bf16_n(x.ctypes.data, x.size, out.ctypes.data)
     return out
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP E4M3 codes -> exact float64 values (NaN for 0x7F / 0xFF)."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.or_e4m3_to_f64_n(c.ctypes.data, c.size, out.ctypes.data)
+    return out
+
+
+def f64_to_e4m3(x) -> np.ndarray:
+    """float64 -> nearest E4M3 code (ties to even, saturating at +-448)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib.or_f64_to_e4m3_n(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def pool_values(pool, kv: "KvFormat" = BF16) -> np.ndarray:
+    """The values a pool [L][P][2][Hkv][16][D] holds, as float64."""
+    if not kv.fp8:
+        return bf16_to_f64(pool)
+    v = e4m3_to_f64(pool)
+    v[:, :, 0] *= kv.k_scale
+    v[:, :, 1] *= kv.v_scale
+    return v
 
 
 def rmsnorm(x, gain_bf16, eps: float = 1e-6) -> np.ndarray:
@@ -166,18 +227,20 @@ def rope_neox(v, pos: int, theta: float = 1e6) -> np.ndarray:
     return v
 
 
-def attention(q, pool, layer: int, table_row, ctx: int, num_kv_heads: int) -> np.ndarray:
-    """q [Hq, D] float64; pool uint16 [L][P][2][Hkv][16][D]; -> o [Hq, D]."""
+def attention(q, pool, layer: int, table_row, ctx: int, num_kv_heads: int,
+              kv: "KvFormat" = BF16) -> np.ndarray:
+    """q [Hq, D] float64; pool [L][P][2][Hkv][16][D] of kv's type; -> o [Hq, D]."""
     lib = _load()
     q = _f64(q)
-    pool = _req(pool, np.uint16)
+    pool = _req(pool, kv.dtype)
     row = _req(np.asarray(table_row, dtype=np.int32), np.int32)
     Hq, D = q.shape
     assert pool.shape[3] == num_kv_heads and pool.shape[5] == D and pool.shape[4] == PAGE
     assert len(row) * PAGE >= ctx
     o = np.empty_like(q)
+    ckv = kv._c()
     lib.or_attention(q.ctypes.data, Hq, num_kv_heads, D, pool.ctypes.data, pool.shape[1],
-                     layer, row.ctypes.data, ctx, o.ctypes.data)
+                     layer, row.ctypes.data, ctx, o.ctypes.data, ctypes.byref(ckv))
     return o
 
 
@@ -235,8 +298,9 @@ class Oracle:
                            ctypes.cast(layers, ctypes.POINTER(_Layer)))
 
     def decode_step(self, tokens, positions, block_tables, pool: np.ndarray,
-                    want_logits: bool = True, tap_layer: Optional[int] = None):
-        """One decode step; appends to ``pool`` in place.
+                    want_logits: bool = True, tap_layer: Optional[int] = None,
+                    kv: KvFormat = BF16):
+        """One decode step; appends to ``pool`` (of kv's type) in place.
 
         Returns (logits [B, V] float64 or None, next [B] int32, taps dict)."""
         lib = _load()
@@ -244,7 +308,7 @@ class Oracle:
         tokens = np.ascontiguousarray(tokens, dtype=np.int32)
         positions = np.ascontiguousarray(positions, dtype=np.int32)
         tables = np.ascontiguousarray(block_tables, dtype=np.int32)
-        pool = _req(pool, np.uint16)
+        pool = _req(pool, kv.dtype)
         B = tokens.shape[0]
         assert positions.shape == (B,) and tables.shape[0] == B
         assert pool.shape[0] == s.num_layers and pool.shape[2] == 2
@@ -266,12 +330,13 @@ class Oracle:
                                 tokens.ctypes.data, positions.ctypes.data, tables.ctypes.data,
                                 tables.shape[1], pool.ctypes.data, pool.shape[1],
                                 logits.ctypes.data if logits is not None else None,
-                                nxt.ctypes.data, ctypes.byref(tp) if tp is not None else None)
+                                nxt.ctypes.data, ctypes.byref(tp) if tp is not None else None,
+                                ctypes.byref(kv._c()))
         if rc != 0:
             raise ValueError("oracle rejected the step arguments")
         return logits, nxt, taps
 
-    def prefill(self, prompt, block_table_row, pool: np.ndarray):
+    def prefill(self, prompt, block_table_row, pool: np.ndarray, kv: KvFormat = BF16):
         """Run the prompt through the decoder one position at a time (0..T-1),
         filling the pool; returns (logits of the last position, greedy next id)."""
         prompt = np.asarray(prompt, dtype=np.int32)
@@ -279,10 +344,11 @@ class Oracle:
         logits = nxt = None
         for t in range(len(prompt)):
             logits, nxt, _ = self.decode_step(prompt[t:t + 1], np.array([t], np.int32), row,
-                                              pool, want_logits=(t == len(prompt) - 1))
+                                              pool, want_logits=(t == len(prompt) - 1), kv=kv)
         return logits[0], int(nxt[0])
 
-    def prefill_chunk(self, tokens, positions, block_tables, pool: np.ndarray, n_head: int):
+    def prefill_chunk(self, tokens, positions, block_tables, pool: np.ndarray, n_head: int,
+                      kv: KvFormat = BF16):
         """The rows of a chunk through the layers as one batch, as
         ``decode_step`` runs its rows: per layer every row's K/V is appended at
         its position before any row attends, so rows of one sequence at
@@ -301,7 +367,7 @@ class Oracle:
         tokens = np.asarray(tokens, dtype=np.int32)
         positions = np.asarray(positions, dtype=np.int32)
         tables = np.ascontiguousarray(block_tables, dtype=np.int32)
-        pool = _req(pool, np.uint16)
+        pool = _req(pool, kv.dtype)
         B = tokens.shape[0]
         H, Hq, Hkv, D = s.hidden, s.num_q_heads, s.num_kv_heads, s.head_dim
         eps, theta = s.rms_eps, s.rope_theta
@@ -322,7 +388,10 @@ class Oracle:
             for b in range(B):
                 q[b] = rope_neox(q[b], int(positions[b]), theta)
                 k[b] = rope_neox(k[b], int(positions[b]), theta)
-            kb, vb = f64_to_bf16(k), f64_to_bf16(v)
+            if kv.fp8:
+                kb, vb = f64_to_e4m3(k / kv.k_scale), f64_to_e4m3(v / kv.v_scale)
+            else:
+                kb, vb = f64_to_bf16(k), f64_to_bf16(v)
             for b in range(B):
                 pos = int(positions[b])
                 page = int(tables[b][pos // PAGE])
@@ -330,7 +399,7 @@ class Oracle:
                     raise ValueError("block-table entry outside the pool")
                 pool[l, page, 0, :, pos % PAGE, :] = kb[b]
                 pool[l, page, 1, :, pos % PAGE, :] = vb[b]
-            att = np.stack([attention(q[b], pool, l, tables[b], int(positions[b]) + 1, Hkv)
+            att = np.stack([attention(q[b], pool, l, tables[b], int(positions[b]) + 1, Hkv, kv)
                             for b in range(B)]).reshape(B, Hq * D)
             x = x + att @ mat(p + "self_attn.o_proj.weight").T
             h2 = rmsnorm(x, W[p + "post_attention_layernorm.weight"], eps)

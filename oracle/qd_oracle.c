@@ -28,11 +28,18 @@
  *   SwiGLU silu(gate)*up          blog Part 6, bullet list
  *   greedy next token = argmax of the logits on the last position
  *                                 blog Part 3 item 1, Part 7
+ *   FP8 KV pool (optional): K and V quantised to 8-bit floating point
+ *                                 "推理引擎里面发生了什么", Tensor Core：精度即吞吐
+ *                                 and Quantization 对 Kernel 的影响
  * Readings where the pages are silent: a final RMSNorm before the LM head;
  * no projection biases; q/k norm gains of length head_dim shared by all
  * heads, eps 1e-6; RoPE inverse frequency theta^(-2i/D) for pair (i, i+D/2);
  * the current token attends to itself (context = position + 1); argmax ties
- * go to the lowest index.
+ * go to the lowest index.  The FP8 pool's format is not named: it is read as
+ * OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, NaN = S.1111.111, largest finite 448), one scale for all of K
+ * and one for all of V (stored code = E4M3(value / scale), round to nearest
+ * even, saturating at +-448; read value = code * scale).
  */
 #include <math.h>
 #include <stdint.h>
@@ -69,6 +76,47 @@ uint16_t or_f64_to_bf16(double v) {
   uint32_t u;
   memcpy(&u, &f, 4);
   return (uint16_t)(u >> 16);
+}
+
+/* OCP E4M3 code -> exact value.  Exponent field e (bias 7), mantissa m:
+ * e = 0 is subnormal, m * 2^-9; e = 15 with m = 7 is NaN; otherwise
+ * (1 + m/8) * 2^(e-7). */
+double or_e4m3_to_f64(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest E4M3 code of v, ties to even, in one rounding step; magnitudes
+ * beyond the largest finite value (448) saturate to it; NaN gives 0x7F.
+ * Near |v| = f*2^x (f in [0.5,1)) the spacing of E4M3 values is 2^(x-4) for
+ * normal results and 2^-9 below 2^-6 (subnormals), so v divided by that
+ * spacing is rounded to an integer with nearbyint (half to even in the
+ * default mode) and multiplied back, exactly. */
+uint8_t or_f64_to_e4m3(double v) {
+  if (isnan(v)) return 0x7F;
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return sign | 0x7E;
+  int x;
+  frexp(a, &x);
+  int qexp = x - 4;
+  if (qexp < -9) qexp = -9;
+  double q = ldexp(nearbyint(ldexp(a, -qexp)), qexp);
+  if (q > 448.0) q = 448.0; /* (cannot happen below 464; kept for clarity) */
+  /* q is now an E4M3 value: find its code */
+  if (q < ldexp(1.0, -6)) return sign | (uint8_t)(q * 512.0);  /* subnormal, or 2^-6 as m = 8 */
+  int e2;
+  double f = frexp(q, &e2);  /* q = f * 2^e2, f in [0.5, 1) */
+  const int e = e2 - 1 + 7;
+  const int m = (int)((2.0 * f - 1.0) * 8.0);
+  return sign | (uint8_t)((e << 3) | m);
 }
 
 /* y = x / sqrt(mean(x^2) + eps) * g */
@@ -109,20 +157,42 @@ void or_rope_neox(double* v, int D, int pos, double theta) {
   }
 }
 
-static inline const uint16_t* pool_row(const uint16_t* pool, int num_pages, int Hkv,
-                                       int D, int layer, int page, int kv, int head,
-                                       int slot) {
-  return pool + (((((int64_t)layer * num_pages + page) * 2 + kv) * Hkv + head) * OR_PAGE +
-                 slot) * D;
+/* Element type of the pool: NULL or fp8 = 0 is bf16; fp8 = 1 is OCP E4M3
+ * with one scale for K and one for V. */
+typedef struct or_kv {
+  int fp8;
+  double k_scale, v_scale;
+} or_kv;
+
+/* Element index of the first of the D values of (layer, page, K|V, head, slot). */
+static inline int64_t pool_index(int num_pages, int Hkv, int D, int layer, int page, int kv,
+                                 int head, int slot) {
+  return ((((int64_t)layer * num_pages + page) * 2 + kv) * Hkv + head) * OR_PAGE * D +
+         (int64_t)slot * D;
+}
+
+/* The value the pool holds at element i (which = 0 for K, 1 for V). */
+static inline double pool_get(const void* pool, const or_kv* kv, int64_t i, int which) {
+  if (!kv || !kv->fp8) return or_bf16_to_f64(((const uint16_t*)pool)[i]);
+  return or_e4m3_to_f64(((const uint8_t*)pool)[i]) * (which ? kv->v_scale : kv->k_scale);
+}
+
+/* Store v at element i, rounded to the pool's type. */
+static inline void pool_put(void* pool, const or_kv* kv, int64_t i, int which, double v) {
+  if (!kv || !kv->fp8)
+    ((uint16_t*)pool)[i] = or_f64_to_bf16(v);
+  else
+    ((uint8_t*)pool)[i] = or_f64_to_e4m3(v / (which ? kv->v_scale : kv->k_scale));
 }
 
 /* Paged GQA decode attention for one sequence.
  * q: [Hq][D]; the sequence's tokens 0..ctx-1 are read from the pool through
  * its block-table row (token t: page table_row[t/16], slot t%16).  Query head
- * h uses KV head h / (Hq/Hkv).  o: [Hq][D]. */
-void or_attention(const double* q, int Hq, int Hkv, int D, const uint16_t* pool,
+ * h uses KV head h / (Hq/Hkv).  o: [Hq][D].  kv: the pool's element type
+ * (NULL: bf16). */
+void or_attention(const double* q, int Hq, int Hkv, int D, const void* pool,
                   int num_pages, int layer, const int32_t* table_row, int ctx,
-                  double* o) {
+                  double* o, const or_kv* kv) {
   int G = Hq / Hkv;
   double scale = 1.0 / sqrt((double)D);
 #pragma omp parallel for schedule(static)
@@ -132,10 +202,10 @@ void or_attention(const double* q, int Hq, int Hkv, int D, const uint16_t* pool,
     const double* qh = q + (int64_t)h * D;
     double mx = -INFINITY;
     for (int t = 0; t < ctx; ++t) {
-      const uint16_t* kr = pool_row(pool, num_pages, Hkv, D, layer,
-                                    table_row[t / OR_PAGE], 0, g, t % OR_PAGE);
+      const int64_t kr = pool_index(num_pages, Hkv, D, layer, table_row[t / OR_PAGE], 0, g,
+                                    t % OR_PAGE);
       double acc = 0.0;
-      for (int d = 0; d < D; ++d) acc += qh[d] * or_bf16_to_f64(kr[d]);
+      for (int d = 0; d < D; ++d) acc += qh[d] * pool_get(pool, kv, kr + d, 0);
       s[t] = acc * scale;
       if (s[t] > mx) mx = s[t];
     }
@@ -147,10 +217,10 @@ void or_attention(const double* q, int Hq, int Hkv, int D, const uint16_t* pool,
     double* oh = o + (int64_t)h * D;
     for (int d = 0; d < D; ++d) oh[d] = 0.0;
     for (int t = 0; t < ctx; ++t) {
-      const uint16_t* vr = pool_row(pool, num_pages, Hkv, D, layer,
-                                    table_row[t / OR_PAGE], 1, g, t % OR_PAGE);
+      const int64_t vr = pool_index(num_pages, Hkv, D, layer, table_row[t / OR_PAGE], 1, g,
+                                    t % OR_PAGE);
       double w = s[t] / den;
-      for (int d = 0; d < D; ++d) oh[d] += w * or_bf16_to_f64(vr[d]);
+      for (int d = 0; d < D; ++d) oh[d] += w * pool_get(pool, kv, vr + d, 1);
     }
     free(s);
   }
@@ -163,6 +233,14 @@ double or_silu(double z) { return z / (1.0 + exp(-z)); }
  * C once per element). */
 void or_f64_to_bf16_n(const double* x, int64_t n, uint16_t* y) {
   for (int64_t i = 0; i < n; ++i) y[i] = or_f64_to_bf16(x[i]);
+}
+
+void or_f64_to_e4m3_n(const double* x, int64_t n, uint8_t* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = or_f64_to_e4m3(x[i]);
+}
+
+void or_e4m3_to_f64_n(const uint8_t* c, int64_t n, double* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = or_e4m3_to_f64(c[i]);
 }
 
 void or_silu_n(const double* z, int64_t n, double* y) {
@@ -204,7 +282,7 @@ typedef struct or_taps {
   double* x_in;   /* [B][H] residual entering the layer */
   double* qkv;    /* [B][(Hq+2Hkv)D] projections q | k | v */
   double* q_rot;  /* [B][Hq][D] after q-norm and RoPE */
-  double* k_rot;  /* [B][Hkv][D] after k-norm and RoPE, before bf16 rounding */
+  double* k_rot;  /* [B][Hkv][D] after k-norm and RoPE, before rounding to the pool type */
   double* attn;   /* [B][Hq][D] attention output */
   double* x_mid;  /* [B][H] residual after the attention block */
   double* act;    /* [B][I] silu(gate) * up */
@@ -215,11 +293,12 @@ typedef struct or_taps {
 /* One decode step for B sequences.  Sequence b decodes token tokens[b] at
  * position positions[b]; its K/V for that position are appended to the pool
  * and attention spans positions 0..positions[b].  logits: [B][V] (may be
- * NULL), next: [B].  Returns 0, or -1 on bad arguments. */
+ * NULL), next: [B].  kv: the pool's element type (NULL: bf16).  Returns 0,
+ * or -1 on bad arguments. */
 int or_decode_step(const or_config* c, const or_weights* w, int B, const int32_t* tokens,
                    const int32_t* positions, const int32_t* block_tables, int max_pages,
-                   uint16_t* pool, int num_pages, double* logits, int32_t* next,
-                   const or_taps* taps) {
+                   void* pool, int num_pages, double* logits, int32_t* next,
+                   const or_taps* taps, const or_kv* kv) {
   const int L = c->num_layers, H = c->hidden, Hq = c->num_q_heads, Hkv = c->num_kv_heads;
   const int D = c->head_dim, I = c->intermediate, V = c->vocab;
   if (B <= 0 || Hq % Hkv != 0 || D % 2 != 0) return -1;
@@ -277,19 +356,17 @@ int or_decode_step(const or_config* c, const or_weights* w, int B, const int32_t
     }
     if (tap && taps->q_rot) memcpy(taps->q_rot, q, sizeof(double) * B * QD);
     if (tap && taps->k_rot) memcpy(taps->k_rot, k, sizeof(double) * B * KD);
-    /* append this step's K/V (bf16) at each sequence's position */
+    /* append this step's K/V (rounded to the pool's type) at each sequence's position */
     for (int b = 0; b < B; ++b) {
       int pos = positions[b];
       int page = block_tables[(int64_t)b * max_pages + pos / OR_PAGE];
       if (page < 0 || page >= num_pages) goto bad;
       for (int g = 0; g < Hkv; ++g) {
-        uint16_t* kd = (uint16_t*)pool_row(pool, num_pages, Hkv, D, l, page, 0, g,
-                                           pos % OR_PAGE);
-        uint16_t* vd = (uint16_t*)pool_row(pool, num_pages, Hkv, D, l, page, 1, g,
-                                           pos % OR_PAGE);
+        const int64_t kd = pool_index(num_pages, Hkv, D, l, page, 0, g, pos % OR_PAGE);
+        const int64_t vd = pool_index(num_pages, Hkv, D, l, page, 1, g, pos % OR_PAGE);
         for (int d = 0; d < D; ++d) {
-          kd[d] = or_f64_to_bf16(k[(int64_t)b * KD + (int64_t)g * D + d]);
-          vd[d] = or_f64_to_bf16(v[(int64_t)b * KD + (int64_t)g * D + d]);
+          pool_put(pool, kv, kd + d, 0, k[(int64_t)b * KD + (int64_t)g * D + d]);
+          pool_put(pool, kv, vd + d, 1, v[(int64_t)b * KD + (int64_t)g * D + d]);
         }
       }
     }
@@ -299,7 +376,7 @@ int or_decode_step(const or_config* c, const or_weights* w, int B, const int32_t
       for (int t = 0; t < (ctx + OR_PAGE - 1) / OR_PAGE; ++t)
         if (row[t] < 0 || row[t] >= num_pages) goto bad;
       or_attention(q + (int64_t)b * QD, Hq, Hkv, D, pool, num_pages, l, row, ctx,
-                   att + (int64_t)b * QD);
+                   att + (int64_t)b * QD, kv);
     }
     if (tap && taps->attn) memcpy(taps->attn, att, sizeof(double) * B * QD);
     or_linear(att, B, QD, ly->wo, H, tmp);

@@ -115,6 +115,43 @@ void synth_fill_pool(uint64_t key, double stdv, uint16_t* pool, int L, int P,
   }
 }
 
+/* The same slots of an 8-bit pool (OCP E4M3 codes) filled with random codes
+ * drawn directly as bit fields: a random sign, an exponent field in 3..8 and
+ * a random 3-bit mantissa, i.e. magnitudes 2^-4 .. 3.75 and never a NaN
+ * code.  (No rounding: the codes themselves are the random draw.) */
+void synth_fill_pool_fp8(uint64_t key, uint8_t* pool, int L, int P, int Hkv, int page, int D,
+                         int nseq, const int32_t* ctx, const int32_t* table, int maxp,
+                         int tmax) {
+  int64_t rows = (int64_t)L * 2 * Hkv * nseq * tmax;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t rr = r;
+    int t = (int)(rr % tmax); rr /= tmax;
+    int s = (int)(rr % nseq); rr /= nseq;
+    int hd = (int)(rr % Hkv); rr /= Hkv;
+    int kv = (int)(rr % 2); rr /= 2;
+    int l = (int)rr;
+    if (t >= ctx[s]) continue;
+    int pg = table[(int64_t)s * maxp + t / page];
+    uint8_t* dst = pool + ((((((int64_t)l * P + pg) * 2 + kv) * Hkv + hd) * page +
+                            (t % page)) * D);
+    int64_t base = r * D;
+    for (int d = 0; d < D; ++d) {
+      uint64_t w = word_at(key, (uint64_t)(base + d));
+      unsigned sign = (unsigned)(w >> 63) << 7;
+      unsigned e = 3 + (unsigned)((w >> 8) % 6);
+      unsigned m = (unsigned)(w >> 32) & 7;
+      dst[d] = (uint8_t)(sign | (e << 3) | m);
+    }
+  }
+}
+
+/* Fill n bytes with a constant (the NaN poison page of an 8-bit pool). */
+void synth_fill_u8(uint8_t* out, uint8_t v, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = v;
+}
+
 /* Fill n bf16 slots with a constant bit pattern (used for the NaN poison page). */
 void synth_fill_u16(uint16_t* out, uint16_t v, int64_t n) {
 #pragma omp parallel for schedule(static)

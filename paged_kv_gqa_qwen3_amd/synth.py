@@ -30,6 +30,7 @@ _lib = None
 
 PAGE = 16
 BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
 
 
 def _load():
@@ -54,6 +55,13 @@ def _load():
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
         lib.synth_fill_u16.restype = None
         lib.synth_fill_u16.argtypes = [ctypes.c_void_p, ctypes.c_uint16, ctypes.c_int64]
+        lib.synth_fill_pool_fp8.restype = None
+        lib.synth_fill_pool_fp8.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.synth_fill_u8.restype = None
+        lib.synth_fill_u8.argtypes = [ctypes.c_void_p, ctypes.c_uint8, ctypes.c_int64]
         _lib = lib
     return _lib
 
@@ -181,7 +189,8 @@ def make_weights(shape: ModelShape, seed: int,
 class PagedBatch:
     """Paged KV pool plus the per-sequence metadata for the first decode step.
 
-    pool          uint16 [L][num_pages][2][Hkv][16][D]  (bf16 bit patterns)
+    pool          uint16 [L][num_pages][2][Hkv][16][D]  (bf16 bit patterns), or
+                  uint8 (E4M3 codes) for an 8-bit pool
     block_tables  int32  [B][max_pages]  physical page ids (poison for unused)
     positions     int32  [B]  position of the token decoded at step 0 (= ctx0)
     tokens        int32  [B]  token decoded at step 0
@@ -203,11 +212,14 @@ def context_lengths(w: Workload) -> np.ndarray:
 
 
 def make_paged_batch(shape: ModelShape, ctx0: np.ndarray, steps: int, seed: int,
-                     fill_kv: bool = True, spare_pages: int = 0) -> PagedBatch:
+                     fill_kv: bool = True, spare_pages: int = 0,
+                     kv_fp8: bool = False) -> PagedBatch:
     """Allocate a pool holding every page the batch touches over `steps` decode
     steps, give each sequence its pages from one seeded permutation of the
     physical page ids (consecutive slices of it), fill the first ctx0[b] slots
-    of each sequence with N(0,1) bf16 K/V, and poison one extra page with NaN."""
+    of each sequence with N(0,1) bf16 K/V (with kv_fp8: an 8-bit pool of
+    random E4M3 codes, magnitudes 2^-4 .. 3.75), and poison one extra page
+    with NaN."""
     ctx0 = np.asarray(ctx0, dtype=np.int32)
     B = len(ctx0)
     need = [-(-(int(c) + steps) // PAGE) for c in ctx0]
@@ -222,16 +234,25 @@ def make_paged_batch(shape: ModelShape, ctx0: np.ndarray, steps: int, seed: int,
         tables[b, :need[b]] = perm[off:off + need[b]]
         off += need[b]
     L, Hkv, D = shape.num_layers, shape.num_kv_heads, shape.head_dim
-    pool = np.zeros((L, num_pages, 2, Hkv, PAGE, D), dtype=np.uint16)
+    pool = np.zeros((L, num_pages, 2, Hkv, PAGE, D), dtype=np.uint8 if kv_fp8 else np.uint16)
     lib = _load()
     # the poison page is NaN in every layer, K and V
     for l in range(L):
         sl = pool[l, poison]
-        lib.synth_fill_u16(sl.ctypes.data, BF16_NAN, sl.size)
+        if kv_fp8:
+            lib.synth_fill_u8(sl.ctypes.data, E4M3_NAN, sl.size)
+        else:
+            lib.synth_fill_u16(sl.ctypes.data, BF16_NAN, sl.size)
     if fill_kv and int(ctx0.max()) > 0:
-        lib.synth_fill_pool(lib.synth_key(seed, b"kv_context"), 1.0, pool.ctypes.data,
-                            L, num_pages, Hkv, PAGE, D, B, ctx0.ctypes.data,
-                            tables.ctypes.data, max_pages, int(ctx0.max()))
+        key = lib.synth_key(seed, b"kv_context")
+        if kv_fp8:
+            lib.synth_fill_pool_fp8(key, pool.ctypes.data, L, num_pages, Hkv, PAGE, D, B,
+                                    ctx0.ctypes.data, tables.ctypes.data, max_pages,
+                                    int(ctx0.max()))
+        else:
+            lib.synth_fill_pool(key, 1.0, pool.ctypes.data, L, num_pages, Hkv, PAGE, D, B,
+                                ctx0.ctypes.data, tables.ctypes.data, max_pages,
+                                int(ctx0.max()))
     tokens = uniform_int(seed, "first_tokens", shape.vocab, B)
     return PagedBatch(pool, tables, ctx0.copy(), tokens, num_pages, max_pages, poison)
 

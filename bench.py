@@ -39,7 +39,7 @@ METRIC = "decode tokens/s + achieved HBM GB/s (% of 8 TB/s), Qwen3-4B shape, bs 
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "4b_bs1_ctx512"
 DEFAULT_WORKLOADS = ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
-                     "8b_bs8_ragged"]
+                     "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv"]
 WEIGHT_SEED = {"qwen3-4b": 2, "qwen3-8b": 6}
 
 
@@ -89,9 +89,9 @@ def gemv_bytes(shape, cls):
     }[cls]
 
 
-def attention_bytes(shape, ctx):
+def attention_bytes(shape, ctx, kv_elem_bytes=2):
     """K/V bytes one attention launch (one layer) reads and appends."""
-    per_tok_layer = 2 * shape.num_kv_heads * shape.head_dim * 2
+    per_tok_layer = 2 * shape.num_kv_heads * shape.head_dim * kv_elem_bytes
     return sum(int(c) for c in ctx) * per_tok_layer
 
 
@@ -102,7 +102,8 @@ class Run:
         self.torch, self.dec, self.w, self.batch = torch, dec, w, batch
         B = w.batch
         dev = "cuda"
-        self.pool = torch.from_numpy(batch.pool.view(np.int16)).to(dev)
+        pool = np.ascontiguousarray(batch.pool)  # bf16 bits, or E4M3 codes (uint8)
+        self.pool = torch.from_numpy(pool if pool.dtype == np.uint8 else pool.view(np.int16)).to(dev)
         self.tab = torch.from_numpy(batch.block_tables).to(dev)
         self.pos0 = torch.from_numpy(batch.positions).to(dev)
         self.pos = self.pos0.clone()
@@ -147,7 +148,8 @@ def time_workload(torch, dec, w, batch, steps, warmup, reps):
     if flags:
         raise RuntimeError(f"device input flags {flags} during {w.name}")
     ctx0 = batch.positions.astype(np.int64) + 1
-    total_bytes = sum(accounting.step_bytes(w.shape, ctx0 + s) for s in range(steps))
+    kvb = 1 if w.kv_fp8 else 2
+    total_bytes = sum(accounting.step_bytes(w.shape, ctx0 + s, kvb) for s in range(steps))
     return run, times, wall, total_bytes
 
 
@@ -251,7 +253,7 @@ def per_stage_roofline(torch, dec, run, shape, w, batch):
             byts = gemv_bytes(shape, c)
             avg_us = binding.qd_profile_class(dec.handle, w.batch, c, reps=20)
         elif c == "attention":
-            byts = attention_bytes(shape, ctx_mid)
+            byts = attention_bytes(shape, ctx_mid, 1 if w.kv_fp8 else 2)
             avg_us = ev_us
         else:
             byts = w.batch * shape.hidden * 2
@@ -470,9 +472,10 @@ def main():
             # one handle per workload, sized for the positions its timed and
             # warmup steps reach
             span = max(w.steps, args.steps + args.warmup)
-            batch = synth.make_paged_batch(shape, synth.context_lengths(w), span, w.seed)
+            batch = synth.make_paged_batch(shape, synth.context_lengths(w), span, w.seed,
+                                           kv_fp8=w.kv_fp8)
             dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True,
-                          persistent=(args.mode == "auto"))
+                          persistent=(args.mode == "auto"), kv_fp8=w.kv_fp8)
             dec.load_numpy_weights(W)
             path = dec.step_path(w.batch)
             log(f"[bench] {w.name}: {path} path, timing {args.steps} steps after "

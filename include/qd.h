@@ -95,6 +95,15 @@ typedef struct qd_config {
                                   (q_dim = Hq*D, kv_dim = Hkv*D; 60 MB for 512 rows of
                                   Qwen3-4B).  0: no workspace, and qd_prefill_prompts
                                   is refused */
+  int32_t kv_dtype;            /* element type of the caller's KV pool: 0 = bf16;
+                                  1 = 8-bit OCP E4M3 codes (the pages' FP8 KV cache:
+                                  "推理引擎里面发生了什么", Quantization 对 Kernel 的影响),
+                                  stored code = E4M3(value / scale), round to nearest
+                                  even, saturating at +-448, read back as code * scale.
+                                  Halves the pool's bytes; batch 1 then takes the
+                                  per-stage kernels (qd_step_path tells) */
+  float k_scale;               /* kv_dtype 1: the scale of every K element (> 0) */
+  float v_scale;               /* kv_dtype 1: the scale of every V element (> 0) */
 } qd_config;
 
 /* A caller tensor for qd_load_weights.  data is a DEVICE pointer to a
@@ -211,7 +220,7 @@ int qd_prefill_prompts(qd_handle* h, int32_t n_seqs, const int32_t* seq_rows,
  *   positions    int32 [batch]       its position p (= tokens already cached)
  *   block_tables int32 [batch][max_pages_per_seq]  physical page ids; entries
  *                                    0 .. p/16 must name pages of kv_pool
- *   kv_pool      bf16 [L][num_pages][2][Hkv][16][D]  caller-owned paged pool
+ *   kv_pool      bf16 (or kv_dtype 1: E4M3 bytes) [L][num_pages][2][Hkv][16][D]  caller-owned paged pool
  *                                    (index 0 = K, 1 = V); this step writes
  *                                    K/V of position p of every sequence and
  *                                    reads positions 0..p

@@ -44,13 +44,14 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
     return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
 
 
-def step_bytes(shape, ctx: Iterable[int]) -> int:
+def step_bytes(shape, ctx: Iterable[int], kv_elem_bytes: int = BF16) -> int:
     """Algorithmic HBM bytes of one step whose sequences attend ctx[b] tokens
     (ctx[b] = position + 1, the appended token included): weights once, the
     embedding rows of the batch, and ctx[b] K/V rows per sequence (ctx-1 read,
-    1 written)."""
+    1 written) of kv_elem_bytes per element (2 for bf16, 1 for an 8-bit
+    pool)."""
     ctx = list(ctx)
-    kv = kv_bytes_per_token(shape.num_layers, shape.num_kv_heads, shape.head_dim)
+    kv = kv_bytes_per_token(shape.num_layers, shape.num_kv_heads, shape.head_dim, kv_elem_bytes)
     return (weight_bytes_per_step(shape) + len(ctx) * shape.hidden * BF16 +
             sum(int(c) for c in ctx) * kv)
 

@@ -50,7 +50,8 @@ class QdConfig(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("use_graphs", ctypes.c_int32), ("persistent", ctypes.c_int32),
-                ("max_prefill_rows", ctypes.c_int32)]
+                ("max_prefill_rows", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class QdTensorDesc(ctypes.Structure):
@@ -154,11 +155,13 @@ def _check(rc: int, handle) -> None:
 
 def make_config(shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
                 use_graphs: bool = True, persistent: bool = False,
-                max_prefill_rows: int = 0) -> QdConfig:
+                max_prefill_rows: int = 0, kv_fp8: bool = False, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> QdConfig:
     return QdConfig(shape.num_layers, shape.hidden, shape.num_q_heads, shape.num_kv_heads,
                     shape.head_dim, shape.intermediate, shape.vocab, int(shape.tie_embeddings),
                     shape.rms_eps, shape.rope_theta, 16, max_batch, max_pages_per_seq,
-                    num_pages, int(use_graphs), int(persistent), int(max_prefill_rows))
+                    num_pages, int(use_graphs), int(persistent), int(max_prefill_rows),
+                    int(bool(kv_fp8)), float(k_scale), float(v_scale))
 
 
 def qd_create(cfg: QdConfig, stream: int = 0) -> int:

@@ -14,6 +14,7 @@ namespace qd {
 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -28,6 +29,31 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
   u += 0x7fffu + ((u >> 16) & 1u);
   return (unsigned short)(u >> 16);
+}
+
+// OCP E4M3, the element of an 8-bit KV pool: 1 sign, 4 exponent bits (bias
+// 7), 3 mantissa bits, no infinities, NaN = S.1111.111, largest finite 448.
+// Encoding rounds to nearest even and saturates at +-448; NaN encodes as 0x7F.
+__device__ __forceinline__ unsigned f2e4m3(float x) {
+  const unsigned u = __float_as_uint(x);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;          // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |x| >= 448, inf included: saturate
+  if (a < 0x3c800000u)                        // |x| < 2^-6: subnormal steps of 2^-9
+    return sign | (unsigned)rintf(__uint_as_float(a) * 512.f);  // 0..8 (8 = 2^-6)
+  // normal: the 23-bit mantissa rounded to 3 bits, ties to even (a carry
+  // into the exponent gives the next binade, as it should)
+  const unsigned r = a + 0x7ffffu + ((a >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));
+}
+
+// The exact value of an E4M3 code (NaN for 0x7F / 0xFF).
+__device__ __forceinline__ float e4m32f(unsigned c) {
+  const unsigned sign = (c & 0x80u) << 24, em = c & 0x7fu;
+  if (em == 0x7fu) return __uint_as_float(0x7fc00000u);
+  if (em < 8u) return __uint_as_float(sign | __float_as_uint((float)em * 0x1p-9f));
+  return __uint_as_float(sign | ((em + (120u << 3)) << 20));
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -76,6 +102,53 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
   f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
   f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
 }
+
+// Element types of the paged KV pool.  Both load a token row's 8
+// consecutive elements per lane (16 bytes of bf16, 8 bytes of E4M3 codes);
+// unpack gives their values (an 8-bit pool's codes times its scale); encode
+// rounds a value to the pool's element.
+struct KvBf16 {
+  using Elem = uint16_t;
+  using Raw = u32x4;
+  static constexpr bool kFp8 = false;
+  static __device__ __forceinline__ Raw load_nt(const Elem* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  static __device__ __forceinline__ Raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float* f, float) { unpack8(r, f); }
+  static __device__ __forceinline__ Elem encode(float v, float) { return f2bf(v); }
+  // 8 elements staged in LDS as 16-bit slots
+  static __device__ __forceinline__ Raw from_slots(const unsigned short* e) {
+    return *reinterpret_cast<const u32x4*>(e);
+  }
+};
+
+struct KvFp8 {
+  using Elem = uint8_t;
+  using Raw = u32x2;
+  static constexpr bool kFp8 = true;
+  static __device__ __forceinline__ Raw load_nt(const Elem* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  static __device__ __forceinline__ Raw zero() { return u32x2{0u, 0u}; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float* f, float scale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = e4m32f((r.x >> (8 * i)) & 0xffu) * scale;
+      f[4 + i] = e4m32f((r.y >> (8 * i)) & 0xffu) * scale;
+    }
+  }
+  static __device__ __forceinline__ Elem encode(float v, float inv_scale) {
+    return (Elem)f2e4m3(v * inv_scale);
+  }
+  static __device__ __forceinline__ Raw from_slots(const unsigned short* e) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(e);
+    return u32x2{(w.x & 0xffu) | ((w.x >> 8) & 0xff00u) | ((w.y & 0xffu) << 16) |
+                     ((w.y >> 16) << 24),
+                 (w.z & 0xffu) | ((w.z >> 8) & 0xff00u) | ((w.w & 0xffu) << 16) |
+                     ((w.w >> 16) << 24)};
+  }
+};
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -928,7 +1001,7 @@ struct AttnSmem {
   float m[NW][G], l[NW][G];
   float wsc[NW][G];        // per-wave rescale factors of the merge
   float mx[G], lsum[G];    // per head: overall max and sum of the item (or of all splits)
-  alignas(16) unsigned short k[D];
+  alignas(16) unsigned short k[D];  // this step's k, v as pool elements (E4M3 codes widened)
   alignas(16) unsigned short v[D];
   unsigned flag;
 };
@@ -994,11 +1067,12 @@ __device__ __forceinline__ int attn_items(const AttnList& l, int B) { return __s
 //
 // Within a wave, a 16-token page tile of K (or V) for one head is NI loads of
 // 1 KB: in load i lane l holds token i*TPI + l/LPT, dims (l%LPT)*8 .. +8.
-template <int D, int G, int NW, int PW, class Wait>
+template <int D, int G, int NW, int PW, class Wait, class KV = KvBf16>
 __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
                                       const float* q_gain, const float* k_gain,
-                                      uint16_t* pool_layer, const Done& done, int item,
+                                      typename KV::Elem* pool_layer, const Done& done, int item,
                                       unsigned char* smem, const Wait& wait) {
+  using Raw = typename KV::Raw;
   using SM = AttnSmem<D, G, NW>;
   constexpr bool kAgent = Wait::kInLaunch;
 #ifdef QD_STEP_TRACE
@@ -1093,8 +1167,8 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   // step's projections, so they go out before the wait).  Every load is
   // issued unconditionally: a page past the context repeats the last page
   // (its scores are masked), so no wait is forced between pages.
-  u32x4 kr[PW][NI], vr[PW][NI];
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  Raw kr[PW][NI], vr[PW][NI];
+  const Raw zero4 = KV::zero();
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
     const int pg = pg0 + wave + NW * j;
@@ -1103,14 +1177,12 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
       if (lane == 0 && pg < npages) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
       ph = 0;
     }
-    const u32x4* kp = reinterpret_cast<const u32x4*>(
-        pool_layer + (((size_t)ph * 2 + 0) * Hkv + g) * head_stride);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(
-        pool_layer + (((size_t)ph * 2 + 1) * Hkv + g) * head_stride);
+    const typename KV::Elem* kp = pool_layer + (((size_t)ph * 2 + 0) * Hkv + g) * head_stride;
+    const typename KV::Elem* vp = pool_layer + (((size_t)ph * 2 + 1) * Hkv + g) * head_stride;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kr[j][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
-      vr[j][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+      kr[j][i] = KV::load_nt(kp + (size_t)(i * 64 + lane) * 8);
+      vr[j][i] = KV::load_nt(vp + (size_t)(i * 64 + lane) * 8);
     }
   }
 
@@ -1152,8 +1224,8 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
             tq[lane] = r1; tq[lane + HALF] = r2;
           }
         } else {
-          sm.k[lane] = f2bf(r1);
-          sm.k[lane + HALF] = f2bf(r2);
+          sm.k[lane] = KV::encode(r1, a.k_inv);
+          sm.k[lane + HALF] = KV::encode(r2, a.k_inv);
           if (a.tap_k != nullptr && s == 0) {
             float* tk = a.tap_k + ((size_t)b * Hkv + g) * D;
             tk[lane] = r1; tk[lane + HALF] = r2;
@@ -1161,8 +1233,8 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
         }
       }
     } else if (act) {
-      sm.v[lane] = f2bf(x1);
-      sm.v[lane + HALF] = f2bf(x2);
+      sm.v[lane] = KV::encode(x1, a.v_inv);
+      sm.v[lane + HALF] = KV::encode(x2, a.v_inv);
     }
   }
   __syncthreads();
@@ -1177,11 +1249,14 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     if (page < 0 || page >= a.num_pages) {
       if (tid == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
     } else {
-      uint16_t* kd = pool_layer + (((size_t)page * 2 + 0) * Hkv + g) * head_stride +
-                     (size_t)(pos % kPage) * D;
-      uint16_t* vd = pool_layer + (((size_t)page * 2 + 1) * Hkv + g) * head_stride +
-                     (size_t)(pos % kPage) * D;
-      for (int i = tid; i < D; i += NW * 64) { kd[i] = sm.k[i]; vd[i] = sm.v[i]; }
+      typename KV::Elem* kd = pool_layer + (((size_t)page * 2 + 0) * Hkv + g) * head_stride +
+                              (size_t)(pos % kPage) * D;
+      typename KV::Elem* vd = pool_layer + (((size_t)page * 2 + 1) * Hkv + g) * head_stride +
+                              (size_t)(pos % kPage) * D;
+      for (int i = tid; i < D; i += NW * 64) {
+        kd[i] = (typename KV::Elem)sm.k[i];
+        vd[i] = (typename KV::Elem)sm.v[i];
+      }
     }
   }
   if (kv_mode == kAppendOnly) return;  // uniform over the workgroup
@@ -1195,8 +1270,8 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;  // softmax state of head (lane % G)
-  const u32x4 kcur = *reinterpret_cast<const u32x4*>(&sm.k[dch * 8]);
-  const u32x4 vcur = *reinterpret_cast<const u32x4*>(&sm.v[dch * 8]);
+  const Raw kcur = KV::from_slots(&sm.k[dch * 8]);
+  const Raw vcur = KV::from_slots(&sm.v[dch * 8]);
 
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
@@ -1206,11 +1281,11 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = pg * kPage + i * TPI + lane / LPT;
-      u32x4 kk = kr[j][i];
+      Raw kk = kr[j][i];
       if (tok == pos) { kk = kcur; vr[j][i] = vcur; }
       if (tok >= ctx) { kk = zero4; vr[j][i] = zero4; }
       float kf[8];
-      unpack8(kk, kf);
+      KV::unpack(kk, kf, a.k_scale);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const f32x4 q0 = *reinterpret_cast<const f32x4*>(&sm.q[h][dch * 8]);
@@ -1260,7 +1335,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     for (int i = 0; i < NI; ++i) {
       const int t = i * TPI + lane / LPT;
       float vf[8];
-      unpack8(vr[j][i], vf);
+      KV::unpack(vr[j][i], vf, a.v_scale);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float pv = sm.p[wave][t * G + h];

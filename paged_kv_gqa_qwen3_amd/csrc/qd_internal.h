@@ -90,8 +90,11 @@ struct AttnArgs {
   const float* rope_cos;   // [max_pos][D/2]
   const float* rope_sin;
   int max_pos;
-  uint16_t* pool_layer;    // this layer's slice of the pool: [P][2][Hkv][16][D]
+  unsigned char* pool_layer;  // this layer's slice of the pool: [P][2][Hkv][16][D] elements
   int num_pages;
+  int kv_fp8;              // pool elements: 0 bf16, 1 E4M3 codes (value = code * scale)
+  float k_scale, v_scale;  // kv_fp8: the scales, and their inverses for encoding
+  float k_inv, v_inv;
   const int* positions;    // [B]
   const int* block_tables; // [B][max_pages]
   int max_pages;
@@ -353,8 +356,10 @@ struct PfAttnArgs {
   const float* k_gain;
   const float* rope_cos;    // [max_pos][D/2]
   const float* rope_sin;
-  uint16_t* pool_layer;     // this layer's slice of the pool: [P][2][Hkv][16][D]
+  unsigned char* pool_layer;  // this layer's slice of the pool: [P][2][Hkv][16][D] elements
   int num_pages;
+  int kv_fp8;               // pool elements: 0 bf16, 1 E4M3 codes (value = code * scale)
+  float k_scale, v_scale, k_inv, v_inv;
   const int* block_tables;  // [nseg][max_pages]
   int max_pages;
   int M, Hq, Hkv;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kern
 
 
 // The workgroups take the step's attention items round robin.
-template <int D, int G, int NW, int PW>
+template <int D, int G, int NW, int PW, class KV>
 __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const AttnList list = attn_list<NW * PW>(a);
@@ -91,8 +91,9 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
   const AttnArgs& at = a;
 #endif
   for (int t = blockIdx.x; t < items; t += gridDim.x)
-    attention_item<D, G, NW, PW>(at, list, a.q_gain, a.k_gain, a.pool_layer, no_done(), t, smem,
-                                 NoWait{});
+    attention_item<D, G, NW, PW, NoWait, KV>(
+        at, list, a.q_gain, a.k_gain, reinterpret_cast<typename KV::Elem*>(a.pool_layer),
+        no_done(), t, smem, NoWait{});
 }
 
 
@@ -276,8 +277,12 @@ hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s) {
 
 template <int D, int G, int NW, int PW>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attention_kernel<D, G, NW, PW>), dim3(a.grid), dim3(NW * 64),
-                     sizeof(AttnSmem<D, G, NW>), s, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KvFp8>), dim3(a.grid), dim3(NW * 64),
+                       sizeof(AttnSmem<D, G, NW>), s, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KvBf16>), dim3(a.grid), dim3(NW * 64),
+                       sizeof(AttnSmem<D, G, NW>), s, a);
   return hipGetLastError();
 }
 

@@ -288,11 +288,14 @@ __global__ __launch_bounds__(256) void pf_gemm_kernel(PfGemmArgs a) {
 
 // One wave per (row, head) of q heads then KV heads; lane i < D/2 holds
 // elements i and i + D/2 (the NeoX rotation pairs).  q heads: RMSNorm with
-// the q gain, RoPE at the row's position, times the softmax scale, stored as
-// a bf16 pair.  KV heads: k as q with the k gain (no scale) and v as is,
-// both rounded to bf16 into the row's slot of the pool.
-template <int D>
+// the q gain, RoPE at the row's position, times the softmax scale (and, for
+// an 8-bit pool, K's scale: attention multiplies q by K's codes), stored as a
+// bf16 pair.  KV heads: k as q with the k gain (no scale) and v as is, both
+// rounded to the pool's element (bf16, or E4M3 of value / scale) into the
+// row's slot of the pool.
+template <int D, class KV>
 __global__ __launch_bounds__(256) void pf_qk_kernel(PfAttnArgs a) {
+  using Elem = typename KV::Elem;
   constexpr int HALF = D / 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int NH = a.Hq + a.Hkv;
@@ -315,7 +318,8 @@ __global__ __launch_bounds__(256) void pf_qk_kernel(PfAttnArgs a) {
   if (hh < a.Hq) {
     if (act) {
       const size_t q = ((size_t)m * a.Hq + hh) * D + i;
-      const float v1 = r1 * a.scale, v2 = r2 * a.scale;
+      const float qs = KV::kFp8 ? a.scale * a.k_scale : a.scale;
+      const float v1 = r1 * qs, v2 = r2 * qs;
       const unsigned h1 = f2bf(v1), h2 = f2bf(v2);
       a.q_hi[q] = (uint16_t)h1;
       a.q_hi[q + HALF] = (uint16_t)h2;
@@ -331,39 +335,46 @@ __global__ __launch_bounds__(256) void pf_qk_kernel(PfAttnArgs a) {
     page = page < 0 ? 0 : a.num_pages - 1;
   }
   if (!act) return;
-  uint16_t* kd = a.pool_layer + (((size_t)page * 2 + 0) * a.Hkv + g) * kPage * D + (p % kPage) * D;
-  uint16_t* vd = kd + (size_t)a.Hkv * kPage * D;
-  kd[i] = f2bf(r1);
-  kd[i + HALF] = f2bf(r2);
+  Elem* kd = reinterpret_cast<Elem*>(a.pool_layer) +
+             (((size_t)page * 2 + 0) * a.Hkv + g) * kPage * D + (p % kPage) * D;
+  Elem* vd = kd + (size_t)a.Hkv * kPage * D;
+  kd[i] = KV::encode(r1, a.k_inv);
+  kd[i + HALF] = KV::encode(r2, a.k_inv);
   const float* vr = row + QD + KD + g * D;
-  vd[i] = f2bf(vr[i]);
-  vd[i + HALF] = f2bf(vr[i + HALF]);
+  vd[i] = KV::encode(vr[i], a.v_inv);
+  vd[i + HALF] = KV::encode(vr[i + HALF], a.v_inv);
 }
 
 // ------------------------------------------------------------------ tiled causal attention
 
 // One workgroup per (segment, 16-row query block, KV head); wave w takes
 // query head g*G + w.  For each page of the block's context (positions
-// 0 .. the block's last), the workgroup stages the page's K (as four 1 KB
-// A-operand tiles: lane l holds key l%16, head dims 32*kk + 8*(l/16)..+7)
-// and V (row-major, each 1 KB chunk padded by 64 bytes so that the
-// transposed reads below spread over the banks) in LDS, kNs pages in flight.
-// Per page a wave forms S^T = K . Q^T (16 keys x 16 queries) with
-// 16x16x32 MFMAs on q's hi and lo, masks keys past each query's position,
-// updates each query's running maximum and sum (online softmax, as the
-// decode kernels), and accumulates O^T += V^T . P^T with 16x16x16 MFMAs on
-// P's hi and lo.  Lane l ends with O^T[d = 16*dt + 4*(l/16)..+3][query l%16]
-// and writes the block's rows as operand tiles for the O projection.
-template <int D, int G>
+// 0 .. the block's last), the workgroup stages the page's K and V in LDS
+// with direct global-to-LDS loads, kNs pages in flight.  K of a bf16 pool
+// lands as 1 KB A-operand tiles (lane l: key l%16, head dims 32*kk +
+// 8*(l/16)..+7); K of an 8-bit pool lands row-major and each lane widens its
+// 8 codes to bf16 (exact: every E4M3 value is a bf16 value).  V lands
+// row-major, each 1 KB chunk padded by 64 bytes so that the transposed reads
+// below spread over the banks.  Per page a wave forms S^T = K . Q^T (16 keys
+// x 16 queries) with 16x16x32 MFMAs on q's hi and lo (q carries the softmax
+// scale, and K's scale for an 8-bit pool), masks keys past each query's
+// position, updates each query's running maximum and sum (online softmax, as
+// the decode kernels), and accumulates O^T += V^T . P^T with 16x16x16 MFMAs
+// on P's hi and lo.  Lane l ends with O^T[d = 16*dt + 4*(l/16)..+3][query
+// l%16] (times V's scale for an 8-bit pool) and writes the block's rows as
+// operand tiles for the O projection.
+template <int D, int G, class KV>
 __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
-  constexpr int KK = D / 32;                 // K tiles per page
-  constexpr int VCH = D / 32;                // V chunks of 1 KB per page (16 keys x D x 2 bytes)
-  constexpr int KPC = 512 / D;               // keys per V chunk
+  constexpr int EB = KV::kFp8 ? 1 : 2;       // bytes per pool element
+  constexpr int KK = D / 32;                 // 32-dim steps of q.k
+  constexpr int PB = kPage * D * EB;         // bytes of one page's K (or V) of one head
+  constexpr int KCH = PB / 1024;             // 1 KB chunks of K, and of V
+  constexpr int KPC = 1024 / (D * EB);       // keys per V chunk
   constexpr int VSTRIDE = 1024 + 64;         // padded V chunk
-  constexpr int SLOT = KK * 1024 + VCH * VSTRIDE;
-  constexpr int CH = KK + VCH;               // 1 KB loads per page
-  static_assert(CH % G == 0, "loads shared evenly by the waves");
-  constexpr int LPW = CH / G;
+  constexpr int SLOT = KCH * 1024 + KCH * VSTRIDE;
+  constexpr int CH = 2 * KCH;                // 1 KB loads per page
+  constexpr int LPW = (CH + G - 1) / G;      // ... per wave (fewer for the last waves if
+                                             // CH is not a multiple of G)
   constexpr int kNs = 4;
   static_assert((kNs - 2) * LPW <= 63, "vmcnt range");
   constexpr int DT = D / 16;
@@ -381,7 +392,9 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
   const int npages = (p_first + nrows - 1) / kPage + 1;
   const int h = g * G + wave;
   const int* table = a.block_tables + (size_t)s * a.max_pages;
-  const size_t head_elems = (size_t)kPage * D;
+  // this wave's loads per page are chunks c = wave + G*u < CH; a wave with
+  // fewer than LPW of them waits for all of its loads
+  const bool full_share = (wave + G * (LPW - 1)) < CH;
 
   // q^T fragments (B operand): lane l holds query l%16, dims 32*kk + 8*(l/16)..+7
   const int qr = r_begin + min(lane & 15, nrows - 1);
@@ -415,23 +428,51 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
       if (lane == 0) set_flag(a.dev_flags, QD_DEV_BAD_PAGE);
       page = page < 0 ? 0 : a.num_pages - 1;
     }
-    const uint16_t* kb = a.pool_layer + (((size_t)page * 2 + 0) * a.Hkv + g) * head_elems;
-    const uint16_t* vb = kb + (size_t)a.Hkv * head_elems;
+    const unsigned char* kb = a.pool_layer + (((size_t)page * 2 + 0) * a.Hkv + g) * PB;
+    const unsigned char* vb = kb + (size_t)a.Hkv * PB;
     unsigned char* base = lds + (size_t)slot * SLOT;
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int c = wave + G * u;
-      if (c < KK) {
-        const uint16_t* gp = kb + (lane & 15) * D + 32 * c + 8 * (lane >> 4);
+      if (c >= CH) break;  // wave-uniform
+      if (c < KCH) {
+        const unsigned char* gp =
+            KV::kFp8 ? kb + c * 1024 + lane * 16
+                     : kb + ((lane & 15) * D + 32 * c + 8 * (lane >> 4)) * 2;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(gp), base + c * 1024, 16,
                                          0, 0);
       } else {
-        const int v = c - KK;
-        const uint16_t* gp = vb + (size_t)v * 512 + lane * 8;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(gp),
-                                         base + KK * 1024 + v * VSTRIDE, 16, 0, 0);
+        const int v = c - KCH;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(vb + v * 1024 + lane * 16),
+                                         base + KCH * 1024 + v * VSTRIDE, 16, 0, 0);
       }
     }
+  };
+  // this lane's K A-operand for dims 32*kk.. of the staged page
+  auto k_frag = [&](const unsigned char* base, int kk) -> bf16x8 {
+    if constexpr (KV::kFp8) {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base + (lane & 15) * D + 32 * kk +
+                                                      8 * (lane >> 4));
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned word = i < 2 ? c.x : c.y, sh = 16 * (i & 1);
+        const unsigned lo = __float_as_uint(e4m32f((word >> sh) & 0xffu)) >> 16;
+        const unsigned hi = __float_as_uint(e4m32f((word >> (sh + 8)) & 0xffu)) >> 16;
+        w[i] = lo | (hi << 16);
+      }
+      return __builtin_bit_cast(bf16x8, w);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(base + kk * 1024 + lane * 16);
+    }
+  };
+  // bf16 bits of V[key][dim] from the staged page
+  auto v_elem = [&](const unsigned char* base, int key, int dim) -> short {
+    const unsigned char* p = base + KCH * 1024 + (key / KPC) * VSTRIDE + (key % KPC) * D * EB + dim * EB;
+    if constexpr (KV::kFp8)
+      return (short)(__float_as_uint(e4m32f(*p)) >> 16);
+    else
+      return *reinterpret_cast<const short*>(p);
   };
 
   f32x4 o[DT];
@@ -446,7 +487,7 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     if (st < npages) issue(st, st);
   for (int pg = 0; pg < npages; ++pg) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (pg + kNs - 2 < npages)
+    if (full_share && pg + kNs - 2 < npages)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kNs - 2) * LPW));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -456,7 +497,7 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(base + kk * 1024 + lane * 16);
+      const bf16x8 ka = k_frag(base, kk);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk][0], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk][1], s1, 0, 0, 0);
     }
@@ -490,17 +531,11 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
       pl[r] = (short)f2bf(p[r] - __uint_as_float(hb << 16));
     }
     // V^T A operand: lane l holds dim 16*dt + l%16 of keys 4*(l/16)..+3
-    const unsigned char* vrow[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = 4 * (lane >> 4) + r;
-      vrow[r] = base + KK * 1024 + (k / KPC) * VSTRIDE + (k % KPC) * D * 2 + (lane & 15) * 2;
-    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       s16x4 va;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) va[r] = *reinterpret_cast<const short*>(vrow[r] + dt * 32);
+      for (int r = 0; r < 4; ++r) va[r] = v_elem(base, 4 * (lane >> 4) + r, 16 * dt + (lane & 15));
       o[dt] = o[dt] * alpha;
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[dt], 0, 0, 0);
@@ -508,7 +543,7 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
   }
 
   if (qvalid) {
-    const float inv = 1.f / l_run;
+    const float inv = (KV::kFp8 ? a.v_scale : 1.f) / l_run;
     const int m = r_begin + (lane & 15);
     const int KT = a.Hq * D / kTileCols;
 #pragma unroll
@@ -609,32 +644,43 @@ hipError_t launch_pf_gemm(const PfGemmArgs& a, int mode, int wn, int wm, hipStre
   }
 }
 
-hipError_t launch_pf_qk(const PfAttnArgs& a, int head_dim, hipStream_t s) {
+template <class KV>
+static hipError_t launch_pf_qk_t(const PfAttnArgs& a, int head_dim, hipStream_t s) {
   const long long tasks = (long long)a.M * (a.Hq + a.Hkv);
   const dim3 grid((unsigned)((tasks + 3) / 4));
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(pf_qk_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(pf_qk_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((pf_qk_kernel<64, KV>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((pf_qk_kernel<128, KV>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int D, int G>
+hipError_t launch_pf_qk(const PfAttnArgs& a, int head_dim, hipStream_t s) {
+  return a.kv_fp8 ? launch_pf_qk_t<KvFp8>(a, head_dim, s) : launch_pf_qk_t<KvBf16>(a, head_dim, s);
+}
+
+template <int D, int G, class KV>
 static hipError_t launch_pf_attn_t(const PfAttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.seg.qb0[a.seg.n] * a.Hkv));
-  hipLaunchKernelGGL((pf_attn_kernel<D, G>), grid, dim3(64 * G), 0, s, a);
+  hipLaunchKernelGGL((pf_attn_kernel<D, G, KV>), grid, dim3(64 * G), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_pf_attn(const PfAttnArgs& a, int head_dim, int group, hipStream_t s) {
-  if (head_dim == 128 && group == 4) return launch_pf_attn_t<128, 4>(a, s);
-  if (head_dim == 128 && group == 2) return launch_pf_attn_t<128, 2>(a, s);
-  if (head_dim == 128 && group == 1) return launch_pf_attn_t<128, 1>(a, s);
-  if (head_dim == 64 && group == 4) return launch_pf_attn_t<64, 4>(a, s);
-  if (head_dim == 64 && group == 2) return launch_pf_attn_t<64, 2>(a, s);
-  if (head_dim == 64 && group == 1) return launch_pf_attn_t<64, 1>(a, s);
+template <class KV>
+static hipError_t launch_pf_attn_kv(const PfAttnArgs& a, int head_dim, int group, hipStream_t s) {
+  if (head_dim == 128 && group == 4) return launch_pf_attn_t<128, 4, KV>(a, s);
+  if (head_dim == 128 && group == 2) return launch_pf_attn_t<128, 2, KV>(a, s);
+  if (head_dim == 128 && group == 1) return launch_pf_attn_t<128, 1, KV>(a, s);
+  if (head_dim == 64 && group == 4) return launch_pf_attn_t<64, 4, KV>(a, s);
+  if (head_dim == 64 && group == 2) return launch_pf_attn_t<64, 2, KV>(a, s);
+  if (head_dim == 64 && group == 1) return launch_pf_attn_t<64, 1, KV>(a, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pf_attn(const PfAttnArgs& a, int head_dim, int group, hipStream_t s) {
+  return a.kv_fp8 ? launch_pf_attn_kv<KvFp8>(a, head_dim, group, s)
+                  : launch_pf_attn_kv<KvBf16>(a, head_dim, group, s);
 }
 
 hipError_t launch_pf_head_rows(const float* x, int H, const PfSegs& seg, int n, const float* gain,

@@ -129,6 +129,11 @@ struct qd_handle {
   float* stream_amax_val = nullptr;  // [stream_grid]
   int* stream_amax_idx = nullptr;
 
+  // KV pool elements: bf16, or E4M3 codes with per-tensor scales
+  bool kv_fp8 = false;
+  int kv_bytes = 2;
+  float k_scale = 1.f, v_scale = 1.f;
+
   // prompt chunks on the matrix cores (qd_prefill_prompts): pf_rows rows of
   // residual stream, QKV output, q pairs and operand tiles (norm outputs and
   // the attention output share pf_tin; the SwiGLU output is pf_tact)
@@ -265,6 +270,11 @@ int validate_config(const qd_config* c) {
   if (c->page_size != kPage) return fail(nullptr, QD_EUNSUPPORTED, "page_size must be 16");
   if (c->max_prefill_rows < 0 || c->max_prefill_rows > kPfMaxRows)
     return fail(nullptr, QD_EINVAL, "max_prefill_rows must be in 0..16384");
+  if (c->kv_dtype != 0 && c->kv_dtype != 1)
+    return fail(nullptr, QD_EINVAL, "kv_dtype must be 0 (bf16) or 1 (E4M3)");
+  if (c->kv_dtype == 1 && !(c->k_scale > 0.f && c->v_scale > 0.f && std::isfinite(c->k_scale) &&
+                            std::isfinite(c->v_scale)))
+    return fail(nullptr, QD_EINVAL, "k_scale and v_scale must be finite and > 0");
   if (c->hidden % 64 || c->hidden > 8192)
     return fail(nullptr, QD_EUNSUPPORTED, "hidden must be a multiple of 64 and at most 8192");
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -289,7 +299,7 @@ struct StepPtrs {
   const int32_t* tokens;
   const int32_t* positions;
   const int32_t* tables;
-  uint16_t* pool;
+  unsigned char* pool;  // the caller's pool, as bytes
   int32_t* next;
   float* logits;
   int n_logits = -1;  // a prefill chunk: rows [0, n_logits) get the LM head; -1: a decode step
@@ -318,6 +328,13 @@ constexpr int kTraceLayer = 17;
 constexpr size_t kTraceSlots = (size_t)kTraceItems * 8;
 unsigned long long* g_trace[QD_PROF_CLASSES];
 #endif
+
+// The pool's element type and scales, for an attention launch.
+void set_kv(const qd_handle* h, AttnArgs& a) {
+  a.kv_fp8 = h->kv_fp8 ? 1 : 0;
+  a.k_scale = h->k_scale; a.v_scale = h->v_scale;
+  a.k_inv = 1.f / h->k_scale; a.v_inv = 1.f / h->v_scale;
+}
 
 // Launch the projection of class cls (QD_PROF_QKV, _O, _GATE_UP, _DOWN or
 // _LM_HEAD) of layer l at batch B on stream s, as the step does.  QKV leaves
@@ -441,7 +458,8 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
     if (part_mode) { aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; aa.qkv_rows = kTileRows * pq.rt; }
     aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
-    aa.pool_layer = sp.pool + (size_t)l * layer_elems;
+    aa.pool_layer = sp.pool + (size_t)l * layer_elems * h->kv_bytes;
+    set_kv(h, aa);
     aa.num_pages = h->cfg.num_pages;
     aa.positions = sp.positions; aa.block_tables = sp.tables;
     aa.max_pages = h->cfg.max_pages_per_seq;
@@ -571,7 +589,8 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     aa.qkv = h->qkv; aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
     aa.qkv_part = h->part_qkv; aa.qkv_S = pq.S; aa.qkv_rows = kTileRows * pq.rt;
     aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin; aa.max_pos = h->max_pos;
-    aa.pool_layer = sp.pool + (size_t)l * layer_elems;
+    aa.pool_layer = sp.pool + (size_t)l * layer_elems * h->kv_bytes;
+    set_kv(h, aa);
     aa.num_pages = h->cfg.num_pages;
     aa.positions = sp.positions; aa.block_tables = sp.tables;
     aa.max_pages = h->cfg.max_pages_per_seq;
@@ -652,7 +671,9 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
 // 1/grid of every projection's row tiles.
 int setup_stream(qd_handle* h) {
   // (inputs under an RMSNorm gain are the hidden size: at most 8192)
-  if (!h->persistent || h->long_ctx || h->L > kStreamMaxLayers || h->H > 8192) return QD_OK;
+  // (the streaming kernel reads a bf16 pool only)
+  if (!h->persistent || h->long_ctx || h->kv_fp8 || h->L > kStreamMaxLayers || h->H > 8192)
+    return QD_OK;
   const int kmax = std::max(h->H, std::max(h->QD, h->I));
   if (kmax > 4 * 256 * kStreamStageVec) return QD_OK;  // staged input: 16 floats per thread
   auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
@@ -733,6 +754,7 @@ int run_stream(qd_handle* h, const StepPtrs& sp, hipStream_t s, const qd_taps* t
   at.qkv_rows = kTileRows;
   at.rope_cos = h->rope_cos; at.rope_sin = h->rope_sin; at.max_pos = h->max_pos;
   at.pool_layer = sp.pool;
+  set_kv(h, at);
   at.num_pages = h->cfg.num_pages;
   at.positions = sp.positions; at.block_tables = sp.tables;
   at.max_pages = h->cfg.max_pages_per_seq;
@@ -852,7 +874,7 @@ hipError_t pf_gemm(qd_handle* h, int mode, const uint16_t* w, int N, int K, cons
 
 // Enqueue a prompt chunk (qd_prefill_prompts) on the handle's stream.
 int record_prefill_prompts(qd_handle* h, const PfSegs& sg, const int32_t* tokens,
-                           const int32_t* tables, uint16_t* pool, int n_logits, int32_t* next,
+                           const int32_t* tables, unsigned char* pool, int n_logits, int32_t* next,
                            float* logits) {
   hipStream_t s = h->stream;
   const int L = h->L, H = h->H, I = h->I, M = sg.row0[sg.n];
@@ -864,6 +886,9 @@ int record_prefill_prompts(qd_handle* h, const PfSegs& sg, const int32_t* tokens
   aa.qkv = h->pf_qkv;
   aa.rope_cos = h->rope_cos; aa.rope_sin = h->rope_sin;
   aa.num_pages = h->cfg.num_pages;
+  aa.kv_fp8 = h->kv_fp8 ? 1 : 0;
+  aa.k_scale = h->k_scale; aa.v_scale = h->v_scale;
+  aa.k_inv = 1.f / h->k_scale; aa.v_inv = 1.f / h->v_scale;
   aa.block_tables = tables; aa.max_pages = h->cfg.max_pages_per_seq;
   aa.M = M; aa.Hq = h->Hq; aa.Hkv = h->Hkv;
   aa.eps = eps; aa.scale = (float)(1.0 / std::sqrt((double)h->D));
@@ -876,7 +901,7 @@ int record_prefill_prompts(qd_handle* h, const PfSegs& sg, const int32_t* tokens
     HIP_TRY(h, launch_pf_norm(h->pf_x, w.in_norm, H, M, Mt, eps, h->pf_tin, s));
     HIP_TRY(h, pf_gemm(h, kPfStore, w.qkv, h->NQKV, H, h->pf_tin, M, h->pf_qkv, h->NQKV, nullptr, s));
     aa.q_gain = w.q_norm; aa.k_gain = w.k_norm;
-    aa.pool_layer = pool + (size_t)l * layer_elems;
+    aa.pool_layer = pool + (size_t)l * layer_elems * h->kv_bytes;
     HIP_TRY(h, launch_pf_qk(aa, h->D, s));
     HIP_TRY(h, launch_pf_attn(aa, h->D, h->G, s));
     HIP_TRY(h, pf_gemm(h, kPfResid, w.o, H, h->QD, h->pf_tin, M, h->pf_x, H, nullptr, s));
@@ -916,6 +941,9 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   h->Hkv = cfg->num_kv_heads; h->D = cfg->head_dim; h->I = cfg->intermediate;
   h->V = cfg->vocab; h->QD = h->Hq * h->D; h->KD = h->Hkv * h->D;
   h->NQKV = h->QD + 2 * h->KD; h->G = h->Hq / h->Hkv;
+  h->kv_fp8 = cfg->kv_dtype == 1;
+  h->kv_bytes = h->kv_fp8 ? 1 : 2;
+  if (h->kv_fp8) { h->k_scale = cfg->k_scale; h->v_scale = cfg->v_scale; }
 
   auto bail = [&](int code) {
     g_create_error = h->err;
@@ -1208,7 +1236,7 @@ int qd_decode_step_taps(qd_handle* h, int32_t batch, const int32_t* token_ids,
                         int32_t* out_next_ids, float* out_logits, const qd_taps* taps) {
   int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
   if (rc) return rc;
-  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<unsigned char*>(kv_pool),
               out_next_ids, out_logits};
   return record_step(h, sp, taps, h->stream);
 }
@@ -1220,7 +1248,7 @@ int qd_stream_step_taps(qd_handle* h, const int32_t* token_ids, const int32_t* p
   if (rc) return rc;
   if (!use_stream(h, 1))
     return fail(h, QD_EUNSUPPORTED, "this handle does not run batch 1 as the streaming kernel");
-  StepPtrs sp{1, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+  StepPtrs sp{1, token_ids, positions, block_tables, static_cast<unsigned char*>(kv_pool),
               out_next_ids, out_logits};
   return run_stream(h, sp, h->stream, taps);
 }
@@ -1230,7 +1258,7 @@ int qd_decode_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
                    int32_t* out_next_ids, float* out_logits) {
   int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
   if (rc) return rc;
-  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<unsigned char*>(kv_pool),
               out_next_ids, out_logits};
   if (use_stream(h, batch)) return run_stream(h, sp, h->stream);
   if (!h->cfg.use_graphs) return record_step(h, sp, nullptr, h->stream);
@@ -1282,7 +1310,7 @@ int qd_prefill(qd_handle* h, int32_t rows, const int32_t* token_ids, const int32
   // (out_next_ids may be NULL here: token_ids stands in for it in the check)
   int rc = check_step_args(h, rows, token_ids, positions, block_tables, kv_pool, token_ids);
   if (rc) return rc;
-  StepPtrs sp{rows, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+  StepPtrs sp{rows, token_ids, positions, block_tables, static_cast<unsigned char*>(kv_pool),
               out_next_ids, out_logits, n_logits};
   return record_step(h, sp, nullptr, h->stream);
 }
@@ -1319,7 +1347,7 @@ int qd_prefill_prompts(qd_handle* h, int32_t n_seqs, const int32_t* seq_rows,
   }
   sg.row0[n_seqs] = (int)rows;
   sg.qb0[n_seqs] = (int)qb;
-  return record_prefill_prompts(h, sg, token_ids, block_tables, static_cast<uint16_t*>(kv_pool),
+  return record_prefill_prompts(h, sg, token_ids, block_tables, static_cast<unsigned char*>(kv_pool),
                                 n_logits, out_next_ids, out_logits);
 }
 
@@ -1330,7 +1358,7 @@ int qd_profile_step(qd_handle* h, int32_t batch, const int32_t* token_ids,
   int rc = check_step_args(h, batch, token_ids, positions, block_tables, kv_pool, out_next_ids);
   if (rc) return rc;
   if (!class_ms || !class_launches) return fail(h, QD_EINVAL, "NULL profile output");
-  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<uint16_t*>(kv_pool),
+  StepPtrs sp{batch, token_ids, positions, block_tables, static_cast<unsigned char*>(kv_pool),
               out_next_ids, out_logits};
   // The step is enqueued twice: while the GPU runs the first copy, the host
   // has time to enqueue the second, profiled one completely, so its kernels

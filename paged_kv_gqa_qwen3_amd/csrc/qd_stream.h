@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256) void stream_step_kernel(const StreamArgs a) {
     // attention (the items read q|k|v, RMSNorm and rotate q and k, append
     // k and v to the pool and attend over it)
     if (!attn_wg) ring_top_up(a, rg, wave, lane, u_lim(u + kPrO));
-    uint16_t* pool_l = a.attn.pool_layer + (size_t)l * a.pool_layer_elems;
+    uint16_t* pool_l = reinterpret_cast<uint16_t*>(a.attn.pool_layer) + (size_t)l * a.pool_layer_elems;
 #ifdef QD_STEP_TRACE
     AttnArgs at = l == a.tap_layer ? a.attn_tap : a.attn;  // (trace builds) the item's
     at.trace = l == 17 ? a.trace + (size_t)wg * 1024 + 960 : nullptr;  // events of layer 17

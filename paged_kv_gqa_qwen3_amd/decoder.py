@@ -29,13 +29,18 @@ def to_device_i32(a: np.ndarray, device="cuda"):
 
 
 def pool_to_device(pool: np.ndarray, device="cuda"):
-    """Paged KV pool (uint16 bf16 bits, [L][P][2][Hkv][16][D]) -> device int16 tensor."""
+    """Paged KV pool ([L][P][2][Hkv][16][D] of uint16 bf16 bits, or uint8 E4M3
+    codes) -> device int16 (or uint8) tensor."""
     torch = _torch()
-    return torch.from_numpy(np.ascontiguousarray(pool).view(np.int16)).to(device)
+    pool = np.ascontiguousarray(pool)
+    if pool.dtype == np.uint8:
+        return torch.from_numpy(pool).to(device)
+    return torch.from_numpy(pool.view(np.int16)).to(device)
 
 
 def pool_to_host(pool_t) -> np.ndarray:
-    return pool_t.cpu().numpy().view(np.uint16)
+    a = pool_t.cpu().numpy()
+    return a if a.dtype == np.uint8 else a.view(np.uint16)
 
 
 class Decoder:
@@ -43,7 +48,8 @@ class Decoder:
 
     def __init__(self, shape, max_batch: int, max_pages_per_seq: int, num_pages: int,
                  use_graphs: bool = True, stream: Optional[int] = None,
-                 persistent: bool = False, max_prefill_rows: int = 0):
+                 persistent: bool = False, max_prefill_rows: int = 0, kv_fp8: bool = False,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         torch = _torch()
         self.shape = shape
         self.max_batch = max_batch
@@ -52,7 +58,8 @@ class Decoder:
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
         self.cfg = binding.make_config(shape, max_batch, max_pages_per_seq, num_pages,
-                                       use_graphs, persistent, max_prefill_rows)
+                                       use_graphs, persistent, max_prefill_rows, kv_fp8,
+                                       k_scale, v_scale)
         self.handle = binding.qd_create(self.cfg, stream)
 
     def load_numpy_weights(self, weights: Dict[str, np.ndarray], chunk: int = 24) -> None:

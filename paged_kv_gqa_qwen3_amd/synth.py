@@ -109,6 +109,7 @@ class Workload:
     steps: int
     seed: int
     prefill_prompt: int = 0  # >0: context comes from a prompt prefilled by the oracle
+    kv_fp8: bool = False     # the KV pool holds E4M3 codes (scales 1) instead of bf16
 
 
 WORKLOADS = {
@@ -119,6 +120,8 @@ WORKLOADS = {
         Workload("4b_bs16_ctx256", QWEN3_4B, 16, 256, 256, 128, 4),
         Workload("4b_bs1_ctx8192", QWEN3_4B, 1, 8192, 8192, 64, 5),
         Workload("8b_bs8_ragged", QWEN3_8B, 8, 256, 2048, 128, 6),
+        Workload("4b_bs8_ctx4096", QWEN3_4B, 8, 4096, 4096, 64, 7),
+        Workload("4b_bs8_ctx4096_fp8kv", QWEN3_4B, 8, 4096, 4096, 64, 7, kv_fp8=True),
     )
 }
 

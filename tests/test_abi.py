@@ -57,6 +57,7 @@ def _cfg(**kw):
     ("max_pages_per_seq", 4097, binding.QD_EUNSUPPORTED),
     ("max_prefill_rows", -1, binding.QD_EINVAL),
     ("max_prefill_rows", 16385, binding.QD_EINVAL),
+    ("kv_dtype", 2, binding.QD_EINVAL),
 ])
 def test_create_rejects_bad_config(lib, field, value, code):
     h = ctypes.c_void_p()
@@ -65,6 +66,15 @@ def test_create_rejects_bad_config(lib, field, value, code):
     assert rc == code
     assert h.value is None
     assert binding.qd_last_error(None) != ""
+
+
+@pytest.mark.parametrize("k,v", [(0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0),
+                                 (1.0, float("nan"))])
+def test_create_rejects_bad_fp8_scales(lib, k, v):
+    h = ctypes.c_void_p()
+    cfg = _cfg(kv_dtype=1, k_scale=k, v_scale=v)
+    assert lib.qd_create(ctypes.byref(cfg), None, ctypes.byref(h)) == binding.QD_EINVAL
+    assert h.value is None
 
 
 def test_null_arguments(lib):

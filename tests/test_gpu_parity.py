@@ -105,7 +105,8 @@ def test_tiny_workload_teacher_forced(torch, persistent):
 
 # ----------------------------------------------------------------------------- stage isolation
 
-def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits, nxt, mfma):
+def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits, nxt, mfma,
+                  kv=oracle.BF16):
     B = batch.tokens.shape[0]
     H, D, Hq, Hkv = shape.hidden, shape.head_dim, shape.num_q_heads, shape.num_kv_heads
     QD, KD = shape.q_dim, shape.kv_dim
@@ -136,22 +137,30 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
         assert np.abs(t["q_rot"][b] - qr).max() <= 2e-5 * max(1.0, np.abs(qr).max()), "q_rot"
         assert np.abs(t["k_rot"][b] - kr).max() <= 2e-5 * max(1.0, np.abs(kr).max()), "k_rot"
 
-    # KV append: bit-exact rounding and placement
+    # KV append: bit-exact rounding and placement.  An 8-bit pool stores the
+    # E4M3 code of value / scale; the tests' scales are powers of two, so the
+    # fp32 product the kernel encodes is exact and the oracle's encoding of
+    # the same value is the same decision.
+    def rounded(x, scale):
+        if kv.fp8:
+            return oracle.f64_to_e4m3(x.astype(np.float64) / scale)
+        return bf16_rne_of_f32(x)
     for b in range(B):
         page = batch.block_tables[b, pos[b] // 16]
         slot = pos[b] % 16
         np.testing.assert_array_equal(pool_after[layer, page, 0, :, slot],
-                                      bf16_rne_of_f32(taps["k_rot"][b]))
+                                      rounded(taps["k_rot"][b], kv.k_scale))
         v = taps["qkv"][b, QD + KD:].reshape(Hkv, D)
-        np.testing.assert_array_equal(pool_after[layer, page, 1, :, slot], bf16_rne_of_f32(v))
+        np.testing.assert_array_equal(pool_after[layer, page, 1, :, slot],
+                                      rounded(v, kv.v_scale))
     m = _appended_mask(batch, list(enumerate(pos)))
     np.testing.assert_array_equal(pool_after[~m], pool_before[~m])
 
     # paged GQA attention, from the GPU's rotated q and the pool after the append
     for b in range(B):
         o = oracle.attention(t["q_rot"][b], pool_after, layer, batch.block_tables[b],
-                             int(pos[b]) + 1, Hkv)
-        vmax = np.abs(oracle.bf16_to_f64(pool_after[layer][:, 1])).max()
+                             int(pos[b]) + 1, Hkv, kv)
+        vmax = np.abs(oracle.pool_values(pool_after, kv)[layer][:, 1]).max()
         vmax = vmax if np.isfinite(vmax) else 10.0
         assert np.abs(t["attn"][b] - o).max() <= 2e-4 * max(1.0, vmax), f"attn seq {b}"
 
@@ -188,15 +197,16 @@ def _stage_checks(shape, W, batch, taps, pool_before, pool_after, layer, logits,
         np.testing.assert_array_equal(nxt, np.argmax(logits, axis=1))
 
 
-def _run_stage_checks(torch, shape, W, batch, what, stream=False):
+def _run_stage_checks(torch, shape, W, batch, what, stream=False, kv=oracle.BF16):
     """One step through a taps entry point, stopping at the first and last
     layer, each stage checked by the oracle from the GPU's own input to it:
     the per-stage kernels (no graph), or with stream=True the batch-1
-    weight-streaming kernel (MFMA tiles on a bf16 pair of the input)."""
+    weight-streaming kernel (MFMA tiles on a bf16 pair of the input).  kv:
+    the pool's element type (an 8-bit pool for kv.fp8)."""
     B = batch.tokens.shape[0]
     mfma = B > 1 or stream
     dec = Decoder(shape, B, batch.max_pages, batch.num_pages, use_graphs=False,
-                  persistent=stream)
+                  persistent=stream, kv_fp8=kv.fp8, k_scale=kv.k_scale, v_scale=kv.v_scale)
     if stream:
         assert B == 1 and dec.step_path(1) == "stream"
     dec.load_numpy_weights(W)
@@ -223,7 +233,7 @@ def _run_stage_checks(torch, shape, W, batch, what, stream=False):
         torch.cuda.synchronize()
         tp = {k: v.cpu().numpy() for k, v in taps.items()}
         _stage_checks(shape, W, batch, tp, batch.pool, pool_to_host(pool), layer,
-                      logits.cpu().numpy(), nxt.cpu().numpy(), mfma)
+                      logits.cpu().numpy(), nxt.cpu().numpy(), mfma, kv)
     assert dec.device_status() == 0
     dec.close()
 
@@ -257,6 +267,59 @@ def test_head_shapes_stages(torch, D, G, ctx):
     W = synth.make_weights(shape, seed)
     batch = synth.make_paged_batch(shape, ctx, 1, seed)
     _run_stage_checks(torch, shape, W, batch, f"D={D} G={G} ctx={ctx}")
+
+
+# An 8-bit (E4M3) pool: the append's codes bit-exact, attention over the
+# codes times their scales, every other stage unchanged; batch 1 (VALU
+# GEMV), 5 and 16 (MFMA items), one split up to a combine of more than 16,
+# head_dim 64 and 128.  The scales are powers of two (0.5 for K, 2 for V).
+@pytest.mark.parametrize("shape_name", ["d64g2", "d128g4"])
+@pytest.mark.parametrize("ctx", [[0], [700], [0, 17, 300, 40, 1100], list(range(0, 320, 20))],
+                         ids=["b1", "b1_700", "b5", "b16"])
+def test_fp8_pool_stages(torch, shape_name, ctx):
+    shape = synth.TINY if shape_name == "d64g2" else \
+        synth.ModelShape("d128g4", 2, 256, 8, 2, 128, 704, 4096, True)
+    seed = 400 + len(ctx) + shape.head_dim
+    W = synth.make_weights(shape, seed)
+    batch = synth.make_paged_batch(shape, ctx, 1, seed, kv_fp8=True)
+    _run_stage_checks(torch, shape, W, batch, f"fp8 {shape_name} ctx={ctx}",
+                      kv=oracle.KvFormat(True, 0.5, 2.0))
+
+
+@pytest.mark.parametrize("persistent", [False, True], ids=["graph", "persistent"])
+@pytest.mark.parametrize("scales", [(1.0, 1.0), (0.25, 3.0)], ids=["unit", "scaled"])
+def test_fp8_pool_teacher_forced(torch, persistent, scales):
+    """Decode steps on an 8-bit pool (batches 1 and 3; a persistent handle
+    runs batch 1 through the per-stage graph, the streaming kernel taking
+    bf16 pools only), each side keeping its own pool, ids teacher-forced by
+    the oracle; logits to the decode step's bound at every step."""
+    shape = synth.TINY
+    kv = oracle.KvFormat(True, *scales)
+    W = synth.make_weights(shape, 501)
+    orc = oracle.Oracle(shape, W)
+    for ctx in ([40], [5, 70, 300]):
+        B = len(ctx)
+        batch = synth.make_paged_batch(shape, ctx, 8, 502 + B, kv_fp8=True)
+        dec = Decoder(shape, B, batch.max_pages, batch.num_pages, persistent=persistent,
+                      kv_fp8=True, k_scale=kv.k_scale, v_scale=kv.v_scale)
+        assert dec.step_path(B) == "graph"
+        dec.load_numpy_weights(W)
+        pool = pool_to_device(batch.pool)
+        pool_or = batch.pool.copy()
+        io = StepIO(torch, B, batch.max_pages, shape.vocab)
+        tokens, positions = batch.tokens.copy(), batch.positions.copy()
+        for step in range(8):
+            say(f"fp8 teacher-forced B={B} persistent={persistent} step {step}")
+            io.set(tokens, positions, batch.block_tables)
+            io.run(dec, pool)
+            lg_or, nx_or, _ = orc.decode_step(tokens, positions, batch.block_tables, pool_or,
+                                              kv=kv)
+            torch.cuda.synchronize()
+            check_logits(io.logits.cpu().numpy(), lg_or, f"fp8 B={B} step {step}")
+            check_next_ids(io.nxt.cpu().numpy(), lg_or, f"fp8 B={B} step {step}")
+            tokens, positions = nx_or.astype(np.int32), positions + 1
+        assert dec.device_status() == 0
+        dec.close()
 
 
 def test_max_context_stages(torch):
@@ -580,19 +643,21 @@ def _weights(shape, seed):
 # also on such a handle.
 @pytest.mark.parametrize("name,persistent", [
     (n, False) for n in ("4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
-                         "8b_bs8_ragged")] + [("4b_bs1_ctx512", True)],
+                         "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv")] +
+    [("4b_bs1_ctx512", True)],
     ids=lambda v: v if isinstance(v, str) else ("persistent" if v else "graph"))
 def test_full_size_steps(torch, name, persistent):
     w = synth.WORKLOADS[name]
     shape = w.shape
     W = _weights(shape, 2 if shape is synth.QWEN3_4B else w.seed)
     ctx0 = synth.context_lengths(w)
-    batch = synth.make_paged_batch(shape, ctx0, w.steps, w.seed)
+    kv = oracle.KvFormat(True) if w.kv_fp8 else oracle.BF16
+    batch = synth.make_paged_batch(shape, ctx0, w.steps, w.seed, kv_fp8=w.kv_fp8)
     say(f"{name} persistent={persistent}: B={w.batch} ctx0={ctx0.tolist()} "
         f"pages={batch.num_pages}")
     orc = oracle.Oracle(shape, W)
     dec = Decoder(shape, w.batch, batch.max_pages, batch.num_pages, use_graphs=True,
-                  persistent=persistent)
+                  persistent=persistent, kv_fp8=w.kv_fp8)
     assert dec.step_path(w.batch) == ("stream" if persistent else "graph")
     dec.load_numpy_weights(W)
     pool = pool_to_device(batch.pool)
@@ -603,7 +668,8 @@ def test_full_size_steps(torch, name, persistent):
         say(f"{name}: step {step}")
         io.set(tokens, positions, batch.block_tables)
         io.run(dec, pool)
-        lg_or, nx_or, _ = orc.decode_step(tokens, positions, batch.block_tables, pool_or)
+        lg_or, nx_or, _ = orc.decode_step(tokens, positions, batch.block_tables, pool_or,
+                                          kv=kv)
         torch.cuda.synchronize()
         r = check_logits(io.logits.cpu().numpy(), lg_or, f"{name} step {step}")
         ex = check_next_ids(io.nxt.cpu().numpy(), lg_or, f"{name} step {step}")

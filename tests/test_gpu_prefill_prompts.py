@@ -161,6 +161,52 @@ def test_full_width_512_row_prompt(torch):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("shape_name", ["d64g2", "d128g4"])
+def test_fp8_pool_prompts_match_oracle(torch, shape_name):
+    """qd_prefill_prompts on an 8-bit (E4M3) pool, scales 0.5 for K and 2 for
+    V: continuation chunks and segments that end no prompt, each prompt's last
+    logits against the oracle on its own 8-bit pool, one position at a time;
+    no other pool byte changes, and layer 0's codes are within one step of
+    the oracle's (the two sides round values that differ by the projection's
+    error only)."""
+    shape = SHAPES[shape_name]
+    kv = oracle.KvFormat(True, 0.5, 2.0)
+    lens, calls = PLANS["chunks"]
+    seed = 770 + len(shape_name)
+    W = synth.make_weights(shape, seed)
+    prompts = [synth.uniform_int(seed + i, "prompt", shape.vocab, n) for i, n in enumerate(lens)]
+    batch = synth.make_paged_batch(shape, [0] * len(lens), max(lens), seed, fill_kv=False,
+                                   kv_fp8=True)
+    pool_start = batch.pool.copy()
+    pool = pool_to_device(batch.pool)
+    rows = max(sum(e - a for _, a, e in segs) for segs in calls)
+    dec = Decoder(shape, 4, batch.max_pages, batch.num_pages, max_prefill_rows=rows,
+                  kv_fp8=True, k_scale=kv.k_scale, v_scale=kv.v_scale)
+    dec.load_numpy_weights(W)
+    got = _run_calls(torch, dec, prompts, batch.block_tables, pool, calls, shape.vocab)
+    assert dec.device_status() == 0
+    dec.close()
+    orc = oracle.Oracle(shape, W)
+    pool_or = batch.pool
+    for s, pr in enumerate(prompts):
+        lg_or, _ = orc.prefill(pr, batch.block_tables[s], pool_or, kv=kv)
+        r = check_logits(got[s][0][None], lg_or[None], f"prompt {s}")
+        check_next_ids(got[s][1], lg_or[None], f"prompt {s}")
+        say(f"fp8 {shape_name} prompt {s} ({len(pr)} tokens): logit ratio {r:.3e}")
+    m = appended_mask(batch, [(s, p) for s, pr in enumerate(prompts) for p in range(len(pr))])
+    host = pool_to_host(pool)
+    np.testing.assert_array_equal(host[~m], pool_start[~m])
+    # layer 0's codes come from the embedding through one projection: the
+    # two sides' values differ by the projection's rounding only, so a code
+    # may differ from the oracle's by one step where the value sits at a
+    # rounding boundary, never more
+    a, b = host[0][m[0]].astype(np.int32), pool_or[0][m[0]].astype(np.int32)
+    same_sign = (a & 0x80) == (b & 0x80)
+    assert np.all(same_sign | ((a & 0x7F) == 0) | ((b & 0x7F) == 0))
+    assert np.abs((a & 0x7F) - (b & 0x7F)).max() <= 1
+    say(f"fp8 {shape_name}: layer-0 codes equal {np.mean(a == b):.4f}")
+
+
 def test_prompt_then_decode(torch):
     """A 40-token prompt through qd_prefill_prompts, then 8 greedy decode
     steps from its own next id, each checked against the oracle (which

@@ -241,6 +241,14 @@ constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false
   return (persistent ? kAttnWavesPersistent : kAttnWaves) *
          attn_pages_per_wave(B, persistent, long_ctx);
 }
+// An 8-bit pool loads half the bytes per page: its items hold more pages
+// per wave (2 instead of 1, 5 instead of 3: 6 would spill registers at head
+// dim 128 with 4 query heads per KV head), so that about the same registers
+// keep as many bytes in flight and a sequence has fewer splits to combine.
+constexpr int attn_pages_per_wave_kv(int B, bool long_ctx, bool kv_fp8) {
+  return !kv_fp8 ? attn_pages_per_wave(B, false, long_ctx)
+                 : attn_pages_per_wave(B, false, long_ctx) == 1 ? 2 : 5;
+}
 // Splits of one sequence the final combine can hold (its (max, sum) pairs sit in LDS).
 constexpr int kMaxSplitsStaged = 512;
 
@@ -277,7 +285,8 @@ hipError_t launch_repack(const uint16_t* src, int rows, int K, uint16_t* dst, in
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s);
-// waves, pages: kAttnWaves with 1 or 3 pages per wave.
+// waves, pages: kAttnWaves with 1 or 3 pages per wave (bf16 pool), 2 or 5
+// (8-bit pool).
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* gain, int H,

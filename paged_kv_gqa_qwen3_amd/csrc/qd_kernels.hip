@@ -275,26 +275,28 @@ hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s) {
   }
 }
 
-template <int D, int G, int NW, int PW>
+template <int D, int G, int NW, int PW, class KV>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  if (a.kv_fp8)
-    hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KvFp8>), dim3(a.grid), dim3(NW * 64),
-                       sizeof(AttnSmem<D, G, NW>), s, a);
-  else
-    hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KvBf16>), dim3(a.grid), dim3(NW * 64),
-                       sizeof(AttnSmem<D, G, NW>), s, a);
+  hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KV>), dim3(a.grid), dim3(NW * 64),
+                     sizeof(AttnSmem<D, G, NW>), s, a);
   return hipGetLastError();
 }
 
 template <int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, int pages, hipStream_t s) {
-  return pages == 1 ? launch_attention_t<D, G, kAttnWaves, 1>(a, s)
-                    : launch_attention_t<D, G, kAttnWaves, 3>(a, s);
+  if (!a.kv_fp8) {
+    if (pages == 1) return launch_attention_t<D, G, kAttnWaves, 1, KvBf16>(a, s);
+    if (pages == 3) return launch_attention_t<D, G, kAttnWaves, 3, KvBf16>(a, s);
+  } else {
+    if (pages == 2) return launch_attention_t<D, G, kAttnWaves, 2, KvFp8>(a, s);
+    if (pages == 5) return launch_attention_t<D, G, kAttnWaves, 5, KvFp8>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int waves, int pages,
                             hipStream_t s) {
-  if (waves != kAttnWaves || (pages != 1 && pages != 3)) return hipErrorInvalidValue;
+  if (waves != kAttnWaves) return hipErrorInvalidValue;  // (pages: launch_attention_dg)
   if (head_dim == 128) {
     if (group == 4) return launch_attention_dg<128, 4>(a, pages, s);
     if (group == 2) return launch_attention_dg<128, 2>(a, pages, s);

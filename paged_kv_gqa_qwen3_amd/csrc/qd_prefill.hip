@@ -20,6 +20,15 @@ namespace qd {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// Two floats that are bf16 values (E4M3 values widened: exact) as a packed
+// pair of bf16 bits, the first in the low half.  (The widening goes through
+// v_cvt_scalef32_pk_f32_fp8: on this part it reproduces the OCP E4M3 table
+// for all 256 codes, while the bf16-output form gave the first code of a
+// pair for both halves in the same check.)
+__device__ __forceinline__ unsigned bf_pair(f32x2 f) {
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
+}
+
 // ------------------------------------------------------------------ helpers
 
 // Segment of chunk row m (rows of segment s are [row0[s], row0[s+1])).
@@ -453,26 +462,36 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     if constexpr (KV::kFp8) {
       const u32x2 c = *reinterpret_cast<const u32x2*>(base + (lane & 15) * D + 32 * kk +
                                                       8 * (lane >> 4));
+      const f32x2 f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.0f, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.0f, true),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.0f, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.0f, true)};
       u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned word = i < 2 ? c.x : c.y, sh = 16 * (i & 1);
-        const unsigned lo = __float_as_uint(e4m32f((word >> sh) & 0xffu)) >> 16;
-        const unsigned hi = __float_as_uint(e4m32f((word >> (sh + 8)) & 0xffu)) >> 16;
-        w[i] = lo | (hi << 16);
-      }
+      for (int i = 0; i < 4; ++i) w[i] = bf_pair(f[i]);
       return __builtin_bit_cast(bf16x8, w);
     } else {
       return *reinterpret_cast<const bf16x8*>(base + kk * 1024 + lane * 16);
     }
   };
-  // bf16 bits of V[key][dim] from the staged page
-  auto v_elem = [&](const unsigned char* base, int key, int dim) -> short {
-    const unsigned char* p = base + KCH * 1024 + (key / KPC) * VSTRIDE + (key % KPC) * D * EB + dim * EB;
-    if constexpr (KV::kFp8)
-      return (short)(__float_as_uint(e4m32f(*p)) >> 16);
-    else
-      return *reinterpret_cast<const short*>(p);
+  // V^T A operand: lane l holds dim `dim` of keys 4*(l/16)..+3 as bf16
+  auto v_frag = [&](const unsigned char* base, int dim) -> s16x4 {
+    auto at = [&](int key) {
+      return base + KCH * 1024 + (key / KPC) * VSTRIDE + (key % KPC) * D * EB + dim * EB;
+    };
+    const int k0 = 4 * (lane >> 4);
+    s16x4 va;
+    if constexpr (KV::kFp8) {
+      const unsigned w = (unsigned)*at(k0) | ((unsigned)*at(k0 + 1) << 8) |
+                         ((unsigned)*at(k0 + 2) << 16) | ((unsigned)*at(k0 + 3) << 24);
+      const u32x2 pr = u32x2{bf_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false)),
+                             bf_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true))};
+      va = __builtin_bit_cast(s16x4, pr);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) va[r] = *reinterpret_cast<const short*>(at(k0 + r));
+    }
+    return va;
   };
 
   f32x4 o[DT];
@@ -533,9 +552,7 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     // V^T A operand: lane l holds dim 16*dt + l%16 of keys 4*(l/16)..+3
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      s16x4 va;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) va[r] = v_elem(base, 4 * (lane >> 4) + r, 16 * dt + (lane & 15));
+      const s16x4 va = v_frag(base, 16 * dt + (lane & 15));
       o[dt] = o[dt] * alpha;
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[dt], 0, 0, 0);

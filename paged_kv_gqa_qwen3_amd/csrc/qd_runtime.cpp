@@ -241,8 +241,9 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false)
 
 // Most splits of one sequence (its longest table) at batch B in the
 // per-stage attention kernel, and in the streaming kernel's items.
+int attn_pw(const qd_handle* h, int B) { return attn_pages_per_wave_kv(B, h->long_ctx, h->kv_fp8); }
 int attn_splits(const qd_handle* h, int B) {
-  const int pps = attn_pages_per_split(B, false, h->long_ctx);
+  const int pps = kAttnWaves * attn_pw(h, B);
   return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
 }
 int stream_attn_splits(const qd_handle* h) {
@@ -479,11 +480,11 @@ int record_step(qd_handle* h, const StepPtrs& sp, const qd_taps* taps, hipStream
     if (sp.n_logits >= 0) {  // prefill: every row's k, v in the pool before any row attends
       aa.kv_mode = kAppendOnly;
       HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
-                                  attn_pages_per_wave(B, false, h->long_ctx), s));
+                                  attn_pw(h, B), s));
       aa.kv_mode = kAttendOnly;
     }
     HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
-                                attn_pages_per_wave(B, false, h->long_ctx), s));
+                                attn_pw(h, B), s));
     PROF(QD_PROF_ATTN);
     if (tap && taps->attn)
       HIP_TRY(h, hipMemcpyAsync(taps->attn, h->attn, sizeof(float) * B * h->QD,
@@ -605,7 +606,7 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
     aa.trace = tr(QD_PROF_ATTN, l);
 #endif
     HIP_TRY(h, launch_attention(aa, h->D, h->G, kAttnWaves,
-                                attn_pages_per_wave(B, false, h->long_ctx), s));
+                                attn_pw(h, B), s));
 
     GemvArgs o = gemv_args(w.o, H, h->QD, po);  // residual in place on this set
     o.x = h->attn; o.xh = h->attn_hi; o.xl = h->attn_lo;

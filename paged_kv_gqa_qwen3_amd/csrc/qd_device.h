@@ -1417,19 +1417,20 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   mark(4);
   if (!arrive_last(cnt, (unsigned)nsplit, &sm.flag)) return;
   mark(5);
-  // (max, sum) of every split into LDS, and (for up to 16 splits) each
+  // (max, sum) of every split into LDS, and (for up to kFastSplits splits) each
   // 4-output chunk's split partials into registers with one 16-byte
   // device-scope load per split, in the same round trip; then per head the
   // overall max and the splits' factors exp(m_s - M)
   constexpr int kChunks = G * D / 4;  // 4-float output chunks, one per thread
   static_assert(kChunks <= NW * 64, "one chunk per thread");
-  f32x4 ov[16];
-  if (nsplit <= 16 && tid < kChunks) {
+  constexpr int kFastSplits = 24;  // (8K context at batch 1: 22 splits)
+  f32x4 ov[kFastSplits];
+  if (nsplit <= kFastSplits && tid < kChunks) {
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         a.o_part, 0, (int)((size_t)a.B * Hq * S_max * D * 4), kBufferWord3);
     const int base = (int)(((qh0 + (4 * tid) / D) * S_max) * D + (4 * tid) % D) * 4;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < kFastSplits; ++j)
       if (j < nsplit)
         ov[j] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, base + j * D * 4, 0, kDeviceScope));
@@ -1453,12 +1454,12 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     sm.lsum[tid] = L;
   }
   __syncthreads();
-  if (nsplit <= 16) {
+  if (nsplit <= kFastSplits) {
     if (tid < kChunks) {
       const int h = (4 * tid) / D, d0 = (4 * tid) % D;
       f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < kFastSplits; ++j)
         if (j < nsplit) o += ov[j] * sm.ml[0][h][j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

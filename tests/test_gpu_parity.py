@@ -242,8 +242,10 @@ def _run_stage_checks(torch, shape, W, batch, what, stream=False, kv=oracle.BF16
     (1, [0]), (1, [15]), (1, [16]), (2, [17, 300]), (3, [31, 32, 33]), (4, [1, 64, 129, 200]),
     (5, [0, 15, 16, 100, 255]), (8, [3] * 8), (16, list(range(0, 320, 20))),
     # splits of 8 pages (batch <= 8, at most 128 pages per sequence) or 24
-    # pages: one to 17 of them, and a combine of more than 16 splits (2100)
-    (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]),
+    # pages: one to 17 of them, a combine of more than 16 splits (2100), and
+    # of 20 (7600: the combine that loads every split's partials in one round
+    # trip, up to 24 splits)
+    (3, [511, 512, 1100]), (6, [0, 511, 512, 1100, 40, 2000]), (1, [2100]), (1, [7600]),
     # 32- and 64-column MFMA items, up to the largest batch a handle takes
     (24, [(37 * i) % 400 for i in range(24)]), (33, [(53 * i) % 300 for i in range(33)]),
     (64, [(29 * i) % 200 for i in range(64)]),

@@ -426,6 +426,67 @@ int qd_blocks_publish(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t 
  * (a multiple of 16), which need no prefill. */
 int qd_blocks_match(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t n);
 
+/* ---- Serving loop: continuous (iteration-level) batching ----
+ * Requests wait in arrival order; every qd_engine_step admits as many as
+ * the batch has room for, prefills their prompts (qd_prefill_prompts;
+ * prompt pages found in the prefix cache are taken over instead), runs one
+ * decode step (qd_decode_step) for every request that already has a token,
+ * and returns the new tokens.  A request joins the decode batch in the
+ * iteration after its prompt is done and leaves it on its end-of-sequence
+ * token or at its token limit, so the batch size changes between
+ * iterations; each batch size replays its own captured graph (the locsic
+ * page "推理引擎里面发生了什么", section Continuous Batching; the rkmt page
+ * "从零构建 Qwen3-8B 推理引擎", sections 4.3.2 on the batching scheduler and
+ * 4.4.4 on the automatic prefix cache).  Greedy decoding.
+ *
+ * The engine owns a page manager (qd_blocks) over all num_pages pages of
+ * the pool and small device buffers; a request takes every page it can need
+ * (prompt plus max_new_tokens) when it is admitted, so nothing is ever
+ * preempted; a request whose pages are not available stays first in line
+ * until others leave.  Prompt rows per iteration are limited by the
+ * handle's max_prefill_rows (a longer prompt continues over several
+ * iterations).  When a request leaves, the full pages of its tokens are
+ * registered in the prefix cache.  Not thread-safe; the handle must outlive
+ * the engine and no other work may use the handle or the pool while the
+ * engine lives.  Errors set qd_last_error(h); an error from the GPU or the
+ * page manager leaves the engine unusable (later calls: QD_ESTATE). */
+typedef struct qd_engine qd_engine;
+
+/* kv_pool: the DEVICE pool laid out as for qd_decode_step.  QD_EUNSUPPORTED
+ * when the handle was created with max_prefill_rows = 0. */
+int qd_engine_create(qd_handle* h, void* kv_pool, qd_engine** out);
+/* Waits for the handle's stream, then frees the engine (not the handle or
+ * the pool).  NULL is a no-op. */
+void qd_engine_destroy(qd_engine* e);
+/* Queue a request: `req` is the caller's id (unique among unfinished
+ * requests), prompt int32 [n_prompt] HOST (copied), n_prompt >= 1, at most
+ * max_new_tokens >= 1 tokens to generate, eos_id the token that ends it
+ * early (-1: none).  QD_EINVAL on a bad argument or token id;
+ * QD_EUNSUPPORTED when n_prompt + max_new_tokens - 1 positions exceed
+ * max_pages_per_seq*16 or the whole pool. */
+int qd_engine_submit(qd_engine* e, int64_t req, const int32_t* prompt, int32_t n_prompt,
+                     int32_t max_new_tokens, int32_t eos_id);
+/* One iteration (synchronous).  Writes *n_out entries (at most max_batch)
+ * to the HOST arrays out_req / out_token / out_done of max_out >= max_batch
+ * entries: a request id, its next token, and 1 when that token is its last
+ * (the request has left).  *n_out = 0 with nothing queued. */
+int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out_token,
+                   int32_t* out_done, int32_t* n_out);
+
+typedef struct qd_engine_stats {
+  int64_t steps;          /* iterations that ran GPU work */
+  int64_t prefill_rows;   /* prompt positions prefilled */
+  int64_t cached_rows;    /* prompt positions taken from the prefix cache */
+  int64_t decode_rows;    /* sequence positions decoded */
+  int64_t tokens_out;     /* tokens returned */
+  int32_t waiting;        /* requests not admitted yet */
+  int32_t running;        /* admitted requests (prefilling or decoding) */
+  int32_t pages_available;
+  int32_t reserved;
+} qd_engine_stats;
+
+int qd_engine_get_stats(const qd_engine* e, qd_engine_stats* out);
+
 /* Free everything the handle owns: captured graphs, packed weights,
  * scratch (it waits for its stream first; the caller's pool and buffers are
  * untouched).  Call it before the HIP runtime is torn down (before process

@@ -36,7 +36,9 @@ EXPORTED = ("qd_create", "qd_load_weights", "qd_decode_step", "qd_prefill", "qd_
             "qd_step_path", "qd_sample", "qd_destroy", "qd_last_error",
             "qd_blocks_create", "qd_blocks_destroy", "qd_blocks_add", "qd_blocks_reserve",
             "qd_blocks_release", "qd_blocks_fork", "qd_blocks_tables", "qd_blocks_length",
-            "qd_blocks_available", "qd_blocks_publish", "qd_blocks_match")
+            "qd_blocks_available", "qd_blocks_publish", "qd_blocks_match",
+            "qd_engine_create", "qd_engine_destroy", "qd_engine_submit", "qd_engine_step",
+            "qd_engine_get_stats")
 
 PROF_CLASSES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head")
 
@@ -68,6 +70,14 @@ class QdTaps(ctypes.Structure):
 TAP_NAMES = ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out", "final_h")
 
 _lib = None
+
+
+class QdEngineStats(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("prefill_rows", ctypes.c_int64),
+                ("cached_rows", ctypes.c_int64), ("decode_rows", ctypes.c_int64),
+                ("tokens_out", ctypes.c_int64), ("waiting", ctypes.c_int32),
+                ("running", ctypes.c_int32), ("pages_available", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class QdError(RuntimeError):
@@ -122,6 +132,14 @@ def load_library():
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = args
         lib.qd_blocks_destroy.restype = None
+        for name, args in (("qd_engine_create", [P, P, ctypes.POINTER(P)]),
+                           ("qd_engine_submit", [P, I64, P, I32, I32, I32]),
+                           ("qd_engine_step", [P, I32, P, P, P, ctypes.POINTER(I32)]),
+                           ("qd_engine_get_stats", [P, ctypes.POINTER(QdEngineStats)])):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = args
+        lib.qd_engine_destroy.restype = None
+        lib.qd_engine_destroy.argtypes = [P]
         lib.qd_blocks_destroy.argtypes = [P]
         lib.qd_sample.restype = ctypes.c_int
         lib.qd_sample.argtypes = [P, ctypes.c_int32, P, P, P, P, P, P]
@@ -380,6 +398,51 @@ class PageManager:
         if self.h:
             self.lib.qd_blocks_destroy(self.h)
             self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Engine:
+    """Continuous-batching serving loop over a handle and its KV pool
+    (qd_engine_* in include/qd.h).  submit() queues a request; step() runs
+    one iteration and returns [(request id, token, finished)]."""
+
+    def __init__(self, handle: int, kv_pool, max_batch: int):
+        self.lib = load_library()
+        self.handle = handle
+        self.max_out = max_batch
+        e = ctypes.c_void_p()
+        _check(self.lib.qd_engine_create(handle, _ptr(kv_pool), ctypes.byref(e)), handle)
+        self.e = e.value
+        self._req = np.empty(max_batch, dtype=np.int64)
+        self._tok = np.empty(max_batch, dtype=np.int32)
+        self._done = np.empty(max_batch, dtype=np.int32)
+
+    def submit(self, req: int, prompt, max_new_tokens: int, eos_id: int = -1) -> None:
+        t = np.ascontiguousarray(prompt, dtype=np.int32)
+        _check(self.lib.qd_engine_submit(self.e, req, t.ctypes.data if len(t) else None, len(t),
+                                         max_new_tokens, eos_id), self.handle)
+
+    def step(self):
+        n = ctypes.c_int32()
+        _check(self.lib.qd_engine_step(self.e, self.max_out, self._req.ctypes.data,
+                                       self._tok.ctypes.data, self._done.ctypes.data,
+                                       ctypes.byref(n)), self.handle)
+        return [(int(self._req[i]), int(self._tok[i]), bool(self._done[i])) for i in range(n.value)]
+
+    def stats(self) -> dict:
+        st = QdEngineStats()
+        _check(self.lib.qd_engine_get_stats(self.e, ctypes.byref(st)), self.handle)
+        return {name: getattr(st, name) for name, _ in QdEngineStats._fields_ if name != "reserved"}
+
+    def close(self) -> None:
+        if self.e:
+            self.lib.qd_engine_destroy(self.e)
+            self.e = None
 
     def __del__(self):
         try:

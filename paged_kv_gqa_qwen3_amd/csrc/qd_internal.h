@@ -8,7 +8,16 @@
 
 #include <string>
 
+struct qd_config;
+struct qd_handle;
+
 namespace qd {
+
+// Host runtime services for the serving loop (qd_engine.cpp): the handle's
+// configuration, and recording an error message on the handle (returned by
+// qd_last_error) together with its code.
+const qd_config* handle_config(const qd_handle* h);
+int handle_fail(qd_handle* h, int code, const std::string& msg);
 
 // Packed weight layout ("tile-major").  A [N][K] bf16 matrix is stored as
 // tiles of 16 rows x 32 columns, tile (rt, kt) at element offset

@@ -928,6 +928,10 @@ int qd::set_global_error(int code, const std::string& msg) {
   return code;
 }
 
+const qd_config* qd::handle_config(const qd_handle* h) { return &h->cfg; }
+
+int qd::handle_fail(qd_handle* h, int code, const std::string& msg) { return fail(h, code, msg); }
+
 extern "C" {
 
 int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {

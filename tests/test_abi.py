@@ -88,3 +88,10 @@ def test_null_arguments(lib):
     assert lib.qd_prefill_prompts(None, 1, None, None, None, None, None, 0, None,
                                   None) == binding.QD_EINVAL
     lib.qd_destroy(None)
+    e = ctypes.c_void_p()
+    assert lib.qd_engine_create(None, None, ctypes.byref(e)) == binding.QD_EINVAL
+    assert lib.qd_engine_submit(None, 0, None, 1, 1, -1) == binding.QD_EINVAL
+    n = ctypes.c_int32()
+    assert lib.qd_engine_step(None, 64, None, None, None, ctypes.byref(n)) == binding.QD_EINVAL
+    assert lib.qd_engine_get_stats(None, None) == binding.QD_EINVAL
+    lib.qd_engine_destroy(None)

@@ -399,6 +399,79 @@ def time_prefill_prompts(torch, shape, W, n_tokens=512, reps=5):
             "projection_tflops": round(proj_flop / (ms / 1e3) / 1e12, 1)}
 
 
+def time_serving(torch, shape, W, n_req=64, max_batch=16, max_new=128, rows=512, seed=17):
+    """Offline serving through the continuous-batching engine (qd_engine_*):
+    n_req requests queued at once, prompts of 128..1024 tokens (uniform),
+    every second one starting with the same 256-token system prompt (or
+    its first tokens, for a shorter prompt),
+    max_new greedy tokens each, at most max_batch decoding together and
+    `rows` prompt rows per iteration.  Graphs for every batch size are
+    captured by a warm-up set of requests first.  Reports wall-clock rates
+    over the whole queue and the median iteration time while the batch is
+    full and no prompt is being prefilled (the engine's host work per
+    iteration shows against the graph replay of the same batch)."""
+    from paged_kv_gqa_qwen3_amd.decoder import Decoder
+    V = shape.vocab
+    rng = np.random.Generator(np.random.PCG64(seed))
+    system = rng.integers(0, V, 256, dtype=np.int32)
+    prompts = []
+    for i in range(n_req):
+        p = rng.integers(0, V, int(rng.integers(128, 1025)), dtype=np.int32)
+        if i % 2 == 0:
+            p[:min(256, len(p))] = system[:len(p)]
+        prompts.append(p)
+    mpps = -(-(1024 + max_new) // 16)
+    num_pages = max_batch * mpps + 256
+    dec = Decoder(shape, max_batch, mpps, num_pages, use_graphs=True, persistent=True,
+                  max_prefill_rows=rows)
+    dec.load_numpy_weights(W)
+    pool = torch.zeros(shape.num_layers, num_pages, 2, shape.num_kv_heads, 16, shape.head_dim,
+                       dtype=torch.int16, device="cuda")
+    eng = binding.Engine(dec.handle, pool, max_batch)
+
+    def drain():
+        per = []
+        prev = eng.stats()
+        while True:
+            t = time.perf_counter()
+            eng.step()
+            dt = time.perf_counter() - t
+            st = eng.stats()
+            per.append((dt, st["decode_rows"] - prev["decode_rows"],
+                        st["prefill_rows"] - prev["prefill_rows"]))
+            prev = st
+            if st["waiting"] == 0 and st["running"] == 0:
+                return per, st
+
+    # warm-up: requests that leave one by one, so every batch size 1..max_batch
+    # captures its graph before the timed queue
+    for i in range(max_batch):
+        eng.submit(1_000_000 + i, rng.integers(0, V, 16, dtype=np.int32), 2 + i)
+    _, st0 = drain()
+    for i, p in enumerate(prompts):
+        eng.submit(i, p, max_new)
+    t0 = time.perf_counter()
+    per, st = drain()
+    wall = time.perf_counter() - t0
+    assert dec.device_status() == 0
+    eng.close()
+    dec.close()
+    del pool
+    torch.cuda.empty_cache()
+    gen = st["tokens_out"] - st0["tokens_out"]
+    n_prompt = int(sum(len(p) for p in prompts))
+    full = [dt for dt, b, r in per if b == max_batch and r == 0]
+    return {"requests": n_req, "prompt_tokens": n_prompt, "generated_tokens": int(gen),
+            "max_batch": max_batch, "prefill_rows_per_iteration": rows,
+            "max_new_tokens": max_new, "iterations": len(per), "wall_s": round(wall, 3),
+            "output_tokens_per_s": round(gen / wall, 1),
+            "total_tokens_per_s": round((gen + n_prompt) / wall, 1),
+            "prompt_tokens_from_prefix_cache": int(st["cached_rows"] - st0["cached_rows"]),
+            "mean_decode_batch": round(float(np.mean([b for _, b, _ in per])), 2),
+            "full_batch_iteration_ms_median": round(1e3 * float(np.median(full)), 4) if full else None,
+            "full_batch_iterations": len(full)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +486,10 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time qd_prefill_prompts on a 512-token prompt of the headline "
                          "model only, print its record and stop (profiling runs)")
+    ap.add_argument("--no-serve", action="store_true",
+                    help="skip the serving-loop record (qd_engine over 64 queued requests)")
+    ap.add_argument("--serve-only", action="store_true",
+                    help="only the serving-loop record")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--mode", choices=("auto", "graph"), default="auto",
                     help="auto: a persistent handle, on which the library runs batch 1 as "
@@ -448,6 +525,14 @@ def main():
         rec = time_prefill_prompts(torch, shape, W, reps=args.reps)
         log(f"[bench] qd_prefill_prompts of 512 prompt tokens {rec}")
         print(json.dumps({"prefill": rec, "model": shape.name}))
+        torch.cuda.synchronize()
+        return
+    if args.serve_only:
+        shape = synth.WORKLOADS[HEADLINE].shape
+        W = synth.make_weights(shape, WEIGHT_SEED[shape.name])
+        rec = time_serving(torch, shape, W)
+        log(f"[bench] serving loop {rec}")
+        print(json.dumps({"serve": rec, "model": shape.name}))
         torch.cuda.synchronize()
         return
     names = [n for n in args.workloads.split(",") if n]
@@ -516,6 +601,9 @@ def main():
                     log(f"[bench] {w.name}: qd_prefill (32-row chunks on the decode "
                         f"kernels) of 512 prompt tokens "
                         f"{results[w.name]['prefill_decode_kernels']}")
+                if not args.no_serve:
+                    results[w.name]["serve"] = time_serving(torch, shape, W)
+                    log(f"[bench] {w.name}: serving loop {results[w.name]['serve']}")
                 if not args.no_cpu_baseline:
                     log("[bench] timing the CPU oracle on a bounded sample")
                     headline_extra["cpu_baseline"] = cpu_baseline(w, W, batch, args.cpu_budget)

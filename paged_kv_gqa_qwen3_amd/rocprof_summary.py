@@ -126,8 +126,8 @@ def traffic_summary(fetch_dir: str, write_dir: str, workload: str, kind: str,
 
     fc, wc = per_class(f), per_class(w)
     sha = bench.kernel_source_sha256(kind)
-    run = (f"python -u bench.py --workloads {workload} --steps 4 --warmup 1 --no-cpu-baseline "
-           f"--no-prefill --copy-calibration-mib 1024")
+    run = (f"python -u bench.py --steps 4 --warmup 1 --reps 1 --no-cpu-baseline --no-prefill "
+           f"--no-serve --copy-calibration-mib 1024 --workloads {workload}")
     lines = [f"# HBM traffic per dispatch (rocprofv3 --pmc), workload {workload}", "",
              "commands (repo root, MI355X), one counter per run, then this summary:",
              f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- {run}",

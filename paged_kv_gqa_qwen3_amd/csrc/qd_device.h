@@ -1133,28 +1133,28 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   };
   const bool early = a.qkv_part == nullptr || a.qkv_S <= 8;
   float xp1[HPW][8], xp2[HPW][8], gn1[HPW], gn2[HPW];
+  // The same 8 loads per value on every path (a materialised q|k|v row
+  // repeats its one address; past 8 splits the loads go unused and
+  // split_sum reads the partials later): with no branch between them and
+  // the block-table loads issued before, the compiler's wait for a page id
+  // does not also wait for these inputs.
   auto load_inputs = [&]() {
+    const bool part = a.qkv_part != nullptr;
+    const int rows = part ? a.qkv_rows : 1, S = part ? max(a.qkv_S, 1) : 1;
+    const float* base = part ? a.qkv_part : a.qkv + (size_t)b * (Hq + 2 * Hkv) * D;
+    const size_t stride = part ? (size_t)rows * a.B : 0;
 #pragma unroll
     for (int uu = 0; uu < HPW; ++uu) {
       const int hh = min(wave + NW * uu, G + 1);
       const int off = head_row(hh);
       const int l2 = act ? lane : 0;
-      if (a.qkv_part != nullptr) {
-        if (early) {
-          const int rows = a.qkv_rows, S = a.qkv_S;
-          const int n1 = off + l2, n2 = off + l2 + HALF;
-          const float* p1 = a.qkv_part + ((size_t)(n1 / rows) * S * rows + n1 % rows) * a.B + b;
-          const float* p2 = a.qkv_part + ((size_t)(n2 / rows) * S * rows + n2 % rows) * a.B + b;
+      const int n1 = off + l2, n2 = off + l2 + HALF;
+      const float* p1 = base + (part ? ((size_t)(n1 / rows) * S * rows + n1 % rows) * a.B + b : n1);
+      const float* p2 = base + (part ? ((size_t)(n2 / rows) * S * rows + n2 % rows) * a.B + b : n2);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            xp1[uu][j] = ld_in<kAgent>(p1 + (size_t)min(j, S - 1) * rows * a.B);
-            xp2[uu][j] = ld_in<kAgent>(p2 + (size_t)min(j, S - 1) * rows * a.B);
-          }
-        }
-      } else {
-        const float* row = a.qkv + (size_t)b * (Hq + 2 * Hkv) * D;
-        xp1[uu][0] = ld_in<kAgent>(row + off + l2);
-        xp2[uu][0] = ld_in<kAgent>(row + off + l2 + HALF);
+      for (int j = 0; j < 8; ++j) {
+        xp1[uu][j] = ld_in<kAgent>(p1 + (size_t)min(j, S - 1) * stride);
+        xp2[uu][j] = ld_in<kAgent>(p2 + (size_t)min(j, S - 1) * stride);
       }
     }
   };

@@ -243,20 +243,29 @@ constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 constexpr int kAttnWaves = 8;
 constexpr int kAttnWavesPersistent = 4;
 constexpr int kAttnPagesPersistent = 1;
-constexpr int attn_pages_per_wave(int B, bool persistent, bool long_ctx = false) {
-  return persistent ? kAttnPagesPersistent : B <= 8 && !long_ctx ? 1 : 3;
+// Handles of at least this many pages per sequence (and at most
+// kStreamMaxPages) give batches up to 8 two pages per wave: contexts that
+// long have splits to spare, and half as many to combine (Qwen3-8B, batch
+// 8, contexts 580-1841: 5.12 -> 4.92 ms per step); shorter handles keep one
+// page per wave, so that short contexts spread over more workgroups (batch
+// 8, context 256: 2.95 against 3.04 ms with two).
+constexpr int kMidCtxPages = 64;
+constexpr int attn_pages_per_wave(int B, bool persistent, bool long_ctx = false,
+                                  bool mid_ctx = false) {
+  return persistent ? kAttnPagesPersistent : B <= 8 && !long_ctx ? (mid_ctx ? 2 : 1) : 3;
 }
-constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false) {
+constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false,
+                                   bool mid_ctx = false) {
   return (persistent ? kAttnWavesPersistent : kAttnWaves) *
-         attn_pages_per_wave(B, persistent, long_ctx);
+         attn_pages_per_wave(B, persistent, long_ctx, mid_ctx);
 }
 // An 8-bit pool loads half the bytes per page: its items hold more pages
 // per wave (2 instead of 1, 5 instead of 3: 6 would spill registers at head
 // dim 128 with 4 query heads per KV head), so that about the same registers
 // keep as many bytes in flight and a sequence has fewer splits to combine.
-constexpr int attn_pages_per_wave_kv(int B, bool long_ctx, bool kv_fp8) {
-  return !kv_fp8 ? attn_pages_per_wave(B, false, long_ctx)
-                 : attn_pages_per_wave(B, false, long_ctx) == 1 ? 2 : 5;
+constexpr int attn_pages_per_wave_kv(int B, bool long_ctx, bool kv_fp8, bool mid_ctx = false) {
+  return !kv_fp8 ? attn_pages_per_wave(B, false, long_ctx, mid_ctx)
+                 : attn_pages_per_wave(B, false, long_ctx) == 3 ? 5 : 2;
 }
 // Splits of one sequence the final combine can hold (its (max, sum) pairs sit in LDS).
 constexpr int kMaxSplitsStaged = 512;

@@ -286,6 +286,7 @@ template <int D, int G>
 static hipError_t launch_attention_dg(const AttnArgs& a, int pages, hipStream_t s) {
   if (!a.kv_fp8) {
     if (pages == 1) return launch_attention_t<D, G, kAttnWaves, 1, KvBf16>(a, s);
+    if (pages == 2) return launch_attention_t<D, G, kAttnWaves, 2, KvBf16>(a, s);
     if (pages == 3) return launch_attention_t<D, G, kAttnWaves, 3, KvBf16>(a, s);
   } else {
     if (pages == 2) return launch_attention_t<D, G, kAttnWaves, 2, KvFp8>(a, s);

@@ -114,6 +114,7 @@ struct qd_handle {
   // batch-1 streaming step (persistent handles)
   bool persistent = false;
   bool long_ctx = false;  // max_pages_per_seq > kStreamMaxPages: batch 1 takes the per-stage kernels
+  bool mid_ctx = false;   // max_pages_per_seq >= kMidCtxPages: 2 attention pages per wave up to batch 8
   LayerDev* layers_dev = nullptr;
   unsigned* step_cnt = nullptr;
   unsigned* step_flags = nullptr;  // [2 * CUs][32]
@@ -241,7 +242,9 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false)
 
 // Most splits of one sequence (its longest table) at batch B in the
 // per-stage attention kernel, and in the streaming kernel's items.
-int attn_pw(const qd_handle* h, int B) { return attn_pages_per_wave_kv(B, h->long_ctx, h->kv_fp8); }
+int attn_pw(const qd_handle* h, int B) {
+  return attn_pages_per_wave_kv(B, h->long_ctx, h->kv_fp8, h->mid_ctx);
+}
 int attn_splits(const qd_handle* h, int B) {
   const int pps = kAttnWaves * attn_pw(h, B);
   return std::max(1, (h->cfg.max_pages_per_seq + pps - 1) / pps);
@@ -995,6 +998,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
 
   h->persistent = cfg->persistent != 0;
   h->long_ctx = cfg->max_pages_per_seq > kStreamMaxPages;
+  h->mid_ctx = cfg->max_pages_per_seq >= kMidCtxPages;
   if ((rc = setup_stream(h))) return bail(rc);
 
   // activations and scratch

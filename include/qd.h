@@ -437,7 +437,7 @@ int qd_blocks_match(qd_blocks* m, int64_t seq, const int32_t* tokens, int32_t n)
  * iterations; each batch size replays its own captured graph (the locsic
  * page "推理引擎里面发生了什么", section Continuous Batching; the rkmt page
  * "从零构建 Qwen3-8B 推理引擎", sections 4.3.2 on the batching scheduler and
- * 4.4.4 on the automatic prefix cache).  Greedy decoding.
+ * 4.4.4 on the automatic prefix cache).
  *
  * The engine owns a page manager (qd_blocks) over all num_pages pages of
  * the pool and small device buffers; a request takes every page it can need
@@ -458,14 +458,30 @@ int qd_engine_create(qd_handle* h, void* kv_pool, qd_engine** out);
 /* Waits for the handle's stream, then frees the engine (not the handle or
  * the pool).  NULL is a no-op. */
 void qd_engine_destroy(qd_engine* e);
-/* Queue a request: `req` is the caller's id (unique among unfinished
- * requests), prompt int32 [n_prompt] HOST (copied), n_prompt >= 1, at most
- * max_new_tokens >= 1 tokens to generate, eos_id the token that ends it
- * early (-1: none).  QD_EINVAL on a bad argument or token id;
- * QD_EUNSUPPORTED when n_prompt + max_new_tokens - 1 positions exceed
- * max_pages_per_seq*16 or the whole pool. */
-int qd_engine_submit(qd_engine* e, int64_t req, const int32_t* prompt, int32_t n_prompt,
-                     int32_t max_new_tokens, int32_t eos_id);
+/* A request for qd_engine_submit.  Tokens are greedy (the step's argmax)
+ * when temperature <= 0, else drawn on the device by qd_sample's rule with
+ * temperature, top_k and top_p (the rkmt page, "从零构建 Qwen3-8B 推理引擎",
+ * 4.1.2: temperature and top_p travel with a request); the uniform draw for
+ * the request's k-th generated token (k = 0, 1, ...) is SplitMix64's output
+ * for the state seed + (k + 1) * 0x9E3779B97F4A7C15, its top 24 bits times
+ * 2^-24, so a request's draws do not depend on the requests it is batched
+ * with. */
+typedef struct qd_engine_request {
+  int64_t id;              /* the caller's id, unique among unfinished requests */
+  const int32_t* prompt;   /* HOST int32 [n_prompt], copied */
+  int32_t n_prompt;        /* >= 1 */
+  int32_t max_new_tokens;  /* >= 1 */
+  int32_t eos_id;          /* the token that ends the request early; -1: none */
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  uint64_t seed;
+} qd_engine_request;
+
+/* Queue a request.  QD_EINVAL on a bad argument or token id; QD_EUNSUPPORTED
+ * when n_prompt + max_new_tokens - 1 positions exceed max_pages_per_seq*16
+ * or the whole pool. */
+int qd_engine_submit(qd_engine* e, const qd_engine_request* r);
 /* One iteration (synchronous).  Writes *n_out entries (at most max_batch)
  * to the HOST arrays out_req / out_token / out_done of max_out >= max_batch
  * entries: a request id, its next token, and 1 when that token is its last
@@ -479,6 +495,7 @@ typedef struct qd_engine_stats {
   int64_t cached_rows;    /* prompt positions taken from the prefix cache */
   int64_t decode_rows;    /* sequence positions decoded */
   int64_t tokens_out;     /* tokens returned */
+  int64_t sampled_iterations; /* iterations whose tokens came from qd_sample */
   int32_t waiting;        /* requests not admitted yet */
   int32_t running;        /* admitted requests (prefilling or decoding) */
   int32_t pages_available;

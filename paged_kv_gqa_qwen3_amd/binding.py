@@ -72,10 +72,18 @@ TAP_NAMES = ("x_in", "qkv", "q_rot", "k_rot", "attn", "x_mid", "act", "x_out", "
 _lib = None
 
 
+class QdEngineRequest(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int64), ("prompt", ctypes.c_void_p), ("n_prompt", ctypes.c_int32),
+                ("max_new_tokens", ctypes.c_int32), ("eos_id", ctypes.c_int32),
+                ("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
 class QdEngineStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("prefill_rows", ctypes.c_int64),
                 ("cached_rows", ctypes.c_int64), ("decode_rows", ctypes.c_int64),
-                ("tokens_out", ctypes.c_int64), ("waiting", ctypes.c_int32),
+                ("tokens_out", ctypes.c_int64), ("sampled_iterations", ctypes.c_int64),
+                ("waiting", ctypes.c_int32),
                 ("running", ctypes.c_int32), ("pages_available", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
@@ -133,7 +141,7 @@ def load_library():
             getattr(lib, name).argtypes = args
         lib.qd_blocks_destroy.restype = None
         for name, args in (("qd_engine_create", [P, P, ctypes.POINTER(P)]),
-                           ("qd_engine_submit", [P, I64, P, I32, I32, I32]),
+                           ("qd_engine_submit", [P, ctypes.POINTER(QdEngineRequest)]),
                            ("qd_engine_step", [P, I32, P, P, P, ctypes.POINTER(I32)]),
                            ("qd_engine_get_stats", [P, ctypes.POINTER(QdEngineStats)])):
             getattr(lib, name).restype = ctypes.c_int
@@ -422,10 +430,14 @@ class Engine:
         self._tok = np.empty(max_batch, dtype=np.int32)
         self._done = np.empty(max_batch, dtype=np.int32)
 
-    def submit(self, req: int, prompt, max_new_tokens: int, eos_id: int = -1) -> None:
+    def submit(self, req: int, prompt, max_new_tokens: int, eos_id: int = -1,
+               temperature: float = 0.0, top_k: int = 0, top_p: float = 1.0,
+               seed: int = 0) -> None:
+        """Queue a request (greedy when temperature <= 0; see qd_engine_request)."""
         t = np.ascontiguousarray(prompt, dtype=np.int32)
-        _check(self.lib.qd_engine_submit(self.e, req, t.ctypes.data if len(t) else None, len(t),
-                                         max_new_tokens, eos_id), self.handle)
+        r = QdEngineRequest(req, t.ctypes.data if len(t) else None, len(t), max_new_tokens, eos_id,
+                            temperature, top_k, top_p, seed & (2 ** 64 - 1))
+        _check(self.lib.qd_engine_submit(self.e, ctypes.byref(r)), self.handle)
 
     def step(self):
         n = ctypes.c_int32()

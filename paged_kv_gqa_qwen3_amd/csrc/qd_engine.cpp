@@ -39,6 +39,10 @@ struct Req {
   int32_t n_prompt = 0;
   int32_t max_new = 0;
   int32_t eos = -1;
+  float temperature = 0.f;  // <= 0: greedy
+  int32_t top_k = 0;
+  float top_p = 1.f;
+  uint64_t seed = 0;
   int32_t cached = 0;  // positions whose K/V are in the pool
   int32_t n_gen = 0;
   St st = St::Waiting;
@@ -66,12 +70,18 @@ struct qd_engine {
   qd_engine_stats stats{};
 
   // decode inputs [tokens max_batch][positions max_batch][tables max_batch*mpps],
-  // prompt inputs [tables kMaxSegs*mpps][tokens max_rows], and the next ids
-  // [prompt-ending segments kMaxSegs][decode rows max_batch]; each in device
-  // memory and in a pinned host mirror
+  // prompt inputs [tables kMaxSegs*mpps][tokens max_rows], the next ids
+  // [prompt-ending segments kMaxSegs][decode rows max_batch], and the
+  // sampling rows [temperature | top_k | top_p | uniform | sampled id], 2 *
+  // max_batch each; each in device memory and in a pinned host mirror
   int32_t *d_dec = nullptr, *h_dec = nullptr;
   int32_t *d_pf = nullptr, *h_pf = nullptr;
   int32_t *d_out = nullptr, *h_out = nullptr;
+  int32_t *d_sp = nullptr, *h_sp = nullptr;
+  // logits of an iteration that samples: [2 * max_batch][vocab]; the decode
+  // rows always at rows max_batch.., the n prompt-ending rows just before
+  // them, so that one qd_sample call covers both
+  float* d_logits = nullptr;
 
   // host scratch reused by every iteration
   std::vector<Seg> segs;
@@ -97,16 +107,32 @@ int ehip(qd_engine* e, hipError_t err, const char* what) {
   } while (0)
 
 void free_buffers(qd_engine* e) {
-  for (int32_t* p : {e->d_dec, e->d_pf, e->d_out})
+  for (int32_t* p : {e->d_dec, e->d_pf, e->d_out, e->d_sp})
     if (p) (void)hipFree(p);
-  for (int32_t* p : {e->h_dec, e->h_pf, e->h_out})
+  for (int32_t* p : {e->h_dec, e->h_pf, e->h_out, e->h_sp})
     if (p) (void)hipHostFree(p);
-  e->d_dec = e->d_pf = e->d_out = e->h_dec = e->h_pf = e->h_out = nullptr;
+  if (e->d_logits) (void)hipFree(e->d_logits);
+  e->d_dec = e->d_pf = e->d_out = e->d_sp = nullptr;
+  e->h_dec = e->h_pf = e->h_out = e->h_sp = nullptr;
+  e->d_logits = nullptr;
+}
+
+// The uniform draw for a request's k-th generated token: SplitMix64 (the
+// splittable generator of Steele, Lea and Flood, as Vigna's 64-bit mixer)
+// at state seed + (k + 1) * 0x9E3779B97F4A7C15, its top 24 bits as a float
+// in [0, 1).
+float draw(uint64_t seed, int32_t k) {
+  uint64_t z = seed + (uint64_t)(k + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (float)(z >> 40) * (1.0f / 16777216.0f);
 }
 
 size_t dec_words(const qd_engine* e) { return (size_t)e->max_batch * (2 + e->mpps); }
 size_t pf_words(const qd_engine* e) { return (size_t)kMaxSegs * e->mpps + e->max_rows; }
 size_t out_words(const qd_engine* e) { return (size_t)kMaxSegs + e->max_batch; }
+size_t sp_words(const qd_engine* e) { return (size_t)5 * 2 * e->max_batch; }
 
 // A request leaves: its pages become cache entries for the tokens whose K/V
 // they hold (the prompt and every generated token but the last, which was
@@ -189,10 +215,12 @@ int qd_engine_create(qd_handle* h, void* kv_pool, qd_engine** out) {
     return qd::handle_fail(h, rc, "qd_engine: page manager");
   }
   hipError_t err = hipSuccess;
-  const size_t bytes[3] = {dec_words(e) * 4, pf_words(e) * 4, out_words(e) * 4};
-  int32_t** dev[3] = {&e->d_dec, &e->d_pf, &e->d_out};
-  int32_t** host[3] = {&e->h_dec, &e->h_pf, &e->h_out};
-  for (int i = 0; i < 3 && err == hipSuccess; ++i) {
+  const size_t bytes[4] = {dec_words(e) * 4, pf_words(e) * 4, out_words(e) * 4, sp_words(e) * 4};
+  int32_t** dev[4] = {&e->d_dec, &e->d_pf, &e->d_out, &e->d_sp};
+  int32_t** host[4] = {&e->h_dec, &e->h_pf, &e->h_out, &e->h_sp};
+  if (err == hipSuccess)
+    err = hipMalloc(reinterpret_cast<void**>(&e->d_logits), (size_t)2 * e->max_batch * e->vocab * 4);
+  for (int i = 0; i < 4 && err == hipSuccess; ++i) {
     err = hipMalloc(reinterpret_cast<void**>(dev[i]), bytes[i]);
     if (err == hipSuccess) err = hipHostMalloc(reinterpret_cast<void**>(host[i]), bytes[i], 0);
     if (err == hipSuccess) std::memset(*host[i], 0, bytes[i]);
@@ -218,14 +246,17 @@ void qd_engine_destroy(qd_engine* e) {
   delete e;
 }
 
-int qd_engine_submit(qd_engine* e, int64_t req, const int32_t* prompt, int32_t n_prompt,
-                     int32_t max_new_tokens, int32_t eos_id) {
+int qd_engine_submit(qd_engine* e, const qd_engine_request* rq) {
   if (!e) return QD_EINVAL;
   if (e->broken) return efail(e, QD_ESTATE, "an earlier failure left the engine unusable");
+  if (!rq) return efail(e, QD_EINVAL, "NULL request");
+  const int32_t n_prompt = rq->n_prompt, max_new_tokens = rq->max_new_tokens;
+  const int32_t* prompt = rq->prompt;
   if (!prompt || n_prompt < 1) return efail(e, QD_EINVAL, "empty or NULL prompt");
   if (max_new_tokens < 1) return efail(e, QD_EINVAL, "max_new_tokens must be >= 1");
-  if (eos_id < -1 || eos_id >= e->vocab) return efail(e, QD_EINVAL, "eos_id outside -1..vocab-1");
-  if (e->reqs.count(req)) return efail(e, QD_EINVAL, "request id already in use");
+  if (rq->eos_id < -1 || rq->eos_id >= e->vocab)
+    return efail(e, QD_EINVAL, "eos_id outside -1..vocab-1");
+  if (e->reqs.count(rq->id)) return efail(e, QD_EINVAL, "request id already in use");
   const int64_t span = (int64_t)n_prompt + max_new_tokens - 1;
   if (span > (int64_t)e->mpps * kPageTokens)
     return efail(e, QD_EUNSUPPORTED, "prompt plus max_new_tokens exceed max_pages_per_seq * 16");
@@ -238,9 +269,13 @@ int qd_engine_submit(qd_engine* e, int64_t req, const int32_t* prompt, int32_t n
   r.tokens.reserve((size_t)n_prompt + max_new_tokens);
   r.n_prompt = n_prompt;
   r.max_new = max_new_tokens;
-  r.eos = eos_id;
-  e->reqs.emplace(req, std::move(r));
-  e->waiting.push_back(req);
+  r.eos = rq->eos_id;
+  r.temperature = rq->temperature;
+  r.top_k = rq->top_k;
+  r.top_p = rq->top_p;
+  r.seed = rq->seed;
+  e->reqs.emplace(rq->id, std::move(r));
+  e->waiting.push_back(rq->id);
   return QD_OK;
 }
 
@@ -278,6 +313,16 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
   const int n_end = (int)std::count_if(e->segs.begin(), e->segs.end(), [](const Seg& s) { return s.ends; });
   const int B = (int)e->dec_ids.size();
 
+  // An iteration samples when one of the requests that gets a token here
+  // does (temperature > 0): the steps then also write logits, prompt rows
+  // just before the decode rows, for one qd_sample call over all of them.
+  bool sample = false;
+  for (int s = 0; s < n_end; ++s) sample |= e->reqs[e->segs[s].id].temperature > 0.f;
+  for (int b = 0; b < B; ++b) sample |= e->reqs[e->dec_ids[b]].temperature > 0.f;
+  const int mb = e->max_batch, r0 = mb - n_end;  // first sampled row
+  float* const lg_pf = sample && n_end > 0 ? e->d_logits + (size_t)r0 * e->vocab : nullptr;
+  float* const lg_dec = sample ? e->d_logits + (size_t)mb * e->vocab : nullptr;
+
   const size_t tab = (size_t)kMaxSegs * e->mpps;
   if (n_seg > 0) {
     e->seg_ids.clear();
@@ -301,7 +346,7 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
                               e->stream));
     ENG_HIP(e, hipMemcpyAsync(e->d_pf + tab, tok, (size_t)row * 4, hipMemcpyHostToDevice, e->stream));
     rc = qd_prefill_prompts(e->h, n_seg, e->seg_rows.data(), e->seg_start.data(), e->d_pf + tab,
-                            e->d_pf, e->pool, n_end, n_end ? e->d_out : nullptr, nullptr);
+                            e->d_pf, e->pool, n_end, n_end ? e->d_out : nullptr, lg_pf);
     if (rc) {
       e->broken = true;
       return rc;
@@ -324,18 +369,48 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
     ENG_HIP(e, hipMemcpyAsync(e->d_dec, e->h_dec, ((size_t)2 * e->max_batch + (size_t)B * e->mpps) * 4,
                               hipMemcpyHostToDevice, e->stream));
     rc = qd_decode_step(e->h, B, e->d_dec, e->d_dec + e->max_batch, e->d_dec + 2 * e->max_batch, e->pool,
-                        e->d_out + kMaxSegs, nullptr);
+                        e->d_out + kMaxSegs, lg_dec);
     if (rc) {
       e->broken = true;
       return rc;
     }
     e->stats.decode_rows += B;
   }
-  if (n_end > 0)
-    ENG_HIP(e, hipMemcpyAsync(e->h_out, e->d_out, (size_t)n_end * 4, hipMemcpyDeviceToHost, e->stream));
-  if (B > 0)
-    ENG_HIP(e, hipMemcpyAsync(e->h_out + kMaxSegs, e->d_out + kMaxSegs, (size_t)B * 4,
+  // sampling rows [temperature | top_k | top_p | uniform | id], 2 * max_batch each
+  const int R2 = 2 * mb;
+  float* const sp_t = reinterpret_cast<float*>(e->h_sp);
+  int32_t* const sp_k = e->h_sp + R2;
+  float* const sp_p = reinterpret_cast<float*>(e->h_sp + 2 * R2);
+  float* const sp_u = reinterpret_cast<float*>(e->h_sp + 3 * R2);
+  int32_t* const sp_id = e->h_sp + 4 * R2;
+  if (sample) {
+    auto row = [&](int r, const Req& q) {
+      sp_t[r] = q.temperature;
+      sp_k[r] = q.top_k;
+      sp_p[r] = q.top_p;
+      sp_u[r] = draw(q.seed, q.n_gen);
+    };
+    for (int s = 0; s < n_end; ++s) row(r0 + s, e->reqs[e->segs[s].id]);
+    for (int b = 0; b < B; ++b) row(mb + b, e->reqs[e->dec_ids[b]]);
+    ENG_HIP(e, hipMemcpyAsync(e->d_sp, e->h_sp, (size_t)4 * R2 * 4, hipMemcpyHostToDevice, e->stream));
+    const int32_t* d_sp = e->d_sp;
+    rc = qd_sample(e->h, n_end + B, e->d_logits + (size_t)r0 * e->vocab,
+                   reinterpret_cast<const float*>(d_sp) + r0, d_sp + R2 + r0,
+                   reinterpret_cast<const float*>(d_sp + 2 * R2) + r0,
+                   reinterpret_cast<const float*>(d_sp + 3 * R2) + r0, e->d_sp + 4 * R2 + r0);
+    if (rc) {
+      e->broken = true;
+      return rc;
+    }
+    ENG_HIP(e, hipMemcpyAsync(sp_id + r0, e->d_sp + 4 * R2 + r0, (size_t)(n_end + B) * 4,
                               hipMemcpyDeviceToHost, e->stream));
+  } else {
+    if (n_end > 0)
+      ENG_HIP(e, hipMemcpyAsync(e->h_out, e->d_out, (size_t)n_end * 4, hipMemcpyDeviceToHost, e->stream));
+    if (B > 0)
+      ENG_HIP(e, hipMemcpyAsync(e->h_out + kMaxSegs, e->d_out + kMaxSegs, (size_t)B * 4,
+                                hipMemcpyDeviceToHost, e->stream));
+  }
   int32_t flags = 0;
   rc = qd_device_status(e->h, &flags);  // waits for the stream
   if (rc) {
@@ -367,7 +442,7 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
   for (int b = 0; b < B; ++b) {
     Req& r = e->reqs[e->dec_ids[b]];
     r.cached += 1;
-    emit(e->dec_ids[b], r, e->h_out[kMaxSegs + b]);
+    emit(e->dec_ids[b], r, sample ? sp_id[mb + b] : e->h_out[kMaxSegs + b]);
   }
   for (int s = 0; s < n_seg; ++s) {
     const Seg& sg = e->segs[s];
@@ -375,10 +450,11 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
     r.cached = sg.start + sg.rows;
     if (sg.ends) {
       r.st = St::Decode;
-      emit(sg.id, r, e->h_out[s]);
+      emit(sg.id, r, sample ? sp_id[r0 + s] : e->h_out[s]);
     }
   }
   e->stats.tokens_out += n;
+  if (sample) e->stats.sampled_iterations += 1;
   for (int64_t id : done) {
     rc = retire(e, id);
     if (rc) return rc;

@@ -90,7 +90,7 @@ def test_null_arguments(lib):
     lib.qd_destroy(None)
     e = ctypes.c_void_p()
     assert lib.qd_engine_create(None, None, ctypes.byref(e)) == binding.QD_EINVAL
-    assert lib.qd_engine_submit(None, 0, None, 1, 1, -1) == binding.QD_EINVAL
+    assert lib.qd_engine_submit(None, None) == binding.QD_EINVAL
     n = ctypes.c_int32()
     assert lib.qd_engine_step(None, 64, None, None, None, ctypes.byref(n)) == binding.QD_EINVAL
     assert lib.qd_engine_get_stats(None, None) == binding.QD_EINVAL

@@ -251,3 +251,94 @@ def test_engine_rejects_bad_requests(torch):
     eng.close()
     assert dec.device_status() == 0
     dec.close()
+
+
+def _plain_plan(seed, n=6):
+    """n requests at iteration 0 and 2, prompts of 9..60 tokens, 10 new tokens."""
+    V = SHAPE.vocab
+    reqs = [(100 + i, synth.uniform_int(seed, f"s{i}", V, 9 + 11 * i), 10) for i in range(n)]
+    return reqs
+
+
+def _run_engine(torch, W, reqs, opts, num_pages=64, mpps=8):
+    pool = pool_to_device(np.zeros((SHAPE.num_layers, num_pages, 2, SHAPE.num_kv_heads, PAGE,
+                                    SHAPE.head_dim), dtype=np.uint16))
+    dec = Decoder(SHAPE, 4, mpps, num_pages, max_prefill_rows=64)
+    dec.load_numpy_weights(W)
+    eng = binding.Engine(dec.handle, pool, 4)
+    for i, (rid, prompt, mx) in enumerate(reqs):
+        eng.submit(rid, prompt, mx, **opts(i))
+    streams = {}
+    while True:
+        out = eng.step()
+        for r, t, d in out:
+            streams.setdefault(r, []).append(t)
+        st = eng.stats()
+        if st["waiting"] == 0 and st["running"] == 0:
+            break
+    eng.close()
+    assert dec.device_status() == 0
+    dec.close()
+    return streams, st
+
+
+def test_engine_top1_sampling_equals_greedy(torch):
+    """Requests that sample with top_k = 1 (any temperature) get the greedy
+    streams exactly: the iterations then run qd_sample on the steps' logits
+    instead of taking the steps' argmax, and both pick the lowest index of
+    the largest logit."""
+    W = synth.make_weights(SHAPE, 903)
+    reqs = _plain_plan(903)
+    greedy, st_g = _run_engine(torch, W, reqs, lambda i: {})
+    top1, st_s = _run_engine(torch, W, reqs,
+                             lambda i: dict(temperature=0.7 + 0.1 * i, top_k=1, seed=i))
+    assert st_g["sampled_iterations"] == 0 and st_s["sampled_iterations"] == st_s["steps"]
+    assert top1 == greedy
+
+
+def test_engine_sampling_valid_and_reproducible(torch):
+    """Greedy and sampling requests in one batch (temperature 1, top_k 5;
+    one with top_p 0.9): greedy streams follow the oracle's argmax, every
+    sampled token is among the oracle's 5 largest logits (teacher-forced on
+    the request's own tokens, within the logit tolerance), sampling does not
+    always pick the argmax, and a second run with the same seeds returns the
+    same streams."""
+    W = synth.make_weights(SHAPE, 904)
+    orc = oracle.Oracle(SHAPE, W)
+    reqs = _plain_plan(904)
+
+    def opts(i):
+        if i % 3 == 0:
+            return {}
+        if i == 5:
+            return dict(temperature=1.0, top_p=0.9, seed=1000 + i)
+        return dict(temperature=1.0, top_k=5, seed=1000 + i)
+    s1, st = _run_engine(torch, W, reqs, opts)
+    s2, _ = _run_engine(torch, W, reqs, opts)
+    assert s1 == s2, "the same seeds gave different streams"
+    assert st["sampled_iterations"] > 0
+    batch = synth.make_paged_batch(SHAPE, [0] * len(reqs), 80, 11, fill_kv=False)
+    pool = batch.pool
+    off_argmax = 0
+    for i, (rid, prompt, mx) in enumerate(reqs):
+        got = s1[rid]
+        assert len(got) == mx
+        row = batch.block_tables[i:i + 1]
+        lg, _ = orc.prefill(prompt, row[0], pool)
+        lgs = [lg]
+        for k in range(1, len(got)):
+            l2, _, _ = orc.decode_step(np.array([got[k - 1]], np.int32),
+                                       np.array([len(prompt) + k - 1], np.int32), row, pool)
+            lgs.append(l2[0])
+        for k, (t, l) in enumerate(zip(got, lgs)):
+            if i % 3 == 0:
+                check_next_ids(np.array([t]), l[None], f"greedy request {rid} token {k}")
+                continue
+            tol = 2e-2 * np.abs(l).max()
+            off_argmax += int(t != int(np.argmax(l)))
+            if i != 5:
+                fifth = np.sort(l)[-5]
+                assert l[t] >= fifth - tol, f"request {rid} token {k}: {t} outside the top 5"
+        say(f"request {rid}: {got}")
+    say(f"sampled tokens off the argmax: {off_argmax}")
+    assert off_argmax > 0, "sampling never left the argmax"

@@ -439,25 +439,27 @@ __device__ inline bool merge_amax(const float* val, const int* idx, int n, int B
 
 // ------------------------------------------------------------------ GEMV
 
-// LDS of a GEMV item: s_inv [64] f32 | s_ssq [256] f32 | s_res [64][NB] f32 |
+// LDS of a GEMV item: s_inv [64] f32 | s_ssq [256] f32 | s_res [rows][NB] f32 |
 // flag (16 B) | input slice: VALU fp32 [NB][Ks], MFMA bf16 hi [NB][Ks+8]
-// then lo [NB][Ks+8].
-__host__ __device__ constexpr size_t gemv_head_bytes(int nb) {
-  return 256 + 1024 + (size_t)kRowsPerGroup * nb * 4 + 16;
+// then lo [NB][Ks+8].  rows: 64, or 128 for items of two row tiles per wave.
+__host__ __device__ constexpr size_t gemv_head_bytes(int nb, int rows = kRowsPerGroup) {
+  return 256 + 1024 + (size_t)rows * nb * 4 + 16;
 }
 
-inline size_t gemv_lds_bytes_impl(int B, int kps) {
+inline size_t gemv_lds_bytes_impl(int B, int kps, int rt) {
   const int nb = gemv_nb(B);
   const size_t ks = (size_t)kps * kTileCols;
   const size_t slice = nb >= 8 ? (size_t)nb * (ks + 8) * 2 * 2 : (size_t)nb * ks * 4;
-  return gemv_head_bytes(nb) + slice;
+  return gemv_head_bytes(nb, rt > 4 ? rt * kTileRows : kRowsPerGroup) + slice;
 }
 
 // y[b][n] = sum_k W[n][k] h[b][k], h = x or RMSNorm(x), W packed bf16.
 //
 // One item = rt row tiles (16 rows each) x one K slice of kps tiles.  Wave w
 // works on row tile w % rt of the item and on every (4/rt)-th k-tile of the
-// slice from w / rt on.  It streams its tiles with one 16-byte load per lane
+// slice from w / rt on; with RPW = 2 (rt = 8, MFMA only) on row tiles w and
+// w + 4 and every k-tile, the two tiles of one k-tile in turn, so that each
+// input operand read from LDS feeds both.  It streams its tiles with one 16-byte load per lane
 // per 1 KB tile and CH tiles in flight: the first CH go out before the item
 // waits for its input, and each later one as soon as the registers it lands
 // in are free.
@@ -482,7 +484,7 @@ inline size_t gemv_lds_bytes_impl(int B, int kps) {
 // S > 1 splits of K, each item writes its partial rows and the last of the
 // row group's S items to arrive sums the partials in split order
 // (deterministic) and runs the epilogue.
-template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait>
+template <int NB, int MODE, int CH = kMaxTilesInFlight, class Wait, int RPW = 1>
 __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const float* gain,
                                  const Done& done, int item, unsigned char* smem,
                                  const Wait& wait) {
@@ -499,14 +501,16 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   constexpr bool kSplitCols = NB == 8;  // hi and lo side by side in one operand
   constexpr bool kAgent = Wait::kInLaunch;
   constexpr int NCB = kMfma && !kSplitCols ? NB / 16 : 1;
+  static_assert(RPW == 1 || (RPW == 2 && kMfma && MODE != kArgmax), "two row tiles per wave: MFMA");
+  constexpr int kRows = RPW * kRowsPerGroup;  // most rows of an item
   float* s_inv = reinterpret_cast<float*>(smem);
   float* s_ssq = s_inv + kMaxBatch;
   float* s_res = s_ssq + 256;
-  unsigned* s_flag = reinterpret_cast<unsigned*>(s_res + kRowsPerGroup * NB);
-  unsigned char* xs_base = smem + gemv_head_bytes(NB);
+  unsigned* s_flag = reinterpret_cast<unsigned*>(s_res + kRows * NB);
+  unsigned char* xs_base = smem + gemv_head_bytes(NB, kRows);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int B = a.B, S = a.S, RT = a.rt, WS = 4 / RT;
+  const int B = a.B, S = a.S, RT = RPW == 2 ? 8 : a.rt, WS = RPW == 2 ? 1 : 4 / RT;
   const int rows = RT * kTileRows;
   const int rg = item / S, s = item - rg * S;
   const int KT = a.K / kTileCols;
@@ -514,7 +518,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   const int kt1 = min(KT, kt0 + a.kps);
   const int nk = kt1 - kt0;
   const int Ks = nk * kTileCols;
-  const int tj = wave % RT, kph = wave / RT;  // row tile in the item, K phase
+  const int tj = RPW == 2 ? wave : wave % RT, kph = RPW == 2 ? 0 : wave / RT;  // row tile, K phase
   const int nkw = kph < nk ? (nk - kph + WS - 1) / WS : 0;  // k-tiles of this wave
   const int lastw = nkw > 0 ? nkw - 1 : 0;
   const int kw0 = kt0 + min(kph, nk - 1);  // first k-tile of this wave
@@ -604,8 +608,15 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // to the wave's range) so that the loads stay in flight together; only
   // compute is guarded.  Offsets in 32 bits (a wave's tiles lie within one
   // projection).
+  // wave-local tile i: k-tile i (RPW 1), or k-tile i / 2 of row tile
+  // tj + 4 * (i % 2) (RPW 2); nt tiles in all
   const unsigned wstep = (unsigned)WS * 64u;
-  auto wtile = [&](int i) { return wp + (unsigned)min(i, lastw) * wstep; };
+  const unsigned rstep = 4u * (unsigned)KT * 64u;  // row tile w -> w + 4
+  const int nt = nkw * RPW;
+  auto wtile = [&](int i) {
+    if constexpr (RPW == 2) return wp + (unsigned)(i & 1) * rstep + (unsigned)min(i >> 1, lastw) * wstep;
+    return wp + (unsigned)min(i, lastw) * wstep;
+  };
   u32x4 wbuf[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) wbuf[i] = __builtin_nontemporal_load(wtile(i));
@@ -696,7 +707,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   const float* xsf = reinterpret_cast<const float*>(xs_base);
   struct BIn { u32x4 h[NCB], l[NCB]; f32x4 f0[NB], f1[NB]; };
   auto read_in = [&](int i, BIn& bi) {
-    const int t = kph + WS * i;
+    const int t = kph + WS * (i / RPW);
     if constexpr (kSplitCols) {
       // LDS rows 0..7 hold the hi halves, 8..15 the lo halves: operand
       // column (lane % 16) reads row lane % 16
@@ -745,45 +756,48 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       }
     }
   };
-  // steady state: consume a batch, refill its registers with the tiles CH ahead
+  // steady state: consume a batch, refill its registers with the tiles CH
+  // ahead.  With RPW 2 a batch's tiles alternate between the two row tiles
+  // (accumulator q % 2), and each pair shares one input operand.
+  static_assert(KB % RPW == 0, "a batch holds both row tiles of its k-tiles");
   int c0 = 0;
-  for (; c0 + CH < nkw; c0 += CH) {
+  for (; c0 + CH < nt; c0 += CH) {
 #pragma unroll
     for (int i0 = 0; i0 < CH; i0 += KB) {
-      BIn bi[KB];
+      BIn bi[KB / RPW];
 #pragma unroll
-      for (int q = 0; q < KB; ++q) read_in(c0 + i0 + q, bi[q]);
+      for (int q = 0; q < KB / RPW; ++q) read_in(c0 + i0 + q * RPW, bi[q]);
 #pragma unroll
       for (int q = 0; q < KB; ++q) {
-        mac(wbuf[i0 + q], bi[q], q);
+        mac(wbuf[i0 + q], bi[q / RPW], q);
         wbuf[i0 + q] = __builtin_nontemporal_load(wtile(c0 + CH + i0 + q));
       }
     }
   }
 #pragma unroll
   for (int i0 = 0; i0 < CH; i0 += KB) {
-    if (c0 + i0 >= nkw) break;
-    BIn bi[KB];
+    if (c0 + i0 >= nt) break;
+    BIn bi[KB / RPW];
 #pragma unroll
-    for (int q = 0; q < KB; ++q) read_in(min(c0 + i0 + q, nkw - 1), bi[q]);
+    for (int q = 0; q < KB / RPW; ++q) read_in(min(c0 + i0 + q * RPW, nt - 1), bi[q]);
 #pragma unroll
     for (int q = 0; q < KB; ++q)
-      if (c0 + i0 + q < nkw) mac(wbuf[i0 + q], bi[q], q);
+      if (c0 + i0 + q < nt) mac(wbuf[i0 + q], bi[q / RPW], q);
   }
-  // the batch accumulators, added in a fixed order
+  // the batch accumulators, added in a fixed order (per row tile: q % RPW)
 #pragma unroll
-  for (int q = 1; q < KB; ++q) {
+  for (int q = RPW; q < KB; ++q) {
 #pragma unroll
-    for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[0][b] += acc_v[q][b];
+    for (int b = 0; b < (kMfma ? 1 : NB); ++b) acc_v[q % RPW][b] += acc_v[q][b];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) acc_m[0][c] += acc_m[q][c];
+    for (int c = 0; c < NCB; ++c) acc_m[q % RPW][c] += acc_m[q][c];
   }
 
   // The residual epilogue's old residual and the next consumer's gain
   // (thread: outputs idx = tid + 256 j, idx = b * rows + r), loaded while
   // the waves' results are reduced.  Every split fetches them; only the one
   // that finishes the row group uses them.
-  constexpr int kXold = (kRowsPerGroup * NB + 255) / 256;
+  constexpr int kXold = (kRows * NB + 255) / 256;
   float x_old[kXold], xo_g[kXold];
   if constexpr (MODE == kResid) {
 #pragma unroll
@@ -804,25 +818,30 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   // of s_res hold the item's rows.
   if constexpr (kSplitCols) {
     // column c < 8 (hi) plus its partner c + 8 (lo), lane ^ 8
-    f32x4 tot;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tot[r] = acc_m[0][0][r] + __shfl_xor(acc_m[0][0][r], 8);
-    const int col = lane & 15;
-    if (col < 8) {
-      const float sc = norm && col < B ? s_inv[col] : 1.f;
+    for (int u = 0; u < RPW; ++u) {
+      f32x4 tot;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = tot[r] * sc;
+      for (int r = 0; r < 4; ++r) tot[r] = acc_m[u][0][r] + __shfl_xor(acc_m[u][0][r], 8);
+      const int col = lane & 15;
+      if (col < 8) {
+        const float sc = norm && col < B ? s_inv[col] : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_res[((wave + 4 * u) * 16 + (lane >> 4) * 4 + r) * NB + col] = tot[r] * sc;
+      }
     }
   } else if constexpr (kMfma) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int col = cb * 16 + (lane & 15);
-      const float sc = norm && col < B ? s_inv[col] : 1.f;
+    for (int u = 0; u < RPW; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_res[(wave * 16 + (lane >> 4) * 4 + r) * NB + col] = acc_m[0][cb][r] * sc;
-    }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 16 + (lane & 15);
+        const float sc = norm && col < B ? s_inv[col] : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_res[((wave + 4 * u) * 16 + (lane >> 4) * 4 + r) * NB + col] = acc_m[u][cb][r] * sc;
+      }
   } else {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {

@@ -330,7 +330,8 @@ bool fused_supported(int B);
 hipError_t launch_fused_mlp(const FusedMlpArgs& a, size_t lds, hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for its input slice.
-size_t gemv_lds_bytes(int B, int kps);
+// LDS of a GEMV item of rt row tiles (the head grows with the item's rows)
+size_t gemv_lds_bytes(int B, int kps, int rt);
 
 // ------------------------------------------------------------------ prefill
 // A prompt chunk of M rows on the GEMM path (qd_prefill_prompts).  The chunk

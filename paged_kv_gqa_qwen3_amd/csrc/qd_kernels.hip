@@ -71,10 +71,12 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const
 // Occupancy floor per batch width: four workgroups per CU for the fp32
 // (batch 1) items, three for the MFMA items up to 32 columns (the LDS cap
 // of their input slices allows three), two above.
-template <int NB, int MODE>
+// RPW 2: items of 128 rows, two row tiles per wave (rt = 8).
+template <int NB, int MODE, int RPW = 1>
 __global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  gemv_item<NB, MODE>(a, a.w, a.gain, no_done(), blockIdx.x, smem, NoWait{});
+  gemv_item<NB, MODE, kMaxTilesInFlight, NoWait, RPW>(a, a.w, a.gain, no_done(), blockIdx.x, smem,
+                                                      NoWait{});
 }
 
 
@@ -110,7 +112,7 @@ constexpr int fused_min_blocks(int NB) { return NB == 1 ? 4 : 3; }
 // workgroups that each run their gate/up items and then their down items
 // was measured slower: batch 8, 3.56 against 2.97 ms per step; down's early
 // weight loads slowed gate/up's without shortening the block.)
-template <int NB>
+template <int NB, int RG = 1, int RD = 1>  // row tiles per wave of gate/up and of down items
 __global__ __launch_bounds__(256, fused_min_blocks(NB)) void fused_mlp_kernel(FusedMlpArgs f) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wg = blockIdx.x;
@@ -123,9 +125,9 @@ __global__ __launch_bounds__(256, fused_min_blocks(NB)) void fused_mlp_kernel(Fu
     // rg * rows/2 / 32, in down's K slice (that) / kps
     const int rg = wg / f.gu.S;
     const int sd = (rg * (rows_gu / 2) / kTileCols) / f.d.kps;
-    gemv_item<NB, kSwiGLU>(f.gu, f.gu.w, f.gu.gain,
-                           Done{f.cnt_g + (size_t)sd * kCntStride, 0u, 0u, nullptr, 0}, wg, smem,
-                           NoWait{});
+    gemv_item<NB, kSwiGLU, kMaxTilesInFlight, NoWait, RG>(
+        f.gu, f.gu.w, f.gu.gain, Done{f.cnt_g + (size_t)sd * kCntStride, 0u, 0u, nullptr, 0}, wg,
+        smem, NoWait{});
     return;
   }
   // down item: waits for the gate/up row groups that feed its K slice
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(256, fused_min_blocks(NB)) void fused_mlp_kernel(Fu
   const int KT = f.d.K / kTileCols;
   const int nk = min(KT, (s + 1) * f.d.kps) - s * f.d.kps;
   const unsigned target = (unsigned)(nk * kTileCols / (rows_gu / 2));
-  gemv_item<NB, kResid>(f.d, f.d.w, nullptr, no_done(), item, smem,
-                        CounterWait{f.cnt_g + (size_t)s * kCntStride, 1, target, f.dev_flags,
-                                    f.spin_limit});
+  gemv_item<NB, kResid, kMaxTilesInFlight, CounterWait, RD>(
+      f.d, f.d.w, nullptr, no_done(), item, smem,
+      CounterWait{f.cnt_g + (size_t)s * kCntStride, 1, target, f.dev_flags, f.spin_limit});
 }
 
 // ------------------------------------------------------------------ read ceiling
@@ -185,23 +187,26 @@ bool fused_supported(int B) {
   return nb == 8 || nb == 16;
 }
 
-template <int NB>
+template <int NB, int RG, int RD>
 static hipError_t launch_fused_mlp_t(const FusedMlpArgs& a, size_t lds, hipStream_t s) {
   static bool attr_set = false;
-  const void* fn = reinterpret_cast<const void*>(&fused_mlp_kernel<NB>);
+  const void* fn = reinterpret_cast<const void*>(&fused_mlp_kernel<NB, RG, RD>);
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fused_mlp_kernel<NB>), dim3(a.ng + a.nd), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((fused_mlp_kernel<NB, RG, RD>), dim3(a.ng + a.nd), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_mlp(const FusedMlpArgs& a, size_t lds, hipStream_t s) {
   switch (gemv_nb(a.gu.B)) {
-    case 8: return launch_fused_mlp_t<8>(a, lds, s);
-    case 16: return launch_fused_mlp_t<16>(a, lds, s);
+    case 8: return launch_fused_mlp_t<8, 1, 1>(a, lds, s);
+    case 16:
+      if (a.gu.rt == 8)
+        return a.d.rt == 8 ? launch_fused_mlp_t<16, 2, 2>(a, lds, s) : launch_fused_mlp_t<16, 2, 1>(a, lds, s);
+      return a.d.rt == 8 ? launch_fused_mlp_t<16, 1, 2>(a, lds, s) : launch_fused_mlp_t<16, 1, 1>(a, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -239,18 +244,18 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* ssq, const float* ga
   return hipGetLastError();
 }
 
-template <int NB, int MODE>
+template <int NB, int MODE, int RPW = 1>
 static hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t s) {
   static bool attr_set = false;
-  const size_t lds = gemv_lds_bytes(a.B, a.kps);
+  const size_t lds = gemv_lds_bytes(a.B, a.kps, a.rt);
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<NB, MODE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<NB, MODE, RPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int grid = (a.N / (kTileRows * a.rt)) * a.S;
-  hipLaunchKernelGGL((gemv_kernel<NB, MODE>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemv_kernel<NB, MODE, RPW>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -259,7 +264,10 @@ static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
   switch (gemv_nb(a.B)) {
     case 1: return launch_gemv_t<1, MODE>(a, s);
     case 8: return launch_gemv_t<8, MODE>(a, s);
-    case 16: return launch_gemv_t<16, MODE>(a, s);
+    case 16:
+      if constexpr (MODE != kArgmax)
+        if (a.rt == 8) return launch_gemv_t<16, MODE, 2>(a, s);
+      return launch_gemv_t<16, MODE>(a, s);
     case 32: return launch_gemv_t<32, MODE>(a, s);
     default: return launch_gemv_t<64, MODE>(a, s);
   }
@@ -310,6 +318,6 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, int wave
   return hipErrorInvalidValue;
 }
 
-size_t gemv_lds_bytes(int B, int kps) { return gemv_lds_bytes_impl(B, kps); }
+size_t gemv_lds_bytes(int B, int kps, int rt) { return gemv_lds_bytes_impl(B, kps, rt); }
 
 }  // namespace qd

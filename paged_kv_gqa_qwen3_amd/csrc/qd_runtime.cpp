@@ -203,7 +203,8 @@ constexpr int kMinValuItems = 128;
 // every other step takes the per-stage kernels.
 bool use_stream(const qd_handle* h, int B) { return h->stream_ok && B == 1; }
 
-GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false) {
+GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
+                   bool wide = true) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
   const int nb = gemv_nb(B);
   GemvPlan p;
@@ -215,7 +216,7 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false)
     for (int S = 1; S <= KT; ++S) {
       const int kps = (KT + S - 1) / S;
       const int Se = (KT + kps - 1) / kps;
-      if (gemv_lds_bytes(B, kps) > kLdsCapValu && kps > 1) continue;
+      if (gemv_lds_bytes(B, kps, p.rt) > kLdsCapValu && kps > 1) continue;
       p.S = Se;
       p.kps = kps;
       if (groups * Se >= kMinValuItems) return p;
@@ -227,16 +228,32 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false)
   // the 4B shape: batch 8 3.39 -> 3.19 ms per step against two items per CU
   // and 20-tile slices; batch 16 4.00 -> 3.93)
   const int mtarget = h->num_cus;
-  for (int S = 1; S <= KT; ++S) {
-    const int kps = (KT + S - 1) / S;
-    const int Se = (KT + kps - 1) / kps;
-    if (kps > 16 && NRG < mtarget) continue;
-    if (gemv_lds_bytes(B, kps) > gemv_lds_cap(nb)) continue;
-    p.S = Se;
-    p.kps = kps;
-    if (NRG * Se >= mtarget) return p;
-  }
-  if (p.S == 1 && p.kps == 1 && KT > 1) { p.S = KT; p.kps = 1; }
+  auto search = [&](int rt, int nrg, GemvPlan& q) {
+    q.rt = rt;
+    for (int S = 1; S <= KT; ++S) {
+      const int kps = (KT + S - 1) / S;
+      const int Se = (KT + kps - 1) / kps;
+      if (kps > 16 && nrg < mtarget) continue;
+      if (gemv_lds_bytes(B, kps, rt) > gemv_lds_cap(nb)) continue;
+      q.S = Se;
+      q.kps = kps;
+      if (nrg * Se >= mtarget) return true;
+    }
+    if (q.S == 1 && q.kps == 1 && KT > 1) { q.S = KT; q.kps = 1; }
+    return false;
+  };
+  search(4, NRG, p);
+  // 16 batch columns: an item's input slice is half the size of its
+  // weights, so items of 128 rows (two row tiles per wave, each input
+  // operand read once for both) where they still give every CU two items,
+  // with at most one more K split.  On the 4B shape that is gate/up alone
+  // (760 items instead of 1216: batch 16 3.62 -> 3.51 ms per step); with
+  // one item per CU (down, QKV) the CUs keep too few tiles in flight (3.68).
+  GemvPlan p8;
+  if (nb == 16 && !argmax && wide && N % (2 * kRowsPerGroup) == 0 &&
+      search(8, N / (2 * kRowsPerGroup), p8) && p8.S <= p.S + 1 &&
+      (long long)(N / (2 * kRowsPerGroup)) * p8.S >= 2LL * mtarget)
+    return p8;
   return p;
 }
 
@@ -547,8 +564,12 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   struct Set { float *x, *ssq; uint16_t *hi, *lo; };
   const Set set[2] = {{h->x, h->ssq, h->xg_hi, h->xg_lo}, {h->x_b, h->ssq_b, h->xg_b_hi, h->xg_b_lo}};
   const GemvPlan pq = plan_gemv(h, h->NQKV, H, B), po = plan_gemv(h, H, h->QD, B);
-  const GemvPlan pg = plan_gemv(h, 2 * I, H, B), pd = plan_gemv(h, H, I, B);
-  const size_t lds_m = std::max(gemv_lds_bytes(B, pg.kps), gemv_lds_bytes(B, pd.kps));
+  const GemvPlan pd = plan_gemv(h, H, I, B);
+  // a 128-row gate/up item yields 64 SwiGLU channels, two of down's k-tiles,
+  // which must fall into one down K slice
+  GemvPlan pg = plan_gemv(h, 2 * I, H, B);
+  if (pg.rt == 8 && pd.kps % 2 != 0) pg = plan_gemv(h, 2 * I, H, B, false, false);
+  const size_t lds_m = std::max(gemv_lds_bytes(B, pg.kps, pg.rt), gemv_lds_bytes(B, pd.kps, pd.rt));
   const int ncnt = h->fused_cnt_n / 2;  // counters per set
   unsigned* const cnt_set[2] = {h->fused_cnt, h->fused_cnt + (size_t)ncnt * kCntStride};
 #ifdef QD_STEP_TRACE

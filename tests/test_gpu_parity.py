@@ -257,6 +257,55 @@ def test_tiny_stages(torch, B, ctx):
     _run_stage_checks(torch, shape, W, batch, f"B={B} ctx={ctx}")
 
 
+def _two_layers(base):
+    return synth.ModelShape(base.name + "-2l", 2, base.hidden, base.num_q_heads,
+                            base.num_kv_heads, base.head_dim, base.intermediate, base.vocab,
+                            base.tie_embeddings)
+
+
+WIDE = {"4b": synth.QWEN3_4B, "8b": synth.QWEN3_8B}
+
+
+@pytest.mark.parametrize("model", list(WIDE))
+def test_wide_items_stages(torch, model):
+    """Qwen3-4B and -8B widths (2 layers) at batch 16, stage by stage: at 16
+    batch columns gate/up (both widths) and down (8B) take items of 128 rows
+    (two row tiles per wave, one input operand read for both), which the
+    tiny shapes are too small to use (too few items for the CUs)."""
+    shape = _two_layers(WIDE[model])
+    W = _weights(shape, 5)
+    ctx = [(97 * i) % 600 for i in range(16)]
+    batch = synth.make_paged_batch(shape, ctx, 1, 250)
+    _run_stage_checks(torch, shape, W, batch, f"{shape.name} B=16")
+
+
+@pytest.mark.parametrize("model", list(WIDE))
+def test_wide_items_fused_matches_staged(torch, model):
+    """The same 128-row items inside the fused MLP launch (qd_decode_step,
+    graph) and as per-stage launches (qd_decode_step_taps) at Qwen3-4B and
+    -8B widths, batch 16: the same logits, ids and pool bits.  (The fused
+    launch sizes its LDS for both item kinds; a 64-row size would cut off
+    the end of a 128-row item's input slice.)"""
+    shape = _two_layers(WIDE[model])
+    W = _weights(shape, 5)
+    ctx = [(53 * i) % 500 for i in range(16)]
+    batch = synth.make_paged_batch(shape, ctx, 1, 251)
+    dec = Decoder(shape, 16, batch.max_pages, batch.num_pages, use_graphs=True)
+    dec.load_numpy_weights(W)
+    pf, ps = pool_to_device(batch.pool), pool_to_device(batch.pool)
+    a = StepIO(torch, 16, batch.max_pages, shape.vocab)
+    b = StepIO(torch, 16, batch.max_pages, shape.vocab)
+    for io in (a, b):
+        io.set(batch.tokens, batch.positions, batch.block_tables)
+    a.run(dec, pf)
+    dec.step_taps(b.tok, b.pos, b.tab, ps, b.nxt, b.logits, None, -1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.logits, b.logits) and torch.equal(a.nxt, b.nxt)
+    assert torch.equal(pf, ps)
+    assert dec.device_status() == 0
+    dec.close()
+
+
 # Every (head_dim, query heads per KV head) pair the attention kernel is
 # built for, on small models (2 layers, hidden 256, 2 KV heads), at batch 1
 # (the fp32-input GEMV items) and batch 5 (MFMA items), with one split, a

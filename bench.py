@@ -407,9 +407,10 @@ def time_serving(torch, shape, W, n_req=64, max_batch=16, max_new=128, rows=512,
     max_new greedy tokens each, at most max_batch decoding together and
     `rows` prompt rows per iteration.  Graphs for every batch size are
     captured by a warm-up set of requests first.  Reports wall-clock rates
-    over the whole queue and the median iteration time while the batch is
-    full and no prompt is being prefilled (the engine's host work per
-    iteration shows against the graph replay of the same batch)."""
+    over the whole queue, the median iteration time while the batch is full
+    and no prompt is being prefilled, the GPU time the engine measured (HIP
+    events from each iteration's first launch to its last kernel) and the
+    rest of the wall time per iteration: the engine's host work."""
     from paged_kv_gqa_qwen3_amd.decoder import Decoder
     V = shape.vocab
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -461,6 +462,7 @@ def time_serving(torch, shape, W, n_req=64, max_batch=16, max_new=128, rows=512,
     gen = st["tokens_out"] - st0["tokens_out"]
     n_prompt = int(sum(len(p) for p in prompts))
     full = [dt for dt, b, r in per if b == max_batch and r == 0]
+    gpu_s = (st["gpu_us"] - st0["gpu_us"]) / 1e6
     return {"requests": n_req, "prompt_tokens": n_prompt, "generated_tokens": int(gen),
             "max_batch": max_batch, "prefill_rows_per_iteration": rows,
             "max_new_tokens": max_new, "iterations": len(per), "wall_s": round(wall, 3),
@@ -469,7 +471,9 @@ def time_serving(torch, shape, W, n_req=64, max_batch=16, max_new=128, rows=512,
             "prompt_tokens_from_prefix_cache": int(st["cached_rows"] - st0["cached_rows"]),
             "mean_decode_batch": round(float(np.mean([b for _, b, _ in per])), 2),
             "full_batch_iteration_ms_median": round(1e3 * float(np.median(full)), 4) if full else None,
-            "full_batch_iterations": len(full)}
+            "full_batch_iterations": len(full),
+            "gpu_s": round(gpu_s, 3),
+            "host_us_per_iteration": round(1e6 * (wall - gpu_s) / len(per), 1)}
 
 
 def main():

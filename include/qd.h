@@ -496,6 +496,9 @@ typedef struct qd_engine_stats {
   int64_t decode_rows;    /* sequence positions decoded */
   int64_t tokens_out;     /* tokens returned */
   int64_t sampled_iterations; /* iterations whose tokens came from qd_sample */
+  int64_t gpu_us;         /* summed GPU time of the iterations, from each one's
+                             first launch to its last kernel (HIP events);
+                             the rest of an iteration's wall time is host work */
   int32_t waiting;        /* requests not admitted yet */
   int32_t running;        /* admitted requests (prefilling or decoding) */
   int32_t pages_available;

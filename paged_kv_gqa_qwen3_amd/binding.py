@@ -83,6 +83,7 @@ class QdEngineStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("prefill_rows", ctypes.c_int64),
                 ("cached_rows", ctypes.c_int64), ("decode_rows", ctypes.c_int64),
                 ("tokens_out", ctypes.c_int64), ("sampled_iterations", ctypes.c_int64),
+                ("gpu_us", ctypes.c_int64),
                 ("waiting", ctypes.c_int32),
                 ("running", ctypes.c_int32), ("pages_available", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]

@@ -82,6 +82,8 @@ struct qd_engine {
   // rows always at rows max_batch.., the n prompt-ending rows just before
   // them, so that one qd_sample call covers both
   float* d_logits = nullptr;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;  // an iteration's GPU span
+  double gpu_us = 0.0;
 
   // host scratch reused by every iteration
   std::vector<Seg> segs;
@@ -112,6 +114,9 @@ void free_buffers(qd_engine* e) {
   for (int32_t* p : {e->h_dec, e->h_pf, e->h_out, e->h_sp})
     if (p) (void)hipHostFree(p);
   if (e->d_logits) (void)hipFree(e->d_logits);
+  if (e->ev0) (void)hipEventDestroy(e->ev0);
+  if (e->ev1) (void)hipEventDestroy(e->ev1);
+  e->ev0 = e->ev1 = nullptr;
   e->d_dec = e->d_pf = e->d_out = e->d_sp = nullptr;
   e->h_dec = e->h_pf = e->h_out = e->h_sp = nullptr;
   e->d_logits = nullptr;
@@ -220,6 +225,8 @@ int qd_engine_create(qd_handle* h, void* kv_pool, qd_engine** out) {
   int32_t** host[4] = {&e->h_dec, &e->h_pf, &e->h_out, &e->h_sp};
   if (err == hipSuccess)
     err = hipMalloc(reinterpret_cast<void**>(&e->d_logits), (size_t)2 * e->max_batch * e->vocab * 4);
+  if (err == hipSuccess) err = hipEventCreate(&e->ev0);
+  if (err == hipSuccess) err = hipEventCreate(&e->ev1);
   for (int i = 0; i < 4 && err == hipSuccess; ++i) {
     err = hipMalloc(reinterpret_cast<void**>(dev[i]), bytes[i]);
     if (err == hipSuccess) err = hipHostMalloc(reinterpret_cast<void**>(host[i]), bytes[i], 0);
@@ -324,6 +331,7 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
   float* const lg_dec = sample ? e->d_logits + (size_t)mb * e->vocab : nullptr;
 
   const size_t tab = (size_t)kMaxSegs * e->mpps;
+  ENG_HIP(e, hipEventRecord(e->ev0, e->stream));
   if (n_seg > 0) {
     e->seg_ids.clear();
     e->seg_rows.clear();
@@ -402,9 +410,11 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
       e->broken = true;
       return rc;
     }
+    ENG_HIP(e, hipEventRecord(e->ev1, e->stream));
     ENG_HIP(e, hipMemcpyAsync(sp_id + r0, e->d_sp + 4 * R2 + r0, (size_t)(n_end + B) * 4,
                               hipMemcpyDeviceToHost, e->stream));
   } else {
+    ENG_HIP(e, hipEventRecord(e->ev1, e->stream));
     if (n_end > 0)
       ENG_HIP(e, hipMemcpyAsync(e->h_out, e->d_out, (size_t)n_end * 4, hipMemcpyDeviceToHost, e->stream));
     if (B > 0)
@@ -422,6 +432,11 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
     return efail(e, QD_EHIP, "the kernels reported device status flags " + std::to_string(flags));
   }
   e->stats.steps += 1;
+  {
+    float ms = 0.f;
+    ENG_HIP(e, hipEventElapsedTime(&ms, e->ev0, e->ev1));
+    e->gpu_us += 1e3 * ms;
+  }
 
   // Hand out the tokens: decode rows first, then the first token of every
   // prompt that ended; a request that reached its limit or its
@@ -466,6 +481,7 @@ int qd_engine_step(qd_engine* e, int32_t max_out, int64_t* out_req, int32_t* out
 int qd_engine_get_stats(const qd_engine* e, qd_engine_stats* out) {
   if (!e || !out) return QD_EINVAL;
   *out = e->stats;
+  out->gpu_us = (int64_t)e->gpu_us;
   out->waiting = (int32_t)e->waiting.size();
   out->running = (int32_t)e->active.size();
   out->pages_available = qd_blocks_available(e->blocks);

@@ -501,7 +501,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   constexpr bool kSplitCols = NB == 8;  // hi and lo side by side in one operand
   constexpr bool kAgent = Wait::kInLaunch;
   constexpr int NCB = kMfma && !kSplitCols ? NB / 16 : 1;
-  static_assert(RPW == 1 || (RPW == 2 && kMfma && MODE != kArgmax), "two row tiles per wave: MFMA");
+  static_assert(RPW == 1 || (RPW == 2 && kMfma), "two row tiles per wave: MFMA items");
   constexpr int kRows = RPW * kRowsPerGroup;  // most rows of an item
   float* s_inv = reinterpret_cast<float*>(smem);
   float* s_ssq = s_inv + kMaxBatch;
@@ -961,7 +961,7 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
     mark(7);
     signal_done(done);
-  } else {  // kArgmax, rows == 64
+  } else {  // kArgmax, rows 64 or 128
     if (a.logits != nullptr) {
       for (int idx = tid; idx < rows * B; idx += 256) {
         const int b = idx / rows, r = idx - b * rows;
@@ -969,8 +969,9 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
       }
     }
     for (int b = wave; b < B; b += 4) {
-      float bv = lane < rows ? s_res[lane * NB + b] : -INFINITY;
+      float bv = s_res[lane * NB + b];
       int bi = (int)row0 + lane;
+      if (RPW == 2) amax_merge(bv, bi, s_res[(lane + 64) * NB + b], (int)row0 + lane + 64);
       wave_amax(bv, bi);
       if (lane == 0) {
         st_agent(a.amax_val + (size_t)rg * a.Bmax + b, bv);

@@ -265,8 +265,7 @@ static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
     case 1: return launch_gemv_t<1, MODE>(a, s);
     case 8: return launch_gemv_t<8, MODE>(a, s);
     case 16:
-      if constexpr (MODE != kArgmax)
-        if (a.rt == 8) return launch_gemv_t<16, MODE, 2>(a, s);
+      if (a.rt == 8) return launch_gemv_t<16, MODE, 2>(a, s);
       return launch_gemv_t<16, MODE>(a, s);
     case 32: return launch_gemv_t<32, MODE>(a, s);
     default: return launch_gemv_t<64, MODE>(a, s);

@@ -250,7 +250,7 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
   // (760 items instead of 1216: batch 16 3.62 -> 3.51 ms per step); with
   // one item per CU (down, QKV) the CUs keep too few tiles in flight (3.68).
   GemvPlan p8;
-  if (nb == 16 && !argmax && wide && N % (2 * kRowsPerGroup) == 0 &&
+  if (nb == 16 && wide && N % (2 * kRowsPerGroup) == 0 &&
       search(8, N / (2 * kRowsPerGroup), p8) && p8.S <= p.S + 1 &&
       (long long)(N / (2 * kRowsPerGroup)) * p8.S >= 2LL * mtarget)
     return p8;

@@ -50,7 +50,7 @@ CLASSES = (
     ("embed_kernel", "embed"),
 )
 GEMV_MODES = {"4": "qkv", "2": "gate_up", "3": "lm_head", "1": "o_proj+down", "0": "gemv_store"}
-_GEMV = re.compile(r"gemv_kernel<(\d+), (\d+)>")
+_GEMV = re.compile(r"gemv_kernel<(\d+), (\d+)(?:, \d+)?>")
 
 
 def kernel_class(name: str):

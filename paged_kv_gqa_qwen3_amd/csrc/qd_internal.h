@@ -57,6 +57,18 @@ enum KvMode : int {
   kAttendOnly = 2,    // prefill, second launch: attend over the filled pages
 };
 
+// The weight tiles of the next projection launch, read into the L2 of the
+// XCD that each of its items will run on (workgroup i of a launch runs on
+// XCD i % 8, and the L2 keeps its lines across launches), by n_wg extra
+// workgroups of a launch that leaves HBM mostly idle.  w = null: none.
+struct L2Prefetch {
+  const uint16_t* w;   // the next GEMV launch's packed weights
+  int KT;              // its k-tiles per row tile
+  int rt, S, kps;      // its plan: row tiles per item, K splits, k-tiles per split
+  int items;           // how many of its items, from its first (at most its grid)
+  int n_wg;            // prefetching workgroups here (a multiple of 8)
+};
+
 // One GEMV work item covers rt row tiles (16*rt rows) and one of S slices
 // of K (kps k-tiles); its 4 waves take the row tiles and, when rt < 4,
 // split the item's K slice between them (reduced in LDS).
@@ -88,6 +100,7 @@ struct GemvArgs {
   unsigned* amax_counter;  // kArgmax: ceil(N/64/64) + 1 counters, kCntStride apart
   int* next_ids;       // kArgmax: [B]
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: 8 event timestamps per item, or null
+  L2Prefetch pf;       // (standalone kernel) workgroups after the items prefetch these
 };
 
 struct AttnArgs {
@@ -123,6 +136,7 @@ struct AttnArgs {
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: item event timestamps, or null
   int kv_mode;             // kAppendAttend (decode), or a prefill layer's kAppendOnly then
                            // kAttendOnly launch (standalone kernel only)
+  L2Prefetch pf;           // (standalone kernel) workgroups after the grid's prefetch these
 };
 
 struct EmbedArgs {
@@ -153,6 +167,7 @@ struct FusedMlpArgs {
   int n_other;
   int* dev_flags;
   unsigned spin_limit;
+  L2Prefetch pf;       // workgroups after the items prefetch these
 };
 
 // Per-layer pointers for the streaming step kernel (device-resident array).

@@ -68,22 +68,69 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* x, const
 }
 
 
+// ------------------------------------------------------------------ L2 prefetch
+
+__device__ unsigned g_prefetch_sink;
+
+// Prefetching workgroup j (of p.n_wg, the first at workgroup index first_wg
+// of this launch, so on XCD (first_wg + j) % 8): with the other prefetchers
+// of its XCD it reads the weight tiles of the next launch's items that will
+// run on that XCD (items x, x + 8, ...), with cached loads, so that they sit
+// in that XCD's L2 when the next launch reads them.  The loads are folded
+// into one word, stored only on a match no weights here produce.
+__device__ inline void l2_prefetch(const L2Prefetch& p, int first_wg, int j) {
+  constexpr int kInFlight = 8;
+  const int x = (first_wg + j) % 8, per = p.n_wg / 8, jj = j / 8;
+  const u32x4* const w = reinterpret_cast<const u32x4*>(p.w);
+  const int nt = blockDim.x;
+  unsigned acc = 0;
+  for (int m = jj; x + 8 * m < p.items; m += per) {
+    const int i = x + 8 * m;
+    const int rg = i / p.S, s = i - rg * p.S;
+    const int kt0 = s * p.kps, nk = min(p.KT, kt0 + p.kps) - kt0;
+    if (nk <= 0) continue;
+    const int n = nk * 64, total = p.rt * n;  // 16-byte pieces: per row tile, in the item
+    for (int q0 = threadIdx.x; q0 < total; q0 += nt * kInFlight) {
+      u32x4 v[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const int q = min(q0 + u * nt, total - 1), t = q / n;
+        v[u] = w[((size_t)(rg * p.rt + t) * p.KT + kt0) * 64 + (q - t * n)];
+      }
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  }
+  if (acc == 0x9e3779b9u) g_prefetch_sink = acc;
+}
+
 // Occupancy floor per batch width: four workgroups per CU for the fp32
 // (batch 1) items, three for the MFMA items up to 32 columns (the LDS cap
 // of their input slices allows three), two above.
 // RPW 2: items of 128 rows, two row tiles per wave (rt = 8).
+// Workgroups past the items prefetch the next launch's weights (a.pf).
 template <int NB, int MODE, int RPW = 1>
 __global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  const int items = a.N / (kTileRows * a.rt) * a.S;
+  if ((int)blockIdx.x >= items) {
+    l2_prefetch(a.pf, items, (int)blockIdx.x - items);
+    return;
+  }
   gemv_item<NB, MODE, kMaxTilesInFlight, NoWait, RPW>(a, a.w, a.gain, no_done(), blockIdx.x, smem,
                                                       NoWait{});
 }
 
 
-// The workgroups take the step's attention items round robin.
+// The workgroups take the step's attention items round robin; workgroups
+// past a.grid prefetch the next launch's weights (a.pf).
 template <int D, int G, int NW, int PW, class KV>
 __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x >= a.grid) {
+    l2_prefetch(a.pf, a.grid, (int)blockIdx.x - a.grid);
+    return;
+  }
   const AttnList list = attn_list<NW * PW>(a);
   const int items = attn_items(list, a.B);
 #ifdef QD_STEP_TRACE
@@ -92,7 +139,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
 #else
   const AttnArgs& at = a;
 #endif
-  for (int t = blockIdx.x; t < items; t += gridDim.x)
+  for (int t = blockIdx.x; t < items; t += a.grid)
     attention_item<D, G, NW, PW, NoWait, KV>(
         at, list, a.q_gain, a.k_gain, reinterpret_cast<typename KV::Elem*>(a.pool_layer),
         no_done(), t, smem, NoWait{});
@@ -116,6 +163,10 @@ template <int NB, int RG = 1, int RD = 1>  // row tiles per wave of gate/up and 
 __global__ __launch_bounds__(256, fused_min_blocks(NB)) void fused_mlp_kernel(FusedMlpArgs f) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wg = blockIdx.x;
+  if (wg >= f.ng + f.nd) {
+    l2_prefetch(f.pf, f.ng + f.nd, wg - f.ng - f.nd);
+    return;
+  }
   if (wg == 0)  // the next launch's counters
     for (int i = threadIdx.x; i < f.n_other; i += blockDim.x)
       st_agent(f.cnt_other + (size_t)i * kCntStride, 0u);
@@ -196,7 +247,8 @@ static hipError_t launch_fused_mlp_t(const FusedMlpArgs& a, size_t lds, hipStrea
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fused_mlp_kernel<NB, RG, RD>), dim3(a.ng + a.nd), dim3(256), lds, s, a);
+  const int pf = a.pf.w != nullptr ? a.pf.n_wg : 0;
+  hipLaunchKernelGGL((fused_mlp_kernel<NB, RG, RD>), dim3(a.ng + a.nd + pf), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -254,7 +306,7 @@ static hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = (a.N / (kTileRows * a.rt)) * a.S;
+  const int grid = (a.N / (kTileRows * a.rt)) * a.S + (a.pf.w != nullptr ? a.pf.n_wg : 0);
   hipLaunchKernelGGL((gemv_kernel<NB, MODE, RPW>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
@@ -284,7 +336,8 @@ hipError_t launch_gemv(const GemvArgs& a, int mode, hipStream_t s) {
 
 template <int D, int G, int NW, int PW, class KV>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KV>), dim3(a.grid), dim3(NW * 64),
+  const int pf = a.pf.w != nullptr ? a.pf.n_wg : 0;
+  hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KV>), dim3(a.grid + pf), dim3(NW * 64),
                      sizeof(AttnSmem<D, G, NW>), s, a);
   return hipGetLastError();
 }

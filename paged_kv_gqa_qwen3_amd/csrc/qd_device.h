@@ -1011,20 +1011,23 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
 // LDS of an attention item with NW waves.  part (partial q.k sums of the
 // page being scored) and acc (the waves' outputs, for the final merge) are
 // never live at the same time.
-template <int D, int G, int NW>
+template <int D, int G, int NW, int PW = 1>
 struct AttnSmem {
   static constexpr int LPT = D / 8;       // lanes per token row in one 1 KB load
   static constexpr int TPI = 64 / LPT;    // tokens per load
   static constexpr int NI = kPage / TPI;  // loads per 16-token tile
   static constexpr int NV = NI * G;       // partial scores per lane per page
   static constexpr int ACC = G * 8 + 1;  // per-lane accumulators, padded against bank conflicts
+  // the softmax weights of a wave's PW pages go into its partials' space
+  // when that holds them, else here
+  static constexpr int PX = PW > NV ? PW : 1;
   union {
     float part[NW][NV][64];
     float acc[NW][64][ACC];  // every lane's G x 8 output partials
     float ml[2][G][kMaxSplitsStaged];  // combine: (max, sum) of the splits
   };
   alignas(16) float q[G][D];
-  float p[NW][64];
+  float p[NW][PX][64];
   float m[NW][G], l[NW][G];
   float wsc[NW][G];        // per-wave rescale factors of the merge
   float mx[G], lsum[G];    // per head: overall max and sum of the item (or of all splits)
@@ -1100,7 +1103,7 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
                                       typename KV::Elem* pool_layer, const Done& done, int item,
                                       unsigned char* smem, const Wait& wait) {
   using Raw = typename KV::Raw;
-  using SM = AttnSmem<D, G, NW>;
+  using SM = AttnSmem<D, G, NW, PW>;
   constexpr bool kAgent = Wait::kInLaunch;
 #ifdef QD_STEP_TRACE
   auto mark = [&](int e) {
@@ -1300,10 +1303,16 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
   const Raw kcur = KV::from_slots(&sm.k[dch * 8]);
   const Raw vcur = KV::from_slots(&sm.v[dch * 8]);
 
+  // The wave's PW pages are scored first, then one online-softmax update
+  // covers all of them (one max and one sum across the lanes instead of one
+  // per page), then the values.  Pages past the context were loaded, not
+  // used (wave-uniform).
+  float sc[PW];  // lane u < 16G: score of (token u/G, head u%G) of page j
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
     const int pg = pg0 + wave + NW * j;
-    if (pg >= npages) break;  // wave-uniform (pages past the context were loaded, not used)
+    sc[j] = -INFINITY;
+    if (pg >= npages) continue;
     // partial q.k over this lane's 8 dims, for its NI tokens and G heads
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -1327,7 +1336,8 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
     }
     __builtin_amdgcn_wave_barrier();
     // lane u < 16G owns score (token u/G, head u%G): sum the LPT partials
-    float sc = -INFINITY;
+    // (the wave's LDS operations run in order, so the next page's partials
+    // are written after these reads)
     if (lane < 16 * G) {
       const int t = lane / G, h = lane % G;
       const float* src = &sm.part[wave][(t / TPI) * G + h][(t % TPI) * LPT];
@@ -1337,27 +1347,40 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
         const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + jj);
         sum += v4.x; sum += v4.y; sum += v4.z; sum += v4.w;
       }
-      if (pg * kPage + t < ctx) sc = sum;
+      if (pg * kPage + t < ctx) sc[j] = sum;
     }
-    float mx = sc;
+  }
+  float mx = sc[0];
 #pragma unroll
-    for (int m = G; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const float m_new = fmaxf(m_run, mx);
-    const float p = (sc == -INFINITY) ? 0.f : expf(sc - m_new);
-    const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-    float psum = p;
+  for (int j = 1; j < PW; ++j) mx = fmaxf(mx, sc[j]);
 #pragma unroll
-    for (int m = G; m < 64; m <<= 1) psum += __shfl_xor(psum, m);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    sm.p[wave][lane] = p;
-    __builtin_amdgcn_wave_barrier();
+  for (int m = G; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  const float m_new = fmaxf(m_run, mx);
+  float pj[PW], psum = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = __shfl(alpha, h);
+  for (int j = 0; j < PW; ++j) {
+    pj[j] = (sc[j] == -INFINITY) ? 0.f : expf(sc[j] - m_new);
+    psum += pj[j];
+  }
+  const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-    }
+  for (int m = G; m < 64; m <<= 1) psum += __shfl_xor(psum, m);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  // the weights of every page, in the partials' space (free now) if it holds them
+  float* const pw = PW <= SM::NV ? &sm.part[wave][0][0] : &sm.p[wave][0][0];
+#pragma unroll
+  for (int j = 0; j < PW; ++j) pw[j * 64 + lane] = pj[j];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float al = __shfl(alpha, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+  }
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    if (pg0 + wave + NW * j >= npages) break;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = i * TPI + lane / LPT;
@@ -1365,13 +1388,13 @@ __device__ inline void attention_item(const AttnArgs& a, const AttnList& list,
       KV::unpack(vr[j][i], vf, a.v_scale);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pv = sm.p[wave][t * G + h];
+        const float pv = pw[j * 64 + t * G + h];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
+  __builtin_amdgcn_wave_barrier();
 
   mark(3);
   // --- merge the waves (and the TPI token groups inside each) through LDS:

@@ -258,16 +258,18 @@ constexpr bool gemv_mfma(int B) { return gemv_nb(B) >= 8; }
 constexpr int kAttnWaves = 8;
 constexpr int kAttnWavesPersistent = 4;
 constexpr int kAttnPagesPersistent = 1;
-// Handles of at least this many pages per sequence (and at most
-// kStreamMaxPages) give batches up to 8 two pages per wave: contexts that
-// long have splits to spare, and half as many to combine (Qwen3-8B, batch
-// 8, contexts 580-1841: 5.12 -> 4.92 ms per step); shorter handles keep one
-// page per wave, so that short contexts spread over more workgroups (batch
-// 8, context 256: 2.95 against 3.04 ms with two).
+// Handles of at least this many pages per sequence give batches up to 8
+// three pages per wave too: contexts that long have splits to spare, and a
+// third as many to combine (Qwen3-8B, batch 8, contexts 580-1841: 4.92 ms
+// per step with one page, 4.74 with two, 4.43 with three, a wave's pages
+// scored before one softmax update); shorter handles keep one page per
+// wave, so that short contexts spread over more workgroups (batch 8,
+// context 256: 2.83 ms against 2.87 with three and 2.92 with two).  Four
+// pages spill registers at head dim 128 (batch 1 at 8K: 2.90 against 2.81).
 constexpr int kMidCtxPages = 64;
 constexpr int attn_pages_per_wave(int B, bool persistent, bool long_ctx = false,
                                   bool mid_ctx = false) {
-  return persistent ? kAttnPagesPersistent : B <= 8 && !long_ctx ? (mid_ctx ? 2 : 1) : 3;
+  return persistent ? kAttnPagesPersistent : B <= 8 && !long_ctx && !mid_ctx ? 1 : 3;
 }
 constexpr int attn_pages_per_split(int B, bool persistent, bool long_ctx = false,
                                    bool mid_ctx = false) {

@@ -338,7 +338,7 @@ template <int D, int G, int NW, int PW, class KV>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t s) {
   const int pf = a.pf.w != nullptr ? a.pf.n_wg : 0;
   hipLaunchKernelGGL((attention_kernel<D, G, NW, PW, KV>), dim3(a.grid + pf), dim3(NW * 64),
-                     sizeof(AttnSmem<D, G, NW>), s, a);
+                     sizeof(AttnSmem<D, G, NW, PW>), s, a);
   return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ struct qd_handle {
   // batch-1 streaming step (persistent handles)
   bool persistent = false;
   bool long_ctx = false;  // max_pages_per_seq > kStreamMaxPages: batch 1 takes the per-stage kernels
-  bool mid_ctx = false;   // max_pages_per_seq >= kMidCtxPages: 2 attention pages per wave up to batch 8
+  bool mid_ctx = false;   // max_pages_per_seq >= kMidCtxPages: 3 attention pages per wave up to batch 8
   LayerDev* layers_dev = nullptr;
   unsigned* step_cnt = nullptr;
   unsigned* step_flags = nullptr;  // [2 * CUs][32]

@@ -309,7 +309,7 @@ struct StreamMisc {
 template <int D, int G>
 constexpr size_t stream_in_bytes_t(int in_floats) {
   const size_t x = (size_t)in_floats * 4;
-  const size_t att = sizeof(AttnSmem<D, G, kAttnWavesPersistent>);
+  const size_t att = sizeof(AttnSmem<D, G, kAttnWavesPersistent, attn_pages_per_wave(1, true)>);
   return ((x > att ? x : att) + 15) / 16 * 16;
 }
 

@@ -453,6 +453,166 @@ inline size_t gemv_lds_bytes_impl(int B, int kps, int rt) {
   return gemv_head_bytes(nb, rt > 4 ? rt * kTileRows : kRowsPerGroup) + slice;
 }
 
+// The end of a GEMV item once rows 0..rows-1 of s_res ([rows][NB]) hold its
+// results (times 1/rms under RMSNorm): the split partials (the last split of
+// a row group to arrive sums them in split order), then the epilogue.
+// x_old / xo_g: a residual epilogue's old residual and the next consumer's
+// gain for outputs idx = tid + 256 j (idx = b * rows + r), loaded by the
+// caller while its results were reduced.  Argmax items have 64 or more rows.
+template <int NB, int MODE, int kRows, class Mark>
+__device__ inline void gemv_finish(const GemvArgs& a, const Done& done, int rg, int s, int rows,
+                                   float* s_res, unsigned* s_flag,
+                                   const float (&x_old)[(kRows * NB + 255) / 256],
+                                   const float (&xo_g)[(kRows * NB + 255) / 256],
+                                   const Mark& mark) {
+  constexpr int kXold = (kRows * NB + 255) / 256;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int B = a.B, S = a.S;
+  if constexpr (MODE == kPartial) {
+    // leave the partial for the consumer, which sums the S splits itself
+    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int r = idx / B, b = idx - r * B;
+      st_agent(mine + idx, s_res[r * NB + b]);
+    }
+    mark(7);
+    signal_done(done);
+    return;
+  }
+  if (S > 1) {
+    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int r = idx / B, b = idx - r * B;
+      st_agent(mine + idx, s_res[r * NB + b]);
+    }
+    if (!arrive_last(&a.counters[(size_t)rg * kCntStride], (unsigned)S, s_flag)) return;
+    mark(5);
+    // sum the S partials of each output in split order; a thread keeps 4
+    // outputs x 8 splits of loads in flight (indices clamped, extras unused)
+    const float* all = a.part + (size_t)rg * S * rows * B;
+    const int n = rows * B;
+    constexpr int J = 4;
+    for (int i0 = tid; i0 < n; i0 += 256 * J) {
+      float acc[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) acc[j] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float v[J][8];
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            v[j][k] = ld_agent(all + (size_t)min(s0 + k, S - 1) * n + min(i0 + j * 256, n - 1));
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (s0 + k < S) acc[j] += v[j][k];
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int idx = i0 + j * 256;
+        if (idx < n) s_res[(idx / B) * NB + idx % B] = acc[j];
+      }
+    }
+    if (tid == 0) reset_counter(&a.counters[(size_t)rg * kCntStride]);
+    __syncthreads();
+    mark(6);
+  }
+
+  const int N = a.N;
+  const size_t row0 = (size_t)rg * rows;
+  if constexpr (MODE == kStore) {
+    for (int idx = tid; idx < rows * B; idx += 256) {
+      const int b = idx / rows, r = idx - b * rows;
+      st_agent(a.out + (size_t)b * N + row0 + r, s_res[r * NB + b]);
+    }
+    mark(7);
+    signal_done(done);
+  } else if constexpr (MODE == kResid) {
+    // new residual, its sums of squares over groups of 16 rows (a group of
+    // 16 lanes never spans two batch columns), and for an MFMA consumer the
+    // bf16 pair of x times the consumer's RMSNorm gain
+#pragma unroll
+    for (int j = 0; j < kXold; ++j) {
+      const int idx = tid + j * 256;  // = b * rows + r
+      const bool ok = idx < rows * B;
+      const int b = idx / rows, r = idx - b * rows;
+      float xv = 0.f;
+      if (ok) {
+        xv = x_old[j] + s_res[r * NB + b];
+        st_agent(a.out + (size_t)b * N + row0 + r, xv);
+        if (a.xo_hi != nullptr)
+          split_hilo(xv * xo_g[j], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
+      }
+      const float ss = group_sum(xv * xv, kSsqRows);
+      if (ok && r % kSsqRows == 0)
+        st_agent(a.ssq_out + ((row0 + r) / kSsqRows) * a.Bmax + b, ss);
+    }
+    mark(7);
+    signal_done(done);
+  } else if constexpr (MODE == kSwiGLU) {
+    // row tile j of the item: gate rows 0-7, the matching up rows 8-15
+    const int half = N / 2, nch = rows / 2;
+    for (int idx = tid; idx < nch * B; idx += 256) {
+      const int b = idx / nch, c = idx - b * nch;
+      const int j = c / 8, i = c % 8;
+      const float gv = s_res[(j * 16 + i) * NB + b];
+      const float uv = s_res[(j * 16 + 8 + i) * NB + b];
+      const float sv = gv / (1.f + expf(-gv));
+      const size_t o = (size_t)b * half + (size_t)rg * nch + c;
+      st_agent(a.out + o, sv * uv);
+      if (a.xo_hi != nullptr) split_hilo(sv * uv, a.xo_hi, a.xo_lo, o);
+    }
+    mark(7);
+    signal_done(done);
+  } else {  // kArgmax, rows 64 or 128
+    if (a.logits != nullptr) {
+      for (int idx = tid; idx < rows * B; idx += 256) {
+        const int b = idx / rows, r = idx - b * rows;
+        a.logits[(size_t)b * N + row0 + r] = s_res[r * NB + b];
+      }
+    }
+    for (int b = wave; b < B; b += 4) {
+      float bv = s_res[lane * NB + b];
+      int bi = (int)row0 + lane;
+#pragma unroll
+      for (int u = 1; u < kRows / 64; ++u)  // (argmax items: rows == kRows)
+        amax_merge(bv, bi, s_res[(lane + 64 * u) * NB + b], (int)row0 + lane + 64 * u);
+      wave_amax(bv, bi);
+      if (lane == 0) {
+        st_agent(a.amax_val + (size_t)rg * a.Bmax + b, bv);
+        st_agent(a.amax_idx + (size_t)rg * a.Bmax + b, bi);
+      }
+    }
+    // two levels of "last to arrive": groups of 64 row groups, then the
+    // groups (no single counter takes every row group's atomic)
+    const int NRG = N / rows, gq = rg / 64, ng2 = (NRG + 63) / 64;
+    const int in_group = min(64, NRG - gq * 64);
+    unsigned* cnt1 = a.amax_counter + (size_t)gq * kCntStride;
+    if (!arrive_last(cnt1, (unsigned)in_group, s_flag)) return;
+    {
+      float bv;
+      int bi, b;
+      if (merge_amax(a.amax_val + (size_t)gq * 64 * a.Bmax, a.amax_idx + (size_t)gq * 64 * a.Bmax,
+                     in_group, B, a.Bmax, s_res, bv, bi, b)) {
+        st_agent(a.amax_val2 + (size_t)gq * a.Bmax + b, bv);
+        st_agent(a.amax_idx2 + (size_t)gq * a.Bmax + b, bi);
+      }
+    }
+    if (tid == 0) reset_counter(cnt1);
+    unsigned* cnt2 = a.amax_counter + (size_t)ng2 * kCntStride;
+    if (!arrive_last(cnt2, (unsigned)ng2, s_flag)) return;
+    {
+      float bv;
+      int bi, b;
+      if (merge_amax(a.amax_val2, a.amax_idx2, ng2, B, a.Bmax, s_res, bv, bi, b))
+        a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
+    }
+    if (tid == 0) reset_counter(cnt2);
+  }
+}
+
 // y[b][n] = sum_k W[n][k] h[b][k], h = x or RMSNorm(x), W packed bf16.
 //
 // One item = rt row tiles (16 rows each) x one K slice of kps tiles.  Wave w
@@ -863,147 +1023,315 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
   }
   mark(4);
 
-  if constexpr (MODE == kPartial) {
-    // leave the partial for the consumer, which sums the S splits itself
-    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
-    for (int idx = tid; idx < rows * B; idx += 256) {
-      const int r = idx / B, b = idx - r * B;
-      st_agent(mine + idx, s_res[r * NB + b]);
-    }
-    mark(7);
-    signal_done(done);
-    return;
-  }
-  if (S > 1) {
-    float* mine = a.part + (size_t)(rg * S + s) * rows * B;
-    for (int idx = tid; idx < rows * B; idx += 256) {
-      const int r = idx / B, b = idx - r * B;
-      st_agent(mine + idx, s_res[r * NB + b]);
-    }
-    if (!arrive_last(&a.counters[(size_t)rg * kCntStride], (unsigned)S, s_flag)) return;
-    mark(5);
-    // sum the S partials of each output in split order; a thread keeps 4
-    // outputs x 8 splits of loads in flight (indices clamped, extras unused)
-    const float* all = a.part + (size_t)rg * S * rows * B;
-    const int n = rows * B;
-    constexpr int J = 4;
-    for (int i0 = tid; i0 < n; i0 += 256 * J) {
-      float acc[J];
-#pragma unroll
-      for (int j = 0; j < J; ++j) acc[j] = 0.f;
-      for (int s0 = 0; s0 < S; s0 += 8) {
-        float v[J][8];
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            v[j][k] = ld_agent(all + (size_t)min(s0 + k, S - 1) * n + min(i0 + j * 256, n - 1));
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (s0 + k < S) acc[j] += v[j][k];
-      }
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int idx = i0 + j * 256;
-        if (idx < n) s_res[(idx / B) * NB + idx % B] = acc[j];
-      }
-    }
-    if (tid == 0) reset_counter(&a.counters[(size_t)rg * kCntStride]);
-    __syncthreads();
-    mark(6);
-  }
+  gemv_finish<NB, MODE, kRows>(a, done, rg, s, rows, s_res, s_flag, x_old, xo_g, mark);
+}
 
-  const int N = a.N;
-  const size_t row0 = (size_t)rg * rows;
-  if constexpr (MODE == kStore) {
-    for (int idx = tid; idx < rows * B; idx += 256) {
-      const int b = idx / rows, r = idx - b * rows;
-      st_agent(a.out + (size_t)b * N + row0 + r, s_res[r * NB + b]);
-    }
-    mark(7);
-    signal_done(done);
-  } else if constexpr (MODE == kResid) {
-    // new residual, its sums of squares over groups of 16 rows (a group of
-    // 16 lanes never spans two batch columns), and for an MFMA consumer the
-    // bf16 pair of x times the consumer's RMSNorm gain
+// ------------------------------------------------------------------ GEMV, 32 and 64 columns
+
+// At 32 and 64 batch columns an item's input (the bf16 pair of every
+// column) is as large per k-tile as 32 or 64 weight rows, so staging a whole
+// K slice in LDS caps the slice at a few k-tiles, and the split partials
+// (S x N x B floats, written and read back) then outweigh the weights.  These
+// items stream their input slice through LDS in chunks of kWideChunk k-tiles
+// instead, in two buffers (the next chunk loads while the current one is
+// consumed), so that K is split only to give every CU work; and each wave
+// owns RW row tiles (w, w + 4, ...), so that each input operand it reads
+// from LDS feeds RW MFMA pairs.  Weight tiles stream one chunk ahead in
+// registers.
+constexpr int kWideChunk = 4;
+constexpr size_t kWideHead = (size_t)(kMaxBatch + 256) * 4 + 16;  // s_inv, s_ssq, flag
+__host__ __device__ constexpr size_t gemv_wide_lds_bytes(int nb, int rw) {
+  // s_res [rows][nb] f32 shares the space of the two input buffers
+  // [hi | lo][nb][kWideChunk * 32 + 8] bf16
+  return kWideHead + ((size_t)rw * kRowsPerGroup * nb * 4 > (size_t)2 * 2 * nb * (kWideChunk * kTileCols + 8) * 2
+                          ? (size_t)rw * kRowsPerGroup * nb * 4
+                          : (size_t)2 * 2 * nb * (kWideChunk * kTileCols + 8) * 2);
+}
+
+// The end of a 32- or 64-column item of a row group split S > 1 ways
+// (kStore, kResid, kSwiGLU).  At these widths a row group's partials are
+// large (S x rows x B floats), so instead of the last split summing all of
+// them, every split writes its partial, waits until all S have (the items
+// of a row group are consecutive workgroups, dispatched in order, so a
+// waiting split only waits for running or dispatched ones; bounded), then
+// sums its 1/S share of the outputs over the S partials in split order and
+// runs the epilogue on that share.  Shares are whole units of 16 outputs
+// (16 rows of one batch column: an RMSNorm sum-of-squares group, or a
+// gate/up row tile).  Partials are laid out [split][B][rows].
+constexpr unsigned kWideSpin = 1u << 22;
+template <int NB, int MODE, int kRows, class Mark>
+__device__ inline void gemv_finish_coop(const GemvArgs& a, int rg, int s, const float* s_res,
+                                        const Mark& mark) {
+  static_assert(MODE == kStore || MODE == kResid || MODE == kSwiGLU, "splittable epilogues");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = a.B, S = a.S, N = a.N, n = kRows * B;
+  float* mine = a.part + (size_t)(rg * S + s) * n;
+  for (int idx = tid; idx < n; idx += 256) {
+    const int b = idx / kRows, r = idx - b * kRows;
+    st_agent(mine + idx, s_res[r * NB + b]);
+  }
+  stores_done();
+  __syncthreads();
+  unsigned* cnt = &a.counters[(size_t)rg * kCntStride];
+  if (tid == 0) {
+    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    poll_counter(cnt, (unsigned)S, a.dev_flags, kWideSpin);
+  }
+  __syncthreads();
+  mark(5);
+  const int units = n / 16;
+  const int lo = 16 * (int)((long long)units * s / S), hi = 16 * (int)((long long)units * (s + 1) / S);
+  const float* all = a.part + (size_t)rg * S * n;
+  const size_t row0 = (size_t)rg * kRows;
+  for (int base = lo; base < hi; base += 256) {
+    const int idx = base + tid;
+    const bool ok = idx < hi;
+    const int ic = ok ? idx : lo;
+    const int b = ic / kRows, r = ic - b * kRows;
+    // the S partials of this output, in split order, 8 loads in flight
+    float v = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float t[8];
 #pragma unroll
-    for (int j = 0; j < kXold; ++j) {
-      const int idx = tid + j * 256;  // = b * rows + r
-      const bool ok = idx < rows * B;
-      const int b = idx / rows, r = idx - b * rows;
+      for (int k = 0; k < 8; ++k) t[k] = ld_agent(all + (size_t)min(s0 + k, S - 1) * n + ic);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < S) v += t[k];
+    }
+    if constexpr (MODE == kStore) {
+      if (ok) st_agent(a.out + (size_t)b * N + row0 + r, v);
+    } else if constexpr (MODE == kResid) {
       float xv = 0.f;
       if (ok) {
-        xv = x_old[j] + s_res[r * NB + b];
+        xv = (a.res_in != nullptr ? a.res_in : a.out)[(size_t)b * N + row0 + r] + v;
         st_agent(a.out + (size_t)b * N + row0 + r, xv);
         if (a.xo_hi != nullptr)
-          split_hilo(xv * xo_g[j], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
+          split_hilo(xv * a.xo_gain[row0 + r], a.xo_hi, a.xo_lo, (size_t)b * N + row0 + r);
       }
       const float ss = group_sum(xv * xv, kSsqRows);
-      if (ok && r % kSsqRows == 0)
-        st_agent(a.ssq_out + ((row0 + r) / kSsqRows) * a.Bmax + b, ss);
-    }
-    mark(7);
-    signal_done(done);
-  } else if constexpr (MODE == kSwiGLU) {
-    // row tile j of the item: gate rows 0-7, the matching up rows 8-15
-    const int half = N / 2, nch = RT * 8;
-    for (int idx = tid; idx < nch * B; idx += 256) {
-      const int b = idx / nch, c = idx - b * nch;
-      const int j = c / 8, i = c % 8;
-      const float gv = s_res[(j * 16 + i) * NB + b];
-      const float uv = s_res[(j * 16 + 8 + i) * NB + b];
-      const float sv = gv / (1.f + expf(-gv));
-      const size_t o = (size_t)b * half + (size_t)rg * nch + c;
-      st_agent(a.out + o, sv * uv);
-      if (a.xo_hi != nullptr) split_hilo(sv * uv, a.xo_hi, a.xo_lo, o);
-    }
-    mark(7);
-    signal_done(done);
-  } else {  // kArgmax, rows 64 or 128
-    if (a.logits != nullptr) {
-      for (int idx = tid; idx < rows * B; idx += 256) {
-        const int b = idx / rows, r = idx - b * rows;
-        a.logits[(size_t)b * N + row0 + r] = s_res[r * NB + b];
+      if (ok && r % kSsqRows == 0) st_agent(a.ssq_out + ((row0 + r) / kSsqRows) * a.Bmax + b, ss);
+    } else {  // kSwiGLU: rows 0-7 of a 16-row unit are gate channels, 8-15 the matching up ones
+      const float uv = __shfl(v, (lane & ~15) + 8 + (lane & 7));
+      if (ok && (r & 15) < 8) {
+        const int c = (r >> 4) * 8 + (r & 7);
+        const float sv = v / (1.f + expf(-v));
+        const size_t o = (size_t)b * (N / 2) + (size_t)rg * (kRows / 2) + c;
+        st_agent(a.out + o, sv * uv);
+        if (a.xo_hi != nullptr) split_hilo(sv * uv, a.xo_hi, a.xo_lo, o);
       }
     }
-    for (int b = wave; b < B; b += 4) {
-      float bv = s_res[lane * NB + b];
-      int bi = (int)row0 + lane;
-      if (RPW == 2) amax_merge(bv, bi, s_res[(lane + 64) * NB + b], (int)row0 + lane + 64);
-      wave_amax(bv, bi);
-      if (lane == 0) {
-        st_agent(a.amax_val + (size_t)rg * a.Bmax + b, bv);
-        st_agent(a.amax_idx + (size_t)rg * a.Bmax + b, bi);
-      }
-    }
-    // two levels of "last to arrive": groups of 64 row groups, then the
-    // groups (no single counter takes every row group's atomic)
-    const int NRG = N / rows, gq = rg / 64, ng2 = (NRG + 63) / 64;
-    const int in_group = min(64, NRG - gq * 64);
-    unsigned* cnt1 = a.amax_counter + (size_t)gq * kCntStride;
-    if (!arrive_last(cnt1, (unsigned)in_group, s_flag)) return;
-    {
-      float bv;
-      int bi, b;
-      if (merge_amax(a.amax_val + (size_t)gq * 64 * a.Bmax, a.amax_idx + (size_t)gq * 64 * a.Bmax,
-                     in_group, B, a.Bmax, s_res, bv, bi, b)) {
-        st_agent(a.amax_val2 + (size_t)gq * a.Bmax + b, bv);
-        st_agent(a.amax_idx2 + (size_t)gq * a.Bmax + b, bi);
-      }
-    }
-    if (tid == 0) reset_counter(cnt1);
-    unsigned* cnt2 = a.amax_counter + (size_t)ng2 * kCntStride;
-    if (!arrive_last(cnt2, (unsigned)ng2, s_flag)) return;
-    {
-      float bv;
-      int bi, b;
-      if (merge_amax(a.amax_val2, a.amax_idx2, ng2, B, a.Bmax, s_res, bv, bi, b))
-        a.next_ids[b] = bi == 0x7fffffff ? -1 : bi;
-    }
-    if (tid == 0) reset_counter(cnt2);
   }
+  mark(6);
+  // every split has passed its wait once all have arrived a second time:
+  // the last one resets the counter for the next launch
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1 == 2u * (unsigned)S) reset_counter(cnt);
+  }
+  mark(7);
+}
+
+template <int NB, int MODE, int RW>
+__device__ inline void gemv_wide_item(const GemvArgs& a, const Done& done, int item,
+                                      unsigned char* smem) {
+#ifdef QD_STEP_TRACE
+  auto mark = [&](int e) {
+    if (a.trace != nullptr && threadIdx.x == 0 && item < kTraceItems)
+      a.trace[(size_t)item * 8 + e] = __builtin_amdgcn_s_memrealtime();
+  };
+#else
+  auto mark = [](int) {};
+#endif
+  mark(0);
+  static_assert(NB == 32 || NB == 64, "32 or 64 batch columns");
+  constexpr int NCB = NB / 16;             // 16-column blocks
+  constexpr int kRows = RW * kRowsPerGroup;
+  constexpr int C = kWideChunk;
+  constexpr int P = C * kTileCols + 8;     // LDS row of one column's chunk (bf16, padded)
+  constexpr int CH = C * RW;               // weight tiles in flight per wave: one chunk
+  constexpr int QPC = C * kTileCols / 8;   // 16-byte pieces of one column's chunk
+  constexpr int kPieces = 2 * NB * QPC / 256;  // input pieces per thread per chunk
+  float* s_inv = reinterpret_cast<float*>(smem);
+  float* s_ssq = s_inv + kMaxBatch;
+  unsigned* s_flag = reinterpret_cast<unsigned*>(s_ssq + 256);
+  unsigned char* body = smem + kWideHead;
+  float* s_res = reinterpret_cast<float*>(body);
+  unsigned short* xb = reinterpret_cast<unsigned short*>(body);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int B = a.B, S = a.S;
+  const int rg = item / S, s = item - rg * S;
+  const int KT = a.K / kTileCols;
+  const int kt0 = s * a.kps, kt1 = min(KT, kt0 + a.kps), nk = kt1 - kt0;
+  const int nch = (nk + C - 1) / C;
+  const bool norm = a.ssq != nullptr;
+
+  // input chunk c: pieces idx = tid + 256 j -> (hi|lo, column b, piece q)
+  u32x4 inr[kPieces];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int idx = tid + j * 256;
+      const int hl = idx / (NB * QPC), rem = idx - hl * (NB * QPC);
+      const int b = rem / QPC, q = rem - b * QPC;
+      const int k = (kt0 + c * C) * kTileCols + q * 8;
+      if (b < B && k < kt1 * kTileCols)
+        inr[j] = *reinterpret_cast<const u32x4*>((hl ? a.xl : a.xh) + (size_t)b * a.K + k);
+    }
+  };
+  auto store_chunk = [&](int c) {
+    unsigned short* buf = xb + (c & 1) * 2 * NB * P;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int idx = tid + j * 256;
+      const int hl = idx / (NB * QPC), rem = idx - hl * (NB * QPC);
+      const int b = rem / QPC, q = rem - b * QPC;
+      const int k = (kt0 + c * C) * kTileCols + q * 8;
+      if (b < B && k < kt1 * kTileCols)
+        *reinterpret_cast<u32x4*>(buf + hl * NB * P + b * P + q * 8) = inr[j];
+    }
+  };
+
+  // weight tile i of this wave: k-tile i / RW of the slice, row tile
+  // wave + 4 * (i % RW) of the item (indices past the slice repeat its last
+  // tile: every load is issued, compute is guarded)
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.w) +
+                    ((size_t)(rg * 4 * RW + wave) * KT + kt0) * 64 + lane;
+  const unsigned rstep = 4u * (unsigned)KT * 64u;
+  const int nt = nk * RW;
+  auto wtile = [&](int i) {
+    const int ii = min(i, nt - 1);
+    return wp + (unsigned)(ii % RW) * rstep + (unsigned)(ii / RW) * 64u;
+  };
+
+  // loads in the order their data is needed: chunk 0 of the input, the
+  // RMSNorm sums of squares, the first chunk's weight tiles
+  load_chunk(0);
+  constexpr int kParts = 256 / NB;
+  constexpr int kSsq = 16;
+  const int ng = a.K / kSsqRows;
+  const int sb = tid % NB, sp = tid / NB;
+  float sv[kSsq];
+  auto load_ssq = [&](int g0) {
+#pragma unroll
+    for (int j = 0; j < kSsq; ++j)
+      sv[j] = a.ssq[(size_t)min(g0 + j * kParts, ng - 1) * a.Bmax + min(sb, B - 1)];
+  };
+  if (norm) load_ssq(sp);
+  u32x4 wbuf[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) wbuf[i] = __builtin_nontemporal_load(wtile(i));
+  mark(1);
+  store_chunk(0);
+  if (norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSsq; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;
+    for (int g0 = sp + kSsq * kParts; g0 < ng; g0 += kSsq * kParts) {
+      load_ssq(g0);
+#pragma unroll
+      for (int j = 0; j < kSsq; ++j) ss += g0 + j * kParts < ng ? sv[j] : 0.f;
+    }
+    s_ssq[tid] = ss;
+  }
+  __syncthreads();
+  if (norm && tid < B) {
+    float ss = 0.f;
+    for (int p = 0; p < kParts; ++p) ss += s_ssq[p * NB + tid];
+    s_inv[tid] = rsqrtf(ss / (float)a.K + a.eps);
+  }
+  mark(2);
+
+  f32x4 acc[RW][NCB];
+#pragma unroll
+  for (int u = 0; u < RW; ++u)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[u][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's input operand of k-tile tt of a chunk buffer: column
+  // cb * 16 + lane % 16, k-group lane / 16
+  auto mac_tile = [&](const unsigned short* buf, int tt) {
+    u32x4 h[NCB], l[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int off = (cb * 16 + (lane & 15)) * P + tt * kTileCols + (lane >> 4) * 8;
+      h[cb] = *reinterpret_cast<const u32x4*>(buf + off);
+      l[cb] = *reinterpret_cast<const u32x4*>(buf + NB * P + off);
+    }
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, wbuf[tt * RW + u]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, h[cb]),
+                                                             acc[u][cb], 0, 0, 0);
+        acc[u][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, l[cb]),
+                                                             acc[u][cb], 0, 0, 0);
+      }
+    }
+  };
+  // every chunk but the last is whole: consume it while the next one's
+  // input loads and its weight tiles replace the consumed ones
+  int c = 0;
+  for (; c + 1 < nch; ++c) {
+    __syncthreads();  // chunk c is in its buffer; the other buffer is free
+    load_chunk(c + 1);
+    const unsigned short* buf = xb + (c & 1) * 2 * NB * P;
+#pragma unroll
+    for (int tt = 0; tt < C; ++tt) {
+      mac_tile(buf, tt);
+#pragma unroll
+      for (int u = 0; u < RW; ++u)
+        wbuf[tt * RW + u] = __builtin_nontemporal_load(wtile((c + 1) * CH + tt * RW + u));
+    }
+    store_chunk(c + 1);
+  }
+  __syncthreads();
+  {
+    const unsigned short* buf = xb + (c & 1) * 2 * NB * P;
+#pragma unroll
+    for (int tt = 0; tt < C; ++tt)
+      if (c * C + tt < nk) mac_tile(buf, tt);  // (wave-uniform)
+  }
+
+  // the residual epilogue's old residual and the next consumer's gain
+  // (outputs idx = tid + 256 j = b * rows + r), while the waves finish
+  // (an unsplit item's; a split one loads its share's in gemv_finish_coop)
+  constexpr int kXold = (kRows * NB + 255) / 256;
+  float x_old[kXold], xo_g[kXold];
+  if (MODE == kResid && S == 1) {
+#pragma unroll
+    for (int j = 0; j < kXold; ++j) {
+      const int idx = tid + j * 256;
+      if (idx < kRows * B) {
+        const size_t n = (size_t)rg * kRows + idx % kRows;
+        x_old[j] = (a.res_in != nullptr ? a.res_in : a.out)[(size_t)(idx / kRows) * a.N + n];
+        xo_g[j] = a.xo_hi != nullptr ? a.xo_gain[n] : 0.f;
+      }
+    }
+  }
+  mark(3);
+  __syncthreads();  // every wave is done with the input buffers (s_res shares them)
+#pragma unroll
+  for (int u = 0; u < RW; ++u)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int col = cb * 16 + (lane & 15);
+      const float sc = norm && col < B ? s_inv[col] : 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_res[((wave + 4 * u) * 16 + (lane >> 4) * 4 + r) * NB + col] = acc[u][cb][r] * sc;
+    }
+  __syncthreads();
+  mark(4);
+  if constexpr (MODE == kStore || MODE == kResid || MODE == kSwiGLU) {
+    if (S > 1) {
+      gemv_finish_coop<NB, MODE, kRows>(a, rg, s, s_res, mark);
+      return;
+    }
+  }
+  gemv_finish<NB, MODE, kRows>(a, done, rg, s, kRows, s_res, s_flag, x_old, xo_g, mark);
 }
 
 // ------------------------------------------------------------------ attention

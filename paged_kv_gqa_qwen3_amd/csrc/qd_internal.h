@@ -101,6 +101,7 @@ struct GemvArgs {
   int* next_ids;       // kArgmax: [B]
   unsigned long long* trace;  // builds with QD_STEP_TRACE only: 8 event timestamps per item, or null
   L2Prefetch pf;       // (standalone kernel) workgroups after the items prefetch these
+  int* dev_flags;      // 32- and 64-column items: a bounded wait that times out is flagged here
 };
 
 struct AttnArgs {

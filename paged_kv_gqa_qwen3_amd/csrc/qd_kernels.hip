@@ -122,6 +122,14 @@ __global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kern
 }
 
 
+// 32 and 64 batch columns: items of 64 * RW rows that stream their input
+// slice through LDS in chunks (gemv_wide_item).
+template <int NB, int MODE, int RW>
+__global__ __launch_bounds__(256, 2) void gemv_wide_kernel(GemvArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  gemv_wide_item<NB, MODE, RW>(a, no_done(), blockIdx.x, smem);
+}
+
 // The workgroups take the step's attention items round robin; workgroups
 // past a.grid prefetch the next launch's weights (a.pf).
 template <int D, int G, int NW, int PW, class KV>
@@ -311,6 +319,29 @@ static hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NB, int MODE, int RW>
+static hipError_t launch_wide_t(const GemvArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  const void* fn = reinterpret_cast<const void*>(&gemv_wide_kernel<NB, MODE, RW>);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int grid = (a.N / (kTileRows * a.rt)) * a.S;
+  hipLaunchKernelGGL((gemv_wide_kernel<NB, MODE, RW>), dim3(grid), dim3(256),
+                     gemv_wide_lds_bytes(NB, RW), s, a);
+  return hipGetLastError();
+}
+
+// 32 and 64 columns: rt 8 (two row tiles per wave) are the chunk-streamed
+// items, rt 4 the staged ones (row counts that are no multiple of 128).
+template <int NB, int MODE>
+static hipError_t launch_wide_or_staged(const GemvArgs& a, hipStream_t s) {
+  if (a.rt == 8) return launch_wide_t<NB, MODE, 2>(a, s);
+  return launch_gemv_t<NB, MODE>(a, s);
+}
+
 template <int MODE>
 static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
   switch (gemv_nb(a.B)) {
@@ -319,8 +350,8 @@ static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
     case 16:
       if (a.rt == 8) return launch_gemv_t<16, MODE, 2>(a, s);
       return launch_gemv_t<16, MODE>(a, s);
-    case 32: return launch_gemv_t<32, MODE>(a, s);
-    default: return launch_gemv_t<64, MODE>(a, s);
+    case 32: return launch_wide_or_staged<32, MODE>(a, s);
+    default: return launch_wide_or_staged<64, MODE>(a, s);
   }
 }
 

@@ -223,6 +223,19 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
     }
     return p;
   }
+  // 32 and 64 columns: chunk-streamed items of 128 rows (rt = 8; two row
+  // tiles per wave), K split only until there are items for half the CUs
+  // (4B shape, per step at batch 32 / 64: one item per CU 4.22 / 6.14 ms,
+  // half 3.73 / 5.44, a third 4.05 / 5.98, one and a half 3.80 / 5.67;
+  // four row tiles per wave spill registers: 7.91 / 14.1)
+  if (nb >= 32 && N % (2 * kRowsPerGroup) == 0) {
+    p.rt = 8;
+    const int nrg = N / (2 * kRowsPerGroup);
+    const int S0 = std::min(KT, std::max(1, (h->num_cus / 2 + nrg - 1) / nrg));
+    p.kps = (KT + S0 - 1) / S0;
+    p.S = (KT + p.kps - 1) / p.kps;
+    return p;
+  }
   // MFMA items (batch >= 2): the fewest K splits that give every CU an item,
   // slices of at most 16 k-tiles while row groups alone do not (measured on
   // the 4B shape: batch 8 3.39 -> 3.19 ms per step against two items per CU
@@ -407,6 +420,7 @@ hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode
     }
     a.ssq = gain ? h->ssq : nullptr;
     a.gain = gain; a.eps = h->cfg.rms_eps;
+    a.dev_flags = h->dev_flags;
     a.part = mode == kPartial ? h->part_qkv : h->part;
     a.counters = h->gemv_cnt;
     a.out = out;

@@ -279,6 +279,22 @@ def test_wide_items_stages(torch, model):
     _run_stage_checks(torch, shape, W, batch, f"{shape.name} B=16")
 
 
+@pytest.mark.parametrize("model,B", [("4b", 24), ("4b", 64), ("8b", 40)])
+def test_wide_batch_stages(torch, model, B):
+    """Qwen3-4B and -8B widths (2 layers) at 24, 40 and 64 batch columns,
+    stage by stage: items of 128 rows that stream their input slice through
+    LDS in chunks of 4 k-tiles, a K split only to give half the CUs an item,
+    and the splits of a row group summing one share of its outputs each
+    (1 to 7 splits; down at K = 9728 and 12288: 11 and 24 chunks per item,
+    8B QKV slices of 43 k-tiles ending in a partial chunk).  The tiny
+    shapes reach these items too, with one k-tile per split."""
+    shape = _two_layers(WIDE[model])
+    W = _weights(shape, 6)
+    ctx = [(61 * i) % 500 for i in range(B)]
+    batch = synth.make_paged_batch(shape, ctx, 1, 252 + B)
+    _run_stage_checks(torch, shape, W, batch, f"{shape.name} B={B}")
+
+
 @pytest.mark.parametrize("model", list(WIDE))
 def test_wide_items_fused_matches_staged(torch, model):
     """The same 128-row items inside the fused MLP launch (qd_decode_step,

@@ -39,7 +39,8 @@ METRIC = "decode tokens/s + achieved HBM GB/s (% of 8 TB/s), Qwen3-4B shape, bs 
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "4b_bs1_ctx512"
 DEFAULT_WORKLOADS = ["4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
-                     "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv"]
+                     "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv", "4b_bs32_ctx256",
+                     "4b_bs64_ctx256"]
 WEIGHT_SEED = {"qwen3-4b": 2, "qwen3-8b": 6}
 
 
@@ -399,7 +400,7 @@ def time_prefill_prompts(torch, shape, W, n_tokens=512, reps=5):
             "projection_tflops": round(proj_flop / (ms / 1e3) / 1e12, 1)}
 
 
-def time_serving(torch, shape, W, n_req=64, max_batch=16, max_new=128, rows=512, seed=17):
+def time_serving(torch, shape, W, n_req=64, max_batch=64, max_new=128, rows=512, seed=17):
     """Offline serving through the continuous-batching engine (qd_engine_*):
     n_req requests queued at once, prompts of 128..1024 tokens (uniform),
     every second one starting with the same 256-token system prompt (or

@@ -226,8 +226,9 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
   // 32 and 64 columns: chunk-streamed items of 128 rows (rt = 8; two row
   // tiles per wave), K split only until there are items for half the CUs
   // (4B shape, per step at batch 32 / 64: one item per CU 4.22 / 6.14 ms,
-  // half 3.73 / 5.44, a third 4.05 / 5.98, one and a half 3.80 / 5.67;
-  // four row tiles per wave spill registers: 7.91 / 14.1)
+  // half 3.73 / 5.44, a third 4.05 / 5.98, one and a half 3.80 / 5.67; one
+  // per CU for O and down alone 3.92 / 5.72; four row tiles per wave spill
+  // registers: 7.91 / 14.1)
   if (nb >= 32 && N % (2 * kRowsPerGroup) == 0) {
     p.rt = 8;
     const int nrg = N / (2 * kRowsPerGroup);

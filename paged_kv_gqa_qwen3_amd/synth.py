@@ -122,6 +122,9 @@ WORKLOADS = {
         Workload("8b_bs8_ragged", QWEN3_8B, 8, 256, 2048, 128, 6),
         Workload("4b_bs8_ctx4096", QWEN3_4B, 8, 4096, 4096, 64, 7),
         Workload("4b_bs8_ctx4096_fp8kv", QWEN3_4B, 8, 4096, 4096, 64, 7, kv_fp8=True),
+        # batches beyond the pages' measurements: the 32- and 64-column items
+        Workload("4b_bs32_ctx256", QWEN3_4B, 32, 256, 256, 128, 9),
+        Workload("4b_bs64_ctx256", QWEN3_4B, 64, 256, 256, 128, 10),
     )
 }
 

@@ -710,7 +710,8 @@ def _weights(shape, seed):
 # also on such a handle.
 @pytest.mark.parametrize("name,persistent", [
     (n, False) for n in ("4b_bs1_ctx512", "4b_bs8_ctx256", "4b_bs16_ctx256", "4b_bs1_ctx8192",
-                         "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv")] +
+                         "8b_bs8_ragged", "4b_bs8_ctx4096", "4b_bs8_ctx4096_fp8kv",
+                         "4b_bs32_ctx256")] +
     [("4b_bs1_ctx512", True)],
     ids=lambda v: v if isinstance(v, str) else ("persistent" if v else "graph"))
 def test_full_size_steps(torch, name, persistent):

@@ -1145,7 +1145,7 @@ __device__ inline void gemv_wide_item(const GemvArgs& a, const Done& done, int i
   auto mark = [](int) {};
 #endif
   mark(0);
-  static_assert(NB == 32 || NB == 64, "32 or 64 batch columns");
+  static_assert(NB == 16 || NB == 32 || NB == 64, "16, 32 or 64 batch columns");
   constexpr int NCB = NB / 16;             // 16-column blocks
   constexpr int kRows = RW * kRowsPerGroup;
   constexpr int C = kWideChunk;

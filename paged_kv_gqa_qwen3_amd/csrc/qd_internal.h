@@ -76,7 +76,8 @@ struct GemvArgs {
   const uint16_t* w;   // packed tiles, N x K
   int N, K, B, Bmax;
   int S, kps;          // K split count and k-tiles per split
-  int rt;              // row tiles per item: 1, 2 or 4
+  int rt;              // row tiles per item: 1, 2, 4 or 8
+  int wide;            // 1: chunk-streamed items of 128 rows (gemv_wide_item)
   const float* x;      // VALU input activations [B][K] fp32
   const uint16_t* xh;  // MFMA input: bf16 pairs [64][K] of the input (times the RMSNorm gain)
   const uint16_t* xl;

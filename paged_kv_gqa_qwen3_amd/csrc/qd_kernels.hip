@@ -127,6 +127,11 @@ __global__ __launch_bounds__(256, NB == 1 ? 4 : NB <= 32 ? 3 : 2) void gemv_kern
 template <int NB, int MODE, int RW>
 __global__ __launch_bounds__(256, 2) void gemv_wide_kernel(GemvArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  const int items = a.N / (kTileRows * a.rt) * a.S;
+  if ((int)blockIdx.x >= items) {  // prefetching workgroups (a.pf)
+    l2_prefetch(a.pf, items, (int)blockIdx.x - items);
+    return;
+  }
   gemv_wide_item<NB, MODE, RW>(a, no_done(), blockIdx.x, smem);
 }
 
@@ -328,30 +333,31 @@ static hipError_t launch_wide_t(const GemvArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = (a.N / (kTileRows * a.rt)) * a.S;
+  const int grid = (a.N / (kTileRows * a.rt)) * a.S + (a.pf.w != nullptr ? a.pf.n_wg : 0);
   hipLaunchKernelGGL((gemv_wide_kernel<NB, MODE, RW>), dim3(grid), dim3(256),
                      gemv_wide_lds_bytes(NB, RW), s, a);
   return hipGetLastError();
 }
 
-// 32 and 64 columns: rt 8 (two row tiles per wave) are the chunk-streamed
-// items, rt 4 the staged ones (row counts that are no multiple of 128).
-template <int NB, int MODE>
-static hipError_t launch_wide_or_staged(const GemvArgs& a, hipStream_t s) {
-  if (a.rt == 8) return launch_wide_t<NB, MODE, 2>(a, s);
-  return launch_gemv_t<NB, MODE>(a, s);
-}
-
 template <int MODE>
 static hipError_t launch_gemv_m(const GemvArgs& a, hipStream_t s) {
+  if (a.wide) {  // chunk-streamed items of 128 rows
+    switch (gemv_nb(a.B)) {
+      case 8:
+      case 16: return launch_wide_t<16, MODE, 2>(a, s);
+      case 32: return launch_wide_t<32, MODE, 2>(a, s);
+      case 64: return launch_wide_t<64, MODE, 2>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (gemv_nb(a.B)) {
     case 1: return launch_gemv_t<1, MODE>(a, s);
     case 8: return launch_gemv_t<8, MODE>(a, s);
     case 16:
       if (a.rt == 8) return launch_gemv_t<16, MODE, 2>(a, s);
       return launch_gemv_t<16, MODE>(a, s);
-    case 32: return launch_wide_or_staged<32, MODE>(a, s);
-    default: return launch_wide_or_staged<64, MODE>(a, s);
+    case 32: return launch_gemv_t<32, MODE>(a, s);
+    default: return launch_gemv_t<64, MODE>(a, s);
   }
 }
 

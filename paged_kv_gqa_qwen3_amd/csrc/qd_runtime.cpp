@@ -43,6 +43,7 @@ constexpr int kMaxGraphs = 64;
 
 struct GemvPlan {
   int S = 1, kps = 1, rt = 4;
+  bool wide = false;  // chunk-streamed items (gemv_wide_item), rt = 8
 };
 
 struct LayerW {
@@ -203,6 +204,19 @@ constexpr int kMinValuItems = 128;
 // every other step takes the per-stage kernels.
 bool use_stream(const qd_handle* h, int B) { return h->stream_ok && B == 1; }
 
+// Chunk-streamed items of 128 rows (gemv_wide_item; N a multiple of 128).
+GemvPlan plan_wide(const qd_handle* h, int N, int K) {
+  GemvPlan p;
+  const int KT = K / kTileCols;
+  p.rt = 8;
+  p.wide = true;
+  const int nrg = N / (2 * kRowsPerGroup);
+  const int S0 = std::min(KT, std::max(1, (h->num_cus / 2 + nrg - 1) / nrg));
+  p.kps = (KT + S0 - 1) / S0;
+  p.S = (KT + p.kps - 1) / p.kps;
+  return p;
+}
+
 GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
                    bool wide = true) {
   const int KT = K / kTileCols, NRG = N / kRowsPerGroup;
@@ -229,14 +243,10 @@ GemvPlan plan_gemv(const qd_handle* h, int N, int K, int B, bool argmax = false,
   // half 3.73 / 5.44, a third 4.05 / 5.98, one and a half 3.80 / 5.67; one
   // per CU for O and down alone 3.92 / 5.72; four row tiles per wave spill
   // registers: 7.91 / 14.1)
-  if (nb >= 32 && N % (2 * kRowsPerGroup) == 0) {
-    p.rt = 8;
-    const int nrg = N / (2 * kRowsPerGroup);
-    const int S0 = std::min(KT, std::max(1, (h->num_cus / 2 + nrg - 1) / nrg));
-    p.kps = (KT + S0 - 1) / S0;
-    p.S = (KT + p.kps - 1) / p.kps;
-    return p;
-  }
+  // The LM head takes them from 8 batch columns up (batch 16: 3.295 ->
+  // 3.247 ms per step; batch 8: 2.832 -> 2.819); QKV and O at 8 and 16
+  // columns were slower with them (batch 8: 2.85 and 2.85 against 2.83).
+  if ((nb >= 32 || argmax) && N % (2 * kRowsPerGroup) == 0) return plan_wide(h, N, K);
   // MFMA items (batch >= 2): the fewest K splits that give every CU an item,
   // slices of at most 16 k-tiles while row groups alone do not (measured on
   // the 4B shape: batch 8 3.39 -> 3.19 ms per step against two items per CU
@@ -413,7 +423,7 @@ hipError_t launch_projection(qd_handle* h, int B, int cls, int l, bool part_mode
     GemvPlan p = plan_gemv(h, N, K, B, mode == kArgmax);
     GemvArgs a{};
     a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
-    a.S = p.S; a.kps = p.kps; a.rt = p.rt;
+    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.wide = p.wide ? 1 : 0;
     a.x = xin;
     if (mfma) {
       a.xh = xin_hl[0]; a.xl = xin_hl[1];
@@ -631,7 +641,7 @@ int record_step_fused(qd_handle* h, const StepPtrs& sp, hipStream_t s) {
   auto gemv_args = [&](const uint16_t* w, int N, int K, const GemvPlan& p) {
     GemvArgs a{};
     a.w = w; a.N = N; a.K = K; a.B = B; a.Bmax = h->cfg.max_batch;
-    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.eps = eps;
+    a.S = p.S; a.kps = p.kps; a.rt = p.rt; a.wide = p.wide ? 1 : 0; a.eps = eps;
     return a;
   };
   // Launches that leave HBM mostly idle (attention, O, the MLP launch's

@@ -50,7 +50,9 @@ CLASSES = (
     ("embed_kernel", "embed"),
 )
 GEMV_MODES = {"4": "qkv", "2": "gate_up", "3": "lm_head", "1": "o_proj+down", "0": "gemv_store"}
-_GEMV = re.compile(r"gemv_kernel<(\d+), (\d+)(?:, \d+)?>")
+# staged items (gemv_kernel<NB, MODE[, RPW]>) and chunk-streamed ones
+# (gemv_wide_kernel<NB, MODE, RW>) alike
+_GEMV = re.compile(r"gemv_(?:wide_)?kernel<(\d+), (\d+)(?:, \d+)?>")
 
 
 def kernel_class(name: str):

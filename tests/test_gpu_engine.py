@@ -14,7 +14,8 @@ two tokens in one iteration; and when everything is done every page of the
 pool is obtainable again.  The prefix cache must have supplied prompt pages
 (a request whose prompt repeats a finished one's).  Variants: graphs for
 every batch size, the weight-streaming kernel at batch 1, an 8-bit E4M3
-pool, and a pool so small that requests wait for pages.
+pool, a pool so small that requests wait for pages, and a batch limit of 24
+(decode batches past 16 columns).
 """
 import numpy as np
 import pytest
@@ -181,6 +182,42 @@ def test_engine_matches_oracle(torch, variant):
     excused = _check_streams(orc, plan, streams, finished, kv)
     say(f"{variant}: {excused} near-tie ids excused")
     assert streams[16][-1] == eos and len(streams[16]) < 8, "request 16 did not end on its eos"
+
+
+def test_engine_wide_batches(torch):
+    """30 requests through a batch limit of 24: the decode batch grows past
+    16 columns (the chunk-streamed 32-column GEMV items and their shared
+    split reductions) and shrinks again as requests end, each size on its
+    own graph; every stream is still the oracle's."""
+    seed = 903
+    W = synth.make_weights(SHAPE, seed)
+    orc = oracle.Oracle(SHAPE, W)
+    V = SHAPE.vocab
+    plan = {}
+    rid = 100
+    for it, n in ((0, 10), (1, 8), (2, 8), (4, 4)):
+        reqs = []
+        for _ in range(n):
+            plen = 3 + (rid * 7) % 37
+            reqs.append((rid, synth.uniform_int(seed, f"w{rid}", V, plen), 5 + rid % 6, -1))
+            rid += 1
+        plan[it] = reqs
+    num_pages, mpps = 96, 4
+    pool = pool_to_device(np.zeros((SHAPE.num_layers, num_pages, 2, SHAPE.num_kv_heads, PAGE,
+                                    SHAPE.head_dim), dtype=np.uint16))
+    dec = Decoder(SHAPE, 24, mpps, num_pages, max_prefill_rows=256)
+    dec.load_numpy_weights(W)
+    eng = binding.Engine(dec.handle, pool, 24)
+    streams, finished, per_iter, st = _drive(torch, eng, plan)
+    say(f"wide: decode batch per iteration {per_iter}")
+    assert max(per_iter) > 16, "the decode batch never passed 16"
+    assert st["pages_available"] == num_pages
+    assert st["tokens_out"] == sum(len(s) for s in streams.values())
+    eng.close()
+    assert dec.device_status() == 0
+    dec.close()
+    excused = _check_streams(orc, plan, streams, finished, oracle.BF16)
+    say(f"wide: {excused} near-tie ids excused")
 
 
 def test_engine_waits_for_pages(torch):

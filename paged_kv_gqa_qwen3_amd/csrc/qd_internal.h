@@ -311,6 +311,14 @@ struct SampleArgs {
   double* part_sum;          // [B][G] chunk weight sums (rows without limits)
   unsigned* counters2;       // [B] at stride kCntStride, for the second launch
   double* row_hist;          // [B][256] weight per top key byte (top-p rows), zero between calls
+  // the third launch (a top-p nucleus beyond the first 64 tokens)
+  double* row_hist3;         // [B][3][256] weight per key byte, passes 2-4, zero between calls
+  double* part_sum2;         // [B][G] chunk weight at the cut key
+  double* part_sum3;         // [B][G] chunk weight kept
+  unsigned* counters3;       // [B] at stride kCntStride, the row's barriers, zero between calls
+  int* row_flag;             // [B] 1: the third launch finishes the row (set by the second)
+  int* row_cut;              // [B] the last id kept at the cut key
+  int* dev_flags;            // a wait that timed out is flagged here (or null)
 };
 void sample_split(int V, int* G, int* C);
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s);

@@ -19,7 +19,7 @@
 //     token is the kept one, in increasing id order, whose running weight
 //     first exceeds t.
 //
-// Two launches per call, G workgroups per row (G = ceil(V / 8192)), each
+// Three launches per call, G workgroups per row (G = ceil(V / 8192)), each
 // owning a chunk of at most 8192 logits.
 //   First launch: every chunk loads its logits into LDS once and leaves its
 //   (max, argmax) and, for 2 <= top_k <= kFastTopK or for top-p without
@@ -34,14 +34,17 @@
 //   the row's histogram); the last workgroup then walks the chunk holding
 //   the draw target (no limit), or takes the top-p cut and the draw over
 //   the row's first 64 tokens when they reach the target.
-// Anything else (top_k above kFastTopK, or a top-p nucleus beyond 64
-// tokens) runs over the whole row in one workgroup (sample_row): cut points
-// in rank order by radix selection over a 32-bit key that orders floats
-// (four passes of 8 bits: token counts for top-k, weight for top-p; the
-// first top-p pass from the row histogram when there is one), then one pass
-// in id order among the tokens whose key equals the cut key; every pass
-// re-reads the row from L2 (608 KB for a 151,936 token vocabulary) and
-// recomputes the weights it needs.
+//   Third launch, top-p rows whose nucleus goes beyond the first 64 tokens:
+//   all G workgroups of the row take the cut by radix selection over the
+//   rest of a 32-bit key that orders floats (bytes 2-4, the first from the
+//   second launch's histogram), then the cut id and the draw in id order,
+//   each chunk from LDS, with barriers between the steps.
+// Anything else (top_k above kFastTopK) runs over the whole row in one
+// workgroup (sample_row): cut points in rank order by the same radix
+// selection (four passes of 8 bits: token counts for top-k, then weight for
+// top-p), then one pass in id order among the tokens whose key equals the
+// cut key; every pass re-reads the row from L2 (608 KB for a 151,936 token
+// vocabulary) and recomputes the weights it needs.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -157,11 +160,9 @@ __device__ __forceinline__ double block_exclusive(double v, SampleSmem& sm) {
 }
 
 // The whole-row path for row b (one workgroup of kSampleThreads), given
-// the row's max M (T > 0, top_p > 0, top_k not 1).  pre_top: sm.mass holds
-// the row's weight per top key byte already (top-p without top-k), so the
-// top-p selection starts at its second byte.
+// the row's max M (T > 0, top_p > 0, top_k above kFastTopK).
 __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, float p,
-                           float u, SampleSmem& sm, bool pre_top = false) {
+                           float u, SampleSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int V = a.V, V4 = a.V >> 2;
   const f32x4* __restrict__ row4 = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V);
@@ -211,22 +212,20 @@ __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, 
   // need(total) (total: the sum over all of them, known after the first
   // pass); leaves the key in sm.key and in sm.need what remains to take
   // among the tokens of that key.  Returns the total.
-  auto select = [&](auto&& in, auto&& unit, auto&& need_of, bool pre = false) {
+  auto select = [&](auto&& in, auto&& unit, auto&& need_of) {
     unsigned prefix = 0u, mask = 0u;
     double need = 0.0, total = 0.0;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (!(pre && shift == 24)) {
-        __syncthreads();
-        for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
-        __syncthreads();
-        strided([&](int i, float l, bool ok) {
-          const unsigned key = sample_key(l);
-          const bool on = ok && (key & mask) == prefix && in(i, l, key);
-          double val = 0.0;
-          if (on) val = unit(l);
-          hist_add(sm, (key >> shift) & 255u, val, on);
-        });
-      }
+      __syncthreads();
+      for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
+      __syncthreads();
+      strided([&](int i, float l, bool ok) {
+        const unsigned key = sample_key(l);
+        const bool on = ok && (key & mask) == prefix && in(i, l, key);
+        double val = 0.0;
+        if (on) val = unit(l);
+        hist_add(sm, (key >> shift) & 255u, val, on);
+      });
       __syncthreads();
       if (shift == 24) {
         double t4 = 0.0;
@@ -283,7 +282,7 @@ __device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, 
   unsigned kp = 0u;
   int ip = V;
   if (use_p) {
-    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); }, pre_top && !use_k);
+    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); });
     kp = sm.key;
     ip = cut_id(kp, in_k, weight, sm.need);
   }
@@ -653,14 +652,14 @@ __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a
       }
     }
     __syncthreads();
-    // the row's top-byte histogram into LDS (and cleared for the next call)
-    for (int j = tid; j < 256; j += kSampleThreads) {
-      double* hp = a.row_hist + (size_t)b * 256 + j;
-      sm.mass[j] = __hip_atomic_load(hp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(hp, 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (s_whole) sample_row(a, b, M, T, k, p, u, sm, true);
+    // a nucleus beyond the first 64 tokens: the third launch takes the row
+    // (and clears the row's top-byte histogram when done); else the
+    // histogram is cleared here for the next call
+    if (tid == 0) a.row_flag[b] = s_whole;
+    if (!s_whole)
+      for (int j = tid; j < 256; j += kSampleThreads)
+        __hip_atomic_store(a.row_hist + (size_t)b * 256 + j, 0.0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -702,6 +701,190 @@ __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a
   }
 }
 
+// Third launch, for top-p rows without a top-k limit whose nucleus the
+// row's first 64 tokens do not reach (row_flag, set by the second launch):
+// all G workgroups of the row select together, each on its chunk (loaded
+// into LDS once), with a barrier between the steps (the row's workgroups
+// are consecutive and dispatched in order, so a waiting one only waits for
+// running ones; every wait is bounded):
+//   the cut key, by radix selection over bytes 2-4 of the key (byte 1 from
+//   the second launch's row histogram): each chunk adds its weight per
+//   digit among the tokens that match the digits fixed so far into the
+//   row's histogram for that byte, then every workgroup picks the same bin;
+//   the cut id among the tokens of the cut key, in id order: each chunk's
+//   weight at that key, then the chunk holding the target walks its tokens;
+//   the draw among the kept tokens, in id order, the same way.
+// The same definitions as the whole-row path, so the same token; the last
+// workgroup to finish clears the row's histograms and counter.
+constexpr unsigned kSampleSpin = 1u << 22;
+__global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleArgs a) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ SampleSmem sm;
+  __shared__ double s_sums[kMaxSampleChunks];
+  __shared__ unsigned s_flag;
+  const int tid = threadIdx.x;
+  const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
+  const int V = a.V;
+  const float T = a.temperature[b];
+  const int k = a.top_k[b];
+  const float p = a.top_p[b];
+  // the second launch's top-p rows, those it left to this one (uniform)
+  if (!(T > 0.f) || p <= 0.f || k == 1 || !(k <= 0 || k >= V) || !(p < 1.f)) return;
+  if (a.row_flag[b] == 0) return;
+  float u = a.uniform[b];
+  if (!(u >= 0.f)) u = 0.f;
+
+  // the row's max and total weight, from the earlier launches
+  float M = -INFINITY;
+  for (int w = 0; w < G; ++w) M = fmaxf(M, a.part_max[(size_t)b * G + w]);
+  double R = 0.0;
+  for (int w = 0; w < G; ++w) R += a.part_sum[(size_t)b * G + w];
+  auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
+
+  // the chunk into LDS; thread t owns its consecutive tokens [lo, hi), so
+  // that thread order is id order
+  float* const xs = reinterpret_cast<float*>(dyn);
+  const int c0 = g * a.C, n = max(0, min(a.C, V - c0));
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V + c0);
+  for (int j = tid; j < n / 4; j += kSampleThreads) reinterpret_cast<f32x4*>(xs)[j] = src[j];
+  const int per = (n + kSampleThreads - 1) / kSampleThreads;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  // (if no chunk finds the cut; an agent-scope store like every value that
+  // crosses workgroups here: a plain one can stay in this XCD's L2, where
+  // this XCD's later loads would still find it over the cut)
+  if (g == 0 && tid == 0)
+    __hip_atomic_store(a.row_cut + b, V - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+
+  unsigned* const cnt = a.counters3 + (size_t)b * kCntStride;
+  unsigned phase = 0;
+  auto row_barrier = [&]() {  // every workgroup of the row past the same point
+    ++phase;
+    stores_done();
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      poll_counter(cnt, phase * (unsigned)G, a.dev_flags, kSampleSpin);
+    }
+    __syncthreads();
+  };
+  // the row's G chunk values at sums into s_sums; returns those before chunk g
+  auto gather = [&](const double* sums) {
+    for (int w = tid; w < G; w += kSampleThreads)
+      s_sums[w] = __hip_atomic_load(sums + (size_t)b * G + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    double before = 0.0;
+    for (int w = 0; w < g; ++w) before += s_sums[w];
+    return before;
+  };
+
+  // --- the cut key: byte 1 from the row histogram, bytes 2-4 here
+  double need = ceil((double)p * R);
+  for (int j = tid; j < 256; j += kSampleThreads)
+    sm.mass[j] = __hip_atomic_load(a.row_hist + (size_t)b * 256 + j, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid < 64) pick_bin(sm, 0u, 24, need);
+  __syncthreads();
+  unsigned prefix = sm.key, mask = 0xff000000u;
+  need = sm.need;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = 16 - 8 * pass;
+    for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
+    __syncthreads();
+    for (int i0 = 0; i0 < n; i0 += kSampleThreads) {  // (wave-uniform bounds for hist_add)
+      const int i = i0 + tid;
+      const float l = i < n ? xs[i] : -INFINITY;
+      const unsigned key = sample_key(l);
+      const bool on = i < n && (key & mask) == prefix;
+      hist_add(sm, (key >> shift) & 255u, on ? weight(l) : 0.0, on);
+    }
+    __syncthreads();
+    double* const rh = a.row_hist3 + ((size_t)b * 3 + pass) * 256;
+    for (int j = tid; j < 256; j += kSampleThreads)
+      if (sm.mass[j] != 0.0) atomicAdd(rh + j, sm.mass[j]);  // exact: integers below 2^53
+    row_barrier();
+    for (int j = tid; j < 256; j += kSampleThreads)
+      sm.mass[j] = __hip_atomic_load(rh + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid < 64) pick_bin(sm, prefix, shift, need);
+    __syncthreads();
+    prefix = sm.key;
+    need = sm.need;
+    mask |= 255u << shift;
+  }
+  const unsigned kc = prefix;
+
+  // --- the cut id: the last token of key kc, in id order, at which the
+  // running weight reaches need
+  double mine = 0.0;
+  for (int i = lo; i < hi; ++i)
+    if (sample_key(xs[i]) == kc) mine += weight(xs[i]);
+  double Sg = block_sum(mine, sm);
+  if (tid == 0)
+    __hip_atomic_store(a.part_sum2 + (size_t)b * G + g, Sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  row_barrier();
+  double before = gather(a.part_sum2);
+  if (before < need && need <= before + Sg) {  // (uniform over the workgroup)
+    double run = before + block_exclusive(mine, sm);
+    if (run < need && need <= run + mine)
+      for (int i = lo; i < hi; ++i)
+        if (sample_key(xs[i]) == kc) {
+          run += weight(xs[i]);
+          if (run >= need) {
+            __hip_atomic_store(a.row_cut + b, c0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+  }
+  row_barrier();
+  const int ic = __hip_atomic_load(a.row_cut + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // --- the draw among the kept tokens (key above kc, or kc up to ic), in
+  // id order
+  auto kept = [&](int i) {
+    const unsigned key = sample_key(xs[i]);
+    return key > kc || (key == kc && c0 + i <= ic);
+  };
+  mine = 0.0;
+  for (int i = lo; i < hi; ++i)
+    if (kept(i)) mine += weight(xs[i]);
+  Sg = block_sum(mine, sm);
+  if (tid == 0)
+    __hip_atomic_store(a.part_sum3 + (size_t)b * G + g, Sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  row_barrier();
+  before = gather(a.part_sum3);
+  double Rk = 0.0;
+  for (int w = 0; w < G; ++w) Rk += s_sums[w];
+  const double t = fmin(floor((double)u * Rk), Rk - 1.0);
+  if (before <= t && t < before + Sg) {  // (uniform over the workgroup)
+    double run = before + block_exclusive(mine, sm);
+    if (run <= t && t < run + mine)
+      for (int i = lo; i < hi; ++i)
+        if (kept(i)) {
+          run += weight(xs[i]);
+          if (t < run) { a.out[b] = c0 + i; break; }
+        }
+  }
+
+  // --- the last workgroup out clears the row's histograms and counter
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = prev + 1 == (phase + 1) * (unsigned)G ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_flag != 0u) {
+    for (int j = tid; j < 4 * 256; j += kSampleThreads) {
+      double* hp = j < 256 ? a.row_hist + (size_t)b * 256 + j
+                           : a.row_hist3 + (size_t)b * 3 * 256 + (j - 256);
+      __hip_atomic_store(hp, 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) reset_counter(cnt);
+  }
+}
+
 void sample_split(int V, int* G, int* C) {
   int g = (V + kSampleChunk - 1) / kSampleChunk;
   if (g < 1) g = 1;
@@ -717,12 +900,15 @@ hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sample_sum_kernel, dim3(B * a.G), dim3(kSampleThreads),
                      (size_t)a.G * 64 * sizeof(unsigned long long), s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sample_nucleus_kernel, dim3(B * a.G), dim3(kSampleThreads), lds, s, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ no-allocation entry point
 
-// qd_sample_noalloc runs the same two launches with its scratch in one
+// qd_sample_noalloc runs the same three launches with its scratch in one
 // file-scope device array instead of a handle's buffers, so that callers
 // that cannot allocate (code under graph capture, tight serving loops) can
 // sample.  The array is sized for batch <= kNoAllocBatch and vocab <=
@@ -739,12 +925,18 @@ constexpr size_t kNaMax = 0;                                             // floa
 constexpr size_t kNaIdx = kNaMax + na_align(kNaSlots * 4);               // int [B][G]
 constexpr size_t kNaCand = kNaIdx + na_align(kNaSlots * 4);              // u64 [B][G][64]
 constexpr size_t kNaSum = kNaCand + na_align(kNaSlots * 64 * 8);         // double [B][G]
-// (counters, second counters and row histograms are contiguous: one fill
-// clears them at the start of every call)
-constexpr size_t kNaCnt = kNaSum + na_align(kNaSlots * 8);               // u32 [B][kCntStride]
+constexpr size_t kNaSum2 = kNaSum + na_align(kNaSlots * 8);              // double [B][G]
+constexpr size_t kNaSum3 = kNaSum2 + na_align(kNaSlots * 8);             // double [B][G]
+constexpr size_t kNaFlag = kNaSum3 + na_align(kNaSlots * 8);             // int [B]
+constexpr size_t kNaCut = kNaFlag + na_align((size_t)kNoAllocBatch * 4);  // int [B]
+// (counters and row histograms of all three launches are contiguous: one
+// fill clears them at the start of every call)
+constexpr size_t kNaCnt = kNaCut + na_align((size_t)kNoAllocBatch * 4);  // u32 [B][kCntStride]
 constexpr size_t kNaCnt2 = kNaCnt + na_align((size_t)kNoAllocBatch * kCntStride * 4);
-constexpr size_t kNaHist = kNaCnt2 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
-constexpr size_t kNaBytes = kNaHist + na_align((size_t)kNoAllocBatch * 256 * 8);  // ~1.2 MB
+constexpr size_t kNaCnt3 = kNaCnt2 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
+constexpr size_t kNaHist = kNaCnt3 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
+constexpr size_t kNaHist3 = kNaHist + na_align((size_t)kNoAllocBatch * 256 * 8);
+constexpr size_t kNaBytes = kNaHist3 + na_align((size_t)kNoAllocBatch * 3 * 256 * 8);  // ~1.6 MB
 
 static __device__ __align__(256) unsigned char scratch[kNaBytes];
 
@@ -814,7 +1006,10 @@ extern "C" int qd_sample_noalloc(int32_t batch, int32_t vocab, const float* logi
                reinterpret_cast<float*>(p + kNaMax), reinterpret_cast<int*>(p + kNaIdx),
                reinterpret_cast<unsigned long long*>(p + kNaCand),
                reinterpret_cast<unsigned*>(p + kNaCnt), reinterpret_cast<double*>(p + kNaSum),
-               reinterpret_cast<unsigned*>(p + kNaCnt2), reinterpret_cast<double*>(p + kNaHist)};
+               reinterpret_cast<unsigned*>(p + kNaCnt2), reinterpret_cast<double*>(p + kNaHist),
+               reinterpret_cast<double*>(p + kNaHist3), reinterpret_cast<double*>(p + kNaSum2),
+               reinterpret_cast<double*>(p + kNaSum3), reinterpret_cast<unsigned*>(p + kNaCnt3),
+               reinterpret_cast<int*>(p + kNaFlag), reinterpret_cast<int*>(p + kNaCut), nullptr};
   e = launch_sample(a, batch, s);
   if (e != hipSuccess)
     return set_global_error(QD_EHIP, std::string("qd_sample_noalloc: ") + hipGetErrorString(e));

@@ -45,6 +45,7 @@ CLASSES = (
     ("fused_mlp_kernel", "gate_up+down"),
     ("read_ceiling_kernel", "read_ceiling"),
     ("sample_sum_kernel", "sample_sum"),
+    ("sample_nucleus_kernel", "sample_nucleus"),
     ("sample_kernel", "sample"),
     ("attention_kernel", "attention"),
     ("embed_kernel", "embed"),

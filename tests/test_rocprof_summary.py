@@ -21,6 +21,7 @@ def test_kernel_classes():
         "void qd::stream_step_kernel<128, 4>(qd::StreamArgs)": "stream_step",
         "qd::sample_kernel(qd::SampleArgs)": "sample",
         "qd::sample_sum_kernel(qd::SampleArgs)": "sample_sum",
+        "qd::sample_nucleus_kernel(qd::SampleArgs)": "sample_nucleus",
         "void qd::pf_gemm_kernel<2, 4, 2, 8>(qd::PfGemmArgs)": "pf_gate_up",
         "qd::repack_kernel(unsigned short const*, int, int, unsigned short*, int, int, int)": None,
     }

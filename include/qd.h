@@ -273,7 +273,7 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
  * results as qd_sample (DEVICE pointers, `batch` rows of `vocab` fp32
  * logits, 16-byte aligned), plus the vocabulary size and the HIP stream
  * (a hipStream_t; NULL = null stream) the three sampling launches and one
- * small fill launch go to.  Scratch is one static device array of ~1.6 MB
+ * small fill launch go to.  Scratch is one static device array of ~2.2 MB
  * per GPU (held until the process ends), sized for batch <= 64 and vocab <=
  * 262144: larger sizes return QD_EINVAL with a message in qd_last_error(NULL).
  * Every call on a GPU shares that GPU's array (its counters are cleared at

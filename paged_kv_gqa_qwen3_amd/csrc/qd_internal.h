@@ -295,6 +295,7 @@ constexpr int kMaxSplitsStaged = 512;
 constexpr int kFastTopK = 64;
 constexpr int kSampleChunk = 8192;  // most logits per workgroup
 constexpr int kMaxSampleChunks = 64;  // most workgroups per row (vocab <= 524288)
+constexpr int kPassHists = 8;  // radix passes of the third launch: 4 by count, 4 by weight
 struct SampleArgs {
   const float* logits;       // [B][V]
   int V;
@@ -311,13 +312,14 @@ struct SampleArgs {
   double* part_sum;          // [B][G] chunk weight sums (rows without limits)
   unsigned* counters2;       // [B] at stride kCntStride, for the second launch
   double* row_hist;          // [B][256] weight per top key byte (top-p rows), zero between calls
-  // the third launch (a top-p nucleus beyond the first 64 tokens)
-  double* row_hist3;         // [B][3][256] weight per key byte, passes 2-4, zero between calls
-  double* part_sum2;         // [B][G] chunk weight at the cut key
+  // the third launch (top-p nuclei beyond the first 64 tokens, top_k above
+  // kFastTopK)
+  double* pass_hist;         // [B][kPassHists][256] count or weight per key byte, zero between calls
+  double* part_sum2;         // [B][G] chunk count or weight at a cut key
   double* part_sum3;         // [B][G] chunk weight kept
   unsigned* counters3;       // [B] at stride kCntStride, the row's barriers, zero between calls
-  int* row_flag;             // [B] 1: the third launch finishes the row (set by the second)
-  int* row_cut;              // [B] the last id kept at the cut key
+  int* row_flag;             // [B] 1: the third launch finishes a top-p row (set by the second)
+  int* row_cut;              // [B][2] the last id kept at the top-k and top-p cut keys
   int* dev_flags;            // a wait that timed out is flagged here (or null)
 };
 void sample_split(int V, int* G, int* C);

@@ -103,7 +103,7 @@ struct qd_handle {
   double* sample_sum = nullptr;
   unsigned* sample_cnt2 = nullptr;
   double* sample_hist = nullptr;
-  double* sample_hist3 = nullptr;  // the third sampling launch's buffers
+  double* sample_pass_hist = nullptr;  // the third sampling launch's buffers
   double *sample_sum2 = nullptr, *sample_sum3 = nullptr;
   unsigned* sample_cnt3 = nullptr;
   int *sample_flag = nullptr, *sample_cut = nullptr;
@@ -1171,16 +1171,16 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     if ((rc = dev_alloc(h, &h->sample_sum, slots))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_cnt2, (size_t)Bm * kCntStride))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_hist, (size_t)Bm * 256))) return bail(rc);
-    if ((rc = dev_alloc(h, &h->sample_hist3, (size_t)Bm * 3 * 256))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_pass_hist, (size_t)Bm * kPassHists * 256))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_sum2, slots))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_sum3, slots))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_cnt3, (size_t)Bm * kCntStride))) return bail(rc);
     if ((rc = dev_alloc(h, &h->sample_flag, (size_t)Bm))) return bail(rc);
-    if ((rc = dev_alloc(h, &h->sample_cut, (size_t)Bm))) return bail(rc);
+    if ((rc = dev_alloc(h, &h->sample_cut, (size_t)Bm * 2))) return bail(rc);
     e = hipMemset(h->sample_cnt, 0, sizeof(unsigned) * Bm * kCntStride);
     if (e == hipSuccess) e = hipMemset(h->sample_cnt2, 0, sizeof(unsigned) * Bm * kCntStride);
     if (e == hipSuccess) e = hipMemset(h->sample_hist, 0, sizeof(double) * Bm * 256);
-    if (e == hipSuccess) e = hipMemset(h->sample_hist3, 0, sizeof(double) * Bm * 3 * 256);
+    if (e == hipSuccess) e = hipMemset(h->sample_pass_hist, 0, sizeof(double) * Bm * kPassHists * 256);
     if (e == hipSuccess) e = hipMemset(h->sample_cnt3, 0, sizeof(unsigned) * Bm * kCntStride);
     if (e == hipSuccess) e = hipMemset(h->sample_flag, 0, sizeof(int) * Bm);
     if (e != hipSuccess) { hip_fail(h, e, "hipMemset"); return bail(QD_EHIP); }
@@ -1539,7 +1539,7 @@ int qd_sample(qd_handle* h, int32_t batch, const float* logits, const float* tem
   SampleArgs a{logits, h->V, temperature, top_k, top_p, uniform, out_ids,
                h->sample_G, h->sample_C, h->sample_max, h->sample_idx,
                h->sample_cand, h->sample_cnt, h->sample_sum, h->sample_cnt2,
-               h->sample_hist, h->sample_hist3, h->sample_sum2, h->sample_sum3,
+               h->sample_hist, h->sample_pass_hist, h->sample_sum2, h->sample_sum3,
                h->sample_cnt3, h->sample_flag, h->sample_cut, h->dev_flags};
   HIP_TRY(h, launch_sample(a, batch, h->stream));
   return QD_OK;

@@ -34,17 +34,13 @@
 //   the row's histogram); the last workgroup then walks the chunk holding
 //   the draw target (no limit), or takes the top-p cut and the draw over
 //   the row's first 64 tokens when they reach the target.
-//   Third launch, top-p rows whose nucleus goes beyond the first 64 tokens:
-//   all G workgroups of the row take the cut by radix selection over the
-//   rest of a 32-bit key that orders floats (bytes 2-4, the first from the
-//   second launch's histogram), then the cut id and the draw in id order,
-//   each chunk from LDS, with barriers between the steps.
-// Anything else (top_k above kFastTopK) runs over the whole row in one
-// workgroup (sample_row): cut points in rank order by the same radix
-// selection (four passes of 8 bits: token counts for top-k, then weight for
-// top-p), then one pass in id order among the tokens whose key equals the
-// cut key; every pass re-reads the row from L2 (608 KB for a 151,936 token
-// vocabulary) and recomputes the weights it needs.
+//   Third launch, the rest: top-p rows whose nucleus goes beyond the first
+//   64 tokens, and top_k above kFastTopK.  All G workgroups of the row take
+//   the cut points in rank order by radix selection over a 32-bit key that
+//   orders floats (four passes of 8 bits: token counts for top-k, then
+//   weight for top-p; for top-p alone the first pass is the second launch's
+//   histogram), then each cut id and the draw in id order, each chunk from
+//   LDS, with barriers between the steps.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -157,155 +153,6 @@ __device__ __forceinline__ double block_exclusive(double v, SampleSmem& sm) {
   double base = 0.0;
   for (int w = 0; w < wave; ++w) base += sm.wd[w];
   return base + inc - v;
-}
-
-// The whole-row path for row b (one workgroup of kSampleThreads), given
-// the row's max M (T > 0, top_p > 0, top_k above kFastTopK).
-__device__ void sample_row(const SampleArgs& a, int b, float M, float T, int k, float p,
-                           float u, SampleSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int V = a.V, V4 = a.V >> 2;
-  const f32x4* __restrict__ row4 = reinterpret_cast<const f32x4*>(a.logits + (size_t)b * V);
-
-  // Passes over the row.  strided: float4 groups tid, tid + 1024, ...
-  // (coalesced), four loads in flight per thread; chunked: the thread's own
-  // run of consecutive groups, so that thread order is id order.  fn(id,
-  // logit, valid) is called in wave-uniform control flow (valid false past
-  // the end), so it may use cross-lane operations.
-  auto strided = [&](auto&& fn) {
-    for (int j0 = tid; j0 < V4; j0 += 4 * kSampleThreads) {
-      f32x4 v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + q * kSampleThreads;
-        v[q] = j < V4 ? row4[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + q * kSampleThreads;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fn(4 * j + e, v[q][e], j < V4);
-      }
-    }
-  };
-  const int c4 = (V4 + kSampleThreads - 1) / kSampleThreads;
-  const int g_lo = min(V4, tid * c4), g_hi = min(V4, g_lo + c4);
-  auto chunked = [&](auto&& fn) {  // no cross-lane operations in fn
-    for (int j0 = g_lo; j0 < g_hi; j0 += 4) {
-      f32x4 v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (j0 + q < g_hi) v[q] = row4[j0 + q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (j0 + q < g_hi) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fn(4 * (j0 + q) + e, v[q][e]);
-        }
-    }
-  };
-
-  auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
-
-  // The cut in rank order: the key at which the running total of unit(l)
-  // over tokens passing `in`, taken from the largest key down, reaches
-  // need(total) (total: the sum over all of them, known after the first
-  // pass); leaves the key in sm.key and in sm.need what remains to take
-  // among the tokens of that key.  Returns the total.
-  auto select = [&](auto&& in, auto&& unit, auto&& need_of) {
-    unsigned prefix = 0u, mask = 0u;
-    double need = 0.0, total = 0.0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
-      __syncthreads();
-      strided([&](int i, float l, bool ok) {
-        const unsigned key = sample_key(l);
-        const bool on = ok && (key & mask) == prefix && in(i, l, key);
-        double val = 0.0;
-        if (on) val = unit(l);
-        hist_add(sm, (key >> shift) & 255u, val, on);
-      });
-      __syncthreads();
-      if (shift == 24) {
-        double t4 = 0.0;
-        for (int j = 0; j < 256; ++j) t4 += sm.mass[j];  // exact: integers < 2^53
-        total = t4;
-        need = need_of(total);
-      }
-      if (tid < 64) pick_bin(sm, prefix, shift, need);
-      __syncthreads();
-      prefix = sm.key;
-      need = sm.need;
-      mask |= 255u << shift;
-    }
-    return total;
-  };
-
-  // The last id (in id order) among tokens with key kc passing `in` at
-  // which the running unit total reaches need.
-  auto cut_id = [&](unsigned kc, auto&& in, auto&& unit, double need) {
-    if (tid == 0) sm.id = V - 1;
-    double mine = 0.0;
-    chunked([&](int i, float l) {
-      if (sample_key(l) == kc && in(i, l, kc)) mine += unit(l);
-    });
-    double run = block_exclusive(mine, sm);
-    if (run < need && need <= run + mine) {
-      bool found = false;
-      chunked([&](int i, float l) {
-        if (!found && sample_key(l) == kc && in(i, l, kc)) {
-          run += unit(l);
-          if (run >= need) { sm.id = i; found = true; }
-        }
-      });
-    }
-    __syncthreads();
-    return sm.id;
-  };
-
-  // --- top-k
-  const bool use_k = k > 0 && k < V;
-  unsigned kk = 0u;
-  int ik = V;
-  auto all = [](int, float, unsigned) { return true; };
-  auto one = [](float) { return 1.0; };
-  if (use_k) {
-    select(all, one, [&](double) { return (double)k; });
-    kk = sm.key;
-    ik = cut_id(kk, all, one, sm.need);
-  }
-  auto in_k = [&](int i, float, unsigned key) { return !use_k || key > kk || (key == kk && i <= ik); };
-
-  // --- top-p (the target is formed from the total weight top-k kept)
-  const bool use_p = p < 1.f;
-  unsigned kp = 0u;
-  int ip = V;
-  if (use_p) {
-    select(in_k, weight, [&](double Q) { return ceil((double)p * Q); });
-    kp = sm.key;
-    ip = cut_id(kp, in_k, weight, sm.need);
-  }
-  auto kept = [&](int i, float l) {
-    const unsigned key = sample_key(l);
-    return in_k(i, l, key) && (!use_p || key > kp || (key == kp && i <= ip));
-  };
-
-  // --- the draw, in id order
-  double mine = 0.0;
-  chunked([&](int i, float l) { if (kept(i, l)) mine += weight(l); });
-  double run = block_exclusive(mine, sm);
-  const double R = block_sum(mine, sm);
-  const double t = fmin(floor((double)u * R), R - 1.0);
-  if (run <= t && t < run + mine) {
-    bool found = false;
-    chunked([&](int i, float l) {
-      if (!found && kept(i, l)) {
-        run += weight(l);
-        if (t < run) { a.out[b] = i; found = true; }
-      }
-    });
-  }
 }
 
 // Top-64 lists, one value per lane, sorted descending across the lanes of a
@@ -486,10 +333,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   if (tid == 0) a.out[b] = bi;  // greedy, and the fallback of the draws below
   if (greedy) return;
   if (plain || topp) return;  // finished by the second launch
-  if (!fast) {
-    sample_row(a, b, bv, T, k, p, u, sm);
-    return;
-  }
+  if (!fast) return;  // top-k above kFastTopK: the third launch
 
   // Fast path: the chunks' lists into LDS (all loads in flight at once; the
   // chunk is no longer needed: G * 512 bytes <= 4 * C), merged pairwise by
@@ -543,7 +387,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
 // through it in id order; with top-p, the total weight gives the target,
 // and if the row's first 64 tokens (merged from the first launch's chunk
 // lists) reach it, the cut and the draw are taken over them in one wave,
-// else over the whole row (sample_row).
+// else the third launch takes the row.
 __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SampleSmem sm;
@@ -701,26 +545,33 @@ __global__ __launch_bounds__(kSampleThreads) void sample_sum_kernel(SampleArgs a
   }
 }
 
-// Third launch, for top-p rows without a top-k limit whose nucleus the
-// row's first 64 tokens do not reach (row_flag, set by the second launch):
-// all G workgroups of the row select together, each on its chunk (loaded
-// into LDS once), with a barrier between the steps (the row's workgroups
-// are consecutive and dispatched in order, so a waiting one only waits for
-// running ones; every wait is bounded):
-//   the cut key, by radix selection over bytes 2-4 of the key (byte 1 from
-//   the second launch's row histogram): each chunk adds its weight per
-//   digit among the tokens that match the digits fixed so far into the
-//   row's histogram for that byte, then every workgroup picks the same bin;
+// Third launch, for the rows the first two leave: top-p without a top-k
+// limit whose nucleus the row's first 64 tokens do not reach (row_flag, set
+// by the second launch), and top-k above kFastTopK (with or without
+// top-p).  All G workgroups of the row select together, each on its chunk
+// (loaded into LDS once), with a barrier between the steps (the row's
+// workgroups are consecutive and dispatched in order, so a waiting one only
+// waits for running ones; every wait is bounded):
+//   a cut key by radix selection: each chunk adds its count or weight per
+//   digit, among the tokens that match the digits fixed so far, into the
+//   row's histogram for that byte, then every workgroup picks the same bin
+//   (for top-p alone the top byte comes from the second launch's row
+//   histogram);
 //   the cut id among the tokens of the cut key, in id order: each chunk's
-//   weight at that key, then the chunk holding the target walks its tokens;
-//   the draw among the kept tokens, in id order, the same way.
-// The same definitions as the whole-row path, so the same token; the last
-// workgroup to finish clears the row's histograms and counter.
+//   sum at that key, then the chunk holding the target walks its tokens;
+//   top-k first (by count), then top-p among the top k (by weight, the
+//   total from the first weight histogram); the draw among the kept tokens
+//   in id order, the same way.
+// The same definitions as the one-workgroup paths, so the same token.
+// Every value that crosses workgroups is written with agent-scope stores or
+// atomics.  The last workgroup to finish clears the row's histograms and
+// counter.
 constexpr unsigned kSampleSpin = 1u << 22;
 __global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleArgs a) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SampleSmem sm;
   __shared__ double s_sums[kMaxSampleChunks];
+  __shared__ double s_total;
   __shared__ unsigned s_flag;
   const int tid = threadIdx.x;
   const int G = a.G, b = blockIdx.x / G, g = blockIdx.x % G;
@@ -728,17 +579,22 @@ __global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleAr
   const float T = a.temperature[b];
   const int k = a.top_k[b];
   const float p = a.top_p[b];
-  // the second launch's top-p rows, those it left to this one (uniform)
-  if (!(T > 0.f) || p <= 0.f || k == 1 || !(k <= 0 || k >= V) || !(p < 1.f)) return;
-  if (a.row_flag[b] == 0) return;
+  if (!(T > 0.f) || p <= 0.f || k == 1) return;  // greedy
+  const bool use_k = k > kFastTopK && k < V;
+  const bool use_p = p < 1.f;
+  if (use_k) {
+    // top-k above the first launch's lists
+  } else if (k > 1 && k <= kFastTopK) {
+    return;  // the first launch's lists
+  } else if (!use_p || a.row_flag[b] == 0) {
+    return;  // no limit, or a nucleus within the first 64 tokens
+  }
   float u = a.uniform[b];
   if (!(u >= 0.f)) u = 0.f;
 
-  // the row's max and total weight, from the earlier launches
+  // the row's max, from the first launch
   float M = -INFINITY;
   for (int w = 0; w < G; ++w) M = fmaxf(M, a.part_max[(size_t)b * G + w]);
-  double R = 0.0;
-  for (int w = 0; w < G; ++w) R += a.part_sum[(size_t)b * G + w];
   auto weight = [&](float l) { return floor((double)expf((l - M) / T) * 4294967296.0); };
 
   // the chunk into LDS; thread t owns its consecutive tokens [lo, hi), so
@@ -749,14 +605,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleAr
   for (int j = tid; j < n / 4; j += kSampleThreads) reinterpret_cast<f32x4*>(xs)[j] = src[j];
   const int per = (n + kSampleThreads - 1) / kSampleThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
-  // (if no chunk finds the cut; an agent-scope store like every value that
-  // crosses workgroups here: a plain one can stay in this XCD's L2, where
-  // this XCD's later loads would still find it over the cut)
-  if (g == 0 && tid == 0)
-    __hip_atomic_store(a.row_cut + b, V - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (g == 0 && tid < 2)  // (if no chunk finds a cut)
+    __hip_atomic_store(a.row_cut + 2 * b + tid, V - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 
   unsigned* const cnt = a.counters3 + (size_t)b * kCntStride;
+  double* const hist = a.pass_hist + (size_t)b * kPassHists * 256;
   unsigned phase = 0;
   auto row_barrier = [&]() {  // every workgroup of the row past the same point
     ++phase;
@@ -777,83 +631,129 @@ __global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleAr
     for (int w = 0; w < g; ++w) before += s_sums[w];
     return before;
   };
-
-  // --- the cut key: byte 1 from the row histogram, bytes 2-4 here
-  double need = ceil((double)p * R);
-  for (int j = tid; j < 256; j += kSampleThreads)
-    sm.mass[j] = __hip_atomic_load(a.row_hist + (size_t)b * 256 + j, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid < 64) pick_bin(sm, 0u, 24, need);
-  __syncthreads();
-  unsigned prefix = sm.key, mask = 0xff000000u;
-  need = sm.need;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = 16 - 8 * pass;
+  // a global histogram into sm.mass
+  auto load_hist = [&](const double* h) {
+    for (int j = tid; j < 256; j += kSampleThreads)
+      sm.mass[j] = __hip_atomic_load(h + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  };
+  // one radix pass: the row's histogram of unit(l) per digit at `shift`
+  // among the chunk's tokens i with (key & mask) == prefix and in(i), built
+  // in global slot `slot`, then in sm.mass
+  auto pass_hist = [&](int slot, int shift, unsigned prefix, unsigned mask, auto&& in,
+                       auto&& unit) {
     for (int j = tid; j < 256; j += kSampleThreads) sm.mass[j] = 0.0;
     __syncthreads();
     for (int i0 = 0; i0 < n; i0 += kSampleThreads) {  // (wave-uniform bounds for hist_add)
       const int i = i0 + tid;
       const float l = i < n ? xs[i] : -INFINITY;
       const unsigned key = sample_key(l);
-      const bool on = i < n && (key & mask) == prefix;
-      hist_add(sm, (key >> shift) & 255u, on ? weight(l) : 0.0, on);
+      const bool on = i < n && (key & mask) == prefix && in(i);
+      hist_add(sm, (key >> shift) & 255u, on ? unit(l) : 0.0, on);
     }
     __syncthreads();
-    double* const rh = a.row_hist3 + ((size_t)b * 3 + pass) * 256;
+    double* const rh = hist + (size_t)slot * 256;
     for (int j = tid; j < 256; j += kSampleThreads)
       if (sm.mass[j] != 0.0) atomicAdd(rh + j, sm.mass[j]);  // exact: integers below 2^53
     row_barrier();
-    for (int j = tid; j < 256; j += kSampleThreads)
-      sm.mass[j] = __hip_atomic_load(rh + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (tid < 64) pick_bin(sm, prefix, shift, need);
-    __syncthreads();
-    prefix = sm.key;
-    need = sm.need;
-    mask |= 255u << shift;
-  }
-  const unsigned kc = prefix;
-
-  // --- the cut id: the last token of key kc, in id order, at which the
-  // running weight reaches need
-  double mine = 0.0;
-  for (int i = lo; i < hi; ++i)
-    if (sample_key(xs[i]) == kc) mine += weight(xs[i]);
-  double Sg = block_sum(mine, sm);
-  if (tid == 0)
-    __hip_atomic_store(a.part_sum2 + (size_t)b * G + g, Sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  row_barrier();
-  double before = gather(a.part_sum2);
-  if (before < need && need <= before + Sg) {  // (uniform over the workgroup)
-    double run = before + block_exclusive(mine, sm);
-    if (run < need && need <= run + mine)
-      for (int i = lo; i < hi; ++i)
-        if (sample_key(xs[i]) == kc) {
-          run += weight(xs[i]);
-          if (run >= need) {
-            __hip_atomic_store(a.row_cut + b, c0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
+    load_hist(rh);
+  };
+  // pick the bin at `shift` (sm.mass holds that byte's histogram) and go on
+  // to the lower bytes; returns the cut key, leaves in sm.need what remains
+  // to take among its tokens
+  auto select = [&](int slot, int shift, unsigned prefix, unsigned mask, double need, auto&& in,
+                    auto&& unit) {
+    for (;;) {
+      if (tid < 64) pick_bin(sm, prefix, shift, need);
+      __syncthreads();
+      prefix = sm.key;
+      need = sm.need;
+      mask |= 255u << shift;
+      if (shift == 0) return prefix;
+      shift -= 8;
+      pass_hist(slot++, shift, prefix, mask, in, unit);
+    }
+  };
+  // the cut id: the token of key kc, in id order among those with in(i), at
+  // which the running unit(l) reaches need; into row_cut[2b + which]
+  auto cut_id = [&](unsigned kc, double need, int which, auto&& in, auto&& unit) {
+    double mine = 0.0;
+    for (int i = lo; i < hi; ++i)
+      if (sample_key(xs[i]) == kc && in(i)) mine += unit(xs[i]);
+    const double Sg = block_sum(mine, sm);
+    if (tid == 0)
+      __hip_atomic_store(a.part_sum2 + (size_t)b * G + g, Sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    row_barrier();
+    const double before = gather(a.part_sum2);
+    if (before < need && need <= before + Sg) {  // (uniform over the workgroup)
+      double run = before + block_exclusive(mine, sm);
+      if (run < need && need <= run + mine)
+        for (int i = lo; i < hi; ++i)
+          if (sample_key(xs[i]) == kc && in(i)) {
+            run += unit(xs[i]);
+            if (run >= need) {
+              __hip_atomic_store(a.row_cut + 2 * b + which, c0 + i, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
           }
-        }
-  }
-  row_barrier();
-  const int ic = __hip_atomic_load(a.row_cut + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    row_barrier();
+    return __hip_atomic_load(a.row_cut + 2 * b + which, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto all = [](int) { return true; };
+  auto count = [](float) { return 1.0; };
 
-  // --- the draw among the kept tokens (key above kc, or kc up to ic), in
-  // id order
+  // --- top-k: the k first tokens in rank order (key, then id)
+  unsigned kk = 0u;
+  int ik = V;
+  auto in_k = [&](int i) {
+    const unsigned key = sample_key(xs[i]);
+    return key > kk || (key == kk && c0 + i <= ik);
+  };
+  if (use_k) {
+    pass_hist(0, 24, 0u, 0u, all, count);
+    kk = select(1, 24, 0u, 0u, (double)k, all, count);
+    ik = cut_id(kk, sm.need, 0, all, count);
+  }
+
+  // --- top-p among them: the shortest rank-order prefix whose weight
+  // reaches ceil(p * their total)
+  unsigned kp = 0u;
+  int ip = V;
+  if (use_p) {
+    if (use_k) {
+      pass_hist(4, 24, 0u, 0u, in_k, weight);
+      if (tid < 64) {  // their total, from the histogram
+        double t4 = 0.0;
+        for (int e = 0; e < 4; ++e) t4 += sm.mass[4 * tid + e];
+        for (int m = 32; m >= 1; m >>= 1) t4 += __shfl_xor(t4, m);
+        if (tid == 0) s_total = t4;
+      }
+      __syncthreads();
+      kp = select(5, 24, 0u, 0u, ceil((double)p * s_total), in_k, weight);
+    } else {
+      double R = 0.0;  // the row's total, from the second launch
+      for (int w = 0; w < G; ++w) R += a.part_sum[(size_t)b * G + w];
+      load_hist(a.row_hist + (size_t)b * 256);
+      kp = select(0, 24, 0u, 0u, ceil((double)p * R), all, weight);
+    }
+    ip = cut_id(kp, sm.need, 1, in_k, weight);
+  }
+
+  // --- the draw among the kept tokens, in id order
   auto kept = [&](int i) {
     const unsigned key = sample_key(xs[i]);
-    return key > kc || (key == kc && c0 + i <= ic);
+    return in_k(i) && (key > kp || (key == kp && c0 + i <= ip));
   };
-  mine = 0.0;
+  double mine = 0.0;
   for (int i = lo; i < hi; ++i)
     if (kept(i)) mine += weight(xs[i]);
-  Sg = block_sum(mine, sm);
+  const double Sg = block_sum(mine, sm);
   if (tid == 0)
     __hip_atomic_store(a.part_sum3 + (size_t)b * G + g, Sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   row_barrier();
-  before = gather(a.part_sum3);
+  const double before = gather(a.part_sum3);
   double Rk = 0.0;
   for (int w = 0; w < G; ++w) Rk += s_sums[w];
   const double t = fmin(floor((double)u * Rk), Rk - 1.0);
@@ -876,9 +776,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_nucleus_kernel(SampleAr
   }
   __syncthreads();
   if (s_flag != 0u) {
-    for (int j = tid; j < 4 * 256; j += kSampleThreads) {
-      double* hp = j < 256 ? a.row_hist + (size_t)b * 256 + j
-                           : a.row_hist3 + (size_t)b * 3 * 256 + (j - 256);
+    for (int j = tid; j < (1 + kPassHists) * 256; j += kSampleThreads) {
+      double* hp = j < 256 ? a.row_hist + (size_t)b * 256 + j : hist + (j - 256);
       __hip_atomic_store(hp, 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) reset_counter(cnt);
@@ -928,15 +827,15 @@ constexpr size_t kNaSum = kNaCand + na_align(kNaSlots * 64 * 8);         // doub
 constexpr size_t kNaSum2 = kNaSum + na_align(kNaSlots * 8);              // double [B][G]
 constexpr size_t kNaSum3 = kNaSum2 + na_align(kNaSlots * 8);             // double [B][G]
 constexpr size_t kNaFlag = kNaSum3 + na_align(kNaSlots * 8);             // int [B]
-constexpr size_t kNaCut = kNaFlag + na_align((size_t)kNoAllocBatch * 4);  // int [B]
+constexpr size_t kNaCut = kNaFlag + na_align((size_t)kNoAllocBatch * 4);  // int [B][2]
 // (counters and row histograms of all three launches are contiguous: one
 // fill clears them at the start of every call)
-constexpr size_t kNaCnt = kNaCut + na_align((size_t)kNoAllocBatch * 4);  // u32 [B][kCntStride]
+constexpr size_t kNaCnt = kNaCut + na_align((size_t)kNoAllocBatch * 2 * 4);  // u32 [B][kCntStride]
 constexpr size_t kNaCnt2 = kNaCnt + na_align((size_t)kNoAllocBatch * kCntStride * 4);
 constexpr size_t kNaCnt3 = kNaCnt2 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
 constexpr size_t kNaHist = kNaCnt3 + na_align((size_t)kNoAllocBatch * kCntStride * 4);
-constexpr size_t kNaHist3 = kNaHist + na_align((size_t)kNoAllocBatch * 256 * 8);
-constexpr size_t kNaBytes = kNaHist3 + na_align((size_t)kNoAllocBatch * 3 * 256 * 8);  // ~1.6 MB
+constexpr size_t kNaPassHist = kNaHist + na_align((size_t)kNoAllocBatch * 256 * 8);
+constexpr size_t kNaBytes = kNaPassHist + na_align((size_t)kNoAllocBatch * kPassHists * 256 * 8);  // ~2.2 MB
 
 static __device__ __align__(256) unsigned char scratch[kNaBytes];
 
@@ -1007,7 +906,7 @@ extern "C" int qd_sample_noalloc(int32_t batch, int32_t vocab, const float* logi
                reinterpret_cast<unsigned long long*>(p + kNaCand),
                reinterpret_cast<unsigned*>(p + kNaCnt), reinterpret_cast<double*>(p + kNaSum),
                reinterpret_cast<unsigned*>(p + kNaCnt2), reinterpret_cast<double*>(p + kNaHist),
-               reinterpret_cast<double*>(p + kNaHist3), reinterpret_cast<double*>(p + kNaSum2),
+               reinterpret_cast<double*>(p + kNaPassHist), reinterpret_cast<double*>(p + kNaSum2),
                reinterpret_cast<double*>(p + kNaSum3), reinterpret_cast<unsigned*>(p + kNaCnt3),
                reinterpret_cast<int*>(p + kNaFlag), reinterpret_cast<int*>(p + kNaCut), nullptr};
   e = launch_sample(a, batch, s);

@@ -134,6 +134,44 @@ def test_sample_grid_of_draws(torch, T, k, p):
     dec.close()
 
 
+def test_sample_third_launch_rows_together(torch):
+    """Whole batches of the rows the multi-workgroup radix selection takes at
+    V = 151,936: top-p without a top-k limit, most with nuclei beyond the
+    row's first 64 tokens, and top_k above 64 with and without top-p.  Every
+    row against the oracle, on consecutive calls of different batch sizes
+    that share the handle's histograms and counters, and a repeat of the
+    first call giving the same ids."""
+    V = 151936
+    rng = np.random.default_rng(5150)
+    dec = _handle(V)
+    runs = []
+    total = exact = beyond = 0
+    for B in (64, 37):
+        logits = _rows(rng, V, B)
+        T = rng.choice([0.6, 1.0, 1.7], size=B).astype(np.float32)
+        k = rng.choice([0, V, -5, 100, 3000], size=B).astype(np.int32)
+        p = rng.choice([0.2, 0.5, 0.9, 0.99, 1.0], size=B).astype(np.float32)
+        p[(k <= 0) | (k >= V)] = np.minimum(p[(k <= 0) | (k >= V)], 0.99)  # top-p or top-k
+        u = rng.random(B).astype(np.float32)
+        say(f"third-launch rows, batch {B}")
+        got = _run(torch, dec, logits, T, k, p, u)
+        exact += _check(logits, T.astype(float), k, p.astype(float), u.astype(float), got)
+        beyond += sum(int(S.sample(logits[r], float(T[r]), int(k[r]), float(p[r]),
+                                   float(u[r])).kept.sum()) > 64 for r in range(B))
+        total += B
+        runs.append((logits, T, k, p, u, got))
+    logits, T, k, p, u, first = runs[0]
+    again = _run(torch, dec, logits, T, k, p, u)
+    np.testing.assert_array_equal(again, first)
+    say(f"third launch: {beyond} of {total} rows keep more than 64 tokens, "
+        f"{exact} compared exactly")
+    assert beyond >= total // 2
+    # flat and near-uniform rows put most of their cuts within the fp32
+    # bound of a boundary (49 of these 101 draws are clear of it)
+    assert exact >= total // 3
+    dec.close()
+
+
 def test_sample_greedy_equals_step_argmax(torch):
     """Temperature 0, top_k 1 and top_p 0 all give the step's own argmax."""
     shape = synth.TINY

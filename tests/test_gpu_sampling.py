@@ -172,6 +172,53 @@ def test_sample_third_launch_rows_together(torch):
     dec.close()
 
 
+def _edge_rows(rng, V):
+    """Settings at the edges of the multi-workgroup selection: top-k just
+    above the 64-token lists and at V - 1, a top-p cut at the first token,
+    masked vocabularies (-inf logits: weight 0, still counted by top-k), a
+    temperature that leaves nearly all weight on the maximum, near-uniform
+    rows and coarse ties."""
+    base = lambda: rng.normal(scale=2.0, size=V)
+    masked = lambda: np.where(rng.random(V) < 0.5, -np.inf, rng.normal(scale=2.0, size=V))
+    spike = lambda: np.where(np.arange(V) == V // 3, 8.0, rng.normal(scale=0.5, size=V))
+    rows = [  # logits, T, top_k, top_p
+        (base(), 1.0, 65, 1.0),
+        (base(), 1.0, V - 1, 1.0),
+        (base(), 0.8, V - 1, 0.999),
+        (base(), 1.0, 1000, 1e-6),
+        (masked(), 1.0, (3 * V) // 4, 1.0),
+        (masked(), 1.2, 0, 0.9),
+        (base(), 1e-3, 1000, 0.9),
+        (rng.normal(scale=0.05, size=V), 2.0, 300, 0.5),
+        (spike(), 1.0, 0, 0.99),
+        (np.round(base() * 2) / 2, 1.0, 5000, 1.0),
+    ]
+    logits = np.array([r[0] for r in rows], np.float32)
+    T = np.array([r[1] for r in rows], np.float32)
+    k = np.array([r[2] for r in rows], np.int32)
+    p = np.array([r[3] for r in rows], np.float32)
+    return logits, T, k, p
+
+
+@pytest.mark.parametrize("V", [4160, 32896, 151936])
+def test_sample_third_launch_edge_cases(torch, V):
+    """The edge settings against the oracle at one, five and nineteen chunks
+    per row, twice with the rows in a different order (the second call
+    finds the first call's histograms and counters cleared)."""
+    rng = np.random.default_rng(V + 1)
+    dec = _handle(V)
+    logits, T, k, p = _edge_rows(rng, V)
+    u = rng.random(len(T)).astype(np.float32)
+    for call, perm in enumerate([np.arange(len(T)), rng.permutation(len(T))]):
+        say(f"edge settings V={V} call {call}")
+        got = _run(torch, dec, logits[perm], T[perm], k[perm], p[perm], u[perm])
+        _check(logits[perm], T[perm].astype(float), k[perm], p[perm].astype(float),
+               u[perm].astype(float), got)
+        d = S.sample(logits[3], float(T[3]), int(k[3]), float(p[3]), float(u[3]))
+        assert got[list(perm).index(3)] == d.token == S.rank_order(logits[3])[0]
+    dec.close()
+
+
 def test_sample_greedy_equals_step_argmax(torch):
     """Temperature 0, top_k 1 and top_p 0 all give the step's own argmax."""
     shape = synth.TINY

@@ -826,6 +826,11 @@ __device__ inline void gemv_item(const GemvArgs& a, const uint16_t* w, const flo
     }
   }
   if (norm) {
+    // The first sums stay opaque until here: otherwise the compiler adds
+    // the first one where it is loaded, so that the wave waits for it (and
+    // for every load issued before it) before the weight tiles go out.
+#pragma unroll
+    for (int j = 0; j < kSsq; ++j) asm volatile("" : "+v"(sv[j]));
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kSsq; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;
@@ -1226,6 +1231,11 @@ __device__ inline void gemv_wide_item(const GemvArgs& a, const Done& done, int i
   mark(1);
   store_chunk(0);
   if (norm) {
+    // The first sums stay opaque until here: otherwise the compiler adds
+    // the first one where it is loaded, so that the wave waits for it (and
+    // for every load issued before it) before the weight tiles go out.
+#pragma unroll
+    for (int j = 0; j < kSsq; ++j) asm volatile("" : "+v"(sv[j]));
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kSsq; ++j) ss += sp + j * kParts < ng ? sv[j] : 0.f;

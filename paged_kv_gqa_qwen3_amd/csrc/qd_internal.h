@@ -291,7 +291,8 @@ constexpr int kMaxSplitsStaged = 512;
 
 // On-device sampling (qd_sample.hip): G workgroups per row of logits, each
 // owning C of them; top_k up to kFastTopK is merged from per-chunk lists of
-// 64 candidates, anything else runs over the whole row in one workgroup.
+// 64 candidates, larger top_k and top-p nuclei beyond those 64 tokens are
+// selected by all G workgroups of the row together (radix passes).
 constexpr int kFastTopK = 64;
 constexpr int kSampleChunk = 8192;  // most logits per workgroup
 constexpr int kMaxSampleChunks = 64;  // most workgroups per row (vocab <= 524288)

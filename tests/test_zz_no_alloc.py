@@ -23,10 +23,11 @@ def torch():
 
 
 # temperature, top_k, top_p: greedy, the fast top-k lists, a top-k beyond
-# them and top-p beyond the first 64 tokens (the multi-workgroup selection),
-# top-p inside the first 64 tokens, no limit
+# them (alone and with top-p) and top-p beyond the first 64 tokens (the
+# multi-workgroup selection), top-p inside the first 64 tokens, no limit
 SETTINGS = [(0.0, 0, 1.0), (0.7, 20, 0.95), (1.0, 200, 1.0), (0.3, 0, 0.9),
-            (1.0, 0, 0.999), (1.0, 0, 1.0), (0.8, 64, 0.5), (1.3, 1, 1.0)]
+            (1.0, 0, 0.999), (1.0, 0, 1.0), (0.8, 64, 0.5), (1.3, 1, 1.0),
+            (1.1, 500, 0.9)]
 
 
 def _inputs(torch, B, V, seed):
